@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""Benchmark of the gated-delta SSM layer core on one MI355X.
+
+One timed step = one decode step of the whole layer core on the batched-decode
+workload (64 sequences x 48 value heads, 128x128 fp32 state per head,
+conv 10240 channels read from 20480-wide rows): decay gate -> conv1d + SiLU +
+L2 -> recurrence (q, k, v read straight out of the conv output rows) ->
+gated RMSNorm, all four launches on one stream.  Inputs are resident in HBM
+before the timed region.  The state lives in one of several pools, rotated
+step by step, so the 192 MiB state cannot stay in the 256 MB MALL between
+steps ("cold"); a same-pool ("MALL-hot") figure is reported beside it.
+
+value = decode state GB/s of the whole step: (state bytes read + written) /
+step time.  The prefill half of the metric (tokens/s of the 4096-token prompt
+through gate, token-parallel conv, chunked recurrence and norm) is timed in the
+same run and reported under "prefill".
+
+Prints ONE JSON line.  --gpus N > 1 is refused: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+FP32_MATRIX_PEAK_TFLOPS = 157.3
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--pools", type=int, default=4, help="state pools rotated for cold timing")
+    p.add_argument("--prefill-iters", type=int, default=10)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+def decode_bytes(wl) -> dict:
+    """Algorithmic HBM bytes of one decode step, per kernel (fp32 = 4 B)."""
+    n, T, H, Hk, S, C, D = wl.n_seq, wl.n_tok, wl.H, wl.Hk, wl.S, wl.conv_dim, wl.d_conv
+    state = n * H * S * S * 4
+    recur = 2 * state + n * T * (2 * Hk * S + 2 * H * S + 2 * H) * 4
+    conv = n * (2 * C * (D - 1) + T * 2 * C) * 4 + C * D * 4
+    norm = n * T * 3 * H * wl.head_dim * 4 + wl.head_dim * 4
+    gate = n * T * H * 2 * 4 + 2 * H * 4
+    return {"state": 2 * state, "recurrence": recur, "conv": conv, "norm": norm, "gate": gate}
+
+
+def chunked_flops(T: int, H: int, S: int, C: int = 64) -> float:
+    """Algorithmic flops of the chunked recurrence: per token-head 10*C*S + 6*S^2."""
+    return float(T) * H * (10 * C * S + 6 * S * S)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: the gated-delta core has no cross-GPU "
+              "step in this build (--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_delta_ssm_amd as gdn
+    from gdn_inputs import WORKLOADS, make_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    # ---------------------------------------------------------------- decode step
+    wl = WORKLOADS["decode64"]
+    inp = make_inputs(wl)
+    cu = {k: v.to(dev) for k, v in inp.items() if isinstance(v, torch.Tensor)}
+    n, H, Hk, S, C = wl.n_seq, wl.H, wl.Hk, wl.S, wl.conv_dim
+    pools = [cu["state"].clone() for _ in range(args.pools)]
+    hists = [cu["conv_hist"].clone() for _ in range(args.pools)]
+    x = cu["x"][:, :, :C]                                   # rows 20480 apart
+    conv_out = torch.empty(n, 1, C, device=dev)            # rows 10240 apart
+    g = torch.empty(n, H, device=dev)
+    y = torch.empty(n, 1, H, S, device=dev)
+    nout = torch.empty(n, H, S, device=dev)
+    qv = conv_out[:, :, :Hk * S].unflatten(-1, (Hk, S))
+    kv = conv_out[:, :, Hk * S:2 * Hk * S].unflatten(-1, (Hk, S))
+    vv = conv_out[:, :, 2 * Hk * S:].unflatten(-1, (H, S))
+    z = cu["z"]                                             # [n][H][S]
+
+    rec_ev = []
+
+    def decode_step(i, timed=False):
+        p = i % len(pools)
+        gdn.gdn_decay_gate(cu["alpha"], cu["dt"], cu["a"], g)
+        gdn.gdn_conv1d_silu_l2norm(x, cu["conv_w"], hists[p], conv_out,
+                                   qk_channels=wl.qk_channels, head_dim=wl.head_dim,
+                                   l2_eps=wl.l2_eps)
+        if timed:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        gdn.gdn_recurrence_decode(pools[p], qv, kv, vv, g.view(n, 1, H), cu["beta"], y,
+                                  scale=wl.scale)
+        if timed:
+            e1 = torch.cuda.Event(enable_timing=True)
+            e1.record(stream)
+            rec_ev.append((e0, e1))
+        gdn.gdn_gated_rmsnorm(y.view(n, H, S), cu["norm_w"], z, nout, eps=wl.norm_eps)
+
+    for i in range(args.warmup):
+        decode_step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        decode_step(i, timed=True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    rec_ms = float(np.mean([a.elapsed_time(b) for a, b in rec_ev]))
+    by = decode_bytes(wl)
+    value = by["state"] / (ms_per_step * 1e-3) / 1e9
+
+    # same-pool repeat: the state may stay in the MALL between launches
+    hot_ev = []
+    for i in range(args.warmup):
+        gdn.gdn_recurrence_decode(pools[0], qv, kv, vv, g.view(n, 1, H), cu["beta"], y,
+                                  scale=wl.scale)
+    for i in range(args.steps):
+        e0 = torch.cuda.Event(enable_timing=True); e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        gdn.gdn_recurrence_decode(pools[0], qv, kv, vv, g.view(n, 1, H), cu["beta"], y,
+                                  scale=wl.scale)
+        e1.record(stream)
+        hot_ev.append((e0, e1))
+    torch.cuda.synchronize()
+    hot_ms = float(np.mean([a.elapsed_time(b) for a, b in hot_ev]))
+    achieved = by["recurrence"] / (rec_ms * 1e-3) / 1e9
+
+    del pools, hists
+    torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- prefill pass
+    pw = WORKLOADS["prefill"]
+    pin = make_inputs(pw)
+    pc = {k: v.to(dev) for k, v in pin.items() if isinstance(v, torch.Tensor)}
+    T, PH, PHk, PS, PC = pw.n_tok, pw.H, pw.Hk, pw.S, pw.conv_dim
+    pg = torch.empty(T, PH, device=dev)
+    pout = torch.empty(1, T, PC, device=dev)
+    pst = torch.empty(1, PH, PS, PS, device=dev)
+    phist = torch.empty_like(pc["conv_hist"])
+    py = torch.empty(1, T, PH, PS, device=dev)
+    pn = torch.empty(T, PH, PS, device=dev)
+    pq = pout[:, :, :PHk * PS].unflatten(-1, (PHk, PS))
+    pk = pout[:, :, PHk * PS:2 * PHk * PS].unflatten(-1, (PHk, PS))
+    pv = pout[:, :, 2 * PHk * PS:].unflatten(-1, (PH, PS))
+    ws = torch.empty(max(gdn.gdn_recurrence_chunked_workspace_bytes(1, T, PH, PHk, PS, 64), 1),
+                     dtype=torch.uint8, device=dev)
+    prefill = None
+    ev = {}
+
+    def prefill_pass(timed=False):
+        pst.zero_()
+        phist.copy_(pc["conv_hist"])
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if timed else None
+        if timed: marks[0].record(stream)
+        gdn.gdn_decay_gate(pc["alpha"], pc["dt"], pc["a"], pg)
+        if timed: marks[1].record(stream)
+        gdn.gdn_conv1d_silu_l2norm(pc["x"], pc["conv_w"], phist, pout,
+                                   qk_channels=pw.qk_channels, head_dim=pw.head_dim,
+                                   l2_eps=pw.l2_eps)
+        if timed: marks[2].record(stream)
+        gdn.gdn_recurrence_chunked(pst, pq, pk, pv, pg.view(1, T, PH), pc["beta"], py,
+                                   scale=pw.scale, workspace=ws)
+        if timed: marks[3].record(stream)
+        gdn.gdn_gated_rmsnorm(py.view(T, PH, PS), pc["norm_w"], pc["z"], pn, eps=pw.norm_eps)
+        if timed:
+            marks[4].record(stream)
+            ev.setdefault("marks", []).append(marks)
+
+    try:
+        for _ in range(2):
+            prefill_pass()
+        torch.cuda.synchronize()
+        for _ in range(args.prefill_iters):
+            prefill_pass(timed=True)
+        torch.cuda.synchronize()
+        seg = np.array([[m[j].elapsed_time(m[j + 1]) for j in range(4)] for m in ev["marks"]])
+        seg = seg.mean(axis=0)                           # ms: gate, conv, chunked, norm
+        total = float(seg.sum())
+        fl = chunked_flops(T, PH, PS)
+        prefill = {
+            "workload": "prefill: 1 seq x 4096 tokens, 32 value / 16 q-k heads, 128x128 state, "
+                        "conv 8192 ch, chunk 64",
+            "tokens_per_s": T / (total * 1e-3),
+            "recurrence_tokens_per_s": T / (seg[2] * 1e-3),
+            "ms": {"gate": seg[0], "conv": seg[1], "chunked_recurrence": seg[2], "norm": seg[3]},
+            "chunked_algorithmic_tflops": fl / (seg[2] * 1e-3) / 1e12,
+            "chunked_frac_of_bf16_peak": fl / (seg[2] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        }
+    except gdn.GdnError as e:
+        prefill = {"error": str(e)}
+
+    # ---------------------------------------------------------------- CPU baseline (oracle)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, inp, args.cpu_seconds)
+
+    out = {
+        "metric": "decode state GB/s (% HBM roof) + chunked-prefill tokens/s per GDN layer",
+        "value": value,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode64: 64 seq x 1 token, 48 value / 16 q-k heads, 128x128 fp32 "
+                        "state per head (192 MiB), conv 10240 ch from 20480-wide rows; "
+                        "gate+conv+recurrence+norm per step, state pools rotated (cold)",
+            "state_pools": args.pools,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "k_recur_decode",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "bytes_per_launch": by["recurrence"],
+            "avg_launch_ms": rec_ms,
+        },
+        "decode": {
+            "recurrence_state_GBs_cold": by["state"] / (rec_ms * 1e-3) / 1e9,
+            "recurrence_ms_cold": rec_ms,
+            "recurrence_ms_mall_hot": hot_ms,
+            "recurrence_state_GBs_mall_hot": by["state"] / (hot_ms * 1e-3) / 1e9,
+            "step_frac_of_hbm": value / HBM_PEAK_GBS,
+        },
+        "prefill": prefill,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out, default=float))
+
+
+def cpu_baseline(wl, inp, seconds: float) -> dict:
+    """The fp64 oracle's decode step (gate, conv, sequential recurrence, norm) on
+    the same decode64 inputs, repeated for about `seconds` of host time."""
+    import numpy as np
+
+    import oracle
+    if not os.path.exists(oracle.LIB_PATH):
+        oracle.build()
+    n, H, S, C = wl.n_seq, wl.H, wl.S, wl.conv_dim
+    x = inp["x"][:, :, :C]
+    times = []
+    t_end = time.perf_counter() + seconds
+    while True:
+        t0 = time.perf_counter()
+        g = oracle.decay_gate(inp["alpha"], inp["dt"], inp["a"])
+        out, _, _ = oracle.conv1d_silu_l2norm(x, inp["conv_w"], inp["conv_hist"],
+                                              wl.qk_channels, wl.head_dim, wl.l2_eps)
+        Hk = wl.Hk
+        q = out[:, :, :Hk * S].reshape(n, 1, Hk, S)
+        k = out[:, :, Hk * S:2 * Hk * S].reshape(n, 1, Hk, S)
+        v = out[:, :, 2 * Hk * S:].reshape(n, 1, H, S)
+        y, _, _ = oracle.recurrence_seq(inp["state"], q, k, v, g.reshape(n, 1, H), inp["beta"],
+                                        wl.scale)
+        oracle.gated_rmsnorm(y.reshape(n, H, S), inp["norm_w"], inp["z"], wl.norm_eps)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() > t_end and len(times) >= 3:
+            break
+    med = float(np.median(times))
+    state_bytes = 2 * n * H * S * S * 4
+    return {"value": state_bytes / med / 1e9, "unit": "GB/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"whole decode64 step (gate, conv, sequential fp64 recurrence, norm), "
+                      f"median of {len(times)} runs over ~{seconds:.0f} s; state bytes of the "
+                      f"fp32 step divided by the oracle's time",
+            "ms_per_step": med * 1e3}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,214 @@
+"""Python binding of libgdn.so, the gfx950 gated-delta SSM layer core.
+
+Argument marshalling only: each function below takes torch tensors that
+already live on the GPU, checks dtype/device/layout, and passes raw device
+pointers, element strides and the current HIP stream to the C entry point of
+the same name (declared in include/gdn.h).  Every step of the computation runs
+in the library's HIP kernels; there is no fallback.  Importing this module
+fails loudly if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; "
+                      "g.build()'` (or gated_delta_ssm_amd/_build.py) first")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_L = ctypes.c_int64
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+
+_SIGS = {
+    "gdn_strerror": (ctypes.c_char_p, [_I]),
+    "gdn_version": (_I, []),
+    "gdn_decay_gate": (_I, [_P, _P, _P, _P, _I, _I, _P]),
+    "gdn_conv1d_silu_l2norm": (_I, [_P, _L, _L, _P, _P, _L, _P, _L, _L, _P, _L, _L,
+                                    _I, _I, _I, _I, _I, _I, _F, _P]),
+    "gdn_recurrence_decode": (_I, [_P, _L, _P, _P, _L, _L, _P, _L, _L, _P, _P, _P, _L, _L,
+                                   _P, _L, _I, _I, _I, _I, _I, _F, _P]),
+    "gdn_recurrence_chunked_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "gdn_recurrence_chunked": (_I, [_P, _L, _P, _P, _L, _L, _P, _L, _L, _P, _P, _P, _L, _L,
+                                    _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
+    "gdn_gated_rmsnorm": (_I, [_P, _L, _P, _P, _L, _P, _L, _I, _I, _I, _F, _P]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTS = tuple(_SIGS)
+
+
+class GdnError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {_lib.gdn_strerror(status).decode()} (status {status})")
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise GdnError(fn, status)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev_f32(name: str, t: torch.Tensor, inner_contig: int) -> None:
+    """fp32 on a GPU, with the innermost `inner_contig` dims densely packed."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    expect = 1
+    for d in range(t.dim() - 1, t.dim() - 1 - inner_contig, -1):
+        if t.shape[d] > 1 and t.stride(d) != expect:
+            raise ValueError(f"{name}: innermost {inner_contig} dims must be dense, "
+                             f"got strides {t.stride()}")
+        expect *= t.shape[d]
+
+
+def version() -> int:
+    return _lib.gdn_version()
+
+
+def gdn_decay_gate(alpha: torch.Tensor, dt: torch.Tensor, a: torch.Tensor,
+                   g: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """g[r][h] = a[h] * softplus(alpha[r][h] + dt[h]); alpha, g [rows][H] dense."""
+    rows, H = alpha.shape
+    if g is None:
+        g = torch.empty_like(alpha)
+    for n, t in (("alpha", alpha), ("dt", dt), ("a", a), ("g", g)):
+        _dev_f32(n, t, t.dim())
+    _check("gdn_decay_gate", _lib.gdn_decay_gate(_ptr(alpha), _ptr(dt), _ptr(a), _ptr(g),
+                                                 rows, H, _stream(stream)))
+    return g
+
+
+def gdn_conv1d_silu_l2norm(x: torch.Tensor, w: torch.Tensor, conv_state: torch.Tensor,
+                           out: torch.Tensor, *, qk_channels: int, head_dim: int,
+                           l2_eps: float, snap: torch.Tensor | None = None,
+                           stream=None) -> torch.Tensor:
+    """Conv1d + SiLU (+ L2 on Q/K channels) over x [n_seq][n_tok][conv_dim] (any
+    row strides), rolling conv_state [n_seq][conv_dim][d_conv-1] in place, into
+    out [n_seq][n_tok][conv_dim]; snap [n_seq][n_tok-1][conv_dim][d_conv-1]."""
+    n_seq, n_tok, C = out.shape
+    D = w.shape[1]
+    if x.shape != out.shape:
+        raise ValueError(f"x {tuple(x.shape)} and out {tuple(out.shape)} differ")
+    if w.shape[0] != C or tuple(conv_state.shape) != (n_seq, C, D - 1):
+        raise ValueError("conv weight / state shape mismatch")
+    _dev_f32("x", x, 1)
+    _dev_f32("out", out, 1)
+    _dev_f32("w", w, 2)
+    _dev_f32("conv_state", conv_state, 2)
+    sn_tok = sn_seq = 0
+    if snap is not None:
+        _dev_f32("snap", snap, 2)
+        if tuple(snap.shape) != (n_seq, n_tok - 1, C, D - 1):
+            raise ValueError("snap shape mismatch")
+        sn_seq, sn_tok = snap.stride(0), snap.stride(1)
+    _check("gdn_conv1d_silu_l2norm", _lib.gdn_conv1d_silu_l2norm(
+        _ptr(x), x.stride(1), x.stride(0), _ptr(w), _ptr(conv_state), conv_state.stride(0),
+        _ptr(out), out.stride(1), out.stride(0), _ptr(snap), sn_tok, sn_seq,
+        n_seq, n_tok, C, D, qk_channels, head_dim, l2_eps, _stream(stream)))
+    return out
+
+
+def _recur_check(state, q, k, v, g, beta, y):
+    n_seq, n_tok, Hk, S = q.shape
+    H = v.shape[2]
+    if tuple(state.shape) != (n_seq, H, S, S) or k.shape != q.shape:
+        raise ValueError("state / q / k shape mismatch")
+    if tuple(v.shape) != (n_seq, n_tok, H, S) or y.shape != v.shape:
+        raise ValueError("v / y shape mismatch")
+    if tuple(g.shape) != (n_seq, n_tok, H) or beta.shape != g.shape:
+        raise ValueError("g / beta shape mismatch")
+    _dev_f32("state", state, 3)
+    for n, t in (("q", q), ("k", k), ("v", v), ("y", y)):
+        _dev_f32(n, t, 2)
+    if q.stride() != k.stride():
+        raise ValueError("q and k must share strides")
+    _dev_f32("g", g, 3)
+    _dev_f32("beta", beta, 3)
+    return n_seq, n_tok, H, Hk, S
+
+
+def gdn_recurrence_decode(state: torch.Tensor, q: torch.Tensor, k: torch.Tensor,
+                          v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+                          y: torch.Tensor, *, scale: float, snap: torch.Tensor | None = None,
+                          stream=None) -> torch.Tensor:
+    """Token-by-token recurrence.  state [n_seq][H][S][S] (value-major, updated
+    in place), q, k [n_seq][n_tok][Hk][S], v, y [n_seq][n_tok][H][S], g, beta
+    [n_seq][n_tok][H]; snap [n_seq][n_tok-1][H][S][S] or None."""
+    n_seq, n_tok, H, Hk, S = _recur_check(state, q, k, v, g, beta, y)
+    sn_seq = 0
+    if snap is not None:
+        _dev_f32("snap", snap, 4)
+        if tuple(snap.shape) != (n_seq, n_tok - 1, H, S, S):
+            raise ValueError("snap shape mismatch")
+        sn_seq = snap.stride(0)
+    _check("gdn_recurrence_decode", _lib.gdn_recurrence_decode(
+        _ptr(state), state.stride(0), _ptr(q), _ptr(k), q.stride(1), q.stride(0),
+        _ptr(v), v.stride(1), v.stride(0), _ptr(g), _ptr(beta), _ptr(y), y.stride(1),
+        y.stride(0), _ptr(snap), sn_seq, n_seq, n_tok, H, Hk, S, scale, _stream(stream)))
+    return y
+
+
+def gdn_recurrence_chunked_workspace_bytes(n_seq: int, n_tok: int, n_v_heads: int,
+                                           n_qk_heads: int, S: int, chunk: int = 64) -> int:
+    return int(_lib.gdn_recurrence_chunked_workspace_bytes(n_seq, n_tok, n_v_heads,
+                                                           n_qk_heads, S, chunk))
+
+
+def gdn_recurrence_chunked(state: torch.Tensor, q: torch.Tensor, k: torch.Tensor,
+                           v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+                           y: torch.Tensor, *, scale: float, chunk: int = 64,
+                           workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Chunked (WY/UT) form of the recurrence; same layouts as decode.  If no
+    workspace is given one is allocated here through torch."""
+    n_seq, n_tok, H, Hk, S = _recur_check(state, q, k, v, g, beta, y)
+    need = gdn_recurrence_chunked_workspace_bytes(n_seq, n_tok, H, Hk, S, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=state.device)
+    _check("gdn_recurrence_chunked", _lib.gdn_recurrence_chunked(
+        _ptr(state), state.stride(0), _ptr(q), _ptr(k), q.stride(1), q.stride(0),
+        _ptr(v), v.stride(1), v.stride(0), _ptr(g), _ptr(beta), _ptr(y), y.stride(1),
+        y.stride(0), n_seq, n_tok, H, Hk, S, scale, chunk, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return y
+
+
+def gdn_gated_rmsnorm(y: torch.Tensor, w: torch.Tensor, z: torch.Tensor, out: torch.Tensor,
+                      *, eps: float, stream=None) -> torch.Tensor:
+    """out = ((y * rsqrt(mean(y^2) + eps)) * w) * silu(z) per (row, head);
+    y, z, out [rows][H][head_dim] with dense heads and any row stride."""
+    rows, H, hd = y.shape
+    if z.shape != y.shape or out.shape != y.shape or tuple(w.shape) != (hd,):
+        raise ValueError("norm shape mismatch")
+    for n, t in (("y", y), ("z", z), ("out", out)):
+        _dev_f32(n, t, 2)
+    _dev_f32("w", w, 1)
+    _check("gdn_gated_rmsnorm", _lib.gdn_gated_rmsnorm(
+        _ptr(y), y.stride(0), _ptr(w), _ptr(z), z.stride(0), _ptr(out), out.stride(0),
+        rows, H, hd, eps, _stream(stream)))
+    return out

@@ -1,0 +1,110 @@
+// gdn_api.cpp -- the extern "C" entry points declared in include/gdn.h:
+// validate on the host, then hand over to the kernel family's launcher.
+#include "gdn.h"
+
+#include "launch.hpp"
+#include "validate.hpp"
+
+extern "C" {
+
+const char *gdn_strerror(int status) {
+  switch (status) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_NULL: return "a required pointer is NULL";
+    case GDN_ERR_SHAPE: return "a size, stride or alignment is out of range or inconsistent";
+    case GDN_ERR_UNSUPPORTED: return "valid shape with no kernel in this library";
+    case GDN_ERR_ALIAS: return "an output overlaps an input where that is not allowed";
+    case GDN_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
+    case GDN_ERR_LAUNCH: return "the HIP runtime refused the kernel launch";
+    default: return "unknown gdn status";
+  }
+}
+
+int gdn_version(void) { return 100; /* 0.1.0 */ }
+
+int gdn_decay_gate(const float *alpha, const float *dt, const float *a, float *g, int rows,
+                   int n_heads, hipStream_t stream) {
+  const int rc = gdn::check_decay_gate(alpha, dt, a, g, rows, n_heads);
+  if (rc != GDN_OK || rows == 0) return rc;
+  return gdn::launch_decay_gate(alpha, dt, a, g, rows, n_heads, stream);
+}
+
+int gdn_conv1d_silu_l2norm(const float *x, int64_t x_tok_stride, int64_t x_seq_stride,
+                           const float *w, float *conv_state, int64_t state_seq_stride,
+                           float *out, int64_t out_tok_stride, int64_t out_seq_stride,
+                           float *snap, int64_t snap_tok_stride, int64_t snap_seq_stride,
+                           int n_seq, int n_tok, int conv_dim, int d_conv, int qk_channels,
+                           int head_dim, float l2_eps, hipStream_t stream) {
+  const int rc = gdn::check_conv(x, x_tok_stride, x_seq_stride, w, conv_state, state_seq_stride,
+                                 out, out_tok_stride, out_seq_stride, snap, snap_tok_stride,
+                                 snap_seq_stride, n_seq, n_tok, conv_dim, d_conv, qk_channels,
+                                 head_dim);
+  if (rc != GDN_OK) return rc;
+  gdn::ConvArgs a{x,        x_tok_stride,  x_seq_stride,   w,       conv_state,
+                  state_seq_stride, out,   out_tok_stride, out_seq_stride,
+                  snap,     snap_tok_stride, snap_seq_stride, n_seq, n_tok,
+                  conv_dim, d_conv,        qk_channels,    head_dim, l2_eps};
+  return gdn::launch_conv(a, stream);
+}
+
+int gdn_recurrence_decode(float *state, int64_t state_seq_stride, const float *q, const float *k,
+                          int64_t qk_tok_stride, int64_t qk_seq_stride, const float *v,
+                          int64_t v_tok_stride, int64_t v_seq_stride, const float *g,
+                          const float *beta, float *y, int64_t y_tok_stride, int64_t y_seq_stride,
+                          float *snap, int64_t snap_seq_stride, int n_seq, int n_tok,
+                          int n_v_heads, int n_qk_heads, int S, float scale, hipStream_t stream) {
+  const int rc = gdn::check_recur(state, state_seq_stride, q, k, qk_tok_stride, qk_seq_stride, v,
+                                  v_tok_stride, v_seq_stride, g, beta, y, y_tok_stride,
+                                  y_seq_stride, snap, snap_seq_stride, n_seq, n_tok, n_v_heads,
+                                  n_qk_heads, S);
+  if (rc != GDN_OK) return rc;
+  gdn::RecurArgs a{state,        state_seq_stride, q,           k,          qk_tok_stride,
+                   qk_seq_stride, v,               v_tok_stride, v_seq_stride, g,
+                   beta,         y,                y_tok_stride, y_seq_stride, snap,
+                   snap_seq_stride, n_seq,         n_tok,        n_v_heads,  n_qk_heads,
+                   S,            scale};
+  return gdn::launch_recur_decode(a, stream);
+}
+
+size_t gdn_recurrence_chunked_workspace_bytes(int n_seq, int n_tok, int n_v_heads,
+                                              int n_qk_heads, int S, int chunk) {
+  if (n_seq < 1 || n_tok < 1 || n_v_heads < 1 || n_qk_heads < 1 || n_v_heads % n_qk_heads)
+    return 0;
+  if (S != 128 || chunk != 64) return 0;
+  return gdn::chunked_workspace_bytes(n_seq, n_tok, n_v_heads, n_qk_heads, S, chunk);
+}
+
+int gdn_recurrence_chunked(float *state, int64_t state_seq_stride, const float *q, const float *k,
+                           int64_t qk_tok_stride, int64_t qk_seq_stride, const float *v,
+                           int64_t v_tok_stride, int64_t v_seq_stride, const float *g,
+                           const float *beta, float *y, int64_t y_tok_stride,
+                           int64_t y_seq_stride, int n_seq, int n_tok, int n_v_heads,
+                           int n_qk_heads, int S, float scale, int chunk, void *workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  const size_t need =
+      gdn_recurrence_chunked_workspace_bytes(n_seq, n_tok, n_v_heads, n_qk_heads, S, chunk);
+  const int rc = gdn::check_chunked(state, state_seq_stride, q, k, qk_tok_stride, qk_seq_stride,
+                                    v, v_tok_stride, v_seq_stride, g, beta, y, y_tok_stride,
+                                    y_seq_stride, n_seq, n_tok, n_v_heads, n_qk_heads, S, chunk,
+                                    workspace, workspace_bytes, need);
+  if (rc != GDN_OK) return rc;
+  gdn::RecurArgs a{state,        state_seq_stride, q,           k,          qk_tok_stride,
+                   qk_seq_stride, v,               v_tok_stride, v_seq_stride, g,
+                   beta,         y,                y_tok_stride, y_seq_stride, nullptr,
+                   0,            n_seq,            n_tok,        n_v_heads,  n_qk_heads,
+                   S,            scale};
+  return gdn::launch_recur_chunked(a, chunk, workspace, workspace_bytes, stream);
+}
+
+int gdn_gated_rmsnorm(const float *y, int64_t y_row_stride, const float *w, const float *z,
+                      int64_t z_row_stride, float *out, int64_t out_row_stride, int rows,
+                      int n_heads, int head_dim, float eps, hipStream_t stream) {
+  const int rc = gdn::check_norm(y, y_row_stride, w, z, z_row_stride, out, out_row_stride, rows,
+                                 n_heads, head_dim);
+  if (rc != GDN_OK || rows == 0) return rc;
+  gdn::NormArgs a{y, y_row_stride, w, z, z_row_stride, out, out_row_stride, rows, n_heads,
+                  head_dim, eps};
+  return gdn::launch_gated_rmsnorm(a, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,84 @@
+// k_norm.hip -- gated RMSNorm, out = ((y * rsqrt(mean(y^2) + eps)) * w) * silu(z)
+// per (row, head), with the weight shared by every head.
+//
+// Math and multiply order: fm_kernel_ssm.h (Foundry), "Gated RMSNorm" section.
+// z read from a wider per-token row at an offset: ssm_mamba.rs (spark_model),
+// gdn_verify_fused_norm_k2 (the caller passes z already offset).
+//
+// Thread map: one wave64 per block of 64*CPL consecutive elements of a row,
+// lane l holding elements l, l+64, ..; a block is one head (head_dim >= 64) or
+// two heads of 32 lanes (head_dim 32).  The sum of squares is an in-wave xor
+// butterfly.  Each lane reads its own y before any lane writes, so out may be
+// y itself.
+#include <hip/hip_runtime.h>
+
+#include "gdn.h"
+#include "launch.hpp"
+#include "wave.hpp"
+
+namespace gdn {
+
+template <int CPL, int LPH>
+__global__ __launch_bounds__(256) void k_gated_rmsnorm(const float *y, int64_t y_row,
+                                                       const float *__restrict__ w,
+                                                       const float *__restrict__ z, int64_t z_row,
+                                                       float *out, int64_t o_row, int rows,
+                                                       int row_elems, int waves_per_row, int hd,
+                                                       float eps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int64_t r = wave / waves_per_row;
+  if (r >= rows) return;  // uniform per wave
+  const int e0 = (int)(wave - r * waves_per_row) * 64 * CPL + lane;
+  const float *yr = y + r * y_row;
+  const float *zr = z + r * z_row;
+  float *orow = out + r * o_row;
+
+  float yv[CPL], zv[CPL];
+  bool ok[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int e = e0 + 64 * c;
+    ok[c] = e < row_elems;
+    yv[c] = ok[c] ? yr[e] : 0.0f;
+    zv[c] = ok[c] ? zr[e] : 0.0f;
+  }
+  float ss = yv[0] * yv[0];
+#pragma unroll
+  for (int c = 1; c < CPL; ++c) ss = __builtin_fmaf(yv[c], yv[c], ss);
+  ss = group_sum<LPH>(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)hd + eps);
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    if (!ok[c]) continue;
+    const int e = e0 + 64 * c;
+    const int col = e % hd;  // position inside the head: the shared weight index
+    orow[e] = ((yv[c] * inv) * w[col]) * silu(zv[c]);
+  }
+}
+
+namespace {
+template <int CPL, int LPH>
+int run_norm(const NormArgs &a, hipStream_t stream) {
+  const int row_elems = a.H * a.hd;
+  const int waves_per_row = (row_elems + 64 * CPL - 1) / (64 * CPL);
+  const int64_t waves = (int64_t)a.rows * waves_per_row;
+  const unsigned blocks = (unsigned)((waves + 3) / 4);
+  return launch_kernel(k_gated_rmsnorm<CPL, LPH>, dim3(blocks), dim3(256), 0, stream, a.y,
+                       a.y_row, a.w, a.z, a.z_row, a.out, a.o_row, a.rows, row_elems,
+                       waves_per_row, a.hd, a.eps);
+}
+}  // namespace
+
+int launch_gated_rmsnorm(const NormArgs &a, hipStream_t stream) {
+  if (a.rows == 0) return GDN_OK;
+  switch (a.hd) {
+    case 32: return run_norm<1, 32>(a, stream);
+    case 64: return run_norm<1, 64>(a, stream);
+    case 128: return run_norm<2, 64>(a, stream);
+    case 256: return run_norm<4, 64>(a, stream);
+    default: return GDN_ERR_UNSUPPORTED;
+  }
+}
+
+}  // namespace gdn

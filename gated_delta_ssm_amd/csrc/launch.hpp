@@ -1,0 +1,84 @@
+// launch.hpp -- host-side launchers, one per kernel family.  Each returns a
+// gdn_status; arguments reaching them are already validated (validate.cpp).
+#pragma once
+#include <cstddef>
+#include <cstdint>
+#include <tuple>
+#include <utility>
+
+#include <hip/hip_runtime_api.h>
+
+#include "gdn.h"
+
+namespace gdn {
+
+// Launch `kern` through hipLaunchKernel and return its status, so a refused
+// launch is reported by this call itself rather than through the thread's
+// last-error slot.  Arguments are converted to the kernel's parameter types.
+template <typename... KArgs, typename... Args>
+int launch_kernel(void (*kern)(KArgs...), dim3 grid, dim3 block, size_t shmem, hipStream_t stream,
+                  Args... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count");
+  std::tuple<KArgs...> params(static_cast<KArgs>(args)...);
+  void *ptrs[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1];
+  std::apply([&ptrs](auto &...p) {
+    int i = 0;
+    ((ptrs[i++] = (void *)&p), ...);
+  }, params);
+  return hipLaunchKernel((const void *)kern, grid, block, ptrs, shmem, stream) == hipSuccess
+             ? GDN_OK
+             : GDN_ERR_LAUNCH;
+}
+
+int launch_decay_gate(const float *alpha, const float *dt, const float *a, float *g, int rows,
+                      int n_heads, hipStream_t stream);
+
+struct ConvArgs {
+  const float *x;
+  int64_t x_tok, x_seq;
+  const float *w;
+  float *hist;
+  int64_t h_seq;
+  float *out;
+  int64_t o_tok, o_seq;
+  float *snap;
+  int64_t sn_tok, sn_seq;
+  int n_seq, n_tok, C, D, qk_channels, head_dim;
+  float eps;
+};
+int launch_conv(const ConvArgs &a, hipStream_t stream);
+
+struct RecurArgs {
+  float *state;
+  int64_t st_seq;
+  const float *q, *k;
+  int64_t qk_tok, qk_seq;
+  const float *v;
+  int64_t v_tok, v_seq;
+  const float *g, *beta;
+  float *y;
+  int64_t y_tok, y_seq;
+  float *snap;
+  int64_t sn_seq;
+  int n_seq, n_tok, H, Hk, S;
+  float scale;
+};
+int launch_recur_decode(const RecurArgs &a, hipStream_t stream);
+
+size_t chunked_workspace_bytes(int n_seq, int n_tok, int H, int Hk, int S, int chunk);
+int launch_recur_chunked(const RecurArgs &a, int chunk, void *ws, size_t ws_bytes,
+                         hipStream_t stream);
+
+struct NormArgs {
+  const float *y;
+  int64_t y_row;
+  const float *w, *z;
+  int64_t z_row;
+  float *out;
+  int64_t o_row;
+  int rows, H, hd;
+  float eps;
+};
+int launch_gated_rmsnorm(const NormArgs &a, hipStream_t stream);
+
+}  // namespace gdn

@@ -1,0 +1,176 @@
+// validate.cpp -- host-only argument checks for every entry point.  Nothing
+// here calls the HIP runtime, so a wrong call is rejected before any launch
+// (and the checks are testable on a machine without a GPU).
+//
+// Shape limits come from fm_kernel_ssm.h (Foundry), "Shape limits" block and
+// the per-function preconditions: state size a multiple of 32 and at most 256,
+// conv kernel 2..8, norm head width a multiple of 32, at least one position.
+#include "validate.hpp"
+
+#include <cstdint>
+
+#include "gdn.h"
+
+namespace gdn {
+
+namespace {
+
+struct Span {
+  uintptr_t lo = 0, hi = 0;  // byte range [lo, hi)
+  bool empty() const { return hi <= lo; }
+};
+
+// Bytes touched by a [n_outer][n_inner][len] view with element strides.
+Span span_of(const void *p, int64_t n_outer, int64_t s_outer, int64_t n_inner, int64_t s_inner,
+             int64_t len) {
+  Span r;
+  if (!p || n_outer <= 0 || n_inner <= 0 || len <= 0) return r;
+  const int64_t last = (n_outer - 1) * s_outer + (n_inner - 1) * s_inner + len;
+  r.lo = (uintptr_t)p;
+  r.hi = r.lo + (uintptr_t)last * sizeof(float);
+  return r;
+}
+
+bool overlap(Span a, Span b) { return !a.empty() && !b.empty() && a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned(const void *p, uintptr_t bytes) { return ((uintptr_t)p % bytes) == 0; }
+
+// Rows of an OUTPUT view must not overlap one another.
+bool rows_disjoint(int64_t n_outer, int64_t s_outer, int64_t n_inner, int64_t s_inner,
+                   int64_t len) {
+  if (n_inner > 1 && s_inner < len) return false;
+  if (n_outer > 1 && s_outer < (n_inner - 1) * s_inner + len) return false;
+  return true;
+}
+
+bool supported_head_dim(int hd) { return hd == 32 || hd == 64 || hd == 128 || hd == 256; }
+
+}  // namespace
+
+int check_decay_gate(const float *alpha, const float *dt, const float *a, const float *g,
+                     int rows, int n_heads) {
+  if (rows < 0 || n_heads < 1) return GDN_ERR_SHAPE;
+  if (rows == 0) return GDN_OK;
+  if (!alpha || !dt || !a || !g) return GDN_ERR_NULL;
+  const Span out = span_of(g, 1, 0, rows, n_heads, n_heads);
+  const Span in = span_of(alpha, 1, 0, rows, n_heads, n_heads);
+  // g may be alpha itself (elementwise), but not a shifted overlap of it
+  if (overlap(out, in) && g != alpha) return GDN_ERR_ALIAS;
+  if (overlap(out, span_of(dt, 1, 0, 1, 0, n_heads)) || overlap(out, span_of(a, 1, 0, 1, 0, n_heads)))
+    return GDN_ERR_ALIAS;
+  return GDN_OK;
+}
+
+int check_conv(const float *x, int64_t x_tok, int64_t x_seq, const float *w, const float *hist,
+               int64_t h_seq, const float *out, int64_t o_tok, int64_t o_seq, const float *snap,
+               int64_t sn_tok, int64_t sn_seq, int n_seq, int n_tok, int C, int D, int qk,
+               int head_dim) {
+  if (n_seq < 1 || n_tok < 1 || C < 1) return GDN_ERR_SHAPE;
+  if (D < 2 || D > 8) return GDN_ERR_SHAPE;
+  if (qk < 0 || qk > C) return GDN_ERR_SHAPE;
+  if (qk > 0) {
+    if (head_dim < 32 || head_dim % 32 != 0 || qk % head_dim != 0) return GDN_ERR_SHAPE;
+    if (!supported_head_dim(head_dim)) return GDN_ERR_UNSUPPORTED;
+  }
+  if (x_tok < 0 || x_seq < 0 || h_seq < 0 || o_tok < 0 || o_seq < 0 || sn_tok < 0 || sn_seq < 0)
+    return GDN_ERR_SHAPE;
+  if (!x || !w || !hist || !out) return GDN_ERR_NULL;
+  const int64_t hlen = (int64_t)C * (D - 1);
+  if (!rows_disjoint(n_seq, o_seq, n_tok, o_tok, C)) return GDN_ERR_SHAPE;
+  if (!rows_disjoint(n_seq, h_seq, 1, 0, hlen)) return GDN_ERR_SHAPE;
+  const int n_snap = n_tok - 1;
+  if (snap && n_snap > 0 && !rows_disjoint(n_seq, sn_seq, n_snap, sn_tok, hlen))
+    return GDN_ERR_SHAPE;
+  const Span sx = span_of(x, n_seq, x_seq, n_tok, x_tok, C);
+  const Span sw = span_of(w, 1, 0, 1, 0, (int64_t)C * D);
+  const Span sh = span_of(hist, n_seq, h_seq, 1, 0, hlen);
+  const Span so = span_of(out, n_seq, o_seq, n_tok, o_tok, C);
+  const Span ss = snap ? span_of(snap, n_seq, sn_seq, n_snap, sn_tok, hlen) : Span{};
+  if (overlap(so, sx) || overlap(so, sw) || overlap(so, sh) || overlap(so, ss)) return GDN_ERR_ALIAS;
+  if (overlap(sh, sx) || overlap(sh, sw) || overlap(ss, sh) || overlap(ss, sx) || overlap(ss, sw))
+    return GDN_ERR_ALIAS;
+  return GDN_OK;
+}
+
+int check_recur(const float *state, int64_t st_seq, const float *q, const float *k,
+                int64_t qk_tok, int64_t qk_seq, const float *v, int64_t v_tok, int64_t v_seq,
+                const float *g, const float *beta, const float *y, int64_t y_tok, int64_t y_seq,
+                const float *snap, int64_t sn_seq, int n_seq, int n_tok, int H, int Hk, int S) {
+  if (n_seq < 1 || n_tok < 1 || H < 1 || Hk < 1 || H % Hk != 0) return GDN_ERR_SHAPE;
+  if (S < 32 || S % 32 != 0 || S > 256) return GDN_ERR_SHAPE;
+  if (S != 32 && S != 64 && S != 128 && S != 256) return GDN_ERR_UNSUPPORTED;
+  if (st_seq < 0 || qk_tok < 0 || qk_seq < 0 || v_tok < 0 || v_seq < 0 || y_tok < 0 ||
+      y_seq < 0 || sn_seq < 0)
+    return GDN_ERR_SHAPE;
+  if (!state || !q || !k || !v || !g || !beta || !y) return GDN_ERR_NULL;
+  const int64_t head = (int64_t)S * S, st_len = head * H;
+  if (!rows_disjoint(n_seq, st_seq, 1, 0, st_len)) return GDN_ERR_SHAPE;
+  if (!rows_disjoint(n_seq, y_seq, n_tok, y_tok, (int64_t)H * S)) return GDN_ERR_SHAPE;
+  const int n_snap = n_tok - 1;
+  if (snap && n_snap > 0 && !rows_disjoint(n_seq, sn_seq, n_snap, st_len, st_len))
+    return GDN_ERR_SHAPE;
+  // vector accesses: float4 rows (float2 at S = 32)
+  const uintptr_t va = S >= 64 ? 16 : 8;
+  const int64_t ve = S >= 64 ? 4 : 2;
+  if (!aligned(state, va) || !aligned(q, va) || !aligned(k, va) || (snap && !aligned(snap, va)))
+    return GDN_ERR_SHAPE;
+  if (st_seq % ve || qk_tok % ve || qk_seq % ve || sn_seq % ve) return GDN_ERR_SHAPE;
+  const Span sst = span_of(state, n_seq, st_seq, 1, 0, st_len);
+  const Span sq = span_of(q, n_seq, qk_seq, n_tok, qk_tok, (int64_t)Hk * S);
+  const Span sk = span_of(k, n_seq, qk_seq, n_tok, qk_tok, (int64_t)Hk * S);
+  const Span sv = span_of(v, n_seq, v_seq, n_tok, v_tok, (int64_t)H * S);
+  const Span sg = span_of(g, 1, 0, 1, 0, (int64_t)n_seq * n_tok * H);
+  const Span sb = span_of(beta, 1, 0, 1, 0, (int64_t)n_seq * n_tok * H);
+  const Span sy = span_of(y, n_seq, y_seq, n_tok, y_tok, (int64_t)H * S);
+  const Span ssn = snap ? span_of(snap, n_seq, sn_seq, n_snap, st_len, st_len) : Span{};
+  for (Span in : {sq, sk, sv, sg, sb})
+    if (overlap(sst, in) || overlap(sy, in) || overlap(ssn, in)) return GDN_ERR_ALIAS;
+  if (overlap(sy, sst) || overlap(ssn, sst) || overlap(ssn, sy)) return GDN_ERR_ALIAS;
+  return GDN_OK;
+}
+
+int check_chunked(const float *state, int64_t st_seq, const float *q, const float *k,
+                  int64_t qk_tok, int64_t qk_seq, const float *v, int64_t v_tok, int64_t v_seq,
+                  const float *g, const float *beta, const float *y, int64_t y_tok,
+                  int64_t y_seq, int n_seq, int n_tok, int H, int Hk, int S, int chunk,
+                  const void *ws, size_t ws_bytes, size_t ws_needed) {
+  const int rc = check_recur(state, st_seq, q, k, qk_tok, qk_seq, v, v_tok, v_seq, g, beta, y,
+                             y_tok, y_seq, nullptr, 0, n_seq, n_tok, H, Hk, S);
+  if (rc != GDN_OK) return rc;
+  if (chunk != 64 || S != 128) return GDN_ERR_UNSUPPORTED;
+  if (v_tok % 4 || v_seq % 4 || y_tok % 4 || y_seq % 4 || !aligned(v, 16) || !aligned(y, 16))
+    return GDN_ERR_SHAPE;
+  if (!ws || ws_bytes < ws_needed || !aligned(ws, 256)) return GDN_ERR_WORKSPACE;
+  const Span sw{(uintptr_t)ws, (uintptr_t)ws + ws_bytes};
+  const int64_t st_len = (int64_t)S * S * H;
+  for (Span t : {span_of(state, n_seq, st_seq, 1, 0, st_len),
+                 span_of(q, n_seq, qk_seq, n_tok, qk_tok, (int64_t)Hk * S),
+                 span_of(k, n_seq, qk_seq, n_tok, qk_tok, (int64_t)Hk * S),
+                 span_of(v, n_seq, v_seq, n_tok, v_tok, (int64_t)H * S),
+                 span_of(y, n_seq, y_seq, n_tok, y_tok, (int64_t)H * S),
+                 span_of(g, 1, 0, 1, 0, (int64_t)n_seq * n_tok * H),
+                 span_of(beta, 1, 0, 1, 0, (int64_t)n_seq * n_tok * H)})
+    if (overlap(sw, t)) return GDN_ERR_ALIAS;
+  return GDN_OK;
+}
+
+int check_norm(const float *y, int64_t y_row, const float *w, const float *z, int64_t z_row,
+               const float *out, int64_t o_row, int rows, int H, int hd) {
+  if (rows < 0 || H < 1) return GDN_ERR_SHAPE;
+  if (hd < 32 || hd % 32 != 0) return GDN_ERR_SHAPE;
+  if (!supported_head_dim(hd)) return GDN_ERR_UNSUPPORTED;
+  if (y_row < 0 || z_row < 0 || o_row < 0) return GDN_ERR_SHAPE;
+  if (rows == 0) return GDN_OK;
+  if (!y || !w || !z || !out) return GDN_ERR_NULL;
+  const int64_t len = (int64_t)H * hd;
+  if (!rows_disjoint(1, 0, rows, o_row, len)) return GDN_ERR_SHAPE;
+  const Span sy = span_of(y, 1, 0, rows, y_row, len);
+  const Span sz = span_of(z, 1, 0, rows, z_row, len);
+  const Span sw = span_of(w, 1, 0, 1, 0, hd);
+  const Span so = span_of(out, 1, 0, rows, o_row, len);
+  if (overlap(so, sz) || overlap(so, sw)) return GDN_ERR_ALIAS;
+  if (overlap(so, sy) && !(out == y && o_row == y_row)) return GDN_ERR_ALIAS;
+  return GDN_OK;
+}
+
+}  // namespace gdn

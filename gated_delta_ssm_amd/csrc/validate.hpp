@@ -1,0 +1,30 @@
+// validate.hpp -- host-only argument checks (no HIP runtime calls).
+#pragma once
+#include <cstddef>
+#include <cstdint>
+
+namespace gdn {
+
+int check_decay_gate(const float *alpha, const float *dt, const float *a, const float *g,
+                     int rows, int n_heads);
+
+int check_conv(const float *x, int64_t x_tok, int64_t x_seq, const float *w, const float *hist,
+               int64_t h_seq, const float *out, int64_t o_tok, int64_t o_seq, const float *snap,
+               int64_t sn_tok, int64_t sn_seq, int n_seq, int n_tok, int C, int D, int qk,
+               int head_dim);
+
+int check_recur(const float *state, int64_t st_seq, const float *q, const float *k,
+                int64_t qk_tok, int64_t qk_seq, const float *v, int64_t v_tok, int64_t v_seq,
+                const float *g, const float *beta, const float *y, int64_t y_tok, int64_t y_seq,
+                const float *snap, int64_t sn_seq, int n_seq, int n_tok, int H, int Hk, int S);
+
+int check_chunked(const float *state, int64_t st_seq, const float *q, const float *k,
+                  int64_t qk_tok, int64_t qk_seq, const float *v, int64_t v_tok, int64_t v_seq,
+                  const float *g, const float *beta, const float *y, int64_t y_tok,
+                  int64_t y_seq, int n_seq, int n_tok, int H, int Hk, int S, int chunk,
+                  const void *ws, size_t ws_bytes, size_t ws_needed);
+
+int check_norm(const float *y, int64_t y_row, const float *w, const float *z, int64_t z_row,
+               const float *out, int64_t o_row, int rows, int H, int hd);
+
+}  // namespace gdn

@@ -1,0 +1,204 @@
+/*
+ * gdn.h -- C ABI of libgdn.so, the MI355X (gfx950) gated-delta SSM layer core.
+ *
+ * Sources (page title, then the part of the page):
+ *   [FM]  fm_kernel_ssm.h, Foundry Metal kernels (git.teamide.dev)
+ *   [AT]  ssm_mamba.rs, spark_model layers/ops (atlas-docs)
+ *   [SCR] scr_state.hpp, regolith Metal engine scripts (tangled.org)
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor is fp32 DEVICE memory allocated, owned and freed by the
+ *     caller, who keeps it alive until the work on `stream` has finished.
+ *   - Strides are in ELEMENTS (floats), not bytes.  Within a row, heads are
+ *     packed densely (head stride = head width).
+ *   - Every call is asynchronous on `stream` (0 = the null stream), allocates
+ *     nothing, never synchronises, and keeps no state between calls.  Calls on
+ *     different streams with disjoint buffers may run concurrently.
+ *   - Arguments are validated on the host before anything is launched; a
+ *     failed check returns a negative gdn_status and launches nothing.  A
+ *     launch failure returns GDN_ERR_LAUNCH.  Faults inside a kernel surface at
+ *     the caller's next synchronisation on that stream.
+ *   - Grouped heads: value head h reads query/key head h / (n_v_heads /
+ *     n_qk_heads); n_v_heads must be a multiple of n_qk_heads.  Passing
+ *     n_qk_heads == n_v_heads is [FM]'s "already repeated" contract.
+ *   - Shape limits ([FM] "Shape limits" block): the state size S is one of
+ *     32, 64, 128, 256; the conv kernel width is 2..8; a norm head width
+ *     (head_dim) is a multiple of 32, and this library has kernels for
+ *     32, 64, 128 and 256 (other multiples return GDN_ERR_UNSUPPORTED).
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_ERR_NULL = -1,        /* a required pointer is NULL */
+  GDN_ERR_SHAPE = -2,       /* a size or stride is out of range or inconsistent */
+  GDN_ERR_UNSUPPORTED = -3, /* a valid shape this library has no kernel for */
+  GDN_ERR_ALIAS = -4,       /* outputs overlap inputs where that is not allowed */
+  GDN_ERR_WORKSPACE = -5,   /* the workspace is missing, too small or misaligned */
+  GDN_ERR_LAUNCH = -6       /* the HIP runtime refused the launch */
+} gdn_status;
+
+/* Static, NUL-terminated description of a status code. */
+const char *gdn_strerror(int status);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int gdn_version(void);
+
+/*
+ * Decay gate.  [FM] "Decay gate" section, fm_ssm_decay_gate_at;
+ * [SCR] "GDN staleness", log_gate.
+ *
+ *   g[r][h] = a[h] * softplus(alpha[r][h] + dt[h]),
+ *   softplus(v) = v if v > 20, else log1p(exp(v)),
+ *
+ * with a = -exp(A_log) pre-baked by the caller, so g < 0; g is returned
+ * PRE-exp (the recurrence exponentiates it).
+ *   alpha [rows][n_heads], row stride n_heads       (in)
+ *   dt, a [n_heads]                                (in)
+ *   g     [rows][n_heads]                          (out, may alias alpha)
+ * rows >= 0 (0 launches nothing), n_heads >= 1.
+ */
+int gdn_decay_gate(const float *alpha, const float *dt, const float *a, float *g, int rows,
+                   int n_heads, hipStream_t stream);
+
+/*
+ * Depthwise causal conv1d + SiLU + per-head L2 norm on the Q/K channels, over
+ * n_tok consecutive positions of n_seq independent sequences.
+ * [FM] "Causal depthwise conv1d + SiLU" section (fm_ssm_conv1d_silu_at,
+ * fm_ssm_conv1d_silu_seq_at); [AT] conv1d_update_l2norm,
+ * conv1d_update_l2norm_strided, gdn_verify_fused_conv_k2 and
+ * conv1d_update_prefill; [SCR] "GDN staleness" for the L2 form.
+ *
+ * Per sequence s, position t, channel c:
+ *   window = [hist[c][0] .. hist[c][d_conv-2], x[t][c]]  (oldest first)
+ *   o      = silu(sum_j w[c][j] * window[j])
+ *   hist[c] drops its oldest tap and appends the RAW x[t][c]
+ *   for c < qk_channels: o /= sqrt(sum over c's head_dim block of o^2 + l2_eps)
+ *
+ *   x     element x[s][t][c] at x + s*x_seq_stride + t*x_tok_stride + c  (in)
+ *   w     [conv_dim][d_conv], row-major; tap d_conv-1 meets the newest input (in)
+ *   conv_state [s][conv_dim][d_conv-1] at conv_state + s*state_seq_stride,
+ *         oldest tap first, updated in place to the window after the last position
+ *   out   element at out + s*out_seq_stride + t*out_tok_stride + c        (out)
+ *   snap  NULL, or the rollback snapshots: the history after position t, for
+ *         t < n_tok-1, at snap + s*snap_seq_stride + t*snap_tok_stride
+ *         ([conv_dim][d_conv-1] each); the committed history stays in conv_state.
+ *
+ * Requirements: n_seq >= 1, n_tok >= 1, conv_dim >= 1, 2 <= d_conv <= 8,
+ * 0 <= qk_channels <= conv_dim, qk_channels % head_dim == 0, head_dim in
+ * {32, 64, 128, 256} (ignored when qk_channels == 0), x_tok_stride >= conv_dim
+ * when n_tok > 1 and out_tok_stride >= conv_dim when n_tok > 1, sequence strides
+ * large enough that sequences do not overlap.  out must not overlap x or
+ * conv_state; snap must not overlap conv_state.
+ * The result does not depend on which internal kernel runs: the multi-position
+ * path and n single-position calls agree bit for bit.
+ */
+int gdn_conv1d_silu_l2norm(const float *x, int64_t x_tok_stride, int64_t x_seq_stride,
+                           const float *w, float *conv_state, int64_t state_seq_stride,
+                           float *out, int64_t out_tok_stride, int64_t out_seq_stride,
+                           float *snap, int64_t snap_tok_stride, int64_t snap_seq_stride,
+                           int n_seq, int n_tok, int conv_dim, int d_conv, int qk_channels,
+                           int head_dim, float l2_eps, hipStream_t stream);
+
+/*
+ * Gated delta-rule recurrence, token by token (decode and K-position verify).
+ * [FM] "Delta-rule recurrence" section (fm_ssm_recurrence_at,
+ * fm_ssm_recurrence_seq_at); [AT] gdn_verify_fused_conv_k2 for the rollback
+ * snapshot semantics.
+ *
+ * For each sequence s, value head h and position t, on the S x S state of
+ * (s, h), in this order:
+ *   S <- exp(g) S;  p = S^T k;  delta = beta (v - p);  S <- S + k delta^T;
+ *   y = scale S^T q        (the readout sees the updated state)
+ *
+ *   state [s][h][j][i] = S[i][j] (TRANSPOSED: row j, value index, is contiguous
+ *         over the key index i), sequence stride state_seq_stride >= H*S*S,
+ *         updated in place                                              (in/out)
+ *   q, k  element [s][t][hk][i] at q + s*qk_seq_stride + t*qk_tok_stride + hk*S + i
+ *   v     element [s][t][h][j]  at v + s*v_seq_stride + t*v_tok_stride + h*S + j
+ *   g, beta  dense [n_seq][n_tok][n_v_heads]; g pre-exp, beta already sigmoid'd
+ *   y     element [s][t][h][j]  at y + s*y_seq_stride + t*y_tok_stride + h*S + j (out)
+ *   snap  NULL, or the state after position t for t < n_tok-1, in the state's
+ *         layout, at snap + s*snap_seq_stride + t*(n_v_heads*S*S)         (out)
+ *
+ * Running n_tok positions in one call and n_tok calls of one position give
+ * bit-identical y and state.  y must not overlap any input; snap must not
+ * overlap state.  S in {32, 64, 128, 256}.
+ */
+int gdn_recurrence_decode(float *state, int64_t state_seq_stride, const float *q, const float *k,
+                          int64_t qk_tok_stride, int64_t qk_seq_stride, const float *v,
+                          int64_t v_tok_stride, int64_t v_seq_stride, const float *g,
+                          const float *beta, float *y, int64_t y_tok_stride, int64_t y_seq_stride,
+                          float *snap, int64_t snap_seq_stride, int n_seq, int n_tok,
+                          int n_v_heads, int n_qk_heads, int S, float scale, hipStream_t stream);
+
+/*
+ * Workspace bytes gdn_recurrence_chunked needs for these sizes (0 if the
+ * sizes are invalid).  [AT] "Mamba-2 SSD chunked prefill scan" comment for
+ * the chunked idea; the WY/UT algebra is given with gdn_recurrence_chunked.
+ */
+size_t gdn_recurrence_chunked_workspace_bytes(int n_seq, int n_tok, int n_v_heads,
+                                              int n_qk_heads, int S, int chunk);
+
+/*
+ * The same recurrence over a long prompt in chunked (WY / UT-transform) form:
+ * the T sequential links become ceil(T/chunk) ([AT] "Mamba-2 SSD chunked
+ * prefill scan" comment); [FM] fm_ssm_recurrence_seq_at is the sequential scan
+ * it is validated against.  Per chunk of n <= chunk tokens from state S0, with
+ * G_t the inclusive within-chunk cumulative sum of g:
+ *   A  = strictly_lower(beta_t e^{G_t-G_s} k_t.k_s),  T = (I + A)^{-1}
+ *   W  = T diag(beta e^G) K,   U = T diag(beta) V - W S0
+ *   y  = scale [diag(e^G) Q S0 + (L o Q K^T) U],  L[t][s] = e^{G_t-G_s} (s <= t)
+ *   S  = e^{G_n} S0 + (diag(e^{G_n-G}) K)^T U
+ * Same tensor arguments and layouts as gdn_recurrence_decode (no snapshots).
+ * The intra-chunk contractions use bf16 MFMA with fp32 accumulation; the
+ * state is carried in fp32.  Agreement with the sequential scan is a
+ * tolerance, not bit identity.
+ *
+ * chunk must be 64.  workspace: device memory of at least
+ * gdn_recurrence_chunked_workspace_bytes(...) bytes, 256-byte aligned, owned by
+ * the caller and not used by anything else until the call's work on `stream`
+ * has finished.  S must be 128.
+ */
+int gdn_recurrence_chunked(float *state, int64_t state_seq_stride, const float *q, const float *k,
+                           int64_t qk_tok_stride, int64_t qk_seq_stride, const float *v,
+                           int64_t v_tok_stride, int64_t v_seq_stride, const float *g,
+                           const float *beta, float *y, int64_t y_tok_stride,
+                           int64_t y_seq_stride, int n_seq, int n_tok, int n_v_heads,
+                           int n_qk_heads, int S, float scale, int chunk, void *workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Gated RMSNorm per (row, head).  [FM] "Gated RMSNorm" section
+ * (fm_ssm_gated_norm_at); [AT] gdn_verify_fused_norm_k2 for reading z out of
+ * a wider per-token row (pass z already offset to its column).
+ *
+ *   out = ((y * (1 / sqrt(mean(y^2) + eps))) * w) * silu(z)
+ *
+ *   y    [rows][n_heads][head_dim] with row stride y_row_stride      (in)
+ *   w    [head_dim], shared by every head                             (in)
+ *   z    [rows][n_heads][head_dim] with row stride z_row_stride      (in)
+ *   out  [rows][n_heads][head_dim] with row stride out_row_stride    (out;
+ *        may alias y exactly, i.e. out == y with equal row strides)
+ * head_dim in {32, 64, 128, 256}; rows >= 0; n_heads >= 1; row strides >=
+ * n_heads*head_dim when rows > 1.
+ */
+int gdn_gated_rmsnorm(const float *y, int64_t y_row_stride, const float *w, const float *z,
+                      int64_t z_row_stride, float *out, int64_t out_row_stride, int rows,
+                      int n_heads, int head_dim, float eps, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,142 @@
+"""CPU-side checks of the C ABI: the library loads, exports every entry point
+include/gdn.h declares, and rejects invalid arguments on the host, before any
+HIP call (so these run without a GPU; nothing here computes)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_ssm_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_ALIAS, ERR_WS = 0, -1, -2, -3, -4, -5
+FAKE = 0x10000            # never dereferenced: validation rejects first
+L = gdn._lib
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declarations_all_exported():
+    names = declared()
+    assert "gdn_recurrence_decode" in names and len(names) >= 8
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in gdn.h but not exported"
+    assert set(names) == set(gdn.EXPORTS)
+
+
+def test_strerror_and_version():
+    for s in (0, -1, -2, -3, -4, -5, -6):
+        assert len(L.gdn_strerror(s)) >= 2
+    assert L.gdn_version() >= 100
+
+
+def F(p):
+    return ctypes.c_void_p(p)
+
+
+def gate(alpha=FAKE, dt=FAKE + 4096, a=FAKE + 8192, g=FAKE + 16384, rows=4, H=4):
+    return L.gdn_decay_gate(alpha, dt, a, g, rows, H, None)
+
+
+def test_gate_validation():
+    assert gate(rows=-1) == ERR_SHAPE
+    assert gate(H=0) == ERR_SHAPE
+    assert gate(alpha=None) == ERR_NULL
+    assert gate(g=FAKE + 4) == ERR_ALIAS           # shifted overlap of alpha
+    assert gate(rows=0, alpha=None) == OK          # empty: nothing launched
+
+
+def conv(**kw):
+    a = dict(x=FAKE, xt=64, xs=64 * 8, w=FAKE + (1 << 20), st=FAKE + (2 << 20), ss=64 * 3,
+             out=FAKE + (3 << 20), ot=64, os=64 * 8, snap=None, snt=0, sns=0,
+             n_seq=2, n_tok=8, C=64, D=4, qk=32, hd=32, eps=1e-6)
+    a.update(kw)
+    return L.gdn_conv1d_silu_l2norm(a["x"], a["xt"], a["xs"], a["w"], a["st"], a["ss"], a["out"],
+                                    a["ot"], a["os"], a["snap"], a["snt"], a["sns"], a["n_seq"],
+                                    a["n_tok"], a["C"], a["D"], a["qk"], a["hd"], a["eps"], None)
+
+
+def test_conv_validation():
+    assert conv(D=1) == ERR_SHAPE and conv(D=9) == ERR_SHAPE          # 2..8 taps
+    assert conv(n_tok=0) == ERR_SHAPE
+    assert conv(qk=48) == ERR_SHAPE                                    # not a multiple of head_dim
+    assert conv(qk=128) == ERR_SHAPE                                   # beyond conv_dim
+    assert conv(hd=96, qk=0) != ERR_UNSUP                              # head_dim unused without Q/K
+    assert conv(hd=96, qk=96, C=192) == ERR_UNSUP                      # multiple of 32, no kernel
+    assert conv(x=None) == ERR_NULL
+    assert conv(ot=32) == ERR_SHAPE                                    # output rows overlap
+    assert conv(out=FAKE + 128) == ERR_ALIAS                           # out overlaps x
+    assert conv(snap=FAKE + (2 << 20) + 16, snt=192, sns=192 * 8) == ERR_ALIAS
+
+
+def recur(**kw):
+    S, H, T, n = kw.pop("S", 32), kw.pop("H", 4), kw.pop("T", 2), kw.pop("n", 2)
+    Hk = kw.pop("Hk", H)
+    MB = 1 << 20
+    a = dict(state=FAKE, sts=H * S * S, q=FAKE + 4 * MB, k=FAKE + 8 * MB, qkt=Hk * S,
+             qks=T * Hk * S, v=FAKE + 12 * MB, vt=H * S, vs=T * H * S, g=FAKE + 16 * MB,
+             beta=FAKE + 20 * MB, y=FAKE + 24 * MB, yt=H * S, ys=T * H * S, snap=None, sns=0)
+    a.update(kw)
+    return L.gdn_recurrence_decode(a["state"], a["sts"], a["q"], a["k"], a["qkt"], a["qks"], a["v"],
+                                   a["vt"], a["vs"], a["g"], a["beta"], a["y"], a["yt"], a["ys"],
+                                   a["snap"], a["sns"], n, T, H, Hk, S, 0.125, None)
+
+
+def test_recurrence_validation():
+    assert recur(S=48) == ERR_SHAPE                                    # not a multiple of 32
+    assert recur(S=288) == ERR_SHAPE                                   # above 256
+    assert recur(S=96) == ERR_UNSUP                                    # valid limit, no kernel
+    assert recur(Hk=3) == ERR_SHAPE                                    # H % Hk
+    assert recur(T=0) == ERR_SHAPE
+    assert recur(q=None) == ERR_NULL
+    assert recur(state=FAKE + 4) == ERR_SHAPE                          # misaligned float4 rows
+    assert recur(sts=100) == ERR_SHAPE                                 # sequences overlap
+    assert recur(y=FAKE + 4 * (1 << 20) + 64) == ERR_ALIAS             # y overlaps q
+    assert recur(snap=FAKE + 256, sns=4 * 32 * 32) == ERR_ALIAS        # snap overlaps state
+
+
+def test_chunked_validation_and_workspace_query():
+    need = L.gdn_recurrence_chunked_workspace_bytes(1, 4096, 32, 16, 128, 64)
+    assert need > 0
+    assert L.gdn_recurrence_chunked_workspace_bytes(1, 4096, 32, 16, 96, 64) == 0
+    assert L.gdn_recurrence_chunked_workspace_bytes(1, 4096, 32, 16, 128, 32) == 0
+    MB = 1 << 20
+    S, H, Hk, T = 128, 4, 2, 100
+    base = [FAKE, H * S * S, FAKE + 4 * MB, FAKE + 8 * MB, Hk * S, T * Hk * S, FAKE + 12 * MB,
+            H * S, T * H * S, FAKE + 16 * MB, FAKE + 20 * MB, FAKE + 24 * MB, H * S, T * H * S,
+            1, T, H, Hk, S, 0.1, 64]
+    ws_need = L.gdn_recurrence_chunked_workspace_bytes(1, T, H, Hk, S, 64)
+    call = lambda args, ws, nb: L.gdn_recurrence_chunked(*args, ws, nb, None)
+    assert call(base, None, ws_need) == ERR_WS
+    assert call(base, FAKE + 64 * MB, ws_need - 1) == ERR_WS
+    assert call(base, FAKE + 64 * MB + 16, ws_need) == ERR_WS          # not 256-byte aligned
+    assert call(base, FAKE + 12 * MB, ws_need) == ERR_ALIAS            # workspace over v
+    bad = list(base); bad[-1] = 32
+    assert call(bad, FAKE + 64 * MB, ws_need) == ERR_UNSUP
+
+
+def test_norm_validation():
+    MB = 1 << 20
+    call = lambda y, ys, w, z, zs, o, os_, rows, H, hd: L.gdn_gated_rmsnorm(
+        y, ys, w, z, zs, o, os_, rows, H, hd, 1e-6, None)
+    assert call(FAKE, 256, FAKE + MB, FAKE + 2 * MB, 256, FAKE + 3 * MB, 256, 4, 2, 48) == ERR_SHAPE
+    assert call(FAKE, 384, FAKE + MB, FAKE + 2 * MB, 384, FAKE + 3 * MB, 384, 4, 2, 192) == ERR_UNSUP
+    assert call(FAKE, 256, None, FAKE + 2 * MB, 256, FAKE + 3 * MB, 256, 4, 2, 128) == ERR_NULL
+    assert call(FAKE, 256, FAKE + MB, FAKE + 2 * MB, 256, FAKE + 2 * MB, 256, 4, 2, 128) == ERR_ALIAS
+    assert call(FAKE, 256, FAKE + MB, FAKE + 2 * MB, 256, FAKE + 64, 256, 4, 2, 128) == ERR_ALIAS
+    assert call(FAKE, 256, FAKE + MB, FAKE + 2 * MB, 256, FAKE + 3 * MB, 128, 4, 2, 128) == ERR_SHAPE
+
+
+def test_page_shape_limits_are_the_abi_limits():
+    import json
+    gold = json.load(open(os.path.join(ROOT, "tests", "golden", "page_constants.json")))
+    assert recur(S=gold["max_state_size"]["value"] + 32) == ERR_SHAPE
+    assert conv(D=gold["max_conv_kernel"]["value"] + 1) == ERR_SHAPE
+    assert conv(D=gold["max_conv_kernel"]["value"], qk=0, x=None) == ERR_NULL   # 8 taps accepted

@@ -1,0 +1,342 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Error metric (the pages do not define "max rel err"): normwise-inf relative
+error per output tensor, max|gpu - ref| / max|ref|, the final state and
+snapshots counted as tensors of their own.  Tolerances: 1e-5 for the gate,
+conv and norm; 1e-4 for the token-by-token recurrence; 2e-3 for the chunked
+recurrence against the sequential scan.  Integer-like results (the conv
+history, which only ever holds raw inputs) must match exactly, and the
+multi-position paths must match their one-position equivalents bit for bit.
+
+Every test runs at the workload's full size and launch configuration, on
+inputs from gdn_inputs.make_inputs; the oracle sees the identical fp32 arrays.
+"""
+import functools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gdn_inputs import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+ALL = list(WORKLOADS)
+
+
+def gdn():
+    import gated_delta_ssm_amd
+    return gated_delta_ssm_amd
+
+
+def rel(x, r):
+    x = x.detach().cpu().double().numpy() if isinstance(x, torch.Tensor) else np.asarray(x)
+    r = np.asarray(r, np.float64)
+    assert x.shape == r.shape, (x.shape, r.shape)
+    assert np.all(np.isfinite(x)), "non-finite output"
+    return float(np.max(np.abs(x - r)) / max(np.max(np.abs(r)), 1e-30))
+
+
+def bits_equal(a: torch.Tensor, b: torch.Tensor) -> bool:
+    return torch.equal(a.contiguous().view(torch.int32), b.contiguous().view(torch.int32))
+
+
+@functools.lru_cache(maxsize=2)
+def inputs(name):
+    return make_inputs(name)
+
+
+def on_dev(t):
+    return t.to(DEV)
+
+
+def oracle_g(inp):
+    """g for the recurrence tests: the oracle's gate, rounded to fp32."""
+    wl = inp["wl"]
+    g = oracle.decay_gate(inp["alpha"], inp["dt"], inp["a"]).astype(np.float32)
+    return torch.from_numpy(g).reshape(wl.n_seq, wl.n_tok, wl.H)
+
+
+def log_case(name, **kw):
+    print(f"[case] {name} " + " ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
+
+
+# ------------------------------------------------------------------------------------- gate
+
+@pytest.mark.parametrize("name", ALL)
+def test_gate(name):
+    inp = inputs(name)
+    log_case("gate", wl=name)
+    g = gdn().gdn_decay_gate(on_dev(inp["alpha"]), on_dev(inp["dt"]), on_dev(inp["a"]))
+    ref = oracle.decay_gate(inp["alpha"], inp["dt"], inp["a"])
+    assert rel(g, ref) < 1e-5
+    assert bool((g < 0).all())
+
+
+def test_gate_guard_edges():
+    log_case("gate_edges")
+    v = torch.tensor([[-100.0, -20.0, 0.0, 19.999, 20.0, 20.001, 21.0, 1e4, 3e38]])
+    H = v.shape[1]
+    dt = torch.zeros(H)
+    a = -torch.linspace(1.0, 16.0, H)
+    g = gdn().gdn_decay_gate(on_dev(v), on_dev(dt), on_dev(a)).cpu()
+    ref = oracle.decay_gate(v, dt, a)
+    assert torch.isfinite(g[0, :-1]).all()
+    # fp32 denormal results (v = -100) carry few significant bits: absolute slack there
+    np.testing.assert_allclose(g[0, :-1].double().numpy(), ref[0, :-1], rtol=2e-6, atol=1e-37)
+    assert g[0, 5] == (a[5] * v[0, 5])            # above the guard: a * v exactly
+
+
+# ------------------------------------------------------------------------------------- conv
+
+def run_conv(inp, x_rows=None, snap=False, n_tok=None, hist=None):
+    wl = inp["wl"]
+    C = wl.conv_dim
+    x_full = on_dev(inp["x"] if x_rows is None else x_rows)
+    T = x_full.shape[1] if n_tok is None else n_tok
+    x = x_full[:, :T, :C]
+    out_full = torch.full((wl.n_seq, T, wl.out_stride), float("nan"), device=DEV)
+    out = out_full[..., :C]
+    st = on_dev(inp["conv_hist"] if hist is None else hist).clone()
+    sn = torch.full((wl.n_seq, T - 1, C, wl.d_conv - 1), float("nan"), device=DEV) if snap else None
+    gdn().gdn_conv1d_silu_l2norm(x, on_dev(inp["conv_w"]), st, out, qk_channels=wl.qk_channels,
+                                 head_dim=wl.head_dim, l2_eps=wl.l2_eps, snap=sn)
+    return out, st, sn, out_full
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_conv(name):
+    inp = inputs(name)
+    wl = inp["wl"]
+    log_case("conv", wl=name, n_seq=wl.n_seq, n_tok=wl.n_tok, C=wl.conv_dim)
+    x = inp["x"].clone()
+    x[..., wl.conv_dim:] = float("nan")       # any read outside the conv channels poisons out
+    out, st, sn, out_full = run_conv(inp, x_rows=x, snap=wl.n_tok > 1 and wl.n_tok <= 8)
+    o_ref, h_ref, s_ref = oracle.conv1d_silu_l2norm(
+        inp["x"][..., :wl.conv_dim], inp["conv_w"], inp["conv_hist"], wl.qk_channels,
+        wl.head_dim, wl.l2_eps, want_snap=sn is not None)
+    assert rel(out, o_ref) < 1e-5
+    assert np.array_equal(st.cpu().double().numpy(), h_ref)
+    if sn is not None:
+        assert np.array_equal(sn.cpu().double().numpy(), s_ref)
+    if wl.out_stride > wl.conv_dim:            # the gap between output rows is untouched
+        assert torch.isnan(out_full[..., wl.conv_dim:]).all()
+
+
+@pytest.mark.parametrize("head_dim,qk,d_conv,T", [(64, 128, 2, 37), (256, 512, 8, 70),
+                                                  (32, 96, 3, 5), (128, 0, 4, 33)])
+def test_conv_other_shapes(head_dim, qk, d_conv, T):
+    C = 3 * max(qk, 64) + 32                      # a ragged last channel block
+    inp = make_inputs("tiny", seed=11, conv_dim=C, qk_channels=qk, head_dim=head_dim,
+                      d_conv=d_conv, n_tok=T, x_stride=C, out_stride=C, hist_std=1.0, n_seq=2)
+    wl = inp["wl"]
+    log_case("conv_shapes", hd=head_dim, qk=qk, d=d_conv, T=T, C=C)
+    out, st, _, _ = run_conv(inp)
+    o_ref, h_ref, _ = oracle.conv1d_silu_l2norm(inp["x"], inp["conv_w"], inp["conv_hist"],
+                                                qk, head_dim, wl.l2_eps)
+    assert rel(out, o_ref) < 1e-5
+    assert np.array_equal(st.cpu().double().numpy(), h_ref)
+
+
+@pytest.mark.parametrize("T", [100, 3])
+def test_conv_token_parallel_bit_identical_to_steps(T):
+    # the long-prompt kernel vs one-position calls, on the decode workload's channels
+    inp = make_inputs("decode", seed=21, n_tok=T)
+    wl = inp["wl"]
+    log_case("conv_tp_vs_steps", T=T)
+    out_all, st_all, _, _ = run_conv(inp)
+    st = on_dev(inp["conv_hist"]).clone()
+    outs = []
+    for t in range(T):
+        o = torch.empty(1, 1, wl.conv_dim, device=DEV)
+        gdn().gdn_conv1d_silu_l2norm(on_dev(inp["x"])[:, t:t + 1, :wl.conv_dim],
+                                     on_dev(inp["conv_w"]), st, o, qk_channels=wl.qk_channels,
+                                     head_dim=wl.head_dim, l2_eps=wl.l2_eps)
+        outs.append(o)
+    assert bits_equal(out_all, torch.cat(outs, dim=1))
+    assert bits_equal(st_all, st)
+
+
+def test_conv_verify2_fused_equals_two_steps_and_rollback():
+    inp = inputs("verify2")
+    wl = inp["wl"]
+    log_case("conv_verify2_bits")
+    out2, st2, sn, _ = run_conv(inp, snap=True)
+    st = on_dev(inp["conv_hist"]).clone()
+    outs = []
+    for t in range(2):
+        o = torch.empty(wl.n_seq, 1, wl.conv_dim, device=DEV)
+        gdn().gdn_conv1d_silu_l2norm(on_dev(inp["x"])[:, t:t + 1, :wl.conv_dim],
+                                     on_dev(inp["conv_w"]), st, o, qk_channels=wl.qk_channels,
+                                     head_dim=wl.head_dim, l2_eps=wl.l2_eps)
+        outs.append(o)
+        if t == 0:
+            after0 = st.clone()
+    assert bits_equal(out2, torch.cat(outs, 1)) and bits_equal(st2, st)
+    assert bits_equal(sn[:, 0], after0)           # the rollback snapshot is position 0's window
+
+
+# ------------------------------------------------------------------------------------- recurrence
+
+def run_decode(inp, g3, state=None, snap=False, t0=0, t1=None):
+    wl = inp["wl"]
+    t1 = wl.n_tok if t1 is None else t1
+    st = on_dev(inp["state"] if state is None else state).clone()
+    sl = lambda a: on_dev(a[:, t0:t1]).contiguous()
+    v = sl(inp["v"])
+    y = torch.empty_like(v)
+    sn = torch.full((wl.n_seq, t1 - t0 - 1, wl.H, wl.S, wl.S), float("nan"), device=DEV) \
+        if snap else None
+    gdn().gdn_recurrence_decode(st, sl(inp["q"]), sl(inp["k"]), v, sl(g3), sl(inp["beta"]), y,
+                                scale=wl.scale, snap=sn)
+    return y, st, sn
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "decode64", "verify2"])
+def test_recurrence_decode(name):
+    inp = inputs(name)
+    wl = inp["wl"]
+    log_case("recurrence_decode", wl=name, n_seq=wl.n_seq, n_tok=wl.n_tok, H=wl.H, S=wl.S)
+    g3 = oracle_g(inp)
+    snap = 1 < wl.n_tok <= 8
+    y, st, sn = run_decode(inp, g3, snap=snap)
+    y_ref, s_ref, sn_ref = oracle.recurrence_seq(inp["state"], inp["q"], inp["k"], inp["v"], g3,
+                                                 inp["beta"], wl.scale, want_snap=snap)
+    assert rel(y, y_ref) < 1e-4
+    assert rel(st, s_ref) < 1e-4
+    if snap:
+        assert rel(sn, sn_ref) < 1e-4
+
+
+@pytest.mark.parametrize("S,H,Hk,T,n_seq", [(64, 6, 3, 17, 3), (256, 2, 1, 5, 2), (32, 3, 1, 1, 5)])
+def test_recurrence_decode_other_shapes(S, H, Hk, T, n_seq):
+    inp = make_inputs("tiny", seed=31, S=S, H=H, Hk=Hk, n_tok=T, n_seq=n_seq, state_std=0.1)
+    wl = inp["wl"]
+    log_case("recurrence_shapes", S=S, H=H, Hk=Hk, T=T, n_seq=n_seq)
+    g3 = oracle_g(inp)
+    y, st, _ = run_decode(inp, g3)
+    y_ref, s_ref, _ = oracle.recurrence_seq(inp["state"], inp["q"], inp["k"], inp["v"], g3,
+                                            inp["beta"], wl.scale)
+    assert rel(y, y_ref) < 1e-4 and rel(st, s_ref) < 1e-4
+
+
+def test_recurrence_verify2_bit_identical_to_two_steps():
+    inp = inputs("verify2")
+    log_case("recurrence_verify2_bits")
+    g3 = oracle_g(inp)
+    y2, st2, sn = run_decode(inp, g3, snap=True)
+    ya, sta, _ = run_decode(inp, g3, t0=0, t1=1)
+    yb, stb, _ = run_decode(inp, g3, state=sta, t0=1, t1=2)
+    assert bits_equal(y2, torch.cat([ya, yb], 1))
+    assert bits_equal(st2, stb)
+    assert bits_equal(sn[:, 0], sta)
+
+
+def test_recurrence_strided_inputs_poisoned_gaps():
+    # q/k/v/y rows inside wider buffers whose gaps hold NaN: a stray read or
+    # write outside the declared rows shows up as NaN in y or a changed gap
+    inp = make_inputs("tiny", seed=41, n_seq=3, n_tok=5, H=4, Hk=2, state_std=0.1)
+    wl = inp["wl"]
+    log_case("recurrence_strided")
+    g3 = oracle_g(inp)
+
+    def wide(a, pad):
+        buf = torch.full((*a.shape[:-2], a.shape[-2] * a.shape[-1] + pad), float("nan"))
+        buf[..., :a.shape[-2] * a.shape[-1]] = a.reshape(*a.shape[:-2], -1)
+        return on_dev(buf)[..., :a.shape[-2] * a.shape[-1]].unflatten(-1, a.shape[-2:])
+
+    qk_buf = torch.full((wl.n_seq, wl.n_tok, 2, wl.Hk * wl.S + 8), float("nan"))
+    qk_buf[:, :, 0, :wl.Hk * wl.S] = inp["q"].reshape(wl.n_seq, wl.n_tok, -1)
+    qk_buf[:, :, 1, :wl.Hk * wl.S] = inp["k"].reshape(wl.n_seq, wl.n_tok, -1)
+    qk_dev = on_dev(qk_buf)
+    q = qk_dev[:, :, 0, :wl.Hk * wl.S].unflatten(-1, (wl.Hk, wl.S))
+    k = qk_dev[:, :, 1, :wl.Hk * wl.S].unflatten(-1, (wl.Hk, wl.S))
+    v = wide(inp["v"], 12)
+    y_buf = torch.full((wl.n_seq, wl.n_tok, wl.H * wl.S + 20), float("nan"), device=DEV)
+    y = y_buf[..., :wl.H * wl.S].unflatten(-1, (wl.H, wl.S))
+    st_buf = torch.full((wl.n_seq, wl.H * wl.S * wl.S + 64), float("nan"), device=DEV)
+    st_buf[:, :wl.H * wl.S * wl.S] = on_dev(inp["state"]).reshape(wl.n_seq, -1)
+    st = st_buf[:, :wl.H * wl.S * wl.S].unflatten(-1, (wl.H, wl.S, wl.S))
+    gdn().gdn_recurrence_decode(st, q, k, v, on_dev(g3), on_dev(inp["beta"]), y, scale=wl.scale)
+    y_ref, s_ref, _ = oracle.recurrence_seq(inp["state"], inp["q"], inp["k"], inp["v"], g3,
+                                            inp["beta"], wl.scale)
+    assert rel(y, y_ref) < 1e-4 and rel(st, s_ref) < 1e-4
+    assert torch.isnan(y_buf[..., wl.H * wl.S:]).all()
+    assert torch.isnan(st_buf[:, wl.H * wl.S * wl.S:]).all()
+
+
+def test_recurrence_decode_deterministic():
+    inp = inputs("decode64")
+    log_case("recurrence_determinism")
+    g3 = oracle_g(inp)
+    ya, sa, _ = run_decode(inp, g3)
+    yb, sb, _ = run_decode(inp, g3)
+    assert bits_equal(ya, yb) and bits_equal(sa, sb)
+
+
+# ------------------------------------------------------------------------------------- norm
+
+@pytest.mark.parametrize("name", ALL)
+def test_gated_rmsnorm(name):
+    inp = inputs(name)
+    wl = inp["wl"]
+    log_case("norm", wl=name, rows=wl.rows, H=wl.H, hd=wl.head_dim)
+    y = on_dev(inp["norm_y"])
+    out = torch.empty_like(y)
+    gdn().gdn_gated_rmsnorm(y, on_dev(inp["norm_w"]), on_dev(inp["z"]), out, eps=wl.norm_eps)
+    ref = oracle.gated_rmsnorm(inp["norm_y"], inp["norm_w"], inp["z"], wl.norm_eps)
+    assert rel(out, ref) < 1e-5
+
+
+@pytest.mark.parametrize("hd,H", [(32, 5), (64, 3), (256, 2)])
+def test_gated_rmsnorm_z_offset_and_in_place(hd, H):
+    # z read at an offset inside a wider [Q|K|V|Z]-style row; out written over y
+    rows = 7
+    inp = make_inputs("tiny", seed=51, head_dim=hd, H=H, n_tok=rows)
+    log_case("norm_offset_inplace", hd=hd, H=H)
+    width = 3 * H * hd
+    row = torch.full((rows, width), float("nan"))
+    z_off = H * hd + 16
+    row[:, z_off:z_off + H * hd] = inp["z"].reshape(rows, -1)
+    row_dev = on_dev(row)
+    z = row_dev[:, z_off:z_off + H * hd].unflatten(-1, (H, hd))
+    y = on_dev(inp["norm_y"]).clone()
+    gdn().gdn_gated_rmsnorm(y, on_dev(inp["norm_w"]), z, y, eps=1e-6)
+    ref = oracle.gated_rmsnorm(inp["norm_y"], inp["norm_w"], inp["z"], 1e-6)
+    assert rel(y, ref) < 1e-5
+
+
+# ------------------------------------------------------------------------------------- chained
+
+def test_tiny_chained_layer_core():
+    # gate -> conv (Q|K|V channels) -> recurrence -> gated norm on one GPU,
+    # against the same chain in the oracle with fp64 intermediates
+    inp = inputs("tiny")
+    wl = inp["wl"]
+    log_case("chained_tiny")
+    T, H, S = wl.n_tok, wl.H, wl.S
+    g = gdn().gdn_decay_gate(on_dev(inp["alpha"]), on_dev(inp["dt"]), on_dev(inp["a"]))
+    out, _, _, _ = run_conv(inp)
+    qd = out[0, :, :H * S].reshape(1, T, H, S).contiguous()
+    kd = out[0, :, H * S:2 * H * S].reshape(1, T, H, S).contiguous()
+    vd = out[0, :, 2 * H * S:].reshape(1, T, H, S).contiguous()
+    st = on_dev(inp["state"]).clone()
+    y = torch.empty_like(vd)
+    gdn().gdn_recurrence_decode(st, qd, kd, vd, g.reshape(1, T, H), on_dev(inp["beta"]), y,
+                                scale=wl.scale)
+    n = torch.empty(T, H, S, device=DEV)
+    gdn().gdn_gated_rmsnorm(y.reshape(T, H, S), on_dev(inp["norm_w"]), on_dev(inp["z"]), n,
+                            eps=wl.norm_eps)
+
+    g_r = oracle.decay_gate(inp["alpha"], inp["dt"], inp["a"]).reshape(1, T, H)
+    o_r, _, _ = oracle.conv1d_silu_l2norm(inp["x"], inp["conv_w"], inp["conv_hist"],
+                                          wl.qk_channels, wl.head_dim, wl.l2_eps)
+    q_r = o_r[0, :, :H * S].reshape(1, T, H, S)
+    k_r = o_r[0, :, H * S:2 * H * S].reshape(1, T, H, S)
+    v_r = o_r[0, :, 2 * H * S:].reshape(1, T, H, S)
+    y_r, _, _ = oracle.recurrence_seq(inp["state"], q_r, k_r, v_r, g_r, inp["beta"], wl.scale)
+    n_r = oracle.gated_rmsnorm(y_r.reshape(T, H, S), inp["norm_w"], inp["z"], wl.norm_eps)
+    assert rel(n, n_r) < 1e-4
