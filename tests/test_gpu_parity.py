@@ -340,3 +340,55 @@ def test_tiny_chained_layer_core():
     y_r, _, _ = oracle.recurrence_seq(inp["state"], q_r, k_r, v_r, g_r, inp["beta"], wl.scale)
     n_r = oracle.gated_rmsnorm(y_r.reshape(T, H, S), inp["norm_w"], inp["z"], wl.norm_eps)
     assert rel(n, n_r) < 1e-4
+
+
+# ------------------------------------------------------------------------------------- chunked
+
+def run_chunked(inp, g3, state=None):
+    wl = inp["wl"]
+    st = on_dev(inp["state"] if state is None else state).clone()
+    v = on_dev(inp["v"])
+    y = torch.full_like(v, float("nan"))
+    gdn().gdn_recurrence_chunked(st, on_dev(inp["q"]), on_dev(inp["k"]), v, on_dev(g3),
+                                 on_dev(inp["beta"]), y, scale=wl.scale, chunk=64)
+    return y, st
+
+
+def test_chunked_prefill_full_size():
+    inp = inputs("prefill")
+    wl = inp["wl"]
+    log_case("chunked_prefill", T=wl.n_tok, H=wl.H, Hk=wl.Hk)
+    g3 = oracle_g(inp)
+    y, st = run_chunked(inp, g3)
+    y_ref, s_ref, _ = oracle.recurrence_seq(inp["state"], inp["q"], inp["k"], inp["v"], g3,
+                                            inp["beta"], wl.scale)
+    ey, es = rel(y, y_ref), rel(st, s_ref)
+    print(f"[chunked prefill] rel err y {ey:.3e} state {es:.3e}", flush=True)
+    assert ey < 2e-3 and es < 2e-3
+
+
+@pytest.mark.parametrize("T,H,Hk,n_seq,g_scale", [(100, 4, 2, 2, 1.0), (37, 2, 2, 1, 1.0),
+                                                  (64, 2, 1, 1, 1.0), (65, 2, 2, 3, 0.3),
+                                                  (300, 2, 2, 1, 0.02)])
+def test_chunked_ragged_and_weak_decay(T, H, Hk, n_seq, g_scale):
+    # nonzero initial state; g_scale < 1 weakens the decay so the state carries
+    # across many chunks (the inter-chunk path dominates)
+    inp = make_inputs("prefill", seed=61, n_tok=T, H=H, Hk=Hk, n_seq=n_seq, state_std=0.05)
+    wl = inp["wl"]
+    log_case("chunked_ragged", T=T, H=H, Hk=Hk, n_seq=n_seq, g_scale=g_scale)
+    g3 = (oracle_g(inp) * g_scale).float()
+    y, st = run_chunked(inp, g3)
+    y_ref, s_ref, _ = oracle.recurrence_seq(inp["state"], inp["q"], inp["k"], inp["v"], g3,
+                                            inp["beta"], wl.scale)
+    ey, es = rel(y, y_ref), rel(st, s_ref)
+    print(f"[chunked] T={T} rel err y {ey:.3e} state {es:.3e}", flush=True)
+    assert ey < 2e-3 and es < 2e-3
+
+
+def test_chunked_deterministic():
+    inp = make_inputs("prefill", seed=71, n_tok=512)
+    log_case("chunked_determinism")
+    g3 = oracle_g(inp)
+    ya, sa = run_chunked(inp, g3)
+    yb, sb = run_chunked(inp, g3)
+    assert bits_equal(ya, yb) and bits_equal(sa, sb)
