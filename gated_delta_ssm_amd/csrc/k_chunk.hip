@@ -177,10 +177,14 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
   unsigned char *wc = ws + (((size_t)s * H + h) * n_chunks + c) * WS_CHUNK;
 
   // 1. gate cumsum (wave 0), beta
+  // Loads past the last position read a valid position and are zeroed by a
+  // select, so no load sits behind a branch (a branch would force the compiler
+  // to wait for every outstanding load at the join).
   if (w == 0) {
-    const int64_t gi = ((int64_t)s * n_tok + t0 + lane) * H + h;
-    float x = lane < n ? g[gi] : 0.0f;
-    const float b = lane < n ? beta[gi] : 0.0f;
+    const int64_t gi = ((int64_t)s * n_tok + t0 + min(lane, n - 1)) * H + h;
+    const float gv = g[gi], bv = beta[gi];
+    float x = lane < n ? gv : 0.0f;
+    const float b = lane < n ? bv : 0.0f;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const float y = __shfl_up(x, off, 64);
@@ -196,11 +200,10 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
 #pragma unroll
   for (int it = 0; it < 8; ++it) {
     const int idx = it * 256 + tid, row = idx >> 5, col = (idx & 31) * 4;
-    float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv;
-    if (row < n) {
-      kv = *reinterpret_cast<const float4 *>(kc + (int64_t)row * qk_tok + col);
-      qv = *reinterpret_cast<const float4 *>(qc + (int64_t)row * qk_tok + col);
-    }
+    const int rr = min(row, n - 1);
+    float4 kv = *reinterpret_cast<const float4 *>(kc + (int64_t)rr * qk_tok + col);
+    float4 qv = *reinterpret_cast<const float4 *>(qc + (int64_t)rr * qk_tok + col);
+    if (row >= n) kv = qv = make_float4(0.f, 0.f, 0.f, 0.f);
     store4_split(r1h + row * P136 + col, r1l + row * P136 + col, kv.x, kv.y, kv.z, kv.w);
     store4_split(r2h + row * P136 + col, r2l + row * P136 + col, qv.x, qv.y, qv.z, qv.w);
   }
@@ -261,12 +264,18 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
     u16 *kth = reinterpret_cast<u16 *>(wc + WS_K), *ktl = kth + DK * CH;
     for (int it = tid; it < DK * 8; it += 256) {
       const int i = it & (DK - 1), tg = it >> 7;
-      float xk[8], xv[8], xkp[8];
+      float xk[8], xv[8], xkp[8], kl[8], vl[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int t = min(8 * tg + e, n - 1);
+        kl[e] = kc[(int64_t)t * qk_tok + i];
+        vl[e] = vc[(int64_t)t * v_tok + i];
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int t = 8 * tg + e;
-        const float kk = t < n ? kc[(int64_t)t * qk_tok + i] : 0.0f;
-        const float vv = t < n ? vc[(int64_t)t * v_tok + i] : 0.0f;
+        const float kk = t < n ? kl[e] : 0.0f;
+        const float vv = t < n ? vl[e] : 0.0f;
         xk[e] = sBeta[t] * sEG[t] * kk;
         xv[e] = sBeta[t] * vv;
         xkp[e] = sEGn[t] * kk;
@@ -381,9 +390,12 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
       const int col = 16 * nt + l16, t = 16 * w + 4 * kg;
       *reinterpret_cast<float4 *>(oig + col * CH + t) =
           make_float4(accO[nt][0], accO[nt][1], accO[nt][2], accO[nt][3]);
+      float ql[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ql[r] = qc[(int64_t)min(t + r, n - 1) * qk_tok + col];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float qv = (t + r) < n ? qc[(int64_t)(t + r) * qk_tok + col] : 0.0f;
+        const float qv = (t + r) < n ? ql[r] : 0.0f;
         u16 hh, ll;
         split(sEG[t + r] * qv - accQ[nt][r], hh, ll);
         sth[(t + r) * P136 + col] = hh;
@@ -508,7 +520,9 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
     load_chunk(b, wh + (size_t)(c + 1) * WS_CHUNK, w, l16, kg, blk);
     scan_chunk(a, st, ssh, ssl, suh, sul, yh + (int64_t)c * CH * y_tok, y_tok,
                min(CH, n_tok - c * CH), scale, w, l16, kg);
-    if (c + 2 < n_chunks) load_chunk(a, wh + (size_t)(c + 2) * WS_CHUNK, w, l16, kg, blk);
+    // always issue the prefetch (the last one re-reads a valid chunk): a
+    // conditional load would make the compiler wait for every load in flight
+    load_chunk(a, wh + (size_t)min(c + 2, n_chunks - 1) * WS_CHUNK, w, l16, kg, blk);
     scan_chunk(b, st, ssh, ssl, suh, sul, yh + (int64_t)(c + 1) * CH * y_tok, y_tok,
                min(CH, n_tok - (c + 1) * CH), scale, w, l16, kg);
   }
