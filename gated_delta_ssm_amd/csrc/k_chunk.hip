@@ -21,9 +21,9 @@
 //     workspace (W, Q', K'^T as bf16 hi/lo planes; Ut^T, Oi^T in fp32; e^{G_n}).
 //   k_chunk_scan (phase B) -- one workgroup per (sequence, head, block of 16
 //     value columns), walking the chunks in order: the value columns of S are
-//     independent, so 8 workgroups share a head.  Each of its 4 waves owns 32
-//     key rows of the state block as MFMA accumulators; per chunk it computes
-//     16 rows of U and y and its 32 state rows.
+//     independent, so 8 workgroups share a head.  Each of its 8 waves owns 16
+//     key rows of the state block as an MFMA accumulator and one 16-token tile
+//     of either U or y; operands are prefetched two chunks ahead.
 //
 // Precision: every contraction runs on MFMA v_mfma_f32_16x16x32_bf16 with each
 // fp32 operand split into bf16 hi + lo, accumulating hi*hi + hi*lo + lo*hi in
@@ -120,14 +120,35 @@ __device__ __forceinline__ void store8_split(u16 *hi, u16 *lo, const float (&x)[
 
 // ----------------------------------------------------------------------------- workspace
 // Per (sequence, head, chunk), all offsets in bytes, each region 256-aligned.
+// The three MFMA A operands of the scan are stored fragment-major: fragment
+// (row tile m, k-step ks, plane) is 64 lanes x 16 bytes, lane (kg, l16)
+// holding row 16m + l16, columns 32ks + 8kg .. +7, so each wave load in the
+// scan is 1 KiB of consecutive bytes.  Ut and Oi are stored in the
+// accumulator layout [column tile][token tile][lane][4], which is the same lane
+// map on the writing and the reading side.
 constexpr size_t WS_PLANE = (size_t)CH * DK * 2;        // one bf16 plane of a 64x128 matrix
-constexpr size_t WS_W = 0;                              // W  [t][i]  hi, lo
-constexpr size_t WS_Q = 2 * WS_PLANE;                   // Q' [t][i]  hi, lo
-constexpr size_t WS_K = 4 * WS_PLANE;                   // K'^T [i][t] hi, lo
-constexpr size_t WS_U = 6 * WS_PLANE;                   // Ut^T [j][t] fp32
-constexpr size_t WS_O = WS_U + (size_t)DV * CH * 4;     // Oi^T [j][t] fp32
+constexpr size_t WS_W = 0;                              // W   (4 row tiles x 4 k-steps) hi, lo
+constexpr size_t WS_Q = 2 * WS_PLANE;                   // Q'  (4 x 4) hi, lo
+constexpr size_t WS_K = 4 * WS_PLANE;                   // K'^T (8 row tiles x 2 k-steps) hi, lo
+constexpr size_t WS_U = 6 * WS_PLANE;                   // Ut  fp32, accumulator layout
+constexpr size_t WS_O = WS_U + (size_t)DV * CH * 4;     // Oi  fp32, accumulator layout
 constexpr size_t WS_G = WS_O + (size_t)DV * CH * 4;     // e^{G_n}
 constexpr size_t WS_CHUNK = WS_G + 256;
+
+// u16 offset of a fragment's 8 elements for lane `lane`
+__device__ __forceinline__ int frag_off(int m, int ks, int n_ks, int plane, int lane) {
+  return (((m * n_ks + ks) * 2 + plane) * 64 + lane) * 8;
+}
+__device__ __forceinline__ Frag frag_ws(const u16 *base, int m, int ks, int n_ks, int lane) {
+  Frag f;
+  f.hi = *reinterpret_cast<const bf16x8 *>(base + frag_off(m, ks, n_ks, 0, lane));
+  f.lo = *reinterpret_cast<const bf16x8 *>(base + frag_off(m, ks, n_ks, 1, lane));
+  return f;
+}
+// float offset of the 4 accumulator values of (column tile nt, token tile mt, lane)
+__device__ __forceinline__ int acc_off(int nt, int mt, int lane) {
+  return ((nt * 4 + mt) * 64 + lane) * 4;
+}
 
 // ----------------------------------------------------------------------------- phase A
 // LDS plan (bytes).  R1/R2 hold, in turn: K/Q rows; X^T = (beta e^G K)^T and
@@ -158,7 +179,11 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
   const int c = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   const int hk = h / (H / Hk);
   const int t0 = c * CH;
-  const int n = min(CH, n_tok - t0);
+  // n == 0 for a padding chunk (an even chunk count keeps the scan's
+  // two-deep operand pipeline free of a tail): it yields e^{G_n} = 1 and
+  // all-zero operands, which leaves the state unchanged.
+  const int n = max(0, min(CH, n_tok - t0));
+  const int nl = max(n - 1, 0);  // last valid position, clamped for the loads
 
   u16 *r1h = reinterpret_cast<u16 *>(smem + L_R1), *r1l = r1h + DK * P72;
   u16 *r2h = reinterpret_cast<u16 *>(smem + L_R2), *r2l = r2h + DK * P72;
@@ -171,9 +196,10 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
   float *sG = reinterpret_cast<float *>(smem + L_R7);
   float *sBeta = sG + CH, *sEG = sG + 2 * CH, *sEGn = sG + 3 * CH;
 
-  const float *kc = k + s * qk_seq + (int64_t)t0 * qk_tok + hk * DK;
-  const float *qc = q + s * qk_seq + (int64_t)t0 * qk_tok + hk * DK;
-  const float *vc = v + s * v_seq + (int64_t)t0 * v_tok + h * DV;
+  const int tb = min(t0, n_tok - 1);  // base position of the loads (valid for padding)
+  const float *kc = k + s * qk_seq + (int64_t)tb * qk_tok + hk * DK;
+  const float *qc = q + s * qk_seq + (int64_t)tb * qk_tok + hk * DK;
+  const float *vc = v + s * v_seq + (int64_t)tb * v_tok + h * DV;
   unsigned char *wc = ws + (((size_t)s * H + h) * n_chunks + c) * WS_CHUNK;
 
   // 1. gate cumsum (wave 0), beta
@@ -181,7 +207,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
   // select, so no load sits behind a branch (a branch would force the compiler
   // to wait for every outstanding load at the join).
   if (w == 0) {
-    const int64_t gi = ((int64_t)s * n_tok + t0 + min(lane, n - 1)) * H + h;
+    const int64_t gi = ((int64_t)s * n_tok + min(t0 + min(lane, nl), n_tok - 1)) * H + h;
     const float gv = g[gi], bv = beta[gi];
     float x = lane < n ? gv : 0.0f;
     const float b = lane < n ? bv : 0.0f;
@@ -200,7 +226,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
 #pragma unroll
   for (int it = 0; it < 8; ++it) {
     const int idx = it * 256 + tid, row = idx >> 5, col = (idx & 31) * 4;
-    const int rr = min(row, n - 1);
+    const int rr = min(row, nl);
     float4 kv = *reinterpret_cast<const float4 *>(kc + (int64_t)rr * qk_tok + col);
     float4 qv = *reinterpret_cast<const float4 *>(qc + (int64_t)rr * qk_tok + col);
     if (row >= n) kv = qv = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -261,13 +287,13 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
     for (int r = 0; r < 16; ++r) sT[(16 * b + r) * PF + 16 * b + cc] = x[r];
   }
   {
-    u16 *kth = reinterpret_cast<u16 *>(wc + WS_K), *ktl = kth + DK * CH;
+    u16 *ktg = reinterpret_cast<u16 *>(wc + WS_K);
     for (int it = tid; it < DK * 8; it += 256) {
       const int i = it & (DK - 1), tg = it >> 7;
       float xk[8], xv[8], xkp[8], kl[8], vl[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int t = min(8 * tg + e, n - 1);
+        const int t = min(8 * tg + e, nl);
         kl[e] = kc[(int64_t)t * qk_tok + i];
         vl[e] = vc[(int64_t)t * v_tok + i];
       }
@@ -282,7 +308,9 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
       }
       store8_split(r1h + i * P72 + 8 * tg, r1l + i * P72 + 8 * tg, xk);
       store8_split(r2h + i * P72 + 8 * tg, r2l + i * P72 + 8 * tg, xv);
-      store8_split(kth + i * CH + 8 * tg, ktl + i * CH + 8 * tg, xkp);
+      const int kl_lane = (tg & 3) * 16 + (i & 15);
+      store8_split(ktg + frag_off(i >> 4, tg >> 2, 2, 0, kl_lane),
+                   ktg + frag_off(i >> 4, tg >> 2, 2, 1, kl_lane), xkp);
     }
   }
   __syncthreads();
@@ -344,7 +372,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
                    accW[nt][2], accW[nt][3]);
       store4_split(r2h + col * P72 + t, r2l + col * P72 + t, accU[nt][0], accU[nt][1],
                    accU[nt][2], accU[nt][3]);
-      *reinterpret_cast<float4 *>(utg + col * CH + t) =
+      *reinterpret_cast<float4 *>(utg + acc_off(nt, w, lane)) =
           make_float4(accU[nt][0], accU[nt][1], accU[nt][2], accU[nt][3]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -356,12 +384,12 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
     }
   }
   __syncthreads();
-  {  // staged W -> workspace, 16 bytes per thread per step
+  {  // staged W -> workspace in fragment order, 16 bytes per thread per step
     u16 *wg = reinterpret_cast<u16 *>(wc + WS_W);
-    for (int it = tid; it < 2 * CH * 16; it += 256) {
-      const int plane = it >> 10, row = (it >> 4) & 63, c16 = (it & 15) * 8;
-      const u16 *src = (plane ? stl : sth) + row * P136 + c16;
-      *reinterpret_cast<uint4 *>(wg + plane * CH * DK + row * DK + c16) =
+    for (int it = tid; it < 4 * 4 * 2 * 64; it += 256) {
+      const int ln = it & 63, plane = (it >> 6) & 1, ks = (it >> 7) & 3, m = it >> 9;
+      const u16 *src = (plane ? stl : sth) + (16 * m + (ln & 15)) * P136 + 32 * ks + 8 * (ln >> 4);
+      *reinterpret_cast<uint4 *>(wg + frag_off(m, ks, 4, plane, ln)) =
           *reinterpret_cast<const uint4 *>(src);
     }
   }
@@ -388,11 +416,11 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
       const int col = 16 * nt + l16, t = 16 * w + 4 * kg;
-      *reinterpret_cast<float4 *>(oig + col * CH + t) =
+      *reinterpret_cast<float4 *>(oig + acc_off(nt, w, lane)) =
           make_float4(accO[nt][0], accO[nt][1], accO[nt][2], accO[nt][3]);
       float ql[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ql[r] = qc[(int64_t)min(t + r, n - 1) * qk_tok + col];
+      for (int r = 0; r < 4; ++r) ql[r] = qc[(int64_t)min(t + r, nl) * qk_tok + col];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float qv = (t + r) < n ? ql[r] : 0.0f;
@@ -404,12 +432,12 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
     }
   }
   __syncthreads();
-  {
+  {  // staged Q' -> workspace in fragment order, 16 bytes per thread per step
     u16 *qg = reinterpret_cast<u16 *>(wc + WS_Q);
-    for (int it = tid; it < 2 * CH * 16; it += 256) {
-      const int plane = it >> 10, row = (it >> 4) & 63, c16 = (it & 15) * 8;
-      const u16 *src = (plane ? stl : sth) + row * P136 + c16;
-      *reinterpret_cast<uint4 *>(qg + plane * CH * DK + row * DK + c16) =
+    for (int it = tid; it < 4 * 4 * 2 * 64; it += 256) {
+      const int ln = it & 63, plane = (it >> 6) & 1, ks = (it >> 7) & 3, m = it >> 9;
+      const u16 *src = (plane ? stl : sth) + (16 * m + (ln & 15)) * P136 + 32 * ks + 8 * (ln >> 4);
+      *reinterpret_cast<uint4 *>(qg + frag_off(m, ks, 4, plane, ln)) =
           *reinterpret_cast<const uint4 *>(src);
     }
   }
@@ -417,80 +445,70 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
 }
 
 // ----------------------------------------------------------------------------- phase B
+// Eight waves per workgroup.  Wave w computes, per chunk:
+//   w < 4 : P = W S for token rows 16(w&3)..+15, then U = Ut - P  (shared via LDS)
+//   w >= 4: R = Q' S for token rows 16(w&3)..+15, then y = scale (R + Oi)
+//   all   : state rows 16w..16w+15 of the block, S <- e^{G_n} S + K'^T U.
+// Each wave's operands for one chunk are ~52 VGPRs; two chunks are kept in
+// flight (prefetch distance 2).
 struct ChunkOps {
-  Frag w[4], q[4], k[2][2];
-  float4 ut, oi;
-  float gam;
+  Frag a[4];      // W or Q' rows of this wave; slot j = k-step (j + blk) mod 4 over keys
+  Frag k[2];      // K'^T rows 16w..; slot j = k-step (j + blk) mod 2 over tokens
+  float4 add;     // Ut (P waves) or Oi (R waves) for this lane's 4 tokens
+  float gam;      // e^{G_n}
 };
 
 __device__ __forceinline__ void load_chunk(ChunkOps &o, const unsigned char *wc, int w, int l16,
                                            int kg, int blk) {
-  const u16 *wh = reinterpret_cast<const u16 *>(wc + WS_W), *wl = wh + CH * DK;
-  const u16 *qh = reinterpret_cast<const u16 *>(wc + WS_Q), *ql = qh + CH * DK;
-  const u16 *kh = reinterpret_cast<const u16 *>(wc + WS_K), *kl = kh + DK * CH;
+  const bool pw = w < 4;
+  const int lane = kg * 16 + l16;
+  const u16 *ag = reinterpret_cast<const u16 *>(wc + (pw ? WS_W : WS_Q));
+  const u16 *kgp = reinterpret_cast<const u16 *>(wc + WS_K);
+  // The 8 workgroups of a head read the same lines at about the same time;
+  // slot j holds k-step (j + blk) mod n, so their requests start on different
+  // lines.  The scan pairs each slot with the matching B fragment.
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    o.w[ks] = frag(wh, wl, DK, 16 * w + l16, 32 * ks + 8 * kg);
-    o.q[ks] = frag(qh, ql, DK, 16 * w + l16, 32 * ks + 8 * kg);
-  }
+  for (int j = 0; j < 4; ++j) o.a[j] = frag_ws(ag, w & 3, (j + blk) & 3, 4, lane);
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      o.k[mt][ks] = frag(kh, kl, CH, 32 * w + 16 * mt + l16, 32 * ks + 8 * kg);
-  const int j = blk * NBLK + l16, t = 16 * w + 4 * kg;
-  o.ut = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(wc + WS_U) + j * CH + t);
-  o.oi = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(wc + WS_O) + j * CH + t);
+  for (int j = 0; j < 2; ++j) o.k[j] = frag_ws(kgp, w, (j + blk) & 1, 2, lane);
+  const float *addp = reinterpret_cast<const float *>(wc + (pw ? WS_U : WS_O));
+  o.add = *reinterpret_cast<const float4 *>(addp + acc_off(blk, w & 3, lane));
   o.gam = *reinterpret_cast<const float *>(wc + WS_G);
 }
 
 constexpr int SP = DK + 8;     // pitch of the S^T block in LDS (bf16)
 constexpr int UP = CH + 8;     // pitch of the U^T block in LDS (bf16)
 
-// One chunk of the scan for this wave: state rows 32w..32w+31 (two 16-row
-// tiles) of the 16-column block in `st`; U and y rows 16w..16w+15.
-__device__ __forceinline__ void scan_chunk(const ChunkOps &o, f32x4 (&st)[2], u16 *ssh,
-                                           u16 *ssl, u16 *suh, u16 *sul, float *yc,
-                                           int64_t y_tok, int n, float scale, int w, int l16,
-                                           int kg) {
-  // state block -> LDS as S^T [j][i] hi/lo (the B operand of W S and Q' S)
+__device__ __forceinline__ void scan_chunk(const ChunkOps &o, f32x4 &st, u16 *ssh, u16 *ssl,
+                                           u16 *suh, u16 *sul, float *yc, int64_t y_tok, int n,
+                                           float scale, int w, int l16, int kg, int rot) {
+  // state tile -> LDS as S^T [j][i] (the B operand of W S and Q' S)
+  store4_split(ssh + l16 * SP + 16 * w + 4 * kg, ssl + l16 * SP + 16 * w + 4 * kg, st[0], st[1],
+               st[2], st[3]);
+  __syncthreads();
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const int i = 32 * w + 16 * mt + 4 * kg;
-    store4_split(ssh + l16 * SP + i, ssl + l16 * SP + i, st[mt][0], st[mt][1], st[mt][2],
-                 st[mt][3]);
+  for (int j = 0; j < 4; ++j)
+    acc = mfma3(o.a[j], frag(ssh, ssl, SP, l16, 32 * ((j + rot) & 3) + 8 * kg), acc);
+  const int t = 16 * (w & 3) + 4 * kg;
+  if (w < 4) {
+    store4_split(suh + l16 * UP + t, sul + l16 * UP + t, o.add.x - acc[0], o.add.y - acc[1],
+                 o.add.z - acc[2], o.add.w - acc[3]);
+  } else {
+    const float yo[4] = {scale * (acc[0] + o.add.x), scale * (acc[1] + o.add.y),
+                         scale * (acc[2] + o.add.z), scale * (acc[3] + o.add.w)};
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (t + r < n) yc[(int64_t)(t + r) * y_tok] = yo[r];
   }
   __syncthreads();
-  f32x4 p = {0.f, 0.f, 0.f, 0.f}, rr = p;
+  st = st * o.gam;
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const Frag b = frag(ssh, ssl, SP, l16, 32 * ks + 8 * kg);
-    p = mfma3(o.w[ks], b, p);
-    rr = mfma3(o.q[ks], b, rr);
-  }
-  // U = Ut - W S;  y = scale (Q' S + Oi)
-  const float u0 = o.ut.x - p[0], u1 = o.ut.y - p[1], u2 = o.ut.z - p[2], u3 = o.ut.w - p[3];
-  const int t = 16 * w + 4 * kg;
-  const float yo[4] = {scale * (rr[0] + o.oi.x), scale * (rr[1] + o.oi.y),
-                       scale * (rr[2] + o.oi.z), scale * (rr[3] + o.oi.w)};
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-    if (t + r < n) yc[(int64_t)(t + r) * y_tok] = yo[r];
-  store4_split(suh + l16 * UP + t, sul + l16 * UP + t, u0, u1, u2, u3);
-  __syncthreads();
-  // S = e^{G_n} S + K'^T U
-  Frag bu[2];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) bu[ks] = frag(suh, sul, UP, l16, 32 * ks + 8 * kg);
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    st[mt] = st[mt] * o.gam;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) st[mt] = mfma3(o.k[mt][ks], bu[ks], st[mt]);
-  }
+  for (int j = 0; j < 2; ++j)
+    st = mfma3(o.k[j], frag(suh, sul, UP, l16, 32 * ((j + rot) & 1) + 8 * kg), st);
 }
 
-__global__ __launch_bounds__(256) void k_chunk_scan(
+__global__ __launch_bounds__(512) void k_chunk_scan(
     float *__restrict__ state, int64_t st_seq, const unsigned char *__restrict__ ws,
     float *__restrict__ y, int64_t y_tok, int64_t y_seq, int n_tok, int n_chunks, int H,
     float scale) {
@@ -503,49 +521,48 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
   const int unit = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   const int blk = unit % NVB, sh = unit / NVB, h = sh % H, s = sh / H;
 
-  float *sp = state + s * st_seq + (int64_t)h * DK * DV + (int64_t)(blk * NBLK + l16) * DK;
-  f32x4 st[2];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const float4 t4 = *reinterpret_cast<const float4 *>(sp + 32 * w + 16 * mt + 4 * kg);
-    st[mt] = f32x4{t4.x, t4.y, t4.z, t4.w};
-  }
+  // state rows 16w + 4kg + r, column blk*16 + l16 (value-major storage)
+  float *sp = state + s * st_seq + (int64_t)h * DK * DV + (int64_t)(blk * NBLK + l16) * DK +
+              16 * w + 4 * kg;
+  const float4 s4 = *reinterpret_cast<const float4 *>(sp);
+  f32x4 st = {s4.x, s4.y, s4.z, s4.w};
   const unsigned char *wh = ws + ((size_t)s * H + h) * n_chunks * WS_CHUNK;
   float *yh = y + s * y_seq + (int64_t)h * DV + blk * NBLK + l16;
+  auto chunk_ptr = [&](int c) { return wh + (size_t)min(c, n_chunks - 1) * WS_CHUNK; };
+  auto run = [&](const ChunkOps &o, int c) {
+    scan_chunk(o, st, ssh, ssl, suh, sul, yh + (int64_t)c * CH * y_tok, y_tok,
+               min(CH, n_tok - c * CH), scale, w, l16, kg, blk);
+  };
 
+  // Two chunks in flight: a chunk's operands are requested two chunks ahead.
+  // n_chunks is even (the workspace is padded with an identity chunk), so the
+  // loop has no tail; a tail would make the compiler copy the operand
+  // registers at the loop head, which waits for every load in flight.
   ChunkOps a, b;
-  load_chunk(a, wh, w, l16, kg, blk);
-  int c = 0;
-  for (; c + 1 < n_chunks; c += 2) {
-    load_chunk(b, wh + (size_t)(c + 1) * WS_CHUNK, w, l16, kg, blk);
-    scan_chunk(a, st, ssh, ssl, suh, sul, yh + (int64_t)c * CH * y_tok, y_tok,
-               min(CH, n_tok - c * CH), scale, w, l16, kg);
-    // always issue the prefetch (the last one re-reads a valid chunk): a
-    // conditional load would make the compiler wait for every load in flight
-    load_chunk(a, wh + (size_t)min(c + 2, n_chunks - 1) * WS_CHUNK, w, l16, kg, blk);
-    scan_chunk(b, st, ssh, ssl, suh, sul, yh + (int64_t)(c + 1) * CH * y_tok, y_tok,
-               min(CH, n_tok - (c + 1) * CH), scale, w, l16, kg);
+  load_chunk(a, chunk_ptr(0), w, l16, kg, blk);
+  load_chunk(b, chunk_ptr(1), w, l16, kg, blk);
+  for (int c = 0; c < n_chunks; c += 2) {
+    run(a, c);
+    load_chunk(a, chunk_ptr(c + 2), w, l16, kg, blk);
+    run(b, c + 1);
+    load_chunk(b, chunk_ptr(c + 3), w, l16, kg, blk);
   }
-  if (c < n_chunks)
-    scan_chunk(a, st, ssh, ssl, suh, sul, yh + (int64_t)c * CH * y_tok, y_tok,
-               min(CH, n_tok - c * CH), scale, w, l16, kg);
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-    *reinterpret_cast<float4 *>(sp + 32 * w + 16 * mt + 4 * kg) =
-        make_float4(st[mt][0], st[mt][1], st[mt][2], st[mt][3]);
+  *reinterpret_cast<float4 *>(sp) = make_float4(st[0], st[1], st[2], st[3]);
 }
 
 }  // namespace
 
+// chunks per sequence in the workspace: ceil(n_tok / 64) rounded up to even
+static int padded_chunks(int n_tok) { return ((n_tok + CH - 1) / CH + 1) & ~1; }
+
 size_t chunked_workspace_bytes(int n_seq, int n_tok, int H, int, int, int) {
-  const size_t n_chunks = ((size_t)n_tok + CH - 1) / CH;
-  return (size_t)n_seq * H * n_chunks * WS_CHUNK;
+  return (size_t)n_seq * H * padded_chunks(n_tok) * WS_CHUNK;
 }
 
 int launch_recur_chunked(const RecurArgs &a, int chunk, void *ws, size_t ws_bytes,
                          hipStream_t stream) {
   if (chunk != CH || a.S != DK) return GDN_ERR_UNSUPPORTED;
-  const int n_chunks = (a.n_tok + CH - 1) / CH;
+  const int n_chunks = padded_chunks(a.n_tok);
   if (ws_bytes < chunked_workspace_bytes(a.n_seq, a.n_tok, a.H, a.Hk, a.S, chunk))
     return GDN_ERR_WORKSPACE;
   unsigned char *wsb = static_cast<unsigned char *>(ws);
@@ -554,7 +571,7 @@ int launch_recur_chunked(const RecurArgs &a, int chunk, void *ws, size_t ws_byte
                          a.n_tok, n_chunks, a.H, a.Hk);
   if (rc != GDN_OK) return rc;
   const int nwg = a.n_seq * a.H * NVB;  // a multiple of 8 (NVB == 8)
-  return launch_kernel(k_chunk_scan, dim3(nwg), dim3(256), 0, stream, a.state, a.st_seq,
+  return launch_kernel(k_chunk_scan, dim3(nwg), dim3(512), 0, stream, a.state, a.st_seq,
                        (const unsigned char *)wsb, a.y, a.y_tok, a.y_seq, a.n_tok, n_chunks, a.H,
                        a.scale);
 }
