@@ -17,13 +17,12 @@
 // Only the last three lines depend on S0, so the work splits in two kernels:
 //
 //   k_chunk_prep (phase A) -- one workgroup per (sequence, head, chunk), all
-//     in parallel: everything that does not depend on S0, written to the
-//     workspace (W, Q', K'^T as bf16 hi/lo planes; Ut^T, Oi^T in fp32; e^{G_n}).
+//     in parallel: everything that does not depend on S0, written to a
+//     workspace in the exact register layout the scan loads.
 //   k_chunk_scan (phase B) -- one workgroup per (sequence, head, block of 16
 //     value columns), walking the chunks in order: the value columns of S are
-//     independent, so 8 workgroups share a head.  Each of its 8 waves owns 16
-//     key rows of the state block as an MFMA accumulator and one 16-token tile
-//     of either U or y; operands are prefetched two chunks ahead.
+//     independent, so 8 workgroups share a head, and they are mapped to one
+//     XCD so they share its L2.  Operands are prefetched two chunks ahead.
 //
 // Precision: every contraction runs on MFMA v_mfma_f32_16x16x32_bf16 with each
 // fp32 operand split into bf16 hi + lo, accumulating hi*hi + hi*lo + lo*hi in
@@ -33,9 +32,9 @@
 // before the exp), so g must be <= 0, which the decay gate guarantees.
 //
 // MFMA operand layout (16x16x32 bf16, wave64): lane l holds row (l % 16) of
-// A / column (l % 16) of B, with k = 8*(l / 16) + e, e = 0..7, so every
-// operand is stored k-contiguous ([row][k]) and one fragment is one 16-byte
-// load per plane.  The accumulator holds D[4*(l/16) + r][l % 16], r = 0..3.
+// A / column (l % 16) of B, and 8 k values chosen by l / 16; the accumulator
+// holds D[4*(l/16) + r][l % 16], r = 0..3.  Operands that are the transpose of
+// a row-major LDS tile are read with ds_read_b64_tr_b16 (gfx950).
 #include <hip/hip_runtime.h>
 
 #include "gdn.h"
@@ -82,11 +81,55 @@ __device__ __forceinline__ f32x4 mfma3(const Frag &a, const Frag &b, f32x4 c) {
   return c;
 }
 
-// Fragment rows [row][k..k+7] of a pair of k-contiguous bf16 planes.
+// ----------------------------------------------------------------------------- fragments
+// Standard fragment of a k-contiguous tile: row `row`, k = k + 8*kg + 0..7.
 __device__ __forceinline__ Frag frag(const u16 *hi, const u16 *lo, int pitch, int row, int k) {
   Frag f;
   f.hi = *reinterpret_cast<const bf16x8 *>(hi + row * pitch + k);
   f.lo = *reinterpret_cast<const bf16x8 *>(lo + row * pitch + k);
+  return f;
+}
+
+// The permuted k order used wherever a fragment meets an accumulator tile:
+// slot e of lane (kg, l16) in k-step ks holds k = 32ks + 4kg + e (e < 4) and
+// k = 32ks + 16 + 4kg + (e - 4) (e >= 4).  Both operands of a product use it
+// (the sum over k does not depend on the order), and it is exactly the set of
+// rows an accumulator tile pair gives one lane, so accumulators turn into
+// fragments without any transpose.
+__device__ __forceinline__ int pi_k(int k0, int kg, int e) {
+  return k0 + 4 * kg + (e & 3) + ((e >> 2) << 4);
+}
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x8 cat(v4s a, v4s b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Permuted fragment of a k-contiguous tile: row `row`, k in pi(k0, kg).
+__device__ __forceinline__ Frag frag_pi(const u16 *hi, const u16 *lo, int pitch, int row, int k0,
+                                        int kg) {
+  const int o = row * pitch + k0 + 4 * kg;
+  Frag f;
+  f.hi = cat(*reinterpret_cast<const v4s *>(hi + o), *reinterpret_cast<const v4s *>(hi + o + 16));
+  f.lo = cat(*reinterpret_cast<const v4s *>(lo + o), *reinterpret_cast<const v4s *>(lo + o + 16));
+  return f;
+}
+
+// Transposed permuted fragment of a row-major [k][n] LDS tile: column
+// nb + l16, rows pi(k0, kg), read with ds_read_b64_tr_b16.  In each 16-lane
+// group, lane j points at row k0 + 4kg + j/4 (then + 16), columns
+// nb + 4(j%4) .. +3; the transpose hands lane i column nb + i of those 4 rows.
+__device__ __forceinline__ v4s tr4(const u16 *p) {
+  typedef short v4s_lds __attribute__((ext_vector_type(4)));
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s_lds *)(p));
+}
+__device__ __forceinline__ Frag frag_tr(const u16 *hi, const u16 *lo, int pitch, int k0, int nb,
+                                        int kg, int l16) {
+  const int o = (k0 + 4 * kg + (l16 >> 2)) * pitch + nb + 4 * (l16 & 3);
+  Frag f;
+  f.hi = cat(tr4(hi + o), tr4(hi + o + 16 * pitch));
+  f.lo = cat(tr4(lo + o), tr4(lo + o + 16 * pitch));
   return f;
 }
 
@@ -120,18 +163,20 @@ __device__ __forceinline__ void store8_split(u16 *hi, u16 *lo, const float (&x)[
 
 // ----------------------------------------------------------------------------- workspace
 // Per (sequence, head, chunk), all offsets in bytes, each region 256-aligned.
-// The three MFMA A operands of the scan are stored fragment-major: fragment
-// (row tile m, k-step ks, plane) is 64 lanes x 16 bytes, lane (kg, l16)
-// holding row 16m + l16, columns 32ks + 8kg .. +7, so each wave load in the
-// scan is 1 KiB of consecutive bytes.  Ut and Oi are stored in the
-// accumulator layout [column tile][token tile][lane][4], which is the same lane
-// map on the writing and the reading side.
+//   W, Q'  : fragment (token tile m, key k-step ks) = 64 lanes x 16 B per plane,
+//            lane (kg, l16) holding row 16m + l16, keys pi(32ks, kg)
+//   K'^T   : fragment (key tile m, token k-step ks), lane holding key row
+//            16m + l16, tokens pi(32ks, kg)
+//   Ut, Oi : fp32 accumulator tiles [value tile][token tile][lane][4], lane
+//            (kg, l16) holding values 16d + 4kg + r of token 16m + l16
+// These are the exact register images the scan loads, so each of its wave
+// loads is 1 KiB (or 1 KiB of float4) of consecutive bytes.
 constexpr size_t WS_PLANE = (size_t)CH * DK * 2;        // one bf16 plane of a 64x128 matrix
-constexpr size_t WS_W = 0;                              // W   (4 row tiles x 4 k-steps) hi, lo
-constexpr size_t WS_Q = 2 * WS_PLANE;                   // Q'  (4 x 4) hi, lo
-constexpr size_t WS_K = 4 * WS_PLANE;                   // K'^T (8 row tiles x 2 k-steps) hi, lo
-constexpr size_t WS_U = 6 * WS_PLANE;                   // Ut  fp32, accumulator layout
-constexpr size_t WS_O = WS_U + (size_t)DV * CH * 4;     // Oi  fp32, accumulator layout
+constexpr size_t WS_W = 0;                              // W   (4 token tiles x 4 k-steps)
+constexpr size_t WS_Q = 2 * WS_PLANE;                   // Q'  (4 x 4)
+constexpr size_t WS_K = 4 * WS_PLANE;                   // K'^T (8 key tiles x 2 k-steps)
+constexpr size_t WS_U = 6 * WS_PLANE;                   // Ut  fp32 accumulator tiles
+constexpr size_t WS_O = WS_U + (size_t)DV * CH * 4;     // Oi  fp32 accumulator tiles
 constexpr size_t WS_G = WS_O + (size_t)DV * CH * 4;     // e^{G_n}
 constexpr size_t WS_CHUNK = WS_G + 256;
 
@@ -145,31 +190,41 @@ __device__ __forceinline__ Frag frag_ws(const u16 *base, int m, int ks, int n_ks
   f.lo = *reinterpret_cast<const bf16x8 *>(base + frag_off(m, ks, n_ks, 1, lane));
   return f;
 }
-// float offset of the 4 accumulator values of (column tile nt, token tile mt, lane)
-__device__ __forceinline__ int acc_off(int nt, int mt, int lane) {
-  return ((nt * 4 + mt) * 64 + lane) * 4;
+// float offset of the accumulator tile (value tile d, token tile m) for lane
+__device__ __forceinline__ int acc_off(int d, int m, int lane) {
+  return ((d * 4 + m) * 64 + lane) * 4;
 }
 
 // ----------------------------------------------------------------------------- phase A
-// LDS plan (bytes).  R1/R2 hold, in turn: K/Q rows; X^T = (beta e^G K)^T and
-// (beta V)^T; W^T and Ut^T.  R3 holds A (fp32) then T (bf16 hi/lo); R4 holds T
-// in fp32 while it is built; R3+R4 then stage W and Q' for coalesced stores.
-constexpr int P136 = 136;  // pitch (bf16) of a [64][128] matrix
-constexpr int P72 = 72;    // pitch (bf16) of a [..][64] matrix
-constexpr int PF = 65;     // pitch (fp32) of a [64][64] matrix
-constexpr int L_R1 = 0;
-constexpr int L_R2 = L_R1 + 2 * DK * P72 * 2;           // 36864
-constexpr int L_R3 = L_R2 + 2 * DK * P72 * 2;           // 73728
-constexpr int L_R4 = L_R3 + 2 * CH * P72 * 2;           // +18432
-constexpr int L_R5 = L_R4 + CH * PF * 4;                // +16640
-constexpr int L_R6 = L_R5 + 2 * CH * P72 * 2;           // +18432
-constexpr int L_R7 = L_R6 + 3 * 16 * 16 * 4;            // +3072
-constexpr int L_TOTAL = L_R7 + 4 * CH * 4;              // +1024
-static_assert(2 * CH * P136 * 2 <= L_R2 - L_R1, "K/Q rows fit in R1/R2");
-static_assert(2 * CH * P136 * 2 <= L_R5 - L_R3, "staging fits in R3+R4");
-static_assert(CH * PF * 4 <= L_R4 - L_R3, "fp32 A fits in R3");
+// One workgroup (8 waves) per (sequence, head, chunk).  All row-major LDS
+// tiles are bf16 hi/lo planes.  Plan (bytes):
+//   L_K : K rows [t][i]            -> later W rows [s][i]
+//   L_Q : Q rows [t][i] -> V rows  -> later Ut rows [s][j]
+//   L_T : T1 = T diag(beta e^G), T2 = T diag(beta)  [t][s]
+//   L_L : L o Q K^T                 [t][s]
+//   L_A : A, then T in place (fp32 [64][68]);  L_S: inverse scratch
+//   L_G : G, beta, e^G, e^{G_n - G}
+// The products are computed transposed (feature index as the MFMA row):
+//   W^T = K^T T1^T,  Ut^T = V^T T2^T,  Q'^T = e^G Q^T - W^T (LQK)^T,
+//   Oi^T = Ut^T (LQK)^T
+// with K^T, V^T, W^T, Ut^T read from row-major tiles by transpose reads, so a
+// wave's accumulators are already the scan's fragments.
+constexpr int PR = 136;   // pitch (bf16) of a [64][128] row-major tile
+constexpr int PS = 72;    // pitch (bf16) of a [64][64] tile
+constexpr int PA = 68;    // pitch (fp32) of the [64][64] inverse
+constexpr int TILE128 = 2 * CH * PR * 2;
+constexpr int TILE64 = 2 * CH * PS * 2;
+constexpr int L_K = 0;
+constexpr int L_Q = L_K + TILE128;
+constexpr int L_T = L_Q + TILE128;
+constexpr int L_L = L_T + 2 * TILE64;
+constexpr int L_A = L_L + TILE64;
+constexpr int L_S = L_A + CH * PA * 4;
+constexpr int L_G = L_S + 3 * 256 * 4;
+constexpr int L_TOTAL = L_G + 4 * CH * 4;
+static_assert(L_TOTAL <= 160 * 1024, "phase A LDS fits one CU");
 
-__global__ __launch_bounds__(256) void k_chunk_prep(
+__global__ __launch_bounds__(512) void k_chunk_prep(
     const float *__restrict__ q, const float *__restrict__ k, int64_t qk_tok, int64_t qk_seq,
     const float *__restrict__ v, int64_t v_tok, int64_t v_seq, const float *__restrict__ g,
     const float *__restrict__ beta, unsigned char *__restrict__ ws, int n_tok, int n_chunks,
@@ -179,33 +234,40 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
   const int c = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   const int hk = h / (H / Hk);
   const int t0 = c * CH;
-  // n == 0 for a padding chunk (an even chunk count keeps the scan's
-  // two-deep operand pipeline free of a tail): it yields e^{G_n} = 1 and
+  // n == 0 for a padding chunk (the chunk count is rounded up to even so the
+  // scan's two-deep operand pipeline has no tail): it yields e^{G_n} = 1 and
   // all-zero operands, which leaves the state unchanged.
   const int n = max(0, min(CH, n_tok - t0));
-  const int nl = max(n - 1, 0);  // last valid position, clamped for the loads
+  const int nl = max(n - 1, 0);       // last valid position, for clamped loads
+  const int tb = min(t0, n_tok - 1);  // base position of the loads (valid for padding)
 
-  u16 *r1h = reinterpret_cast<u16 *>(smem + L_R1), *r1l = r1h + DK * P72;
-  u16 *r2h = reinterpret_cast<u16 *>(smem + L_R2), *r2l = r2h + DK * P72;
-  float *sA = reinterpret_cast<float *>(smem + L_R3);
-  u16 *r3h = reinterpret_cast<u16 *>(smem + L_R3), *r3l = r3h + CH * P72;
-  float *sT = reinterpret_cast<float *>(smem + L_R4);
-  u16 *sth = reinterpret_cast<u16 *>(smem + L_R3), *stl = sth + CH * P136;  // staging
-  u16 *r5h = reinterpret_cast<u16 *>(smem + L_R5), *r5l = r5h + CH * P72;
-  float *scratch = reinterpret_cast<float *>(smem + L_R6);
-  float *sG = reinterpret_cast<float *>(smem + L_R7);
+  u16 *kh = reinterpret_cast<u16 *>(smem + L_K), *klo = kh + CH * PR;
+  u16 *qh = reinterpret_cast<u16 *>(smem + L_Q), *qlo = qh + CH * PR;
+  u16 *t1h = reinterpret_cast<u16 *>(smem + L_T), *t1l = t1h + CH * PS;
+  u16 *t2h = t1l + CH * PS, *t2l = t2h + CH * PS;
+  u16 *lqh = reinterpret_cast<u16 *>(smem + L_L), *lql = lqh + CH * PS;
+  float *sA = reinterpret_cast<float *>(smem + L_A);
+  float *scratch = reinterpret_cast<float *>(smem + L_S);
+  float *sG = reinterpret_cast<float *>(smem + L_G);
   float *sBeta = sG + CH, *sEG = sG + 2 * CH, *sEGn = sG + 3 * CH;
 
-  const int tb = min(t0, n_tok - 1);  // base position of the loads (valid for padding)
   const float *kc = k + s * qk_seq + (int64_t)tb * qk_tok + hk * DK;
   const float *qc = q + s * qk_seq + (int64_t)tb * qk_tok + hk * DK;
   const float *vc = v + s * v_seq + (int64_t)tb * v_tok + h * DV;
   unsigned char *wc = ws + (((size_t)s * H + h) * n_chunks + c) * WS_CHUNK;
 
-  // 1. gate cumsum (wave 0), beta
-  // Loads past the last position read a valid position and are zeroed by a
-  // select, so no load sits behind a branch (a branch would force the compiler
-  // to wait for every outstanding load at the join).
+  // S0. every load of the chunk is issued first (rows past n read a valid row
+  // and are zeroed by a select: a load behind a branch would make the
+  // compiler wait for all loads in flight at the join)
+  float4 kr[4], qr[4], vr[4];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int idx = it * 512 + tid, row = idx >> 5, col = (idx & 31) * 4;
+    const int rr = min(row, nl);
+    kr[it] = *reinterpret_cast<const float4 *>(kc + (int64_t)rr * qk_tok + col);
+    qr[it] = *reinterpret_cast<const float4 *>(qc + (int64_t)rr * qk_tok + col);
+    vr[it] = *reinterpret_cast<const float4 *>(vc + (int64_t)rr * v_tok + col);
+  }
   if (w == 0) {
     const int64_t gi = ((int64_t)s * n_tok + min(t0 + min(lane, nl), n_tok - 1)) * H + h;
     const float gv = g[gi], bv = beta[gi];
@@ -222,298 +284,310 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
     sEG[lane] = expf(x);
     sEGn[lane] = expf(gn - x);
   }
-  // 2. K, Q rows -> R1, R2 (bf16 hi/lo, [t][i])
+  // zero A and (L o QK^T): their upper triangles stay zero
+  for (int e = tid; e < CH * PA; e += 512) sA[e] = 0.0f;
+  for (int e = tid; e < CH * PS; e += 512) lqh[e] = lql[e] = 0;
+  // S1. K, Q rows -> LDS (bf16 hi/lo)
 #pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int idx = it * 256 + tid, row = idx >> 5, col = (idx & 31) * 4;
-    const int rr = min(row, nl);
-    float4 kv = *reinterpret_cast<const float4 *>(kc + (int64_t)rr * qk_tok + col);
-    float4 qv = *reinterpret_cast<const float4 *>(qc + (int64_t)rr * qk_tok + col);
-    if (row >= n) kv = qv = make_float4(0.f, 0.f, 0.f, 0.f);
-    store4_split(r1h + row * P136 + col, r1l + row * P136 + col, kv.x, kv.y, kv.z, kv.w);
-    store4_split(r2h + row * P136 + col, r2l + row * P136 + col, qv.x, qv.y, qv.z, qv.w);
+  for (int it = 0; it < 4; ++it) {
+    const int idx = it * 512 + tid, row = idx >> 5, col = (idx & 31) * 4;
+    const float4 kv = row < n ? kr[it] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 qv = row < n ? qr[it] : make_float4(0.f, 0.f, 0.f, 0.f);
+    store4_split(kh + row * PR + col, klo + row * PR + col, kv.x, kv.y, kv.z, kv.w);
+    store4_split(qh + row * PR + col, qlo + row * PR + col, qv.x, qv.y, qv.z, qv.w);
   }
   __syncthreads();
 
-  // 3. K K^T and Q K^T, lower tiles; wave w owns tile row w
-  for (int j = 0; j < 4; ++j) {
-    if (j <= w) {
-      f32x4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = akk;
+  // S2a. K K^T and Q K^T on the 10 lower tiles each: 20 jobs over 8 waves
+  for (int job = w; job < 20; job += 8) {
+    const bool qk = job >= 10;
+    const int jt = qk ? job - 10 : job;
+    const int ti = jt < 1 ? 0 : jt < 3 ? 1 : jt < 6 ? 2 : 3;   // lower-tile index -> (ti, tj)
+    const int tj = jt - ti * (ti + 1) / 2;
+    const u16 *ah = qk ? qh : kh, *al = qk ? qlo : klo;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const Frag fk = frag(r1h, r1l, P136, 16 * w + l16, 32 * ks + 8 * kg);
-        const Frag fq = frag(r2h, r2l, P136, 16 * w + l16, 32 * ks + 8 * kg);
-        const Frag fb = frag(r1h, r1l, P136, 16 * j + l16, 32 * ks + 8 * kg);
-        akk = mfma3(fk, fb, akk);
-        aqk = mfma3(fq, fb, aqk);
-      }
+    for (int ks = 0; ks < 4; ++ks)
+      acc = mfma3(frag(ah, al, PR, 16 * ti + l16, 32 * ks + 8 * kg),
+                  frag(kh, klo, PR, 16 * tj + l16, 32 * ks + 8 * kg), acc);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * w + 4 * kg + r, sidx = 16 * j + l16;
-        const float e = sidx <= t ? expf(sG[t] - sG[sidx]) : 0.0f;
-        sA[t * PF + sidx] = sidx < t ? sBeta[t] * e * akk[r] : 0.0f;
-        u16 hh, ll;
-        split(e * aqk[r], hh, ll);
-        r5h[t * P72 + sidx] = hh;
-        r5l[t * P72 + sidx] = ll;
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * w + 4 * kg + r, sidx = 16 * j + l16;
-        sA[t * PF + sidx] = 0.0f;
-        r5h[t * P72 + sidx] = 0;
-        r5l[t * P72 + sidx] = 0;
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * ti + 4 * kg + r, sx = 16 * tj + l16;
+      if (sx <= t) {
+        const float e = expf(sG[t] - sG[sx]);
+        if (!qk) {
+          if (sx < t) sA[t * PA + sx] = sBeta[t] * e * acc[r];
+        } else {
+          u16 hh, ll;
+          split(e * acc[r], hh, ll);
+          lqh[t * PS + sx] = hh;
+          lql[t * PS + sx] = ll;
+        }
       }
     }
   }
-  // zero the fp32 inverse buffer
-  for (int e = tid; e < CH * PF; e += 256) sT[e] = 0.0f;
+  // S2b. K'^T fragments (K' = diag(e^{G_n - G}) K) straight from the K tile:
+  // wave w writes key tile w, both token k-steps
+  {
+    u16 *ktg = reinterpret_cast<u16 *>(wc + WS_K);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const Frag f = frag_tr(kh, klo, PR, 32 * ks, 16 * w, kg, l16);
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        x[e] = (bf16_value((u16)f.hi[e]) + bf16_value((u16)f.lo[e])) * sEGn[pi_k(32 * ks, kg, e)];
+      store8_split(ktg + frag_off(w, ks, 2, 0, lane), ktg + frag_off(w, ks, 2, 1, lane), x);
+    }
+  }
   __syncthreads();
 
-  // 4. R1 <- X^T = (beta e^G K)^T, R2 <- (beta V)^T, K'^T -> workspace;
-  //    meanwhile threads 0..63 invert the four 16x16 diagonal blocks of I + A.
+  // S3a. T = (I + A)^{-1} in place: threads 0..63 invert the four 16x16
+  // diagonal blocks (one column each, forward substitution in fp32); the
+  // other threads move V into the Q tile (Q is no longer needed).
+  float x[16];
   if (tid < 64) {
     const int b = tid >> 4, cc = tid & 15;
-    float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float acc = r == cc ? 1.0f : 0.0f;
 #pragma unroll
-      for (int j = 0; j < r; ++j) acc -= sA[(16 * b + r) * PF + 16 * b + j] * x[j];
+      for (int j = 0; j < r; ++j) acc -= sA[(16 * b + r) * PA + 16 * b + j] * x[j];
       x[r] = acc;
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sT[(16 * b + r) * PF + 16 * b + cc] = x[r];
   }
-  {
-    u16 *ktg = reinterpret_cast<u16 *>(wc + WS_K);
-    for (int it = tid; it < DK * 8; it += 256) {
-      const int i = it & (DK - 1), tg = it >> 7;
-      float xk[8], xv[8], xkp[8], kl[8], vl[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int t = min(8 * tg + e, nl);
-        kl[e] = kc[(int64_t)t * qk_tok + i];
-        vl[e] = vc[(int64_t)t * v_tok + i];
-      }
+  for (int it = 0; it < 4; ++it) {
+    const int idx = it * 512 + tid, row = idx >> 5, col = (idx & 31) * 4;
+    const float4 vv = row < n ? vr[it] : make_float4(0.f, 0.f, 0.f, 0.f);
+    store4_split(qh + row * PR + col, qlo + row * PR + col, vv.x, vv.y, vv.z, vv.w);
+  }
+  __syncthreads();  // every diagonal block read before any is overwritten
+  if (tid < 64) {
+    const int b = tid >> 4, cc = tid & 15;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int t = 8 * tg + e;
-        const float kk = t < n ? kl[e] : 0.0f;
-        const float vv = t < n ? vl[e] : 0.0f;
-        xk[e] = sBeta[t] * sEG[t] * kk;
-        xv[e] = sBeta[t] * vv;
-        xkp[e] = sEGn[t] * kk;
-      }
-      store8_split(r1h + i * P72 + 8 * tg, r1l + i * P72 + 8 * tg, xk);
-      store8_split(r2h + i * P72 + 8 * tg, r2l + i * P72 + 8 * tg, xv);
-      const int kl_lane = (tg & 3) * 16 + (i & 15);
-      store8_split(ktg + frag_off(i >> 4, tg >> 2, 2, 0, kl_lane),
-                   ktg + frag_off(i >> 4, tg >> 2, 2, 1, kl_lane), xkp);
-    }
+    for (int r = 0; r < 16; ++r) sA[(16 * b + r) * PA + 16 * b + cc] = x[r];
   }
   __syncthreads();
-  // off-diagonal blocks: T_ib,jb = -T_ib,ib * sum_{kb=jb}^{ib-1} A_ib,kb T_kb,jb
+  // S3b. off-diagonal blocks, block row by block row:
+  //   T_ib,jb = -T_ib,ib * sum_{kb=jb}^{ib-1} A_ib,kb T_kb,jb
+  // (A_ib,* is still in place until its own row is finished)
   for (int ib = 1; ib < 4; ++ib) {
-    for (int e = tid; e < ib * 256; e += 256) {
+    for (int e = tid; e < ib * 256; e += 512) {
       const int jb = e >> 8, r = (e >> 4) & 15, cc = e & 15;
       float acc = 0.0f;
       for (int kb = jb; kb < ib; ++kb)
 #pragma unroll
         for (int m = 0; m < 16; ++m)
-          acc += sA[(16 * ib + r) * PF + 16 * kb + m] * sT[(16 * kb + m) * PF + 16 * jb + cc];
+          acc += sA[(16 * ib + r) * PA + 16 * kb + m] * sA[(16 * kb + m) * PA + 16 * jb + cc];
       scratch[e] = acc;
     }
     __syncthreads();
-    for (int e = tid; e < ib * 256; e += 256) {
+    for (int e = tid; e < ib * 256; e += 512) {
       const int jb = e >> 8, r = (e >> 4) & 15, cc = e & 15;
       float acc = 0.0f;
 #pragma unroll
       for (int m = 0; m < 16; ++m)
-        acc += sT[(16 * ib + r) * PF + 16 * ib + m] * scratch[(jb << 8) + (m << 4) + cc];
-      sT[(16 * ib + r) * PF + 16 * jb + cc] = -acc;
+        acc += sA[(16 * ib + r) * PA + 16 * ib + m] * scratch[(jb << 8) + (m << 4) + cc];
+      sA[(16 * ib + r) * PA + 16 * jb + cc] = -acc;
     }
     __syncthreads();
   }
-  // T (fp32) -> R3 as bf16 hi/lo [t][s]
-  for (int it = tid; it < CH * 8; it += 256) {
-    const int row = it >> 3, cg = (it & 7) * 8;
-    float x[8];
+  // S4. T1 = T diag(beta e^G), T2 = T diag(beta) as bf16 hi/lo [t][s]
+  {
+    const int row = tid >> 3, cg = (tid & 7) * 8;
+    const float4 a0 = *reinterpret_cast<const float4 *>(sA + row * PA + cg);
+    const float4 a1 = *reinterpret_cast<const float4 *>(sA + row * PA + cg + 4);
+    const float tv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    float x1[8], x2[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = sT[row * PF + cg + e];
-    store8_split(r3h + row * P72 + cg, r3l + row * P72 + cg, x);
+    for (int e = 0; e < 8; ++e) {
+      x1[e] = tv[e] * (sBeta[cg + e] * sEG[cg + e]);
+      x2[e] = tv[e] * sBeta[cg + e];
+    }
+    store8_split(t1h + row * PS + cg, t1l + row * PS + cg, x1);
+    store8_split(t2h + row * PS + cg, t2l + row * PS + cg, x2);
   }
   __syncthreads();
 
-  // 5. W = T X and Ut = T (beta V): wave w -> rows 16w..16w+15, all 128 columns
-  f32x4 accW[8], accU[8];
+  // S5. W^T = K^T T1^T and Ut^T = V^T T2^T.  Wave w owns key/value tiles
+  // 2kp, 2kp+1 (kp = w & 3) and token tiles 2tp, 2tp+1 (tp = w >> 2).
+  const int kp = w & 3, tp = w >> 2;
+  // Q at the accumulator positions of Q'^T, needed in S6; loaded now so the
+  // loads are in flight during the products
+  float4 qa[2][2];
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt) {
-    accW[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    accU[nt] = accW[nt];
-  }
+  for (int d = 0; d < 2; ++d)
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int t = 16 * (2 * tp + m) + l16;
+      qa[d][m] = *reinterpret_cast<const float4 *>(qc + (int64_t)min(t, nl) * qk_tok +
+                                                   16 * (2 * kp + d) + 4 * kg);
+    }
+  f32x4 accW[2][2], accU[2][2];
+#pragma unroll
+  for (int d = 0; d < 2; ++d)
+#pragma unroll
+    for (int m = 0; m < 2; ++m) accW[d][m] = accU[d][m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
-    const Frag ft = frag(r3h, r3l, P72, 16 * w + l16, 32 * ks + 8 * kg);
+    Frag bt1[2], bt2[2];
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      accW[nt] = mfma3(ft, frag(r1h, r1l, P72, 16 * nt + l16, 32 * ks + 8 * kg), accW[nt]);
-      accU[nt] = mfma3(ft, frag(r2h, r2l, P72, 16 * nt + l16, 32 * ks + 8 * kg), accU[nt]);
+    for (int m = 0; m < 2; ++m) {
+      bt1[m] = frag_pi(t1h, t1l, PS, 16 * (2 * tp + m) + l16, 32 * ks, kg);
+      bt2[m] = frag_pi(t2h, t2l, PS, 16 * (2 * tp + m) + l16, 32 * ks, kg);
     }
-  }
-  __syncthreads();  // R1, R2, R3 are rewritten below
-  {
-    float *utg = reinterpret_cast<float *>(wc + WS_U);
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const int col = 16 * nt + l16, t = 16 * w + 4 * kg;
-      store4_split(r1h + col * P72 + t, r1l + col * P72 + t, accW[nt][0], accW[nt][1],
-                   accW[nt][2], accW[nt][3]);
-      store4_split(r2h + col * P72 + t, r2l + col * P72 + t, accU[nt][0], accU[nt][1],
-                   accU[nt][2], accU[nt][3]);
-      *reinterpret_cast<float4 *>(utg + acc_off(nt, w, lane)) =
-          make_float4(accU[nt][0], accU[nt][1], accU[nt][2], accU[nt][3]);
+    for (int d = 0; d < 2; ++d) {
+      const Frag ak = frag_tr(kh, klo, PR, 32 * ks, 16 * (2 * kp + d), kg, l16);
+      const Frag av = frag_tr(qh, qlo, PR, 32 * ks, 16 * (2 * kp + d), kg, l16);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        u16 hh, ll;
-        split(accW[nt][r], hh, ll);
-        sth[(t + r) * P136 + col] = hh;
-        stl[(t + r) * P136 + col] = ll;
+      for (int m = 0; m < 2; ++m) {
+        accW[d][m] = mfma3(ak, bt1[m], accW[d][m]);
+        accU[d][m] = mfma3(av, bt2[m], accU[d][m]);
       }
     }
   }
-  __syncthreads();
-  {  // staged W -> workspace in fragment order, 16 bytes per thread per step
+  {  // W fragments and Ut tiles -> workspace
     u16 *wg = reinterpret_cast<u16 *>(wc + WS_W);
-    for (int it = tid; it < 4 * 4 * 2 * 64; it += 256) {
-      const int ln = it & 63, plane = (it >> 6) & 1, ks = (it >> 7) & 3, m = it >> 9;
-      const u16 *src = (plane ? stl : sth) + (16 * m + (ln & 15)) * P136 + 32 * ks + 8 * (ln >> 4);
-      *reinterpret_cast<uint4 *>(wg + frag_off(m, ks, 4, plane, ln)) =
-          *reinterpret_cast<const uint4 *>(src);
+    float *ug = reinterpret_cast<float *>(wc + WS_U);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const float xw[8] = {accW[0][m][0], accW[0][m][1], accW[0][m][2], accW[0][m][3],
+                           accW[1][m][0], accW[1][m][1], accW[1][m][2], accW[1][m][3]};
+      store8_split(wg + frag_off(2 * tp + m, kp, 4, 0, lane),
+                   wg + frag_off(2 * tp + m, kp, 4, 1, lane), xw);
+#pragma unroll
+      for (int d = 0; d < 2; ++d)
+        *reinterpret_cast<float4 *>(ug + acc_off(2 * kp + d, 2 * tp + m, lane)) =
+            make_float4(accU[d][m][0], accU[d][m][1], accU[d][m][2], accU[d][m][3]);
     }
   }
-
-  // 6. Q' = e^G Q - (L o QK^T) W and Oi = (L o QK^T) Ut
-  f32x4 accQ[8], accO[8];
+  __syncthreads();  // K and V tiles are rewritten below
+  // W rows [s][i] into the K tile, Ut rows [s][j] into the Q/V tile
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt) {
-    accQ[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    accO[nt] = accQ[nt];
-  }
+  for (int d = 0; d < 2; ++d)
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int row = 16 * (2 * tp + m) + l16, col = 16 * (2 * kp + d) + 4 * kg;
+      store4_split(kh + row * PR + col, klo + row * PR + col, accW[d][m][0], accW[d][m][1],
+                   accW[d][m][2], accW[d][m][3]);
+      store4_split(qh + row * PR + col, qlo + row * PR + col, accU[d][m][0], accU[d][m][1],
+                   accU[d][m][2], accU[d][m][3]);
+    }
+  __syncthreads();
+
+  // S6. Q'^T = e^G Q^T - W^T (LQK)^T and Oi^T = Ut^T (LQK)^T
+  f32x4 accQ[2][2], accO[2][2];
+#pragma unroll
+  for (int d = 0; d < 2; ++d)
+#pragma unroll
+    for (int m = 0; m < 2; ++m) accQ[d][m] = accO[d][m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
-    const Frag fl = frag(r5h, r5l, P72, 16 * w + l16, 32 * ks + 8 * kg);
+    Frag bl[2];
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      accQ[nt] = mfma3(fl, frag(r1h, r1l, P72, 16 * nt + l16, 32 * ks + 8 * kg), accQ[nt]);
-      accO[nt] = mfma3(fl, frag(r2h, r2l, P72, 16 * nt + l16, 32 * ks + 8 * kg), accO[nt]);
-    }
-  }
-  __syncthreads();  // staging reads of W are done before Q' overwrites it
-  {
-    float *oig = reinterpret_cast<float *>(wc + WS_O);
+    for (int m = 0; m < 2; ++m) bl[m] = frag_pi(lqh, lql, PS, 16 * (2 * tp + m) + l16, 32 * ks, kg);
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const int col = 16 * nt + l16, t = 16 * w + 4 * kg;
-      *reinterpret_cast<float4 *>(oig + acc_off(nt, w, lane)) =
-          make_float4(accO[nt][0], accO[nt][1], accO[nt][2], accO[nt][3]);
-      float ql[4];
+    for (int d = 0; d < 2; ++d) {
+      const Frag aw = frag_tr(kh, klo, PR, 32 * ks, 16 * (2 * kp + d), kg, l16);
+      const Frag au = frag_tr(qh, qlo, PR, 32 * ks, 16 * (2 * kp + d), kg, l16);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ql[r] = qc[(int64_t)min(t + r, nl) * qk_tok + col];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float qv = (t + r) < n ? ql[r] : 0.0f;
-        u16 hh, ll;
-        split(sEG[t + r] * qv - accQ[nt][r], hh, ll);
-        sth[(t + r) * P136 + col] = hh;
-        stl[(t + r) * P136 + col] = ll;
+      for (int m = 0; m < 2; ++m) {
+        accQ[d][m] = mfma3(aw, bl[m], accQ[d][m]);
+        accO[d][m] = mfma3(au, bl[m], accO[d][m]);
       }
     }
   }
-  __syncthreads();
-  {  // staged Q' -> workspace in fragment order, 16 bytes per thread per step
+  {
     u16 *qg = reinterpret_cast<u16 *>(wc + WS_Q);
-    for (int it = tid; it < 4 * 4 * 2 * 64; it += 256) {
-      const int ln = it & 63, plane = (it >> 6) & 1, ks = (it >> 7) & 3, m = it >> 9;
-      const u16 *src = (plane ? stl : sth) + (16 * m + (ln & 15)) * P136 + 32 * ks + 8 * (ln >> 4);
-      *reinterpret_cast<uint4 *>(qg + frag_off(m, ks, 4, plane, ln)) =
-          *reinterpret_cast<const uint4 *>(src);
+    float *og = reinterpret_cast<float *>(wc + WS_O);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int t = 16 * (2 * tp + m) + l16;
+      const float eg = t < n ? sEG[t] : 0.0f;
+      float xq[8];
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const float4 qv = qa[d][m];
+        xq[4 * d + 0] = eg * qv.x - accQ[d][m][0];
+        xq[4 * d + 1] = eg * qv.y - accQ[d][m][1];
+        xq[4 * d + 2] = eg * qv.z - accQ[d][m][2];
+        xq[4 * d + 3] = eg * qv.w - accQ[d][m][3];
+        *reinterpret_cast<float4 *>(og + acc_off(2 * kp + d, 2 * tp + m, lane)) =
+            make_float4(accO[d][m][0], accO[d][m][1], accO[d][m][2], accO[d][m][3]);
+      }
+      store8_split(qg + frag_off(2 * tp + m, kp, 4, 0, lane),
+                   qg + frag_off(2 * tp + m, kp, 4, 1, lane), xq);
     }
   }
   if (tid == 0) *reinterpret_cast<float *>(wc + WS_G) = sEG[CH - 1];
 }
 
 // ----------------------------------------------------------------------------- phase B
-// Eight waves per workgroup.  Wave w computes, per chunk:
-//   w < 4 : P = W S for token rows 16(w&3)..+15, then U = Ut - P  (shared via LDS)
-//   w >= 4: R = Q' S for token rows 16(w&3)..+15, then y = scale (R + Oi)
-//   all   : state rows 16w..16w+15 of the block, S <- e^{G_n} S + K'^T U.
-// Each wave's operands for one chunk are ~52 VGPRs; two chunks are kept in
-// flight (prefetch distance 2).
+// One workgroup (8 waves) per (sequence, head, block b of 16 value columns),
+// computing the transposed recurrence on the state block S^T[j][i] (j in the
+// block, i over all 128 keys):
+//   P^T = S^T W^T,  U^T = Ut^T - P^T,  y^T = scale (S^T Q'^T + Oi^T),
+//   S^T <- e^{G_n} S^T + U^T K'
+// Wave w owns key tile w of the state (one accumulator) and token tile w & 3
+// of P^T (w < 4) or of y^T (w >= 4).  S and U travel through LDS as row-major
+// [key][j] / [token][j] tiles and are read back by transpose reads.
 struct ChunkOps {
-  Frag a[4];      // W or Q' rows of this wave; slot j = k-step (j + blk) mod 4 over keys
-  Frag k[2];      // K'^T rows 16w..; slot j = k-step (j + blk) mod 2 over tokens
-  float4 add;     // Ut (P waves) or Oi (R waves) for this lane's 4 tokens
-  float gam;      // e^{G_n}
+  Frag b[4];     // W (P waves) or Q' (y waves) fragments of token tile w & 3, 4 key k-steps
+  Frag k[2];     // K'^T fragments of key tile w, 2 token k-steps
+  float4 add;    // Ut (P waves) or Oi (y waves) accumulator tile (b, w & 3)
+  float gam;     // e^{G_n}
 };
 
-__device__ __forceinline__ void load_chunk(ChunkOps &o, const unsigned char *wc, int w, int l16,
-                                           int kg, int blk) {
+__device__ __forceinline__ void load_chunk(ChunkOps &o, const unsigned char *wc, int w, int lane,
+                                           int blk) {
   const bool pw = w < 4;
-  const int lane = kg * 16 + l16;
-  const u16 *ag = reinterpret_cast<const u16 *>(wc + (pw ? WS_W : WS_Q));
+  const u16 *bg = reinterpret_cast<const u16 *>(wc + (pw ? WS_W : WS_Q));
   const u16 *kgp = reinterpret_cast<const u16 *>(wc + WS_K);
-  // The 8 workgroups of a head read the same lines at about the same time;
-  // slot j holds k-step (j + blk) mod n, so their requests start on different
-  // lines.  The scan pairs each slot with the matching B fragment.
 #pragma unroll
-  for (int j = 0; j < 4; ++j) o.a[j] = frag_ws(ag, w & 3, (j + blk) & 3, 4, lane);
+  for (int ks = 0; ks < 4; ++ks) o.b[ks] = frag_ws(bg, w & 3, ks, 4, lane);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) o.k[j] = frag_ws(kgp, w, (j + blk) & 1, 2, lane);
+  for (int ks = 0; ks < 2; ++ks) o.k[ks] = frag_ws(kgp, w, ks, 2, lane);
   const float *addp = reinterpret_cast<const float *>(wc + (pw ? WS_U : WS_O));
   o.add = *reinterpret_cast<const float4 *>(addp + acc_off(blk, w & 3, lane));
   o.gam = *reinterpret_cast<const float *>(wc + WS_G);
 }
 
-constexpr int SP = DK + 8;     // pitch of the S^T block in LDS (bf16)
-constexpr int UP = CH + 8;     // pitch of the U^T block in LDS (bf16)
+constexpr int SPB = 24;   // pitch (bf16) of the [128][16] S tile and the [64][16] U tile
 
 __device__ __forceinline__ void scan_chunk(const ChunkOps &o, f32x4 &st, u16 *ssh, u16 *ssl,
                                            u16 *suh, u16 *sul, float *yc, int64_t y_tok, int n,
-                                           float scale, int w, int l16, int kg, int rot) {
-  // state tile -> LDS as S^T [j][i] (the B operand of W S and Q' S)
-  store4_split(ssh + l16 * SP + 16 * w + 4 * kg, ssl + l16 * SP + 16 * w + 4 * kg, st[0], st[1],
-               st[2], st[3]);
+                                           float scale, int w, int l16, int kg) {
+  // state tile (values 4kg+r of key 16w + l16) -> S rows [i][j]
+  store4_split(ssh + (16 * w + l16) * SPB + 4 * kg, ssl + (16 * w + l16) * SPB + 4 * kg, st[0],
+               st[1], st[2], st[3]);
   __syncthreads();
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    acc = mfma3(o.a[j], frag(ssh, ssl, SP, l16, 32 * ((j + rot) & 3) + 8 * kg), acc);
-  const int t = 16 * (w & 3) + 4 * kg;
+  for (int ks = 0; ks < 4; ++ks)
+    acc = mfma3(frag_tr(ssh, ssl, SPB, 32 * ks, 0, kg, l16), o.b[ks], acc);
+  const int t = 16 * (w & 3) + l16;   // this lane's token; values 4kg + r
   if (w < 4) {
-    store4_split(suh + l16 * UP + t, sul + l16 * UP + t, o.add.x - acc[0], o.add.y - acc[1],
-                 o.add.z - acc[2], o.add.w - acc[3]);
-  } else {
-    const float yo[4] = {scale * (acc[0] + o.add.x), scale * (acc[1] + o.add.y),
-                         scale * (acc[2] + o.add.z), scale * (acc[3] + o.add.w)};
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (t + r < n) yc[(int64_t)(t + r) * y_tok] = yo[r];
+    store4_split(suh + t * SPB + 4 * kg, sul + t * SPB + 4 * kg, o.add.x - acc[0],
+                 o.add.y - acc[1], o.add.z - acc[2], o.add.w - acc[3]);
+  } else if (t < n) {
+    *reinterpret_cast<float4 *>(yc + (int64_t)t * y_tok + 4 * kg) =
+        make_float4(scale * (acc[0] + o.add.x), scale * (acc[1] + o.add.y),
+                    scale * (acc[2] + o.add.z), scale * (acc[3] + o.add.w));
   }
   __syncthreads();
   st = st * o.gam;
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
-    st = mfma3(o.k[j], frag(suh, sul, UP, l16, 32 * ((j + rot) & 1) + 8 * kg), st);
+  for (int ks = 0; ks < 2; ++ks) st = mfma3(frag_tr(suh, sul, SPB, 32 * ks, 0, kg, l16), o.k[ks], st);
 }
 
 __global__ __launch_bounds__(512) void k_chunk_scan(
     float *__restrict__ state, int64_t st_seq, const unsigned char *__restrict__ ws,
     float *__restrict__ y, int64_t y_tok, int64_t y_seq, int n_tok, int n_chunks, int H,
     float scale) {
-  __shared__ __attribute__((aligned(16))) u16 ssh[NBLK * SP], ssl[NBLK * SP];
-  __shared__ __attribute__((aligned(16))) u16 suh[NBLK * UP], sul[NBLK * UP];
+  __shared__ __attribute__((aligned(16))) u16 ssh[DK * SPB], ssl[DK * SPB];
+  __shared__ __attribute__((aligned(16))) u16 suh[CH * SPB], sul[CH * SPB];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
   // XCD-aware order: consecutive workgroup ids go to different XCDs, so map
   // them so that the 8 blocks of one head land on the same XCD (shared L2).
@@ -521,17 +595,16 @@ __global__ __launch_bounds__(512) void k_chunk_scan(
   const int unit = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   const int blk = unit % NVB, sh = unit / NVB, h = sh % H, s = sh / H;
 
-  // state rows 16w + 4kg + r, column blk*16 + l16 (value-major storage)
-  float *sp = state + s * st_seq + (int64_t)h * DK * DV + (int64_t)(blk * NBLK + l16) * DK +
-              16 * w + 4 * kg;
-  const float4 s4 = *reinterpret_cast<const float4 *>(sp);
-  f32x4 st = {s4.x, s4.y, s4.z, s4.w};
+  // state element (value j = 16 blk + 4kg + r, key i = 16w + l16), value-major
+  float *sp = state + s * st_seq + (int64_t)h * DK * DV +
+              (int64_t)(blk * NBLK + 4 * kg) * DK + 16 * w + l16;
+  f32x4 st = {sp[0], sp[DK], sp[2 * DK], sp[3 * DK]};
   const unsigned char *wh = ws + ((size_t)s * H + h) * n_chunks * WS_CHUNK;
-  float *yh = y + s * y_seq + (int64_t)h * DV + blk * NBLK + l16;
+  float *yh = y + s * y_seq + (int64_t)h * DV + blk * NBLK;
   auto chunk_ptr = [&](int c) { return wh + (size_t)min(c, n_chunks - 1) * WS_CHUNK; };
   auto run = [&](const ChunkOps &o, int c) {
     scan_chunk(o, st, ssh, ssl, suh, sul, yh + (int64_t)c * CH * y_tok, y_tok,
-               min(CH, n_tok - c * CH), scale, w, l16, kg, blk);
+               min(CH, n_tok - c * CH), scale, w, l16, kg);
   };
 
   // Two chunks in flight: a chunk's operands are requested two chunks ahead.
@@ -539,15 +612,18 @@ __global__ __launch_bounds__(512) void k_chunk_scan(
   // loop has no tail; a tail would make the compiler copy the operand
   // registers at the loop head, which waits for every load in flight.
   ChunkOps a, b;
-  load_chunk(a, chunk_ptr(0), w, l16, kg, blk);
-  load_chunk(b, chunk_ptr(1), w, l16, kg, blk);
+  load_chunk(a, chunk_ptr(0), w, lane, blk);
+  load_chunk(b, chunk_ptr(1), w, lane, blk);
   for (int c = 0; c < n_chunks; c += 2) {
     run(a, c);
-    load_chunk(a, chunk_ptr(c + 2), w, l16, kg, blk);
+    load_chunk(a, chunk_ptr(c + 2), w, lane, blk);
     run(b, c + 1);
-    load_chunk(b, chunk_ptr(c + 3), w, l16, kg, blk);
+    load_chunk(b, chunk_ptr(c + 3), w, lane, blk);
   }
-  *reinterpret_cast<float4 *>(sp) = make_float4(st[0], st[1], st[2], st[3]);
+  sp[0] = st[0];
+  sp[DK] = st[1];
+  sp[2 * DK] = st[2];
+  sp[3 * DK] = st[3];
 }
 
 }  // namespace
@@ -566,7 +642,7 @@ int launch_recur_chunked(const RecurArgs &a, int chunk, void *ws, size_t ws_byte
   if (ws_bytes < chunked_workspace_bytes(a.n_seq, a.n_tok, a.H, a.Hk, a.S, chunk))
     return GDN_ERR_WORKSPACE;
   unsigned char *wsb = static_cast<unsigned char *>(ws);
-  int rc = launch_kernel(k_chunk_prep, dim3(n_chunks, a.H, a.n_seq), dim3(256), 0, stream, a.q,
+  int rc = launch_kernel(k_chunk_prep, dim3(n_chunks, a.H, a.n_seq), dim3(512), 0, stream, a.q,
                          a.k, a.qk_tok, a.qk_seq, a.v, a.v_tok, a.v_seq, a.g, a.beta, wsb,
                          a.n_tok, n_chunks, a.H, a.Hk);
   if (rc != GDN_OK) return rc;
