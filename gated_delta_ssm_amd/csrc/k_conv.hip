@@ -39,6 +39,20 @@ __device__ __forceinline__ float conv_position(const float (&w)[D], const float 
   return silu(acc);
 }
 
+// Taps of channel ch (clamped to a valid channel by the caller): one 16-byte
+// load when there are 4 taps.  Loads are never behind a branch: a branch
+// would make the compiler wait for every load in flight where it rejoins.
+template <int D>
+__device__ __forceinline__ void load_taps(const float *__restrict__ w, int ch, float (&wt)[D]) {
+  if constexpr (D == 4) {
+    const float4 t = *reinterpret_cast<const float4 *>(w + (int64_t)ch * 4);
+    wt[0] = t.x; wt[1] = t.y; wt[2] = t.z; wt[3] = t.w;
+  } else {
+#pragma unroll
+    for (int j = 0; j < D; ++j) wt[j] = w[(int64_t)ch * D + j];
+  }
+}
+
 // 1 / sqrt(sum over the lane's L2 head of o^2 + eps); LPH lanes per head.
 template <int CPL, int LPH>
 __device__ __forceinline__ float l2_scale(const float (&o)[CPL], float eps) {
@@ -65,16 +79,18 @@ __global__ __launch_bounds__(256) void k_conv_step(
   out += s * o_seq;
   hist += s * h_seq;
 
+  // lanes past the last channel compute on channel C-1 and store nothing
   float wt[CPL][D], win[CPL][D];
   bool ok[CPL];
+  int chc[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     const int ch = blk0 + lane + 64 * c;
     ok[c] = ch < C;
+    chc[c] = min(ch, C - 1);
+    load_taps<D>(w, chc[c], wt[c]);
 #pragma unroll
-    for (int j = 0; j < D; ++j) wt[c][j] = ok[c] ? w[(int64_t)ch * D + j] : 0.0f;
-#pragma unroll
-    for (int j = 0; j < DH; ++j) win[c][j] = ok[c] ? hist[(int64_t)ch * DH + j] : 0.0f;
+    for (int j = 0; j < DH; ++j) win[c][j] = hist[(int64_t)chc[c] * DH + j];
   }
   const bool qk = LPH > 0 && blk0 + lane < qk_channels;
 
@@ -82,8 +98,7 @@ __global__ __launch_bounds__(256) void k_conv_step(
     float o[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      const int ch = blk0 + lane + 64 * c;
-      win[c][DH] = ok[c] ? x[(int64_t)t * x_tok + ch] : 0.0f;
+      win[c][DH] = x[(int64_t)t * x_tok + chc[c]];
       o[c] = conv_position<D>(wt[c], win[c]);
 #pragma unroll
       for (int j = 0; j < DH; ++j) win[c][j] = win[c][j + 1];  // roll with the raw input
@@ -137,21 +152,27 @@ __global__ __launch_bounds__(256) void k_conv_tp(
   out += s * o_seq;
   hist += s * h_seq;
 
+  // lanes past the last channel compute on channel C-1 and store nothing;
+  // both window sources are loaded and one is selected (no load behind a
+  // branch)
   float wt[CPL][D], win[CPL][D], old[CPL][DH];
   bool ok[CPL];
+  int chc[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     const int ch = blk0 + lane + 64 * c;
     ok[c] = ch < C;
-#pragma unroll
-    for (int j = 0; j < D; ++j) wt[c][j] = ok[c] ? w[(int64_t)ch * D + j] : 0.0f;
+    chc[c] = min(ch, C - 1);
+    load_taps<D>(w, chc[c], wt[c]);
 #pragma unroll
     for (int j = 0; j < DH; ++j) {
-      // window slot j before position t0 holds position p = t0 - DH + j
+      // window slot j before position t0 holds position p = t0 - DH + j,
+      // which is before position 0 only in tile 0 (TT >= DH), where it is
+      // history slot j
       const int p = t0 - DH + j;
-      old[c][j] = (t0 == 0 && ok[c]) ? hist[(int64_t)ch * DH + j] : 0.0f;
-      win[c][j] = !ok[c] ? 0.0f : (p < 0 ? hist[(int64_t)ch * DH + (p + DH)]
-                                         : x[(int64_t)p * x_tok + ch]);
+      old[c][j] = hist[(int64_t)chc[c] * DH + j];
+      const float xp = x[(int64_t)max(p, 0) * x_tok + chc[c]];
+      win[c][j] = t0 == 0 ? old[c][j] : xp;
     }
   }
   const bool qk = LPH > 0 && blk0 + lane < qk_channels;
@@ -160,8 +181,7 @@ __global__ __launch_bounds__(256) void k_conv_tp(
     float o[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      const int ch = blk0 + lane + 64 * c;
-      win[c][DH] = ok[c] ? x[(int64_t)t * x_tok + ch] : 0.0f;
+      win[c][DH] = x[(int64_t)t * x_tok + chc[c]];
       o[c] = conv_position<D>(wt[c], win[c]);
 #pragma unroll
       for (int j = 0; j < DH; ++j) win[c][j] = win[c][j + 1];
@@ -185,8 +205,14 @@ __global__ __launch_bounds__(256) void k_conv_tp(
         const int ch = blk0 + lane + 64 * c;
 #pragma unroll
         for (int j = 0; j < DH; ++j) {
+          // position p = n_tok - DH + j; before position 0 it is old slot p + DH
           const int p = n_tok - DH + j;
-          hist[(int64_t)ch * DH + j] = p < 0 ? old[c][p + DH] : x[(int64_t)p * x_tok + ch];
+          const float xp = x[(int64_t)max(p, 0) * x_tok + ch];
+          float hv = xp;
+#pragma unroll
+          for (int k2 = 0; k2 < DH; ++k2)
+            if (p + DH == k2) hv = old[c][k2];
+          hist[(int64_t)ch * DH + j] = hv;
         }
       }
   }
