@@ -35,31 +35,42 @@ struct RowMap {
   __device__ static int off(int l16, int m) { return S >= 64 ? 64 * m + 4 * l16 : 2 * l16; }
 };
 
-template <int S>
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// NT selects non-temporal accesses: the state streams through once per call,
+// so its lines are not kept in the caches, which leaves them to k, q and v,
+// read by every wave of a head.
+template <int S, bool NT = false>
 __device__ __forceinline__ void load_row(const float *p, int l16, float (&r)[S / 16]) {
   using M = RowMap<S>;
 #pragma unroll
   for (int m = 0; m < M::NV; ++m) {
     if constexpr (M::VEC == 4) {
-      const float4 t = *reinterpret_cast<const float4 *>(p + M::off(l16, m));
+      const f32x4 *a = reinterpret_cast<const f32x4 *>(p + M::off(l16, m));
+      const f32x4 t = NT ? __builtin_nontemporal_load(a) : *a;
       r[4 * m] = t.x; r[4 * m + 1] = t.y; r[4 * m + 2] = t.z; r[4 * m + 3] = t.w;
     } else {
-      const float2 t = *reinterpret_cast<const float2 *>(p + M::off(l16, m));
+      const f32x2 *a = reinterpret_cast<const f32x2 *>(p + M::off(l16, m));
+      const f32x2 t = NT ? __builtin_nontemporal_load(a) : *a;
       r[2 * m] = t.x; r[2 * m + 1] = t.y;
     }
   }
 }
 
-template <int S>
+template <int S, bool NT = false>
 __device__ __forceinline__ void store_row(float *p, int l16, const float (&r)[S / 16]) {
   using M = RowMap<S>;
 #pragma unroll
   for (int m = 0; m < M::NV; ++m) {
     if constexpr (M::VEC == 4) {
-      *reinterpret_cast<float4 *>(p + M::off(l16, m)) =
-          make_float4(r[4 * m], r[4 * m + 1], r[4 * m + 2], r[4 * m + 3]);
+      f32x4 *a = reinterpret_cast<f32x4 *>(p + M::off(l16, m));
+      const f32x4 t = {r[4 * m], r[4 * m + 1], r[4 * m + 2], r[4 * m + 3]};
+      if constexpr (NT) __builtin_nontemporal_store(t, a); else *a = t;
     } else {
-      *reinterpret_cast<float2 *>(p + M::off(l16, m)) = make_float2(r[2 * m], r[2 * m + 1]);
+      f32x2 *a = reinterpret_cast<f32x2 *>(p + M::off(l16, m));
+      const f32x2 t = {r[2 * m], r[2 * m + 1]};
+      if constexpr (NT) __builtin_nontemporal_store(t, a); else *a = t;
     }
   }
 }
@@ -120,7 +131,7 @@ __global__ __launch_bounds__(256) void k_recur_decode(
 
   float st[RG][EPL];
 #pragma unroll
-  for (int r = 0; r < RG; ++r) load_row<S>(st_base + (int64_t)(row0 + 4 * r) * S, l16, st[r]);
+  for (int r = 0; r < RG; ++r) load_row<S, true>(st_base + (int64_t)(row0 + 4 * r) * S, l16, st[r]);
 
   const float *qs = q + s * qk_seq + (int64_t)hk * S;
   const float *ks = k + s * qk_seq + (int64_t)hk * S;
@@ -145,11 +156,11 @@ __global__ __launch_bounds__(256) void k_recur_decode(
     if (snap != nullptr && t < n_tok - 1) {
       float *sp = snap + s * sn_seq + (int64_t)t * H * S * S + (int64_t)h * S * S;
 #pragma unroll
-      for (int r = 0; r < RG; ++r) store_row<S>(sp + (int64_t)(row0 + 4 * r) * S, l16, st[r]);
+      for (int r = 0; r < RG; ++r) store_row<S, true>(sp + (int64_t)(row0 + 4 * r) * S, l16, st[r]);
     }
   }
 #pragma unroll
-  for (int r = 0; r < RG; ++r) store_row<S>(st_base + (int64_t)(row0 + 4 * r) * S, l16, st[r]);
+  for (int r = 0; r < RG; ++r) store_row<S, true>(st_base + (int64_t)(row0 + 4 * r) * S, l16, st[r]);
 }
 
 namespace {
@@ -170,10 +181,10 @@ int run_recur(const RecurArgs &a, hipStream_t stream) {
 
 template <int S>
 int pick_rows(const RecurArgs &a, hipStream_t stream) {
-  // Enough waves to cover 256 CUs several times over before packing more
-  // rows (and more bytes in flight) into each wave.
+  // Two rows per lane once there are enough waves to cover 256 CUs several
+  // times over; beyond two, the extra bytes in flight per wave cost more in
+  // occupancy than they gain (measured at 64 sequences x 48 heads, S = 128).
   const int64_t rows = (int64_t)a.n_seq * a.H * S;
-  if (rows / 16 >= 8192) return run_recur<S, 4>(a, stream);
   if (rows / 8 >= 4096) return run_recur<S, 2>(a, stream);
   return run_recur<S, 1>(a, stream);
 }
