@@ -179,7 +179,41 @@ def main():
     hot_ms = float(np.mean([a.elapsed_time(b) for a, b in hot_ev]))
     achieved = by["recurrence"] / (rec_ms * 1e-3) / 1e9
 
+    # back-to-back bursts: events around 50 launches, 10 bursts, median per launch
+    def burst(launch, n_launch=50, reps=10):
+        launch(0)
+        torch.cuda.synchronize()
+        per = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True); b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for i in range(n_launch):
+                launch(i)
+            b.record(stream)
+            b.synchronize()
+            per.append(a.elapsed_time(b) / n_launch)
+        return float(np.median(per))
+
+    bursts = {
+        "recurrence_rotated_pools": burst(lambda i: gdn.gdn_recurrence_decode(
+            pools[i % len(pools)], qv, kv, vv, g.view(n, 1, H), cu["beta"], y, scale=wl.scale)),
+        "conv_step_rotated_hist": burst(lambda i: gdn.gdn_conv1d_silu_l2norm(
+            x, cu["conv_w"], hists[i % len(hists)], conv_out, qk_channels=wl.qk_channels,
+            head_dim=wl.head_dim, l2_eps=wl.l2_eps)),
+        "norm": burst(lambda i: gdn.gdn_gated_rmsnorm(y.view(n, H, S), cu["norm_w"], z, nout,
+                                                       eps=wl.norm_eps)),
+        "gate": burst(lambda i: gdn.gdn_decay_gate(cu["alpha"], cu["dt"], cu["a"], g)),
+    }
     del pools, hists
+    torch.cuda.empty_cache()
+
+    # achievable copy bandwidth: torch's device copy of the state's size (read +
+    # write = the recurrence's state bytes), sources rotated like the state pools
+    srcs = [torch.ones(n * H * S * S, device=dev) for _ in range(args.pools)]
+    dst = torch.empty_like(srcs[0])
+    copy_ms = burst(lambda i: dst.copy_(srcs[i % len(srcs)]))
+    copy_gbs = by["state"] / (copy_ms * 1e-3) / 1e9
+    del srcs, dst
     torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- prefill pass
@@ -284,6 +318,12 @@ def main():
             "recurrence_ms_mall_hot": hot_ms,
             "recurrence_state_GBs_mall_hot": by["state"] / (hot_ms * 1e-3) / 1e9,
             "step_frac_of_hbm": value / HBM_PEAK_GBS,
+            "burst_ms_per_launch": bursts,
+            "recurrence_burst_GBs": by["recurrence"] / (bursts["recurrence_rotated_pools"] * 1e-3) / 1e9,
+            "copy_peak": {"what": "torch device copy, 192 MiB per launch, sources rotated, "
+                                  "50-launch bursts", "ms": copy_ms, "GBs": copy_gbs,
+                          "frac_of_hbm": copy_gbs / HBM_PEAK_GBS},
+            "recurrence_frac_of_copy_peak": achieved / copy_gbs,
         },
         "prefill": prefill,
         "cpu_baseline": cpu,
@@ -301,10 +341,7 @@ def cpu_baseline(wl, inp, seconds: float) -> dict:
         oracle.build()
     n, H, S, C = wl.n_seq, wl.H, wl.S, wl.conv_dim
     x = inp["x"][:, :, :C]
-    times = []
-    t_end = time.perf_counter() + seconds
-    while True:
-        t0 = time.perf_counter()
+    def step():
         g = oracle.decay_gate(inp["alpha"], inp["dt"], inp["a"])
         out, _, _ = oracle.conv1d_silu_l2norm(x, inp["conv_w"], inp["conv_hist"],
                                               wl.qk_channels, wl.head_dim, wl.l2_eps)
@@ -315,17 +352,40 @@ def cpu_baseline(wl, inp, seconds: float) -> dict:
         y, _, _ = oracle.recurrence_seq(inp["state"], q, k, v, g.reshape(n, 1, H), inp["beta"],
                                         wl.scale)
         oracle.gated_rmsnorm(y.reshape(n, H, S), inp["norm_w"], inp["z"], wl.norm_eps)
+
+    times = []
+    t_end = time.perf_counter() + seconds
+    while True:
+        t0 = time.perf_counter()
+        step()
         times.append(time.perf_counter() - t0)
         if time.perf_counter() > t_end and len(times) >= 3:
             break
     med = float(np.median(times))
+    threads = oracle.max_threads()
+    # the same step on one thread, fewer repetitions
+    oracle.set_threads(1)
+    one = []
+    try:
+        t_end = time.perf_counter() + seconds / 2
+        while len(one) < 3 or time.perf_counter() < t_end:
+            t0 = time.perf_counter()
+            step()
+            one.append(time.perf_counter() - t0)
+    finally:
+        oracle.set_threads(threads)
+    model = next((l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo")
+                  if l.startswith("model name")), "unknown")
     state_bytes = 2 * n * H * S * S * 4
-    return {"value": state_bytes / med / 1e9, "unit": "GB/s", "cores": oracle.max_threads(),
+    return {"value": state_bytes / med / 1e9, "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"whole decode64 step (gate, conv, sequential fp64 recurrence, norm), "
                       f"median of {len(times)} runs over ~{seconds:.0f} s; state bytes of the "
                       f"fp32 step divided by the oracle's time",
-            "ms_per_step": med * 1e3}
+            "ms_per_step": med * 1e3,
+            "one_thread": {"value": state_bytes / float(np.median(one)) / 1e9,
+                           "ms_per_step": float(np.median(one)) * 1e3, "runs": len(one)},
+            "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": model}
 
 
 if __name__ == "__main__":
