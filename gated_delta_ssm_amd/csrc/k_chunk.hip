@@ -202,7 +202,7 @@ __device__ __forceinline__ int acc_off(int d, int m, int lane) {
 //   L_Q : Q rows [t][i] -> V rows  -> later Ut rows [s][j]
 //   L_T : T1 = T diag(beta e^G), T2 = T diag(beta)  [t][s]
 //   L_L : L o Q K^T                 [t][s]
-//   L_A : A, then T in place (fp32 [64][68]);  L_S: inverse scratch
+//   L_A : A, then T in place (fp32 [64][68]);  L_S: four 16x16 blocks (pitch XP) of the inverse
 //   L_G : G, beta, e^G, e^{G_n - G}
 // The products are computed transposed (feature index as the MFMA row):
 //   W^T = K^T T1^T,  Ut^T = V^T T2^T,  Q'^T = e^G Q^T - W^T (LQK)^T,
@@ -220,26 +220,165 @@ constexpr int L_T = L_Q + TILE128;
 constexpr int L_L = L_T + 2 * TILE64;
 constexpr int L_A = L_L + TILE64;
 constexpr int L_S = L_A + CH * PA * 4;
-constexpr int L_G = L_S + 3 * 256 * 4;
+constexpr int XP = 17;   // pitch (fp32) of the inverse's scratch blocks
+constexpr int L_G = L_S + 4 * 16 * XP * 4;
 constexpr int L_TOTAL = L_G + 4 * CH * 4;
 static_assert(L_TOTAL <= 160 * 1024, "phase A LDS fits one CU");
 
+// Lower 16x16 tiles of K K^T (tile index jt < 10: A = beta_t e^{G_t - G_s} k_t.k_s,
+// strictly lower) and of Q K^T (jt >= 10: e^{G_t - G_s} q_t.k_s, diagonal
+// included, stored as bf16 hi/lo): this wave's NJ tiles w, w + 8, w + 16.
+template <int NJ>
+__device__ __forceinline__ void lower_tiles(int w, const u16 *kh, const u16 *klo, const u16 *qh,
+                                            const u16 *qlo, float *sA, u16 *lqh, u16 *lql,
+                                            const float *sG, const float *sBeta, int l16, int kg) {
+  bool qk[NJ];
+  int ti[NJ], tj[NJ];
+  f32x4 acc[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int job = w + 8 * j;
+    qk[j] = job >= 10;
+    const int jt = qk[j] ? job - 10 : job;
+    ti[j] = jt < 1 ? 0 : jt < 3 ? 1 : jt < 6 ? 2 : 3;   // lower-tile index -> (ti, tj)
+    tj[j] = jt - ti[j] * (ti[j] + 1) / 2;
+    acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    Frag fa[NJ], fb[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      fa[j] = frag(qk[j] ? qh : kh, qk[j] ? qlo : klo, PR, 16 * ti[j] + l16, 32 * ks + 8 * kg);
+      fb[j] = frag(kh, klo, PR, 16 * tj[j] + l16, 32 * ks + 8 * kg);
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[j] = mfma3(fa[j], fb[j], acc[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * ti[j] + 4 * kg + r, sx = 16 * tj[j] + l16;
+      if (sx <= t) {
+        const float e = expf(sG[t] - sG[sx]);
+        if (!qk[j]) {
+          if (sx < t) sA[t * PA + sx] = sBeta[t] * e * acc[j][r];
+        } else {
+          u16 hh, ll;
+          split(e * acc[j][r], hh, ll);
+          lqh[t * PS + sx] = hh;
+          lql[t * PS + sx] = ll;
+        }
+      }
+    }
+  }
+}
+
+// ---- fp32 16x16 block products for the triangular inverse
+// v_mfma_f32_16x16x4f32: lane l supplies A[l%16][k], B[k][l%16] with
+// k = l/16 of the step, and holds D[4(l/16) + r][l%16].  Step s of a 16-long
+// sum uses k = 4(l/16) + s, so an accumulator block (which holds rows
+// 4(l/16) + r) is already the B operand of the next product, with r = s.
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+// c += A B, A and B 16x16 blocks of row-major fp32 LDS arrays (pitches PA_, PB_)
+template <int PA_, int PB_>
+__device__ __forceinline__ f32x4 blk_mm(const float *A, const float *B, f32x4 c, int l16, int kg) {
+#pragma unroll
+  for (int st = 0; st < 4; ++st)
+    c = mfma_f32(A[l16 * PA_ + 4 * kg + st], B[(4 * kg + st) * PB_ + l16], c);
+  return c;
+}
+// c += A Bacc, Bacc an accumulator block held by this wave
+template <int PA_>
+__device__ __forceinline__ f32x4 blk_mm_acc(const float *A, const f32x4 &b, f32x4 c, int l16,
+                                            int kg) {
+#pragma unroll
+  for (int st = 0; st < 4; ++st) c = mfma_f32(A[l16 * PA_ + 4 * kg + st], b[st], c);
+  return c;
+}
+// store an accumulator block times `sign` to a row-major block with pitch PD_
+template <int PD_>
+__device__ __forceinline__ void blk_store(float *D, const f32x4 &c, float sign, int l16, int kg) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) D[(4 * kg + r) * PD_ + l16] = sign * c[r];
+}
+
+// One phase A work item: chunk c of value head h of sequence s.
+struct PrepItem {
+  int c, h, s, hk;
+  int t0;   // first position of the chunk
+  int n;    // positions in the chunk; 0 for a padding chunk (the chunk count is
+            // rounded up to even so the scan's two-deep operand pipeline has no
+            // tail): it yields e^{G_n} = 1 and all-zero operands, which leaves
+            // the state unchanged
+  int nl;   // last valid row, for clamped loads
+  int tb;   // base position of the loads (valid for padding chunks)
+};
+__device__ __forceinline__ PrepItem prep_item(int u, int n_chunks, int H, int Hk, int n_tok) {
+  PrepItem it;
+  it.c = u % n_chunks;
+  it.h = (u / n_chunks) % H;
+  it.s = u / (n_chunks * H);
+  it.hk = it.h / (H / Hk);
+  it.t0 = it.c * CH;
+  it.n = max(0, min(CH, n_tok - it.t0));
+  it.nl = max(it.n - 1, 0);
+  it.tb = min(it.t0, n_tok - 1);
+  return it;
+}
+
+// The loads of one item, in the order they are first needed.  Rows past n
+// read a valid row and are zeroed where they are used: a load behind a branch
+// would make the compiler wait for every load in flight at the join.
+struct PrepIn {
+  const float *q, *k, *v, *g, *beta;
+  int64_t qk_tok, qk_seq, v_tok, v_seq;
+  int n_tok, H;
+};
+__device__ __forceinline__ void load_gb(const PrepIn &in, const PrepItem &it, int lane, float &gv,
+                                        float &bv) {
+  const int64_t gi =
+      ((int64_t)it.s * in.n_tok + min(it.t0 + min(lane, it.nl), in.n_tok - 1)) * in.H + it.h;
+  gv = in.g[gi];
+  bv = in.beta[gi];
+}
+__device__ __forceinline__ void load_kq(const PrepIn &in, const PrepItem &it, int tid,
+                                        float4 (&kr)[4], float4 (&qr)[4]) {
+  const int64_t base = it.s * in.qk_seq + (int64_t)it.tb * in.qk_tok + it.hk * DK;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = i * 512 + tid, row = idx >> 5, col = (idx & 31) * 4;
+    const int64_t o = base + (int64_t)min(row, it.nl) * in.qk_tok + col;
+    kr[i] = *reinterpret_cast<const float4 *>(in.k + o);
+    qr[i] = *reinterpret_cast<const float4 *>(in.q + o);
+  }
+}
+__device__ __forceinline__ void load_v(const PrepIn &in, const PrepItem &it, int tid,
+                                       float4 (&vr)[4]) {
+  const int64_t base = it.s * in.v_seq + (int64_t)it.tb * in.v_tok + it.h * DV;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = i * 512 + tid, row = idx >> 5, col = (idx & 31) * 4;
+    vr[i] = *reinterpret_cast<const float4 *>(in.v + base + (int64_t)min(row, it.nl) * in.v_tok +
+                                              col);
+  }
+}
+
+// Persistent: workgroup b handles items b, b + G, b + 2G, ... (G = grid size,
+// at most one workgroup per CU given the LDS it takes).  The next item's g,
+// beta, K, Q and V are loaded into registers as soon as the current item has
+// consumed them, so a workgroup's loads and stores overlap its own compute
+// instead of every CU loading, then computing, then storing in lockstep.
 __global__ __launch_bounds__(512) void k_chunk_prep(
     const float *__restrict__ q, const float *__restrict__ k, int64_t qk_tok, int64_t qk_seq,
     const float *__restrict__ v, int64_t v_tok, int64_t v_seq, const float *__restrict__ g,
     const float *__restrict__ beta, unsigned char *__restrict__ ws, int n_tok, int n_chunks,
-    int H, int Hk) {
+    int H, int Hk, int n_items) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[L_TOTAL];
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
-  const int c = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
-  const int hk = h / (H / Hk);
-  const int t0 = c * CH;
-  // n == 0 for a padding chunk (the chunk count is rounded up to even so the
-  // scan's two-deep operand pipeline has no tail): it yields e^{G_n} = 1 and
-  // all-zero operands, which leaves the state unchanged.
-  const int n = max(0, min(CH, n_tok - t0));
-  const int nl = max(n - 1, 0);       // last valid position, for clamped loads
-  const int tb = min(t0, n_tok - 1);  // base position of the loads (valid for padding)
+  const PrepIn in{q, k, v, g, beta, qk_tok, qk_seq, v_tok, v_seq, n_tok, H};
 
   u16 *kh = reinterpret_cast<u16 *>(smem + L_K), *klo = kh + CH * PR;
   u16 *qh = reinterpret_cast<u16 *>(smem + L_Q), *qlo = qh + CH * PR;
@@ -251,26 +390,34 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
   float *sG = reinterpret_cast<float *>(smem + L_G);
   float *sBeta = sG + CH, *sEG = sG + 2 * CH, *sEGn = sG + 3 * CH;
 
-  const float *kc = k + s * qk_seq + (int64_t)tb * qk_tok + hk * DK;
-  const float *qc = q + s * qk_seq + (int64_t)tb * qk_tok + hk * DK;
-  const float *vc = v + s * v_seq + (int64_t)tb * v_tok + h * DV;
-  unsigned char *wc = ws + (((size_t)s * H + h) * n_chunks + c) * WS_CHUNK;
-
-  // S0. every load of the chunk is issued first (rows past n read a valid row
-  // and are zeroed by a select: a load behind a branch would make the
-  // compiler wait for all loads in flight at the join)
+  // the grid never exceeds n_items, so every workgroup has a first item
+  PrepItem it = prep_item(blockIdx.x, n_chunks, H, Hk, n_tok);
+  float gv, bv;
   float4 kr[4], qr[4], vr[4];
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int idx = it * 512 + tid, row = idx >> 5, col = (idx & 31) * 4;
-    const int rr = min(row, nl);
-    kr[it] = *reinterpret_cast<const float4 *>(kc + (int64_t)rr * qk_tok + col);
-    qr[it] = *reinterpret_cast<const float4 *>(qc + (int64_t)rr * qk_tok + col);
-    vr[it] = *reinterpret_cast<const float4 *>(vc + (int64_t)rr * v_tok + col);
-  }
+  load_gb(in, it, threadIdx.x & 63, gv, bv);
+  load_kq(in, it, threadIdx.x, kr, qr);
+  load_v(in, it, threadIdx.x, vr);
+
+  // One item; the first is peeled off the loop below so that the loop head is
+  // reached from one place only and the compiler's load/store counts there
+  // are exact (a merged count forces waits for every store still in flight).
+  auto run_item = [&](int u) {
+  // The thread index is re-read opaquely on every pass: otherwise the
+  // compiler hoists every per-lane LDS and workspace offset of the item out of
+  // the loop and keeps them all live, which spills.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
+  // the item after this one (this one again on the last pass: its loads are
+  // then redundant but in bounds, and no load sits behind a branch)
+  const PrepItem nx = prep_item(u + gridDim.x < n_items ? u + gridDim.x : u, n_chunks, H, Hk,
+                                n_tok);
+  const int n = it.n, nl = it.nl;
+  const float *qc = q + it.s * qk_seq + (int64_t)it.tb * qk_tok + it.hk * DK;
+  unsigned char *wc = ws + (((size_t)it.s * H + it.h) * n_chunks + it.c) * WS_CHUNK;
+
+  // S0. gate cumsum (wave 0) and cleared tiles
   if (w == 0) {
-    const int64_t gi = ((int64_t)s * n_tok + min(t0 + min(lane, nl), n_tok - 1)) * H + h;
-    const float gv = g[gi], bv = beta[gi];
     float x = lane < n ? gv : 0.0f;
     const float b = lane < n ? bv : 0.0f;
 #pragma unroll
@@ -284,47 +431,29 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
     sEG[lane] = expf(x);
     sEGn[lane] = expf(gn - x);
   }
+  load_gb(in, nx, lane, gv, bv);
   // zero A and (L o QK^T): their upper triangles stay zero
   for (int e = tid; e < CH * PA; e += 512) sA[e] = 0.0f;
   for (int e = tid; e < CH * PS; e += 512) lqh[e] = lql[e] = 0;
   // S1. K, Q rows -> LDS (bf16 hi/lo)
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int idx = it * 512 + tid, row = idx >> 5, col = (idx & 31) * 4;
-    const float4 kv = row < n ? kr[it] : make_float4(0.f, 0.f, 0.f, 0.f);
-    const float4 qv = row < n ? qr[it] : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i = 0; i < 4; ++i) {
+    const int idx = i * 512 + tid, row = idx >> 5, col = (idx & 31) * 4;
+    const float4 kv = row < n ? kr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 qv = row < n ? qr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
     store4_split(kh + row * PR + col, klo + row * PR + col, kv.x, kv.y, kv.z, kv.w);
     store4_split(qh + row * PR + col, qlo + row * PR + col, qv.x, qv.y, qv.z, qv.w);
   }
+  load_kq(in, nx, tid, kr, qr);
   __syncthreads();
 
-  // S2a. K K^T and Q K^T on the 10 lower tiles each: 20 jobs over 8 waves
-  for (int job = w; job < 20; job += 8) {
-    const bool qk = job >= 10;
-    const int jt = qk ? job - 10 : job;
-    const int ti = jt < 1 ? 0 : jt < 3 ? 1 : jt < 6 ? 2 : 3;   // lower-tile index -> (ti, tj)
-    const int tj = jt - ti * (ti + 1) / 2;
-    const u16 *ah = qk ? qh : kh, *al = qk ? qlo : klo;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      acc = mfma3(frag(ah, al, PR, 16 * ti + l16, 32 * ks + 8 * kg),
-                  frag(kh, klo, PR, 16 * tj + l16, 32 * ks + 8 * kg), acc);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 16 * ti + 4 * kg + r, sx = 16 * tj + l16;
-      if (sx <= t) {
-        const float e = expf(sG[t] - sG[sx]);
-        if (!qk) {
-          if (sx < t) sA[t * PA + sx] = sBeta[t] * e * acc[r];
-        } else {
-          u16 hh, ll;
-          split(e * acc[r], hh, ll);
-          lqh[t * PS + sx] = hh;
-          lql[t * PS + sx] = ll;
-        }
-      }
-    }
+  // S2a. K K^T and Q K^T on the 10 lower tiles each: 20 tiles, wave w takes
+  // tiles w, w + 8 (and w + 16 for w < 4), all at once, so their MFMA chains
+  // interleave instead of running back to back
+  if (w < 4) {
+    lower_tiles<3>(w, kh, klo, qh, qlo, sA, lqh, lql, sG, sBeta, l16, kg);
+  } else {
+    lower_tiles<2>(w, kh, klo, qh, qlo, sA, lqh, lql, sG, sBeta, l16, kg);
   }
   // S2b. K'^T fragments (K' = diag(e^{G_n - G}) K) straight from the K tile:
   // wave w writes key tile w, both token k-steps
@@ -357,11 +486,12 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
     }
   }
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int idx = it * 512 + tid, row = idx >> 5, col = (idx & 31) * 4;
-    const float4 vv = row < n ? vr[it] : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i = 0; i < 4; ++i) {
+    const int idx = i * 512 + tid, row = idx >> 5, col = (idx & 31) * 4;
+    const float4 vv = row < n ? vr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
     store4_split(qh + row * PR + col, qlo + row * PR + col, vv.x, vv.y, vv.z, vv.w);
   }
+  load_v(in, nx, tid, vr);
   __syncthreads();  // every diagonal block read before any is overwritten
   if (tid < 64) {
     const int b = tid >> 4, cc = tid & 15;
@@ -369,27 +499,41 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
     for (int r = 0; r < 16; ++r) sA[(16 * b + r) * PA + 16 * b + cc] = x[r];
   }
   __syncthreads();
-  // S3b. off-diagonal blocks, block row by block row:
-  //   T_ib,jb = -T_ib,ib * sum_{kb=jb}^{ib-1} A_ib,kb T_kb,jb
-  // (A_ib,* is still in place until its own row is finished)
-  for (int ib = 1; ib < 4; ++ib) {
-    for (int e = tid; e < ib * 256; e += 512) {
-      const int jb = e >> 8, r = (e >> 4) & 15, cc = e & 15;
-      float acc = 0.0f;
-      for (int kb = jb; kb < ib; ++kb)
-#pragma unroll
-        for (int m = 0; m < 16; ++m)
-          acc += sA[(16 * ib + r) * PA + 16 * kb + m] * sA[(16 * kb + m) * PA + 16 * jb + cc];
-      scratch[e] = acc;
+  // S3b. off-diagonal blocks of T, with D_b = T_bb and A_ij the blocks of A:
+  //   T10 = -D1 A10 D0,  T32 = -D3 A32 D2,
+  //   X20 = A20 D0 + A21 T10, X21 = A21 D1, X30 = A30 D0 + A31 T10, X31 = A31 D1,
+  //   T20 = -D2 X20, T21 = -D2 X21, T30 = -(T32 X20 + D3 X30), T31 = -(T32 X21 + D3 X31)
+  // (the 2x2 block-triangular inverse applied twice).  Three stages; each
+  // product is four fp32 MFMAs; a block of T overwrites the block of A that
+  // only its own wave reads.
+  {
+    auto B_ = [&](int bi, int bj) { return sA + (16 * bi) * PA + 16 * bj; };
+    auto X_ = [&](int i) { return scratch + i * 16 * XP; };    // X20, X21, X30, X31
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    f32x4 xa = z;
+    if (w == 0 || w == 1) {                // stage 1: T10, T32
+      const int b0 = 2 * w;                // 0 or 2
+      const f32x4 p = blk_mm<PA, PA>(B_(b0 + 1, b0), B_(b0, b0), z, l16, kg);
+      const f32x4 t = blk_mm_acc<PA>(B_(b0 + 1, b0 + 1), p, z, l16, kg);
+      blk_store<PA>(B_(b0 + 1, b0), t, -1.0f, l16, kg);
+    } else if (w == 2 || w == 3) {         // X21 = A21 D1, X31 = A31 D1
+      const f32x4 x = blk_mm<PA, PA>(B_(w, 1), B_(1, 1), z, l16, kg);
+      blk_store<XP>(X_(w == 2 ? 1 : 3), x, 1.0f, l16, kg);
+    } else if (w == 4 || w == 5) {         // A20 D0, A30 D0 (kept for stage 2)
+      xa = blk_mm<PA, PA>(B_(w - 2, 0), B_(0, 0), z, l16, kg);
     }
     __syncthreads();
-    for (int e = tid; e < ib * 256; e += 512) {
-      const int jb = e >> 8, r = (e >> 4) & 15, cc = e & 15;
-      float acc = 0.0f;
-#pragma unroll
-      for (int m = 0; m < 16; ++m)
-        acc += sA[(16 * ib + r) * PA + 16 * ib + m] * scratch[(jb << 8) + (m << 4) + cc];
-      sA[(16 * ib + r) * PA + 16 * jb + cc] = -acc;
+    if (w == 4 || w == 5) {                // stage 2: X20 = A20 D0 + A21 T10, X30 likewise
+      xa = blk_mm<PA, PA>(B_(w - 2, 1), B_(1, 0), xa, l16, kg);
+      blk_store<XP>(X_(w == 4 ? 0 : 2), xa, 1.0f, l16, kg);
+    }
+    __syncthreads();
+    if (w < 4) {                           // stage 3: T20, T21, T30, T31
+      const int bi = 2 + (w >> 1), bj = w & 1;
+      f32x4 t = z;
+      if (bi == 3) t = blk_mm<PA, XP>(B_(3, 2), X_(bj), t, l16, kg);          // T32 X2bj
+      t = blk_mm<PA, XP>(B_(bi, bi), X_(2 * (bi - 2) + bj), t, l16, kg);      // D_bi X_bi,bj
+      blk_store<PA>(B_(bi, bj), t, -1.0f, l16, kg);
     }
     __syncthreads();
   }
@@ -521,7 +665,13 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
                    qg + frag_off(2 * tp + m, kp, 4, 1, lane), xq);
     }
   }
-  if (tid == 0) *reinterpret_cast<float *>(wc + WS_G) = sEG[CH - 1];
+  // every thread stores the same value: no store behind a branch
+  *reinterpret_cast<float *>(wc + WS_G) = sEG[CH - 1];
+  __syncthreads();   // the next item rewrites every LDS tile
+  it = nx;
+  };
+  run_item(blockIdx.x);
+  for (int u = blockIdx.x + gridDim.x; u < n_items; u += gridDim.x) run_item(u);
 }
 
 // ----------------------------------------------------------------------------- phase B
@@ -635,6 +785,21 @@ size_t chunked_workspace_bytes(int n_seq, int n_tok, int H, int, int, int) {
   return (size_t)n_seq * H * padded_chunks(n_tok) * WS_CHUNK;
 }
 
+// Compute units of the current device, queried once per device.
+static int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      return -1;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 int launch_recur_chunked(const RecurArgs &a, int chunk, void *ws, size_t ws_bytes,
                          hipStream_t stream) {
   if (chunk != CH || a.S != DK) return GDN_ERR_UNSUPPORTED;
@@ -642,9 +807,15 @@ int launch_recur_chunked(const RecurArgs &a, int chunk, void *ws, size_t ws_byte
   if (ws_bytes < chunked_workspace_bytes(a.n_seq, a.n_tok, a.H, a.Hk, a.S, chunk))
     return GDN_ERR_WORKSPACE;
   unsigned char *wsb = static_cast<unsigned char *>(ws);
-  int rc = launch_kernel(k_chunk_prep, dim3(n_chunks, a.H, a.n_seq), dim3(512), 0, stream, a.q,
-                         a.k, a.qk_tok, a.qk_seq, a.v, a.v_tok, a.v_seq, a.g, a.beta, wsb,
-                         a.n_tok, n_chunks, a.H, a.Hk);
+  // phase A: one persistent workgroup per CU (its LDS allows no more), or one
+  // per item when there are fewer items than CUs
+  const int n_items = n_chunks * a.H * a.n_seq;
+  const int cus = device_cu_count();
+  if (cus <= 0) return GDN_ERR_LAUNCH;
+  const int grid_a = n_items < cus ? n_items : cus;
+  int rc = launch_kernel(k_chunk_prep, dim3(grid_a), dim3(512), 0, stream, a.q, a.k, a.qk_tok,
+                         a.qk_seq, a.v, a.v_tok, a.v_seq, a.g, a.beta, wsb, a.n_tok, n_chunks,
+                         a.H, a.Hk, n_items);
   if (rc != GDN_OK) return rc;
   const int nwg = a.n_seq * a.H * NVB;  // a multiple of 8 (NVB == 8)
   return launch_kernel(k_chunk_scan, dim3(nwg), dim3(512), 0, stream, a.state, a.st_seq,
