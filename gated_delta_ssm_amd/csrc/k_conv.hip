@@ -9,19 +9,23 @@
 // output depends on inputs only, so positions can run in parallel with the
 // same per-position arithmetic).
 //
-// Thread map (both kernels): one wave64 owns a block of 64*CPL consecutive
-// channels; lane l holds channels l, l+64, .., so every per-position load and
-// store of x / out is a coalesced 256-byte wave access.  A block is one L2 head
-// (head_dim = 64*CPL) or, at head_dim 32, two heads of 32 lanes each; the
-// head's sum of squares is an in-wave xor butterfly (wave.hpp), no LDS.
+// Thread map (both kernels): lane l of a wave owns the 4 consecutive channels
+// c0 = blk0 + 4l .. c0 + 3, so a wave covers 256 channels and each
+// per-position access of x and out is one 16-byte load or store per lane (a
+// 1 KiB wave access) when the rows are 16-byte aligned (VEC), or four 4-byte
+// accesses otherwise; the lane's taps, history and snapshot records are its 4
+// channels' consecutive [channel][tap] entries, likewise 16-byte accesses
+// when VEC.  The arithmetic is the same either way.  An L2 head of
+// head_dim channels is head_dim/4 consecutive lanes (LPH4); its sum of
+// squares is an in-wave xor butterfly (wave.hpp), no LDS.
 //
 //   k_conv_step : one wave walks every position of its sequence in order
 //                 (decode, K-position verify with snapshots).
 //   k_conv_tp   : one wave per (channel block, tile of TT positions); the
 //                 window is preloaded from x (or from the history before
 //                 position 0), so long prompts spread over the whole chip.
-// Both call conv_position() and l2_scale() below with the same lane map and
-// the same FMA order, so their outputs and histories agree bit for bit.
+// Both call conv_step4() below with the same lane map and the same FMA order,
+// so their outputs and histories agree bit for bit.
 #include <hip/hip_runtime.h>
 
 #include "gdn.h"
@@ -29,6 +33,8 @@
 #include "wave.hpp"
 
 namespace gdn {
+
+constexpr int CPL = 4;   // channels per lane
 
 // acc = sum_j w[j] * win[j] in tap order, oldest tap first, explicit FMAs.
 template <int D>
@@ -39,32 +45,151 @@ __device__ __forceinline__ float conv_position(const float (&w)[D], const float 
   return silu(acc);
 }
 
-// Taps of channel ch (clamped to a valid channel by the caller): one 16-byte
-// load when there are 4 taps.  Loads are never behind a branch: a branch
-// would make the compiler wait for every load in flight where it rejoins.
-template <int D>
-__device__ __forceinline__ void load_taps(const float *__restrict__ w, int ch, float (&wt)[D]) {
-  if constexpr (D == 4) {
-    const float4 t = *reinterpret_cast<const float4 *>(w + (int64_t)ch * 4);
-    wt[0] = t.x; wt[1] = t.y; wt[2] = t.z; wt[3] = t.w;
-  } else {
-#pragma unroll
-    for (int j = 0; j < D; ++j) wt[j] = w[(int64_t)ch * D + j];
-  }
-}
-
-// 1 / sqrt(sum over the lane's L2 head of o^2 + eps); LPH lanes per head.
-template <int CPL, int LPH>
+// 1 / sqrt(sum over the lane's L2 head of o^2 + eps); LPH4 lanes per head.
+template <int LPH4>
 __device__ __forceinline__ float l2_scale(const float (&o)[CPL], float eps) {
   float ss = o[0] * o[0];
 #pragma unroll
   for (int c = 1; c < CPL; ++c) ss = __builtin_fmaf(o[c], o[c], ss);
-  ss = group_sum<LPH>(ss);
+  ss = group_sum<LPH4>(ss);
   return 1.0f / sqrtf(ss + eps);
 }
 
-// LPH == 0: SiLU only (no channel of the block is a Q/K channel).
-template <int D, int CPL, int LPH>
+// The lane's channels: chc[c] is channel c0 + c clamped to the last channel
+// (lanes past the end compute on valid data and store nothing), ok[c] says
+// whether it exists.  c0v is the float4 base of VEC loads: with C a multiple
+// of 4 a lane is all valid or all past the end, and c0v is c0 or the last
+// group of 4.
+struct LaneChans {
+  int c0, c0v;
+  int chc[CPL];
+  bool ok[CPL];
+  bool all_ok;
+};
+__device__ __forceinline__ LaneChans lane_chans(int blk0, int lane, int C) {
+  LaneChans L;
+  L.c0 = blk0 + 4 * lane;
+  L.c0v = min(L.c0, C - 4);
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    L.ok[c] = L.c0 + c < C;
+    L.chc[c] = min(L.c0 + c, C - 1);
+  }
+  L.all_ok = L.c0 + CPL - 1 < C;
+  return L;
+}
+
+// The lane's 4 values of one per-position row.  No load sits behind a branch:
+// a branch would make the compiler wait for every load in flight where it
+// rejoins.
+template <bool VEC>
+__device__ __forceinline__ void load_row4(const float *__restrict__ row, const LaneChans &L,
+                                          float (&v)[CPL]) {
+  if constexpr (VEC) {
+    const float4 t = *reinterpret_cast<const float4 *>(row + L.c0v);
+    v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+  } else {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) v[c] = row[L.chc[c]];
+  }
+}
+template <bool VEC>
+__device__ __forceinline__ void store_row4(float *__restrict__ row, const LaneChans &L,
+                                           const float (&v)[CPL]) {
+  if constexpr (VEC) {
+    if (L.all_ok) *reinterpret_cast<float4 *>(row + L.c0) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+      if (L.ok[c]) row[L.c0 + c] = v[c];
+  }
+}
+
+// The lane's 4 channels' records of N floats each ([channel][N] layout: taps,
+// history, snapshots): 4N consecutive floats, N 16-byte accesses when VEC.
+template <int N, bool VEC>
+__device__ __forceinline__ void load_recs(const float *__restrict__ p, const LaneChans &L,
+                                          float (&r)[CPL][N]) {
+  if constexpr (VEC) {
+#pragma unroll
+    for (int q = 0; q < N; ++q) {
+      const float4 t = *reinterpret_cast<const float4 *>(p + (int64_t)L.c0v * N + 4 * q);
+      const float f[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[(4 * q + e) / N][(4 * q + e) % N] = f[e];
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+#pragma unroll
+      for (int j = 0; j < N; ++j) r[c][j] = p[(int64_t)L.chc[c] * N + j];
+  }
+}
+template <int N, bool VEC>
+__device__ __forceinline__ void store_recs(float *__restrict__ p, const LaneChans &L,
+                                           const float (&r)[CPL][N]) {
+  if constexpr (VEC) {
+    if (L.all_ok) {
+#pragma unroll
+      for (int q = 0; q < N; ++q) {
+        float f[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[e] = r[(4 * q + e) / N][(4 * q + e) % N];
+        *reinterpret_cast<float4 *>(p + (int64_t)L.c0 * N + 4 * q) =
+            make_float4(f[0], f[1], f[2], f[3]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+      if (L.ok[c]) {
+#pragma unroll
+        for (int j = 0; j < N; ++j) p[(int64_t)(L.c0 + c) * N + j] = r[c][j];
+      }
+  }
+}
+
+// Taps and history of the lane's channels (once per wave).
+template <int D, bool VEC>
+__device__ __forceinline__ void load_taps_hist(const float *__restrict__ w,
+                                               const float *__restrict__ hist, const LaneChans &L,
+                                               float (&wt)[CPL][D], float (&hv)[CPL][D - 1]) {
+  load_recs<D, VEC>(w, L, wt);
+  load_recs<D - 1, VEC>(hist, L, hv);
+}
+
+// The window's first D-1 slots (the history after the last position).
+template <int D>
+__device__ __forceinline__ void window_hist(const float (&win)[CPL][D], float (&h)[CPL][D - 1]) {
+#pragma unroll
+  for (int c = 0; c < CPL; ++c)
+#pragma unroll
+    for (int j = 0; j < D - 1; ++j) h[c][j] = win[c][j];
+}
+
+// One position: output of the lane's 4 channels from the window, which then
+// rolls with the raw input.  LPH4 == 0: SiLU only (no Q/K channel here).
+template <int D, int LPH4>
+__device__ __forceinline__ void conv_step4(const float (&wt)[CPL][D], float (&win)[CPL][D],
+                                           const float (&xv)[CPL], bool qk, float eps,
+                                           float (&o)[CPL]) {
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    win[c][D - 1] = xv[c];
+    o[c] = conv_position<D>(wt[c], win[c]);
+#pragma unroll
+    for (int j = 0; j < D - 1; ++j) win[c][j] = win[c][j + 1];
+  }
+  if constexpr (LPH4 > 0) {
+    const float inv = l2_scale<LPH4>(o, eps);
+    if (qk) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) o[c] *= inv;
+    }
+  }
+}
+
+template <int D, int LPH4, bool VEC>
 __global__ __launch_bounds__(256) void k_conv_step(
     const float *__restrict__ x, int64_t x_tok, int64_t x_seq, const float *__restrict__ w,
     float *__restrict__ hist, int64_t h_seq, float *__restrict__ out, int64_t o_tok, int64_t o_seq,
@@ -79,64 +204,39 @@ __global__ __launch_bounds__(256) void k_conv_step(
   out += s * o_seq;
   hist += s * h_seq;
 
-  // lanes past the last channel compute on channel C-1 and store nothing
+  const LaneChans L = lane_chans(blk0, lane, C);
   float wt[CPL][D], win[CPL][D];
-  bool ok[CPL];
-  int chc[CPL];
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    const int ch = blk0 + lane + 64 * c;
-    ok[c] = ch < C;
-    chc[c] = min(ch, C - 1);
-    load_taps<D>(w, chc[c], wt[c]);
-#pragma unroll
-    for (int j = 0; j < DH; ++j) win[c][j] = hist[(int64_t)chc[c] * DH + j];
-  }
-  const bool qk = LPH > 0 && blk0 + lane < qk_channels;
-
-  for (int t = 0; t < n_tok; ++t) {
-    float o[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      win[c][DH] = x[(int64_t)t * x_tok + chc[c]];
-      o[c] = conv_position<D>(wt[c], win[c]);
-#pragma unroll
-      for (int j = 0; j < DH; ++j) win[c][j] = win[c][j + 1];  // roll with the raw input
-    }
-    if (snap != nullptr && t < n_tok - 1) {
-      float *sp = snap + s * sn_seq + t * sn_tok;
-#pragma unroll
-      for (int c = 0; c < CPL; ++c)
-        if (ok[c]) {
-          const int ch = blk0 + lane + 64 * c;
-#pragma unroll
-          for (int j = 0; j < DH; ++j) sp[(int64_t)ch * DH + j] = win[c][j];
-        }
-    }
-    if constexpr (LPH > 0) {
-      const float inv = l2_scale<CPL, LPH>(o, eps);
-      if (qk) {
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) o[c] *= inv;
-      }
-    }
+  {
+    float hv[CPL][DH];
+    load_taps_hist<D, VEC>(w, hist, L, wt, hv);
 #pragma unroll
     for (int c = 0; c < CPL; ++c)
-      if (ok[c]) out[(int64_t)t * o_tok + blk0 + lane + 64 * c] = o[c];
+#pragma unroll
+      for (int j = 0; j < DH; ++j) win[c][j] = hv[c][j];
   }
-#pragma unroll
-  for (int c = 0; c < CPL; ++c)
-    if (ok[c]) {
-      const int ch = blk0 + lane + 64 * c;
-#pragma unroll
-      for (int j = 0; j < DH; ++j) hist[(int64_t)ch * DH + j] = win[c][j];
+  const bool qk = LPH4 > 0 && L.c0 < qk_channels;
+
+  for (int t = 0; t < n_tok; ++t) {
+    float xv[CPL], o[CPL];
+    load_row4<VEC>(x + (int64_t)t * x_tok, L, xv);
+    conv_step4<D, LPH4>(wt, win, xv, qk, eps, o);
+    if (snap != nullptr && t < n_tok - 1) {
+      float h[CPL][DH];
+      window_hist<D>(win, h);
+      store_recs<DH, VEC>(snap + s * sn_seq + t * sn_tok, L, h);
     }
+    store_row4<VEC>(out + (int64_t)t * o_tok, L, o);
+  }
+  float h[CPL][DH];
+  window_hist<D>(win, h);
+  store_recs<DH, VEC>(hist, L, h);
 }
 
 // Token-parallel form: grid (channel-block waves, position tiles, sequences).
-// Only the wave of tile 0 reads the old history, and it is also the one that
-// writes the new history, so no other wave can observe a half-updated history.
-template <int D, int CPL, int LPH, int TT>
+// Only the wave of tile 0 uses the old history, and it is also the one that
+// writes the new history, so no other wave can observe a half-updated history
+// (the other tiles load it too, unconditionally, and discard it).
+template <int D, int LPH4, bool VEC, int TT>
 __global__ __launch_bounds__(256) void k_conv_tp(
     const float *__restrict__ x, int64_t x_tok, int64_t x_seq, const float *__restrict__ w,
     float *__restrict__ hist, int64_t h_seq, float *__restrict__ out, int64_t o_tok, int64_t o_seq,
@@ -152,69 +252,57 @@ __global__ __launch_bounds__(256) void k_conv_tp(
   out += s * o_seq;
   hist += s * h_seq;
 
-  // lanes past the last channel compute on channel C-1 and store nothing;
-  // both window sources are loaded and one is selected (no load behind a
-  // branch)
+  const LaneChans L = lane_chans(blk0, lane, C);
   float wt[CPL][D], win[CPL][D], old[CPL][DH];
-  bool ok[CPL];
-  int chc[CPL];
+  load_taps_hist<D, VEC>(w, hist, L, wt, old);
+  // window slot j before position t0 holds position p = t0 - DH + j, which is
+  // before position 0 only in tile 0 (TT >= DH), where it is history slot j;
+  // both sources are loaded and one is selected
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    const int ch = blk0 + lane + 64 * c;
-    ok[c] = ch < C;
-    chc[c] = min(ch, C - 1);
-    load_taps<D>(w, chc[c], wt[c]);
+  for (int j = 0; j < DH; ++j) {
+    float xp[CPL];
+    load_row4<VEC>(x + (int64_t)max(t0 - DH + j, 0) * x_tok, L, xp);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) win[c][j] = t0 == 0 ? old[c][j] : xp[c];
+  }
+  const bool qk = LPH4 > 0 && L.c0 < qk_channels;
+
+  // positions in batches of TB: the batch's rows are loaded first (rows past
+  // the end are clamped to the last position and not used), so TB loads are
+  // in flight per wave instead of one
+  constexpr int TB = 8;
+  static_assert(TT % TB == 0, "tile of whole batches");
+  for (int tb = t0; tb < t1; tb += TB) {
+    float xv[TB][CPL];
+#pragma unroll
+    for (int i = 0; i < TB; ++i) load_row4<VEC>(x + (int64_t)min(tb + i, n_tok - 1) * x_tok, L, xv[i]);
+#pragma unroll
+    for (int i = 0; i < TB; ++i) {
+      if (tb + i < t1) {   // uniform per wave
+        float o[CPL];
+        conv_step4<D, LPH4>(wt, win, xv[i], qk, eps, o);
+        store_row4<VEC>(out + (int64_t)(tb + i) * o_tok, L, o);
+      }
+    }
+  }
+  if (t0 == 0) {  // the new history: positions n_tok-DH .. n_tok-1
+    float h[CPL][DH];
 #pragma unroll
     for (int j = 0; j < DH; ++j) {
-      // window slot j before position t0 holds position p = t0 - DH + j,
-      // which is before position 0 only in tile 0 (TT >= DH), where it is
-      // history slot j
-      const int p = t0 - DH + j;
-      old[c][j] = hist[(int64_t)chc[c] * DH + j];
-      const float xp = x[(int64_t)max(p, 0) * x_tok + chc[c]];
-      win[c][j] = t0 == 0 ? old[c][j] : xp;
-    }
-  }
-  const bool qk = LPH > 0 && blk0 + lane < qk_channels;
-
-  for (int t = t0; t < t1; ++t) {
-    float o[CPL];
+      // position p = n_tok - DH + j; before position 0 it is old slot p + DH
+      const int p = n_tok - DH + j;
+      float xp[CPL];
+      load_row4<VEC>(x + (int64_t)max(p, 0) * x_tok, L, xp);
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      win[c][DH] = x[(int64_t)t * x_tok + chc[c]];
-      o[c] = conv_position<D>(wt[c], win[c]);
+      for (int c = 0; c < CPL; ++c) {
+        float hv = xp[c];
 #pragma unroll
-      for (int j = 0; j < DH; ++j) win[c][j] = win[c][j + 1];
-    }
-    if constexpr (LPH > 0) {
-      const float inv = l2_scale<CPL, LPH>(o, eps);
-      if (qk) {
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) o[c] *= inv;
+        for (int k2 = 0; k2 < DH; ++k2)
+          if (p + DH == k2) hv = old[c][k2];
+        h[c][j] = hv;
       }
     }
-#pragma unroll
-    for (int c = 0; c < CPL; ++c)
-      if (ok[c]) out[(int64_t)t * o_tok + blk0 + lane + 64 * c] = o[c];
-  }
-
-  if (t0 == 0) {  // the new history: positions n_tok-DH .. n_tok-1
-#pragma unroll
-    for (int c = 0; c < CPL; ++c)
-      if (ok[c]) {
-        const int ch = blk0 + lane + 64 * c;
-#pragma unroll
-        for (int j = 0; j < DH; ++j) {
-          // position p = n_tok - DH + j; before position 0 it is old slot p + DH
-          const int p = n_tok - DH + j;
-          const float xp = x[(int64_t)max(p, 0) * x_tok + ch];
-          float hv = xp;
-#pragma unroll
-          for (int k2 = 0; k2 < DH; ++k2)
-            if (p + DH == k2) hv = old[c][k2];
-          hist[(int64_t)ch * DH + j] = hv;
-        }
-      }
+    store_recs<DH, VEC>(hist, L, h);
   }
 }
 
@@ -223,46 +311,60 @@ namespace {
 constexpr int kTileTok = 32;   // positions per wave in the token-parallel kernel
 constexpr int kWavesPerBlock = 4;
 
-template <int D, int CPL, int LPH>
+template <int D, int LPH4, bool VEC>
 int run_conv(const ConvArgs &a, hipStream_t stream) {
   const int blocks_ch = (a.C + 64 * CPL - 1) / (64 * CPL);           // one wave each
   const int grid_x = (blocks_ch + kWavesPerBlock - 1) / kWavesPerBlock;
   const dim3 block(64 * kWavesPerBlock);
   if (a.snap == nullptr && a.n_tok > 8) {
     const dim3 grid(grid_x, (a.n_tok + kTileTok - 1) / kTileTok, a.n_seq);
-    return launch_kernel(k_conv_tp<D, CPL, LPH, kTileTok>, grid, block, 0, stream, a.x, a.x_tok,
+    return launch_kernel(k_conv_tp<D, LPH4, VEC, kTileTok>, grid, block, 0, stream, a.x, a.x_tok,
                          a.x_seq, a.w, a.hist, a.h_seq, a.out, a.o_tok, a.o_seq, a.n_tok, a.C,
                          a.qk_channels, a.eps);
   }
-  const dim3 grid(grid_x, a.n_seq);
-  return launch_kernel(k_conv_step<D, CPL, LPH>, grid, block, 0, stream, a.x, a.x_tok, a.x_seq,
+  // the step kernel is latency-bound (a few loads per wave, then one chain of
+  // arithmetic): one-wave blocks spread its waves evenly over the CUs
+  const dim3 grid(blocks_ch, a.n_seq);
+  return launch_kernel(k_conv_step<D, LPH4, VEC>, grid, dim3(64), 0, stream, a.x, a.x_tok, a.x_seq,
                        a.w, a.hist, a.h_seq, a.out, a.o_tok, a.o_seq, a.snap, a.sn_tok, a.sn_seq,
                        a.n_tok, a.C, a.qk_channels, a.eps);
 }
 
-template <int D>
+template <int D, bool VEC>
 int dispatch_head(const ConvArgs &a, hipStream_t stream) {
-  if (a.qk_channels == 0) return run_conv<D, 2, 0>(a, stream);
+  if (a.qk_channels == 0) return run_conv<D, 0, VEC>(a, stream);
   switch (a.head_dim) {
-    case 32: return run_conv<D, 1, 32>(a, stream);
-    case 64: return run_conv<D, 1, 64>(a, stream);
-    case 128: return run_conv<D, 2, 64>(a, stream);
-    case 256: return run_conv<D, 4, 64>(a, stream);
+    case 32: return run_conv<D, 8, VEC>(a, stream);
+    case 64: return run_conv<D, 16, VEC>(a, stream);
+    case 128: return run_conv<D, 32, VEC>(a, stream);
+    case 256: return run_conv<D, 64, VEC>(a, stream);
     default: return GDN_ERR_UNSUPPORTED;
   }
+}
+
+template <int D>
+int dispatch_vec(const ConvArgs &a, hipStream_t stream) {
+  // 16-byte accesses need whole groups of 4 channels and 16-byte aligned
+  // rows of x, out, the weights, the history and the snapshots
+  auto al = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  const bool vec = a.C % 4 == 0 && al(a.x) && al(a.out) && al(a.w) && al(a.hist) &&
+                   (a.snap == nullptr || al(a.snap)) && a.x_tok % 4 == 0 && a.x_seq % 4 == 0 &&
+                   a.o_tok % 4 == 0 && a.o_seq % 4 == 0 && a.h_seq % 4 == 0 &&
+                   a.sn_tok % 4 == 0 && a.sn_seq % 4 == 0;
+  return vec ? dispatch_head<D, true>(a, stream) : dispatch_head<D, false>(a, stream);
 }
 
 }  // namespace
 
 int launch_conv(const ConvArgs &a, hipStream_t stream) {
   switch (a.D) {
-    case 2: return dispatch_head<2>(a, stream);
-    case 3: return dispatch_head<3>(a, stream);
-    case 4: return dispatch_head<4>(a, stream);
-    case 5: return dispatch_head<5>(a, stream);
-    case 6: return dispatch_head<6>(a, stream);
-    case 7: return dispatch_head<7>(a, stream);
-    case 8: return dispatch_head<8>(a, stream);
+    case 2: return dispatch_vec<2>(a, stream);
+    case 3: return dispatch_vec<3>(a, stream);
+    case 4: return dispatch_vec<4>(a, stream);
+    case 5: return dispatch_vec<5>(a, stream);
+    case 6: return dispatch_vec<6>(a, stream);
+    case 7: return dispatch_vec<7>(a, stream);
+    case 8: return dispatch_vec<8>(a, stream);
     default: return GDN_ERR_UNSUPPORTED;
   }
 }

@@ -5,11 +5,16 @@
 // z read from a wider per-token row at an offset: ssm_mamba.rs (spark_model),
 // gdn_verify_fused_norm_k2 (the caller passes z already offset).
 //
-// Thread map: one wave64 per block of 64*CPL consecutive elements of a row,
-// lane l holding elements l, l+64, ..; a block is one head (head_dim >= 64) or
-// two heads of 32 lanes (head_dim 32).  The sum of squares is an in-wave xor
-// butterfly.  Each lane reads its own y before any lane writes, so out may be
-// y itself.
+// Thread maps (each lane reads its own y before any lane writes, so out may be
+// y itself; the sum of squares is an in-wave xor butterfly):
+//   k_gated_rmsnorm_v4 : lane i of the launch owns elements 4i .. 4i+3 of the
+//     flattened [rows][H * head_dim] space, one 16-byte access per tensor;
+//     a head is head_dim/4 consecutive lanes, so one wave covers 256 elements
+//     (possibly of several rows).  Used when every pointer is 16-byte aligned
+//     and every row stride is a multiple of 4 elements.
+//   k_gated_rmsnorm : any alignment; one wave64 per block of 64*CPL
+//     consecutive elements of a row, lane l holding elements l, l+64, ..; a
+//     block is one head (head_dim >= 64) or two heads of 32 lanes.
 #include <hip/hip_runtime.h>
 
 #include "gdn.h"
@@ -57,6 +62,36 @@ __global__ __launch_bounds__(256) void k_gated_rmsnorm(const float *y, int64_t y
   }
 }
 
+// LPH4 = head_dim / 4 lanes per head.  Lanes past the end load a clamped
+// (valid) float4 and store nothing; heads never straddle that boundary, so no
+// valid head sums an invalid lane.
+template <int LPH4>
+__global__ __launch_bounds__(256) void k_gated_rmsnorm_v4(const float *y, int64_t y_row,
+                                                          const float *__restrict__ w,
+                                                          const float *__restrict__ z,
+                                                          int64_t z_row, float *out, int64_t o_row,
+                                                          unsigned total4, unsigned row4,
+                                                          float eps) {
+  constexpr int HD = 4 * LPH4;
+  const unsigned i4 = blockIdx.x * blockDim.x + threadIdx.x;
+  const unsigned ic = i4 < total4 ? i4 : total4 - 1;
+  const unsigned r = ic / row4;
+  const int e = (int)(ic - r * row4) * 4;
+  const int col = e % HD;
+  const float4 yv = *reinterpret_cast<const float4 *>(y + r * y_row + e);
+  const float4 zv = *reinterpret_cast<const float4 *>(z + r * z_row + e);
+  const float4 wv = *reinterpret_cast<const float4 *>(w + col);
+  float ss = yv.x * yv.x;
+  ss = __builtin_fmaf(yv.y, yv.y, ss);
+  ss = __builtin_fmaf(yv.z, yv.z, ss);
+  ss = __builtin_fmaf(yv.w, yv.w, ss);
+  ss = group_sum<LPH4>(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)HD + eps);
+  const float4 o = make_float4(((yv.x * inv) * wv.x) * silu(zv.x), ((yv.y * inv) * wv.y) * silu(zv.y),
+                               ((yv.z * inv) * wv.z) * silu(zv.z), ((yv.w * inv) * wv.w) * silu(zv.w));
+  if (i4 < total4) *reinterpret_cast<float4 *>(out + r * o_row + e) = o;
+}
+
 namespace {
 template <int CPL, int LPH>
 int run_norm(const NormArgs &a, hipStream_t stream) {
@@ -70,8 +105,31 @@ int run_norm(const NormArgs &a, hipStream_t stream) {
 }
 }  // namespace
 
+namespace {
+template <int LPH4>
+int run_norm_v4(const NormArgs &a, unsigned total4, hipStream_t stream) {
+  const unsigned blocks = (total4 + 255) / 256;
+  return launch_kernel(k_gated_rmsnorm_v4<LPH4>, dim3(blocks), dim3(256), 0, stream, a.y, a.y_row,
+                       a.w, a.z, a.z_row, a.out, a.o_row, total4,
+                       (unsigned)(a.H * a.hd / 4), a.eps);
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+}  // namespace
+
 int launch_gated_rmsnorm(const NormArgs &a, hipStream_t stream) {
   if (a.rows == 0) return GDN_OK;
+  const int64_t total4 = (int64_t)a.rows * a.H * a.hd / 4;
+  if (aligned16(a.y) && aligned16(a.z) && aligned16(a.out) && aligned16(a.w) &&
+      a.y_row % 4 == 0 && a.z_row % 4 == 0 && a.o_row % 4 == 0 && total4 < (int64_t)1 << 31) {
+    switch (a.hd) {
+      case 32: return run_norm_v4<8>(a, (unsigned)total4, stream);
+      case 64: return run_norm_v4<16>(a, (unsigned)total4, stream);
+      case 128: return run_norm_v4<32>(a, (unsigned)total4, stream);
+      case 256: return run_norm_v4<64>(a, (unsigned)total4, stream);
+      default: break;
+    }
+  }
   switch (a.hd) {
     case 32: return run_norm<1, 32>(a, stream);
     case 64: return run_norm<1, 64>(a, stream);

@@ -34,11 +34,17 @@ __device__ __forceinline__ float sum16(float x) {
   return x;
 }
 
-// Sum over aligned groups of WIDTH lanes (16, 32 or 64).
+// Sum over aligned groups of WIDTH lanes (8, 16, 32 or 64).
 template <int WIDTH>
 __device__ __forceinline__ float group_sum(float x) {
-  static_assert(WIDTH == 16 || WIDTH == 32 || WIDTH == 64, "group width");
-  x = sum16(x);
+  static_assert(WIDTH == 8 || WIDTH == 16 || WIDTH == 32 || WIDTH == 64, "group width");
+  if constexpr (WIDTH == 8) {
+    x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
+    x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
+    x += dpp_mov<0x141>(x);  // row_half_mirror: pairs the two quads of 8 lanes
+  } else {
+    x = sum16(x);
+  }
   if constexpr (WIDTH >= 32) x += __shfl_xor(x, 16, 64);
   if constexpr (WIDTH >= 64) x += __shfl_xor(x, 32, 64);
   return x;

@@ -141,6 +141,41 @@ def test_conv_other_shapes(head_dim, qk, d_conv, T):
     assert np.array_equal(st.cpu().double().numpy(), h_ref)
 
 
+@pytest.mark.parametrize("T", [1, 40])
+def test_conv_unaligned_rows_bit_identical_to_aligned(T):
+    # x and out one element off 16-byte alignment take the 4-byte-access path;
+    # its arithmetic is the 16-byte path's, so the results agree bit for bit
+    inp = make_inputs("tiny", seed=13, n_tok=T, n_seq=2, hist_std=1.0)
+    wl = inp["wl"]
+    C = wl.conv_dim
+    log_case("conv_unaligned", T=T, C=C)
+    out_a, st_a, _, _ = run_conv(inp)
+    x_sh = torch.full((wl.n_seq, T, C + 1), float("nan"))
+    x_sh[..., 1:] = inp["x"][..., :C]
+    o_full = torch.full((wl.n_seq, T, C + 1), float("nan"), device=DEV)
+    st = on_dev(inp["conv_hist"]).clone()
+    gdn().gdn_conv1d_silu_l2norm(on_dev(x_sh)[..., 1:], on_dev(inp["conv_w"]), st,
+                                 o_full[..., 1:], qk_channels=wl.qk_channels,
+                                 head_dim=wl.head_dim, l2_eps=wl.l2_eps)
+    assert bits_equal(o_full[..., 1:], out_a) and bits_equal(st, st_a)
+    assert torch.isnan(o_full[..., 0]).all()
+
+
+@pytest.mark.parametrize("C,qk,hd", [(222, 0, 32), (263, 128, 64)])
+def test_conv_channels_not_multiple_of_4(C, qk, hd):
+    # a last lane with fewer than 4 channels (scalar path), against the oracle
+    T = 37
+    inp = make_inputs("tiny", seed=17, conv_dim=C, qk_channels=qk, head_dim=hd, n_tok=T,
+                      x_stride=C, out_stride=C, hist_std=1.0, n_seq=2)
+    wl = inp["wl"]
+    log_case("conv_ragged_channels", C=C, qk=qk, hd=hd)
+    out, st, _, _ = run_conv(inp)
+    o_ref, h_ref, _ = oracle.conv1d_silu_l2norm(inp["x"], inp["conv_w"], inp["conv_hist"],
+                                                qk, hd, wl.l2_eps)
+    assert rel(out, o_ref) < 1e-5
+    assert np.array_equal(st.cpu().double().numpy(), h_ref)
+
+
 @pytest.mark.parametrize("T", [100, 3])
 def test_conv_token_parallel_bit_identical_to_steps(T):
     # the long-prompt kernel vs one-position calls, on the decode workload's channels
@@ -292,14 +327,17 @@ def test_gated_rmsnorm(name):
 
 
 @pytest.mark.parametrize("hd,H", [(32, 5), (64, 3), (256, 2)])
-def test_gated_rmsnorm_z_offset_and_in_place(hd, H):
-    # z read at an offset inside a wider [Q|K|V|Z]-style row; out written over y
+@pytest.mark.parametrize("z_shift", [16, 17])
+def test_gated_rmsnorm_z_offset_and_in_place(hd, H, z_shift):
+    # z read at an offset inside a wider [Q|K|V|Z]-style row; out written over y.
+    # A shift of 16 elements keeps z 16-byte aligned (the float4 kernel), 17
+    # does not (the general kernel).
     rows = 7
     inp = make_inputs("tiny", seed=51, head_dim=hd, H=H, n_tok=rows)
-    log_case("norm_offset_inplace", hd=hd, H=H)
+    log_case("norm_offset_inplace", hd=hd, H=H, z_shift=z_shift)
     width = 3 * H * hd
     row = torch.full((rows, width), float("nan"))
-    z_off = H * hd + 16
+    z_off = H * hd + z_shift
     row[:, z_off:z_off + H * hd] = inp["z"].reshape(rows, -1)
     row_dev = on_dev(row)
     z = row_dev[:, z_off:z_off + H * hd].unflatten(-1, (H, hd))
