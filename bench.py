@@ -150,15 +150,44 @@ def main():
             rec_ev.append((e0, e1))
         gdn.gdn_gated_rmsnorm(y.view(n, H, S), cu["norm_w"], z, nout, eps=wl.norm_eps)
 
+    def decode_step_fused(i):
+        # the same step with gate, recurrence and norm in one launch
+        p = i % len(pools)
+        gdn.gdn_conv1d_silu_l2norm(x, cu["conv_w"], hists[p], conv_out,
+                                   qk_channels=wl.qk_channels, head_dim=wl.head_dim,
+                                   l2_eps=wl.l2_eps)
+        gdn.gdn_decode_fused(pools[p], qv, kv, vv, cu["alpha"].view(n, 1, H), cu["dt"], cu["a"],
+                             cu["beta"], cu["norm_w"], z.view(n, 1, H, S), nout.view(n, 1, H, S),
+                             scale=wl.scale, norm_eps=wl.norm_eps)
+
+    def time_steps(step):
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.steps
+
+    fused_ms_per_step = time_steps(decode_step_fused)
+
     for i in range(args.warmup):
         decode_step(i)
     torch.cuda.synchronize()
+    # timed region: K whole steps, nothing else on the stream
     t0 = time.perf_counter()
     for i in range(args.steps):
-        decode_step(i, timed=True)
+        decode_step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
+    # the same K steps again with HIP events around each recurrence launch (an
+    # event pair adds about 5 us of dispatch gap on each side of the kernel,
+    # so it is kept out of the timed region above)
+    for i in range(args.steps):
+        decode_step(i, timed=True)
+    torch.cuda.synchronize()
     rec_ms = float(np.mean([a.elapsed_time(b) for a, b in rec_ev]))
     by = decode_bytes(wl)
     value = by["state"] / (ms_per_step * 1e-3) / 1e9
@@ -177,7 +206,6 @@ def main():
         hot_ev.append((e0, e1))
     torch.cuda.synchronize()
     hot_ms = float(np.mean([a.elapsed_time(b) for a, b in hot_ev]))
-    achieved = by["recurrence"] / (rec_ms * 1e-3) / 1e9
 
     # back-to-back bursts: events around 50 launches, 10 bursts, median per launch
     def burst(launch, n_launch=50, reps=10):
@@ -213,8 +241,40 @@ def main():
     dst = torch.empty_like(srcs[0])
     copy_ms = burst(lambda i: dst.copy_(srcs[i % len(srcs)]))
     copy_gbs = by["state"] / (copy_ms * 1e-3) / 1e9
+    # roofline of the dominant kernel: its launches back to back on rotated
+    # (cold) state pools, HIP events around 50 launches on the launch stream
+    burst_ms = bursts["recurrence_rotated_pools"]
+    achieved = by["recurrence"] / (burst_ms * 1e-3) / 1e9
     del srcs, dst
     torch.cuda.empty_cache()
+
+    # launch-bound regime: one sequence x 32 heads, where the fused entry point
+    # (gate + recurrence + norm in one launch) replaces three launches
+    sw = WORKLOADS["decode"]
+    si = make_inputs(sw)
+    sc = {k: v.to(dev) for k, v in si.items() if isinstance(v, torch.Tensor)}
+    sn, sT, sH, sS = sw.n_seq, sw.n_tok, sw.H, sw.S
+    s_st = sc["state"].clone()
+    s_g = torch.empty(sn * sT, sH, device=dev)
+    s_y = torch.empty(sn, sT, sH, sS, device=dev)
+    s_o = torch.empty(sn * sT, sH, sS, device=dev)
+
+    def small_three(i):
+        gdn.gdn_decay_gate(sc["alpha"], sc["dt"], sc["a"], s_g)
+        gdn.gdn_recurrence_decode(s_st, sc["q"], sc["k"], sc["v"], s_g.view(sn, sT, sH),
+                                  sc["beta"], s_y, scale=sw.scale)
+        gdn.gdn_gated_rmsnorm(s_y.view(sn * sT, sH, sS), sc["norm_w"], sc["z"], s_o,
+                              eps=sw.norm_eps)
+
+    def small_fused(i):
+        gdn.gdn_decode_fused(s_st, sc["q"], sc["k"], sc["v"], sc["alpha"].view(sn, sT, sH),
+                             sc["dt"], sc["a"], sc["beta"], sc["norm_w"],
+                             sc["z"].view(sn, sT, sH, sS), s_o.view(sn, sT, sH, sS),
+                             scale=sw.scale, norm_eps=sw.norm_eps)
+
+    small = {"workload": "decode: 1 seq x 1 token, 32 value / 16 q-k heads, 128x128 state",
+             "three_calls_ms": burst(small_three), "fused_ms": burst(small_fused)}
+    del s_st, s_g, s_y, s_o, sc
 
     # ---------------------------------------------------------------- prefill pass
     pw = WORKLOADS["prefill"]
@@ -310,14 +370,23 @@ def main():
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": recorded_traffic("k_recur_decode_decode64.md"),
             "bytes_per_launch": by["recurrence"],
-            "avg_launch_ms": rec_ms,
+            "avg_launch_ms": burst_ms,
+            "timing": "HIP events around 50 back-to-back launches on rotated state pools, "
+                      "median of 10 bursts",
         },
         "decode": {
             "recurrence_state_GBs_cold": by["state"] / (rec_ms * 1e-3) / 1e9,
             "recurrence_ms_cold": rec_ms,
+            "recurrence_ms_cold_note": "events around each launch inside the step sequence "
+                                       "(includes the event pair's dispatch gap)",
             "recurrence_ms_mall_hot": hot_ms,
             "recurrence_state_GBs_mall_hot": by["state"] / (hot_ms * 1e-3) / 1e9,
             "step_frac_of_hbm": value / HBM_PEAK_GBS,
+            "fused_ms_per_step": fused_ms_per_step,
+            "fused_state_GBs": by["state"] / (fused_ms_per_step * 1e-3) / 1e9,
+            "fused_note": "conv + gdn_decode_fused per step; at this batch the four separate "
+                          "launches (the timed step) are faster",
+            "small_batch_gate_recurrence_norm": small,
             "burst_ms_per_launch": bursts,
             "recurrence_burst_GBs": by["recurrence"] / (bursts["recurrence_rotated_pools"] * 1e-3) / 1e9,
             "copy_peak": {"what": "torch device copy, 192 MiB per launch, sources rotated, "

@@ -41,6 +41,9 @@ _SIGS = {
     "gdn_recurrence_chunked": (_I, [_P, _L, _P, _P, _L, _L, _P, _L, _L, _P, _P, _P, _L, _L,
                                     _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
     "gdn_gated_rmsnorm": (_I, [_P, _L, _P, _P, _L, _P, _L, _I, _I, _I, _F, _P]),
+    "gdn_decode_fused": (_I, [_P, _L, _P, _P, _L, _L, _P, _L, _L, _P, _P, _P, _P, _P, _P, _L,
+                              _L, _P, _L, _L, _P, _P, _L, _L, _P, _L, _I, _I, _I, _I, _I, _F,
+                              _F, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -225,4 +228,58 @@ def gdn_gated_rmsnorm(y: torch.Tensor, w: torch.Tensor, z: torch.Tensor, out: to
     _check("gdn_gated_rmsnorm", _lib.gdn_gated_rmsnorm(
         _ptr(y), y.stride(0), _ptr(w), _ptr(z), z.stride(0), _ptr(out), out.stride(0),
         rows, H, hd, eps, _stream(stream, out)))
+    return out
+
+
+def gdn_decode_fused(state: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                     alpha: torch.Tensor, dt: torch.Tensor, a: torch.Tensor,
+                     beta: torch.Tensor, norm_w: torch.Tensor, z: torch.Tensor,
+                     out: torch.Tensor, *, scale: float, norm_eps: float,
+                     g: torch.Tensor | None = None, y: torch.Tensor | None = None,
+                     snap: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Decay gate -> recurrence -> gated RMSNorm in one launch.  Layouts as
+    gdn_recurrence_decode; alpha, beta [n_seq][n_tok][H]; dt, a [H]; norm_w [S];
+    z, out [n_seq][n_tok][H][S]; optional g [n_seq][n_tok][H] and pre-norm y
+    [n_seq][n_tok][H][S] outputs; optional snap as gdn_recurrence_decode."""
+    n_seq, n_tok, Hk, S = q.shape
+    H = v.shape[2]
+    if tuple(state.shape) != (n_seq, H, S, S) or k.shape != q.shape:
+        raise ValueError("state / q / k shape mismatch")
+    if tuple(v.shape) != (n_seq, n_tok, H, S) or out.shape != v.shape or z.shape != v.shape:
+        raise ValueError("v / z / out shape mismatch")
+    if tuple(alpha.shape) != (n_seq, n_tok, H) or beta.shape != alpha.shape:
+        raise ValueError("alpha / beta shape mismatch")
+    if tuple(dt.shape) != (H,) or tuple(a.shape) != (H,) or tuple(norm_w.shape) != (S,):
+        raise ValueError("dt / a / norm_w shape mismatch")
+    _dev_f32("state", state, 3)
+    for n, t in (("q", q), ("k", k), ("v", v), ("z", z), ("out", out)):
+        _dev_f32(n, t, 2)
+    if q.stride() != k.stride():
+        raise ValueError("q and k must share strides")
+    for n, t in (("alpha", alpha), ("beta", beta)):
+        _dev_f32(n, t, 3)
+    for n, t in (("dt", dt), ("a", a), ("norm_w", norm_w)):
+        _dev_f32(n, t, 1)
+    y_tok = y_seq = 0
+    if g is not None:
+        _dev_f32("g", g, 3)
+        if g.shape != alpha.shape:
+            raise ValueError("g shape mismatch")
+    if y is not None:
+        _dev_f32("y", y, 2)
+        if y.shape != v.shape:
+            raise ValueError("y shape mismatch")
+        y_seq, y_tok = y.stride(0), y.stride(1)
+    sn_seq = 0
+    if snap is not None:
+        _dev_f32("snap", snap, 4)
+        if tuple(snap.shape) != (n_seq, n_tok - 1, H, S, S):
+            raise ValueError("snap shape mismatch")
+        sn_seq = snap.stride(0)
+    _check("gdn_decode_fused", _lib.gdn_decode_fused(
+        _ptr(state), state.stride(0), _ptr(q), _ptr(k), q.stride(1), q.stride(0),
+        _ptr(v), v.stride(1), v.stride(0), _ptr(alpha), _ptr(dt), _ptr(a), _ptr(beta),
+        _ptr(norm_w), _ptr(z), z.stride(1), z.stride(0), _ptr(out), out.stride(1),
+        out.stride(0), _ptr(g), _ptr(y), y_tok, y_seq, _ptr(snap), sn_seq, n_seq, n_tok, H,
+        Hk, S, scale, norm_eps, _stream(stream, out)))
     return out

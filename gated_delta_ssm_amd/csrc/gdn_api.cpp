@@ -107,4 +107,41 @@ int gdn_gated_rmsnorm(const float *y, int64_t y_row_stride, const float *w, cons
   return gdn::launch_gated_rmsnorm(a, stream);
 }
 
+int gdn_decode_fused(float *state, int64_t state_seq_stride, const float *q, const float *k,
+                     int64_t qk_tok_stride, int64_t qk_seq_stride, const float *v,
+                     int64_t v_tok_stride, int64_t v_seq_stride, const float *alpha,
+                     const float *dt, const float *a, const float *beta, const float *norm_w,
+                     const float *z, int64_t z_tok_stride, int64_t z_seq_stride, float *out,
+                     int64_t out_tok_stride, int64_t out_seq_stride, float *g, float *y,
+                     int64_t y_tok_stride, int64_t y_seq_stride, float *snap,
+                     int64_t snap_seq_stride, int n_seq, int n_tok, int n_v_heads,
+                     int n_qk_heads, int S, float scale, float norm_eps, hipStream_t stream) {
+  const int rc = gdn::check_fused(state, state_seq_stride, q, k, qk_tok_stride, qk_seq_stride, v,
+                                  v_tok_stride, v_seq_stride, alpha, dt, a, beta, norm_w, z,
+                                  z_tok_stride, z_seq_stride, out, out_tok_stride,
+                                  out_seq_stride, g, y, y_tok_stride, y_seq_stride, snap,
+                                  snap_seq_stride, n_seq, n_tok, n_v_heads, n_qk_heads, S);
+  if (rc != GDN_OK) return rc;
+  gdn::FusedArgs fa{};
+  fa.r = gdn::RecurArgs{state,          state_seq_stride, q,           k,
+                        qk_tok_stride,  qk_seq_stride,    v,           v_tok_stride,
+                        v_seq_stride,   nullptr,          beta,        out,
+                        out_tok_stride, out_seq_stride,   snap,        snap_seq_stride,
+                        n_seq,          n_tok,            n_v_heads,   n_qk_heads,
+                        S,              scale};
+  fa.alpha = alpha;
+  fa.dt = dt;
+  fa.a = a;
+  fa.w = norm_w;
+  fa.z = z;
+  fa.z_tok = z_tok_stride;
+  fa.z_seq = z_seq_stride;
+  fa.g = g;
+  fa.y = y;
+  fa.y_tok = y_tok_stride;
+  fa.y_seq = y_seq_stride;
+  fa.eps = norm_eps;
+  return gdn::launch_decode_fused(fa, stream);
+}
+
 }  // extern "C"

@@ -4,6 +4,7 @@
 // few bytes per element and launch-latency bound at decode sizes.
 #include <hip/hip_runtime.h>
 
+#include "gate.hpp"
 #include "gdn.h"
 #include "launch.hpp"
 
@@ -16,9 +17,7 @@ __global__ __launch_bounds__(256) void k_decay_gate(const float *__restrict__ al
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   const int h = (int)(i % H);
-  const float v = alpha[i] + dt[h];
-  const float sp = v > 20.0f ? v : log1pf(expf(v));
-  g[i] = a[h] * sp;
+  g[i] = decay_gate_value(alpha[i], dt[h], a[h]);
 }
 
 int launch_decay_gate(const float *alpha, const float *dt, const float *a, float *g, int rows,

@@ -19,6 +19,7 @@
 
 #include "gdn.h"
 #include "launch.hpp"
+#include "norm.hpp"
 #include "wave.hpp"
 
 namespace gdn {
@@ -81,14 +82,8 @@ __global__ __launch_bounds__(256) void k_gated_rmsnorm_v4(const float *y, int64_
   const float4 yv = *reinterpret_cast<const float4 *>(y + r * y_row + e);
   const float4 zv = *reinterpret_cast<const float4 *>(z + r * z_row + e);
   const float4 wv = *reinterpret_cast<const float4 *>(w + col);
-  float ss = yv.x * yv.x;
-  ss = __builtin_fmaf(yv.y, yv.y, ss);
-  ss = __builtin_fmaf(yv.z, yv.z, ss);
-  ss = __builtin_fmaf(yv.w, yv.w, ss);
-  ss = group_sum<LPH4>(ss);
-  const float inv = 1.0f / sqrtf(ss / (float)HD + eps);
-  const float4 o = make_float4(((yv.x * inv) * wv.x) * silu(zv.x), ((yv.y * inv) * wv.y) * silu(zv.y),
-                               ((yv.z * inv) * wv.z) * silu(zv.z), ((yv.w * inv) * wv.w) * silu(zv.w));
+  const float ss = group_sum<LPH4>(sumsq4(yv));
+  const float4 o = gated_norm4(yv, zv, wv, norm_inv(ss, HD, eps));
   if (i4 < total4) *reinterpret_cast<float4 *>(out + r * o_row + e) = o;
 }
 

@@ -81,4 +81,17 @@ struct NormArgs {
 };
 int launch_gated_rmsnorm(const NormArgs &a, hipStream_t stream);
 
+// Fused decode: r.y / r.y_tok / r.y_seq describe the normed output, r.g is
+// unused (the gate is computed from alpha, dt, a); g and y are optional
+// outputs (nullptr: not written).
+struct FusedArgs {
+  RecurArgs r;
+  const float *alpha, *dt, *a, *w, *z;
+  int64_t z_tok, z_seq;
+  float *g, *y;
+  int64_t y_tok, y_seq;
+  float eps;
+};
+int launch_decode_fused(const FusedArgs &a, hipStream_t stream);
+
 }  // namespace gdn

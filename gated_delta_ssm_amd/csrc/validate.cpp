@@ -173,4 +173,50 @@ int check_norm(const float *y, int64_t y_row, const float *w, const float *z, in
   return GDN_OK;
 }
 
+int check_fused(const float *state, int64_t st_seq, const float *q, const float *k,
+                int64_t qk_tok, int64_t qk_seq, const float *v, int64_t v_tok, int64_t v_seq,
+                const float *alpha, const float *dt, const float *a, const float *beta,
+                const float *w, const float *z, int64_t z_tok, int64_t z_seq, const float *out,
+                int64_t o_tok, int64_t o_seq, const float *g, const float *y, int64_t y_tok,
+                int64_t y_seq, const float *snap, int64_t sn_seq, int n_seq, int n_tok, int H,
+                int Hk, int S) {
+  // the recurrence's own rules, with alpha in the place of g and out in the
+  // place of y (same shapes)
+  const int rc = check_recur(state, st_seq, q, k, qk_tok, qk_seq, v, v_tok, v_seq, alpha, beta,
+                             out, o_tok, o_seq, snap, sn_seq, n_seq, n_tok, H, Hk, S);
+  if (rc != GDN_OK) return rc;
+  if (!dt || !a || !w || !z) return GDN_ERR_NULL;
+  if (z_tok < 0 || z_seq < 0 || (y && (y_tok < 0 || y_seq < 0))) return GDN_ERR_SHAPE;
+  // the norm reads z and w and writes out as float4
+  if (!aligned(out, 16) || !aligned(z, 16) || !aligned(w, 16) || o_tok % 4 || o_seq % 4 ||
+      z_tok % 4 || z_seq % 4)
+    return GDN_ERR_SHAPE;
+  const int64_t row = (int64_t)H * S, st_len = (int64_t)S * S * H;
+  if (y && !rows_disjoint(n_seq, y_seq, n_tok, y_tok, row)) return GDN_ERR_SHAPE;
+  const int n_snap = n_tok - 1;
+  const Span in[] = {span_of(q, n_seq, qk_seq, n_tok, qk_tok, (int64_t)Hk * S),
+                     span_of(k, n_seq, qk_seq, n_tok, qk_tok, (int64_t)Hk * S),
+                     span_of(v, n_seq, v_seq, n_tok, v_tok, row),
+                     span_of(alpha, 1, 0, 1, 0, (int64_t)n_seq * n_tok * H),
+                     span_of(beta, 1, 0, 1, 0, (int64_t)n_seq * n_tok * H),
+                     span_of(dt, 1, 0, 1, 0, H),
+                     span_of(a, 1, 0, 1, 0, H),
+                     span_of(w, 1, 0, 1, 0, S),
+                     span_of(z, n_seq, z_seq, n_tok, z_tok, row)};
+  const Span outs[] = {span_of(state, n_seq, st_seq, 1, 0, st_len),
+                       span_of(out, n_seq, o_seq, n_tok, o_tok, row),
+                       g ? span_of(g, 1, 0, 1, 0, (int64_t)n_seq * n_tok * H) : Span{},
+                       y ? span_of(y, n_seq, y_seq, n_tok, y_tok, row) : Span{},
+                       snap && n_snap > 0 ? span_of(snap, n_seq, sn_seq, n_snap, st_len, st_len)
+                                          : Span{}};
+  for (const Span &o : outs) {
+    for (const Span &i : in)
+      if (overlap(o, i)) return GDN_ERR_ALIAS;
+  }
+  for (int i = 0; i < 5; ++i)
+    for (int j = i + 1; j < 5; ++j)
+      if (overlap(outs[i], outs[j])) return GDN_ERR_ALIAS;
+  return GDN_OK;
+}
+
 }  // namespace gdn

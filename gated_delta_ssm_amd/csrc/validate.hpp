@@ -27,4 +27,12 @@ int check_chunked(const float *state, int64_t st_seq, const float *q, const floa
 int check_norm(const float *y, int64_t y_row, const float *w, const float *z, int64_t z_row,
                const float *out, int64_t o_row, int rows, int H, int hd);
 
+int check_fused(const float *state, int64_t st_seq, const float *q, const float *k,
+                int64_t qk_tok, int64_t qk_seq, const float *v, int64_t v_tok, int64_t v_seq,
+                const float *alpha, const float *dt, const float *a, const float *beta,
+                const float *w, const float *z, int64_t z_tok, int64_t z_seq, const float *out,
+                int64_t o_tok, int64_t o_seq, const float *g, const float *y, int64_t y_tok,
+                int64_t y_seq, const float *snap, int64_t sn_seq, int n_seq, int n_tok, int H,
+                int Hk, int S);
+
 }  // namespace gdn

@@ -197,6 +197,43 @@ int gdn_gated_rmsnorm(const float *y, int64_t y_row_stride, const float *w, cons
                       int64_t z_row_stride, float *out, int64_t out_row_stride, int rows,
                       int n_heads, int head_dim, float eps, hipStream_t stream);
 
+/*
+ * The decode / K-position verify layer core in one launch: decay gate ->
+ * recurrence -> gated RMSNorm (the norm's head_dim is S).  [FM] header notes
+ * on timing: the decay gate is dispatch cost that should ride with its
+ * neighbours; [AT] conv1d_update_l2norm: fusing neighbouring ops saves a
+ * launch per layer.
+ *
+ * Per (s, t, h):  g = a[h] * softplus(alpha[s][t][h] + dt[h])  (as
+ * gdn_decay_gate), then the recurrence of gdn_recurrence_decode with that g,
+ * then out = gated_rmsnorm(y, norm_w, z) per head (as gdn_gated_rmsnorm).
+ * Each value is computed with the same operations in the same order as those
+ * three calls; with 16-byte aligned buffers (on which gdn_gated_rmsnorm takes
+ * its 16-byte path) the results are bit-identical to them.
+ *
+ *   state, q, k, v, beta, snap: as gdn_recurrence_decode
+ *   alpha  dense [n_seq][n_tok][n_v_heads]; dt, a: [n_v_heads]          (in)
+ *   norm_w [S], 16-byte aligned                                          (in)
+ *   z      element [s][t][h][j] at z + s*z_seq_stride + t*z_tok_stride + h*S + j,
+ *          16-byte aligned, strides multiples of 4                       (in)
+ *   out    the normed output, element [s][t][h][j] at
+ *          out + s*out_seq_stride + t*out_tok_stride + h*S + j, 16-byte
+ *          aligned, strides multiples of 4                              (out)
+ *   g      NULL, or dense [n_seq][n_tok][n_v_heads]: the gate values    (out)
+ *   y      NULL, or the pre-norm output in the layout of out with its own
+ *          strides                                                      (out)
+ * No output may overlap an input or another output.  S in {32, 64, 128, 256}.
+ */
+int gdn_decode_fused(float *state, int64_t state_seq_stride, const float *q, const float *k,
+                     int64_t qk_tok_stride, int64_t qk_seq_stride, const float *v,
+                     int64_t v_tok_stride, int64_t v_seq_stride, const float *alpha,
+                     const float *dt, const float *a, const float *beta, const float *norm_w,
+                     const float *z, int64_t z_tok_stride, int64_t z_seq_stride, float *out,
+                     int64_t out_tok_stride, int64_t out_seq_stride, float *g, float *y,
+                     int64_t y_tok_stride, int64_t y_seq_stride, float *snap,
+                     int64_t snap_seq_stride, int n_seq, int n_tok, int n_v_heads,
+                     int n_qk_heads, int S, float scale, float norm_eps, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

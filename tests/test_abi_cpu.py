@@ -134,6 +134,34 @@ def test_norm_validation():
     assert call(FAKE, 256, FAKE + MB, FAKE + 2 * MB, 256, FAKE + 3 * MB, 128, 4, 2, 128) == ERR_SHAPE
 
 
+def fused(**kw):
+    S, H, T, n = kw.pop("S", 32), 4, 2, 2
+    MB = 1 << 20
+    a = dict(state=FAKE, sts=H * S * S, q=FAKE + 4 * MB, k=FAKE + 8 * MB, qkt=H * S,
+             qks=T * H * S, v=FAKE + 12 * MB, vt=H * S, vs=T * H * S, alpha=FAKE + 16 * MB,
+             dt=FAKE + 17 * MB, a=FAKE + 18 * MB, beta=FAKE + 20 * MB, w=FAKE + 22 * MB,
+             z=FAKE + 24 * MB, zt=H * S, zs=T * H * S, out=FAKE + 28 * MB, ot=H * S,
+             os=T * H * S, g=None, y=None, yt=0, ys=0, snap=None, sns=0)
+    a.update(kw)
+    return L.gdn_decode_fused(a["state"], a["sts"], a["q"], a["k"], a["qkt"], a["qks"], a["v"],
+                              a["vt"], a["vs"], a["alpha"], a["dt"], a["a"], a["beta"], a["w"],
+                              a["z"], a["zt"], a["zs"], a["out"], a["ot"], a["os"], a["g"],
+                              a["y"], a["yt"], a["ys"], a["snap"], a["sns"], n, T, H, H, S,
+                              0.125, 1e-6, None)
+
+
+def test_fused_validation():
+    MB = 1 << 20
+    assert fused(S=96) == ERR_UNSUP
+    assert fused(dt=None) == ERR_NULL and fused(z=None) == ERR_NULL
+    assert fused(out=FAKE + 28 * MB + 4) == ERR_SHAPE                  # out not 16-byte aligned
+    assert fused(zt=4 * 32 + 2) == ERR_SHAPE                           # z stride not a multiple of 4
+    assert fused(out=FAKE + 24 * MB + 64) == ERR_ALIAS                 # out overlaps z
+    assert fused(g=FAKE + 16 * MB) == ERR_ALIAS                        # g overlaps alpha
+    assert fused(y=FAKE + 28 * MB, yt=128, ys=256) == ERR_ALIAS        # y overlaps out
+    assert fused(snap=FAKE + 22 * MB, sns=4 * 32 * 32) == ERR_ALIAS    # snapshot over norm_w
+
+
 def test_page_shape_limits_are_the_abi_limits():
     import json
     gold = json.load(open(os.path.join(ROOT, "tests", "golden", "page_constants.json")))

@@ -380,6 +380,58 @@ def test_tiny_chained_layer_core():
     assert rel(n, n_r) < 1e-4
 
 
+# ------------------------------------------------------------------------------------- fused decode
+
+@pytest.mark.parametrize("name,opt,shape", [
+    ("tiny", True, None), ("decode", True, None), ("decode", False, None),
+    ("decode64", True, None), ("verify2", True, None),
+    ("tiny", True, dict(S=64, head_dim=64, H=6, Hk=3, n_tok=3, n_seq=2)),
+    ("tiny", True, dict(S=256, head_dim=256, H=2, Hk=1, n_tok=2, n_seq=2))])
+def test_decode_fused_bit_identical_to_three_calls(name, opt, shape):
+    # gate -> recurrence -> norm in one launch against the three separate calls
+    # (bit for bit: same operations in the same order) and the fp64 oracle chain
+    inp = inputs(name) if shape is None else make_inputs(name, seed=41, state_std=0.1, **shape)
+    wl = inp["wl"]
+    n, T, H, S = wl.n_seq, wl.n_tok, wl.H, wl.S
+    assert wl.head_dim == S
+    log_case("decode_fused", wl=name, n_seq=n, n_tok=T, H=H, S=S, optional_outputs=opt)
+    snap = 1 < T <= 8
+    d = {k: on_dev(inp[k]) for k in ("alpha", "dt", "a", "beta", "q", "k", "v", "norm_w", "z")}
+    nan = float("nan")
+    g3 = torch.empty(n * T, H, device=DEV)
+    gdn().gdn_decay_gate(d["alpha"], d["dt"], d["a"], g3)
+    st3 = on_dev(inp["state"]).clone()
+    y3 = torch.empty(n, T, H, S, device=DEV)
+    sn3 = torch.full((n, T - 1, H, S, S), nan, device=DEV) if snap else None
+    gdn().gdn_recurrence_decode(st3, d["q"], d["k"], d["v"], g3.view(n, T, H), d["beta"], y3,
+                                scale=wl.scale, snap=sn3)
+    o3 = torch.empty(n * T, H, S, device=DEV)
+    gdn().gdn_gated_rmsnorm(y3.view(n * T, H, S), d["norm_w"], d["z"], o3, eps=wl.norm_eps)
+
+    stf = on_dev(inp["state"]).clone()
+    of = torch.full((n, T, H, S), nan, device=DEV)
+    gf = torch.full((n, T, H), nan, device=DEV) if opt else None
+    yf = torch.full((n, T, H, S), nan, device=DEV) if opt else None
+    snf = torch.full((n, T - 1, H, S, S), nan, device=DEV) if snap else None
+    gdn().gdn_decode_fused(stf, d["q"], d["k"], d["v"], d["alpha"].view(n, T, H), d["dt"],
+                           d["a"], d["beta"], d["norm_w"], d["z"].view(n, T, H, S), of,
+                           scale=wl.scale, norm_eps=wl.norm_eps, g=gf, y=yf, snap=snf)
+    assert bits_equal(of, o3.view(n, T, H, S))
+    assert bits_equal(stf, st3)
+    if opt:
+        assert bits_equal(gf, g3.view(n, T, H)) and bits_equal(yf, y3)
+    if snap:
+        assert bits_equal(snf, sn3)
+
+    g_ref = oracle.decay_gate(inp["alpha"], inp["dt"], inp["a"]).reshape(n, T, H)
+    y_ref, s_ref, _ = oracle.recurrence_seq(inp["state"], inp["q"], inp["k"], inp["v"], g_ref,
+                                            inp["beta"], wl.scale)
+    o_ref = oracle.gated_rmsnorm(y_ref.reshape(n * T, H, S), inp["norm_w"], inp["z"],
+                                 wl.norm_eps)
+    assert rel(of.view(n * T, H, S), o_ref) < 1e-4
+    assert rel(stf, s_ref) < 1e-4
+
+
 # ------------------------------------------------------------------------------------- chunked
 
 def run_chunked(inp, g3, state=None):
