@@ -40,6 +40,9 @@ def parse():
     p.add_argument("--prefill-iters", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--burst-launches", type=int, default=50,
+                   help="launches per back-to-back burst")
+    p.add_argument("--burst-reps", type=int, default=10, help="bursts per figure (median)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="run one device-to-device copy of this many MiB first (counter calibration)")
     return p.parse_args()
@@ -208,7 +211,7 @@ def main():
     hot_ms = float(np.mean([a.elapsed_time(b) for a, b in hot_ev]))
 
     # back-to-back bursts: events around 50 launches, 10 bursts, median per launch
-    def burst(launch, n_launch=50, reps=10):
+    def burst(launch, n_launch=args.burst_launches, reps=args.burst_reps):
         launch(0)
         torch.cuda.synchronize()
         per = []
