@@ -270,6 +270,37 @@ def test_recurrence_verify2_bit_identical_to_two_steps():
     assert bits_equal(sn[:, 0], sta)
 
 
+@pytest.mark.parametrize("K", [4, 17])
+def test_verify_k_positions_snapshots_and_steps(K):
+    # K-position verify (batched speculative decoding): all K-1 rollback
+    # snapshots, for the conv and the recurrence, against the oracle and
+    # against K one-position calls
+    inp = make_inputs("verify2", seed=81, n_tok=K, n_seq=4)
+    wl = inp["wl"]
+    log_case("verify_k", K=K, n_seq=wl.n_seq)
+    g3 = oracle_g(inp)
+    yK, stK, snK = run_decode(inp, g3, snap=True)
+    y_ref, s_ref, sn_ref = oracle.recurrence_seq(inp["state"], inp["q"], inp["k"], inp["v"], g3,
+                                                 inp["beta"], wl.scale, want_snap=True)
+    assert rel(yK, y_ref) < 1e-4 and rel(stK, s_ref) < 1e-4 and rel(snK, sn_ref) < 1e-4
+    st = on_dev(inp["state"]).clone()
+    ys = []
+    for t in range(K):
+        y1, st, _ = run_decode(inp, g3, state=st, t0=t, t1=t + 1)
+        ys.append(y1)
+        if t < K - 1:
+            assert bits_equal(snK[:, t], st)
+    assert bits_equal(yK, torch.cat(ys, 1)) and bits_equal(stK, st)
+
+    out, hist, sn, _ = run_conv(inp, snap=True)
+    o_ref, h_ref, c_ref = oracle.conv1d_silu_l2norm(
+        inp["x"][..., :wl.conv_dim], inp["conv_w"], inp["conv_hist"], wl.qk_channels,
+        wl.head_dim, wl.l2_eps, want_snap=True)
+    assert rel(out, o_ref) < 1e-5
+    assert np.array_equal(hist.cpu().double().numpy(), h_ref)
+    assert np.array_equal(sn.cpu().double().numpy(), c_ref)
+
+
 def test_recurrence_strided_inputs_poisoned_gaps():
     # q/k/v/y rows inside wider buffers whose gaps hold NaN: a stray read or
     # write outside the declared rows shows up as NaN in y or a changed gap
