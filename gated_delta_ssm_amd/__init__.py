@@ -41,6 +41,7 @@ _SIGS = {
     "gdn_recurrence_chunked": (_I, [_P, _L, _P, _P, _L, _L, _P, _L, _L, _P, _P, _P, _L, _L,
                                     _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
     "gdn_gated_rmsnorm": (_I, [_P, _L, _P, _P, _L, _P, _L, _I, _I, _I, _F, _P]),
+    "gdn_stream_copy": (_I, [_P, _P, _SZ, _P]),
     "gdn_decode_fused": (_I, [_P, _L, _P, _P, _L, _L, _P, _L, _L, _P, _P, _P, _P, _P, _P, _L,
                               _L, _P, _L, _L, _P, _P, _L, _L, _P, _L, _I, _I, _I, _I, _I, _F,
                               _F, _P]),
@@ -283,3 +284,15 @@ def gdn_decode_fused(state: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: t
         out.stride(0), _ptr(g), _ptr(y), y_tok, y_seq, _ptr(snap), sn_seq, n_seq, n_tok, H,
         Hk, S, scale, norm_eps, _stream(stream, out)))
     return out
+
+
+def gdn_stream_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> torch.Tensor:
+    """Non-temporal device copy of src into dst (same byte size, 16-byte
+    aligned): the achievable-bandwidth reference of the benchmark."""
+    nb = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nb or not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("src and dst must be contiguous and of the same byte size")
+    if not (src.is_cuda and dst.is_cuda):
+        raise ValueError("src and dst must be on the GPU")
+    _check("gdn_stream_copy", _lib.gdn_stream_copy(_ptr(dst), _ptr(src), nb, _stream(stream, dst)))
+    return dst

@@ -10,7 +10,7 @@ import pytest
 import gated_delta_ssm_amd as gdn
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "gdn.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("gdn.h", "gdn_measure.h")]
 
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_ALIAS, ERR_WS = 0, -1, -2, -3, -4, -5
 FAKE = 0x10000            # never dereferenced: validation rejects first
@@ -18,7 +18,7 @@ L = gdn._lib
 
 
 def declared():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text)))
 
@@ -160,6 +160,14 @@ def test_fused_validation():
     assert fused(g=FAKE + 16 * MB) == ERR_ALIAS                        # g overlaps alpha
     assert fused(y=FAKE + 28 * MB, yt=128, ys=256) == ERR_ALIAS        # y overlaps out
     assert fused(snap=FAKE + 22 * MB, sns=4 * 32 * 32) == ERR_ALIAS    # snapshot over norm_w
+
+
+def test_stream_copy_validation():
+    assert L.gdn_stream_copy(FAKE, FAKE + (1 << 20), 0, None) == OK            # nothing launched
+    assert L.gdn_stream_copy(None, FAKE, 64, None) == ERR_NULL
+    assert L.gdn_stream_copy(FAKE + 4, FAKE + (1 << 20), 64, None) == ERR_SHAPE  # misaligned
+    assert L.gdn_stream_copy(FAKE, FAKE + (1 << 20), 60, None) == ERR_SHAPE      # not whole 16 B
+    assert L.gdn_stream_copy(FAKE, FAKE + 32, 64, None) == ERR_ALIAS
 
 
 def test_page_shape_limits_are_the_abi_limits():

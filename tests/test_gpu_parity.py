@@ -513,3 +513,17 @@ def test_chunked_deterministic():
     ya, sa = run_chunked(inp, g3)
     yb, sb = run_chunked(inp, g3)
     assert bits_equal(ya, yb) and bits_equal(sa, sb)
+
+
+# ------------------------------------------------------------------------------------- measurement aid
+
+def test_stream_copy_exact():
+    # the benchmark's bandwidth reference copies every byte, including a
+    # ragged tail of the grid, and nothing else
+    log_case("stream_copy")
+    n = (1 << 20) + 12                                      # float4 count not a multiple of 256
+    src = torch.randn(n * 4, device=DEV)
+    dst = torch.full((n * 4 + 8,), float("nan"), device=DEV)
+    gdn().gdn_stream_copy(dst[:n * 4], src)
+    assert bits_equal(dst[:n * 4], src)
+    assert torch.isnan(dst[n * 4:]).all()
