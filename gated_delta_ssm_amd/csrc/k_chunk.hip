@@ -432,9 +432,14 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
     sEGn[lane] = expf(gn - x);
   }
   load_gb(in, nx, lane, gv, bv);
-  // zero A and (L o QK^T): their upper triangles stay zero
-  for (int e = tid; e < CH * PA; e += 512) sA[e] = 0.0f;
-  for (int e = tid; e < CH * PS; e += 512) lqh[e] = lql[e] = 0;
+  // zero (L o QK^T) and A, which lie back to back: their upper triangles stay
+  // zero.  16-byte stores.
+  {
+    static_assert(L_A == L_L + TILE64 && (TILE64 + CH * PA * 4) % 16 == 0 && L_L % 16 == 0,
+                  "one contiguous region");
+    uint4 *zp = reinterpret_cast<uint4 *>(smem + L_L);
+    for (int e = tid; e < (TILE64 + CH * PA * 4) / 16; e += 512) zp[e] = make_uint4(0, 0, 0, 0);
+  }
   // S1. K, Q rows -> LDS (bf16 hi/lo)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
