@@ -345,26 +345,46 @@ __device__ __forceinline__ void load_gb(const PrepIn &in, const PrepItem &it, in
   gv = in.g[gi];
   bv = in.beta[gi];
 }
+// Thread tid holds 8 consecutive floats of a row in each of two passes:
+// pass i covers row (i * 512 + tid) / 16, columns 8 * (tid % 16) .. + 7, as
+// registers r[2i] and r[2i + 1].
+__device__ __forceinline__ void row8_of(int i, int tid, int &row, int &col) {
+  const int idx = i * 512 + tid;
+  row = idx >> 4;
+  col = (idx & 15) * 8;
+}
 __device__ __forceinline__ void load_kq(const PrepIn &in, const PrepItem &it, int tid,
                                         float4 (&kr)[4], float4 (&qr)[4]) {
   const int64_t base = it.s * in.qk_seq + (int64_t)it.tb * in.qk_tok + it.hk * DK;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = i * 512 + tid, row = idx >> 5, col = (idx & 31) * 4;
+  for (int i = 0; i < 2; ++i) {
+    int row, col;
+    row8_of(i, tid, row, col);
     const int64_t o = base + (int64_t)min(row, it.nl) * in.qk_tok + col;
-    kr[i] = *reinterpret_cast<const float4 *>(in.k + o);
-    qr[i] = *reinterpret_cast<const float4 *>(in.q + o);
+    kr[2 * i] = *reinterpret_cast<const float4 *>(in.k + o);
+    kr[2 * i + 1] = *reinterpret_cast<const float4 *>(in.k + o + 4);
+    qr[2 * i] = *reinterpret_cast<const float4 *>(in.q + o);
+    qr[2 * i + 1] = *reinterpret_cast<const float4 *>(in.q + o + 4);
   }
 }
 __device__ __forceinline__ void load_v(const PrepIn &in, const PrepItem &it, int tid,
                                        float4 (&vr)[4]) {
   const int64_t base = it.s * in.v_seq + (int64_t)it.tb * in.v_tok + it.h * DV;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = i * 512 + tid, row = idx >> 5, col = (idx & 31) * 4;
-    vr[i] = *reinterpret_cast<const float4 *>(in.v + base + (int64_t)min(row, it.nl) * in.v_tok +
-                                              col);
+  for (int i = 0; i < 2; ++i) {
+    int row, col;
+    row8_of(i, tid, row, col);
+    const float *p = in.v + base + (int64_t)min(row, it.nl) * in.v_tok + col;
+    vr[2 * i] = *reinterpret_cast<const float4 *>(p);
+    vr[2 * i + 1] = *reinterpret_cast<const float4 *>(p + 4);
   }
+}
+// rows past n are written as zeros
+__device__ __forceinline__ void store_row8(u16 *hi, u16 *lo, const float4 &a, const float4 &b,
+                                           bool valid) {
+  const float x[8] = {valid ? a.x : 0.f, valid ? a.y : 0.f, valid ? a.z : 0.f, valid ? a.w : 0.f,
+                      valid ? b.x : 0.f, valid ? b.y : 0.f, valid ? b.z : 0.f, valid ? b.w : 0.f};
+  store8_split(hi, lo, x);
 }
 
 // Persistent: workgroup b handles items b, b + G, b + 2G, ... (G = grid size,
@@ -442,12 +462,11 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
   }
   // S1. K, Q rows -> LDS (bf16 hi/lo)
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = i * 512 + tid, row = idx >> 5, col = (idx & 31) * 4;
-    const float4 kv = row < n ? kr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-    const float4 qv = row < n ? qr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-    store4_split(kh + row * PR + col, klo + row * PR + col, kv.x, kv.y, kv.z, kv.w);
-    store4_split(qh + row * PR + col, qlo + row * PR + col, qv.x, qv.y, qv.z, qv.w);
+  for (int i = 0; i < 2; ++i) {
+    int row, col;
+    row8_of(i, tid, row, col);
+    store_row8(kh + row * PR + col, klo + row * PR + col, kr[2 * i], kr[2 * i + 1], row < n);
+    store_row8(qh + row * PR + col, qlo + row * PR + col, qr[2 * i], qr[2 * i + 1], row < n);
   }
   load_kq(in, nx, tid, kr, qr);
   __syncthreads();
@@ -491,10 +510,10 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = i * 512 + tid, row = idx >> 5, col = (idx & 31) * 4;
-    const float4 vv = row < n ? vr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-    store4_split(qh + row * PR + col, qlo + row * PR + col, vv.x, vv.y, vv.z, vv.w);
+  for (int i = 0; i < 2; ++i) {
+    int row, col;
+    row8_of(i, tid, row, col);
+    store_row8(qh + row * PR + col, qlo + row * PR + col, vr[2 * i], vr[2 * i + 1], row < n);
   }
   load_v(in, nx, tid, vr);
   __syncthreads();  // every diagonal block read before any is overwritten
