@@ -89,6 +89,25 @@ def chunked_flops(T: int, H: int, S: int, C: int = 64) -> float:
     return float(T) * H * (10 * C * S + 6 * S * S)
 
 
+def chunked_attainable(T: int, H: int, Hk: int, S: int, ws_bytes: int, tflops: float) -> dict:
+    """Roofline-attainable bf16 MFMA fraction of the chunked recurrence: its
+    algorithmic flops over its HBM bytes give the arithmetic intensity, and
+    min(peak, AI x 8 TB/s) / peak bounds the fraction any schedule reaches.
+    Two byte counts: the path's own I/O (q, k read once, v read, y written, g,
+    beta, state in and out) and that plus this two-pass design's workspace
+    (written once by phase A, read back by phase B)."""
+    fl = chunked_flops(T, H, S)
+    io = (2 * T * Hk * S + 2 * T * H * S + 2 * T * H + 2 * H * S * S) * 4
+    out = {}
+    for name, b in (("single_pass_io", io), ("with_workspace_round_trip", io + 2 * ws_bytes)):
+        ai = fl / b
+        att = min(BF16_PEAK_TFLOPS, ai * HBM_PEAK_GBS / 1e3)
+        out[name] = {"bytes": b, "flop_per_byte": ai, "attainable_tflops": att,
+                     "attainable_frac_of_bf16_peak": att / BF16_PEAK_TFLOPS,
+                     "measured_frac_of_attainable": tflops / att}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -339,6 +358,8 @@ def main():
             "ms": {"gate": seg[0], "conv": seg[1], "chunked_recurrence": seg[2], "norm": seg[3]},
             "chunked_algorithmic_tflops": fl / (seg[2] * 1e-3) / 1e12,
             "chunked_frac_of_bf16_peak": fl / (seg[2] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "chunked_attainable": chunked_attainable(T, PH, PHk, PS, ws.numel(),
+                                                     fl / (seg[2] * 1e-3) / 1e12),
         }
     except gdn.GdnError as e:
         prefill = {"error": str(e)}
