@@ -16,13 +16,15 @@
 //   K' = diag(e^{G_n-G}) K.
 // Only the last three lines depend on S0, so the work splits in two kernels:
 //
-//   k_chunk_prep (phase A) -- one workgroup per (sequence, head, chunk), all
-//     in parallel: everything that does not depend on S0, written to a
-//     workspace in the exact register layout the scan loads.
+//   k_chunk_prep (phase A) -- every (sequence, head, chunk) independently:
+//     everything that does not depend on S0, written to a workspace in the
+//     exact register layout the scan loads.  Persistent: one workgroup per CU
+//     walks its chunks, loading the next chunk while computing this one.
 //   k_chunk_scan (phase B) -- one workgroup per (sequence, head, block of 16
 //     value columns), walking the chunks in order: the value columns of S are
 //     independent, so 8 workgroups share a head, and they are mapped to one
-//     XCD so they share its L2.  Operands are prefetched two chunks ahead.
+//     XCD so they share its L2.  A chunk's operands are requested while the
+//     chunk before it runs.
 //
 // Precision: every contraction runs on MFMA v_mfma_f32_16x16x32_bf16 with each
 // fp32 operand split into bf16 hi + lo, accumulating hi*hi + hi*lo + lo*hi in
@@ -196,8 +198,8 @@ __device__ __forceinline__ int acc_off(int d, int m, int lane) {
 }
 
 // ----------------------------------------------------------------------------- phase A
-// One workgroup (8 waves) per (sequence, head, chunk).  All row-major LDS
-// tiles are bf16 hi/lo planes.  Plan (bytes):
+// One workgroup (8 waves) per CU, one (sequence, head, chunk) at a time.  All
+// row-major LDS tiles are bf16 hi/lo planes.  Plan (bytes):
 //   L_K : K rows [t][i]            -> later W rows [s][i]
 //   L_Q : Q rows [t][i] -> V rows  -> later Ut rows [s][j]
 //   L_T : T1 = T diag(beta e^G), T2 = T diag(beta)  [t][s]
@@ -781,8 +783,9 @@ __global__ __launch_bounds__(512) void k_chunk_scan(
                min(CH, n_tok - c * CH), scale, w, l16, kg);
   };
 
-  // Two chunks in flight: a chunk's operands are requested two chunks ahead.
-  // n_chunks is even (the workspace is padded with an identity chunk), so the
+  // Two operand sets: chunk c + 2's are requested as soon as chunk c has run
+  // (into the registers chunk c used), so each request has the whole of
+  // chunk c + 1 to arrive.  n_chunks is even (the workspace is padded with an identity chunk), so the
   // loop has no tail; a tail would make the compiler copy the operand
   // registers at the loop head, which waits for every load in flight.
   ChunkOps a, b;
