@@ -297,9 +297,39 @@ def main():
                              sc["z"].view(sn, sT, sH, sS), s_o.view(sn, sT, sH, sS),
                              scale=sw.scale, norm_eps=sw.norm_eps)
 
+    # the whole one-sequence step (gate, conv, recurrence, norm), eager and
+    # replayed from a HIP graph captured once (the launches then cost no host time)
+    s_hist = sc["conv_hist"].clone()
+    s_conv = torch.empty(sn, sT, sw.conv_dim, device=dev)
+    s_q = s_conv[..., :sw.Hk * sS].unflatten(-1, (sw.Hk, sS))
+    s_k = s_conv[..., sw.Hk * sS:2 * sw.Hk * sS].unflatten(-1, (sw.Hk, sS))
+    s_v = s_conv[..., 2 * sw.Hk * sS:].unflatten(-1, (sH, sS))
+
+    def small_step(i=0):
+        gdn.gdn_decay_gate(sc["alpha"], sc["dt"], sc["a"], s_g)
+        gdn.gdn_conv1d_silu_l2norm(sc["x"][..., :sw.conv_dim], sc["conv_w"], s_hist, s_conv,
+                                   qk_channels=sw.qk_channels, head_dim=sw.head_dim,
+                                   l2_eps=sw.l2_eps)
+        gdn.gdn_recurrence_decode(s_st, s_q, s_k, s_v, s_g.view(sn, sT, sH), sc["beta"], s_y,
+                                  scale=sw.scale)
+        gdn.gdn_gated_rmsnorm(s_y.view(sn * sT, sH, sS), sc["norm_w"], sc["z"], s_o,
+                              eps=sw.norm_eps)
+
+    step_eager = burst(small_step)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        small_step()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        small_step()
+    step_graph = burst(lambda i: graph.replay())
     small = {"workload": "decode: 1 seq x 1 token, 32 value / 16 q-k heads, 128x128 state",
-             "three_calls_ms": burst(small_three), "fused_ms": burst(small_fused)}
-    del s_st, s_g, s_y, s_o, sc
+             "three_calls_ms": burst(small_three), "fused_ms": burst(small_fused),
+             "step_eager_ms": step_eager, "step_graph_replay_ms": step_graph}
+    del graph, s_st, s_g, s_y, s_o, sc, s_hist, s_conv
 
     # ---------------------------------------------------------------- prefill pass
     pw = WORKLOADS["prefill"]

@@ -527,3 +527,65 @@ def test_stream_copy_exact():
     gdn().gdn_stream_copy(dst[:n * 4], src)
     assert bits_equal(dst[:n * 4], src)
     assert torch.isnan(dst[n * 4:]).all()
+
+
+# ------------------------------------------------------------------------------------- graph replay
+
+def test_decode_step_graph_replay_matches_eager():
+    # the decode step (gate -> conv -> recurrence -> norm) captured once into a
+    # HIP graph and replayed several times, with eager work and synchronisation
+    # between replays: every replay equals the eager step bit for bit
+    inp = inputs("decode")
+    wl = inp["wl"]
+    log_case("graph_replay", wl="decode")
+    n, T, H, Hk, S, C = wl.n_seq, wl.n_tok, wl.H, wl.Hk, wl.S, wl.conv_dim
+    cu = {k: on_dev(v) for k, v in inp.items() if isinstance(v, torch.Tensor)}
+    st = cu["state"].clone()
+    hist = cu["conv_hist"].clone()
+    conv_out = torch.empty(n, T, C, device=DEV)
+    g = torch.empty(n * T, H, device=DEV)
+    y = torch.empty(n, T, H, S, device=DEV)
+    out = torch.empty(n * T, H, S, device=DEV)
+    q = conv_out[..., :Hk * S].unflatten(-1, (Hk, S))
+    k = conv_out[..., Hk * S:2 * Hk * S].unflatten(-1, (Hk, S))
+    v = conv_out[..., 2 * Hk * S:].unflatten(-1, (H, S))
+
+    def step():
+        gdn().gdn_decay_gate(cu["alpha"], cu["dt"], cu["a"], g)
+        gdn().gdn_conv1d_silu_l2norm(cu["x"][..., :C], cu["conv_w"], hist, conv_out,
+                                     qk_channels=wl.qk_channels, head_dim=wl.head_dim,
+                                     l2_eps=wl.l2_eps)
+        gdn().gdn_recurrence_decode(st, q, k, v, g.view(n, T, H), cu["beta"], y, scale=wl.scale)
+        gdn().gdn_gated_rmsnorm(y.view(n * T, H, S), cu["norm_w"], cu["z"], out,
+                                eps=wl.norm_eps)
+
+    def reset():
+        st.copy_(cu["state"])
+        hist.copy_(cu["conv_hist"])
+
+    reset()
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (out, st, hist, g, y)]
+
+    reset()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()                                    # warm up the allocator-free path
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    reset()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(3):
+        reset()                                   # eager work between replays
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((out, st, hist, g, y), ref):
+            assert bits_equal(a, b)
