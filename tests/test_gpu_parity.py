@@ -589,3 +589,55 @@ def test_decode_step_graph_replay_matches_eager():
         torch.cuda.synchronize()
         for a, b in zip((out, st, hist, g, y), ref):
             assert bits_equal(a, b)
+
+
+# ------------------------------------------------------------------------------------- degenerate cases
+
+@pytest.mark.parametrize("path", ["decode", "chunked"])
+def test_no_decay_no_update_keeps_state_bits(path):
+    # g = 0 and beta = 0: S <- 1 * S and delta = 0, so the state must come back
+    # bit for bit (chunked: A = 0, T = I, W = Ut = 0, e^{G_n} = 1), and y is the
+    # readout of the unchanged state
+    T = 3 if path == "decode" else 130
+    inp = make_inputs("prefill", seed=91, n_tok=T, H=4, Hk=2, state_std=0.1)
+    wl = inp["wl"]
+    log_case("no_decay_no_update", path=path, T=T)
+    g0 = torch.zeros(wl.n_seq, T, wl.H)
+    b0 = torch.zeros(wl.n_seq, T, wl.H)
+    st = on_dev(inp["state"]).clone()
+    y = torch.empty(wl.n_seq, T, wl.H, wl.S, device=DEV)
+    args = (st, on_dev(inp["q"]), on_dev(inp["k"]), on_dev(inp["v"]), on_dev(g0), on_dev(b0), y)
+    if path == "decode":
+        gdn().gdn_recurrence_decode(*args, scale=wl.scale)
+    else:
+        gdn().gdn_recurrence_chunked(*args, scale=wl.scale)
+    assert bits_equal(st, on_dev(inp["state"]))
+    y_ref, _, _ = oracle.recurrence_seq(inp["state"], inp["q"], inp["k"], inp["v"], g0, b0,
+                                        wl.scale)
+    assert rel(y, y_ref) < (1e-4 if path == "decode" else 2e-3)
+
+
+@pytest.mark.parametrize("path", ["decode", "chunked"])
+def test_total_decay_forgets_the_state(path):
+    # g = -200: exp(g) underflows to 0 in fp32, so after a position the state
+    # holds only that position's update, whatever it held before
+    T = 2 if path == "decode" else 70
+    inp = make_inputs("prefill", seed=93, n_tok=T, H=4, Hk=2, state_std=1.0)
+    wl = inp["wl"]
+    log_case("total_decay", path=path, T=T)
+    g = torch.full((wl.n_seq, T, wl.H), -200.0)
+    st = on_dev(inp["state"]).clone()
+    y = torch.empty(wl.n_seq, T, wl.H, wl.S, device=DEV)
+    args = (st, on_dev(inp["q"]), on_dev(inp["k"]), on_dev(inp["v"]), on_dev(g),
+            on_dev(inp["beta"]), y)
+    if path == "decode":
+        gdn().gdn_recurrence_decode(*args, scale=wl.scale)
+    else:
+        gdn().gdn_recurrence_chunked(*args, scale=wl.scale)
+    zero = np.zeros_like(inp["state"].numpy())
+    y_ref, s_ref, _ = oracle.recurrence_seq(zero, inp["q"][:, -1:], inp["k"][:, -1:],
+                                            inp["v"][:, -1:], g[:, -1:], inp["beta"][:, -1:],
+                                            wl.scale)
+    tol = 1e-4 if path == "decode" else 2e-3
+    assert rel(st, s_ref) < tol
+    assert rel(y[:, -1:], y_ref) < tol
