@@ -803,6 +803,140 @@ __global__ __launch_bounds__(512) void k_chunk_scan(
   sp[3 * DK] = st[3];
 }
 
+// ---- phase B for grids that exceed one pass of the chip
+// One 16-wave workgroup per (sequence, head, pair of value blocks): waves
+// 8g .. 8g+7 run exactly the per-wave arithmetic of k_chunk_scan on value
+// block 2p + g, so the results are bit-identical to it.  The two groups share
+// one copy of each chunk's W, Q' and K' (the first 96 KB of its workspace,
+// copied byte for byte), which halves the head's operand reads from L2; the
+// price is that every wave now reads its fragments from LDS, about 0.9 us of
+// LDS traffic per chunk, so this form only pays once the 8-wave grid would
+// need a second pass (48 heads: 180 us against 270 us for 4096 positions).
+// The copy is staged through registers one chunk ahead: each thread holds 64
+// bytes of W and Q' and 32 bytes of K'.  W and Q' are rewritten in LDS right
+// after the barrier that ends their last reads (the U barrier), K' right
+// after the barrier that ends the state update's reads (the S barrier).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int OPS_WQ = (int)(4 * WS_PLANE);   // W and Q', workspace bytes [0, 64 KiB)
+constexpr int OPS_K = (int)(2 * WS_PLANE);    // K'^T, workspace bytes [64, 96 KiB)
+constexpr int PAIR_THREADS = 1024;
+static_assert(WS_W == 0 && WS_Q == 2 * WS_PLANE && WS_K == (size_t)OPS_WQ, "operand layout");
+static_assert(OPS_WQ % (16 * PAIR_THREADS) == 0 && OPS_K % (16 * PAIR_THREADS) == 0, "copy split");
+
+__global__ __launch_bounds__(PAIR_THREADS) void k_chunk_scan_pair(
+    float *__restrict__ state, int64_t st_seq, const unsigned char *__restrict__ ws,
+    float *__restrict__ y, int64_t y_tok, int64_t y_seq, int n_tok, int n_chunks, int H,
+    float scale) {
+  constexpr int NWQ = OPS_WQ / (16 * PAIR_THREADS), NK = OPS_K / (16 * PAIR_THREADS);
+  __shared__ __attribute__((aligned(16))) u16 ssh[2][DK * SPB], ssl[2][DK * SPB];
+  __shared__ __attribute__((aligned(16))) u16 suh[2][CH * SPB], sul[2][CH * SPB];
+  __shared__ __attribute__((aligned(16))) unsigned char ops[OPS_WQ + OPS_K];
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
+  const int grp = tid >> 9, w = (tid >> 6) & 7;
+  // XCD-aware order as in k_chunk_scan, so the 4 workgroups of a head share an
+  // L2; the grid (4 per head) need not be a multiple of 8: XCD x < r of
+  // nwg = 8q + r takes q + 1 consecutive units, the others q
+  const int nwg = gridDim.x, q8 = nwg / 8, r8 = nwg % 8;
+  const int xcd = blockIdx.x % 8, idx = blockIdx.x / 8;
+  const int unit = (xcd < r8 ? xcd * (q8 + 1) : r8 * (q8 + 1) + (xcd - r8) * q8) + idx;
+  const int pair = unit % (NVB / 2), sh = unit / (NVB / 2), h = sh % H, s = sh / H;
+  const int blk = 2 * pair + grp;
+
+  float *sp = state + s * st_seq + (int64_t)h * DK * DV +
+              (int64_t)(blk * NBLK + 4 * kg) * DK + 16 * w + l16;
+  f32x4 st = {sp[0], sp[DK], sp[2 * DK], sp[3 * DK]};
+  const unsigned char *wh = ws + ((size_t)s * H + h) * n_chunks * WS_CHUNK;
+  float *yh = y + s * y_seq + (int64_t)h * DV + blk * NBLK;
+  auto chunk_ptr = [&](int c) { return wh + (size_t)min(c, n_chunks - 1) * WS_CHUNK; };
+  u16 *s_hi = ssh[grp], *s_lo = ssl[grp], *u_hi = suh[grp], *u_lo = sul[grp];
+  const u16 *b_lds = reinterpret_cast<const u16 *>(ops + (w < 4 ? WS_W : WS_Q));
+  const u16 *k_lds = reinterpret_cast<const u16 *>(ops + OPS_WQ);
+  const int add_off = acc_off(blk, w & 3, lane);
+  const int t = 16 * (w & 3) + l16;   // this lane's token; values 4kg + r
+
+  u32x4 rwq[NWQ], rk[NK];
+  auto load_wq = [&](const unsigned char *wc) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NWQ; ++i)
+      rwq[i] = *reinterpret_cast<const u32x4 *>(wc + 16 * (tid + PAIR_THREADS * i));
+  };
+  auto load_k = [&](const unsigned char *wc) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NK; ++i)
+      rk[i] = *reinterpret_cast<const u32x4 *>(wc + OPS_WQ + 16 * (tid + PAIR_THREADS * i));
+  };
+  auto put_wq = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NWQ; ++i)
+      *reinterpret_cast<u32x4 *>(ops + 16 * (tid + PAIR_THREADS * i)) = rwq[i];
+  };
+  auto put_k = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NK; ++i)
+      *reinterpret_cast<u32x4 *>(ops + OPS_WQ + 16 * (tid + PAIR_THREADS * i)) = rk[i];
+  };
+  auto load_add = [&](const unsigned char *wc, float4 &add, float &gam)
+      __attribute__((always_inline)) {
+    const float *addp = reinterpret_cast<const float *>(wc + (w < 4 ? WS_U : WS_O));
+    add = *reinterpret_cast<const float4 *>(addp + add_off);
+    gam = *reinterpret_cast<const float *>(wc + WS_G);
+  };
+  auto run = [&](int c, const float4 &add, float gam) __attribute__((always_inline)) {
+    store4_split(s_hi + (16 * w + l16) * SPB + 4 * kg, s_lo + (16 * w + l16) * SPB + 4 * kg,
+                 st[0], st[1], st[2], st[3]);
+    __syncthreads();   // S barrier: W, Q' of chunk c and the S tiles are in LDS
+    put_k();           // K' of chunk c, first read after the U barrier
+    load_k(chunk_ptr(c + 1));
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      Frag b;
+      b.hi = *reinterpret_cast<const bf16x8 *>(b_lds + frag_off(w & 3, ks, 4, 0, lane));
+      b.lo = *reinterpret_cast<const bf16x8 *>(b_lds + frag_off(w & 3, ks, 4, 1, lane));
+      acc = mfma3(frag_tr(s_hi, s_lo, SPB, 32 * ks, 0, kg, l16), b, acc);
+    }
+    if (w < 4) {
+      store4_split(u_hi + t * SPB + 4 * kg, u_lo + t * SPB + 4 * kg, add.x - acc[0],
+                   add.y - acc[1], add.z - acc[2], add.w - acc[3]);
+    } else if (t < min(CH, n_tok - c * CH)) {
+      *reinterpret_cast<float4 *>(yh + (int64_t)(c * CH + t) * y_tok + 4 * kg) =
+          make_float4(scale * (acc[0] + add.x), scale * (acc[1] + add.y),
+                      scale * (acc[2] + add.z), scale * (acc[3] + add.w));
+    }
+    __syncthreads();   // U barrier: K' and the U tiles are in LDS, W and Q' are read
+    put_wq();          // W, Q' of chunk c + 1
+    load_wq(chunk_ptr(c + 2));
+    st = st * gam;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      Frag kf;
+      kf.hi = *reinterpret_cast<const bf16x8 *>(k_lds + frag_off(w, ks, 2, 0, lane));
+      kf.lo = *reinterpret_cast<const bf16x8 *>(k_lds + frag_off(w, ks, 2, 1, lane));
+      st = mfma3(frag_tr(u_hi, u_lo, SPB, 32 * ks, 0, kg, l16), kf, st);
+    }
+  };
+
+  load_wq(chunk_ptr(0));
+  put_wq();   // visible after the first S barrier
+  load_wq(chunk_ptr(1));
+  load_k(chunk_ptr(0));
+  float4 add0, add1;
+  float gam0, gam1;
+  load_add(chunk_ptr(0), add0, gam0);
+  load_add(chunk_ptr(1), add1, gam1);
+  // n_chunks is even, as for k_chunk_scan
+  for (int c = 0; c < n_chunks; c += 2) {
+    run(c, add0, gam0);
+    load_add(chunk_ptr(c + 2), add0, gam0);
+    run(c + 1, add1, gam1);
+    load_add(chunk_ptr(c + 3), add1, gam1);
+  }
+  sp[0] = st[0];
+  sp[DK] = st[1];
+  sp[2 * DK] = st[2];
+  sp[3 * DK] = st[3];
+}
+
 }  // namespace
 
 // chunks per sequence in the workspace: ceil(n_tok / 64) rounded up to even
@@ -844,7 +978,14 @@ int launch_recur_chunked(const RecurArgs &a, int chunk, void *ws, size_t ws_byte
                          a.qk_seq, a.v, a.v_tok, a.v_seq, a.g, a.beta, wsb, a.n_tok, n_chunks,
                          a.H, a.Hk, n_items);
   if (rc != GDN_OK) return rc;
+  // phase B: 8-wave workgroups while they fit in one pass of the chip (one per
+  // CU: their registers allow no second); past that, the 16-wave form whose
+  // pairs of value blocks share operand copies
   const int nwg = a.n_seq * a.H * NVB;  // a multiple of 8 (NVB == 8)
+  if (nwg > cus)
+    return launch_kernel(k_chunk_scan_pair, dim3(nwg / 2), dim3(PAIR_THREADS), 0, stream,
+                         a.state, a.st_seq, (const unsigned char *)wsb, a.y, a.y_tok, a.y_seq,
+                         a.n_tok, n_chunks, a.H, a.scale);
   return launch_kernel(k_chunk_scan, dim3(nwg), dim3(512), 0, stream, a.state, a.st_seq,
                        (const unsigned char *)wsb, a.y, a.y_tok, a.y_seq, a.n_tok, n_chunks, a.H,
                        a.scale);

@@ -506,6 +506,49 @@ def test_chunked_ragged_and_weak_decay(T, H, Hk, n_seq, g_scale):
     assert ey < 2e-3 and es < 2e-3
 
 
+@pytest.mark.parametrize("T,H,Hk,n_seq", [(130, 33, 11, 1), (64, 20, 5, 2)])
+def test_chunked_paired_scan_grid(T, H, Hk, n_seq):
+    # more than 256 sequence x head x 16-column units, so the scan runs as
+    # 16-wave workgroups over pairs of value blocks; 33 heads give a grid of
+    # 132 workgroups, not a multiple of the 8 XCDs
+    inp = make_inputs("prefill", seed=67, n_tok=T, H=H, Hk=Hk, n_seq=n_seq, state_std=0.05)
+    wl = inp["wl"]
+    log_case("chunked_paired", T=T, H=H, Hk=Hk, n_seq=n_seq)
+    assert n_seq * H * 8 > 256
+    g3 = oracle_g(inp)
+    y, st = run_chunked(inp, g3)
+    y_ref, s_ref, _ = oracle.recurrence_seq(inp["state"], inp["q"], inp["k"], inp["v"], g3,
+                                            inp["beta"], wl.scale)
+    ey, es = rel(y, y_ref), rel(st, s_ref)
+    print(f"[chunked paired] H={H} rel err y {ey:.3e} state {es:.3e}", flush=True)
+    assert ey < 2e-3 and es < 2e-3
+
+
+def test_chunked_paired_scan_bit_identical():
+    # heads are independent: one call over 48 heads (paired 16-wave scan) must
+    # equal, bit for bit, two calls over 24 heads each (8-wave scan, 192
+    # workgroups), since both forms run the same per-wave arithmetic
+    n, T, H, Hk = 1, 200, 48, 16
+    inp = make_inputs("prefill", seed=73, n_tok=T, H=H, Hk=Hk, n_seq=n, state_std=0.05)
+    wl = inp["wl"]
+    log_case("chunked_paired_bits", T=T, H=H, Hk=Hk)
+    q, k, v, beta = (on_dev(inp[x]) for x in ("q", "k", "v", "beta"))
+    g3 = on_dev(oracle_g(inp))
+    st_full = on_dev(inp["state"]).clone()
+    y_full = torch.full_like(v, float("nan"))
+    gdn().gdn_recurrence_chunked(st_full, q, k, v, g3, beta, y_full, scale=wl.scale, chunk=64)
+    st_half = on_dev(inp["state"]).clone()
+    y_half = torch.full_like(v, float("nan"))
+    hv, hk = H // 2, Hk // 2
+    for i in range(2):
+        vs, ks = slice(i * hv, (i + 1) * hv), slice(i * hk, (i + 1) * hk)
+        gdn().gdn_recurrence_chunked(st_half[:, vs], q[:, :, ks], k[:, :, ks], v[:, :, vs],
+                                     g3[:, :, vs].contiguous(), beta[:, :, vs].contiguous(),
+                                     y_half[:, :, vs], scale=wl.scale, chunk=64)
+    assert bits_equal(y_full, y_half)
+    assert bits_equal(st_full, st_half)
+
+
 def test_chunked_deterministic():
     inp = make_inputs("prefill", seed=71, n_tok=512)
     log_case("chunked_determinism")
