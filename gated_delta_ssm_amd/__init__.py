@@ -45,6 +45,10 @@ _SIGS = {
     "gdn_decode_fused": (_I, [_P, _L, _P, _P, _L, _L, _P, _L, _L, _P, _P, _P, _P, _P, _P, _L,
                               _L, _P, _L, _L, _P, _P, _L, _L, _P, _L, _I, _I, _I, _I, _I, _F,
                               _F, _P]),
+    "gdn_decode_step_workspace_bytes": (_SZ, [_I, _I]),
+    "gdn_decode_step": (_I, [_P, _L, _P, _L, _L, _P, _P, _L, _P, _L, _L, _P, _P, _P, _P, _P,
+                             _P, _L, _L, _P, _L, _L, _P, _P, _L, _L, _P, _L, _I, _I, _I, _I,
+                             _I, _I, _F, _F, _F, _P, _SZ, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -283,6 +287,85 @@ def gdn_decode_fused(state: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: t
         _ptr(norm_w), _ptr(z), z.stride(1), z.stride(0), _ptr(out), out.stride(1),
         out.stride(0), _ptr(g), _ptr(y), y_tok, y_seq, _ptr(snap), sn_seq, n_seq, n_tok, H,
         Hk, S, scale, norm_eps, _stream(stream, out)))
+    return out
+
+
+def gdn_decode_step_workspace_bytes(n_seq: int, n_qk_heads: int) -> int:
+    return int(_lib.gdn_decode_step_workspace_bytes(n_seq, n_qk_heads))
+
+
+def gdn_decode_step(state: torch.Tensor, x: torch.Tensor, conv_w: torch.Tensor,
+                    conv_state: torch.Tensor, alpha: torch.Tensor, dt: torch.Tensor,
+                    a: torch.Tensor, beta: torch.Tensor, norm_w: torch.Tensor, z: torch.Tensor,
+                    out: torch.Tensor, *, scale: float, l2_eps: float, norm_eps: float,
+                    workspace: torch.Tensor | None = None, g: torch.Tensor | None = None,
+                    y: torch.Tensor | None = None, snap: torch.Tensor | None = None,
+                    conv_snap: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Conv1d + SiLU + L2 -> decay gate -> recurrence -> gated RMSNorm in one
+    launch.  x [n_seq][n_tok][>= conv_dim] (any row strides) with conv_dim =
+    (2*Hk + H)*S channels q | k | v; conv_w [conv_dim][d_conv]; conv_state
+    [n_seq][conv_dim][d_conv-1] rolled in place; the other tensors as
+    gdn_decode_fused; conv_snap [n_seq][n_tok-1][conv_dim][d_conv-1].
+    workspace: int32 counters, zero before first use and left zero by every
+    call (allocated zeroed here when None)."""
+    n_seq, H, S, _ = state.shape
+    C, D = conv_w.shape
+    if C % S or (C // S - H) < 2 or (C // S - H) % 2:
+        raise ValueError(f"conv_dim {C} is not (2*Hk + H)*S for H={H}, S={S}")
+    Hk = (C // S - H) // 2
+    n_tok = x.shape[1]
+    if x.dim() != 3 or x.shape[0] != n_seq or x.shape[2] < C:
+        raise ValueError("x shape mismatch")
+    if tuple(conv_state.shape) != (n_seq, C, D - 1):
+        raise ValueError("conv_state shape mismatch")
+    if tuple(out.shape) != (n_seq, n_tok, H, S) or z.shape != out.shape:
+        raise ValueError("z / out shape mismatch")
+    if tuple(alpha.shape) != (n_seq, n_tok, H) or beta.shape != alpha.shape:
+        raise ValueError("alpha / beta shape mismatch")
+    if tuple(dt.shape) != (H,) or tuple(a.shape) != (H,) or tuple(norm_w.shape) != (S,):
+        raise ValueError("dt / a / norm_w shape mismatch")
+    _dev_f32("state", state, 3)
+    _dev_f32("x", x, 1)
+    _dev_f32("conv_w", conv_w, 2)
+    _dev_f32("conv_state", conv_state, 2)
+    for n, t in (("z", z), ("out", out)):
+        _dev_f32(n, t, 2)
+    for n, t in (("alpha", alpha), ("beta", beta)):
+        _dev_f32(n, t, 3)
+    for n, t in (("dt", dt), ("a", a), ("norm_w", norm_w)):
+        _dev_f32(n, t, 1)
+    y_tok = y_seq = 0
+    if g is not None:
+        _dev_f32("g", g, 3)
+        if g.shape != alpha.shape:
+            raise ValueError("g shape mismatch")
+    if y is not None:
+        _dev_f32("y", y, 2)
+        if y.shape != out.shape:
+            raise ValueError("y shape mismatch")
+        y_seq, y_tok = y.stride(0), y.stride(1)
+    sn_seq = 0
+    if snap is not None:
+        _dev_f32("snap", snap, 4)
+        if tuple(snap.shape) != (n_seq, n_tok - 1, H, S, S):
+            raise ValueError("snap shape mismatch")
+        sn_seq = snap.stride(0)
+    cs_tok = cs_seq = 0
+    if conv_snap is not None:
+        _dev_f32("conv_snap", conv_snap, 2)
+        if tuple(conv_snap.shape) != (n_seq, n_tok - 1, C, D - 1):
+            raise ValueError("conv_snap shape mismatch")
+        cs_seq, cs_tok = conv_snap.stride(0), conv_snap.stride(1)
+    need = gdn_decode_step_workspace_bytes(n_seq, Hk)
+    if workspace is None:
+        workspace = torch.zeros(max(need, 4) // 4, dtype=torch.int32, device=state.device)
+    _check("gdn_decode_step", _lib.gdn_decode_step(
+        _ptr(state), state.stride(0), _ptr(x), x.stride(1), x.stride(0), _ptr(conv_w),
+        _ptr(conv_state), conv_state.stride(0), _ptr(conv_snap), cs_tok, cs_seq, _ptr(alpha),
+        _ptr(dt), _ptr(a), _ptr(beta), _ptr(norm_w), _ptr(z), z.stride(1), z.stride(0),
+        _ptr(out), out.stride(1), out.stride(0), _ptr(g), _ptr(y), y_tok, y_seq, _ptr(snap),
+        sn_seq, n_seq, n_tok, H, Hk, S, D, scale, l2_eps, norm_eps, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream, out)))
     return out
 
 

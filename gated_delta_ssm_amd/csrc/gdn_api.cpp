@@ -144,4 +144,61 @@ int gdn_decode_fused(float *state, int64_t state_seq_stride, const float *q, con
   return gdn::launch_decode_fused(fa, stream);
 }
 
+size_t gdn_decode_step_workspace_bytes(int n_seq, int n_qk_heads) {
+  return gdn::step_workspace_bytes(n_seq, n_qk_heads);
+}
+
+int gdn_decode_step(float *state, int64_t state_seq_stride, const float *x, int64_t x_tok_stride,
+                    int64_t x_seq_stride, const float *conv_w, float *conv_state,
+                    int64_t conv_state_seq_stride, float *conv_snap,
+                    int64_t conv_snap_tok_stride, int64_t conv_snap_seq_stride,
+                    const float *alpha, const float *dt, const float *a, const float *beta,
+                    const float *norm_w, const float *z, int64_t z_tok_stride,
+                    int64_t z_seq_stride, float *out, int64_t out_tok_stride,
+                    int64_t out_seq_stride, float *g, float *y, int64_t y_tok_stride,
+                    int64_t y_seq_stride, float *snap, int64_t snap_seq_stride, int n_seq,
+                    int n_tok, int n_v_heads, int n_qk_heads, int S, int d_conv, float scale,
+                    float l2_eps, float norm_eps, void *workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+  const int rc = gdn::check_step(
+      state, state_seq_stride, x, x_tok_stride, x_seq_stride, conv_w, conv_state,
+      conv_state_seq_stride, conv_snap, conv_snap_tok_stride, conv_snap_seq_stride, alpha, dt, a,
+      beta, norm_w, z, z_tok_stride, z_seq_stride, out, out_tok_stride, out_seq_stride, g, y,
+      y_tok_stride, y_seq_stride, snap, snap_seq_stride, n_seq, n_tok, n_v_heads, n_qk_heads, S,
+      d_conv, workspace, workspace_bytes);
+  if (rc != GDN_OK) return rc;
+  gdn::StepArgs sa{};
+  sa.f.r = gdn::RecurArgs{state,          state_seq_stride, nullptr,     nullptr,
+                          0,              0,                nullptr,     0,
+                          0,              nullptr,          beta,        out,
+                          out_tok_stride, out_seq_stride,   snap,        snap_seq_stride,
+                          n_seq,          n_tok,            n_v_heads,   n_qk_heads,
+                          S,              scale};
+  sa.f.alpha = alpha;
+  sa.f.dt = dt;
+  sa.f.a = a;
+  sa.f.w = norm_w;
+  sa.f.z = z;
+  sa.f.z_tok = z_tok_stride;
+  sa.f.z_seq = z_seq_stride;
+  sa.f.g = g;
+  sa.f.y = y;
+  sa.f.y_tok = y_tok_stride;
+  sa.f.y_seq = y_seq_stride;
+  sa.f.eps = norm_eps;
+  sa.x = x;
+  sa.x_tok = x_tok_stride;
+  sa.x_seq = x_seq_stride;
+  sa.cw = conv_w;
+  sa.hist = conv_state;
+  sa.h_seq = conv_state_seq_stride;
+  sa.csnap = conv_snap;
+  sa.cs_tok = conv_snap_tok_stride;
+  sa.cs_seq = conv_snap_seq_stride;
+  sa.D = d_conv;
+  sa.l2_eps = l2_eps;
+  sa.cnt = static_cast<int *>(workspace);
+  return gdn::launch_decode_step(sa, stream);
+}
+
 }  // extern "C"

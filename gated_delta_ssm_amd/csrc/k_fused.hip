@@ -22,11 +22,11 @@
 // position suffices.
 //
 // When to use it: the single launch replaces three, which dominates at small
-// batches (one sequence of 32 heads: 17.4 us against 27.4 us for the three
-// calls).  At 64 sequences x 48 heads the three calls are faster (69 us
-// against 80 us): a whole head per workgroup means 16-wave workgroups, which
-// stream the state about 6% slower than the decode kernel's 4-wave ones, and
-// the per-position barrier holds every wave of a head to the slowest.
+// batches (one sequence of 32 heads: 15.3 us against 28.5 us for the three
+// calls).  At 64 sequences x 48 heads the two are even (70.2 us against
+// 70.9 us): a whole head per workgroup streams the state a little slower than
+// the decode kernel's 4-wave blocks, and the per-position barrier holds every
+// wave of a head to the slowest.
 #include <hip/hip_runtime.h>
 
 #include "gate.hpp"
@@ -39,7 +39,7 @@
 namespace gdn {
 
 template <int S, int RG>
-__global__ __launch_bounds__(1024) void k_decode_fused(
+__global__ __launch_bounds__(16 * S / RG) void k_decode_fused(
     float *__restrict__ state, int64_t st_seq, const float *__restrict__ q,
     const float *__restrict__ k, int64_t qk_tok, int64_t qk_seq, const float *__restrict__ v,
     int64_t v_tok, int64_t v_seq, const float *__restrict__ alpha, const float *__restrict__ dt,
@@ -133,12 +133,16 @@ int run_fused(const FusedArgs &a, hipStream_t stream) {
 }  // namespace
 
 int launch_decode_fused(const FusedArgs &a, hipStream_t stream) {
-  // rows per lane: enough that one workgroup (at most 16 waves) holds a head
+  // rows per lane: enough that one workgroup (at most 16 waves) holds a head;
+  // at S = 128, 4 rows per lane (8 waves) beat 2 (16 waves) from one sequence
+  // (15.3 against 16.0 us, 32 heads) to 64 (70.2 against 73.4 us, 48 heads)
+  // at S = 256, 8 rows per lane keep the state in registers (with 4 the
+  // 16-wave bound of 128 registers spills)
   switch (a.r.S) {
     case 32: return run_fused<32, 1>(a, stream);
     case 64: return run_fused<64, 1>(a, stream);
-    case 128: return run_fused<128, 2>(a, stream);
-    case 256: return run_fused<256, 4>(a, stream);
+    case 128: return run_fused<128, 4>(a, stream);
+    case 256: return run_fused<256, 8>(a, stream);
     default: return GDN_ERR_UNSUPPORTED;
   }
 }

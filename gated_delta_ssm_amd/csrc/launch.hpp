@@ -94,4 +94,21 @@ struct FusedArgs {
 };
 int launch_decode_fused(const FusedArgs &a, hipStream_t stream);
 
+// Fused decode step: conv -> gate -> recurrence -> norm.  f.r.q, f.r.k, f.r.v
+// are unused (the conv produces them on chip); cnt is the ticket workspace.
+struct StepArgs {
+  FusedArgs f;
+  const float *x;
+  int64_t x_tok, x_seq;
+  const float *cw;
+  float *hist;
+  int64_t h_seq;
+  float *csnap;
+  int64_t cs_tok, cs_seq;
+  int D;
+  float l2_eps;
+  int *cnt;
+};
+int launch_decode_step(const StepArgs &a, hipStream_t stream);
+
 }  // namespace gdn

@@ -219,4 +219,74 @@ int check_fused(const float *state, int64_t st_seq, const float *q, const float 
   return GDN_OK;
 }
 
+size_t step_workspace_bytes(int n_seq, int Hk) {
+  if (n_seq < 1 || Hk < 1) return 0;
+  return (size_t)n_seq * (size_t)Hk * 2 * sizeof(int32_t);
+}
+
+int check_step(const float *state, int64_t st_seq, const float *x, int64_t x_tok, int64_t x_seq,
+               const float *cw, const float *hist, int64_t h_seq, const float *csnap,
+               int64_t cs_tok, int64_t cs_seq, const float *alpha, const float *dt,
+               const float *a, const float *beta, const float *w, const float *z, int64_t z_tok,
+               int64_t z_seq, const float *out, int64_t o_tok, int64_t o_seq, const float *g,
+               const float *y, int64_t y_tok, int64_t y_seq, const float *snap, int64_t sn_seq,
+               int n_seq, int n_tok, int H, int Hk, int S, int D, const void *ws,
+               size_t ws_bytes) {
+  if (n_seq < 1 || n_tok < 1 || H < 1 || Hk < 1 || H % Hk != 0) return GDN_ERR_SHAPE;
+  if (n_tok > 8) return GDN_ERR_SHAPE;
+  if (D < 2 || D > 8) return GDN_ERR_SHAPE;
+  if (x_tok < 0 || x_seq < 0 || h_seq < 0 || cs_tok < 0 || cs_seq < 0) return GDN_ERR_SHAPE;
+  if (!x || !cw || !hist) return GDN_ERR_NULL;
+  // the recurrence, gate and norm rules, with q, k, v the channel ranges of x
+  const int64_t qk = (int64_t)Hk * S;
+  const int rc = check_fused(state, st_seq, x, x + qk, x_tok, x_seq, x + 2 * qk, x_tok, x_seq,
+                             alpha, dt, a, beta, w, z, z_tok, z_seq, out, o_tok, o_seq, g, y,
+                             y_tok, y_seq, snap, sn_seq, n_seq, n_tok, H, Hk, S);
+  if (rc != GDN_OK) return rc;
+  // the conv rules for this channel layout (q and k L2-normalised per S-wide
+  // head, which check_fused has already limited to the supported widths)
+  const int64_t C = (2 * (int64_t)Hk + H) * S;
+  if (C > INT32_MAX / 8) return GDN_ERR_SHAPE;
+  if (n_tok > 1 && x_tok < C) return GDN_ERR_SHAPE;
+  const int64_t hlen = C * (D - 1);
+  if (!rows_disjoint(n_seq, h_seq, 1, 0, hlen)) return GDN_ERR_SHAPE;
+  const int n_snap = n_tok - 1;
+  if (csnap && n_snap > 0 && !rows_disjoint(n_seq, cs_seq, n_snap, cs_tok, hlen))
+    return GDN_ERR_SHAPE;
+  // 16-byte conv accesses
+  if (!aligned(x, 16) || !aligned(cw, 16) || !aligned(hist, 16) || (csnap && !aligned(csnap, 16)) ||
+      x_tok % 4 || x_seq % 4 || h_seq % 4 || cs_tok % 4 || cs_seq % 4)
+    return GDN_ERR_SHAPE;
+  if (!ws || ws_bytes < step_workspace_bytes(n_seq, Hk) || !aligned(ws, 4))
+    return GDN_ERR_WORKSPACE;
+  const int64_t row = (int64_t)H * S, st_len = (int64_t)S * S * H;
+  const Span in[] = {span_of(x, n_seq, x_seq, n_tok, x_tok, C),
+                     span_of(cw, 1, 0, 1, 0, (int64_t)C * D),
+                     span_of(alpha, 1, 0, 1, 0, (int64_t)n_seq * n_tok * H),
+                     span_of(beta, 1, 0, 1, 0, (int64_t)n_seq * n_tok * H),
+                     span_of(dt, 1, 0, 1, 0, H),
+                     span_of(a, 1, 0, 1, 0, H),
+                     span_of(w, 1, 0, 1, 0, S),
+                     span_of(z, n_seq, z_seq, n_tok, z_tok, row)};
+  const Span outs[] = {span_of(state, n_seq, st_seq, 1, 0, st_len),
+                       span_of(out, n_seq, o_seq, n_tok, o_tok, row),
+                       g ? span_of(g, 1, 0, 1, 0, (int64_t)n_seq * n_tok * H) : Span{},
+                       y ? span_of(y, n_seq, y_seq, n_tok, y_tok, row) : Span{},
+                       snap && n_snap > 0 ? span_of(snap, n_seq, sn_seq, n_snap, st_len, st_len)
+                                          : Span{},
+                       span_of(hist, n_seq, h_seq, 1, 0, hlen),
+                       csnap && n_snap > 0 ? span_of(csnap, n_seq, cs_seq, n_snap, cs_tok, hlen)
+                                           : Span{},
+                       Span{(uintptr_t)ws, (uintptr_t)ws + ws_bytes}};
+  constexpr int NO = sizeof(outs) / sizeof(outs[0]);
+  for (const Span &o : outs)
+    for (const Span &i : in)
+      if (overlap(o, i)) return GDN_ERR_ALIAS;
+  for (int i = 0; i < NO; ++i)
+    for (int j = i + 1; j < NO; ++j)
+      if (overlap(outs[i], outs[j])) return GDN_ERR_ALIAS;
+  if (D > 4) return GDN_ERR_UNSUPPORTED;
+  return GDN_OK;
+}
+
 }  // namespace gdn

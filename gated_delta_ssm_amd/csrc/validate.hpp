@@ -35,4 +35,15 @@ int check_fused(const float *state, int64_t st_seq, const float *q, const float 
                 int64_t y_seq, const float *snap, int64_t sn_seq, int n_seq, int n_tok, int H,
                 int Hk, int S);
 
+size_t step_workspace_bytes(int n_seq, int Hk);
+
+int check_step(const float *state, int64_t st_seq, const float *x, int64_t x_tok, int64_t x_seq,
+               const float *cw, const float *hist, int64_t h_seq, const float *csnap,
+               int64_t cs_tok, int64_t cs_seq, const float *alpha, const float *dt,
+               const float *a, const float *beta, const float *w, const float *z, int64_t z_tok,
+               int64_t z_seq, const float *out, int64_t o_tok, int64_t o_seq, const float *g,
+               const float *y, int64_t y_tok, int64_t y_seq, const float *snap, int64_t sn_seq,
+               int n_seq, int n_tok, int H, int Hk, int S, int D, const void *ws,
+               size_t ws_bytes);
+
 }  // namespace gdn

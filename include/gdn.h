@@ -234,6 +234,59 @@ int gdn_decode_fused(float *state, int64_t state_seq_stride, const float *q, con
                      int64_t snap_seq_stride, int n_seq, int n_tok, int n_v_heads,
                      int n_qk_heads, int S, float scale, float norm_eps, hipStream_t stream);
 
+/*
+ * Workspace bytes gdn_decode_step needs: n_seq * n_qk_heads * 2 int32
+ * counters (0 if the sizes are invalid).
+ */
+size_t gdn_decode_step_workspace_bytes(int n_seq, int n_qk_heads);
+
+/*
+ * The whole decode / K-position verify layer core in one launch: conv1d +
+ * SiLU + per-head L2 (as gdn_conv1d_silu_l2norm) -> decay gate -> recurrence
+ * -> gated RMSNorm (as gdn_decode_fused).  [AT] gdn_verify_fused_conv_k2
+ * (the conv, its rollback snapshot and the recurrence of a K = 2 verify in
+ * one launch) and conv1d_update_l2norm (fusing neighbouring ops saves
+ * launches per layer); [FM] header notes (the gate rides with its
+ * neighbours).
+ *
+ * The conv row of a position carries conv_dim = (2*n_qk_heads + n_v_heads)*S
+ * channels: q heads at [0, Hk*S), k heads at [Hk*S, 2*Hk*S), v heads at
+ * [2*Hk*S, conv_dim), i.e. qk_channels = 2*Hk*S and head_dim = S in the terms
+ * of gdn_conv1d_silu_l2norm.  The conv outputs feed the recurrence on chip
+ * and are not written out.
+ *
+ *   x, conv_w, conv_state, conv_snap: as gdn_conv1d_silu_l2norm with that
+ *          conv_dim; x, conv_w, conv_state and conv_snap 16-byte aligned,
+ *          their strides multiples of 4                             (in / in/out)
+ *   state, alpha, dt, a, beta, norm_w, z, out, g, y, snap: as gdn_decode_fused
+ *   workspace: at least gdn_decode_step_workspace_bytes(n_seq, n_qk_heads)
+ *          bytes of device memory, 4-byte aligned, ZERO-FILLED by the caller
+ *          before its first use; the work of every call that returns GDN_OK
+ *          leaves it zero-filled again.  Calls whose work may overlap in time
+ *          (other streams) need workspaces of their own.
+ *
+ * The value heads of one query/key group all read the group's q/k conv
+ * history; each takes a ticket from a workspace counter once it has read it,
+ * and the last one writes the new history, so no workgroup waits for another.
+ * Results are bit-identical to gdn_conv1d_silu_l2norm into a buffer followed
+ * by gdn_decode_fused on its q, k, v channels.  1 <= n_tok <= 8; S in {32,
+ * 64, 128, 256}; d_conv in {2, 3, 4} (2..8 are valid widths; the others
+ * return GDN_ERR_UNSUPPORTED).  No output may overlap an input, another
+ * output or the workspace.
+ */
+int gdn_decode_step(float *state, int64_t state_seq_stride, const float *x, int64_t x_tok_stride,
+                    int64_t x_seq_stride, const float *conv_w, float *conv_state,
+                    int64_t conv_state_seq_stride, float *conv_snap,
+                    int64_t conv_snap_tok_stride, int64_t conv_snap_seq_stride,
+                    const float *alpha, const float *dt, const float *a, const float *beta,
+                    const float *norm_w, const float *z, int64_t z_tok_stride,
+                    int64_t z_seq_stride, float *out, int64_t out_tok_stride,
+                    int64_t out_seq_stride, float *g, float *y, int64_t y_tok_stride,
+                    int64_t y_seq_stride, float *snap, int64_t snap_seq_stride, int n_seq,
+                    int n_tok, int n_v_heads, int n_qk_heads, int S, int d_conv, float scale,
+                    float l2_eps, float norm_eps, void *workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -162,6 +162,51 @@ def test_fused_validation():
     assert fused(snap=FAKE + 22 * MB, sns=4 * 32 * 32) == ERR_ALIAS    # snapshot over norm_w
 
 
+def step(**kw):
+    S, H, Hk, n = 32, 4, 2, 2
+    T = kw.pop("T", 2)
+    MB = 1 << 20
+    C = (2 * Hk + H) * S
+    a = dict(state=FAKE, sts=H * S * S, x=FAKE + 4 * MB, xt=C, xs=2 * C, cw=FAKE + 5 * MB,
+             hist=FAKE + 6 * MB, hs=3 * C, csnap=None, cst=0, css=0, alpha=FAKE + 16 * MB,
+             dt=FAKE + 17 * MB, a=FAKE + 18 * MB, beta=FAKE + 20 * MB, w=FAKE + 22 * MB,
+             z=FAKE + 24 * MB, zt=H * S, zs=2 * H * S, out=FAKE + 28 * MB, ot=H * S,
+             os=2 * H * S, g=None, y=None, yt=0, ys=0, snap=None, sns=0, Hk=Hk, D=4,
+             ws=FAKE + 40 * MB, wsb=n * Hk * 8)
+    a.update(kw)
+    if "hs" not in kw:
+        a["hs"] = (a["D"] - 1) * C            # histories packed for the width asked for
+    return L.gdn_decode_step(a["state"], a["sts"], a["x"], a["xt"], a["xs"], a["cw"], a["hist"],
+                             a["hs"], a["csnap"], a["cst"], a["css"], a["alpha"], a["dt"],
+                             a["a"], a["beta"], a["w"], a["z"], a["zt"], a["zs"], a["out"],
+                             a["ot"], a["os"], a["g"], a["y"], a["yt"], a["ys"], a["snap"],
+                             a["sns"], n, T, H, a["Hk"], S, a["D"], 0.125, 1e-6, 1e-6, a["ws"],
+                             a["wsb"], None)
+
+
+def test_step_validation_and_workspace_query():
+    MB = 1 << 20
+    assert L.gdn_decode_step_workspace_bytes(64, 16) == 64 * 16 * 2 * 4
+    assert L.gdn_decode_step_workspace_bytes(0, 16) == 0
+    # everything valid but a conv width without a kernel: the last check
+    assert step(D=5) == ERR_UNSUP
+    assert step(D=5, csnap=FAKE + 7 * MB, cst=4 * 256, css=4 * 256) == ERR_UNSUP
+    assert step(D=9) == ERR_SHAPE and step(D=1) == ERR_SHAPE
+    assert step(T=9) == ERR_SHAPE                                       # at most 8 positions
+    assert step(Hk=3) == ERR_SHAPE                                      # H not a multiple of Hk
+    assert step(x=None) == ERR_NULL and step(cw=None) == ERR_NULL and step(hist=None) == ERR_NULL
+    assert step(ws=None) == ERR_WS and step(wsb=16) == ERR_WS
+    assert step(ws=FAKE + 40 * MB + 2) == ERR_WS                        # counters misaligned
+    assert step(x=FAKE + 4 * MB + 8) == ERR_SHAPE                       # x not 16-byte aligned
+    assert step(xt=258, xs=516) == ERR_SHAPE                            # x stride not a multiple of 4
+    assert step(xt=128, xs=256) == ERR_SHAPE                            # rows shorter than conv_dim
+    assert step(hs=100) == ERR_SHAPE                                    # histories overlap each other
+    assert step(hist=FAKE + 4 * MB + 64) == ERR_ALIAS                   # history over x
+    assert step(ws=FAKE) == ERR_ALIAS                                   # counters over the state
+    assert step(csnap=FAKE + 6 * MB + 256, cst=768, css=768) == ERR_ALIAS  # snapshot over history
+    assert step(out=FAKE + 4 * MB + 512) == ERR_ALIAS                   # out over x
+
+
 def test_stream_copy_validation():
     assert L.gdn_stream_copy(FAKE, FAKE + (1 << 20), 0, None) == OK            # nothing launched
     assert L.gdn_stream_copy(None, FAKE, 64, None) == ERR_NULL

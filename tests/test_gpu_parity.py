@@ -463,6 +463,117 @@ def test_decode_fused_bit_identical_to_three_calls(name, opt, shape):
     assert rel(stf, s_ref) < 1e-4
 
 
+# ------------------------------------------------------------------------------------- fused step
+
+def step_shape(S, H, Hk, n_tok, n_seq, D=4, x_pad=0):
+    """Workload overrides for a conv row laid out q | k | v (head width S)."""
+    C = (2 * Hk + H) * S
+    return dict(S=S, head_dim=S, H=H, Hk=Hk, n_tok=n_tok, n_seq=n_seq, d_conv=D, conv_dim=C,
+                qk_channels=2 * Hk * S, x_stride=C + x_pad, out_stride=C, state_std=0.1,
+                hist_std=1.0)
+
+
+def step_two_ways(inp, opt=True, ws=None):
+    """The decode step as one gdn_decode_step launch and as gdn_conv1d_silu_l2norm
+    into a buffer followed by gdn_decode_fused; returns both results."""
+    wl = inp["wl"]
+    n, T, H, Hk, S, C, D = wl.n_seq, wl.n_tok, wl.H, wl.Hk, wl.S, wl.conv_dim, wl.d_conv
+    nan = float("nan")
+    d = {k: on_dev(inp[k]) for k in ("alpha", "dt", "a", "beta", "norm_w", "z", "x", "conv_w")}
+    x = d["x"][:, :, :C]
+    alpha3, z4 = d["alpha"].view(n, T, H), d["z"].view(n, T, H, S)
+    snap = T > 1
+
+    def outs():
+        return dict(state=on_dev(inp["state"]).clone(), hist=on_dev(inp["conv_hist"]).clone(),
+                    out=torch.full((n, T, H, S), nan, device=DEV),
+                    g=torch.full((n, T, H), nan, device=DEV) if opt else None,
+                    y=torch.full((n, T, H, S), nan, device=DEV) if opt else None,
+                    snap=torch.full((n, T - 1, H, S, S), nan, device=DEV) if snap else None,
+                    csnap=torch.full((n, T - 1, C, D - 1), nan, device=DEV) if snap else None)
+
+    r = outs()
+    cout = torch.full((n, T, C), nan, device=DEV)
+    gdn().gdn_conv1d_silu_l2norm(x, d["conv_w"], r["hist"], cout, qk_channels=2 * Hk * S,
+                                 head_dim=S, l2_eps=wl.l2_eps, snap=r["csnap"])
+    q = cout[:, :, :Hk * S].unflatten(-1, (Hk, S))
+    k = cout[:, :, Hk * S:2 * Hk * S].unflatten(-1, (Hk, S))
+    v = cout[:, :, 2 * Hk * S:].unflatten(-1, (H, S))
+    gdn().gdn_decode_fused(r["state"], q, k, v, alpha3, d["dt"], d["a"], d["beta"], d["norm_w"],
+                           z4, r["out"], scale=wl.scale, norm_eps=wl.norm_eps, g=r["g"], y=r["y"],
+                           snap=r["snap"])
+    f = outs()
+    if ws is None:
+        ws = torch.zeros(gdn().gdn_decode_step_workspace_bytes(n, Hk) // 4, dtype=torch.int32,
+                         device=DEV)
+    gdn().gdn_decode_step(f["state"], x, d["conv_w"], f["hist"], alpha3, d["dt"], d["a"],
+                          d["beta"], d["norm_w"], z4, f["out"], scale=wl.scale, l2_eps=wl.l2_eps,
+                          norm_eps=wl.norm_eps, workspace=ws, g=f["g"], y=f["y"], snap=f["snap"],
+                          conv_snap=f["csnap"])
+    return r, f, ws
+
+
+STEP_CASES = [("decode64", None), ("verify2", None), ("decode", None),
+              ("tiny", dict(n_tok=4)),                                    # H == Hk: no tickets
+              ("tiny", step_shape(32, 6, 2, 3, 2, D=2)),
+              ("tiny", step_shape(64, 6, 3, 4, 2, D=3, x_pad=8)),
+              ("tiny", step_shape(256, 4, 2, 2, 3)),
+              ("tiny", step_shape(128, 4, 1, 8, 2)),                      # 8 positions, G = 4
+              ("tiny", step_shape(128, 4, 4, 2, 2))]
+
+
+@pytest.mark.parametrize("name,shape", STEP_CASES)
+def test_decode_step_bit_identical_to_conv_then_fused(name, shape):
+    inp = inputs(name) if shape is None else make_inputs(name, seed=43, **shape)
+    wl = inp["wl"]
+    log_case("decode_step", wl=name, n_seq=wl.n_seq, n_tok=wl.n_tok, H=wl.H, Hk=wl.Hk, S=wl.S,
+             D=wl.d_conv)
+    r, f, ws = step_two_ways(inp)
+    for key in r:
+        if r[key] is not None:
+            assert bits_equal(f[key], r[key]), key
+    assert int(ws.abs().sum()) == 0          # the tickets are reset for the next call
+
+
+def test_decode_step_twice_in_a_row():
+    # state and conv history carried from one call to the next; the second call
+    # reuses the first's workspace, which must have come back zero-filled
+    inp = make_inputs("verify2", seed=47)
+    wl = inp["wl"]
+    log_case("decode_step_twice", n_seq=wl.n_seq, n_tok=wl.n_tok)
+    r1, f1, ws = step_two_ways(inp, opt=False)
+    assert bits_equal(f1["state"], r1["state"]) and bits_equal(f1["hist"], r1["hist"])
+    inp2 = dict(inp)
+    inp2["state"], inp2["conv_hist"] = r1["state"].cpu(), r1["hist"].cpu()
+    inp2["x"] = make_inputs("verify2", seed=48)["x"]
+    r2, f2, _ = step_two_ways(inp2, opt=False, ws=ws)
+    for key in ("state", "hist", "out", "snap", "csnap"):
+        assert bits_equal(f2[key], r2[key]), key
+    assert int(ws.abs().sum()) == 0
+
+
+def test_decode_step_against_oracle_chain():
+    # conv -> gate -> recurrence -> norm in the fp64 oracle at the 64-sequence size
+    inp = inputs("decode64")
+    wl = inp["wl"]
+    log_case("decode_step_oracle", n_seq=wl.n_seq, H=wl.H)
+    n, T, H, Hk, S, C = wl.n_seq, wl.n_tok, wl.H, wl.Hk, wl.S, wl.conv_dim
+    _, f, _ = step_two_ways(inp)
+    o_r, hist_r, _ = oracle.conv1d_silu_l2norm(inp["x"][:, :, :C], inp["conv_w"],
+                                               inp["conv_hist"], wl.qk_channels, wl.head_dim,
+                                               wl.l2_eps)
+    q_r = o_r[:, :, :Hk * S].reshape(n, T, Hk, S)
+    k_r = o_r[:, :, Hk * S:2 * Hk * S].reshape(n, T, Hk, S)
+    v_r = o_r[:, :, 2 * Hk * S:].reshape(n, T, H, S)
+    g_r = oracle.decay_gate(inp["alpha"], inp["dt"], inp["a"]).reshape(n, T, H)
+    y_r, s_r, _ = oracle.recurrence_seq(inp["state"], q_r, k_r, v_r, g_r, inp["beta"], wl.scale)
+    n_r = oracle.gated_rmsnorm(y_r.reshape(n * T, H, S), inp["norm_w"], inp["z"], wl.norm_eps)
+    assert rel(f["hist"], hist_r) == 0.0     # the history only holds raw inputs
+    assert rel(f["out"].view(n * T, H, S), n_r) < 1e-4
+    assert rel(f["state"], s_r) < 1e-4
+    assert rel(f["g"], g_r) < 1e-5
+
+
 # ------------------------------------------------------------------------------------- chunked
 
 def run_chunked(inp, g3, state=None):
