@@ -3,12 +3,14 @@
 
 One timed step = one decode step of the whole layer core on the batched-decode
 workload (64 sequences x 48 value heads, 128x128 fp32 state per head,
-conv 10240 channels read from 20480-wide rows): decay gate -> conv1d + SiLU +
-L2 -> recurrence (q, k, v read straight out of the conv output rows) ->
-gated RMSNorm, all four launches on one stream.  Inputs are resident in HBM
-before the timed region.  The state lives in one of several pools, rotated
-step by step, so the 192 MiB state cannot stay in the 256 MB MALL between
-steps ("cold"); a same-pool ("MALL-hot") figure is reported beside it.
+conv 10240 channels read from 20480-wide rows): conv1d + SiLU + L2 -> decay
+gate -> recurrence -> gated RMSNorm in one launch (gdn_decode_step, whose
+results are bit-identical to the separate entry points).  The same step as
+four separate launches and as conv + gdn_decode_fused is timed beside it.
+Inputs are resident in HBM before the timed region.  The state and conv
+history live in one of several pools, rotated step by step, so the 192 MiB
+state cannot stay in the 256 MB MALL between steps ("cold"); a same-pool
+("MALL-hot") figure of the recurrence is reported beside it.
 
 value = decode state GB/s of the whole step: (state bytes read + written) /
 step time.  The prefill half of the metric (tokens/s of the 4096-token prompt
@@ -56,7 +58,11 @@ def decode_bytes(wl) -> dict:
     conv = n * (2 * C * (D - 1) + T * 2 * C) * 4 + C * D * 4
     norm = n * T * 3 * H * wl.head_dim * 4 + wl.head_dim * 4
     gate = n * T * H * 2 * 4 + 2 * H * 4
-    return {"state": 2 * state, "recurrence": recur, "conv": conv, "norm": norm, "gate": gate}
+    # the one-launch step: q, k, v, y and g stay on chip; z is read, out written
+    step = (2 * state + conv - n * T * C * 4 + n * T * 2 * H * S * 4 + wl.head_dim * 4
+            + n * T * H * 2 * 4 + 2 * H * 4)
+    return {"state": 2 * state, "recurrence": recur, "conv": conv, "norm": norm, "gate": gate,
+            "step": step}
 
 
 def recorded_traffic(profile: str):
@@ -182,6 +188,17 @@ def main():
                              cu["beta"], cu["norm_w"], z.view(n, 1, H, S), nout.view(n, 1, H, S),
                              scale=wl.scale, norm_eps=wl.norm_eps)
 
+    step_ws = torch.zeros(gdn.gdn_decode_step_workspace_bytes(n, Hk) // 4, dtype=torch.int32,
+                          device=dev)
+
+    def decode_step_one(i):
+        # the whole step (conv, gate, recurrence, norm) in one launch
+        p = i % len(pools)
+        gdn.gdn_decode_step(pools[p], x, cu["conv_w"], hists[p], cu["alpha"].view(n, 1, H),
+                            cu["dt"], cu["a"], cu["beta"], cu["norm_w"], z.view(n, 1, H, S),
+                            nout.view(n, 1, H, S), scale=wl.scale, l2_eps=wl.l2_eps,
+                            norm_eps=wl.norm_eps, workspace=step_ws)
+
     def time_steps(step):
         for i in range(args.warmup):
             step(i)
@@ -193,14 +210,15 @@ def main():
         return (time.perf_counter() - t0) * 1e3 / args.steps
 
     fused_ms_per_step = time_steps(decode_step_fused)
+    four_ms_per_step = time_steps(decode_step)
 
     for i in range(args.warmup):
-        decode_step(i)
+        decode_step_one(i)
     torch.cuda.synchronize()
     # timed region: K whole steps, nothing else on the stream
     t0 = time.perf_counter()
     for i in range(args.steps):
-        decode_step(i)
+        decode_step_one(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
@@ -245,6 +263,7 @@ def main():
         return float(np.median(per))
 
     bursts = {
+        "step_one_launch_rotated": burst(decode_step_one),
         "recurrence_rotated_pools": burst(lambda i: gdn.gdn_recurrence_decode(
             pools[i % len(pools)], qv, kv, vv, g.view(n, 1, H), cu["beta"], y, scale=wl.scale)),
         "conv_step_rotated_hist": burst(lambda i: gdn.gdn_conv1d_silu_l2norm(
@@ -266,10 +285,12 @@ def main():
     # pattern without its arithmetic
     copy_ms = burst(lambda i: gdn.gdn_stream_copy(dst, srcs[i % len(srcs)]))
     copy_gbs = by["state"] / (copy_ms * 1e-3) / 1e9
-    # roofline of the dominant kernel: its launches back to back on rotated
-    # (cold) state pools, HIP events around 50 launches on the launch stream
-    burst_ms = bursts["recurrence_rotated_pools"]
-    achieved = by["recurrence"] / (burst_ms * 1e-3) / 1e9
+    # roofline of the timed step's one kernel: its launches back to back on
+    # rotated (cold) state pools and histories, HIP events around 50 launches
+    # on the launch stream
+    burst_ms = bursts["step_one_launch_rotated"]
+    achieved = by["step"] / (burst_ms * 1e-3) / 1e9
+    rec_burst_gbs = by["recurrence"] / (bursts["recurrence_rotated_pools"] * 1e-3) / 1e9
     del srcs, dst
     torch.cuda.empty_cache()
 
@@ -415,21 +436,22 @@ def main():
         "config": {
             "workload": "decode64: 64 seq x 1 token, 48 value / 16 q-k heads, 128x128 fp32 "
                         "state per head (192 MiB), conv 10240 ch from 20480-wide rows; "
-                        "gate+conv+recurrence+norm per step, state pools rotated (cold)",
+                        "conv+gate+recurrence+norm per step in one launch (gdn_decode_step), "
+                        "state pools and conv histories rotated (cold)",
             "state_pools": args.pools,
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_recur_decode",
+            "kernel": "k_decode_step",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": recorded_traffic("k_recur_decode_decode64.md"),
-            "bytes_per_launch": by["recurrence"],
+            "traffic": recorded_traffic("k_decode_step_decode64.md"),
+            "bytes_per_launch": by["step"],
             "avg_launch_ms": burst_ms,
-            "timing": "HIP events around 50 back-to-back launches on rotated state pools, "
-                      "median of 10 bursts",
+            "timing": "HIP events around 50 back-to-back launches on rotated state pools and "
+                      "conv histories, median of 10 bursts",
         },
         "decode": {
             "recurrence_state_GBs_cold": by["state"] / (rec_ms * 1e-3) / 1e9,
@@ -439,19 +461,28 @@ def main():
             "recurrence_ms_mall_hot": hot_ms,
             "recurrence_state_GBs_mall_hot": by["state"] / (hot_ms * 1e-3) / 1e9,
             "step_frac_of_hbm": value / HBM_PEAK_GBS,
+            "four_launch_ms_per_step": four_ms_per_step,
+            "four_launch_state_GBs": by["state"] / (four_ms_per_step * 1e-3) / 1e9,
+            "four_launch_note": "gate, conv, recurrence, norm as four launches",
             "fused_ms_per_step": fused_ms_per_step,
             "fused_state_GBs": by["state"] / (fused_ms_per_step * 1e-3) / 1e9,
-            "fused_note": "conv + gdn_decode_fused per step; at this batch the four separate "
-                          "launches (the timed step) are faster",
+            "fused_note": "conv + gdn_decode_fused (two launches) per step",
+            "step_bytes_per_launch": by["step"],
+            "conv_bytes_in_step": by["conv"] - n * C * 4,
+            "conv_note": "inside the one-launch step the conv's bytes stream at the step "
+                         "kernel's rate (roofline.achieved); on its own the conv launch is "
+                         "bound by its ramp and drain (burst_ms_per_launch.conv_step_rotated_hist)",
+            "conv_alone_GBs": by["conv"] / (bursts["conv_step_rotated_hist"] * 1e-3) / 1e9,
             "small_batch_gate_recurrence_norm": small,
             "burst_ms_per_launch": bursts,
-            "recurrence_burst_GBs": by["recurrence"] / (bursts["recurrence_rotated_pools"] * 1e-3) / 1e9,
+            "recurrence_burst_GBs": rec_burst_gbs,
             "copy_peak": {"what": "gdn_stream_copy (16-byte non-temporal loads and stores), "
                                   "192 MiB per launch, sources rotated, 50-launch bursts",
                           "ms": copy_ms, "GBs": copy_gbs, "frac_of_hbm": copy_gbs / HBM_PEAK_GBS,
                           "torch_copy_ms": torch_copy_ms,
                           "torch_copy_GBs": by["state"] / (torch_copy_ms * 1e-3) / 1e9},
-            "recurrence_frac_of_copy_peak": achieved / copy_gbs,
+            "recurrence_frac_of_copy_peak": rec_burst_gbs / copy_gbs,
+            "step_frac_of_copy_peak": achieved / copy_gbs,
         },
         "prefill": prefill,
         "cpu_baseline": cpu,
