@@ -337,6 +337,17 @@ def main():
                               eps=sw.norm_eps)
 
     step_eager = burst(small_step)
+    s_ws = torch.zeros(gdn.gdn_decode_step_workspace_bytes(sn, sw.Hk) // 4, dtype=torch.int32,
+                       device=dev)
+
+    def small_step_one(i=0):
+        gdn.gdn_decode_step(s_st, sc["x"][..., :sw.conv_dim], sc["conv_w"], s_hist,
+                            sc["alpha"].view(sn, sT, sH), sc["dt"], sc["a"], sc["beta"],
+                            sc["norm_w"], sc["z"].view(sn, sT, sH, sS),
+                            s_o.view(sn, sT, sH, sS), scale=sw.scale, l2_eps=sw.l2_eps,
+                            norm_eps=sw.norm_eps, workspace=s_ws)
+
+    step_one = burst(small_step_one)
     graph = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(stream)
@@ -349,7 +360,8 @@ def main():
     step_graph = burst(lambda i: graph.replay())
     small = {"workload": "decode: 1 seq x 1 token, 32 value / 16 q-k heads, 128x128 state",
              "three_calls_ms": burst(small_three), "fused_ms": burst(small_fused),
-             "step_eager_ms": step_eager, "step_graph_replay_ms": step_graph}
+             "step_eager_ms": step_eager, "step_graph_replay_ms": step_graph,
+             "step_one_launch_ms": step_one}
     del graph, s_st, s_g, s_y, s_o, sc, s_hist, s_conv
 
     # ---------------------------------------------------------------- prefill pass

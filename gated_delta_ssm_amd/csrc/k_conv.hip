@@ -113,15 +113,17 @@ __global__ __launch_bounds__(256) void k_conv_tp(
   }
   const bool qk = LPH4 > 0 && L.c0 < qk_channels;
 
-  // positions in batches of TB: the batch's rows are loaded first (rows past
-  // the end are clamped to the last position and not used), so TB loads are
-  // in flight per wave instead of one
-  constexpr int TB = 8;
-  static_assert(TT % TB == 0, "tile of whole batches");
-  for (int tb = t0; tb < t1; tb += TB) {
-    float xv[TB][CPL];
+  // positions in batches of TB, two batches in flight: the next batch's rows
+  // are requested before the current batch is computed (rows past the end are
+  // clamped to the last position and not used)
+  constexpr int TB = 4;
+  static_assert(TT % (2 * TB) == 0 && TT >= DH, "whole pairs of batches; a tile covers the history");
+  auto load_batch = [&](float (&xv)[TB][CPL], int tb) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < TB; ++i) load_row4<VEC>(x + (int64_t)min(tb + i, n_tok - 1) * x_tok, L, xv[i]);
+    for (int i = 0; i < TB; ++i)
+      load_row4<VEC>(x + (int64_t)min(tb + i, n_tok - 1) * x_tok, L, xv[i]);
+  };
+  auto run_batch = [&](float (&xv)[TB][CPL], int tb) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < TB; ++i) {
       if (tb + i < t1) {   // uniform per wave
@@ -130,6 +132,14 @@ __global__ __launch_bounds__(256) void k_conv_tp(
         store_row4<VEC>(out + (int64_t)(tb + i) * o_tok, L, o);
       }
     }
+  };
+  float xa[TB][CPL], xb[TB][CPL];
+  load_batch(xa, t0);
+  for (int tb = t0; tb < t1; tb += 2 * TB) {
+    load_batch(xb, tb + TB);
+    run_batch(xa, tb);
+    load_batch(xa, tb + 2 * TB);
+    run_batch(xb, tb + TB);
   }
   if (t0 == 0) {  // the new history: positions n_tok-DH .. n_tok-1
     float h[CPL][DH];
@@ -154,7 +164,14 @@ __global__ __launch_bounds__(256) void k_conv_tp(
 
 namespace {
 
-constexpr int kTileTok = 32;   // positions per wave in the token-parallel kernel
+// positions per wave in the token-parallel kernel: at 4096 positions x 8192
+// channels, 8-position tiles (8192 waves) took 58 us against 67 us for 32
+// (2048 waves, batches of 8 without the prefetch) and 62 us for 16; the extra
+// window rows each tile reloads (d_conv - 1) cost less than the waves gain
+constexpr int kTileTok = 8;
+// tiles for prompts whose 8-position tiles would exceed the grid's y limit
+constexpr int kTileTokLong = 64;
+constexpr int kMaxGridY = 65535;
 constexpr int kWavesPerBlock = 4;
 
 template <int D, int LPH4, bool VEC>
@@ -163,10 +180,17 @@ int run_conv(const ConvArgs &a, hipStream_t stream) {
   const int grid_x = (blocks_ch + kWavesPerBlock - 1) / kWavesPerBlock;
   const dim3 block(64 * kWavesPerBlock);
   if (a.snap == nullptr && a.n_tok > 8) {
-    const dim3 grid(grid_x, (a.n_tok + kTileTok - 1) / kTileTok, a.n_seq);
-    return launch_kernel(k_conv_tp<D, LPH4, VEC, kTileTok>, grid, block, 0, stream, a.x, a.x_tok,
-                         a.x_seq, a.w, a.hist, a.h_seq, a.out, a.o_tok, a.o_seq, a.n_tok, a.C,
-                         a.qk_channels, a.eps);
+    const int64_t tiles = ((int64_t)a.n_tok + kTileTok - 1) / kTileTok;
+    if (tiles <= kMaxGridY)
+      return launch_kernel(k_conv_tp<D, LPH4, VEC, kTileTok>, dim3(grid_x, (unsigned)tiles, a.n_seq),
+                           block, 0, stream, a.x, a.x_tok, a.x_seq, a.w, a.hist, a.h_seq, a.out,
+                           a.o_tok, a.o_seq, a.n_tok, a.C, a.qk_channels, a.eps);
+    const int64_t tiles_long = ((int64_t)a.n_tok + kTileTokLong - 1) / kTileTokLong;
+    if (tiles_long > kMaxGridY) return GDN_ERR_UNSUPPORTED;
+    return launch_kernel(k_conv_tp<D, LPH4, VEC, kTileTokLong>,
+                         dim3(grid_x, (unsigned)tiles_long, a.n_seq), block, 0, stream, a.x,
+                         a.x_tok, a.x_seq, a.w, a.hist, a.h_seq, a.out, a.o_tok, a.o_seq, a.n_tok,
+                         a.C, a.qk_channels, a.eps);
   }
   // the step kernel is latency-bound (a few loads per wave, then one chain of
   // arithmetic): one-wave blocks spread its waves evenly over the CUs

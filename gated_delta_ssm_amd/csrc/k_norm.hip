@@ -65,7 +65,10 @@ __global__ __launch_bounds__(256) void k_gated_rmsnorm(const float *y, int64_t y
 
 // LPH4 = head_dim / 4 lanes per head.  Lanes past the end load a clamped
 // (valid) float4 and store nothing; heads never straddle that boundary, so no
-// valid head sums an invalid lane.
+// valid head sums an invalid lane.  y, z and out stream through once, so
+// their accesses are non-temporal (at 4096 rows x 32 heads x 128: 36.6 us
+// against 39.7 us with ordinary accesses); the shared weight stays cached.
+typedef float norm_f4 __attribute__((ext_vector_type(4)));
 template <int LPH4>
 __global__ __launch_bounds__(256) void k_gated_rmsnorm_v4(const float *y, int64_t y_row,
                                                           const float *__restrict__ w,
@@ -79,12 +82,17 @@ __global__ __launch_bounds__(256) void k_gated_rmsnorm_v4(const float *y, int64_
   const unsigned r = ic / row4;
   const int e = (int)(ic - r * row4) * 4;
   const int col = e % HD;
-  const float4 yv = *reinterpret_cast<const float4 *>(y + r * y_row + e);
-  const float4 zv = *reinterpret_cast<const float4 *>(z + r * z_row + e);
+  const norm_f4 yn = __builtin_nontemporal_load(reinterpret_cast<const norm_f4 *>(y + r * y_row + e));
+  const norm_f4 zn = __builtin_nontemporal_load(reinterpret_cast<const norm_f4 *>(z + r * z_row + e));
+  const float4 yv = make_float4(yn.x, yn.y, yn.z, yn.w);
+  const float4 zv = make_float4(zn.x, zn.y, zn.z, zn.w);
   const float4 wv = *reinterpret_cast<const float4 *>(w + col);
   const float ss = group_sum<LPH4>(sumsq4(yv));
   const float4 o = gated_norm4(yv, zv, wv, norm_inv(ss, HD, eps));
-  if (i4 < total4) *reinterpret_cast<float4 *>(out + r * o_row + e) = o;
+  if (i4 < total4) {
+    const norm_f4 on = {o.x, o.y, o.z, o.w};
+    __builtin_nontemporal_store(on, reinterpret_cast<norm_f4 *>(out + r * o_row + e));
+  }
 }
 
 namespace {
