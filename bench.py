@@ -421,6 +421,11 @@ def main():
             "ms": {"gate": seg[0], "conv": seg[1], "chunked_recurrence": seg[2], "norm": seg[3]},
             "chunked_algorithmic_tflops": fl / (seg[2] * 1e-3) / 1e12,
             "chunked_frac_of_bf16_peak": fl / (seg[2] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "chunked_frac_of_fp32_matrix_peak": fl / (seg[2] * 1e-3) / 1e12 / FP32_MATRIX_PEAK_TFLOPS,
+            "chunked_peak_note": "algorithmic flops (one product each); the kernels take every "
+                                 "product as three bf16 MFMAs (hi*hi + hi*lo + lo*hi), which keeps "
+                                 "fp32-level precision, so bf16 peak bounds the executed MFMAs and "
+                                 "the fp32 matrix peak is what single fp32 MFMAs would reach",
             "chunked_attainable": chunked_attainable(T, PH, PHk, PS, ws.numel(),
                                                      fl / (seg[2] * 1e-3) / 1e12),
         }

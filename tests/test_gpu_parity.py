@@ -161,6 +161,24 @@ def test_conv_unaligned_rows_bit_identical_to_aligned(T):
     assert torch.isnan(o_full[..., 0]).all()
 
 
+def test_conv_long_prompt_tiles():
+    # more positions than 8-position tiles can put in the grid's y dimension
+    # (65535 tiles): the launcher switches to 64-position tiles, same arithmetic
+    T, C, D = 8 * 65535 + 40, 8, 4
+    gen = torch.Generator("cpu").manual_seed(29)
+    x = torch.randn(1, T, C, generator=gen)
+    w = torch.randn(C, D, generator=gen) * 0.25
+    hist = torch.randn(1, C, D - 1, generator=gen)
+    log_case("conv_long_prompt", T=T, C=C)
+    out = torch.full((1, T, C), float("nan"), device=DEV)
+    st = on_dev(hist).clone()
+    gdn().gdn_conv1d_silu_l2norm(on_dev(x), on_dev(w), st, out, qk_channels=0, head_dim=32,
+                                 l2_eps=1e-6)
+    o_ref, h_ref, _ = oracle.conv1d_silu_l2norm(x, w, hist, 0, 32, 1e-6)
+    assert rel(out, o_ref) < 1e-5
+    assert np.array_equal(st.cpu().double().numpy(), h_ref)
+
+
 @pytest.mark.parametrize("C,qk,hd", [(222, 0, 32), (263, 128, 64)])
 def test_conv_channels_not_multiple_of_4(C, qk, hd):
     # a last lane with fewer than 4 channels (scalar path), against the oracle
