@@ -570,6 +570,44 @@ def test_decode_step_twice_in_a_row():
     assert int(ws.abs().sum()) == 0
 
 
+def test_decode_step_verify_equals_two_single_steps():
+    # K = 2 in one launch (snapshots inline) against two one-position launches:
+    # outputs, final state and history bit for bit, and the position-0
+    # snapshots equal to the state and history after the first one-position step
+    inp = make_inputs("verify2", seed=53)
+    wl = inp["wl"]
+    n, T, H, Hk, S, C, D = wl.n_seq, wl.n_tok, wl.H, wl.Hk, wl.S, wl.conv_dim, wl.d_conv
+    assert T == 2
+    log_case("decode_step_verify_vs_steps", n_seq=n, H=H)
+    d = {k: on_dev(inp[k]) for k in ("alpha", "dt", "a", "beta", "norm_w", "z", "x", "conv_w")}
+    x = d["x"][:, :, :C]
+    alpha3, z4 = d["alpha"].view(n, T, H), d["z"].view(n, T, H, S)
+    nan = float("nan")
+    ws = torch.zeros(gdn().gdn_decode_step_workspace_bytes(n, Hk) // 4, dtype=torch.int32,
+                     device=DEV)
+    kw = dict(scale=wl.scale, l2_eps=wl.l2_eps, norm_eps=wl.norm_eps, workspace=ws)
+
+    st_k, hist_k = on_dev(inp["state"]).clone(), on_dev(inp["conv_hist"]).clone()
+    out_k = torch.full((n, T, H, S), nan, device=DEV)
+    snap = torch.full((n, 1, H, S, S), nan, device=DEV)
+    csnap = torch.full((n, 1, C, D - 1), nan, device=DEV)
+    gdn().gdn_decode_step(st_k, x, d["conv_w"], hist_k, alpha3, d["dt"], d["a"], d["beta"],
+                          d["norm_w"], z4, out_k, snap=snap, conv_snap=csnap, **kw)
+
+    st_1, hist_1 = on_dev(inp["state"]).clone(), on_dev(inp["conv_hist"]).clone()
+    out_1 = torch.full((n, T, H, S), nan, device=DEV)
+    for t in range(T):
+        gdn().gdn_decode_step(st_1, x[:, t:t + 1], d["conv_w"], hist_1,
+                              alpha3[:, t:t + 1].contiguous(), d["dt"], d["a"],
+                              d["beta"][:, t:t + 1].contiguous(), d["norm_w"], z4[:, t:t + 1],
+                              out_1[:, t:t + 1], **kw)
+        if t == 0:
+            assert bits_equal(snap[:, 0], st_1) and bits_equal(csnap[:, 0], hist_1)
+    assert bits_equal(out_k, out_1)
+    assert bits_equal(st_k, st_1) and bits_equal(hist_k, hist_1)
+    assert int(ws.abs().sum()) == 0
+
+
 def test_decode_step_against_oracle_chain():
     # conv -> gate -> recurrence -> norm in the fp64 oracle at the 64-sequence size
     inp = inputs("decode64")
