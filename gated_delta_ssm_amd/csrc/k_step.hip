@@ -46,7 +46,10 @@
 
 namespace gdn {
 
-constexpr int STEP_MAX_TOK = 8;
+// positions per launch, staged in LDS: up to 32 (16 at S = 256), which keeps
+// two workgroups' LDS per CU at S = 128 (about 70 KB each)
+template <int S>
+constexpr int step_max_tok() { return S <= 128 ? 32 : 16; }
 
 template <int S, int RG, int D>
 __global__ __launch_bounds__(16 * S / RG) void k_decode_step(const StepArgs A) {
@@ -54,11 +57,12 @@ __global__ __launch_bounds__(16 * S / RG) void k_decode_step(const StepArgs A) {
   constexpr int L4 = S / 4;                       // lanes of one S-channel head
   constexpr int DH = D - 1;
   constexpr int CONV_WAVES = (3 * L4 + 63) / 64;  // waves holding q, k, v heads
-  __shared__ __attribute__((aligned(16))) float cbuf[STEP_MAX_TOK][3][S];  // q, k, v
+  constexpr int MAXT = step_max_tok<S>();
+  __shared__ __attribute__((aligned(16))) float cbuf[MAXT][3][S];  // q, k, v
   __shared__ __attribute__((aligned(16))) float ybuf[2][S];
   __shared__ float hstash[2 * L4][CPL * DH];      // q/k windows after the last position
-  __shared__ __attribute__((aligned(16))) float zbuf[STEP_MAX_TOK][S];   // norm gate z
-  __shared__ float gbuf[STEP_MAX_TOK], bbuf[STEP_MAX_TOK];             // gate value, beta
+  __shared__ __attribute__((aligned(16))) float zbuf[MAXT][S];   // norm gate z
+  __shared__ float gbuf[MAXT], bbuf[MAXT];                       // gate value, beta
   constexpr int NWAVES = S / (4 * RG);
   static_assert(NWAVES > CONV_WAVES, "the last wave stages the per-position inputs");
   const FusedArgs &F = A.f;
@@ -241,6 +245,7 @@ namespace {
 
 template <int S, int RG, int D>
 int run_step(const StepArgs &a, hipStream_t stream) {
+  if (a.f.r.n_tok > step_max_tok<S>()) return GDN_ERR_SHAPE;
   static_assert(S % (4 * RG) == 0 && S / (4 * RG) <= 16, "a workgroup holds the whole head");
   static_assert((3 * S / 4 + 63) / 64 <= S / (4 * RG), "the conv fits in the workgroup");
   const int64_t units = (int64_t)a.f.r.n_seq * a.f.r.H;
@@ -262,7 +267,6 @@ int pick_d(const StepArgs &a, hipStream_t stream) {
 }  // namespace
 
 int launch_decode_step(const StepArgs &a, hipStream_t stream) {
-  if (a.f.r.n_tok > STEP_MAX_TOK) return GDN_ERR_SHAPE;
   // rows per lane as k_decode_fused
   switch (a.f.r.S) {
     case 32: return pick_d<32, 1>(a, stream);

@@ -233,7 +233,7 @@ int check_step(const float *state, int64_t st_seq, const float *x, int64_t x_tok
                int n_seq, int n_tok, int H, int Hk, int S, int D, const void *ws,
                size_t ws_bytes) {
   if (n_seq < 1 || n_tok < 1 || H < 1 || Hk < 1 || H % Hk != 0) return GDN_ERR_SHAPE;
-  if (n_tok > 8) return GDN_ERR_SHAPE;
+  if (n_tok > (S <= 128 ? 32 : 16)) return GDN_ERR_SHAPE;   // positions staged in LDS
   if (D < 2 || D > 8) return GDN_ERR_SHAPE;
   if (x_tok < 0 || x_seq < 0 || h_seq < 0 || cs_tok < 0 || cs_seq < 0) return GDN_ERR_SHAPE;
   if (!x || !cw || !hist) return GDN_ERR_NULL;

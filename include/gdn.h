@@ -269,10 +269,10 @@ size_t gdn_decode_step_workspace_bytes(int n_seq, int n_qk_heads);
  * history; each takes a ticket from a workspace counter once it has read it,
  * and the last one writes the new history, so no workgroup waits for another.
  * Results are bit-identical to gdn_conv1d_silu_l2norm into a buffer followed
- * by gdn_decode_fused on its q, k, v channels.  1 <= n_tok <= 8; S in {32,
- * 64, 128, 256}; d_conv in {2, 3, 4} (2..8 are valid widths; the others
- * return GDN_ERR_UNSUPPORTED).  No output may overlap an input, another
- * output or the workspace.
+ * by gdn_decode_fused on its q, k, v channels.  1 <= n_tok <= 32 (<= 16 at
+ * S = 256); S in {32, 64, 128, 256}; d_conv in {2, 3, 4} (2..8 are valid
+ * widths; the others return GDN_ERR_UNSUPPORTED).  No output may overlap an
+ * input, another output or the workspace.
  */
 int gdn_decode_step(float *state, int64_t state_seq_stride, const float *x, int64_t x_tok_stride,
                     int64_t x_seq_stride, const float *conv_w, float *conv_state,

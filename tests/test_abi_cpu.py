@@ -192,7 +192,7 @@ def test_step_validation_and_workspace_query():
     assert step(D=5) == ERR_UNSUP
     assert step(D=5, csnap=FAKE + 7 * MB, cst=4 * 256, css=4 * 256) == ERR_UNSUP
     assert step(D=9) == ERR_SHAPE and step(D=1) == ERR_SHAPE
-    assert step(T=9) == ERR_SHAPE                                       # at most 8 positions
+    assert step(T=33) == ERR_SHAPE                                      # at most 32 positions
     assert step(Hk=3) == ERR_SHAPE                                      # H not a multiple of Hk
     assert step(x=None) == ERR_NULL and step(cw=None) == ERR_NULL and step(hist=None) == ERR_NULL
     assert step(ws=None) == ERR_WS and step(wsb=16) == ERR_WS

@@ -537,6 +537,9 @@ STEP_CASES = [("decode64", None), ("verify2", None), ("decode", None),
               ("tiny", step_shape(64, 6, 3, 4, 2, D=3, x_pad=8)),
               ("tiny", step_shape(256, 4, 2, 2, 3)),
               ("tiny", step_shape(128, 4, 1, 8, 2)),                      # 8 positions, G = 4
+              ("tiny", step_shape(128, 4, 2, 17, 2)),                     # K = 17 verify
+              ("tiny", step_shape(256, 2, 1, 16, 2)),                     # most positions at S = 256
+              ("tiny", step_shape(32, 6, 2, 32, 2, D=3)),                 # most positions
               ("tiny", step_shape(128, 4, 4, 2, 2))]
 
 
