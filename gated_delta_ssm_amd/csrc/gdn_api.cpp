@@ -70,7 +70,7 @@ size_t gdn_recurrence_chunked_workspace_bytes(int n_seq, int n_tok, int n_v_head
                                               int n_qk_heads, int S, int chunk) {
   if (n_seq < 1 || n_tok < 1 || n_v_heads < 1 || n_qk_heads < 1 || n_v_heads % n_qk_heads)
     return 0;
-  if (S != 128 || chunk != 64) return 0;
+  if ((S != 32 && S != 64 && S != 128) || chunk != 64) return 0;
   return gdn::chunked_workspace_bytes(n_seq, n_tok, n_v_heads, n_qk_heads, S, chunk);
 }
 

@@ -1,5 +1,6 @@
 // k_chunk.hip -- chunked (WY / UT-transform) prefill form of the gated
-// delta-rule recurrence, for S = 128 and chunks of 64 positions.
+// delta-rule recurrence, for S = 128 and chunks of 64 positions (S = 32 and 64:
+// k_chunk_small.hip).
 //
 // The pages state the chunked idea (ssm_mamba.rs, spark_model, "Mamba-2 SSD
 // chunked prefill scan" comment: ceil(T/64) sequential links instead of T) and
@@ -942,7 +943,8 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_chunk_scan_pair(
 // chunks per sequence in the workspace: ceil(n_tok / 64) rounded up to even
 static int padded_chunks(int n_tok) { return ((n_tok + CH - 1) / CH + 1) & ~1; }
 
-size_t chunked_workspace_bytes(int n_seq, int n_tok, int H, int, int, int) {
+size_t chunked_workspace_bytes(int n_seq, int n_tok, int H, int, int S, int) {
+  if (S != DK) return 0;   // the S = 32 / 64 form keeps everything on chip
   return (size_t)n_seq * H * padded_chunks(n_tok) * WS_CHUNK;
 }
 
@@ -963,7 +965,8 @@ static int device_cu_count() {
 
 int launch_recur_chunked(const RecurArgs &a, int chunk, void *ws, size_t ws_bytes,
                          hipStream_t stream) {
-  if (chunk != CH || a.S != DK) return GDN_ERR_UNSUPPORTED;
+  if (chunk != CH) return GDN_ERR_UNSUPPORTED;
+  if (a.S != DK) return launch_chunk_small(a, stream);
   const int n_chunks = padded_chunks(a.n_tok);
   if (ws_bytes < chunked_workspace_bytes(a.n_seq, a.n_tok, a.H, a.Hk, a.S, chunk))
     return GDN_ERR_WORKSPACE;

@@ -68,6 +68,8 @@ int launch_recur_decode(const RecurArgs &a, hipStream_t stream);
 size_t chunked_workspace_bytes(int n_seq, int n_tok, int H, int Hk, int S, int chunk);
 int launch_recur_chunked(const RecurArgs &a, int chunk, void *ws, size_t ws_bytes,
                          hipStream_t stream);
+// The chunked form for S = 32 and 64 (fp32, one pass, no workspace).
+int launch_chunk_small(const RecurArgs &a, hipStream_t stream);
 
 struct NormArgs {
   const float *y;

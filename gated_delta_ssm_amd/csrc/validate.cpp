@@ -137,7 +137,8 @@ int check_chunked(const float *state, int64_t st_seq, const float *q, const floa
   const int rc = check_recur(state, st_seq, q, k, qk_tok, qk_seq, v, v_tok, v_seq, g, beta, y,
                              y_tok, y_seq, nullptr, 0, n_seq, n_tok, H, Hk, S);
   if (rc != GDN_OK) return rc;
-  if (chunk != 64 || S != 128) return GDN_ERR_UNSUPPORTED;
+  if (chunk != 64 || (S != 32 && S != 64 && S != 128)) return GDN_ERR_UNSUPPORTED;
+  if (S != 128) return GDN_OK;   // the one-pass fp32 form: no workspace, no vector rows
   if (v_tok % 4 || v_seq % 4 || y_tok % 4 || y_seq % 4 || !aligned(v, 16) || !aligned(y, 16))
     return GDN_ERR_SHAPE;
   if (!ws || ws_bytes < ws_needed || !aligned(ws, 256)) return GDN_ERR_WORKSPACE;

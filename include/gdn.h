@@ -165,10 +165,13 @@ size_t gdn_recurrence_chunked_workspace_bytes(int n_seq, int n_tok, int n_v_head
  * state is carried in fp32.  Agreement with the sequential scan is a
  * tolerance, not bit identity.
  *
- * chunk must be 64.  workspace: device memory of at least
- * gdn_recurrence_chunked_workspace_bytes(...) bytes, 256-byte aligned, owned by
- * the caller and not used by anything else until the call's work on `stream`
- * has finished.  S must be 128.
+ * chunk must be 64; S in {32, 64, 128} (256 returns GDN_ERR_UNSUPPORTED).
+ * S = 128 runs the two-phase MFMA form above and needs a workspace: device
+ * memory of at least gdn_recurrence_chunked_workspace_bytes(...) bytes,
+ * 256-byte aligned, owned by the caller and not used by anything else until
+ * the call's work on `stream` has finished.  S = 32 and 64 run the same
+ * algebra in fp32, one workgroup per (sequence, head) with every chunk tile on
+ * chip; the workspace size is 0 and workspace may be NULL.
  */
 int gdn_recurrence_chunked(float *state, int64_t state_seq_stride, const float *q, const float *k,
                            int64_t qk_tok_stride, int64_t qk_seq_stride, const float *v,

@@ -120,6 +120,12 @@ def test_chunked_validation_and_workspace_query():
     assert call(base, FAKE + 12 * MB, ws_need) == ERR_ALIAS            # workspace over v
     bad = list(base); bad[-1] = 32
     assert call(bad, FAKE + 64 * MB, ws_need) == ERR_UNSUP
+    # S = 32 and 64 run the on-chip fp32 form: no workspace; S = 256 has no chunked kernel
+    assert L.gdn_recurrence_chunked_workspace_bytes(1, 4096, 32, 16, 32, 64) == 0
+    assert L.gdn_recurrence_chunked_workspace_bytes(1, 4096, 32, 16, 64, 64) == 0
+    big = list(base); big[1] = H * 256 * 256; big[4] = Hk * 256; big[5] = T * Hk * 256
+    big[7] = H * 256; big[8] = T * H * 256; big[12] = H * 256; big[13] = T * H * 256; big[18] = 256
+    assert call(big, FAKE + 64 * MB, ws_need) == ERR_UNSUP
 
 
 def test_norm_validation():

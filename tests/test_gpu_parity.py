@@ -719,6 +719,31 @@ def test_chunked_paired_scan_bit_identical():
     assert bits_equal(st_full, st_half)
 
 
+@pytest.mark.parametrize("S,T,H,Hk,n_seq,g_scale", [(32, 64, 4, 4, 1, 1.0),      # the 64-token workload
+                                                   (32, 100, 4, 2, 2, 1.0),
+                                                   (64, 200, 3, 1, 2, 0.05),
+                                                   (64, 37, 2, 2, 1, 1.0)])
+def test_chunked_small_state(S, T, H, Hk, n_seq, g_scale):
+    # S = 32 and 64: the one-pass fp32 chunked form, no workspace, against the
+    # sequential scan; ragged last chunks, GQA, nonzero and weakly decaying state
+    inp = make_inputs("tiny", seed=79, S=S, head_dim=S, n_tok=T, H=H, Hk=Hk, n_seq=n_seq,
+                      state_std=0.1)
+    wl = inp["wl"]
+    log_case("chunked_small", S=S, T=T, H=H, Hk=Hk, n_seq=n_seq)
+    assert gdn().gdn_recurrence_chunked_workspace_bytes(n_seq, T, H, Hk, S, 64) == 0
+    g3 = (oracle_g(inp) * g_scale).float()
+    st = on_dev(inp["state"]).clone()
+    v = on_dev(inp["v"])
+    y = torch.full_like(v, float("nan"))
+    gdn().gdn_recurrence_chunked(st, on_dev(inp["q"]), on_dev(inp["k"]), v, on_dev(g3),
+                                 on_dev(inp["beta"]), y, scale=wl.scale, chunk=64)
+    y_ref, s_ref, _ = oracle.recurrence_seq(inp["state"], inp["q"], inp["k"], inp["v"], g3,
+                                            inp["beta"], wl.scale)
+    ey, es = rel(y, y_ref), rel(st, s_ref)
+    print(f"[chunked S={S}] rel err y {ey:.3e} state {es:.3e}", flush=True)
+    assert ey < 2e-3 and es < 2e-3
+
+
 def test_chunked_deterministic():
     inp = make_inputs("prefill", seed=71, n_tok=512)
     log_case("chunked_determinism")
