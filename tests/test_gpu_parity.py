@@ -829,6 +829,58 @@ def test_decode_step_graph_replay_matches_eager():
             assert bits_equal(a, b)
 
 
+def test_one_launch_step_graph_replay_matches_eager():
+    # gdn_decode_step captured once into a HIP graph and replayed with eager
+    # work between replays: every replay equals the eager call bit for bit and
+    # leaves the ticket workspace at zero (two value heads share each q/k head)
+    inp = inputs("decode")
+    wl = inp["wl"]
+    log_case("graph_replay_one_launch", wl="decode")
+    n, T, H, Hk, S, C = wl.n_seq, wl.n_tok, wl.H, wl.Hk, wl.S, wl.conv_dim
+    assert H > Hk
+    cu = {k: on_dev(v) for k, v in inp.items() if isinstance(v, torch.Tensor)}
+    st, hist = cu["state"].clone(), cu["conv_hist"].clone()
+    out = torch.empty(n, T, H, S, device=DEV)
+    ws = torch.zeros(gdn().gdn_decode_step_workspace_bytes(n, Hk) // 4, dtype=torch.int32,
+                     device=DEV)
+
+    def step():
+        gdn().gdn_decode_step(st, cu["x"][..., :C], cu["conv_w"], hist,
+                              cu["alpha"].view(n, T, H), cu["dt"], cu["a"], cu["beta"],
+                              cu["norm_w"], cu["z"].view(n, T, H, S), out, scale=wl.scale,
+                              l2_eps=wl.l2_eps, norm_eps=wl.norm_eps, workspace=ws)
+
+    def reset():
+        st.copy_(cu["state"])
+        hist.copy_(cu["conv_hist"])
+
+    reset()
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (out, st, hist)]
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        reset()
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    reset()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(3):
+        reset()
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((out, st, hist), ref):
+            assert bits_equal(a, b)
+        assert int(ws.abs().sum()) == 0
+
+
 # ------------------------------------------------------------------------------------- degenerate cases
 
 @pytest.mark.parametrize("path", ["decode", "chunked"])
