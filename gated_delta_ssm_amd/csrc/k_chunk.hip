@@ -166,7 +166,7 @@ __device__ __forceinline__ void store8_split(u16 *hi, u16 *lo, const float (&x)[
 
 // ----------------------------------------------------------------------------- workspace
 // Per (sequence, head, chunk), all offsets in bytes, each region 256-aligned.
-//   W, Q'  : fragment (token tile m, key k-step ks) = 64 lanes x 16 B per plane,
+//   W, Q'  : fragment (token tile m, key k-step ks) = 64 lanes x 16 B (8 fp16),
 //            lane (kg, l16) holding row 16m + l16, keys pi(32ks, kg)
 //   K'^T   : fragment (key tile m, token k-step ks), lane holding key row
 //            16m + l16, tokens pi(32ks, kg)
@@ -174,24 +174,51 @@ __device__ __forceinline__ void store8_split(u16 *hi, u16 *lo, const float (&x)[
 //            (kg, l16) holding values 16d + 4kg + r of token 16m + l16
 // These are the exact register images the scan loads, so each of its wave
 // loads is 1 KiB (or 1 KiB of float4) of consecutive bytes.
-constexpr size_t WS_PLANE = (size_t)CH * DK * 2;        // one bf16 plane of a 64x128 matrix
+//
+// W, Q' and K' are stored as fp16 (relative rounding 2^-11), half the bytes
+// of a bf16 hi + lo pair: the scan is bound by the operand bytes each CU
+// pulls from L2 per chunk, so this halves its operand traffic.  The scan
+// splits each fp16 value into bf16 hi + lo in registers, which is exact (11
+// significant bits), so its products stay split-bf16 and its own operands --
+// the state and U tiles -- keep fp32 range.  W, Q' and K' themselves are
+// bounded by the unit-length keys and queries (K' entries by |k|, W and Q'
+// through T = (I + A)^{-1} with beta <= 1), far inside fp16's range.
+constexpr size_t WS_PLANE = (size_t)CH * DK * 2;        // one fp16 64x128 matrix
 constexpr size_t WS_W = 0;                              // W   (4 token tiles x 4 k-steps)
-constexpr size_t WS_Q = 2 * WS_PLANE;                   // Q'  (4 x 4)
-constexpr size_t WS_K = 4 * WS_PLANE;                   // K'^T (8 key tiles x 2 k-steps)
-constexpr size_t WS_U = 6 * WS_PLANE;                   // Ut  fp32 accumulator tiles
+constexpr size_t WS_Q = WS_PLANE;                       // Q'  (4 x 4)
+constexpr size_t WS_K = 2 * WS_PLANE;                   // K'^T (8 key tiles x 2 k-steps)
+constexpr size_t WS_U = 3 * WS_PLANE;                   // Ut  fp32 accumulator tiles
 constexpr size_t WS_O = WS_U + (size_t)DV * CH * 4;     // Oi  fp32 accumulator tiles
 constexpr size_t WS_G = WS_O + (size_t)DV * CH * 4;     // e^{G_n}
 constexpr size_t WS_CHUNK = WS_G + 256;
 
-// u16 offset of a fragment's 8 elements for lane `lane`
-__device__ __forceinline__ int frag_off(int m, int ks, int n_ks, int plane, int lane) {
-  return (((m * n_ks + ks) * 2 + plane) * 64 + lane) * 8;
+typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
+
+// u16 offset of a fragment's 8 fp16 values for lane `lane`
+__device__ __forceinline__ int frag_off(int m, int ks, int n_ks, int lane) {
+  return ((m * n_ks + ks) * 64 + lane) * 8;
 }
-__device__ __forceinline__ Frag frag_ws(const u16 *base, int m, int ks, int n_ks, int lane) {
+__device__ __forceinline__ h16x8 frag_ws(const u16 *base, int m, int ks, int n_ks, int lane) {
+  return *reinterpret_cast<const h16x8 *>(base + frag_off(m, ks, n_ks, lane));
+}
+// fp16 -> bf16 hi + lo, exactly (an fp16 value has 11 significant bits)
+__device__ __forceinline__ Frag split_h(const h16x8 &x) {
   Frag f;
-  f.hi = *reinterpret_cast<const bf16x8 *>(base + frag_off(m, ks, n_ks, 0, lane));
-  f.lo = *reinterpret_cast<const bf16x8 *>(base + frag_off(m, ks, n_ks, 1, lane));
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    u16 hi, lo;
+    split((float)x[e], hi, lo);
+    f.hi[e] = (short)hi;
+    f.lo[e] = (short)lo;
+  }
   return f;
+}
+// 8 floats -> one 16-byte store of fp16 (round to nearest even)
+__device__ __forceinline__ void store8_h(u16 *p, const float (&x)[8]) {
+  h16x8 h;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) h[e] = (_Float16)x[e];
+  *reinterpret_cast<h16x8 *>(p) = h;
 }
 // float offset of the accumulator tile (value tile d, token tile m) for lane
 __device__ __forceinline__ int acc_off(int d, int m, int lane) {
@@ -493,7 +520,7 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         x[e] = (bf16_value((u16)f.hi[e]) + bf16_value((u16)f.lo[e])) * sEGn[pi_k(32 * ks, kg, e)];
-      store8_split(ktg + frag_off(w, ks, 2, 0, lane), ktg + frag_off(w, ks, 2, 1, lane), x);
+      store8_h(ktg + frag_off(w, ks, 2, lane), x);
     }
   }
   __syncthreads();
@@ -626,8 +653,7 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
     for (int m = 0; m < 2; ++m) {
       const float xw[8] = {accW[0][m][0], accW[0][m][1], accW[0][m][2], accW[0][m][3],
                            accW[1][m][0], accW[1][m][1], accW[1][m][2], accW[1][m][3]};
-      store8_split(wg + frag_off(2 * tp + m, kp, 4, 0, lane),
-                   wg + frag_off(2 * tp + m, kp, 4, 1, lane), xw);
+      store8_h(wg + frag_off(2 * tp + m, kp, 4, lane), xw);
 #pragma unroll
       for (int d = 0; d < 2; ++d)
         *reinterpret_cast<float4 *>(ug + acc_off(2 * kp + d, 2 * tp + m, lane)) =
@@ -688,8 +714,7 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
         *reinterpret_cast<float4 *>(og + acc_off(2 * kp + d, 2 * tp + m, lane)) =
             make_float4(accO[d][m][0], accO[d][m][1], accO[d][m][2], accO[d][m][3]);
       }
-      store8_split(qg + frag_off(2 * tp + m, kp, 4, 0, lane),
-                   qg + frag_off(2 * tp + m, kp, 4, 1, lane), xq);
+      store8_h(qg + frag_off(2 * tp + m, kp, 4, lane), xq);
     }
   }
   // every thread stores the same value: no store behind a branch
@@ -711,8 +736,8 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
 // of P^T (w < 4) or of y^T (w >= 4).  S and U travel through LDS as row-major
 // [key][j] / [token][j] tiles and are read back by transpose reads.
 struct ChunkOps {
-  Frag b[4];     // W (P waves) or Q' (y waves) fragments of token tile w & 3, 4 key k-steps
-  Frag k[2];     // K'^T fragments of key tile w, 2 token k-steps
+  h16x8 b[4];    // W (P waves) or Q' (y waves) fragments of token tile w & 3, 4 key k-steps
+  h16x8 k[2];    // K'^T fragments of key tile w, 2 token k-steps
   float4 add;    // Ut (P waves) or Oi (y waves) accumulator tile (b, w & 3)
   float gam;     // e^{G_n}
 };
@@ -743,7 +768,7 @@ __device__ __forceinline__ void scan_chunk(const ChunkOps &o, f32x4 &st, u16 *ss
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
-    acc = mfma3(frag_tr(ssh, ssl, SPB, 32 * ks, 0, kg, l16), o.b[ks], acc);
+    acc = mfma3(frag_tr(ssh, ssl, SPB, 32 * ks, 0, kg, l16), split_h(o.b[ks]), acc);
   const int t = 16 * (w & 3) + l16;   // this lane's token; values 4kg + r
   if (w < 4) {
     store4_split(suh + t * SPB + 4 * kg, sul + t * SPB + 4 * kg, o.add.x - acc[0],
@@ -756,7 +781,8 @@ __device__ __forceinline__ void scan_chunk(const ChunkOps &o, f32x4 &st, u16 *ss
   __syncthreads();
   st = st * o.gam;
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) st = mfma3(frag_tr(suh, sul, SPB, 32 * ks, 0, kg, l16), o.k[ks], st);
+  for (int ks = 0; ks < 2; ++ks)
+    st = mfma3(frag_tr(suh, sul, SPB, 32 * ks, 0, kg, l16), split_h(o.k[ks]), st);
 }
 
 __global__ __launch_bounds__(512) void k_chunk_scan(
@@ -808,20 +834,19 @@ __global__ __launch_bounds__(512) void k_chunk_scan(
 // One 16-wave workgroup per (sequence, head, pair of value blocks): waves
 // 8g .. 8g+7 run exactly the per-wave arithmetic of k_chunk_scan on value
 // block 2p + g, so the results are bit-identical to it.  The two groups share
-// one copy of each chunk's W, Q' and K' (the first 96 KB of its workspace,
+// one copy of each chunk's W, Q' and K' (the first 48 KB of its workspace,
 // copied byte for byte), which halves the head's operand reads from L2; the
-// price is that every wave now reads its fragments from LDS, about 0.9 us of
-// LDS traffic per chunk, so this form only pays once the 8-wave grid would
-// need a second pass (48 heads: 180 us against 270 us for 4096 positions).
-// The copy is staged through registers one chunk ahead: each thread holds 64
-// bytes of W and Q' and 32 bytes of K'.  W and Q' are rewritten in LDS right
+// price is that every wave now reads its fragments from LDS, so this form
+// only pays once the 8-wave grid would need a second pass.
+// The copy is staged through registers one chunk ahead: each thread holds 32
+// bytes of W and Q' and 16 bytes of K'.  W and Q' are rewritten in LDS right
 // after the barrier that ends their last reads (the U barrier), K' right
 // after the barrier that ends the state update's reads (the S barrier).
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-constexpr int OPS_WQ = (int)(4 * WS_PLANE);   // W and Q', workspace bytes [0, 64 KiB)
-constexpr int OPS_K = (int)(2 * WS_PLANE);    // K'^T, workspace bytes [64, 96 KiB)
+constexpr int OPS_WQ = (int)(2 * WS_PLANE);   // W and Q', workspace bytes [0, 32 KiB)
+constexpr int OPS_K = (int)WS_PLANE;          // K'^T, workspace bytes [32, 48 KiB)
 constexpr int PAIR_THREADS = 1024;
-static_assert(WS_W == 0 && WS_Q == 2 * WS_PLANE && WS_K == (size_t)OPS_WQ, "operand layout");
+static_assert(WS_W == 0 && WS_Q == WS_PLANE && WS_K == (size_t)OPS_WQ, "operand layout");
 static_assert(OPS_WQ % (16 * PAIR_THREADS) == 0 && OPS_K % (16 * PAIR_THREADS) == 0, "copy split");
 
 __global__ __launch_bounds__(PAIR_THREADS) void k_chunk_scan_pair(
@@ -891,9 +916,7 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_chunk_scan_pair(
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      Frag b;
-      b.hi = *reinterpret_cast<const bf16x8 *>(b_lds + frag_off(w & 3, ks, 4, 0, lane));
-      b.lo = *reinterpret_cast<const bf16x8 *>(b_lds + frag_off(w & 3, ks, 4, 1, lane));
+      const Frag b = split_h(*reinterpret_cast<const h16x8 *>(b_lds + frag_off(w & 3, ks, 4, lane)));
       acc = mfma3(frag_tr(s_hi, s_lo, SPB, 32 * ks, 0, kg, l16), b, acc);
     }
     if (w < 4) {
@@ -910,9 +933,7 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_chunk_scan_pair(
     st = st * gam;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      Frag kf;
-      kf.hi = *reinterpret_cast<const bf16x8 *>(k_lds + frag_off(w, ks, 2, 0, lane));
-      kf.lo = *reinterpret_cast<const bf16x8 *>(k_lds + frag_off(w, ks, 2, 1, lane));
+      const Frag kf = split_h(*reinterpret_cast<const h16x8 *>(k_lds + frag_off(w, ks, 2, lane)));
       st = mfma3(frag_tr(u_hi, u_lo, SPB, 32 * ks, 0, kg, l16), kf, st);
     }
   };
