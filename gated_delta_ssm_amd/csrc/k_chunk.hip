@@ -230,9 +230,10 @@ __device__ __forceinline__ int acc_off(int d, int m, int lane) {
 // row-major LDS tiles are bf16 hi/lo planes.  Plan (bytes):
 //   L_K : K rows [t][i]            -> later W rows [s][i]
 //   L_Q : Q rows [t][i] -> V rows  -> later Ut rows [s][j]
-//   L_T : T1 = T diag(beta e^G), T2 = T diag(beta)  [t][s]
 //   L_L : L o Q K^T                 [t][s]
 //   L_A : A, then T in place (fp32 [64][68]);  L_S: four 16x16 blocks (pitch XP) of the inverse
+//         (T1 = T diag(beta e^G) and T2 = T diag(beta) are formed from it as
+//         fragments, in registers)
 //   L_G : G, beta, e^G, e^{G_n - G}
 // The products are computed transposed (feature index as the MFMA row):
 //   W^T = K^T T1^T,  Ut^T = V^T T2^T,  Q'^T = e^G Q^T - W^T (LQK)^T,
@@ -246,8 +247,7 @@ constexpr int TILE128 = 2 * CH * PR * 2;
 constexpr int TILE64 = 2 * CH * PS * 2;
 constexpr int L_K = 0;
 constexpr int L_Q = L_K + TILE128;
-constexpr int L_T = L_Q + TILE128;
-constexpr int L_L = L_T + 2 * TILE64;
+constexpr int L_L = L_Q + TILE128;
 constexpr int L_A = L_L + TILE64;
 constexpr int L_S = L_A + CH * PA * 4;
 constexpr int XP = 17;   // pitch (fp32) of the inverse's scratch blocks
@@ -285,23 +285,54 @@ __device__ __forceinline__ void lower_tiles(int w, const u16 *kh, const u16 *klo
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[j] = mfma3(fa[j], fb[j], acc[j]);
   }
+  // e^{G_t - G_s} is the hardware base-2 exponential of (G_t - G_s) log2(e),
+  // with the argument masked to 0 above the diagonal before it is taken; every
+  // entry of the tile is stored (zeros above the diagonal), so no lane branches
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
+    const int sx = 16 * tj[j] + l16;
+    const float gs = sG[sx];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = 16 * ti[j] + 4 * kg + r, sx = 16 * tj[j] + l16;
-      if (sx <= t) {
-        const float e = expf(sG[t] - sG[sx]);
-        if (!qk[j]) {
-          if (sx < t) sA[t * PA + sx] = sBeta[t] * e * acc[j][r];
-        } else {
-          u16 hh, ll;
-          split(e * acc[j][r], hh, ll);
-          lqh[t * PS + sx] = hh;
-          lql[t * PS + sx] = ll;
-        }
+      const int t = 16 * ti[j] + 4 * kg + r;
+      const float d = sx <= t ? sG[t] - gs : 0.0f;
+      const float e = __builtin_amdgcn_exp2f(d * 1.4426950408889634f);
+      if (!qk[j]) {
+        sA[t * PA + sx] = sx < t ? sBeta[t] * e * acc[j][r] : 0.0f;
+      } else {
+        u16 hh, ll;
+        split(sx <= t ? e * acc[j][r] : 0.0f, hh, ll);
+        lqh[t * PS + sx] = hh;
+        lql[t * PS + sx] = ll;
       }
     }
+  }
+}
+
+
+// Fragments of T1 = T diag(beta e^G) and T2 = T diag(beta), row `row`, k in
+// pi(k0, kg), formed from the fp32 inverse in LDS and split into bf16 hi + lo.
+__device__ __forceinline__ void t_frags(const float *sA, const float *sBeta, const float *sEG,
+                                        int row, int k0, int kg, Frag &f1, Frag &f2) {
+  const int c = k0 + 4 * kg;
+  const float4 a0 = *reinterpret_cast<const float4 *>(sA + row * PA + c);
+  const float4 a1 = *reinterpret_cast<const float4 *>(sA + row * PA + c + 16);
+  const float4 b0 = *reinterpret_cast<const float4 *>(sBeta + c);
+  const float4 b1 = *reinterpret_cast<const float4 *>(sBeta + c + 16);
+  const float4 e0 = *reinterpret_cast<const float4 *>(sEG + c);
+  const float4 e1 = *reinterpret_cast<const float4 *>(sEG + c + 16);
+  const float tv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+  const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+  const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    u16 h, l;
+    split(tv[e] * (bv[e] * ev[e]), h, l);
+    f1.hi[e] = (short)h;
+    f1.lo[e] = (short)l;
+    split(tv[e] * bv[e], h, l);
+    f2.hi[e] = (short)h;
+    f2.lo[e] = (short)l;
   }
 }
 
@@ -432,8 +463,6 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
 
   u16 *kh = reinterpret_cast<u16 *>(smem + L_K), *klo = kh + CH * PR;
   u16 *qh = reinterpret_cast<u16 *>(smem + L_Q), *qlo = qh + CH * PR;
-  u16 *t1h = reinterpret_cast<u16 *>(smem + L_T), *t1l = t1h + CH * PS;
-  u16 *t2h = t1l + CH * PS, *t2l = t2h + CH * PS;
   u16 *lqh = reinterpret_cast<u16 *>(smem + L_L), *lql = lqh + CH * PS;
   float *sA = reinterpret_cast<float *>(smem + L_A);
   float *scratch = reinterpret_cast<float *>(smem + L_S);
@@ -591,23 +620,6 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
     }
     __syncthreads();
   }
-  // S4. T1 = T diag(beta e^G), T2 = T diag(beta) as bf16 hi/lo [t][s]
-  {
-    const int row = tid >> 3, cg = (tid & 7) * 8;
-    const float4 a0 = *reinterpret_cast<const float4 *>(sA + row * PA + cg);
-    const float4 a1 = *reinterpret_cast<const float4 *>(sA + row * PA + cg + 4);
-    const float tv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-    float x1[8], x2[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      x1[e] = tv[e] * (sBeta[cg + e] * sEG[cg + e]);
-      x2[e] = tv[e] * sBeta[cg + e];
-    }
-    store8_split(t1h + row * PS + cg, t1l + row * PS + cg, x1);
-    store8_split(t2h + row * PS + cg, t2l + row * PS + cg, x2);
-  }
-  __syncthreads();
-
   // S5. W^T = K^T T1^T and Ut^T = V^T T2^T.  Wave w owns key/value tiles
   // 2kp, 2kp+1 (kp = w & 3) and token tiles 2tp, 2tp+1 (tp = w >> 2).
   const int kp = w & 3, tp = w >> 2;
@@ -632,8 +644,7 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
     Frag bt1[2], bt2[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      bt1[m] = frag_pi(t1h, t1l, PS, 16 * (2 * tp + m) + l16, 32 * ks, kg);
-      bt2[m] = frag_pi(t2h, t2l, PS, 16 * (2 * tp + m) + l16, 32 * ks, kg);
+      t_frags(sA, sBeta, sEG, 16 * (2 * tp + m) + l16, 32 * ks, kg, bt1[m], bt2[m]);
     }
 #pragma unroll
     for (int d = 0; d < 2; ++d) {
