@@ -40,6 +40,9 @@ _SIGS = {
     "gdn_recurrence_chunked_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "gdn_recurrence_chunked": (_I, [_P, _L, _P, _P, _L, _L, _P, _L, _L, _P, _P, _P, _L, _L,
                                     _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
+    "gdn_recurrence_chunked_varlen_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "gdn_recurrence_chunked_varlen": (_I, [_P, _L, _P, _P, _L, _P, _L, _P, _P, _P, _L, _P,
+                                           _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
     "gdn_gated_rmsnorm": (_I, [_P, _L, _P, _P, _L, _P, _L, _I, _I, _I, _F, _P]),
     "gdn_stream_copy": (_I, [_P, _P, _SZ, _P]),
     "gdn_decode_fused": (_I, [_P, _L, _P, _P, _L, _L, _P, _L, _L, _P, _P, _P, _P, _P, _P, _L,
@@ -217,6 +220,53 @@ def gdn_recurrence_chunked(state: torch.Tensor, q: torch.Tensor, k: torch.Tensor
         _ptr(v), v.stride(1), v.stride(0), _ptr(g), _ptr(beta), _ptr(y), y.stride(1),
         y.stride(0), n_seq, n_tok, H, Hk, S, scale, chunk, _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream, y)))
+    return y
+
+
+def gdn_recurrence_chunked_varlen_workspace_bytes(n_seq: int, total_tok: int, n_v_heads: int,
+                                                  n_qk_heads: int, S: int,
+                                                  chunk: int = 64) -> int:
+    return int(_lib.gdn_recurrence_chunked_varlen_workspace_bytes(n_seq, total_tok, n_v_heads,
+                                                                  n_qk_heads, S, chunk))
+
+
+def gdn_recurrence_chunked_varlen(state: torch.Tensor, q: torch.Tensor, k: torch.Tensor,
+                                  v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+                                  y: torch.Tensor, cu_seqlens, *, scale: float, chunk: int = 64,
+                                  workspace: torch.Tensor | None = None,
+                                  stream=None) -> torch.Tensor:
+    """Chunked recurrence over a packed batch of sequences of different lengths.
+    state [n_seq][H][S][S] (updated in place), q, k [total][Hk][S], v, y
+    [total][H][S], g, beta [total][H]; cu_seqlens: n_seq + 1 row offsets on the
+    host (a list or a CPU integer tensor).  If no workspace is given one is
+    allocated here through torch."""
+    cu = [int(c) for c in (cu_seqlens.tolist() if isinstance(cu_seqlens, torch.Tensor)
+                           else cu_seqlens)]
+    n_seq = len(cu) - 1
+    total, Hk, S = q.shape
+    H = v.shape[1]
+    if n_seq < 1 or tuple(state.shape) != (n_seq, H, S, S) or k.shape != q.shape:
+        raise ValueError("state / q / k / cu_seqlens shape mismatch")
+    if tuple(v.shape) != (total, H, S) or y.shape != v.shape:
+        raise ValueError("v / y shape mismatch")
+    if tuple(g.shape) != (total, H) or beta.shape != g.shape:
+        raise ValueError("g / beta shape mismatch")
+    _dev_f32("state", state, 3)
+    for n, t in (("q", q), ("k", k), ("v", v), ("y", y)):
+        _dev_f32(n, t, 2)
+    if q.stride() != k.stride():
+        raise ValueError("q and k must share strides")
+    _dev_f32("g", g, 2)
+    _dev_f32("beta", beta, 2)
+    cu_arr = (ctypes.c_int32 * (n_seq + 1))(*cu)
+    need = gdn_recurrence_chunked_varlen_workspace_bytes(n_seq, total, H, Hk, S, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=state.device)
+    _check("gdn_recurrence_chunked_varlen", _lib.gdn_recurrence_chunked_varlen(
+        _ptr(state), state.stride(0), _ptr(q), _ptr(k), q.stride(0), _ptr(v), v.stride(0),
+        _ptr(g), _ptr(beta), _ptr(y), y.stride(0), ctypes.cast(cu_arr, _P), n_seq, total, H,
+        Hk, S, scale, chunk, _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream, y)))
     return y
 
 

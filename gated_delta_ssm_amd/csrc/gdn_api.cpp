@@ -96,6 +96,45 @@ int gdn_recurrence_chunked(float *state, int64_t state_seq_stride, const float *
   return gdn::launch_recur_chunked(a, chunk, workspace, workspace_bytes, stream);
 }
 
+size_t gdn_recurrence_chunked_varlen_workspace_bytes(int n_seq, int total_tok, int n_v_heads,
+                                                     int n_qk_heads, int S, int chunk) {
+  if (n_seq < 1 || n_seq > GDN_VARLEN_MAX_SEQ || total_tok < 0 || n_v_heads < 1 ||
+      n_qk_heads < 1 || n_v_heads % n_qk_heads)
+    return 0;
+  if ((S != 32 && S != 64 && S != 128) || chunk != 64) return 0;
+  return gdn::chunked_varlen_workspace_bytes(n_seq, total_tok, n_v_heads, S);
+}
+
+int gdn_recurrence_chunked_varlen(float *state, int64_t state_seq_stride, const float *q,
+                                  const float *k, int64_t qk_tok_stride, const float *v,
+                                  int64_t v_tok_stride, const float *g, const float *beta,
+                                  float *y, int64_t y_tok_stride, const int32_t *cu_seqlens,
+                                  int n_seq, int total_tok, int n_v_heads, int n_qk_heads, int S,
+                                  float scale, int chunk, void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  const size_t need = gdn_recurrence_chunked_varlen_workspace_bytes(n_seq, total_tok, n_v_heads,
+                                                                    n_qk_heads, S, chunk);
+  const int rc = gdn::check_chunked_varlen(state, state_seq_stride, q, k, qk_tok_stride, v,
+                                           v_tok_stride, g, beta, y, y_tok_stride, cu_seqlens,
+                                           n_seq, total_tok, n_v_heads, n_qk_heads, S, chunk,
+                                           workspace, workspace_bytes, need);
+  if (rc != GDN_OK || total_tok == 0) return rc;
+  gdn::VarTab tab;
+  tab.n_seq = n_seq;
+  tab.tok0[0] = 0;
+  tab.ch0[0] = 0;
+  for (int s = 0; s < n_seq; ++s) {
+    tab.tok0[s + 1] = cu_seqlens[s + 1];
+    tab.ch0[s + 1] = tab.ch0[s] + gdn::padded_chunks(cu_seqlens[s + 1] - cu_seqlens[s]);
+  }
+  gdn::RecurArgs a{state,   state_seq_stride, q,            k,          qk_tok_stride,
+                   0,       v,                v_tok_stride, 0,          g,
+                   beta,    y,                y_tok_stride, 0,          nullptr,
+                   0,       n_seq,            total_tok,    n_v_heads,  n_qk_heads,
+                   S,       scale};
+  return gdn::launch_recur_chunked_varlen(a, tab, chunk, workspace, workspace_bytes, stream);
+}
+
 int gdn_gated_rmsnorm(const float *y, int64_t y_row_stride, const float *w, const float *z,
                       int64_t z_row_stride, float *out, int64_t out_row_stride, int rows,
                       int n_heads, int head_dim, float eps, hipStream_t stream) {

@@ -369,25 +369,55 @@ __device__ __forceinline__ void blk_store(float *D, const f32x4 &c, float sign, 
 
 // One phase A work item: chunk c of value head h of sequence s.
 struct PrepItem {
-  int c, h, s, hk;
-  int t0;   // first position of the chunk
-  int n;    // positions in the chunk; 0 for a padding chunk (the chunk count is
-            // rounded up to even so the scan's two-deep operand pipeline has no
-            // tail): it yields e^{G_n} = 1 and all-zero operands, which leaves
-            // the state unchanged
-  int nl;   // last valid row, for clamped loads
-  int tb;   // base position of the loads (valid for padding chunks)
+  int h, s, hk;
+  int n;      // positions in the chunk; 0 for a padding chunk (each sequence's
+              // chunk count is rounded up to even so the scan's two-deep operand
+              // pipeline has no tail): it yields e^{G_n} = 1 and all-zero
+              // operands, which leaves the state unchanged
+  int nl;     // last valid row, for clamped loads
+  int tb;     // row of the chunk's first load (clamped to the sequence's last
+              // row for padding chunks); within the sequence for a fixed-length
+              // batch, within the packed token rows for a variable-length one
+  int64_t grow;   // g / beta row of tb
+  size_t slot;    // workspace chunk slot
 };
-__device__ __forceinline__ PrepItem prep_item(int u, int n_chunks, int H, int Hk, int n_tok) {
+// Fixed-length batch: item u = (sequence, head, chunk), chunks fastest.
+__device__ __forceinline__ PrepItem prep_item(int u, int n_chunks, int H, int Hk, int n_tok,
+                                              const NoTab &) {
   PrepItem it;
-  it.c = u % n_chunks;
+  const int c = u % n_chunks;
   it.h = (u / n_chunks) % H;
   it.s = u / (n_chunks * H);
   it.hk = it.h / (H / Hk);
-  it.t0 = it.c * CH;
-  it.n = max(0, min(CH, n_tok - it.t0));
+  const int t0 = c * CH;
+  it.n = max(0, min(CH, n_tok - t0));
   it.nl = max(it.n - 1, 0);
-  it.tb = min(it.t0, n_tok - 1);
+  it.tb = min(t0, n_tok - 1);
+  it.grow = (int64_t)it.s * n_tok + it.tb;
+  it.slot = ((size_t)it.s * H + it.h) * n_chunks + c;
+  return it;
+}
+// Variable-length batch: item u = (head, packed chunk gc), gc fastest; the
+// sequence holding gc is found by binary search over the chunk offsets.
+__device__ __forceinline__ PrepItem prep_item(int u, int n_chunks, int H, int Hk, int,
+                                              const VarTab &tab) {
+  PrepItem it;
+  const int gc = u % n_chunks;
+  it.h = u / n_chunks;
+  it.hk = it.h / (H / Hk);
+  int lo = 0, hi = tab.n_seq - 1;   // last s with ch0[s] <= gc: a nonempty sequence
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (tab.ch0[mid] <= gc) lo = mid; else hi = mid - 1;
+  }
+  it.s = lo;
+  const int len = tab.tok0[lo + 1] - tab.tok0[lo];
+  const int t0 = (gc - tab.ch0[lo]) * CH;
+  it.n = max(0, min(CH, len - t0));
+  it.nl = max(it.n - 1, 0);
+  it.tb = tab.tok0[lo] + min(t0, len - 1);
+  it.grow = it.tb;
+  it.slot = (size_t)it.h * n_chunks + gc;
   return it;
 }
 
@@ -401,8 +431,7 @@ struct PrepIn {
 };
 __device__ __forceinline__ void load_gb(const PrepIn &in, const PrepItem &it, int lane, float &gv,
                                         float &bv) {
-  const int64_t gi =
-      ((int64_t)it.s * in.n_tok + min(it.t0 + min(lane, it.nl), in.n_tok - 1)) * in.H + it.h;
+  const int64_t gi = (it.grow + min(lane, it.nl)) * in.H + it.h;
   gv = in.g[gi];
   bv = in.beta[gi];
 }
@@ -453,11 +482,12 @@ __device__ __forceinline__ void store_row8(u16 *hi, u16 *lo, const float4 &a, co
 // beta, K, Q and V are loaded into registers as soon as the current item has
 // consumed them, so a workgroup's loads and stores overlap its own compute
 // instead of every CU loading, then computing, then storing in lockstep.
+template <class TAB>
 __global__ __launch_bounds__(512) void k_chunk_prep(
     const float *__restrict__ q, const float *__restrict__ k, int64_t qk_tok, int64_t qk_seq,
     const float *__restrict__ v, int64_t v_tok, int64_t v_seq, const float *__restrict__ g,
     const float *__restrict__ beta, unsigned char *__restrict__ ws, int n_tok, int n_chunks,
-    int H, int Hk, int n_items) {
+    int H, int Hk, int n_items, const TAB tab) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[L_TOTAL];
   const PrepIn in{q, k, v, g, beta, qk_tok, qk_seq, v_tok, v_seq, n_tok, H};
 
@@ -470,7 +500,7 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
   float *sBeta = sG + CH, *sEG = sG + 2 * CH, *sEGn = sG + 3 * CH;
 
   // the grid never exceeds n_items, so every workgroup has a first item
-  PrepItem it = prep_item(blockIdx.x, n_chunks, H, Hk, n_tok);
+  PrepItem it = prep_item(blockIdx.x, n_chunks, H, Hk, n_tok, tab);
   float gv, bv;
   float4 kr[4], qr[4], vr[4];
   load_gb(in, it, threadIdx.x & 63, gv, bv);
@@ -490,10 +520,10 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
   // the item after this one (this one again on the last pass: its loads are
   // then redundant but in bounds, and no load sits behind a branch)
   const PrepItem nx = prep_item(u + gridDim.x < n_items ? u + gridDim.x : u, n_chunks, H, Hk,
-                                n_tok);
+                                n_tok, tab);
   const int n = it.n, nl = it.nl;
   const float *qc = q + it.s * qk_seq + (int64_t)it.tb * qk_tok + it.hk * DK;
-  unsigned char *wc = ws + (((size_t)it.s * H + it.h) * n_chunks + it.c) * WS_CHUNK;
+  unsigned char *wc = ws + it.slot * WS_CHUNK;
 
   // S0. gate cumsum (wave 0) and cleared tiles
   if (w == 0) {
@@ -767,6 +797,28 @@ __device__ __forceinline__ void load_chunk(ChunkOps &o, const unsigned char *wc,
   o.gam = *reinterpret_cast<const float *>(wc + WS_G);
 }
 
+// The chunks one (sequence, head) walks in phase B: its first workspace slot,
+// chunk count (even), positions and first token row.  An empty sequence has
+// no chunks; its first slot is then slot 0, so the operand loads issued before
+// the (empty) chunk loop stay inside the workspace, and the state is written
+// back as it was read.  (The scan kernels have no early exit: on the 16-wave
+// form one changed its results even where it was never taken.)
+struct HeadChunks {
+  size_t first;
+  int nch, len;
+  int64_t row0;
+};
+__device__ __forceinline__ HeadChunks head_chunks(const NoTab &, int s, int h, int H, int n_tok,
+                                                  int n_chunks) {
+  return HeadChunks{((size_t)s * H + h) * n_chunks, n_chunks, n_tok, 0};
+}
+__device__ __forceinline__ HeadChunks head_chunks(const VarTab &tab, int s, int h, int, int,
+                                                  int n_chunks) {
+  const int nch = tab.ch0[s + 1] - tab.ch0[s];
+  return HeadChunks{nch > 0 ? (size_t)h * n_chunks + tab.ch0[s] : 0, nch,
+                    tab.tok0[s + 1] - tab.tok0[s], tab.tok0[s]};
+}
+
 constexpr int SPB = 24;   // pitch (bf16) of the [128][16] S tile and the [64][16] U tile
 
 __device__ __forceinline__ void scan_chunk(const ChunkOps &o, f32x4 &st, u16 *ssh, u16 *ssl,
@@ -796,10 +848,11 @@ __device__ __forceinline__ void scan_chunk(const ChunkOps &o, f32x4 &st, u16 *ss
     st = mfma3(frag_tr(suh, sul, SPB, 32 * ks, 0, kg, l16), split_h(o.k[ks]), st);
 }
 
+template <class TAB>
 __global__ __launch_bounds__(512) void k_chunk_scan(
     float *__restrict__ state, int64_t st_seq, const unsigned char *__restrict__ ws,
     float *__restrict__ y, int64_t y_tok, int64_t y_seq, int n_tok, int n_chunks, int H,
-    float scale) {
+    float scale, const TAB tab) {
   __shared__ __attribute__((aligned(16))) u16 ssh[DK * SPB], ssl[DK * SPB];
   __shared__ __attribute__((aligned(16))) u16 suh[CH * SPB], sul[CH * SPB];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
@@ -808,17 +861,18 @@ __global__ __launch_bounds__(512) void k_chunk_scan(
   const int nwg = gridDim.x, per_xcd = nwg / 8;
   const int unit = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   const int blk = unit % NVB, sh = unit / NVB, h = sh % H, s = sh / H;
+  const HeadChunks hc = head_chunks(tab, s, h, H, n_tok, n_chunks);
 
   // state element (value j = 16 blk + 4kg + r, key i = 16w + l16), value-major
   float *sp = state + s * st_seq + (int64_t)h * DK * DV +
               (int64_t)(blk * NBLK + 4 * kg) * DK + 16 * w + l16;
   f32x4 st = {sp[0], sp[DK], sp[2 * DK], sp[3 * DK]};
-  const unsigned char *wh = ws + ((size_t)s * H + h) * n_chunks * WS_CHUNK;
-  float *yh = y + s * y_seq + (int64_t)h * DV + blk * NBLK;
-  auto chunk_ptr = [&](int c) { return wh + (size_t)min(c, n_chunks - 1) * WS_CHUNK; };
+  const unsigned char *wh = ws + hc.first * WS_CHUNK;
+  float *yh = y + s * y_seq + hc.row0 * y_tok + (int64_t)h * DV + blk * NBLK;
+  auto chunk_ptr = [&](int c) { return wh + (size_t)max(min(c, hc.nch - 1), 0) * WS_CHUNK; };
   auto run = [&](const ChunkOps &o, int c) {
     scan_chunk(o, st, ssh, ssl, suh, sul, yh + (int64_t)c * CH * y_tok, y_tok,
-               min(CH, n_tok - c * CH), scale, w, l16, kg);
+               min(CH, hc.len - c * CH), scale, w, l16, kg);
   };
 
   // Two operand sets: chunk c + 2's are requested as soon as chunk c has run
@@ -829,7 +883,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan(
   ChunkOps a, b;
   load_chunk(a, chunk_ptr(0), w, lane, blk);
   load_chunk(b, chunk_ptr(1), w, lane, blk);
-  for (int c = 0; c < n_chunks; c += 2) {
+  for (int c = 0; c < hc.nch; c += 2) {
     run(a, c);
     load_chunk(a, chunk_ptr(c + 2), w, lane, blk);
     run(b, c + 1);
@@ -860,10 +914,11 @@ constexpr int PAIR_THREADS = 1024;
 static_assert(WS_W == 0 && WS_Q == WS_PLANE && WS_K == (size_t)OPS_WQ, "operand layout");
 static_assert(OPS_WQ % (16 * PAIR_THREADS) == 0 && OPS_K % (16 * PAIR_THREADS) == 0, "copy split");
 
+template <class TAB>
 __global__ __launch_bounds__(PAIR_THREADS) void k_chunk_scan_pair(
     float *__restrict__ state, int64_t st_seq, const unsigned char *__restrict__ ws,
     float *__restrict__ y, int64_t y_tok, int64_t y_seq, int n_tok, int n_chunks, int H,
-    float scale) {
+    float scale, const TAB tab) {
   constexpr int NWQ = OPS_WQ / (16 * PAIR_THREADS), NK = OPS_K / (16 * PAIR_THREADS);
   __shared__ __attribute__((aligned(16))) u16 ssh[2][DK * SPB], ssl[2][DK * SPB];
   __shared__ __attribute__((aligned(16))) u16 suh[2][CH * SPB], sul[2][CH * SPB];
@@ -878,13 +933,14 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_chunk_scan_pair(
   const int unit = (xcd < r8 ? xcd * (q8 + 1) : r8 * (q8 + 1) + (xcd - r8) * q8) + idx;
   const int pair = unit % (NVB / 2), sh = unit / (NVB / 2), h = sh % H, s = sh / H;
   const int blk = 2 * pair + grp;
+  const HeadChunks hc = head_chunks(tab, s, h, H, n_tok, n_chunks);
 
   float *sp = state + s * st_seq + (int64_t)h * DK * DV +
               (int64_t)(blk * NBLK + 4 * kg) * DK + 16 * w + l16;
   f32x4 st = {sp[0], sp[DK], sp[2 * DK], sp[3 * DK]};
-  const unsigned char *wh = ws + ((size_t)s * H + h) * n_chunks * WS_CHUNK;
-  float *yh = y + s * y_seq + (int64_t)h * DV + blk * NBLK;
-  auto chunk_ptr = [&](int c) { return wh + (size_t)min(c, n_chunks - 1) * WS_CHUNK; };
+  const unsigned char *wh = ws + hc.first * WS_CHUNK;
+  float *yh = y + s * y_seq + hc.row0 * y_tok + (int64_t)h * DV + blk * NBLK;
+  auto chunk_ptr = [&](int c) { return wh + (size_t)max(min(c, hc.nch - 1), 0) * WS_CHUNK; };
   u16 *s_hi = ssh[grp], *s_lo = ssl[grp], *u_hi = suh[grp], *u_lo = sul[grp];
   const u16 *b_lds = reinterpret_cast<const u16 *>(ops + (w < 4 ? WS_W : WS_Q));
   const u16 *k_lds = reinterpret_cast<const u16 *>(ops + OPS_WQ);
@@ -933,7 +989,7 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_chunk_scan_pair(
     if (w < 4) {
       store4_split(u_hi + t * SPB + 4 * kg, u_lo + t * SPB + 4 * kg, add.x - acc[0],
                    add.y - acc[1], add.z - acc[2], add.w - acc[3]);
-    } else if (t < min(CH, n_tok - c * CH)) {
+    } else if (t < min(CH, hc.len - c * CH)) {
       *reinterpret_cast<float4 *>(yh + (int64_t)(c * CH + t) * y_tok + 4 * kg) =
           make_float4(scale * (acc[0] + add.x), scale * (acc[1] + add.y),
                       scale * (acc[2] + add.z), scale * (acc[3] + add.w));
@@ -957,8 +1013,8 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_chunk_scan_pair(
   float gam0, gam1;
   load_add(chunk_ptr(0), add0, gam0);
   load_add(chunk_ptr(1), add1, gam1);
-  // n_chunks is even, as for k_chunk_scan
-  for (int c = 0; c < n_chunks; c += 2) {
+  // the chunk count is even, as for k_chunk_scan
+  for (int c = 0; c < hc.nch; c += 2) {
     run(c, add0, gam0);
     load_add(chunk_ptr(c + 2), add0, gam0);
     run(c + 1, add1, gam1);
@@ -972,12 +1028,19 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_chunk_scan_pair(
 
 }  // namespace
 
-// chunks per sequence in the workspace: ceil(n_tok / 64) rounded up to even
-static int padded_chunks(int n_tok) { return ((n_tok + CH - 1) / CH + 1) & ~1; }
+static_assert(CH == 64, "padded_chunks counts 64-position chunks");
 
 size_t chunked_workspace_bytes(int n_seq, int n_tok, int H, int, int S, int) {
   if (S != DK) return 0;   // the S = 32 / 64 form keeps everything on chip
   return (size_t)n_seq * H * padded_chunks(n_tok) * WS_CHUNK;
+}
+
+// Sum over sequences of padded_chunks(len) <= sum(ceil(len / 64)) + n_seq
+// <= (total_tok + 63 n_seq) / 64 + n_seq, for any split of total_tok.
+size_t chunked_varlen_workspace_bytes(int n_seq, int total_tok, int H, int S) {
+  if (S != DK) return 0;
+  const int64_t slots = ((int64_t)total_tok + 63 * (int64_t)n_seq) / CH + n_seq;
+  return (size_t)slots * H * WS_CHUNK;
 }
 
 // Compute units of the current device, queried once per device.
@@ -995,6 +1058,33 @@ static int device_cu_count() {
   return cached[dev];
 }
 
+// Phase A then phase B of one call; n_chunks is the per-sequence chunk count
+// (fixed-length batch) or the packed total (variable-length batch).
+template <class TAB>
+static int launch_two_phase(const RecurArgs &a, const TAB &tab, int n_chunks, int n_items,
+                            unsigned char *wsb, hipStream_t stream) {
+  // phase A: one persistent workgroup per CU (its LDS allows no more), or one
+  // per item when there are fewer items than CUs
+  const int cus = device_cu_count();
+  if (cus <= 0) return GDN_ERR_LAUNCH;
+  const int grid_a = n_items < cus ? n_items : cus;
+  int rc = launch_kernel(k_chunk_prep<TAB>, dim3(grid_a), dim3(512), 0, stream, a.q, a.k,
+                         a.qk_tok, a.qk_seq, a.v, a.v_tok, a.v_seq, a.g, a.beta, wsb, a.n_tok,
+                         n_chunks, a.H, a.Hk, n_items, tab);
+  if (rc != GDN_OK) return rc;
+  // phase B: 8-wave workgroups while they fit in one pass of the chip (one per
+  // CU: their registers allow no second); past that, the 16-wave form whose
+  // pairs of value blocks share operand copies
+  const int nwg = a.n_seq * a.H * NVB;  // a multiple of 8 (NVB == 8)
+  if (nwg > cus)
+    return launch_kernel(k_chunk_scan_pair<TAB>, dim3(nwg / 2), dim3(PAIR_THREADS), 0, stream,
+                         a.state, a.st_seq, (const unsigned char *)wsb, a.y, a.y_tok, a.y_seq,
+                         a.n_tok, n_chunks, a.H, a.scale, tab);
+  return launch_kernel(k_chunk_scan<TAB>, dim3(nwg), dim3(512), 0, stream, a.state, a.st_seq,
+                       (const unsigned char *)wsb, a.y, a.y_tok, a.y_seq, a.n_tok, n_chunks, a.H,
+                       a.scale, tab);
+}
+
 int launch_recur_chunked(const RecurArgs &a, int chunk, void *ws, size_t ws_bytes,
                          hipStream_t stream) {
   if (chunk != CH) return GDN_ERR_UNSUPPORTED;
@@ -1002,28 +1092,19 @@ int launch_recur_chunked(const RecurArgs &a, int chunk, void *ws, size_t ws_byte
   const int n_chunks = padded_chunks(a.n_tok);
   if (ws_bytes < chunked_workspace_bytes(a.n_seq, a.n_tok, a.H, a.Hk, a.S, chunk))
     return GDN_ERR_WORKSPACE;
-  unsigned char *wsb = static_cast<unsigned char *>(ws);
-  // phase A: one persistent workgroup per CU (its LDS allows no more), or one
-  // per item when there are fewer items than CUs
-  const int n_items = n_chunks * a.H * a.n_seq;
-  const int cus = device_cu_count();
-  if (cus <= 0) return GDN_ERR_LAUNCH;
-  const int grid_a = n_items < cus ? n_items : cus;
-  int rc = launch_kernel(k_chunk_prep, dim3(grid_a), dim3(512), 0, stream, a.q, a.k, a.qk_tok,
-                         a.qk_seq, a.v, a.v_tok, a.v_seq, a.g, a.beta, wsb, a.n_tok, n_chunks,
-                         a.H, a.Hk, n_items);
-  if (rc != GDN_OK) return rc;
-  // phase B: 8-wave workgroups while they fit in one pass of the chip (one per
-  // CU: their registers allow no second); past that, the 16-wave form whose
-  // pairs of value blocks share operand copies
-  const int nwg = a.n_seq * a.H * NVB;  // a multiple of 8 (NVB == 8)
-  if (nwg > cus)
-    return launch_kernel(k_chunk_scan_pair, dim3(nwg / 2), dim3(PAIR_THREADS), 0, stream,
-                         a.state, a.st_seq, (const unsigned char *)wsb, a.y, a.y_tok, a.y_seq,
-                         a.n_tok, n_chunks, a.H, a.scale);
-  return launch_kernel(k_chunk_scan, dim3(nwg), dim3(512), 0, stream, a.state, a.st_seq,
-                       (const unsigned char *)wsb, a.y, a.y_tok, a.y_seq, a.n_tok, n_chunks, a.H,
-                       a.scale);
+  return launch_two_phase(a, NoTab{}, n_chunks, n_chunks * a.H * a.n_seq,
+                          static_cast<unsigned char *>(ws), stream);
+}
+
+int launch_recur_chunked_varlen(const RecurArgs &a, const VarTab &tab, int chunk, void *ws,
+                                size_t ws_bytes, hipStream_t stream) {
+  if (chunk != CH) return GDN_ERR_UNSUPPORTED;
+  if (a.S != DK) return launch_chunk_small_varlen(a, tab, stream);
+  const int n_chunks = tab.ch0[tab.n_seq];   // packed total, even per sequence
+  if (n_chunks == 0) return GDN_OK;           // every sequence is empty
+  if (ws_bytes < (size_t)n_chunks * a.H * WS_CHUNK) return GDN_ERR_WORKSPACE;
+  return launch_two_phase(a, tab, n_chunks, n_chunks * a.H, static_cast<unsigned char *>(ws),
+                          stream);
 }
 
 }  // namespace gdn

@@ -28,12 +28,27 @@ namespace {
 
 constexpr int SC = 64;   // positions per chunk
 
-template <int S>
+// First token row and length of sequence s: a fixed-length batch addresses
+// sequences through their strides (row 0, n_tok positions; g and beta rows
+// s * n_tok + t), a packed one through its row table (seq strides are 0).
+struct SeqRows {
+  int64_t row0, grow0;
+  int len;
+};
+__device__ __forceinline__ SeqRows seq_rows(const NoTab &, int s, int n_tok) {
+  return SeqRows{0, (int64_t)s * n_tok, n_tok};
+}
+__device__ __forceinline__ SeqRows seq_rows(const VarTab &tab, int s, int) {
+  return SeqRows{tab.tok0[s], tab.tok0[s], tab.tok0[s + 1] - tab.tok0[s]};
+}
+
+template <int S, class TAB>
 __global__ __launch_bounds__(256) void k_chunk_small(
     float *__restrict__ state, int64_t st_seq, const float *__restrict__ q,
     const float *__restrict__ k, int64_t qk_tok, int64_t qk_seq, const float *__restrict__ v,
     int64_t v_tok, int64_t v_seq, const float *__restrict__ g, const float *__restrict__ beta,
-    float *__restrict__ y, int64_t y_tok, int64_t y_seq, int n_tok, int H, int Hk, float scale) {
+    float *__restrict__ y, int64_t y_tok, int64_t y_seq, int n_tok_arg, int H, int Hk,
+    float scale, const TAB tab) {
   constexpr int P = S + 1;        // row pitch of the [64][S] and [S][S] tiles
   constexpr int PC = SC + 1;      // row pitch of the [64][64] tiles
   static_assert(SC * PC >= SC * P, "U reuses the A tile");
@@ -47,6 +62,8 @@ __global__ __launch_bounds__(256) void k_chunk_small(
 
   const int tid = threadIdx.x;
   const int h = blockIdx.x, s = blockIdx.y, hk = h / (H / Hk);
+  const SeqRows sr = seq_rows(tab, s, n_tok_arg);
+  const int n_tok = sr.len;
   float *st = state + s * st_seq + (int64_t)h * S * S;   // st[j * S + i] = S0[i][j]
   for (int e = tid; e < S * S; e += 256) sS[(e % S) * P + e / S] = st[e];
 
@@ -57,7 +74,7 @@ __global__ __launch_bounds__(256) void k_chunk_small(
     for (int e = tid; e < SC * S; e += 256) {
       const int t = e / S, i = e - t * S;
       const bool ok = t < n;
-      const int64_t tt = ok ? t0 + t : t0;
+      const int64_t tt = sr.row0 + (ok ? t0 + t : t0);
       const float kv = k[s * qk_seq + tt * qk_tok + (int64_t)hk * S + i];
       const float qv = q[s * qk_seq + tt * qk_tok + (int64_t)hk * S + i];
       const float vv = v[s * v_seq + tt * v_tok + (int64_t)h * S + i];
@@ -67,7 +84,7 @@ __global__ __launch_bounds__(256) void k_chunk_small(
     }
     if (tid < SC) {   // wave 0: G (inclusive cumsum), beta
       const int t = tid;
-      const int64_t gi = ((int64_t)s * n_tok + t0 + (t < n ? t : 0)) * H + h;
+      const int64_t gi = (sr.grow0 + t0 + (t < n ? t : 0)) * H + h;
       float gv = t < n ? g[gi] : 0.0f;
       const float bv = t < n ? beta[gi] : 0.0f;
 #pragma unroll
@@ -146,7 +163,7 @@ __global__ __launch_bounds__(256) void k_chunk_small(
 #pragma unroll 8
         for (int i = 0; i < S; ++i) qs = __builtin_fmaf(sQ[t * P + i], sS[i * P + j], qs);
         for (int u = 0; u <= t; ++u) lu = __builtin_fmaf(sL[t * PC + u], sU[u * P + j], lu);
-        y[s * y_seq + (int64_t)(t0 + t) * y_tok + (int64_t)h * S + j] =
+        y[s * y_seq + (sr.row0 + t0 + t) * y_tok + (int64_t)h * S + j] =
             scale * (sEG[t] * qs + lu);
       }
     }
@@ -166,21 +183,31 @@ __global__ __launch_bounds__(256) void k_chunk_small(
   for (int e = tid; e < S * S; e += 256) st[e] = sS[(e % S) * P + e / S];
 }
 
-template <int S>
-int run_small(const RecurArgs &a, hipStream_t stream) {
-  return launch_kernel(k_chunk_small<S>, dim3((unsigned)a.H, (unsigned)a.n_seq), dim3(256), 0,
-                       stream, a.state, a.st_seq, a.q, a.k, a.qk_tok, a.qk_seq, a.v, a.v_tok,
-                       a.v_seq, a.g, a.beta, a.y, a.y_tok, a.y_seq, a.n_tok, a.H, a.Hk, a.scale);
+template <int S, class TAB>
+int run_small(const RecurArgs &a, const TAB &tab, hipStream_t stream) {
+  return launch_kernel(k_chunk_small<S, TAB>, dim3((unsigned)a.H, (unsigned)a.n_seq), dim3(256),
+                       0, stream, a.state, a.st_seq, a.q, a.k, a.qk_tok, a.qk_seq, a.v, a.v_tok,
+                       a.v_seq, a.g, a.beta, a.y, a.y_tok, a.y_seq, a.n_tok, a.H, a.Hk, a.scale,
+                       tab);
+}
+
+template <class TAB>
+int run_small_s(const RecurArgs &a, const TAB &tab, hipStream_t stream) {
+  switch (a.S) {
+    case 32: return run_small<32>(a, tab, stream);
+    case 64: return run_small<64>(a, tab, stream);
+    default: return GDN_ERR_UNSUPPORTED;
+  }
 }
 
 }  // namespace
 
 int launch_chunk_small(const RecurArgs &a, hipStream_t stream) {
-  switch (a.S) {
-    case 32: return run_small<32>(a, stream);
-    case 64: return run_small<64>(a, stream);
-    default: return GDN_ERR_UNSUPPORTED;
-  }
+  return run_small_s(a, NoTab{}, stream);
+}
+
+int launch_chunk_small_varlen(const RecurArgs &a, const VarTab &tab, hipStream_t stream) {
+  return run_small_s(a, tab, stream);
 }
 
 }  // namespace gdn

@@ -68,8 +68,29 @@ int launch_recur_decode(const RecurArgs &a, hipStream_t stream);
 size_t chunked_workspace_bytes(int n_seq, int n_tok, int H, int Hk, int S, int chunk);
 int launch_recur_chunked(const RecurArgs &a, int chunk, void *ws, size_t ws_bytes,
                          hipStream_t stream);
+
+// Sequence map of a chunked call, passed to the kernels by value.  NoTab: a
+// fixed-length batch (sequence s at s * seq_stride, n_tok positions each).
+// VarTab: a packed variable-length batch; sequence s holds token rows
+// tok0[s] .. tok0[s+1]-1 and workspace chunks ch0[s] .. ch0[s+1]-1 (its chunk
+// count rounded up to even); ch0[n_seq] is the total.
+struct NoTab {};
+struct VarTab {
+  int n_seq;
+  int tok0[GDN_VARLEN_MAX_SEQ + 1];
+  int ch0[GDN_VARLEN_MAX_SEQ + 1];
+};
+// Chunk slots a sequence of n_tok positions takes: ceil(n_tok / 64) rounded up
+// to even (0 for an empty sequence).
+inline int padded_chunks(int n_tok) { return ((n_tok + 63) / 64 + 1) & ~1; }
+// Workspace bound of a packed batch of n_seq sequences and total_tok positions.
+size_t chunked_varlen_workspace_bytes(int n_seq, int total_tok, int H, int S);
+// a.n_tok is the packed total; a.qk_seq, a.v_seq, a.y_seq are unused.
+int launch_recur_chunked_varlen(const RecurArgs &a, const VarTab &tab, int chunk, void *ws,
+                                size_t ws_bytes, hipStream_t stream);
 // The chunked form for S = 32 and 64 (fp32, one pass, no workspace).
 int launch_chunk_small(const RecurArgs &a, hipStream_t stream);
+int launch_chunk_small_varlen(const RecurArgs &a, const VarTab &tab, hipStream_t stream);
 
 struct NormArgs {
   const float *y;

@@ -155,6 +155,43 @@ int check_chunked(const float *state, int64_t st_seq, const float *q, const floa
   return GDN_OK;
 }
 
+int check_chunked_varlen(const float *state, int64_t st_seq, const float *q, const float *k,
+                         int64_t qk_tok, const float *v, int64_t v_tok, const float *g,
+                         const float *beta, const float *y, int64_t y_tok, const int32_t *cu,
+                         int n_seq, int total_tok, int H, int Hk, int S, int chunk,
+                         const void *ws, size_t ws_bytes, size_t ws_needed) {
+  if (n_seq < 1 || n_seq > GDN_VARLEN_MAX_SEQ || total_tok < 0) return GDN_ERR_SHAPE;
+  if (!cu) return GDN_ERR_NULL;
+  if (cu[0] != 0 || cu[n_seq] != total_tok) return GDN_ERR_SHAPE;
+  for (int s = 0; s < n_seq; ++s)
+    if (cu[s + 1] < cu[s]) return GDN_ERR_SHAPE;
+  if (total_tok == 0) {   // nothing to compute; the shape rules still apply
+    if (H < 1 || Hk < 1 || H % Hk != 0) return GDN_ERR_SHAPE;
+    if (chunk != 64 || (S != 32 && S != 64 && S != 128)) return GDN_ERR_UNSUPPORTED;
+    return state ? GDN_OK : GDN_ERR_NULL;
+  }
+  // the token tensors as one sequence of total_tok rows; the state checked
+  // below over all n_seq sequences
+  int rc = check_chunked(state, 0, q, k, qk_tok, 0, v, v_tok, 0, g, beta, y, y_tok, 0, 1,
+                         total_tok, H, Hk, S, chunk, ws, ws_bytes, ws_needed);
+  if (rc != GDN_OK) return rc;
+  if (st_seq < 0) return GDN_ERR_SHAPE;
+  const int64_t st_len = (int64_t)S * S * H;
+  if (!rows_disjoint(n_seq, st_seq, 1, 0, st_len)) return GDN_ERR_SHAPE;
+  if (st_seq % (S >= 64 ? 4 : 2)) return GDN_ERR_SHAPE;
+  const Span sst = span_of(state, n_seq, st_seq, 1, 0, st_len);
+  for (Span t : {span_of(q, 1, 0, total_tok, qk_tok, (int64_t)Hk * S),
+                 span_of(k, 1, 0, total_tok, qk_tok, (int64_t)Hk * S),
+                 span_of(v, 1, 0, total_tok, v_tok, (int64_t)H * S),
+                 span_of(y, 1, 0, total_tok, y_tok, (int64_t)H * S),
+                 span_of(g, 1, 0, 1, 0, (int64_t)total_tok * H),
+                 span_of(beta, 1, 0, 1, 0, (int64_t)total_tok * H)})
+    if (overlap(sst, t)) return GDN_ERR_ALIAS;
+  if (S == 128 && ws && overlap(sst, Span{(uintptr_t)ws, (uintptr_t)ws + ws_bytes}))
+    return GDN_ERR_ALIAS;
+  return GDN_OK;
+}
+
 int check_norm(const float *y, int64_t y_row, const float *w, const float *z, int64_t z_row,
                const float *out, int64_t o_row, int rows, int H, int hd) {
   if (rows < 0 || H < 1) return GDN_ERR_SHAPE;

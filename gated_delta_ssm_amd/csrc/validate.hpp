@@ -24,6 +24,14 @@ int check_chunked(const float *state, int64_t st_seq, const float *q, const floa
                   int64_t y_seq, int n_seq, int n_tok, int H, int Hk, int S, int chunk,
                   const void *ws, size_t ws_bytes, size_t ws_needed);
 
+// A packed batch: cu host array of n_seq + 1 offsets; token tensors are one
+// [total_tok] run of rows, the state n_seq rows of st_seq.
+int check_chunked_varlen(const float *state, int64_t st_seq, const float *q, const float *k,
+                         int64_t qk_tok, const float *v, int64_t v_tok, const float *g,
+                         const float *beta, const float *y, int64_t y_tok, const int32_t *cu,
+                         int n_seq, int total_tok, int H, int Hk, int S, int chunk,
+                         const void *ws, size_t ws_bytes, size_t ws_needed);
+
 int check_norm(const float *y, int64_t y_row, const float *w, const float *z, int64_t z_row,
                const float *out, int64_t o_row, int rows, int H, int hd);
 

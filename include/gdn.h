@@ -181,6 +181,50 @@ int gdn_recurrence_chunked(float *state, int64_t state_seq_stride, const float *
                            int n_qk_heads, int S, float scale, int chunk, void *workspace,
                            size_t workspace_bytes, hipStream_t stream);
 
+/* Most sequences one gdn_recurrence_chunked_varlen call takes. */
+#define GDN_VARLEN_MAX_SEQ 256
+
+/*
+ * Workspace bytes gdn_recurrence_chunked_varlen needs for any split of
+ * total_tok positions into n_seq sequences (a bound; 0 if the sizes are
+ * invalid or S is 32 or 64, which need none).
+ */
+size_t gdn_recurrence_chunked_varlen_workspace_bytes(int n_seq, int total_tok, int n_v_heads,
+                                                     int n_qk_heads, int S, int chunk);
+
+/*
+ * The chunked recurrence of gdn_recurrence_chunked over a packed batch of
+ * sequences of different lengths, in one call: every sequence runs the
+ * chunked form from its own state, its chunks starting at its own first
+ * position.  [AT] "Mamba-2 SSD chunked prefill scan" comment (ceil(T/64)
+ * sequential links per sequence); [FM] fm_ssm_recurrence_seq_at is the
+ * per-sequence definition.
+ *
+ *   cu_seqlens  HOST array of n_seq + 1 int32: sequence s holds packed token
+ *               rows cu_seqlens[s] .. cu_seqlens[s+1]-1; cu_seqlens[0] = 0,
+ *               non-decreasing, cu_seqlens[n_seq] = total_tok.  Empty
+ *               sequences are allowed (their state is left as it is).  Read
+ *               during the call only.
+ *   state       [n_seq][H][S][S] fp32, sequence stride state_seq_stride (in/out)
+ *   q, k        [total_tok][Hk][S], row stride qk_tok_stride               (in)
+ *   v           [total_tok][H][S],  row stride v_tok_stride                (in)
+ *   g, beta     [total_tok][H] dense                                       (in)
+ *   y           [total_tok][H][S],  row stride y_tok_stride                (out)
+ * 1 <= n_seq <= GDN_VARLEN_MAX_SEQ, total_tok >= 0 (0: nothing to do), chunk
+ * 64, S in {32, 64, 128}.  S = 128 needs a workspace of at least
+ * gdn_recurrence_chunked_varlen_workspace_bytes(...) bytes, 256-byte aligned,
+ * under the same rules as gdn_recurrence_chunked's.  Each sequence's results
+ * are bit-identical to a gdn_recurrence_chunked call on that sequence alone.
+ * A malformed cu_seqlens returns GDN_ERR_SHAPE before any launch.
+ */
+int gdn_recurrence_chunked_varlen(float *state, int64_t state_seq_stride, const float *q,
+                                  const float *k, int64_t qk_tok_stride, const float *v,
+                                  int64_t v_tok_stride, const float *g, const float *beta,
+                                  float *y, int64_t y_tok_stride, const int32_t *cu_seqlens,
+                                  int n_seq, int total_tok, int n_v_heads, int n_qk_heads, int S,
+                                  float scale, int chunk, void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
 /*
  * Gated RMSNorm per (row, head).  [FM] "Gated RMSNorm" section
  * (fm_ssm_gated_norm_at); [AT] gdn_verify_fused_norm_k2 for reading z out of

@@ -128,6 +128,47 @@ def test_chunked_validation_and_workspace_query():
     assert call(big, FAKE + 64 * MB, ws_need) == ERR_UNSUP
 
 
+def test_chunked_varlen_validation_and_workspace_query():
+    MB = 1 << 20
+    S, H, Hk = 128, 4, 2
+    lens = [100, 0, 64, 1]
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + n)
+    T = cu[-1]
+    ws_need = L.gdn_recurrence_chunked_varlen_workspace_bytes(len(lens), T, H, Hk, S, 64)
+    # the bound covers the padded chunk count of this split: 2 + 0 + 2 + 2 chunks
+    per_chunk = L.gdn_recurrence_chunked_workspace_bytes(1, 64, 1, 1, S, 64) // 2
+    assert ws_need >= 6 * H * per_chunk
+    # and of the worst split of T positions into 4 sequences
+    assert ws_need >= ((T + 63 * 4) // 64 + 4) * H * per_chunk
+    assert L.gdn_recurrence_chunked_varlen_workspace_bytes(0, T, H, Hk, S, 64) == 0
+    assert L.gdn_recurrence_chunked_varlen_workspace_bytes(257, T, H, Hk, S, 64) == 0
+    assert L.gdn_recurrence_chunked_varlen_workspace_bytes(4, T, H, Hk, 64, 64) == 0
+
+    def call(cu_list, n_seq=None, total=None, ws=FAKE + 64 * MB, nb=ws_need, state=FAKE,
+             sts=H * S * S, y=FAKE + 24 * MB, S_=S):
+        n = len(cu_list) - 1 if n_seq is None else n_seq
+        arr = (ctypes.c_int32 * max(len(cu_list), 1))(*cu_list) if cu_list is not None else None
+        return L.gdn_recurrence_chunked_varlen(
+            state, sts, FAKE + 4 * MB, FAKE + 8 * MB, Hk * S_, FAKE + 12 * MB, H * S_,
+            FAKE + 16 * MB, FAKE + 20 * MB, y, H * S_,
+            ctypes.cast(arr, ctypes.c_void_p) if arr is not None else None,
+            n, T if total is None else total, H, Hk, S_, 0.1, 64, ws, nb, None)
+    assert call(None, n_seq=4) == ERR_NULL
+    assert call([1, 100, 100, 164, 165]) == ERR_SHAPE                 # cu[0] != 0
+    assert call([0, 100, 99, 164, 165]) == ERR_SHAPE                  # decreasing
+    assert call(cu, total=T + 1) == ERR_SHAPE                         # cu[n] != total
+    assert call([0] * 258, n_seq=257, total=0) == ERR_SHAPE           # too many sequences
+    assert call(cu, ws=None) == ERR_WS
+    assert call(cu, nb=ws_need - 1) == ERR_WS
+    assert call(cu, sts=100) == ERR_SHAPE                             # state rows overlap
+    assert call(cu, state=FAKE + 12 * MB) == ERR_ALIAS                # a state over v
+    assert call(cu, state=FAKE + 64 * MB) == ERR_ALIAS                # a state over the workspace
+    assert call(cu, y=FAKE + 4 * MB + 64) == ERR_ALIAS                # y over q
+    assert call([0, 0, 0], total=0) == OK                             # nothing to do
+
+
 def test_norm_validation():
     MB = 1 << 20
     call = lambda y, ys, w, z, zs, o, os_, rows, H, hd: L.gdn_gated_rmsnorm(

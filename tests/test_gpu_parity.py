@@ -744,6 +744,65 @@ def test_chunked_small_state(S, T, H, Hk, n_seq, g_scale):
     assert ey < 2e-3 and es < 2e-3
 
 
+def pack_varlen(inp, lens, g3):
+    """First lens[s] positions of every sequence, packed along one token axis."""
+    take = lambda t: torch.cat([t[s, :n] for s, n in enumerate(lens)], 0)
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + n)
+    return {"q": take(inp["q"]), "k": take(inp["k"]), "v": take(inp["v"]), "g": take(g3),
+            "beta": take(inp["beta"]), "cu": cu}
+
+
+@pytest.mark.parametrize("S,lens,H,Hk,g_scale", [
+    (128, [100, 0, 64, 300, 1, 129], 4, 2, 1.0),                  # 8-wave scan grid
+    (128, [64, 200, 37, 130, 0, 65, 3, 90, 150], 6, 3, 0.3),       # paired scan grid
+    (128, [1000, 1500, 596, 1000], 32, 16, 1.0),                  # the 4096-token prompt, split
+    (32, [64, 17, 0, 100], 4, 2, 1.0),
+    (64, [37, 129, 5], 3, 1, 0.05)])
+def test_chunked_varlen(S, lens, H, Hk, g_scale):
+    # one packed call over sequences of different lengths from nonzero states:
+    # every sequence bit for bit as a call on it alone, and within the chunked
+    # tolerance of the sequential scan; empty sequences keep their state
+    base = "prefill" if S == 128 else "tiny"
+    inp = make_inputs(base, seed=83, S=S, head_dim=S, n_tok=max(lens), H=H, Hk=Hk,
+                      n_seq=len(lens), state_std=0.05)
+    wl = inp["wl"]
+    log_case("chunked_varlen", S=S, lens=lens, H=H, Hk=Hk)
+    g3 = (oracle_g(inp) * g_scale).float()
+    pk = pack_varlen(inp, lens, g3)
+    total = pk["cu"][-1]
+    # v and y as strided views of wider rows; y poisoned
+    vbuf = torch.full((total, H * S + 8), float("nan"), device=DEV)
+    vbuf[:, :H * S] = on_dev(pk["v"]).reshape(total, H * S)
+    v = vbuf[:, :H * S].unflatten(1, (H, S))
+    ybuf = torch.full((total, H * S + 8), float("nan"), device=DEV)
+    y = ybuf[:, :H * S].unflatten(1, (H, S))
+    st = on_dev(inp["state"]).clone()
+    gdn().gdn_recurrence_chunked_varlen(st, on_dev(pk["q"]), on_dev(pk["k"]), v, on_dev(pk["g"]),
+                                        on_dev(pk["beta"]), y, pk["cu"], scale=wl.scale, chunk=64)
+    assert torch.isnan(ybuf[:, H * S:]).all(), "write outside y's rows"
+    for s, n in enumerate(lens):
+        st1 = on_dev(inp["state"][s:s + 1]).clone()
+        if n == 0:
+            assert bits_equal(st[s:s + 1], st1)
+            continue
+        sl = slice(pk["cu"][s], pk["cu"][s + 1])
+        y1 = torch.full((1, n, H, S), float("nan"), device=DEV)
+        gdn().gdn_recurrence_chunked(st1, on_dev(pk["q"][sl])[None], on_dev(pk["k"][sl])[None],
+                                     v[sl][None], on_dev(pk["g"][sl])[None],
+                                     on_dev(pk["beta"][sl])[None], y1, scale=wl.scale, chunk=64)
+        assert bits_equal(y[sl], y1[0]), f"sequence {s}: y differs from its own call"
+        assert bits_equal(st[s:s + 1], st1), f"sequence {s}: state differs from its own call"
+        y_ref, s_ref, _ = oracle.recurrence_seq(
+            inp["state"][s:s + 1], pk["q"][sl][None], pk["k"][sl][None], pk["v"][sl][None],
+            pk["g"][sl][None], pk["beta"][sl][None], wl.scale)
+        ey, es = rel(y[sl][None], y_ref), rel(st[s:s + 1], s_ref)
+        print(f"[chunked varlen S={S}] seq {s} len {n} rel err y {ey:.3e} state {es:.3e}",
+              flush=True)
+        assert ey < 2e-3 and es < 2e-3
+
+
 def test_chunked_deterministic():
     inp = make_inputs("prefill", seed=71, n_tok=512)
     log_case("chunked_determinism")
