@@ -456,6 +456,51 @@ def main():
     except gdn.GdnError as e:
         prefill = {"error": str(e)}
 
+    # ------------------------------------------------- packed batch of prompts (varlen)
+    # eight prompts of different lengths in one chunked call, each from its own
+    # state: the recurrence's throughput at batch > 1
+    try:
+        lens = [4096, 3000, 2048, 1500, 1024, 700, 300, 100]
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(int).tolist()
+        total, n_p = cu[-1], len(lens)
+        vin = make_inputs(pw, seed=5, n_tok=total, n_seq=1)
+        vq = vin["q"][0].to(dev)
+        vk = vin["k"][0].to(dev)
+        vv = vin["v"][0].to(dev)
+        vbeta = vin["beta"][0].to(dev)
+        vg = torch.empty(total, PH, device=dev)
+        gdn.gdn_decay_gate(vin["alpha"].to(dev), vin["dt"].to(dev), vin["a"].to(dev), vg)
+        vst = torch.zeros(n_p, PH, PS, PS, device=dev)
+        vy = torch.empty(total, PH, PS, device=dev)
+        vws = torch.empty(max(gdn.gdn_recurrence_chunked_varlen_workspace_bytes(
+            n_p, total, PH, PHk, PS, 64), 1), dtype=torch.uint8, device=dev)
+
+        def varlen_call():
+            gdn.gdn_recurrence_chunked_varlen(vst, vq, vk, vv, vg, vbeta, vy, cu,
+                                              scale=pw.scale, workspace=vws)
+        for _ in range(2):
+            varlen_call()
+        torch.cuda.synchronize()
+        v0 = torch.cuda.Event(enable_timing=True)
+        v1 = torch.cuda.Event(enable_timing=True)
+        v0.record(stream)
+        for _ in range(args.prefill_iters):
+            varlen_call()
+        v1.record(stream)
+        v1.synchronize()
+        vms = v0.elapsed_time(v1) / args.prefill_iters
+        vfl = sum(chunked_flops(n, PH, PS) for n in lens)
+        prefill_varlen = {
+            "workload": f"{n_p} prompts of {lens} positions ({total} in all), 32 value / 16 q-k "
+                        "heads, 128x128 state each, one gdn_recurrence_chunked_varlen call",
+            "ms": vms, "recurrence_tokens_per_s": total / (vms * 1e-3),
+            "chunked_algorithmic_tflops": vfl / (vms * 1e-3) / 1e12,
+            "note": "the chunked recurrence only (gate, conv, norm are per-token kernels); "
+                    f"{args.prefill_iters} calls back to back between one event pair"}
+        del vq, vk, vv, vg, vbeta, vst, vy, vws
+    except gdn.GdnError as e:
+        prefill_varlen = {"error": str(e)}
+
     # ---------------------------------------------------------------- CPU baseline (oracle)
     cpu = None
     if not args.no_cpu_baseline:
@@ -526,6 +571,7 @@ def main():
             "step_frac_of_copy_peak": achieved / copy_gbs,
         },
         "prefill": prefill,
+        "prefill_varlen": prefill_varlen,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out, default=float))
