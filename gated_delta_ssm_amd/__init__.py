@@ -41,8 +41,8 @@ _SIGS = {
     "gdn_recurrence_chunked": (_I, [_P, _L, _P, _P, _L, _L, _P, _L, _L, _P, _P, _P, _L, _L,
                                     _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
     "gdn_recurrence_chunked_varlen_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
-    "gdn_recurrence_chunked_varlen": (_I, [_P, _L, _P, _P, _L, _P, _L, _P, _P, _P, _L, _P,
-                                           _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
+    "gdn_recurrence_chunked_varlen": (_I, [_P, _L, _P, _P, _L, _P, _L, _I, _P, _P, _P, _L,
+                                           _P, _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
     "gdn_gated_rmsnorm": (_I, [_P, _L, _P, _P, _L, _P, _L, _I, _I, _I, _F, _P]),
     "gdn_stream_copy": (_I, [_P, _P, _SZ, _P]),
     "gdn_decode_fused": (_I, [_P, _L, _P, _P, _L, _L, _P, _L, _L, _P, _P, _P, _P, _P, _P, _L,
@@ -238,8 +238,9 @@ def gdn_recurrence_chunked_varlen(state: torch.Tensor, q: torch.Tensor, k: torch
     """Chunked recurrence over a packed batch of sequences of different lengths.
     state [n_seq][H][S][S] (updated in place), q, k [total][Hk][S], v, y
     [total][H][S], g, beta [total][H]; cu_seqlens: n_seq + 1 row offsets on the
-    host (a list or a CPU integer tensor).  If no workspace is given one is
-    allocated here through torch."""
+    host (a list or a CPU integer tensor).  q, k, v are float32 or bfloat16
+    (all three the same); everything else is float32.  If no workspace is
+    given one is allocated here through torch."""
     cu = [int(c) for c in (cu_seqlens.tolist() if isinstance(cu_seqlens, torch.Tensor)
                            else cu_seqlens)]
     n_seq = len(cu) - 1
@@ -252,19 +253,30 @@ def gdn_recurrence_chunked_varlen(state: torch.Tensor, q: torch.Tensor, k: torch
     if tuple(g.shape) != (total, H) or beta.shape != g.shape:
         raise ValueError("g / beta shape mismatch")
     _dev_f32("state", state, 3)
-    for n, t in (("q", q), ("k", k), ("v", v), ("y", y)):
-        _dev_f32(n, t, 2)
+    _dev_f32("y", y, 2)
+    in_dtype = q.dtype
+    if in_dtype not in (torch.float32, torch.bfloat16) or k.dtype != in_dtype or \
+            v.dtype != in_dtype:
+        raise TypeError(f"q, k, v must all be float32 or all bfloat16, got "
+                        f"{q.dtype}, {k.dtype}, {v.dtype}")
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{n} must be on the GPU")
+        if (t.shape[2] > 1 and t.stride(2) != 1) or (t.shape[1] > 1 and t.stride(1) != t.shape[2]):
+            raise ValueError(f"{n}: innermost 2 dims must be dense, got strides {t.stride()}")
     if q.stride() != k.stride():
         raise ValueError("q and k must share strides")
     _dev_f32("g", g, 2)
     _dev_f32("beta", beta, 2)
+    dt_code = 1 if in_dtype == torch.bfloat16 else 0
     cu_arr = (ctypes.c_int32 * (n_seq + 1))(*cu)
     need = gdn_recurrence_chunked_varlen_workspace_bytes(n_seq, total, H, Hk, S, chunk)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=state.device)
     _check("gdn_recurrence_chunked_varlen", _lib.gdn_recurrence_chunked_varlen(
         _ptr(state), state.stride(0), _ptr(q), _ptr(k), q.stride(0), _ptr(v), v.stride(0),
-        _ptr(g), _ptr(beta), _ptr(y), y.stride(0), ctypes.cast(cu_arr, _P), n_seq, total, H,
+        dt_code, _ptr(g), _ptr(beta), _ptr(y), y.stride(0), ctypes.cast(cu_arr, _P), n_seq,
+        total, H,
         Hk, S, scale, chunk, _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream, y)))
     return y

@@ -105,18 +105,20 @@ size_t gdn_recurrence_chunked_varlen_workspace_bytes(int n_seq, int total_tok, i
   return gdn::chunked_varlen_workspace_bytes(n_seq, total_tok, n_v_heads, S);
 }
 
-int gdn_recurrence_chunked_varlen(float *state, int64_t state_seq_stride, const float *q,
-                                  const float *k, int64_t qk_tok_stride, const float *v,
-                                  int64_t v_tok_stride, const float *g, const float *beta,
-                                  float *y, int64_t y_tok_stride, const int32_t *cu_seqlens,
+int gdn_recurrence_chunked_varlen(float *state, int64_t state_seq_stride, const void *q,
+                                  const void *k, int64_t qk_tok_stride, const void *v,
+                                  int64_t v_tok_stride, int qkv_dtype, const float *g,
+                                  const float *beta, float *y, int64_t y_tok_stride,
+                                  const int32_t *cu_seqlens,
                                   int n_seq, int total_tok, int n_v_heads, int n_qk_heads, int S,
                                   float scale, int chunk, void *workspace, size_t workspace_bytes,
                                   hipStream_t stream) {
   const size_t need = gdn_recurrence_chunked_varlen_workspace_bytes(n_seq, total_tok, n_v_heads,
                                                                     n_qk_heads, S, chunk);
   const int rc = gdn::check_chunked_varlen(state, state_seq_stride, q, k, qk_tok_stride, v,
-                                           v_tok_stride, g, beta, y, y_tok_stride, cu_seqlens,
-                                           n_seq, total_tok, n_v_heads, n_qk_heads, S, chunk,
+                                           v_tok_stride, qkv_dtype, g, beta, y, y_tok_stride,
+                                           cu_seqlens, n_seq, total_tok, n_v_heads, n_qk_heads,
+                                           S, chunk,
                                            workspace, workspace_bytes, need);
   if (rc != GDN_OK || total_tok == 0) return rc;
   gdn::VarTab tab;
@@ -127,12 +129,15 @@ int gdn_recurrence_chunked_varlen(float *state, int64_t state_seq_stride, const 
     tab.tok0[s + 1] = cu_seqlens[s + 1];
     tab.ch0[s + 1] = tab.ch0[s] + gdn::padded_chunks(cu_seqlens[s + 1] - cu_seqlens[s]);
   }
-  gdn::RecurArgs a{state,   state_seq_stride, q,            k,          qk_tok_stride,
-                   0,       v,                v_tok_stride, 0,          g,
+  // q, k, v travel as untyped pointers; the launcher reinterprets them per dtype
+  gdn::RecurArgs a{state,   state_seq_stride, static_cast<const float *>(q),
+                   static_cast<const float *>(k), qk_tok_stride,
+                   0,       static_cast<const float *>(v), v_tok_stride, 0, g,
                    beta,    y,                y_tok_stride, 0,          nullptr,
                    0,       n_seq,            total_tok,    n_v_heads,  n_qk_heads,
                    S,       scale};
-  return gdn::launch_recur_chunked_varlen(a, tab, chunk, workspace, workspace_bytes, stream);
+  return gdn::launch_recur_chunked_varlen(a, tab, qkv_dtype == GDN_DTYPE_BF16, chunk, workspace,
+                                          workspace_bytes, stream);
 }
 
 int gdn_gated_rmsnorm(const float *y, int64_t y_row_stride, const float *w, const float *z,

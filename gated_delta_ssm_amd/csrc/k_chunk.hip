@@ -424,12 +424,40 @@ __device__ __forceinline__ PrepItem prep_item(int u, int n_chunks, int H, int Hk
 // The loads of one item, in the order they are first needed.  Rows past n
 // read a valid row and are zeroed where they are used: a load behind a branch
 // would make the compiler wait for every load in flight at the join.
+// q, k, v elements are fp32 or bf16 (TIN = u16, the bit pattern); either way
+// they are widened to fp32 on load, exactly, so a bf16 call equals an fp32
+// call on the same values bit for bit.
+template <class TIN>
 struct PrepIn {
-  const float *q, *k, *v, *g, *beta;
+  const TIN *q, *k, *v;
+  const float *g, *beta;
   int64_t qk_tok, qk_seq, v_tok, v_seq;
   int n_tok, H;
 };
-__device__ __forceinline__ void load_gb(const PrepIn &in, const PrepItem &it, int lane, float &gv,
+__device__ __forceinline__ float bf16_to_f32(unsigned b) { return __builtin_bit_cast(float, b << 16); }
+// 8 consecutive elements as two float4 (16- or 32-byte aligned loads)
+__device__ __forceinline__ void load8f(const float *p, float4 &a, float4 &b) {
+  a = *reinterpret_cast<const float4 *>(p);
+  b = *reinterpret_cast<const float4 *>(p + 4);
+}
+__device__ __forceinline__ void load8f(const u16 *p, float4 &a, float4 &b) {
+  const uint4 u = *reinterpret_cast<const uint4 *>(p);
+  a = make_float4(bf16_to_f32(u.x & 0xffffu), bf16_to_f32(u.x >> 16), bf16_to_f32(u.y & 0xffffu),
+                  bf16_to_f32(u.y >> 16));
+  b = make_float4(bf16_to_f32(u.z & 0xffffu), bf16_to_f32(u.z >> 16), bf16_to_f32(u.w & 0xffffu),
+                  bf16_to_f32(u.w >> 16));
+}
+// 4 consecutive elements as a float4
+__device__ __forceinline__ float4 load4f(const float *p) {
+  return *reinterpret_cast<const float4 *>(p);
+}
+__device__ __forceinline__ float4 load4f(const u16 *p) {
+  const uint2 u = *reinterpret_cast<const uint2 *>(p);
+  return make_float4(bf16_to_f32(u.x & 0xffffu), bf16_to_f32(u.x >> 16),
+                     bf16_to_f32(u.y & 0xffffu), bf16_to_f32(u.y >> 16));
+}
+template <class TIN>
+__device__ __forceinline__ void load_gb(const PrepIn<TIN> &in, const PrepItem &it, int lane, float &gv,
                                         float &bv) {
   const int64_t gi = (it.grow + min(lane, it.nl)) * in.H + it.h;
   gv = in.g[gi];
@@ -443,7 +471,8 @@ __device__ __forceinline__ void row8_of(int i, int tid, int &row, int &col) {
   row = idx >> 4;
   col = (idx & 15) * 8;
 }
-__device__ __forceinline__ void load_kq(const PrepIn &in, const PrepItem &it, int tid,
+template <class TIN>
+__device__ __forceinline__ void load_kq(const PrepIn<TIN> &in, const PrepItem &it, int tid,
                                         float4 (&kr)[4], float4 (&qr)[4]) {
   const int64_t base = it.s * in.qk_seq + (int64_t)it.tb * in.qk_tok + it.hk * DK;
 #pragma unroll
@@ -451,22 +480,19 @@ __device__ __forceinline__ void load_kq(const PrepIn &in, const PrepItem &it, in
     int row, col;
     row8_of(i, tid, row, col);
     const int64_t o = base + (int64_t)min(row, it.nl) * in.qk_tok + col;
-    kr[2 * i] = *reinterpret_cast<const float4 *>(in.k + o);
-    kr[2 * i + 1] = *reinterpret_cast<const float4 *>(in.k + o + 4);
-    qr[2 * i] = *reinterpret_cast<const float4 *>(in.q + o);
-    qr[2 * i + 1] = *reinterpret_cast<const float4 *>(in.q + o + 4);
+    load8f(in.k + o, kr[2 * i], kr[2 * i + 1]);
+    load8f(in.q + o, qr[2 * i], qr[2 * i + 1]);
   }
 }
-__device__ __forceinline__ void load_v(const PrepIn &in, const PrepItem &it, int tid,
+template <class TIN>
+__device__ __forceinline__ void load_v(const PrepIn<TIN> &in, const PrepItem &it, int tid,
                                        float4 (&vr)[4]) {
   const int64_t base = it.s * in.v_seq + (int64_t)it.tb * in.v_tok + it.h * DV;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     int row, col;
     row8_of(i, tid, row, col);
-    const float *p = in.v + base + (int64_t)min(row, it.nl) * in.v_tok + col;
-    vr[2 * i] = *reinterpret_cast<const float4 *>(p);
-    vr[2 * i + 1] = *reinterpret_cast<const float4 *>(p + 4);
+    load8f(in.v + base + (int64_t)min(row, it.nl) * in.v_tok + col, vr[2 * i], vr[2 * i + 1]);
   }
 }
 // rows past n are written as zeros
@@ -482,14 +508,14 @@ __device__ __forceinline__ void store_row8(u16 *hi, u16 *lo, const float4 &a, co
 // beta, K, Q and V are loaded into registers as soon as the current item has
 // consumed them, so a workgroup's loads and stores overlap its own compute
 // instead of every CU loading, then computing, then storing in lockstep.
-template <class TAB>
+template <class TAB, class TIN>
 __global__ __launch_bounds__(512) void k_chunk_prep(
-    const float *__restrict__ q, const float *__restrict__ k, int64_t qk_tok, int64_t qk_seq,
-    const float *__restrict__ v, int64_t v_tok, int64_t v_seq, const float *__restrict__ g,
+    const TIN *__restrict__ q, const TIN *__restrict__ k, int64_t qk_tok, int64_t qk_seq,
+    const TIN *__restrict__ v, int64_t v_tok, int64_t v_seq, const float *__restrict__ g,
     const float *__restrict__ beta, unsigned char *__restrict__ ws, int n_tok, int n_chunks,
     int H, int Hk, int n_items, const TAB tab) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[L_TOTAL];
-  const PrepIn in{q, k, v, g, beta, qk_tok, qk_seq, v_tok, v_seq, n_tok, H};
+  const PrepIn<TIN> in{q, k, v, g, beta, qk_tok, qk_seq, v_tok, v_seq, n_tok, H};
 
   u16 *kh = reinterpret_cast<u16 *>(smem + L_K), *klo = kh + CH * PR;
   u16 *qh = reinterpret_cast<u16 *>(smem + L_Q), *qlo = qh + CH * PR;
@@ -522,7 +548,7 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
   const PrepItem nx = prep_item(u + gridDim.x < n_items ? u + gridDim.x : u, n_chunks, H, Hk,
                                 n_tok, tab);
   const int n = it.n, nl = it.nl;
-  const float *qc = q + it.s * qk_seq + (int64_t)it.tb * qk_tok + it.hk * DK;
+  const TIN *qc = q + it.s * qk_seq + (int64_t)it.tb * qk_tok + it.hk * DK;
   unsigned char *wc = ws + it.slot * WS_CHUNK;
 
   // S0. gate cumsum (wave 0) and cleared tiles
@@ -661,8 +687,7 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const int t = 16 * (2 * tp + m) + l16;
-      qa[d][m] = *reinterpret_cast<const float4 *>(qc + (int64_t)min(t, nl) * qk_tok +
-                                                   16 * (2 * kp + d) + 4 * kg);
+      qa[d][m] = load4f(qc + (int64_t)min(t, nl) * qk_tok + 16 * (2 * kp + d) + 4 * kg);
     }
   f32x4 accW[2][2], accU[2][2];
 #pragma unroll
@@ -1060,16 +1085,17 @@ static int device_cu_count() {
 
 // Phase A then phase B of one call; n_chunks is the per-sequence chunk count
 // (fixed-length batch) or the packed total (variable-length batch).
-template <class TAB>
-static int launch_two_phase(const RecurArgs &a, const TAB &tab, int n_chunks, int n_items,
-                            unsigned char *wsb, hipStream_t stream) {
+template <class TAB, class TIN>
+static int launch_two_phase(const RecurArgs &a, const TAB &tab, const TIN *q, const TIN *k,
+                            const TIN *v, int n_chunks, int n_items, unsigned char *wsb,
+                            hipStream_t stream) {
   // phase A: one persistent workgroup per CU (its LDS allows no more), or one
   // per item when there are fewer items than CUs
   const int cus = device_cu_count();
   if (cus <= 0) return GDN_ERR_LAUNCH;
   const int grid_a = n_items < cus ? n_items : cus;
-  int rc = launch_kernel(k_chunk_prep<TAB>, dim3(grid_a), dim3(512), 0, stream, a.q, a.k,
-                         a.qk_tok, a.qk_seq, a.v, a.v_tok, a.v_seq, a.g, a.beta, wsb, a.n_tok,
+  int rc = launch_kernel(k_chunk_prep<TAB, TIN>, dim3(grid_a), dim3(512), 0, stream, q, k,
+                         a.qk_tok, a.qk_seq, v, a.v_tok, a.v_seq, a.g, a.beta, wsb, a.n_tok,
                          n_chunks, a.H, a.Hk, n_items, tab);
   if (rc != GDN_OK) return rc;
   // phase B: 8-wave workgroups while they fit in one pass of the chip (one per
@@ -1092,19 +1118,23 @@ int launch_recur_chunked(const RecurArgs &a, int chunk, void *ws, size_t ws_byte
   const int n_chunks = padded_chunks(a.n_tok);
   if (ws_bytes < chunked_workspace_bytes(a.n_seq, a.n_tok, a.H, a.Hk, a.S, chunk))
     return GDN_ERR_WORKSPACE;
-  return launch_two_phase(a, NoTab{}, n_chunks, n_chunks * a.H * a.n_seq,
+  return launch_two_phase(a, NoTab{}, a.q, a.k, a.v, n_chunks, n_chunks * a.H * a.n_seq,
                           static_cast<unsigned char *>(ws), stream);
 }
 
-int launch_recur_chunked_varlen(const RecurArgs &a, const VarTab &tab, int chunk, void *ws,
-                                size_t ws_bytes, hipStream_t stream) {
+int launch_recur_chunked_varlen(const RecurArgs &a, const VarTab &tab, bool bf16_in, int chunk,
+                                void *ws, size_t ws_bytes, hipStream_t stream) {
   if (chunk != CH) return GDN_ERR_UNSUPPORTED;
-  if (a.S != DK) return launch_chunk_small_varlen(a, tab, stream);
+  if (a.S != DK) return launch_chunk_small_varlen(a, tab, bf16_in, stream);
   const int n_chunks = tab.ch0[tab.n_seq];   // packed total, even per sequence
   if (n_chunks == 0) return GDN_OK;           // every sequence is empty
   if (ws_bytes < (size_t)n_chunks * a.H * WS_CHUNK) return GDN_ERR_WORKSPACE;
-  return launch_two_phase(a, tab, n_chunks, n_chunks * a.H, static_cast<unsigned char *>(ws),
-                          stream);
+  unsigned char *wsb = static_cast<unsigned char *>(ws);
+  if (bf16_in)
+    return launch_two_phase(a, tab, reinterpret_cast<const u16 *>(a.q),
+                            reinterpret_cast<const u16 *>(a.k), reinterpret_cast<const u16 *>(a.v),
+                            n_chunks, n_chunks * a.H, wsb, stream);
+  return launch_two_phase(a, tab, a.q, a.k, a.v, n_chunks, n_chunks * a.H, wsb, stream);
 }
 
 }  // namespace gdn

@@ -42,10 +42,16 @@ __device__ __forceinline__ SeqRows seq_rows(const VarTab &tab, int s, int) {
   return SeqRows{tab.tok0[s], tab.tok0[s], tab.tok0[s + 1] - tab.tok0[s]};
 }
 
-template <int S, class TAB>
+// q, k, v elements: fp32, or bf16 bit patterns widened exactly to fp32
+__device__ __forceinline__ float in_f32(float x) { return x; }
+__device__ __forceinline__ float in_f32(unsigned short b) {
+  return __builtin_bit_cast(float, (unsigned)b << 16);
+}
+
+template <int S, class TAB, class TIN>
 __global__ __launch_bounds__(256) void k_chunk_small(
-    float *__restrict__ state, int64_t st_seq, const float *__restrict__ q,
-    const float *__restrict__ k, int64_t qk_tok, int64_t qk_seq, const float *__restrict__ v,
+    float *__restrict__ state, int64_t st_seq, const TIN *__restrict__ q,
+    const TIN *__restrict__ k, int64_t qk_tok, int64_t qk_seq, const TIN *__restrict__ v,
     int64_t v_tok, int64_t v_seq, const float *__restrict__ g, const float *__restrict__ beta,
     float *__restrict__ y, int64_t y_tok, int64_t y_seq, int n_tok_arg, int H, int Hk,
     float scale, const TAB tab) {
@@ -75,9 +81,9 @@ __global__ __launch_bounds__(256) void k_chunk_small(
       const int t = e / S, i = e - t * S;
       const bool ok = t < n;
       const int64_t tt = sr.row0 + (ok ? t0 + t : t0);
-      const float kv = k[s * qk_seq + tt * qk_tok + (int64_t)hk * S + i];
-      const float qv = q[s * qk_seq + tt * qk_tok + (int64_t)hk * S + i];
-      const float vv = v[s * v_seq + tt * v_tok + (int64_t)h * S + i];
+      const float kv = in_f32(k[s * qk_seq + tt * qk_tok + (int64_t)hk * S + i]);
+      const float qv = in_f32(q[s * qk_seq + tt * qk_tok + (int64_t)hk * S + i]);
+      const float vv = in_f32(v[s * v_seq + tt * v_tok + (int64_t)h * S + i]);
       sK[t * P + i] = ok ? kv : 0.0f;
       sQ[t * P + i] = ok ? qv : 0.0f;
       sV[t * P + i] = ok ? vv : 0.0f;
@@ -183,19 +189,21 @@ __global__ __launch_bounds__(256) void k_chunk_small(
   for (int e = tid; e < S * S; e += 256) st[e] = sS[(e % S) * P + e / S];
 }
 
-template <int S, class TAB>
-int run_small(const RecurArgs &a, const TAB &tab, hipStream_t stream) {
-  return launch_kernel(k_chunk_small<S, TAB>, dim3((unsigned)a.H, (unsigned)a.n_seq), dim3(256),
-                       0, stream, a.state, a.st_seq, a.q, a.k, a.qk_tok, a.qk_seq, a.v, a.v_tok,
-                       a.v_seq, a.g, a.beta, a.y, a.y_tok, a.y_seq, a.n_tok, a.H, a.Hk, a.scale,
-                       tab);
+template <int S, class TAB, class TIN>
+int run_small(const RecurArgs &a, const TAB &tab, const TIN *q, const TIN *k, const TIN *v,
+              hipStream_t stream) {
+  return launch_kernel(k_chunk_small<S, TAB, TIN>, dim3((unsigned)a.H, (unsigned)a.n_seq),
+                       dim3(256), 0, stream, a.state, a.st_seq, q, k, a.qk_tok, a.qk_seq, v,
+                       a.v_tok, a.v_seq, a.g, a.beta, a.y, a.y_tok, a.y_seq, a.n_tok, a.H, a.Hk,
+                       a.scale, tab);
 }
 
-template <class TAB>
-int run_small_s(const RecurArgs &a, const TAB &tab, hipStream_t stream) {
+template <class TAB, class TIN>
+int run_small_s(const RecurArgs &a, const TAB &tab, const TIN *q, const TIN *k, const TIN *v,
+                hipStream_t stream) {
   switch (a.S) {
-    case 32: return run_small<32>(a, tab, stream);
-    case 64: return run_small<64>(a, tab, stream);
+    case 32: return run_small<32>(a, tab, q, k, v, stream);
+    case 64: return run_small<64>(a, tab, q, k, v, stream);
     default: return GDN_ERR_UNSUPPORTED;
   }
 }
@@ -203,11 +211,18 @@ int run_small_s(const RecurArgs &a, const TAB &tab, hipStream_t stream) {
 }  // namespace
 
 int launch_chunk_small(const RecurArgs &a, hipStream_t stream) {
-  return run_small_s(a, NoTab{}, stream);
+  return run_small_s(a, NoTab{}, a.q, a.k, a.v, stream);
 }
 
-int launch_chunk_small_varlen(const RecurArgs &a, const VarTab &tab, hipStream_t stream) {
-  return run_small_s(a, tab, stream);
+int launch_chunk_small_varlen(const RecurArgs &a, const VarTab &tab, bool bf16_in,
+                              hipStream_t stream) {
+  if (bf16_in) {
+    typedef unsigned short b16;
+    return run_small_s(a, tab, reinterpret_cast<const b16 *>(a.q),
+                       reinterpret_cast<const b16 *>(a.k), reinterpret_cast<const b16 *>(a.v),
+                       stream);
+  }
+  return run_small_s(a, tab, a.q, a.k, a.v, stream);
 }
 
 }  // namespace gdn

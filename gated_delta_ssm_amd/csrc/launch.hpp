@@ -85,12 +85,14 @@ struct VarTab {
 inline int padded_chunks(int n_tok) { return ((n_tok + 63) / 64 + 1) & ~1; }
 // Workspace bound of a packed batch of n_seq sequences and total_tok positions.
 size_t chunked_varlen_workspace_bytes(int n_seq, int total_tok, int H, int S);
-// a.n_tok is the packed total; a.qk_seq, a.v_seq, a.y_seq are unused.
-int launch_recur_chunked_varlen(const RecurArgs &a, const VarTab &tab, int chunk, void *ws,
-                                size_t ws_bytes, hipStream_t stream);
+// a.n_tok is the packed total; a.qk_seq, a.v_seq, a.y_seq are unused.  With
+// bf16_in, a.q, a.k, a.v point at bf16 elements (strides still in elements).
+int launch_recur_chunked_varlen(const RecurArgs &a, const VarTab &tab, bool bf16_in, int chunk,
+                                void *ws, size_t ws_bytes, hipStream_t stream);
 // The chunked form for S = 32 and 64 (fp32, one pass, no workspace).
 int launch_chunk_small(const RecurArgs &a, hipStream_t stream);
-int launch_chunk_small_varlen(const RecurArgs &a, const VarTab &tab, hipStream_t stream);
+int launch_chunk_small_varlen(const RecurArgs &a, const VarTab &tab, bool bf16_in,
+                              hipStream_t stream);
 
 struct NormArgs {
   const float *y;

@@ -20,14 +20,15 @@ struct Span {
   bool empty() const { return hi <= lo; }
 };
 
-// Bytes touched by a [n_outer][n_inner][len] view with element strides.
+// Bytes touched by a [n_outer][n_inner][len] view with element strides
+// (elements of esz bytes; fp32 unless stated).
 Span span_of(const void *p, int64_t n_outer, int64_t s_outer, int64_t n_inner, int64_t s_inner,
-             int64_t len) {
+             int64_t len, int64_t esz = sizeof(float)) {
   Span r;
   if (!p || n_outer <= 0 || n_inner <= 0 || len <= 0) return r;
   const int64_t last = (n_outer - 1) * s_outer + (n_inner - 1) * s_inner + len;
   r.lo = (uintptr_t)p;
-  r.hi = r.lo + (uintptr_t)last * sizeof(float);
+  r.hi = r.lo + (uintptr_t)(last * esz);
   return r;
 }
 
@@ -155,40 +156,55 @@ int check_chunked(const float *state, int64_t st_seq, const float *q, const floa
   return GDN_OK;
 }
 
-int check_chunked_varlen(const float *state, int64_t st_seq, const float *q, const float *k,
-                         int64_t qk_tok, const float *v, int64_t v_tok, const float *g,
+int check_chunked_varlen(const float *state, int64_t st_seq, const void *q, const void *k,
+                         int64_t qk_tok, const void *v, int64_t v_tok, int dtype, const float *g,
                          const float *beta, const float *y, int64_t y_tok, const int32_t *cu,
                          int n_seq, int total_tok, int H, int Hk, int S, int chunk,
                          const void *ws, size_t ws_bytes, size_t ws_needed) {
   if (n_seq < 1 || n_seq > GDN_VARLEN_MAX_SEQ || total_tok < 0) return GDN_ERR_SHAPE;
+  if (H < 1 || Hk < 1 || H % Hk != 0) return GDN_ERR_SHAPE;
+  if (S < 32 || S % 32 != 0 || S > 256) return GDN_ERR_SHAPE;
+  if (chunk != 64 || (S != 32 && S != 64 && S != 128)) return GDN_ERR_UNSUPPORTED;
+  if (dtype != GDN_DTYPE_F32 && dtype != GDN_DTYPE_BF16) return GDN_ERR_UNSUPPORTED;
   if (!cu) return GDN_ERR_NULL;
   if (cu[0] != 0 || cu[n_seq] != total_tok) return GDN_ERR_SHAPE;
   for (int s = 0; s < n_seq; ++s)
     if (cu[s + 1] < cu[s]) return GDN_ERR_SHAPE;
-  if (total_tok == 0) {   // nothing to compute; the shape rules still apply
-    if (H < 1 || Hk < 1 || H % Hk != 0) return GDN_ERR_SHAPE;
-    if (chunk != 64 || (S != 32 && S != 64 && S != 128)) return GDN_ERR_UNSUPPORTED;
-    return state ? GDN_OK : GDN_ERR_NULL;
-  }
-  // the token tensors as one sequence of total_tok rows; the state checked
-  // below over all n_seq sequences
-  int rc = check_chunked(state, 0, q, k, qk_tok, 0, v, v_tok, 0, g, beta, y, y_tok, 0, 1,
-                         total_tok, H, Hk, S, chunk, ws, ws_bytes, ws_needed);
-  if (rc != GDN_OK) return rc;
-  if (st_seq < 0) return GDN_ERR_SHAPE;
+  if (!state) return GDN_ERR_NULL;
+  if (total_tok == 0) return GDN_OK;   // nothing to compute
+  if (!q || !k || !v || !g || !beta || !y) return GDN_ERR_NULL;
+  if (st_seq < 0 || qk_tok < 0 || v_tok < 0 || y_tok < 0) return GDN_ERR_SHAPE;
+  const int64_t esz = dtype == GDN_DTYPE_BF16 ? 2 : 4;
   const int64_t st_len = (int64_t)S * S * H;
   if (!rows_disjoint(n_seq, st_seq, 1, 0, st_len)) return GDN_ERR_SHAPE;
-  if (st_seq % (S >= 64 ? 4 : 2)) return GDN_ERR_SHAPE;
+  if (!rows_disjoint(1, 0, total_tok, y_tok, (int64_t)H * S)) return GDN_ERR_SHAPE;
+  // vector accesses: the state and y as float4 (float2 at S = 32); at S = 128
+  // q, k, v rows are read 16 bytes at a time
+  const uintptr_t va = S >= 64 ? 16 : 8;
+  const int64_t ve = S >= 64 ? 4 : 2;
+  if (!aligned(state, va) || st_seq % ve) return GDN_ERR_SHAPE;
+  if (S == 128) {
+    const int64_t in_vec = 16 / esz;   // elements per 16-byte load
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || qk_tok % in_vec ||
+        v_tok % in_vec)
+      return GDN_ERR_SHAPE;
+    if (!aligned(y, 16) || y_tok % 4) return GDN_ERR_SHAPE;
+    if (!ws || ws_bytes < ws_needed || !aligned(ws, 256)) return GDN_ERR_WORKSPACE;
+  } else {
+    if (!aligned(q, esz) || !aligned(k, esz) || !aligned(v, esz)) return GDN_ERR_SHAPE;
+    if (dtype == GDN_DTYPE_F32 && (!aligned(q, va) || !aligned(k, va) || qk_tok % ve))
+      return GDN_ERR_SHAPE;   // the fp32 rules of the fixed-length entry point
+  }
   const Span sst = span_of(state, n_seq, st_seq, 1, 0, st_len);
-  for (Span t : {span_of(q, 1, 0, total_tok, qk_tok, (int64_t)Hk * S),
-                 span_of(k, 1, 0, total_tok, qk_tok, (int64_t)Hk * S),
-                 span_of(v, 1, 0, total_tok, v_tok, (int64_t)H * S),
-                 span_of(y, 1, 0, total_tok, y_tok, (int64_t)H * S),
-                 span_of(g, 1, 0, 1, 0, (int64_t)total_tok * H),
-                 span_of(beta, 1, 0, 1, 0, (int64_t)total_tok * H)})
-    if (overlap(sst, t)) return GDN_ERR_ALIAS;
-  if (S == 128 && ws && overlap(sst, Span{(uintptr_t)ws, (uintptr_t)ws + ws_bytes}))
-    return GDN_ERR_ALIAS;
+  const Span sy = span_of(y, 1, 0, total_tok, y_tok, (int64_t)H * S);
+  const Span sw = S == 128 ? Span{(uintptr_t)ws, (uintptr_t)ws + ws_bytes} : Span{};
+  for (Span in : {span_of(q, 1, 0, total_tok, qk_tok, (int64_t)Hk * S, esz),
+                  span_of(k, 1, 0, total_tok, qk_tok, (int64_t)Hk * S, esz),
+                  span_of(v, 1, 0, total_tok, v_tok, (int64_t)H * S, esz),
+                  span_of(g, 1, 0, 1, 0, (int64_t)total_tok * H),
+                  span_of(beta, 1, 0, 1, 0, (int64_t)total_tok * H)})
+    if (overlap(sst, in) || overlap(sy, in) || overlap(sw, in)) return GDN_ERR_ALIAS;
+  if (overlap(sy, sst) || overlap(sw, sst) || overlap(sw, sy)) return GDN_ERR_ALIAS;
   return GDN_OK;
 }
 

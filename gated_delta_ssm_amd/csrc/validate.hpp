@@ -25,9 +25,10 @@ int check_chunked(const float *state, int64_t st_seq, const float *q, const floa
                   const void *ws, size_t ws_bytes, size_t ws_needed);
 
 // A packed batch: cu host array of n_seq + 1 offsets; token tensors are one
-// [total_tok] run of rows, the state n_seq rows of st_seq.
-int check_chunked_varlen(const float *state, int64_t st_seq, const float *q, const float *k,
-                         int64_t qk_tok, const float *v, int64_t v_tok, const float *g,
+// [total_tok] run of rows (q, k, v of the given gdn_dtype), the state n_seq
+// rows of st_seq.
+int check_chunked_varlen(const float *state, int64_t st_seq, const void *q, const void *k,
+                         int64_t qk_tok, const void *v, int64_t v_tok, int dtype, const float *g,
                          const float *beta, const float *y, int64_t y_tok, const int32_t *cu,
                          int n_seq, int total_tok, int H, int Hk, int S, int chunk,
                          const void *ws, size_t ws_bytes, size_t ws_needed);

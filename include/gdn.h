@@ -184,6 +184,12 @@ int gdn_recurrence_chunked(float *state, int64_t state_seq_stride, const float *
 /* Most sequences one gdn_recurrence_chunked_varlen call takes. */
 #define GDN_VARLEN_MAX_SEQ 256
 
+/* Element type of the q, k, v inputs of gdn_recurrence_chunked_varlen. */
+typedef enum {
+  GDN_DTYPE_F32 = 0,  /* IEEE binary32 */
+  GDN_DTYPE_BF16 = 1  /* bfloat16: the upper 16 bits of a binary32 */
+} gdn_dtype;
+
 /*
  * Workspace bytes gdn_recurrence_chunked_varlen needs for any split of
  * total_tok positions into n_seq sequences (a bound; 0 if the sizes are
@@ -208,6 +214,12 @@ size_t gdn_recurrence_chunked_varlen_workspace_bytes(int n_seq, int total_tok, i
  *   state       [n_seq][H][S][S] fp32, sequence stride state_seq_stride (in/out)
  *   q, k        [total_tok][Hk][S], row stride qk_tok_stride               (in)
  *   v           [total_tok][H][S],  row stride v_tok_stride                (in)
+ *   qkv_dtype   element type of q, k and v (gdn_dtype; strides count
+ *               elements of that type).  bf16 values are widened to fp32
+ *               exactly on load, so a bf16 call equals, bit for bit, an fp32
+ *               call on the same values; everything else stays fp32.  At
+ *               S = 128, q, k, v are 16-byte aligned and their row strides a
+ *               multiple of 16 bytes.
  *   g, beta     [total_tok][H] dense                                       (in)
  *   y           [total_tok][H][S],  row stride y_tok_stride                (out)
  * 1 <= n_seq <= GDN_VARLEN_MAX_SEQ, total_tok >= 0 (0: nothing to do), chunk
@@ -217,10 +229,11 @@ size_t gdn_recurrence_chunked_varlen_workspace_bytes(int n_seq, int total_tok, i
  * are bit-identical to a gdn_recurrence_chunked call on that sequence alone.
  * A malformed cu_seqlens returns GDN_ERR_SHAPE before any launch.
  */
-int gdn_recurrence_chunked_varlen(float *state, int64_t state_seq_stride, const float *q,
-                                  const float *k, int64_t qk_tok_stride, const float *v,
-                                  int64_t v_tok_stride, const float *g, const float *beta,
-                                  float *y, int64_t y_tok_stride, const int32_t *cu_seqlens,
+int gdn_recurrence_chunked_varlen(float *state, int64_t state_seq_stride, const void *q,
+                                  const void *k, int64_t qk_tok_stride, const void *v,
+                                  int64_t v_tok_stride, int qkv_dtype, const float *g,
+                                  const float *beta, float *y, int64_t y_tok_stride,
+                                  const int32_t *cu_seqlens,
                                   int n_seq, int total_tok, int n_v_heads, int n_qk_heads, int S,
                                   float scale, int chunk, void *workspace, size_t workspace_bytes,
                                   hipStream_t stream);

@@ -147,11 +147,12 @@ def test_chunked_varlen_validation_and_workspace_query():
     assert L.gdn_recurrence_chunked_varlen_workspace_bytes(4, T, H, Hk, 64, 64) == 0
 
     def call(cu_list, n_seq=None, total=None, ws=FAKE + 64 * MB, nb=ws_need, state=FAKE,
-             sts=H * S * S, y=FAKE + 24 * MB, S_=S):
+             sts=H * S * S, y=FAKE + 24 * MB, S_=S, dtype=0, qkt=None, q=FAKE + 4 * MB):
         n = len(cu_list) - 1 if n_seq is None else n_seq
         arr = (ctypes.c_int32 * max(len(cu_list), 1))(*cu_list) if cu_list is not None else None
         return L.gdn_recurrence_chunked_varlen(
-            state, sts, FAKE + 4 * MB, FAKE + 8 * MB, Hk * S_, FAKE + 12 * MB, H * S_,
+            state, sts, q, FAKE + 8 * MB, Hk * S_ if qkt is None else qkt, FAKE + 12 * MB,
+            H * S_, dtype,
             FAKE + 16 * MB, FAKE + 20 * MB, y, H * S_,
             ctypes.cast(arr, ctypes.c_void_p) if arr is not None else None,
             n, T if total is None else total, H, Hk, S_, 0.1, 64, ws, nb, None)
@@ -167,6 +168,10 @@ def test_chunked_varlen_validation_and_workspace_query():
     assert call(cu, state=FAKE + 64 * MB) == ERR_ALIAS                # a state over the workspace
     assert call(cu, y=FAKE + 4 * MB + 64) == ERR_ALIAS                # y over q
     assert call([0, 0, 0], total=0) == OK                             # nothing to do
+    assert call(cu, dtype=2) == ERR_UNSUP                             # unknown element type
+    # bf16 q, k, v at S = 128: 16-byte rows (strides a multiple of 8 elements)
+    assert call(cu, dtype=1, qkt=Hk * S + 4) == ERR_SHAPE
+    assert call(cu, dtype=1, q=FAKE + 4 * MB + 8) == ERR_SHAPE
 
 
 def test_norm_validation():

@@ -803,6 +803,41 @@ def test_chunked_varlen(S, lens, H, Hk, g_scale):
         assert ey < 2e-3 and es < 2e-3
 
 
+@pytest.mark.parametrize("S,H,Hk", [(128, 4, 2), (64, 3, 1), (32, 4, 4)])
+def test_chunked_varlen_bf16_inputs(S, H, Hk):
+    # bf16 q, k, v are widened exactly on load: the call must equal, bit for
+    # bit, the fp32 call on the same (bf16-representable) values, and match the
+    # sequential scan on them
+    lens = [100, 0, 300, 65]
+    base = "prefill" if S == 128 else "tiny"
+    inp = make_inputs(base, seed=89, S=S, head_dim=S, n_tok=max(lens), H=H, Hk=Hk,
+                      n_seq=len(lens), state_std=0.05)
+    wl = inp["wl"]
+    log_case("chunked_varlen_bf16", S=S, lens=lens, H=H, Hk=Hk)
+    pk = pack_varlen(inp, lens, oracle_g(inp))
+    qb, kb, vb = (on_dev(pk[x]).bfloat16() for x in ("q", "k", "v"))
+    g, beta = on_dev(pk["g"]), on_dev(pk["beta"])
+    st_b = on_dev(inp["state"]).clone()
+    y_b = torch.full((pk["cu"][-1], H, S), float("nan"), device=DEV)
+    gdn().gdn_recurrence_chunked_varlen(st_b, qb, kb, vb, g, beta, y_b, pk["cu"],
+                                        scale=wl.scale, chunk=64)
+    st_f = on_dev(inp["state"]).clone()
+    y_f = torch.full_like(y_b, float("nan"))
+    qf, kf, vf = qb.float(), kb.float(), vb.float()
+    gdn().gdn_recurrence_chunked_varlen(st_f, qf, kf, vf, g, beta, y_f, pk["cu"],
+                                        scale=wl.scale, chunk=64)
+    assert bits_equal(y_b, y_f) and bits_equal(st_b, st_f)
+    for s, n in enumerate(lens):
+        if n == 0:
+            continue
+        sl = slice(pk["cu"][s], pk["cu"][s + 1])
+        y_ref, s_ref, _ = oracle.recurrence_seq(
+            inp["state"][s:s + 1], qf[sl].cpu()[None], kf[sl].cpu()[None], vf[sl].cpu()[None],
+            pk["g"][sl][None], pk["beta"][sl][None], wl.scale)
+        ey, es = rel(y_b[sl][None], y_ref), rel(st_b[s:s + 1], s_ref)
+        assert ey < 2e-3 and es < 2e-3, (s, ey, es)
+
+
 def test_chunked_deterministic():
     inp = make_inputs("prefill", seed=71, n_tok=512)
     log_case("chunked_determinism")
