@@ -131,3 +131,32 @@ def make_inputs(wl: Workload | str, seed: int | None = None, **overrides) -> dic
     out["a"] = -torch.exp(out["A_log"])
     out["beta"] = torch.sigmoid(beta_logit)
     return out
+
+
+def make_mamba2_inputs(n_seq: int, n_tok: int, H: int, G: int, P: int, N: int, seed: int,
+                       state_std: float = 0.0) -> dict:
+    """Seeded fp32 inputs of one Mamba-2 selective-scan layer (the chunked SSD
+    scan's operands).  Draw order: dt_raw, dt_bias, A_log, D, x, B, C, state.
+
+      dt_raw [n_seq][n_tok][H] ~ N(0, 1);  dt_bias [H] ~ U(-7, -2.3)
+      A_log [H] ~ U(0, ln 16);  D [H] ~ N(0, 1)
+      x [n_seq][n_tok][H][P] ~ N(0, 1);  B, C [n_seq][n_tok][G][N] ~ N(0, 1)
+      state [n_seq][H][P][N] ~ N(0, state_std) (zero when state_std is 0)
+    dt_min, dt_max = 1e-3, 1e-1 are returned with them.
+    """
+    gen = torch.Generator("cpu").manual_seed(seed)
+
+    def normal(*shape, std=1.0):
+        return (torch.randn(*shape, generator=gen) * std).float()
+
+    def uniform(lo, hi, *shape):
+        return (lo + (hi - lo) * torch.rand(*shape, generator=gen)).float()
+
+    out = {"dt_raw": normal(n_seq, n_tok, H), "dt_bias": uniform(-7.0, -2.3, H),
+           "A_log": uniform(0.0, math.log(16.0), H), "D": normal(H),
+           "x": normal(n_seq, n_tok, H, P), "B": normal(n_seq, n_tok, G, N),
+           "C": normal(n_seq, n_tok, G, N)}
+    out["state"] = normal(n_seq, H, P, N, std=state_std) if state_std > 0 else \
+        torch.zeros(n_seq, H, P, N)
+    out["dt_min"], out["dt_max"] = 1e-3, 1e-1
+    return out

@@ -51,10 +51,14 @@ def _load():
     lib.oracle_recurrence_seq.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, D]
     lib.oracle_recurrence_chunked.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, D]
     lib.oracle_gated_rmsnorm.argtypes = [P, P, P, P, L, I, I, D]
+    lib.oracle_mamba2_dt.argtypes = [P, P, P, L, I, D, D]
+    lib.oracle_mamba2_ssd_seq.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I]
+    lib.oracle_mamba2_ssd_chunked.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I]
     lib.oracle_max_threads.restype = I
     lib.oracle_set_threads.argtypes = [I]
     for f in (lib.oracle_decay_gate, lib.oracle_conv1d_silu_l2norm, lib.oracle_recurrence_seq,
-              lib.oracle_recurrence_chunked, lib.oracle_gated_rmsnorm, lib.oracle_set_threads):
+              lib.oracle_recurrence_chunked, lib.oracle_gated_rmsnorm, lib.oracle_set_threads,
+              lib.oracle_mamba2_dt, lib.oracle_mamba2_ssd_seq, lib.oracle_mamba2_ssd_chunked):
         f.restype = None
     _lib = lib
     return lib
@@ -151,3 +155,43 @@ def gated_rmsnorm(y, w, z, eps: float) -> np.ndarray:
     out = np.empty_like(y)
     _load().oracle_gated_rmsnorm(_p(y), _p(w), _p(z), _p(out), rows, H, hd, float(eps))
     return out
+
+
+def mamba2_dt(dt_raw, dt_bias, dt_min: float, dt_max: float) -> np.ndarray:
+    """oracle_mamba2_dt: dt_raw [rows][H], dt_bias [H] -> dt [rows][H] (fp64)."""
+    dt_raw, dt_bias = _f64(dt_raw), _f64(dt_bias)
+    shape = dt_raw.shape
+    H = shape[-1]
+    rows = dt_raw.size // H
+    out = np.empty(shape, np.float64)
+    _load().oracle_mamba2_dt(_p(dt_raw), _p(dt_bias), _p(out), rows, H, float(dt_min),
+                             float(dt_max))
+    return out
+
+
+def _ssd_args(state, x, Bm, Cm, dt, A_log, D):
+    st = _f64(state).copy()
+    x, Bm, Cm, dt, D = _f64(x), _f64(Bm), _f64(Cm), _f64(dt), _f64(D)
+    A = -np.exp(_f64(A_log))
+    n_seq, T, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    return st, x, Bm, Cm, dt, A, D, n_seq, T, H, G, P, N
+
+
+def mamba2_ssd_seq(state, x, Bm, Cm, dt, A_log, D):
+    """oracle_mamba2_ssd_seq: state [n][H][P][N], x [n][T][H][P], Bm, Cm [n][T][G][N],
+    dt [n][T][H] (already clamped), A_log, D [H].  Returns (y, new state), fp64."""
+    st, x, Bm, Cm, dt, A, D, n_seq, T, H, G, P, N = _ssd_args(state, x, Bm, Cm, dt, A_log, D)
+    y = np.empty_like(x)
+    _load().oracle_mamba2_ssd_seq(_p(st), _p(x), _p(Bm), _p(Cm), _p(dt), _p(A), _p(D), _p(y),
+                                  n_seq, T, H, G, P, N)
+    return y, st
+
+
+def mamba2_ssd_chunked(state, x, Bm, Cm, dt, A_log, D, chunk: int = 64):
+    """oracle_mamba2_ssd_chunked: same arguments and results as mamba2_ssd_seq."""
+    st, x, Bm, Cm, dt, A, D, n_seq, T, H, G, P, N = _ssd_args(state, x, Bm, Cm, dt, A_log, D)
+    y = np.empty_like(x)
+    _load().oracle_mamba2_ssd_chunked(_p(st), _p(x), _p(Bm), _p(Cm), _p(dt), _p(A), _p(D),
+                                      _p(y), n_seq, T, H, G, P, N, int(chunk))
+    return y, st

@@ -22,6 +22,22 @@
  *                              staleness bound)
  *   oracle_recurrence_chunked  pinned against oracle_recurrence_seq (fp64, 1e-12)
  *   oracle_gated_rmsnorm       pinned (constant-input closed form, library rms_norm)
+ *   oracle_mamba2_dt           pinned (library softplus, clamp limits)
+ *   oracle_mamba2_ssd_seq      pinned (one-token closed form, pure decay, D skip,
+ *                              brute-force quadratic form on tiny inputs)
+ *   oracle_mamba2_ssd_chunked  pinned against oracle_mamba2_ssd_seq (fp64, 1e-12)
+ *
+ * The Mamba-2 functions follow [AT]'s mamba2_ssm_prefill wrapper (its
+ * arguments: state h, x, B and C projections, raw dt with a per-head bias and
+ * dt_min / dt_max limits, A_log, the D skip, n_groups; "same algorithm as
+ * decode", one thread per state index) and its "Mamba-2 SSD chunked prefill
+ * scan" comment (the chunked state-space-duality form of the same scan).  The
+ * page prints no formula; the recurrence written here is the published
+ * Mamba-2 selective scan those arguments name:
+ *   dt = clamp(softplus(dt_raw + dt_bias), dt_min, dt_max),  A = -exp(A_log)
+ *   h  <- exp(dt A) h + dt x B^T          (h [head_dim][state], per head)
+ *   y  =  h C + D x
+ * with value head h reading B, C of group h / (H / n_groups).
  */
 #include <math.h>
 #include <stddef.h>
@@ -313,6 +329,128 @@ void oracle_gated_rmsnorm(const double *y, const double *w, const double *z, dou
     for (int e = 0; e < head_dim; ++e) ss += yu[e] * yu[e];
     const double inv = 1.0 / sqrt(ss / head_dim + eps);
     for (int e = 0; e < head_dim; ++e) ou[e] = ((yu[e] * inv) * w[e]) * silu(zu[e]);
+  }
+}
+
+/*
+ * Mamba-2 step size per (row, head): dt = softplus(dt_raw + dt_bias) with the
+ * guard at 20 (as the decay gate's), then clamped to [dt_min, dt_max]: [AT]
+ * mamba2_ssm_prefill passes the raw projection, a per-head bias and the two
+ * limits.  Layouts: dt_raw, dt [rows][H]; dt_bias [H].
+ */
+void oracle_mamba2_dt(const double *dt_raw, const double *dt_bias, double *dt, long rows, int H,
+                      double dt_min, double dt_max) {
+  long r;
+#pragma omp parallel for schedule(static)
+  for (r = 0; r < rows; ++r)
+    for (int h = 0; h < H; ++h) {
+      double d = softplus_guarded(dt_raw[r * H + h] + dt_bias[h]);
+      if (d < dt_min) d = dt_min;
+      if (d > dt_max) d = dt_max;
+      dt[r * H + h] = d;
+    }
+}
+
+/*
+ * Mamba-2 selective scan, token by token (the definition; [AT]
+ * mamba2_ssm_prefill: "same algorithm as decode", looped over the tokens).
+ * Per sequence b, head h (group gi = h / (H / G)), token t:
+ *   a = exp(dt[t][h] * A[h])
+ *   h[p][n] = a * h[p][n] + dt[t][h] * x[t][h][p] * B[t][gi][n]
+ *   y[t][h][p] = sum_n h[p][n] * C[t][gi][n] + D[h] * x[t][h][p]
+ * Layouts (dense, fp64): state [B][H][P][N] in/out; x, y [B][T][H][P];
+ * Bm, Cm [B][T][G][N]; dt [B][T][H] (already through oracle_mamba2_dt);
+ * A [H] (= -exp(A_log)), D [H].
+ */
+void oracle_mamba2_ssd_seq(double *state, const double *x, const double *Bm, const double *Cm,
+                           const double *dt, const double *A, const double *D, double *y,
+                           int n_seq, int T, int H, int G, int P, int N) {
+  int u;
+#pragma omp parallel for schedule(dynamic)
+  for (u = 0; u < n_seq * H; ++u) {
+    const int b = u / H, h = u % H, gi = h / (H / G);
+    double *st = state + (size_t)u * P * N;
+    for (int t = 0; t < T; ++t) {
+      const size_t row = (size_t)b * T + t;
+      const double d = dt[row * H + h];
+      const double a = exp(d * A[h]);
+      const double *xt = x + (row * H + h) * P;
+      const double *bt = Bm + (row * G + gi) * N;
+      const double *ct = Cm + (row * G + gi) * N;
+      double *yt = y + (row * H + h) * P;
+      for (int p = 0; p < P; ++p) {
+        double acc = 0.0;
+        for (int n = 0; n < N; ++n) {
+          st[p * N + n] = a * st[p * N + n] + d * xt[p] * bt[n];
+          acc += st[p * N + n] * ct[n];
+        }
+        yt[p] = acc + D[h] * xt[p];
+      }
+    }
+  }
+}
+
+/*
+ * The same scan in chunked (state-space-duality) form: [AT] "Mamba-2 SSD
+ * chunked prefill scan" comment (ceil(T/chunk) sequential links, the rest
+ * dense products).  Derived from the sequential definition: with
+ * c_t = sum_{s<=t} dt_s A (inclusive, within the chunk) and h0 the state
+ * entering the chunk,
+ *   y_t  = sum_{s<=t} e^{c_t - c_s} (C_t . B_s) dt_s x_s + e^{c_t} C_t h0^T + D x_t
+ *   h_n  = e^{c_n} h0 + sum_s e^{c_n - c_s} dt_s x_s B_s^T
+ * (h0^T C_t meaning sum_n h0[p][n] C_t[n]).  Same layouts as the sequential form.
+ */
+void oracle_mamba2_ssd_chunked(double *state, const double *x, const double *Bm,
+                               const double *Cm, const double *dt, const double *A,
+                               const double *D, double *y, int n_seq, int T, int H, int G, int P,
+                               int N, int chunk) {
+  int u;
+#pragma omp parallel for schedule(dynamic)
+  for (u = 0; u < n_seq * H; ++u) {
+    const int b = u / H, h = u % H, gi = h / (H / G);
+    double *st = state + (size_t)u * P * N;
+    double *c = malloc(sizeof(double) * chunk);
+    double *hn = malloc(sizeof(double) * P * N);
+    for (int t0 = 0; t0 < T; t0 += chunk) {
+      const int n = T - t0 < chunk ? T - t0 : chunk;
+      double run = 0.0;
+      for (int t = 0; t < n; ++t) {
+        run += dt[((size_t)b * T + t0 + t) * H + h] * A[h];
+        c[t] = run;
+      }
+      for (int t = 0; t < n; ++t) {
+        const size_t rt = (size_t)b * T + t0 + t;
+        const double *ct = Cm + (rt * G + gi) * N;
+        const double *xt = x + (rt * H + h) * P;
+        double *yt = y + (rt * H + h) * P;
+        for (int p = 0; p < P; ++p) {
+          double inter = 0.0;
+          for (int k = 0; k < N; ++k) inter += st[p * N + k] * ct[k];
+          double intra = 0.0;
+          for (int s = 0; s <= t; ++s) {
+            const size_t rs = (size_t)b * T + t0 + s;
+            const double *bs = Bm + (rs * G + gi) * N;
+            double cb = 0.0;
+            for (int k = 0; k < N; ++k) cb += ct[k] * bs[k];
+            intra += exp(c[t] - c[s]) * cb * dt[rs * H + h] * x[(rs * H + h) * P + p];
+          }
+          yt[p] = intra + exp(c[t]) * inter + D[h] * xt[p];
+        }
+      }
+      for (int p = 0; p < P; ++p)
+        for (int k = 0; k < N; ++k) {
+          double acc = exp(c[n - 1]) * st[p * N + k];
+          for (int s = 0; s < n; ++s) {
+            const size_t rs = (size_t)b * T + t0 + s;
+            acc += exp(c[n - 1] - c[s]) * dt[rs * H + h] * x[(rs * H + h) * P + p] *
+                   Bm[(rs * G + gi) * N + k];
+          }
+          hn[p * N + k] = acc;
+        }
+      memcpy(st, hn, sizeof(double) * P * N);
+    }
+    free(c);
+    free(hn);
   }
 }
 

@@ -354,3 +354,104 @@ def test_workload_sizes_match_page_printed_layouts():
     assert wl.conv_dim * (wl.d_conv - 1) * 4 == gold["conv_history_bytes_per_layer"]["value"]
     d1 = WORKLOADS["decode"]
     assert 2 * d1.state_bytes == gold["decode_state_bytes_moved_mib"]["value"] * 2 ** 20
+
+
+# --------------------------------------------------------------------------- Mamba-2 SSD
+# ssm_mamba.rs, mamba2_ssm_prefill (its arguments: dt with bias and limits,
+# A_log, D skip, groups) and the "Mamba-2 SSD chunked prefill scan" comment.
+
+from gdn_inputs import make_mamba2_inputs  # noqa: E402
+
+
+def test_mamba2_dt_matches_library_softplus_and_clamps():
+    raw = np.concatenate([RNG.normal(0, 3, (50, 4)), [[25.0, 20.0, -40.0, 0.0]]])
+    bias = RNG.uniform(-7, -2.3, 4)
+    got = oracle.mamba2_dt(raw, bias, 1e-3, 1e-1)
+    ref = F.softplus(torch.from_numpy(raw + bias[None, :]), threshold=20.0).clamp(1e-3, 1e-1)
+    assert np.allclose(got, ref.numpy(), rtol=1e-14, atol=0)   # last-bit libm differences
+    assert got.min() >= 1e-3 and got.max() <= 1e-1
+    assert got[-1, 0] == 1e-1 and got[-1, 2] == 1e-3     # both limits reached
+
+
+def ssd_case(n, T, H, G, P, N, seed, state_std=0.0):
+    inp = make_mamba2_inputs(n, T, H, G, P, N, seed, state_std)
+    dt = oracle.mamba2_dt(inp["dt_raw"].reshape(-1, H), inp["dt_bias"], inp["dt_min"],
+                          inp["dt_max"]).reshape(n, T, H)
+    return inp, dt
+
+
+def test_mamba2_one_token_from_zero_closed_form():
+    n, H, G, P, N = 2, 4, 2, 8, 16
+    inp, dt = ssd_case(n, 1, H, G, P, N, 3)
+    y, st = oracle.mamba2_ssd_seq(inp["state"], inp["x"], inp["B"], inp["C"], dt, inp["A_log"],
+                                  inp["D"])
+    x, B, C, D = (inp[k].double().numpy() for k in ("x", "B", "C", "D"))
+    for b in range(n):
+        for h in range(H):
+            gi = h // (H // G)
+            d = dt[b, 0, h]
+            assert np.allclose(st[b, h], d * np.outer(x[b, 0, h], B[b, 0, gi]), rtol=1e-14,
+                               atol=0)
+            ref = d * (B[b, 0, gi] @ C[b, 0, gi]) * x[b, 0, h] + D[h] * x[b, 0, h]
+            assert rel_inf(y[b, 0, h], ref) < 1e-13
+
+
+def test_mamba2_pure_decay_closed_form():
+    n, T, H, G, P, N = 1, 37, 3, 1, 4, 8
+    inp, dt = ssd_case(n, T, H, G, P, N, 5, state_std=0.5)
+    x0 = torch.zeros_like(inp["x"])
+    y, st = oracle.mamba2_ssd_seq(inp["state"], x0, inp["B"], inp["C"], dt, inp["A_log"],
+                                  inp["D"])
+    A = -np.exp(inp["A_log"].double().numpy())
+    h0 = inp["state"].double().numpy()
+    C = inp["C"].double().numpy()
+    cum = np.cumsum(dt[0], axis=0) * A[None, :]          # [T][H]
+    for h in range(H):
+        assert rel_inf(st[0, h], np.exp(cum[-1, h]) * h0[0, h]) < 1e-13
+        ref = np.exp(cum[:, h])[:, None] * (C[0, :, 0] @ h0[0, h].T)
+        assert rel_inf(y[0, :, h], ref) < 1e-13
+
+
+def test_mamba2_d_skip_only_without_input_path():
+    n, T, H, G, P, N = 1, 20, 4, 2, 8, 8
+    inp, dt = ssd_case(n, T, H, G, P, N, 7)
+    B = inp["B"].clone()
+    B[:, :, 1] = 0.0                                     # group 1: heads 2, 3 see no input
+    y, st = oracle.mamba2_ssd_seq(inp["state"], inp["x"], B, inp["C"], dt, inp["A_log"],
+                                  inp["D"])
+    x, D = inp["x"].double().numpy(), inp["D"].double().numpy()
+    for h in (2, 3):
+        assert np.array_equal(y[0, :, h], D[h] * x[0, :, h])
+        assert not st[0, h].any()
+    assert st[0, 0].any() and st[0, 1].any()
+
+
+def test_mamba2_brute_force_quadratic_form():
+    # the unrolled scan: y_t = sum_{s<=t} (C_t . B_s) exp(A sum_{s<r<=t} dt_r) dt_s x_s
+    #                        + exp(A sum_{r<=t} dt_r) h0 C_t + D x_t
+    n, T, H, G, P, N = 1, 11, 2, 1, 3, 5
+    inp, dt = ssd_case(n, T, H, G, P, N, 9, state_std=0.3)
+    y, st = oracle.mamba2_ssd_seq(inp["state"], inp["x"], inp["B"], inp["C"], dt, inp["A_log"],
+                                  inp["D"])
+    A = -np.exp(inp["A_log"].double().numpy())
+    x, B, C, D = (inp[k].double().numpy() for k in ("x", "B", "C", "D"))
+    h0 = inp["state"].double().numpy()
+    for h in range(H):
+        for t in range(T):
+            ref = D[h] * x[0, t, h] + math.exp(A[h] * dt[0, :t + 1, h].sum()) * (h0[0, h] @ C[0, t, 0])
+            for s_ in range(t + 1):
+                decay = math.exp(A[h] * dt[0, s_ + 1:t + 1, h].sum())
+                ref = ref + (C[0, t, 0] @ B[0, s_, 0]) * decay * dt[0, s_, h] * x[0, s_, h]
+            assert rel_inf(y[0, t, h], ref) < 1e-12
+
+
+@pytest.mark.parametrize("T,H,G,P,N,chunk,state_std", [(100, 4, 2, 8, 16, 16, 0.0),
+                                                        (64, 2, 1, 16, 8, 64, 0.3),
+                                                        (130, 3, 3, 4, 32, 64, 0.1),
+                                                        (5, 2, 1, 4, 4, 64, 0.2)])
+def test_mamba2_chunked_equals_sequential(T, H, G, P, N, chunk, state_std):
+    inp, dt = ssd_case(2, T, H, G, P, N, 11, state_std)
+    args = (inp["state"], inp["x"], inp["B"], inp["C"], dt, inp["A_log"], inp["D"])
+    y_s, st_s = oracle.mamba2_ssd_seq(*args)
+    y_c, st_c = oracle.mamba2_ssd_chunked(*args, chunk=chunk)
+    assert rel_inf(y_c, y_s) < 1e-12 and rel_inf(st_c, st_s) < 1e-12
