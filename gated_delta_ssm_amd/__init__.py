@@ -43,6 +43,10 @@ _SIGS = {
     "gdn_recurrence_chunked_varlen_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "gdn_recurrence_chunked_varlen": (_I, [_P, _L, _P, _P, _L, _P, _L, _I, _P, _P, _P, _L,
                                            _P, _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
+    "gdn_mamba2_ssd_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "gdn_mamba2_ssd_chunked": (_I, [_P, _L, _P, _L, _L, _P, _P, _L, _L, _P, _L, _L, _P, _P, _P,
+                                    _P, _L, _L, _I, _I, _I, _I, _I, _I, _F, _F, _I, _P, _SZ,
+                                    _P]),
     "gdn_gated_rmsnorm": (_I, [_P, _L, _P, _P, _L, _P, _L, _I, _I, _I, _F, _P]),
     "gdn_stream_copy": (_I, [_P, _P, _SZ, _P]),
     "gdn_decode_fused": (_I, [_P, _L, _P, _P, _L, _L, _P, _L, _L, _P, _P, _P, _P, _P, _P, _L,
@@ -279,6 +283,49 @@ def gdn_recurrence_chunked_varlen(state: torch.Tensor, q: torch.Tensor, k: torch
         total, H,
         Hk, S, scale, chunk, _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream, y)))
+    return y
+
+
+def gdn_mamba2_ssd_workspace_bytes(n_seq: int, n_tok: int, n_heads: int, head_dim: int,
+                                   d_state: int, chunk: int = 64) -> int:
+    return int(_lib.gdn_mamba2_ssd_workspace_bytes(n_seq, n_tok, n_heads, head_dim, d_state,
+                                                   chunk))
+
+
+def gdn_mamba2_ssd_chunked(state: torch.Tensor, x: torch.Tensor, B: torch.Tensor,
+                           C: torch.Tensor, dt_raw: torch.Tensor, A_log: torch.Tensor,
+                           D: torch.Tensor, dt_bias: torch.Tensor, y: torch.Tensor, *,
+                           dt_min: float, dt_max: float, chunk: int = 64,
+                           workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Mamba-2 selective scan, chunked.  state [n_seq][H][P][N] (in place),
+    x, y [n_seq][T][H][P], B, C [n_seq][T][G][N] (same strides), dt_raw
+    [n_seq][T][H], A_log, D, dt_bias [H].  If no workspace is given one is
+    allocated here through torch."""
+    n_seq, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if tuple(state.shape) != (n_seq, H, P, N) or y.shape != x.shape or C.shape != B.shape:
+        raise ValueError("state / x / y / B / C shape mismatch")
+    if tuple(B.shape[:2]) != (n_seq, T) or tuple(dt_raw.shape) != (n_seq, T, H):
+        raise ValueError("B / dt_raw shape mismatch")
+    for n, t in (("A_log", A_log), ("D", D), ("dt_bias", dt_bias)):
+        if tuple(t.shape) != (H,):
+            raise ValueError(f"{n} must have shape [H]")
+        _dev_f32(n, t, 1)
+    _dev_f32("state", state, 3)
+    for n, t in (("x", x), ("y", y), ("B", B), ("C", C)):
+        _dev_f32(n, t, 2)
+    _dev_f32("dt_raw", dt_raw, 1)
+    if B.stride() != C.stride():
+        raise ValueError("B and C must share strides")
+    need = gdn_mamba2_ssd_workspace_bytes(n_seq, T, H, P, N, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=state.device)
+    _check("gdn_mamba2_ssd_chunked", _lib.gdn_mamba2_ssd_chunked(
+        _ptr(state), state.stride(0), _ptr(x), x.stride(1), x.stride(0), _ptr(B), _ptr(C),
+        B.stride(1), B.stride(0), _ptr(dt_raw), dt_raw.stride(1), dt_raw.stride(0),
+        _ptr(A_log), _ptr(D), _ptr(dt_bias), _ptr(y), y.stride(1), y.stride(0), n_seq, T, H, G,
+        P, N, dt_min, dt_max, chunk, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream, y)))
     return y
 
 

@@ -140,6 +140,39 @@ int gdn_recurrence_chunked_varlen(float *state, int64_t state_seq_stride, const 
                                           workspace_bytes, stream);
 }
 
+size_t gdn_mamba2_ssd_workspace_bytes(int n_seq, int n_tok, int n_heads, int head_dim,
+                                      int d_state, int chunk) {
+  if (n_seq < 1 || n_tok < 1 || n_heads < 1 || chunk != 64) return 0;
+  if ((head_dim != 32 && head_dim != 64) || (d_state != 64 && d_state != 128)) return 0;
+  return gdn::ssd_workspace_bytes(n_seq, n_tok, n_heads, head_dim, d_state);
+}
+
+int gdn_mamba2_ssd_chunked(float *state, int64_t state_seq_stride, const float *x,
+                           int64_t x_tok_stride, int64_t x_seq_stride, const float *B,
+                           const float *C, int64_t bc_tok_stride, int64_t bc_seq_stride,
+                           const float *dt_raw, int64_t dt_tok_stride, int64_t dt_seq_stride,
+                           const float *A_log, const float *D, const float *dt_bias, float *y,
+                           int64_t y_tok_stride, int64_t y_seq_stride, int n_seq, int n_tok,
+                           int n_heads, int n_groups, int head_dim, int d_state, float dt_min,
+                           float dt_max, int chunk, void *workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  const size_t need =
+      gdn_mamba2_ssd_workspace_bytes(n_seq, n_tok, n_heads, head_dim, d_state, chunk);
+  const int rc = gdn::check_ssd(state, state_seq_stride, x, x_tok_stride, x_seq_stride, B, C,
+                                bc_tok_stride, bc_seq_stride, dt_raw, dt_tok_stride,
+                                dt_seq_stride, A_log, D, dt_bias, y, y_tok_stride, y_seq_stride,
+                                n_seq, n_tok, n_heads, n_groups, head_dim, d_state, chunk,
+                                workspace, workspace_bytes, need);
+  if (rc != GDN_OK) return rc;
+  gdn::SsdLaunch l{state,         state_seq_stride, x,      x_tok_stride, x_seq_stride,
+                   B,             C,                bc_tok_stride, bc_seq_stride,
+                   dt_raw,        dt_tok_stride,    dt_seq_stride, A_log,  D,
+                   dt_bias,       y,                y_tok_stride,  y_seq_stride,
+                   n_seq,         n_tok,            n_heads,       n_groups, head_dim,
+                   d_state,       dt_min,           dt_max,        workspace};
+  return gdn::launch_ssd(l, stream);
+}
+
 int gdn_gated_rmsnorm(const float *y, int64_t y_row_stride, const float *w, const float *z,
                       int64_t z_row_stride, float *out, int64_t out_row_stride, int rows,
                       int n_heads, int head_dim, float eps, hipStream_t stream) {

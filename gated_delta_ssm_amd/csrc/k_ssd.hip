@@ -1,0 +1,340 @@
+// k_ssd.hip -- the Mamba-2 selective scan in chunked (state-space-duality)
+// form.  ssm_mamba.rs (spark_model layers/ops), mamba2_ssm_prefill: its
+// arguments (state h, x, B and C projections, raw dt with a per-head bias and
+// dt_min / dt_max limits, A_log, the D skip, n_groups) and the "Mamba-2 SSD
+// chunked prefill scan" comment (the scan as dense products with ceil(T/64)
+// sequential links).  Per head (group gi = h / (H / G)), token t:
+//   dt = clamp(softplus(dt_raw + dt_bias), dt_min, dt_max),  A = -exp(A_log)
+//   h  <- exp(dt A) h + dt x B^T        (h [P][N])
+//   y  =  h C + D x
+// For a chunk of n <= 64 positions entering with state h0, with c_t the
+// inclusive within-chunk sum of dt A (so every exponential below takes a
+// non-positive argument):
+//   y_t = sum_{s<=t} e^{c_t - c_s} (C_t . B_s) dt_s x_s + e^{c_t} h0 C_t + D x_t
+//   h_n = e^{c_n} h0 + sum_s e^{c_n - c_s} dt_s x_s B_s^T
+// Three launches:
+//   k_ssd_chunk  every (sequence, head, chunk) at once: the intra-chunk output
+//                (first sum, plus D x) into y, and the chunk's own state
+//                contribution (second sum) and decay e^{c_n} into a workspace
+//   k_ssd_state  the sequential link, elementwise over h: for each chunk, the
+//                state entering it is written over its contribution, then
+//                h <- e^{c_n} h + contribution; the last h is the new state
+//   k_ssd_out    every chunk again: y_t += e^{c_t} h0 C_t
+// All arithmetic is fp32 on the vector ALUs, 4 x 4 (or 4 x 8) register tiles
+// over LDS rows read as float4.
+#include <hip/hip_runtime.h>
+
+#include "gdn.h"
+#include "launch.hpp"
+
+namespace gdn {
+
+namespace {
+
+constexpr int SC = 64;     // positions per chunk
+constexpr int NT = 256;    // threads per workgroup
+
+__device__ __forceinline__ float softplus20(float v) { return v > 20.0f ? v : log1pf(expf(v)); }
+
+// Per-position dt and inclusive cumsum of dt A for the chunk, in LDS (wave 0;
+// positions past n get dt = 0, so the cumsum stays flat there).  Both
+// kernels that need c_t call this, so they agree bit for bit.
+__device__ __forceinline__ void chunk_dt(const float *dt_raw, int64_t dt_row0, int64_t dt_tok,
+                                         int h, int n, float bias, float A, float dt_min,
+                                         float dt_max, float *sDt, float *sCs) {
+  const int t = threadIdx.x;
+  if (t < SC) {
+    float d = 0.0f;
+    if (t < n) {
+      d = softplus20(dt_raw[dt_row0 + (int64_t)t * dt_tok + h] + bias);
+      d = fminf(fmaxf(d, dt_min), dt_max);
+    }
+    float c = d * A;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float o = __shfl_up(c, off, 64);
+      if (t >= off) c += o;
+    }
+    sDt[t] = d;
+    sCs[t] = c;
+  }
+}
+
+// Rows [0, n) of a [ROWS][W] tile with row stride `tok` (elements) into LDS
+// (pitch W + 4); rows n .. ROWS-1 are zero.  16-byte accesses.
+template <int W, int ROWS = SC>
+__device__ __forceinline__ void load_rows(float *dst, const float *src, int64_t tok, int n) {
+  constexpr int PW = W + 4, V = W / 4;
+  for (int e = threadIdx.x; e < ROWS * V; e += NT) {
+    const int r = e / V, c4 = (e - r * V) * 4;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (r < n) v = *reinterpret_cast<const float4 *>(src + (int64_t)r * tok + c4);
+    *reinterpret_cast<float4 *>(dst + r * PW + c4) = v;
+  }
+}
+
+struct SsdArgs {
+  const float *x, *Bm, *Cm, *dt_raw, *A_log, *D, *dt_bias;
+  int64_t x_tok, x_seq, bc_tok, bc_seq, dt_tok, dt_seq, y_tok, y_seq;
+  float *y;
+  int n_tok, H, G, n_chunks;
+  float dt_min, dt_max;
+};
+
+// Workspace: per (sequence, head, chunk) a [P][N] fp32 block (the chunk's
+// state contribution, then the state entering the chunk), and after all of
+// them one float per (sequence, head, chunk): e^{c_n}.
+template <int P, int N>
+__device__ __forceinline__ float *ws_block(float *ws, int s, int h, int c, int H, int nc) {
+  return ws + (((size_t)s * H + h) * nc + c) * (size_t)(P * N);
+}
+__device__ __forceinline__ float *ws_decay(float *ws, size_t blocks_floats, int s, int h, int c,
+                                           int H, int nc) {
+  return ws + blocks_floats + ((size_t)s * H + h) * nc + c;
+}
+
+template <int P, int N>
+__global__ __launch_bounds__(NT) void k_ssd_chunk(SsdArgs a, float *__restrict__ ws) {
+  constexpr int PX = P + 4, PB = N + 4, PM = SC + 4;
+  __shared__ __attribute__((aligned(16))) float sX[SC * PX];
+  __shared__ __attribute__((aligned(16))) float sB[SC * PB];
+  __shared__ __attribute__((aligned(16))) float sC[SC * PB];
+  __shared__ __attribute__((aligned(16))) float sM[SC * PM];
+  __shared__ float sDt[SC], sCs[SC];
+  const int c = blockIdx.x, h = blockIdx.y, s = blockIdx.z, tid = threadIdx.x;
+  const int gi = h / (a.H / a.G);
+  const int t0 = c * SC, n = min(SC, a.n_tok - t0);
+  const float A = -expf(a.A_log[h]);
+
+  chunk_dt(a.dt_raw, s * a.dt_seq + (int64_t)t0 * a.dt_tok, a.dt_tok, h, n, a.dt_bias[h], A,
+           a.dt_min, a.dt_max, sDt, sCs);
+  const float *xc = a.x + s * a.x_seq + (int64_t)t0 * a.x_tok + (int64_t)h * P;
+  const float *bc = a.Bm + s * a.bc_seq + (int64_t)t0 * a.bc_tok + (int64_t)gi * N;
+  const float *cc = a.Cm + s * a.bc_seq + (int64_t)t0 * a.bc_tok + (int64_t)gi * N;
+  load_rows<P>(sX, xc, a.x_tok, n);
+  load_rows<N>(sB, bc, a.bc_tok, n);
+  load_rows<N>(sC, cc, a.bc_tok, n);
+  __syncthreads();
+
+  // M[t][s] = e^{c_t - c_s} (C_t . B_s) dt_s for s <= t, else 0: a 4 x 4 block
+  // per thread (rows 4 tr .. +3, columns 4 sc .. +3)
+  {
+    const int tr = tid >> 4, sc = tid & 15;
+    float acc[4][4] = {};
+    for (int k = 0; k < N; k += 4) {
+      float4 cv[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        cv[i] = *reinterpret_cast<const float4 *>(sC + (4 * tr + i) * PB + k);
+        bv[i] = *reinterpret_cast<const float4 *>(sB + (4 * sc + i) * PB + k);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = fmaf(cv[i].w, bv[j].w, fmaf(cv[i].z, bv[j].z,
+                      fmaf(cv[i].y, bv[j].y, fmaf(cv[i].x, bv[j].x, acc[i][j]))));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 4 * tr + i;
+      float4 m;
+      float *mp = &m.x;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int u = 4 * sc + j;
+        const float arg = u <= t ? sCs[t] - sCs[u] : 0.0f;
+        mp[j] = u <= t ? expf(arg) * acc[i][j] * sDt[u] : 0.0f;
+      }
+      *reinterpret_cast<float4 *>(sM + t * PM + 4 * sc) = m;
+    }
+  }
+  __syncthreads();
+
+  // y_t (intra-chunk part) = sum_s M[t][s] x_s + D x_t: a 4 x (P/16) block per
+  // thread (rows 4 tr .. +3, columns 4 pc .. +3 for P = 64)
+  {
+    constexpr int PCOLS = P / 4;              // float4 columns of a row
+    constexpr int TROWS = NT / PCOLS;         // row groups
+    constexpr int RPT = SC / TROWS;           // rows per thread
+    const int pc = tid % PCOLS, tr = tid / PCOLS;
+    float4 acc[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int u = 0; u < SC; u += 4) {
+      float4 xv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xv[j] = *reinterpret_cast<const float4 *>(sX + (u + j) * PX + 4 * pc);
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const float4 m = *reinterpret_cast<const float4 *>(sM + (RPT * tr + i) * PM + u);
+        acc[i].x = fmaf(m.w, xv[3].x, fmaf(m.z, xv[2].x, fmaf(m.y, xv[1].x, fmaf(m.x, xv[0].x, acc[i].x))));
+        acc[i].y = fmaf(m.w, xv[3].y, fmaf(m.z, xv[2].y, fmaf(m.y, xv[1].y, fmaf(m.x, xv[0].y, acc[i].y))));
+        acc[i].z = fmaf(m.w, xv[3].z, fmaf(m.z, xv[2].z, fmaf(m.y, xv[1].z, fmaf(m.x, xv[0].z, acc[i].z))));
+        acc[i].w = fmaf(m.w, xv[3].w, fmaf(m.z, xv[2].w, fmaf(m.y, xv[1].w, fmaf(m.x, xv[0].w, acc[i].w))));
+      }
+    }
+    const float Dh = a.D[h];
+    float *yc = a.y + s * a.y_seq + (int64_t)t0 * a.y_tok + (int64_t)h * P;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int t = RPT * tr + i;
+      if (t < n) {
+        const float4 xv = *reinterpret_cast<const float4 *>(sX + t * PX + 4 * pc);
+        *reinterpret_cast<float4 *>(yc + (int64_t)t * a.y_tok + 4 * pc) =
+            make_float4(acc[i].x + Dh * xv.x, acc[i].y + Dh * xv.y, acc[i].z + Dh * xv.z,
+                        acc[i].w + Dh * xv.w);
+      }
+    }
+  }
+
+  // chunk contribution Hc[p][k] = sum_s w_s x_s[p] B_s[k], w_s = e^{c_n - c_s} dt_s:
+  // P x N outputs, a 4 x 8 block per thread at P = 64, N = 128 (rows 4 pr .. +3,
+  // columns 8 kc .. +7); in general (4 rows) x (P N / (4 NT) columns)
+  {
+    constexpr int KC = N / 8;                 // 8-column groups
+    constexpr int PR = NT / KC;               // row groups
+    constexpr int RPT = P / PR;               // rows per thread
+    static_assert(RPT >= 1 && P % PR == 0, "thread map");
+    const int kc = tid % KC, pr = tid / KC;
+    const float cn = sCs[SC - 1];
+    float acc[RPT][8] = {};
+    for (int u = 0; u < SC; ++u) {
+      const float w = expf(cn - sCs[u]) * sDt[u];
+      const float4 b0 = *reinterpret_cast<const float4 *>(sB + u * PB + 8 * kc);
+      const float4 b1 = *reinterpret_cast<const float4 *>(sB + u * PB + 8 * kc + 4);
+      const float bw[8] = {w * b0.x, w * b0.y, w * b0.z, w * b0.w,
+                           w * b1.x, w * b1.y, w * b1.z, w * b1.w};
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const float xv = sX[u * PX + RPT * pr + i];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(xv, bw[j], acc[i][j]);
+      }
+    }
+    float *blk = ws_block<P, N>(ws, s, h, c, a.H, a.n_chunks);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      float *row = blk + (RPT * pr + i) * N + 8 * kc;
+      *reinterpret_cast<float4 *>(row) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+      *reinterpret_cast<float4 *>(row + 4) =
+          make_float4(acc[i][4], acc[i][5], acc[i][6], acc[i][7]);
+    }
+    if (tid == 0) {
+      const size_t blocks = (size_t)gridDim.z * a.H * a.n_chunks * (P * N);
+      *ws_decay(ws, blocks, s, h, c, a.H, a.n_chunks) = expf(cn);
+    }
+  }
+}
+
+// The sequential link: thread e of (sequence, head) owns elements 4e .. 4e+3
+// of the [P][N] state.
+template <int P, int N>
+__global__ __launch_bounds__(NT) void k_ssd_state(float *__restrict__ state, int64_t st_seq,
+                                                  float *__restrict__ ws, int n_seq, int H,
+                                                  int nc) {
+  const int h = blockIdx.y, s = blockIdx.z;
+  const int e = blockIdx.x * NT + threadIdx.x;   // float4 index, < P N / 4 by the grid
+  float4 *sp = reinterpret_cast<float4 *>(state + s * st_seq + (size_t)h * P * N) + e;
+  float4 st = *sp;
+  const size_t blocks = (size_t)n_seq * H * nc * (P * N);
+  const float *dec = ws_decay(ws, blocks, s, h, 0, H, nc);
+  for (int c = 0; c < nc; ++c) {
+    float4 *bp = reinterpret_cast<float4 *>(ws_block<P, N>(ws, s, h, c, H, nc)) + e;
+    const float4 contrib = *bp;
+    const float gam = dec[c];
+    *bp = st;   // the state entering chunk c
+    st = make_float4(gam * st.x + contrib.x, gam * st.y + contrib.y, gam * st.z + contrib.z,
+                     gam * st.w + contrib.w);
+  }
+  *sp = st;
+}
+
+// y_t += e^{c_t} sum_k h0[p][k] C_t[k] with h0 the state entering the chunk.
+template <int P, int N>
+__global__ __launch_bounds__(NT) void k_ssd_out(SsdArgs a, const float *__restrict__ ws) {
+  constexpr int PB = N + 4;
+  __shared__ __attribute__((aligned(16))) float sC[SC * PB];
+  __shared__ __attribute__((aligned(16))) float sH[P * PB];
+  __shared__ float sDt[SC], sCs[SC];
+  const int c = blockIdx.x, h = blockIdx.y, s = blockIdx.z, tid = threadIdx.x;
+  const int gi = h / (a.H / a.G);
+  const int t0 = c * SC, n = min(SC, a.n_tok - t0);
+  const float A = -expf(a.A_log[h]);
+  chunk_dt(a.dt_raw, s * a.dt_seq + (int64_t)t0 * a.dt_tok, a.dt_tok, h, n, a.dt_bias[h], A,
+           a.dt_min, a.dt_max, sDt, sCs);
+  load_rows<N>(sC, a.Cm + s * a.bc_seq + (int64_t)t0 * a.bc_tok + (int64_t)gi * N, a.bc_tok, n);
+  const float *blk = ws_block<P, N>(const_cast<float *>(ws), s, h, c, a.H, a.n_chunks);
+  load_rows<N, P>(sH, blk, N, P);   // the P rows of the entering state, row stride N
+  __syncthreads();
+
+  constexpr int PCOLS = P / 4;
+  constexpr int TROWS = NT / PCOLS;
+  constexpr int RPT = SC / TROWS;
+  const int pc = tid % PCOLS, tr = tid / PCOLS;
+  float4 acc[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k = 0; k < N; k += 4) {
+    float4 hv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hv[j] = *reinterpret_cast<const float4 *>(sH + (4 * pc + j) * PB + k);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const float4 cv = *reinterpret_cast<const float4 *>(sC + (RPT * tr + i) * PB + k);
+      acc[i].x = fmaf(cv.w, hv[0].w, fmaf(cv.z, hv[0].z, fmaf(cv.y, hv[0].y, fmaf(cv.x, hv[0].x, acc[i].x))));
+      acc[i].y = fmaf(cv.w, hv[1].w, fmaf(cv.z, hv[1].z, fmaf(cv.y, hv[1].y, fmaf(cv.x, hv[1].x, acc[i].y))));
+      acc[i].z = fmaf(cv.w, hv[2].w, fmaf(cv.z, hv[2].z, fmaf(cv.y, hv[2].y, fmaf(cv.x, hv[2].x, acc[i].z))));
+      acc[i].w = fmaf(cv.w, hv[3].w, fmaf(cv.z, hv[3].z, fmaf(cv.y, hv[3].y, fmaf(cv.x, hv[3].x, acc[i].w))));
+    }
+  }
+  float *yc = a.y + s * a.y_seq + (int64_t)t0 * a.y_tok + (int64_t)h * P;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int t = RPT * tr + i;
+    if (t < n) {
+      const float e = expf(sCs[t]);
+      float4 *yp = reinterpret_cast<float4 *>(yc + (int64_t)t * a.y_tok + 4 * pc);
+      const float4 yv = *yp;
+      *yp = make_float4(yv.x + e * acc[i].x, yv.y + e * acc[i].y, yv.z + e * acc[i].z,
+                        yv.w + e * acc[i].w);
+    }
+  }
+}
+
+template <int P, int N>
+int run_ssd(const SsdLaunch &l, hipStream_t stream) {
+  const int nc = (l.n_tok + SC - 1) / SC;
+  SsdArgs a{l.x,     l.Bm,     l.Cm,     l.dt_raw, l.A_log,  l.D,    l.dt_bias,
+            l.x_tok, l.x_seq,  l.bc_tok, l.bc_seq, l.dt_tok, l.dt_seq, l.y_tok,
+            l.y_seq, l.y,      l.n_tok,  l.H,      l.G,      nc,     l.dt_min,
+            l.dt_max};
+  float *ws = static_cast<float *>(l.ws);
+  const dim3 grid_c((unsigned)nc, (unsigned)l.H, (unsigned)l.n_seq);
+  int rc = launch_kernel(k_ssd_chunk<P, N>, grid_c, dim3(NT), 0, stream, a, ws);
+  if (rc != GDN_OK) return rc;
+  static_assert((P * N / 4) % NT == 0, "state grid");
+  rc = launch_kernel(k_ssd_state<P, N>, dim3(P * N / 4 / NT, (unsigned)l.H, (unsigned)l.n_seq),
+                     dim3(NT), 0, stream, l.state, l.st_seq, ws, l.n_seq, l.H, nc);
+  if (rc != GDN_OK) return rc;
+  return launch_kernel(k_ssd_out<P, N>, grid_c, dim3(NT), 0, stream, a,
+                       static_cast<const float *>(ws));
+}
+
+}  // namespace
+
+size_t ssd_workspace_bytes(int n_seq, int n_tok, int H, int P, int N) {
+  const size_t nc = (size_t)((n_tok + SC - 1) / SC);
+  const size_t units = (size_t)n_seq * H * nc;
+  return units * (size_t)P * N * sizeof(float) + ((units * sizeof(float) + 255) & ~(size_t)255);
+}
+
+int launch_ssd(const SsdLaunch &l, hipStream_t stream) {
+  if (l.P == 64 && l.N == 128) return run_ssd<64, 128>(l, stream);
+  if (l.P == 64 && l.N == 64) return run_ssd<64, 64>(l, stream);
+  if (l.P == 32 && l.N == 128) return run_ssd<32, 128>(l, stream);
+  if (l.P == 32 && l.N == 64) return run_ssd<32, 64>(l, stream);
+  return GDN_ERR_UNSUPPORTED;
+}
+
+}  // namespace gdn

@@ -94,6 +94,26 @@ int launch_chunk_small(const RecurArgs &a, hipStream_t stream);
 int launch_chunk_small_varlen(const RecurArgs &a, const VarTab &tab, bool bf16_in,
                               hipStream_t stream);
 
+// The Mamba-2 chunked SSD scan (k_ssd.hip); arguments already validated.
+struct SsdLaunch {
+  float *state;
+  int64_t st_seq;
+  const float *x;
+  int64_t x_tok, x_seq;
+  const float *Bm, *Cm;
+  int64_t bc_tok, bc_seq;
+  const float *dt_raw;
+  int64_t dt_tok, dt_seq;
+  const float *A_log, *D, *dt_bias;
+  float *y;
+  int64_t y_tok, y_seq;
+  int n_seq, n_tok, H, G, P, N;
+  float dt_min, dt_max;
+  void *ws;
+};
+size_t ssd_workspace_bytes(int n_seq, int n_tok, int H, int P, int N);
+int launch_ssd(const SsdLaunch &l, hipStream_t stream);
+
 struct NormArgs {
   const float *y;
   int64_t y_row;

@@ -208,6 +208,42 @@ int check_chunked_varlen(const float *state, int64_t st_seq, const void *q, cons
   return GDN_OK;
 }
 
+int check_ssd(const float *state, int64_t st_seq, const float *x, int64_t x_tok, int64_t x_seq,
+              const float *B, const float *C, int64_t bc_tok, int64_t bc_seq,
+              const float *dt_raw, int64_t dt_tok, int64_t dt_seq, const float *A_log,
+              const float *D, const float *dt_bias, const float *y, int64_t y_tok,
+              int64_t y_seq, int n_seq, int n_tok, int H, int G, int P, int N, int chunk,
+              const void *ws, size_t ws_bytes, size_t ws_needed) {
+  if (n_seq < 1 || n_tok < 1 || H < 1 || G < 1 || H % G != 0) return GDN_ERR_SHAPE;
+  if (P < 32 || P % 32 != 0 || N < 32 || N % 32 != 0) return GDN_ERR_SHAPE;
+  if ((P != 32 && P != 64) || (N != 64 && N != 128) || chunk != 64) return GDN_ERR_UNSUPPORTED;
+  if (st_seq < 0 || x_tok < 0 || x_seq < 0 || bc_tok < 0 || bc_seq < 0 || dt_tok < 0 ||
+      dt_seq < 0 || y_tok < 0 || y_seq < 0)
+    return GDN_ERR_SHAPE;
+  if (!state || !x || !B || !C || !dt_raw || !A_log || !D || !dt_bias || !y) return GDN_ERR_NULL;
+  const int64_t st_len = (int64_t)H * P * N;
+  if (!rows_disjoint(n_seq, st_seq, 1, 0, st_len)) return GDN_ERR_SHAPE;
+  if (!rows_disjoint(n_seq, y_seq, n_tok, y_tok, (int64_t)H * P)) return GDN_ERR_SHAPE;
+  for (const void *p : {(const void *)state, (const void *)x, (const void *)B, (const void *)C,
+                        (const void *)y})
+    if (!aligned(p, 16)) return GDN_ERR_SHAPE;
+  if (st_seq % 4 || x_tok % 4 || x_seq % 4 || bc_tok % 4 || bc_seq % 4 || y_tok % 4 || y_seq % 4)
+    return GDN_ERR_SHAPE;
+  if (!ws || ws_bytes < ws_needed || !aligned(ws, 256)) return GDN_ERR_WORKSPACE;
+  const Span sst = span_of(state, n_seq, st_seq, 1, 0, st_len);
+  const Span sy = span_of(y, n_seq, y_seq, n_tok, y_tok, (int64_t)H * P);
+  const Span sw{(uintptr_t)ws, (uintptr_t)ws + ws_bytes};
+  for (Span in : {span_of(x, n_seq, x_seq, n_tok, x_tok, (int64_t)H * P),
+                  span_of(B, n_seq, bc_seq, n_tok, bc_tok, (int64_t)G * N),
+                  span_of(C, n_seq, bc_seq, n_tok, bc_tok, (int64_t)G * N),
+                  span_of(dt_raw, n_seq, dt_seq, n_tok, dt_tok, H),
+                  span_of(A_log, 1, 0, 1, 0, H), span_of(D, 1, 0, 1, 0, H),
+                  span_of(dt_bias, 1, 0, 1, 0, H)})
+    if (overlap(sst, in) || overlap(sy, in) || overlap(sw, in)) return GDN_ERR_ALIAS;
+  if (overlap(sy, sst) || overlap(sw, sst) || overlap(sw, sy)) return GDN_ERR_ALIAS;
+  return GDN_OK;
+}
+
 int check_norm(const float *y, int64_t y_row, const float *w, const float *z, int64_t z_row,
                const float *out, int64_t o_row, int rows, int H, int hd) {
   if (rows < 0 || H < 1) return GDN_ERR_SHAPE;

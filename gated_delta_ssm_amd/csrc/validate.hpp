@@ -33,6 +33,13 @@ int check_chunked_varlen(const float *state, int64_t st_seq, const void *q, cons
                          int n_seq, int total_tok, int H, int Hk, int S, int chunk,
                          const void *ws, size_t ws_bytes, size_t ws_needed);
 
+int check_ssd(const float *state, int64_t st_seq, const float *x, int64_t x_tok, int64_t x_seq,
+              const float *B, const float *C, int64_t bc_tok, int64_t bc_seq,
+              const float *dt_raw, int64_t dt_tok, int64_t dt_seq, const float *A_log,
+              const float *D, const float *dt_bias, const float *y, int64_t y_tok,
+              int64_t y_seq, int n_seq, int n_tok, int H, int G, int P, int N, int chunk,
+              const void *ws, size_t ws_bytes, size_t ws_needed);
+
 int check_norm(const float *y, int64_t y_row, const float *w, const float *z, int64_t z_row,
                const float *out, int64_t o_row, int rows, int H, int hd);
 

@@ -239,6 +239,46 @@ int gdn_recurrence_chunked_varlen(float *state, int64_t state_seq_stride, const 
                                   hipStream_t stream);
 
 /*
+ * Workspace bytes gdn_mamba2_ssd_chunked needs (0 if the sizes are invalid).
+ */
+size_t gdn_mamba2_ssd_workspace_bytes(int n_seq, int n_tok, int n_heads, int head_dim,
+                                      int d_state, int chunk);
+
+/*
+ * Mamba-2 selective scan over a prompt, chunked (state-space-duality) form.
+ * [AT] mamba2_ssm_prefill (its arguments: state, x, B and C projections, raw
+ * dt with a per-head bias and dt_min / dt_max limits, A_log, the D skip,
+ * n_groups, per-tensor token strides) and its "Mamba-2 SSD chunked prefill
+ * scan" comment (ceil(T/64) sequential links, the rest dense products).  Per
+ * sequence, head h (group h / (n_heads / n_groups)) and token t:
+ *   dt = min(max(softplus(dt_raw + dt_bias), dt_min), dt_max)   (softplus
+ *        guarded at 20),  A = -exp(A_log)
+ *   state <- exp(dt A) state + dt x B^T,   y = state C + D x
+ *
+ *   state   [n_seq][H][head_dim][d_state] fp32, sequence stride        (in/out)
+ *   x       [n_seq][T][H][head_dim], token / sequence strides          (in)
+ *   B, C    [n_seq][T][G][d_state], shared token / sequence strides    (in)
+ *   dt_raw  [n_seq][T][H], token / sequence strides                    (in)
+ *   A_log, D, dt_bias  [H]                                             (in)
+ *   y       [n_seq][T][H][head_dim], token / sequence strides          (out)
+ * All fp32 device memory, strides in elements.  head_dim in {32, 64},
+ * d_state in {64, 128}, chunk 64, n_heads % n_groups == 0, T >= 1.  x, B, C,
+ * y, state 16-byte aligned with strides a multiple of 4.  The workspace is
+ * device memory of gdn_mamba2_ssd_workspace_bytes(...) bytes, 256-byte
+ * aligned, owned by the caller.  fp32 arithmetic throughout; the result
+ * matches the token-by-token scan to rounding, not bit for bit.
+ */
+int gdn_mamba2_ssd_chunked(float *state, int64_t state_seq_stride, const float *x,
+                           int64_t x_tok_stride, int64_t x_seq_stride, const float *B,
+                           const float *C, int64_t bc_tok_stride, int64_t bc_seq_stride,
+                           const float *dt_raw, int64_t dt_tok_stride, int64_t dt_seq_stride,
+                           const float *A_log, const float *D, const float *dt_bias, float *y,
+                           int64_t y_tok_stride, int64_t y_seq_stride, int n_seq, int n_tok,
+                           int n_heads, int n_groups, int head_dim, int d_state, float dt_min,
+                           float dt_max, int chunk, void *workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/*
  * Gated RMSNorm per (row, head).  [FM] "Gated RMSNorm" section
  * (fm_ssm_gated_norm_at); [AT] gdn_verify_fused_norm_k2 for reading z out of
  * a wider per-token row (pass z already offset to its column).

@@ -174,6 +174,37 @@ def test_chunked_varlen_validation_and_workspace_query():
     assert call(cu, dtype=1, q=FAKE + 4 * MB + 8) == ERR_SHAPE
 
 
+def test_mamba2_ssd_validation_and_workspace_query():
+    MB = 1 << 20
+    n, T, H, G, P, N = 2, 100, 4, 2, 64, 128
+    need = L.gdn_mamba2_ssd_workspace_bytes(n, T, H, P, N, 64)
+    assert need >= n * H * 2 * P * N * 4                     # two chunks of state blocks
+    assert L.gdn_mamba2_ssd_workspace_bytes(n, T, H, 48, N, 64) == 0
+    assert L.gdn_mamba2_ssd_workspace_bytes(n, T, H, P, 96, 64) == 0
+    assert L.gdn_mamba2_ssd_workspace_bytes(n, T, H, P, N, 32) == 0
+
+    def call(state=FAKE, sts=H * P * N, x=FAKE + 8 * MB, xt=H * P, B=FAKE + 16 * MB,
+             C=FAKE + 24 * MB, bct=G * N, y=FAKE + 32 * MB, H_=H, G_=G, P_=P, N_=N,
+             ws=FAKE + 64 * MB, nb=need, chunk=64):
+        return L.gdn_mamba2_ssd_chunked(
+            state, sts, x, xt, T * xt, B, C, bct, T * bct, FAKE + 40 * MB, H_, T * H_,
+            FAKE + 41 * MB, FAKE + 42 * MB, FAKE + 43 * MB, y, H_ * P_, T * H_ * P_, n, T, H_,
+            G_, P_, N_, 1e-3, 1e-1, chunk, ws, nb, None)
+    assert call(G_=3) == ERR_SHAPE                           # H % G
+    assert call(P_=48) == ERR_SHAPE
+    assert call(P_=128) == ERR_UNSUP
+    assert call(chunk=32) == ERR_UNSUP
+    assert call(x=None) == ERR_NULL
+    assert call(x=FAKE + 8 * MB + 4) == ERR_SHAPE            # misaligned 16-byte rows
+    assert call(xt=H * P + 2) == ERR_SHAPE                   # stride not a multiple of 4
+    assert call(sts=100) == ERR_SHAPE                        # state rows overlap
+    assert call(ws=None) == ERR_WS
+    assert call(nb=need - 1) == ERR_WS
+    assert call(y=FAKE + 8 * MB + 64) == ERR_ALIAS           # y over x
+    assert call(state=FAKE + 16 * MB) == ERR_ALIAS           # state over B
+    assert call(ws=FAKE + 24 * MB) == ERR_ALIAS              # workspace over C
+
+
 def test_norm_validation():
     MB = 1 << 20
     call = lambda y, ys, w, z, zs, o, os_, rows, H, hd: L.gdn_gated_rmsnorm(

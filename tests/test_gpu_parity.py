@@ -19,7 +19,7 @@ import pytest
 import torch
 
 import oracle
-from gdn_inputs import WORKLOADS, make_inputs
+from gdn_inputs import WORKLOADS, make_inputs, make_mamba2_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -844,6 +844,67 @@ def test_chunked_deterministic():
     g3 = oracle_g(inp)
     ya, sa = run_chunked(inp, g3)
     yb, sb = run_chunked(inp, g3)
+    assert bits_equal(ya, yb) and bits_equal(sa, sb)
+
+
+# ------------------------------------------------------------------------------------- Mamba-2 SSD
+
+def ssd_oracle(inp):
+    n, T, H = inp["dt_raw"].shape
+    dt = oracle.mamba2_dt(inp["dt_raw"].reshape(-1, H), inp["dt_bias"], inp["dt_min"],
+                          inp["dt_max"]).reshape(n, T, H)
+    return oracle.mamba2_ssd_seq(inp["state"], inp["x"], inp["B"], inp["C"], dt, inp["A_log"],
+                                 inp["D"])
+
+
+def run_ssd(inp, pad=0):
+    """The GPU scan; with pad > 0, x, B, C, y are views into rows `pad` wider
+    (y's gaps poisoned with NaN and checked afterwards)."""
+    n, T, H, P = inp["x"].shape
+    G, N = inp["B"].shape[2], inp["B"].shape[3]
+
+    def wide(t, inner):
+        buf = torch.full((n, T, inner + pad), float("nan"), device=DEV)
+        buf[:, :, :inner] = on_dev(t).reshape(n, T, inner)
+        return buf, buf[:, :, :inner]
+    _, x = wide(inp["x"], H * P)
+    _, Bm = wide(inp["B"], G * N)
+    cbuf = torch.full((n, T, G * N + pad), float("nan"), device=DEV)
+    cbuf[:, :, :G * N] = on_dev(inp["C"]).reshape(n, T, G * N)
+    Cm = cbuf[:, :, :G * N]
+    ybuf = torch.full((n, T, H * P + pad), float("nan"), device=DEV)
+    y = ybuf[:, :, :H * P].unflatten(2, (H, P))
+    st = on_dev(inp["state"]).clone()
+    gdn().gdn_mamba2_ssd_chunked(st, x.unflatten(2, (H, P)), Bm.unflatten(2, (G, N)),
+                                 Cm.unflatten(2, (G, N)), on_dev(inp["dt_raw"]),
+                                 on_dev(inp["A_log"]), on_dev(inp["D"]), on_dev(inp["dt_bias"]),
+                                 y, dt_min=inp["dt_min"], dt_max=inp["dt_max"])
+    if pad:
+        assert torch.isnan(ybuf[:, :, H * P:]).all(), "write outside y's rows"
+    return y, st
+
+
+@pytest.mark.parametrize("n,T,H,G,P,N,state_std,pad", [
+    (1, 4096, 32, 1, 64, 128, 0.0, 0),       # a 4096-token prompt, 32 heads x 64, state 128
+    (2, 100, 4, 2, 32, 64, 0.2, 8),
+    (3, 1, 6, 3, 64, 64, 0.2, 0),
+    (1, 65, 2, 1, 32, 128, 0.1, 4),
+    (2, 200, 8, 4, 64, 128, 0.05, 0)])
+def test_mamba2_ssd_chunked(n, T, H, G, P, N, state_std, pad):
+    inp = make_mamba2_inputs(n, T, H, G, P, N, seed=97, state_std=state_std)
+    log_case("mamba2_ssd", n=n, T=T, H=H, G=G, P=P, N=N)
+    y, st = run_ssd(inp, pad)
+    y_ref, s_ref = ssd_oracle(inp)
+    ey, es = rel(y, y_ref), rel(st, s_ref)
+    print(f"[mamba2 ssd] T={T} rel err y {ey:.3e} state {es:.3e}", flush=True)
+    assert ey < 1e-4 and es < 1e-4
+
+
+def test_mamba2_ssd_deterministic():
+    inp = make_mamba2_inputs(1, 300, 8, 2, 64, 128, seed=101, state_std=0.1)
+    log_case("mamba2_ssd_determinism")
+    ya, sa = run_ssd(inp)
+    yb, sb = run_ssd(inp)
     assert bits_equal(ya, yb) and bits_equal(sa, sb)
 
 
