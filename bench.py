@@ -501,6 +501,48 @@ def main():
     except gdn.GdnError as e:
         prefill_varlen = {"error": str(e)}
 
+    # ------------------------------------------------- Mamba-2 SSD chunked scan
+    try:
+        from gdn_inputs import make_mamba2_inputs
+        mT, mH, mG, mP, mN = 4096, 32, 1, 64, 128
+        mi = make_mamba2_inputs(1, mT, mH, mG, mP, mN, seed=7)
+        mx, mB, mC, mdt = (mi[k].to(dev) for k in ("x", "B", "C", "dt_raw"))
+        mAl, mD, mbias = (mi[k].to(dev) for k in ("A_log", "D", "dt_bias"))
+        mst = torch.zeros(1, mH, mP, mN, device=dev)
+        my = torch.empty_like(mx)
+        mws = torch.empty(gdn.gdn_mamba2_ssd_workspace_bytes(1, mT, mH, mP, mN, 64),
+                          dtype=torch.uint8, device=dev)
+
+        def ssd_call():
+            gdn.gdn_mamba2_ssd_chunked(mst, mx, mB, mC, mdt, mAl, mD, mbias, my,
+                                       dt_min=mi["dt_min"], dt_max=mi["dt_max"], workspace=mws)
+        for _ in range(2):
+            ssd_call()
+        torch.cuda.synchronize()
+        m0 = torch.cuda.Event(enable_timing=True)
+        m1 = torch.cuda.Event(enable_timing=True)
+        m0.record(stream)
+        for _ in range(args.prefill_iters):
+            ssd_call()
+        m1.record(stream)
+        m1.synchronize()
+        mms = m0.elapsed_time(m1) / args.prefill_iters
+        nch = (mT + 63) // 64
+        # multiply-adds per (head, chunk): C B^T 64x64x N, M x 64x64x P, state 64 x P x N,
+        # inter-chunk output 64 x P x N
+        ssd_flops = 2.0 * mH * nch * (64 * 64 * mN + 64 * 64 * mP + 2 * 64 * mP * mN)
+        mamba2 = {
+            "workload": f"Mamba-2 selective scan, 1 seq x {mT} tokens, {mH} heads x head_dim {mP}, "
+                        f"state {mN}, {mG} group, chunk 64, fp32",
+            "ms": mms, "tokens_per_s": mT / (mms * 1e-3),
+            "tflops": ssd_flops / (mms * 1e-3) / 1e12,
+            "frac_of_fp32_vector_peak": ssd_flops / (mms * 1e-3) / 1e12 / FP32_MATRIX_PEAK_TFLOPS,
+            "note": "three launches (chunk outputs and states, state link, inter-chunk outputs); "
+                    "fp32 FMA on the vector ALUs, whose peak equals the fp32 matrix figure"}
+        del mx, mB, mC, mdt, mst, my, mws
+    except gdn.GdnError as e:
+        mamba2 = {"error": str(e)}
+
     # ---------------------------------------------------------------- CPU baseline (oracle)
     cpu = None
     if not args.no_cpu_baseline:
@@ -572,6 +614,7 @@ def main():
         },
         "prefill": prefill,
         "prefill_varlen": prefill_varlen,
+        "mamba2_ssd": mamba2,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out, default=float))
