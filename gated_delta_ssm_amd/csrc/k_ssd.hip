@@ -116,8 +116,9 @@ __global__ __launch_bounds__(NT) void k_ssd_chunk(SsdArgs a, float *__restrict__
   load_rows<N>(sC, cc, a.bc_tok, n);
   __syncthreads();
 
-  // M[t][s] = e^{c_t - c_s} (C_t . B_s) dt_s for s <= t, else 0: a 4 x 4 block
-  // per thread (rows 4 tr .. +3, columns 4 sc .. +3)
+  // M[t][s] = e^{c_t - c_s} (C_t . B_s) dt_s for s <= t, else 0: 4 x 4 entries
+  // per thread, rows 4 tr .. +3 and columns sc + 16 j (the 16 lanes of a row
+  // group read 16 consecutive B rows, which fall in distinct LDS banks)
   {
     const int tr = tid >> 4, sc = tid & 15;
     float acc[4][4] = {};
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(NT) void k_ssd_chunk(SsdArgs a, float *__restrict__
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         cv[i] = *reinterpret_cast<const float4 *>(sC + (4 * tr + i) * PB + k);
-        bv[i] = *reinterpret_cast<const float4 *>(sB + (4 * sc + i) * PB + k);
+        bv[i] = *reinterpret_cast<const float4 *>(sB + (sc + 16 * i) * PB + k);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -138,15 +139,12 @@ __global__ __launch_bounds__(NT) void k_ssd_chunk(SsdArgs a, float *__restrict__
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = 4 * tr + i;
-      float4 m;
-      float *mp = &m.x;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int u = 4 * sc + j;
+        const int u = sc + 16 * j;
         const float arg = u <= t ? sCs[t] - sCs[u] : 0.0f;
-        mp[j] = u <= t ? expf(arg) * acc[i][j] * sDt[u] : 0.0f;
+        sM[t * PM + u] = u <= t ? expf(arg) * acc[i][j] * sDt[u] : 0.0f;
       }
-      *reinterpret_cast<float4 *>(sM + t * PM + 4 * sc) = m;
     }
   }
   __syncthreads();
@@ -189,8 +187,8 @@ __global__ __launch_bounds__(NT) void k_ssd_chunk(SsdArgs a, float *__restrict__
   }
 
   // chunk contribution Hc[p][k] = sum_s w_s x_s[p] B_s[k], w_s = e^{c_n - c_s} dt_s:
-  // P x N outputs, a 4 x 8 block per thread at P = 64, N = 128 (rows 4 pr .. +3,
-  // columns 8 kc .. +7); in general (4 rows) x (P N / (4 NT) columns)
+  // P x N outputs; a thread holds RPT rows x 8 columns, the columns 4 kc .. +3
+  // and N/2 + 4 kc .. +3 (consecutive lanes read consecutive 16 bytes)
   {
     constexpr int KC = N / 8;                 // 8-column groups
     constexpr int PR = NT / KC;               // row groups
@@ -201,8 +199,8 @@ __global__ __launch_bounds__(NT) void k_ssd_chunk(SsdArgs a, float *__restrict__
     float acc[RPT][8] = {};
     for (int u = 0; u < SC; ++u) {
       const float w = expf(cn - sCs[u]) * sDt[u];
-      const float4 b0 = *reinterpret_cast<const float4 *>(sB + u * PB + 8 * kc);
-      const float4 b1 = *reinterpret_cast<const float4 *>(sB + u * PB + 8 * kc + 4);
+      const float4 b0 = *reinterpret_cast<const float4 *>(sB + u * PB + 4 * kc);
+      const float4 b1 = *reinterpret_cast<const float4 *>(sB + u * PB + N / 2 + 4 * kc);
       const float bw[8] = {w * b0.x, w * b0.y, w * b0.z, w * b0.w,
                            w * b1.x, w * b1.y, w * b1.z, w * b1.w};
 #pragma unroll
@@ -215,9 +213,9 @@ __global__ __launch_bounds__(NT) void k_ssd_chunk(SsdArgs a, float *__restrict__
     float *blk = ws_block<P, N>(ws, s, h, c, a.H, a.n_chunks);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      float *row = blk + (RPT * pr + i) * N + 8 * kc;
+      float *row = blk + (RPT * pr + i) * N + 4 * kc;
       *reinterpret_cast<float4 *>(row) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
-      *reinterpret_cast<float4 *>(row + 4) =
+      *reinterpret_cast<float4 *>(row + N / 2) =
           make_float4(acc[i][4], acc[i][5], acc[i][6], acc[i][7]);
     }
     if (tid == 0) {
@@ -278,7 +276,7 @@ __global__ __launch_bounds__(NT) void k_ssd_out(SsdArgs a, const float *__restri
   for (int k = 0; k < N; k += 4) {
     float4 hv[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) hv[j] = *reinterpret_cast<const float4 *>(sH + (4 * pc + j) * PB + k);
+    for (int j = 0; j < 4; ++j) hv[j] = *reinterpret_cast<const float4 *>(sH + (pc + PCOLS * j) * PB + k);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const float4 cv = *reinterpret_cast<const float4 *>(sC + (RPT * tr + i) * PB + k);
@@ -293,11 +291,13 @@ __global__ __launch_bounds__(NT) void k_ssd_out(SsdArgs a, const float *__restri
   for (int i = 0; i < RPT; ++i) {
     const int t = RPT * tr + i;
     if (t < n) {
+      // columns pc + PCOLS j: consecutive lanes hit consecutive elements
       const float e = expf(sCs[t]);
-      float4 *yp = reinterpret_cast<float4 *>(yc + (int64_t)t * a.y_tok + 4 * pc);
-      const float4 yv = *yp;
-      *yp = make_float4(yv.x + e * acc[i].x, yv.y + e * acc[i].y, yv.z + e * acc[i].z,
-                        yv.w + e * acc[i].w);
+      float *yr = yc + (int64_t)t * a.y_tok + pc;
+      yr[0] += e * acc[i].x;
+      yr[PCOLS] += e * acc[i].y;
+      yr[2 * PCOLS] += e * acc[i].z;
+      yr[3 * PCOLS] += e * acc[i].w;
     }
   }
 }
