@@ -803,6 +803,49 @@ def test_chunked_varlen(S, lens, H, Hk, g_scale):
         assert ey < 2e-3 and es < 2e-3
 
 
+@pytest.mark.parametrize("S", [128, 64])
+def test_chunked_varlen_most_sequences(S):
+    # the largest packed batch a call takes (256 sequences), lengths 0 .. 150
+    # including empty ones and exact chunk multiples: every sequence bit for bit
+    # as a call on it alone (on a sample of sequences), and the empty ones untouched
+    n_seq, H, Hk = 256, 2, 1
+    rng = np.random.default_rng(7)
+    lens = [int(x) for x in rng.integers(0, 151, n_seq)]
+    lens[:6] = [0, 64, 128, 1, 63, 65]
+    base = "prefill" if S == 128 else "tiny"
+    inp = make_inputs(base, seed=103, S=S, head_dim=S, n_tok=max(lens), H=H, Hk=Hk,
+                      n_seq=n_seq, state_std=0.05)
+    wl = inp["wl"]
+    log_case("chunked_varlen_max", S=S, n_seq=n_seq, total=sum(lens))
+    pk = pack_varlen(inp, lens, oracle_g(inp))
+    st = on_dev(inp["state"]).clone()
+    y = torch.full((pk["cu"][-1], H, S), float("nan"), device=DEV)
+    gdn().gdn_recurrence_chunked_varlen(st, on_dev(pk["q"]), on_dev(pk["k"]), on_dev(pk["v"]),
+                                        on_dev(pk["g"]), on_dev(pk["beta"]), y, pk["cu"],
+                                        scale=wl.scale, chunk=64)
+    assert not torch.isnan(y).any()
+    for s in list(range(8)) + [100, 200, 255]:
+        n = lens[s]
+        st1 = on_dev(inp["state"][s:s + 1]).clone()
+        if n == 0:
+            assert bits_equal(st[s:s + 1], st1)
+            continue
+        sl = slice(pk["cu"][s], pk["cu"][s + 1])
+        y1 = torch.empty((1, n, H, S), device=DEV)
+        gdn().gdn_recurrence_chunked(st1, on_dev(pk["q"][sl])[None], on_dev(pk["k"][sl])[None],
+                                     on_dev(pk["v"][sl])[None], on_dev(pk["g"][sl])[None],
+                                     on_dev(pk["beta"][sl])[None], y1, scale=wl.scale, chunk=64)
+        assert bits_equal(y[sl], y1[0]) and bits_equal(st[s:s + 1], st1), s
+    for s in (3, 255):   # and against the sequential scan
+        if lens[s] == 0:
+            continue
+        sl = slice(pk["cu"][s], pk["cu"][s + 1])
+        y_ref, s_ref, _ = oracle.recurrence_seq(
+            inp["state"][s:s + 1], pk["q"][sl][None], pk["k"][sl][None], pk["v"][sl][None],
+            pk["g"][sl][None], pk["beta"][sl][None], wl.scale)
+        assert rel(y[sl][None], y_ref) < 2e-3 and rel(st[s:s + 1], s_ref) < 2e-3
+
+
 @pytest.mark.parametrize("S,H,Hk", [(128, 4, 2), (64, 3, 1), (32, 4, 4)])
 def test_chunked_varlen_bf16_inputs(S, H, Hk):
     # bf16 q, k, v are widened exactly on load: the call must equal, bit for
