@@ -40,6 +40,7 @@
 // a row-major LDS tile are read with ds_read_b64_tr_b16 (gfx950).
 #include <hip/hip_runtime.h>
 
+#include "bf16_frag.hpp"
 #include "gdn.h"
 #include "launch.hpp"
 
@@ -52,117 +53,6 @@ constexpr int DK = 128;          // key dimension (state rows)
 constexpr int DV = 128;          // value dimension (state columns)
 constexpr int NBLK = 16;         // value columns per scan workgroup
 constexpr int NVB = DV / NBLK;   // scan workgroups per head
-
-typedef short bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned short u16;
-
-struct Frag {
-  bf16x8 hi, lo;
-};
-
-__device__ __forceinline__ u16 bf16_bits(float x) {
-  return __builtin_bit_cast(u16, (__bf16)x);  // round to nearest even (v_cvt_pk_bf16_f32)
-}
-__device__ __forceinline__ float bf16_value(u16 b) {
-  return __builtin_bit_cast(float, (unsigned)b << 16);
-}
-// x = hi + lo + O(2^-16 |x|); x - hi is exact in fp32.
-__device__ __forceinline__ void split(float x, u16 &hi, u16 &lo) {
-  hi = bf16_bits(x);
-  lo = bf16_bits(x - bf16_value(hi));
-}
-
-__device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-// c += a*b with both operands split: hi*hi + hi*lo + lo*hi.
-__device__ __forceinline__ f32x4 mfma3(const Frag &a, const Frag &b, f32x4 c) {
-  c = mfma(a.lo, b.hi, c);
-  c = mfma(a.hi, b.lo, c);
-  c = mfma(a.hi, b.hi, c);
-  return c;
-}
-
-// ----------------------------------------------------------------------------- fragments
-// Standard fragment of a k-contiguous tile: row `row`, k = k + 8*kg + 0..7.
-__device__ __forceinline__ Frag frag(const u16 *hi, const u16 *lo, int pitch, int row, int k) {
-  Frag f;
-  f.hi = *reinterpret_cast<const bf16x8 *>(hi + row * pitch + k);
-  f.lo = *reinterpret_cast<const bf16x8 *>(lo + row * pitch + k);
-  return f;
-}
-
-// The permuted k order used wherever a fragment meets an accumulator tile:
-// slot e of lane (kg, l16) in k-step ks holds k = 32ks + 4kg + e (e < 4) and
-// k = 32ks + 16 + 4kg + (e - 4) (e >= 4).  Both operands of a product use it
-// (the sum over k does not depend on the order), and it is exactly the set of
-// rows an accumulator tile pair gives one lane, so accumulators turn into
-// fragments without any transpose.
-__device__ __forceinline__ int pi_k(int k0, int kg, int e) {
-  return k0 + 4 * kg + (e & 3) + ((e >> 2) << 4);
-}
-
-typedef short v4s __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ bf16x8 cat(v4s a, v4s b) {
-  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// Permuted fragment of a k-contiguous tile: row `row`, k in pi(k0, kg).
-__device__ __forceinline__ Frag frag_pi(const u16 *hi, const u16 *lo, int pitch, int row, int k0,
-                                        int kg) {
-  const int o = row * pitch + k0 + 4 * kg;
-  Frag f;
-  f.hi = cat(*reinterpret_cast<const v4s *>(hi + o), *reinterpret_cast<const v4s *>(hi + o + 16));
-  f.lo = cat(*reinterpret_cast<const v4s *>(lo + o), *reinterpret_cast<const v4s *>(lo + o + 16));
-  return f;
-}
-
-// Transposed permuted fragment of a row-major [k][n] LDS tile: column
-// nb + l16, rows pi(k0, kg), read with ds_read_b64_tr_b16.  In each 16-lane
-// group, lane j points at row k0 + 4kg + j/4 (then + 16), columns
-// nb + 4(j%4) .. +3; the transpose hands lane i column nb + i of those 4 rows.
-__device__ __forceinline__ v4s tr4(const u16 *p) {
-  typedef short v4s_lds __attribute__((ext_vector_type(4)));
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) v4s_lds *)(p));
-}
-__device__ __forceinline__ Frag frag_tr(const u16 *hi, const u16 *lo, int pitch, int k0, int nb,
-                                        int kg, int l16) {
-  const int o = (k0 + 4 * kg + (l16 >> 2)) * pitch + nb + 4 * (l16 & 3);
-  Frag f;
-  f.hi = cat(tr4(hi + o), tr4(hi + o + 16 * pitch));
-  f.lo = cat(tr4(lo + o), tr4(lo + o + 16 * pitch));
-  return f;
-}
-
-// Split 4 floats and store them as 4 consecutive bf16 in each plane.
-__device__ __forceinline__ void store4_split(u16 *hi, u16 *lo, float a, float b, float c, float d) {
-  u16 h[4], l[4];
-  split(a, h[0], l[0]);
-  split(b, h[1], l[1]);
-  split(c, h[2], l[2]);
-  split(d, h[3], l[3]);
-  *reinterpret_cast<uint2 *>(hi) =
-      make_uint2(h[0] | ((unsigned)h[1] << 16), h[2] | ((unsigned)h[3] << 16));
-  *reinterpret_cast<uint2 *>(lo) =
-      make_uint2(l[0] | ((unsigned)l[1] << 16), l[2] | ((unsigned)l[3] << 16));
-}
-
-// Split 8 floats into one 16-byte store per plane.
-__device__ __forceinline__ void store8_split(u16 *hi, u16 *lo, const float (&x)[8]) {
-  unsigned h[4], l[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    u16 h0, l0, h1, l1;
-    split(x[2 * e], h0, l0);
-    split(x[2 * e + 1], h1, l1);
-    h[e] = h0 | ((unsigned)h1 << 16);
-    l[e] = l0 | ((unsigned)l1 << 16);
-  }
-  *reinterpret_cast<uint4 *>(hi) = make_uint4(h[0], h[1], h[2], h[3]);
-  *reinterpret_cast<uint4 *>(lo) = make_uint4(l[0], l[1], l[2], l[3]);
-}
 
 // ----------------------------------------------------------------------------- workspace
 // Per (sequence, head, chunk), all offsets in bytes, each region 256-aligned.

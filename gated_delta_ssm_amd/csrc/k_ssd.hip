@@ -24,6 +24,7 @@
 // over LDS rows read as float4.
 #include <hip/hip_runtime.h>
 
+#include "bf16_frag.hpp"
 #include "gdn.h"
 #include "launch.hpp"
 
@@ -302,6 +303,182 @@ __global__ __launch_bounds__(NT) void k_ssd_out(SsdArgs a, const float *__restri
   }
 }
 
+// ----------------------------------------------------------------------------- MFMA form
+// The same three launches for head_dim 64 and state 128 with the dense
+// products on v_mfma_f32_16x16x32_bf16, each fp32 operand split into bf16
+// hi + lo (hi*hi + hi*lo + lo*hi, fp32 accumulation; ~2^-16 relative per
+// product).  8 waves; LDS tiles are row-major bf16 hi/lo planes.
+constexpr int MP = 64, MN = 128;          // head_dim, state
+constexpr int MNT = 512;                  // threads
+constexpr int PXb = MP + 8, PBb = MN + 8, PMb = SC + 8;   // pitches (bf16 elements)
+
+// rows [0, n) of a [ROWS][W] fp32 tile (row stride `tok`), each scaled by
+// scale[r] (or not), into bf16 hi/lo planes of pitch PW; rows n .. ROWS-1 zero
+template <int W, int ROWS, int PW>
+__device__ __forceinline__ void split_rows(u16 *hi, u16 *lo, const float *src, int64_t tok, int n,
+                                           const float *scale) {
+  constexpr int V = W / 4;
+  for (int e = threadIdx.x; e < ROWS * V; e += MNT) {
+    const int r = e / V, c4 = (e - r * V) * 4;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (r < n) {
+      v = *reinterpret_cast<const float4 *>(src + (int64_t)r * tok + c4);
+      if (scale) {
+        const float f = scale[r];
+        v = make_float4(f * v.x, f * v.y, f * v.z, f * v.w);
+      }
+    }
+    store4_split(hi + r * PW + c4, lo + r * PW + c4, v.x, v.y, v.z, v.w);
+  }
+}
+
+__global__ __launch_bounds__(MNT) void k_ssd_chunk_mma(SsdArgs a, float *__restrict__ ws) {
+  __shared__ __attribute__((aligned(16))) u16 sXh[SC * PXb], sXl[SC * PXb];
+  __shared__ __attribute__((aligned(16))) u16 sBh[SC * PBb], sBl[SC * PBb];
+  __shared__ __attribute__((aligned(16))) u16 sCh[SC * PBb], sCl[SC * PBb];   // C, then w B
+  __shared__ __attribute__((aligned(16))) u16 sMh[SC * PMb], sMl[SC * PMb];
+  __shared__ float sDt[SC], sCs[SC], sW[SC];
+  const int c = blockIdx.x, h = blockIdx.y, s = blockIdx.z, tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
+  const int gi = h / (a.H / a.G);
+  const int t0 = c * SC, n = min(SC, a.n_tok - t0);
+  const float A = -expf(a.A_log[h]);
+  chunk_dt(a.dt_raw, s * a.dt_seq + (int64_t)t0 * a.dt_tok, a.dt_tok, h, n, a.dt_bias[h], A,
+           a.dt_min, a.dt_max, sDt, sCs);
+  const float *xc = a.x + s * a.x_seq + (int64_t)t0 * a.x_tok + (int64_t)h * MP;
+  const float *bc = a.Bm + s * a.bc_seq + (int64_t)t0 * a.bc_tok + (int64_t)gi * MN;
+  const float *cc = a.Cm + s * a.bc_seq + (int64_t)t0 * a.bc_tok + (int64_t)gi * MN;
+  split_rows<MP, SC, PXb>(sXh, sXl, xc, a.x_tok, n, nullptr);
+  split_rows<MN, SC, PBb>(sBh, sBl, bc, a.bc_tok, n, nullptr);
+  split_rows<MN, SC, PBb>(sCh, sCl, cc, a.bc_tok, n, nullptr);
+  {   // M starts at zero (its upper tiles stay so)
+    uint4 *z0 = reinterpret_cast<uint4 *>(sMh), *z1 = reinterpret_cast<uint4 *>(sMl);
+    for (int e = tid; e < SC * PMb * 2 / 16; e += MNT) z0[e] = z1[e] = make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();
+  if (tid < SC) sW[tid] = expf(sCs[SC - 1] - sCs[tid]) * sDt[tid];   // w_s = e^{c_n - c_s} dt_s
+
+  // M[t][s] = e^{c_t - c_s} (C_t . B_s) dt_s, lower 16x16 tiles (ti >= tj):
+  // 10 tiles, wave w takes tiles w and w + 8
+  for (int jt = w; jt < 10; jt += 8) {
+    const int ti = jt < 1 ? 0 : jt < 3 ? 1 : jt < 6 ? 2 : 3, tj = jt - ti * (ti + 1) / 2;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < MN / 32; ++ks)
+      acc = mfma3(frag(sCh, sCl, PBb, 16 * ti + l16, 32 * ks + 8 * kg),
+                  frag(sBh, sBl, PBb, 16 * tj + l16, 32 * ks + 8 * kg), acc);
+    const int u = 16 * tj + l16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * ti + 4 * kg + r;
+      const float arg = u <= t ? sCs[t] - sCs[u] : 0.0f;
+      const float m = u <= t ? expf(arg) * acc[r] * sDt[u] : 0.0f;
+      u16 hh, ll;
+      split(m, hh, ll);
+      sMh[t * PMb + u] = hh;
+      sMl[t * PMb + u] = ll;
+    }
+  }
+  __syncthreads();   // M complete; C no longer needed
+  // w_s B_s into C's planes, for the state contribution
+  split_rows<MN, SC, PBb>(sCh, sCl, bc, a.bc_tok, n, sW);
+
+  // y_t (intra-chunk part) = sum_s M[t][s] x_s + D x_t: 16 tiles (t, p), wave w
+  // takes token tile w & 3 and value tiles 2 (w >> 2), +1
+  {
+    const int ti = w & 3;
+    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < SC / 32; ++ks) {
+      const Frag fm = frag_pi(sMh, sMl, PMb, 16 * ti + l16, 32 * ks, kg);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[j] = mfma3(fm, frag_tr(sXh, sXl, PXb, 32 * ks, 16 * (2 * (w >> 2) + j), kg, l16),
+                       acc[j]);
+    }
+    const float Dh = a.D[h];
+    float *yc = a.y + s * a.y_seq + (int64_t)t0 * a.y_tok + (int64_t)h * MP;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int p = 16 * (2 * (w >> 2) + j) + l16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * ti + 4 * kg + r;
+        if (t < n) yc[(int64_t)t * a.y_tok + p] = acc[j][r] + Dh * xc[(int64_t)t * a.x_tok + p];
+      }
+    }
+  }
+  __syncthreads();   // w B in LDS
+
+  // state contribution Hc[p][k] = sum_s x_s[p] w_s B_s[k]: 4 x 8 tiles (p, k),
+  // wave w takes value tile w & 3 and state tiles 4 (w >> 2) .. +3
+  {
+    const int tp = w & 3;
+    f32x4 acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < SC / 32; ++ks) {
+      const Frag fx = frag_tr(sXh, sXl, PXb, 32 * ks, 16 * tp, kg, l16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[j] = mfma3(fx, frag_tr(sCh, sCl, PBb, 32 * ks, 16 * (4 * (w >> 2) + j), kg, l16),
+                       acc[j]);
+    }
+    float *blk = ws_block<MP, MN>(ws, s, h, c, a.H, a.n_chunks);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = 16 * (4 * (w >> 2) + j) + l16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) blk[(16 * tp + 4 * kg + r) * MN + k] = acc[j][r];
+    }
+    if (tid == 0) {
+      const size_t blocks = (size_t)gridDim.z * a.H * a.n_chunks * (MP * MN);
+      *ws_decay(ws, blocks, s, h, c, a.H, a.n_chunks) = expf(sCs[SC - 1]);
+    }
+  }
+}
+
+// y_t += e^{c_t} sum_k C_t[k] h0[p][k]: 16 tiles (t, p), wave w takes token
+// tile w & 3 and value tiles 2 (w >> 2), +1
+__global__ __launch_bounds__(MNT) void k_ssd_out_mma(SsdArgs a, const float *__restrict__ ws) {
+  __shared__ __attribute__((aligned(16))) u16 sCh[SC * PBb], sCl[SC * PBb];
+  __shared__ __attribute__((aligned(16))) u16 sHh[MP * PBb], sHl[MP * PBb];
+  __shared__ float sDt[SC], sCs[SC];
+  const int c = blockIdx.x, h = blockIdx.y, s = blockIdx.z, tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
+  const int gi = h / (a.H / a.G);
+  const int t0 = c * SC, n = min(SC, a.n_tok - t0);
+  const float A = -expf(a.A_log[h]);
+  chunk_dt(a.dt_raw, s * a.dt_seq + (int64_t)t0 * a.dt_tok, a.dt_tok, h, n, a.dt_bias[h], A,
+           a.dt_min, a.dt_max, sDt, sCs);
+  split_rows<MN, SC, PBb>(sCh, sCl, a.Cm + s * a.bc_seq + (int64_t)t0 * a.bc_tok +
+                                        (int64_t)gi * MN, a.bc_tok, n, nullptr);
+  split_rows<MN, MP, PBb>(sHh, sHl, ws_block<MP, MN>(const_cast<float *>(ws), s, h, c, a.H,
+                                                      a.n_chunks), MN, MP, nullptr);
+  __syncthreads();
+  const int ti = w & 3;
+  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int ks = 0; ks < MN / 32; ++ks) {
+    const Frag fc = frag(sCh, sCl, PBb, 16 * ti + l16, 32 * ks + 8 * kg);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      acc[j] = mfma3(fc, frag(sHh, sHl, PBb, 16 * (2 * (w >> 2) + j) + l16, 32 * ks + 8 * kg),
+                     acc[j]);
+  }
+  float *yc = a.y + s * a.y_seq + (int64_t)t0 * a.y_tok + (int64_t)h * MP;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int p = 16 * (2 * (w >> 2) + j) + l16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * ti + 4 * kg + r;
+      if (t < n) yc[(int64_t)t * a.y_tok + p] += expf(sCs[t]) * acc[j][r];
+    }
+  }
+}
+
 template <int P, int N>
 int run_ssd(const SsdLaunch &l, hipStream_t stream) {
   const int nc = (l.n_tok + SC - 1) / SC;
@@ -321,6 +498,23 @@ int run_ssd(const SsdLaunch &l, hipStream_t stream) {
                        static_cast<const float *>(ws));
 }
 
+int run_ssd_mma(const SsdLaunch &l, hipStream_t stream) {
+  const int nc = (l.n_tok + SC - 1) / SC;
+  SsdArgs a{l.x,     l.Bm,     l.Cm,     l.dt_raw, l.A_log,  l.D,    l.dt_bias,
+            l.x_tok, l.x_seq,  l.bc_tok, l.bc_seq, l.dt_tok, l.dt_seq, l.y_tok,
+            l.y_seq, l.y,      l.n_tok,  l.H,      l.G,      nc,     l.dt_min,
+            l.dt_max};
+  float *ws = static_cast<float *>(l.ws);
+  const dim3 grid_c((unsigned)nc, (unsigned)l.H, (unsigned)l.n_seq);
+  int rc = launch_kernel(k_ssd_chunk_mma, grid_c, dim3(MNT), 0, stream, a, ws);
+  if (rc != GDN_OK) return rc;
+  rc = launch_kernel(k_ssd_state<MP, MN>, dim3(MP * MN / 4 / NT, (unsigned)l.H, (unsigned)l.n_seq),
+                     dim3(NT), 0, stream, l.state, l.st_seq, ws, l.n_seq, l.H, nc);
+  if (rc != GDN_OK) return rc;
+  return launch_kernel(k_ssd_out_mma, grid_c, dim3(MNT), 0, stream, a,
+                       static_cast<const float *>(ws));
+}
+
 }  // namespace
 
 size_t ssd_workspace_bytes(int n_seq, int n_tok, int H, int P, int N) {
@@ -330,7 +524,7 @@ size_t ssd_workspace_bytes(int n_seq, int n_tok, int H, int P, int N) {
 }
 
 int launch_ssd(const SsdLaunch &l, hipStream_t stream) {
-  if (l.P == 64 && l.N == 128) return run_ssd<64, 128>(l, stream);
+  if (l.P == 64 && l.N == 128) return run_ssd_mma(l, stream);
   if (l.P == 64 && l.N == 64) return run_ssd<64, 64>(l, stream);
   if (l.P == 32 && l.N == 128) return run_ssd<32, 128>(l, stream);
   if (l.P == 32 && l.N == 64) return run_ssd<32, 64>(l, stream);
