@@ -1129,3 +1129,63 @@ def test_total_decay_forgets_the_state(path):
     tol = 1e-4 if path == "decode" else 2e-3
     assert rel(st, s_ref) < tol
     assert rel(y[:, -1:], y_ref) < tol
+
+
+def test_chunked_prefill_graph_replay_matches_eager():
+    # a packed two-prompt chunked call (workspace passed in) and the Mamba-2
+    # scan captured once into a HIP graph, replayed with eager work between
+    # replays: every replay equals the eager calls bit for bit
+    inp = make_inputs("prefill", seed=107, n_tok=200, H=4, Hk=2, n_seq=2, state_std=0.05)
+    wl = inp["wl"]
+    log_case("graph_replay_chunked")
+    lens = [200, 77]
+    pk = pack_varlen(inp, lens, oracle_g(inp))
+    q, k, v, g, beta = (on_dev(pk[x]) for x in ("q", "k", "v", "g", "beta"))
+    st0 = on_dev(inp["state"])
+    st = st0.clone()
+    y = torch.empty(sum(lens), wl.H, wl.S, device=DEV)
+    ws = torch.empty(gdn().gdn_recurrence_chunked_varlen_workspace_bytes(2, sum(lens), wl.H,
+                                                                       wl.Hk, wl.S, 64),
+                     dtype=torch.uint8, device=DEV)
+    mi = make_mamba2_inputs(1, 150, 4, 2, 64, 128, seed=109, state_std=0.1)
+    mc = {kk: on_dev(vv) for kk, vv in mi.items() if isinstance(vv, torch.Tensor)}
+    mst, my = mc["state"].clone(), torch.empty_like(mc["x"])
+    mws = torch.empty(gdn().gdn_mamba2_ssd_workspace_bytes(1, 150, 4, 64, 128, 64),
+                      dtype=torch.uint8, device=DEV)
+
+    def run():
+        gdn().gdn_recurrence_chunked_varlen(st, q, k, v, g, beta, y, pk["cu"], scale=wl.scale,
+                                            chunk=64, workspace=ws)
+        gdn().gdn_mamba2_ssd_chunked(mst, mc["x"], mc["B"], mc["C"], mc["dt_raw"], mc["A_log"],
+                                     mc["D"], mc["dt_bias"], my, dt_min=mi["dt_min"],
+                                     dt_max=mi["dt_max"], workspace=mws)
+
+    def reset():
+        st.copy_(st0)
+        mst.copy_(mc["state"])
+
+    reset()
+    run()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (y, st, my, mst)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        reset()
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    reset()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for _ in range(3):
+        reset()
+        y.fill_(float("nan"))
+        my.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((y, st, my, mst), ref):
+            assert bits_equal(a, b)
