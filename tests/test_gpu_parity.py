@@ -932,7 +932,10 @@ def run_ssd(inp, pad=0):
     (2, 100, 4, 2, 32, 64, 0.2, 8),
     (3, 1, 6, 3, 64, 64, 0.2, 0),
     (1, 65, 2, 1, 32, 128, 0.1, 4),
-    (2, 200, 8, 4, 64, 128, 0.05, 0)])
+    (2, 200, 8, 4, 64, 128, 0.05, 0),
+    (1, 1, 2, 1, 64, 128, 0.2, 0),           # the MFMA form: one position,
+    (1, 65, 3, 3, 64, 128, 0.1, 0),          # a one-position last chunk,
+    (2, 130, 4, 2, 64, 128, 0.2, 8)])        # strided rows with poisoned gaps
 def test_mamba2_ssd_chunked(n, T, H, G, P, N, state_std, pad):
     inp = make_mamba2_inputs(n, T, H, G, P, N, seed=97, state_std=state_std)
     log_case("mamba2_ssd", n=n, T=T, H=H, G=G, P=P, N=N)
