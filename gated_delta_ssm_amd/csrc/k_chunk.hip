@@ -734,6 +734,28 @@ __device__ __forceinline__ HeadChunks head_chunks(const VarTab &tab, int s, int 
                     tab.tok0[s + 1] - tab.tok0[s], tab.tok0[s]};
 }
 
+// XCD-aware order of the scan's workgroups.  Consecutive workgroup ids go to
+// different XCDs (id % 8).  The `per` workgroups of one (sequence, head) unit
+// get ids on one XCD, so they share its L2.  When the unit count is a multiple
+// of 8, consecutive units are interleaved over the 8 XCDs, so every XCD holds
+// an even share of every sequence: dealing each XCD a contiguous run of units
+// would give it whole sequences, and with sequences of different lengths the
+// XCD holding the longest would run long after the others are idle.
+// Otherwise units are dealt in contiguous runs (XCD x < r of nwg = 8q + r
+// taking q + 1 workgroups, the others q).
+__device__ __forceinline__ void xcd_order(int b, int nwg, int per, int &sh, int &sub) {
+  const int xcd = b % 8, idx = b / 8;
+  if ((nwg / per) % 8 == 0) {
+    sh = (idx / per) * 8 + xcd;
+    sub = idx % per;
+  } else {
+    const int q8 = nwg / 8, r8 = nwg % 8;
+    const int unit = (xcd < r8 ? xcd * (q8 + 1) : r8 * (q8 + 1) + (xcd - r8) * q8) + idx;
+    sh = unit / per;
+    sub = unit % per;
+  }
+}
+
 constexpr int SPB = 24;   // pitch (bf16) of the [128][16] S tile and the [64][16] U tile
 
 __device__ __forceinline__ void scan_chunk(const ChunkOps &o, f32x4 &st, u16 *ssh, u16 *ssl,
@@ -771,11 +793,10 @@ __global__ __launch_bounds__(512) void k_chunk_scan(
   __shared__ __attribute__((aligned(16))) u16 ssh[DK * SPB], ssl[DK * SPB];
   __shared__ __attribute__((aligned(16))) u16 suh[CH * SPB], sul[CH * SPB];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
-  // XCD-aware order: consecutive workgroup ids go to different XCDs, so map
-  // them so that the 8 blocks of one head land on the same XCD (shared L2).
-  const int nwg = gridDim.x, per_xcd = nwg / 8;
-  const int unit = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  const int blk = unit % NVB, sh = unit / NVB, h = sh % H, s = sh / H;
+  // the 8 value blocks of one head on one XCD (xcd_order)
+  int sh, blk;
+  xcd_order(blockIdx.x, gridDim.x, NVB, sh, blk);
+  const int h = sh % H, s = sh / H;
   const HeadChunks hc = head_chunks(tab, s, h, H, n_tok, n_chunks);
 
   // state element (value j = 16 blk + 4kg + r, key i = 16w + l16), value-major
@@ -840,13 +861,11 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_chunk_scan_pair(
   __shared__ __attribute__((aligned(16))) unsigned char ops[OPS_WQ + OPS_K];
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
   const int grp = tid >> 9, w = (tid >> 6) & 7;
-  // XCD-aware order as in k_chunk_scan, so the 4 workgroups of a head share an
-  // L2; the grid (4 per head) need not be a multiple of 8: XCD x < r of
-  // nwg = 8q + r takes q + 1 consecutive units, the others q
-  const int nwg = gridDim.x, q8 = nwg / 8, r8 = nwg % 8;
-  const int xcd = blockIdx.x % 8, idx = blockIdx.x / 8;
-  const int unit = (xcd < r8 ? xcd * (q8 + 1) : r8 * (q8 + 1) + (xcd - r8) * q8) + idx;
-  const int pair = unit % (NVB / 2), sh = unit / (NVB / 2), h = sh % H, s = sh / H;
+  // the 4 workgroups of one head on one XCD (xcd_order; the grid, 4 per head,
+  // need not be a multiple of 8)
+  int sh, pair;
+  xcd_order(blockIdx.x, gridDim.x, NVB / 2, sh, pair);
+  const int h = sh % H, s = sh / H;
   const int blk = 2 * pair + grp;
   const HeadChunks hc = head_chunks(tab, s, h, H, n_tok, n_chunks);
 
