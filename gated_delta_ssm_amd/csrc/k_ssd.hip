@@ -380,8 +380,20 @@ __global__ __launch_bounds__(MNT) void k_ssd_chunk_mma(SsdArgs a, float *__restr
     }
   }
   __syncthreads();   // M complete; C no longer needed
-  // w_s B_s into C's planes, for the state contribution
-  split_rows<MN, SC, PBb>(sCh, sCl, bc, a.bc_tok, n, sW);
+  // w_s B_s into C's planes, for the state contribution, from the B planes
+  // already in LDS (hi + lo is B to 2^-16 relative; rows past n are zero)
+  for (int e = tid; e < SC * MN / 4; e += MNT) {
+    const int r = e / (MN / 4), c4 = (e - r * (MN / 4)) * 4;
+    const uint2 hb = *reinterpret_cast<const uint2 *>(sBh + r * PBb + c4);
+    const uint2 lb = *reinterpret_cast<const uint2 *>(sBl + r * PBb + c4);
+    const float f = sW[r];
+    float v[4];
+    v[0] = bf16_value((u16)(hb.x & 0xffffu)) + bf16_value((u16)(lb.x & 0xffffu));
+    v[1] = bf16_value((u16)(hb.x >> 16)) + bf16_value((u16)(lb.x >> 16));
+    v[2] = bf16_value((u16)(hb.y & 0xffffu)) + bf16_value((u16)(lb.y & 0xffffu));
+    v[3] = bf16_value((u16)(hb.y >> 16)) + bf16_value((u16)(lb.y >> 16));
+    store4_split(sCh + r * PBb + c4, sCl + r * PBb + c4, f * v[0], f * v[1], f * v[2], f * v[3]);
+  }
 
   // y_t (intra-chunk part) = sum_s M[t][s] x_s + D x_t: 16 tiles (t, p), wave w
   // takes token tile w & 3 and value tiles 2 (w >> 2), +1
