@@ -145,35 +145,46 @@ constexpr int L_G = L_S + 4 * 16 * XP * 4;
 constexpr int L_TOTAL = L_G + 4 * CH * 4;
 static_assert(L_TOTAL <= 160 * 1024, "phase A LDS fits one CU");
 
-// Lower 16x16 tiles of K K^T (tile index jt < 10: A = beta_t e^{G_t - G_s} k_t.k_s,
-// strictly lower) and of Q K^T (jt >= 10: e^{G_t - G_s} q_t.k_s, diagonal
-// included, stored as bf16 hi/lo): this wave's NJ tiles w, w + 8, w + 16.
+// Lower 16x16 tiles of K K^T (A = beta_t e^{G_t - G_s} k_t.k_s, strictly lower)
+// and of Q K^T (e^{G_t - G_s} q_t.k_s, diagonal included, stored as bf16 hi/lo):
+// a wave takes one or two tile positions (ti, tj) and both products at each,
+// so each k-step reads the K fragment of column tile tj once for two tiles
+// (and the row fragments once when a wave's two positions share ti).
 template <int NJ>
 __device__ __forceinline__ void lower_tiles(int w, const u16 *kh, const u16 *klo, const u16 *qh,
                                             const u16 *qlo, float *sA, u16 *lqh, u16 *lql,
                                             const float *sG, const float *sBeta, int l16, int kg) {
+  // positions: waves 0, 1 take (3,0),(3,1) and (3,2),(3,3); waves 2..7 one of
+  // (0,0),(1,0),(1,1),(2,0),(2,1),(2,2); each position gives a K K^T and a Q K^T
+  // tile, which share the K fragment of column tile tj and the row tile ti
   bool qk[NJ];
   int ti[NJ], tj[NJ];
   f32x4 acc[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const int job = w + 8 * j;
-    qk[j] = job >= 10;
-    const int jt = qk[j] ? job - 10 : job;
-    ti[j] = jt < 1 ? 0 : jt < 3 ? 1 : jt < 6 ? 2 : 3;   // lower-tile index -> (ti, tj)
-    tj[j] = jt - ti[j] * (ti[j] + 1) / 2;
+    const int pos = w < 2 ? 2 * w + (j >> 1) : w - 2;
+    const int pti = w < 2 ? 3 : (pos < 1 ? 0 : pos < 3 ? 1 : 2);
+    const int ptj = w < 2 ? pos : pos - pti * (pti + 1) / 2;
+    qk[j] = (j & 1) != 0;
+    ti[j] = pti;
+    tj[j] = ptj;
     acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    Frag fa[NJ], fb[NJ];
+    Frag fk[NJ / 2], fq[NJ / 2], fb[NJ / 2];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      fa[j] = frag(qk[j] ? qh : kh, qk[j] ? qlo : klo, PR, 16 * ti[j] + l16, 32 * ks + 8 * kg);
-      fb[j] = frag(kh, klo, PR, 16 * tj[j] + l16, 32 * ks + 8 * kg);
+    for (int p = 0; p < NJ / 2; ++p) {
+      fb[p] = frag(kh, klo, PR, 16 * tj[2 * p] + l16, 32 * ks + 8 * kg);
+      if (ti[2 * p] == tj[2 * p]) fk[p] = fb[p];
+      else fk[p] = frag(kh, klo, PR, 16 * ti[2 * p] + l16, 32 * ks + 8 * kg);
+      fq[p] = frag(qh, qlo, PR, 16 * ti[2 * p] + l16, 32 * ks + 8 * kg);
     }
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[j] = mfma3(fa[j], fb[j], acc[j]);
+    for (int p = 0; p < NJ / 2; ++p) {
+      acc[2 * p] = mfma3(fk[p], fb[p], acc[2 * p]);
+      acc[2 * p + 1] = mfma3(fq[p], fb[p], acc[2 * p + 1]);
+    }
   }
   // e^{G_t - G_s} is the hardware base-2 exponential of (G_t - G_s) log2(e),
   // with the argument masked to 0 above the diagonal before it is taken; every
@@ -476,11 +487,12 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
   load_kq(in, nx, tid, kr, qr);
   __syncthreads();
 
-  // S2a. K K^T and Q K^T on the 10 lower tiles each: 20 tiles, wave w takes
-  // tiles w, w + 8 (and w + 16 for w < 4), all at once, so their MFMA chains
-  // interleave instead of running back to back
-  if (w < 4) {
-    lower_tiles<3>(w, kh, klo, qh, qlo, sA, lqh, lql, sG, sBeta, l16, kg);
+  // S2a. K K^T and Q K^T on the 10 lower tile positions each: 20 tiles; waves
+  // 0 and 1 take two positions of row tile 3 (four tiles), waves 2..7 one of
+  // the other six positions (two tiles), each wave's tiles all at once so their
+  // MFMA chains interleave
+  if (w < 2) {
+    lower_tiles<4>(w, kh, klo, qh, qlo, sA, lqh, lql, sG, sBeta, l16, kg);
   } else {
     lower_tiles<2>(w, kh, klo, qh, qlo, sA, lqh, lql, sG, sBeta, l16, kg);
   }
