@@ -426,6 +426,17 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
   float *sG = reinterpret_cast<float *>(smem + L_G);
   float *sBeta = sG + CH, *sEG = sG + 2 * CH, *sEGn = sG + 3 * CH;
 
+  // (L o QK^T) and A, which lie back to back, are cleared once: every item
+  // writes every entry of their lower 16x16 tiles (zeros above the diagonal
+  // included) and nothing writes their upper tiles, which must stay zero (the
+  // first item's first barrier orders this before any use).  16-byte stores.
+  {
+    static_assert(L_A == L_L + TILE64 && (TILE64 + CH * PA * 4) % 16 == 0 && L_L % 16 == 0,
+                  "one contiguous region");
+    uint4 *zp = reinterpret_cast<uint4 *>(smem + L_L);
+    for (int e = threadIdx.x; e < (TILE64 + CH * PA * 4) / 16; e += 512)
+      zp[e] = make_uint4(0, 0, 0, 0);
+  }
   // the grid never exceeds n_items, so every workgroup has a first item
   PrepItem it = prep_item(blockIdx.x, n_chunks, H, Hk, n_tok, tab);
   float gv, bv;
@@ -452,7 +463,7 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
   const TIN *qc = q + it.s * qk_seq + (int64_t)it.tb * qk_tok + it.hk * DK;
   unsigned char *wc = ws + it.slot * WS_CHUNK;
 
-  // S0. gate cumsum (wave 0) and cleared tiles
+  // S0. gate cumsum (wave 0)
   if (w == 0) {
     float x = lane < n ? gv : 0.0f;
     const float b = lane < n ? bv : 0.0f;
@@ -468,14 +479,6 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
     sEGn[lane] = expf(gn - x);
   }
   load_gb(in, nx, lane, gv, bv);
-  // zero (L o QK^T) and A, which lie back to back: their upper triangles stay
-  // zero.  16-byte stores.
-  {
-    static_assert(L_A == L_L + TILE64 && (TILE64 + CH * PA * 4) % 16 == 0 && L_L % 16 == 0,
-                  "one contiguous region");
-    uint4 *zp = reinterpret_cast<uint4 *>(smem + L_L);
-    for (int e = tid; e < (TILE64 + CH * PA * 4) / 16; e += 512) zp[e] = make_uint4(0, 0, 0, 0);
-  }
   // S1. K, Q rows -> LDS (bf16 hi/lo)
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
