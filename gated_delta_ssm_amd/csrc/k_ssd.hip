@@ -312,23 +312,31 @@ constexpr int MP = 64, MN = 128;          // head_dim, state
 constexpr int MNT = 512;                  // threads
 constexpr int PXb = MP + 8, PBb = MN + 8, PMb = SC + 8;   // pitches (bf16 elements)
 
-// rows [0, n) of a [ROWS][W] fp32 tile (row stride `tok`), each scaled by
-// scale[r] (or not), into bf16 hi/lo planes of pitch PW; rows n .. ROWS-1 zero
-template <int W, int ROWS, int PW>
-__device__ __forceinline__ void split_rows(u16 *hi, u16 *lo, const float *src, int64_t tok, int n,
-                                           const float *scale) {
+// A [ROWS][W] fp32 tile (row stride `tok`) moves to LDS in two steps, so a
+// thread's loads are all in flight before the first is used: rows [0, n) into
+// registers (zeros past n), then split into bf16 hi/lo planes of pitch PW.
+template <int W, int ROWS>
+constexpr int rows_per_thread() { return ROWS * (W / 4) / MNT; }
+template <int W, int ROWS>
+__device__ __forceinline__ void fetch_rows(const float *src, int64_t tok, int n,
+                                           float4 (&v)[rows_per_thread<W, ROWS>()]) {
   constexpr int V = W / 4;
-  for (int e = threadIdx.x; e < ROWS * V; e += MNT) {
-    const int r = e / V, c4 = (e - r * V) * 4;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (r < n) {
-      v = *reinterpret_cast<const float4 *>(src + (int64_t)r * tok + c4);
-      if (scale) {
-        const float f = scale[r];
-        v = make_float4(f * v.x, f * v.y, f * v.z, f * v.w);
-      }
-    }
-    store4_split(hi + r * PW + c4, lo + r * PW + c4, v.x, v.y, v.z, v.w);
+  static_assert(ROWS * V % MNT == 0, "whole passes");
+#pragma unroll
+  for (int i = 0; i < rows_per_thread<W, ROWS>(); ++i) {
+    const int e = threadIdx.x + i * MNT, r = e / V, c4 = (e - r * V) * 4;
+    v[i] = r < n ? *reinterpret_cast<const float4 *>(src + (int64_t)r * tok + c4)
+                 : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+template <int W, int ROWS, int PW>
+__device__ __forceinline__ void put_rows(u16 *hi, u16 *lo,
+                                         const float4 (&v)[rows_per_thread<W, ROWS>()]) {
+  constexpr int V = W / 4;
+#pragma unroll
+  for (int i = 0; i < rows_per_thread<W, ROWS>(); ++i) {
+    const int e = threadIdx.x + i * MNT, r = e / V, c4 = (e - r * V) * 4;
+    store4_split(hi + r * PW + c4, lo + r * PW + c4, v[i].x, v[i].y, v[i].z, v[i].w);
   }
 }
 
@@ -348,9 +356,16 @@ __global__ __launch_bounds__(MNT) void k_ssd_chunk_mma(SsdArgs a, float *__restr
   const float *xc = a.x + s * a.x_seq + (int64_t)t0 * a.x_tok + (int64_t)h * MP;
   const float *bc = a.Bm + s * a.bc_seq + (int64_t)t0 * a.bc_tok + (int64_t)gi * MN;
   const float *cc = a.Cm + s * a.bc_seq + (int64_t)t0 * a.bc_tok + (int64_t)gi * MN;
-  split_rows<MP, SC, PXb>(sXh, sXl, xc, a.x_tok, n, nullptr);
-  split_rows<MN, SC, PBb>(sBh, sBl, bc, a.bc_tok, n, nullptr);
-  split_rows<MN, SC, PBb>(sCh, sCl, cc, a.bc_tok, n, nullptr);
+  {
+    float4 vx[rows_per_thread<MP, SC>()], vb[rows_per_thread<MN, SC>()],
+        vcc[rows_per_thread<MN, SC>()];
+    fetch_rows<MP, SC>(xc, a.x_tok, n, vx);
+    fetch_rows<MN, SC>(bc, a.bc_tok, n, vb);
+    fetch_rows<MN, SC>(cc, a.bc_tok, n, vcc);
+    put_rows<MP, SC, PXb>(sXh, sXl, vx);
+    put_rows<MN, SC, PBb>(sBh, sBl, vb);
+    put_rows<MN, SC, PBb>(sCh, sCl, vcc);
+  }
   {   // M starts at zero (its upper tiles stay so)
     uint4 *z0 = reinterpret_cast<uint4 *>(sMh), *z1 = reinterpret_cast<uint4 *>(sMl);
     for (int e = tid; e < SC * PMb * 2 / 16; e += MNT) z0[e] = z1[e] = make_uint4(0, 0, 0, 0);
@@ -464,10 +479,15 @@ __global__ __launch_bounds__(MNT) void k_ssd_out_mma(SsdArgs a, const float *__r
   const float A = -expf(a.A_log[h]);
   chunk_dt(a.dt_raw, s * a.dt_seq + (int64_t)t0 * a.dt_tok, a.dt_tok, h, n, a.dt_bias[h], A,
            a.dt_min, a.dt_max, sDt, sCs);
-  split_rows<MN, SC, PBb>(sCh, sCl, a.Cm + s * a.bc_seq + (int64_t)t0 * a.bc_tok +
-                                        (int64_t)gi * MN, a.bc_tok, n, nullptr);
-  split_rows<MN, MP, PBb>(sHh, sHl, ws_block<MP, MN>(const_cast<float *>(ws), s, h, c, a.H,
-                                                      a.n_chunks), MN, MP, nullptr);
+  {
+    float4 vcc[rows_per_thread<MN, SC>()], vh[rows_per_thread<MN, MP>()];
+    fetch_rows<MN, SC>(a.Cm + s * a.bc_seq + (int64_t)t0 * a.bc_tok + (int64_t)gi * MN,
+                       a.bc_tok, n, vcc);
+    fetch_rows<MN, MP>(ws_block<MP, MN>(const_cast<float *>(ws), s, h, c, a.H, a.n_chunks), MN,
+                       MP, vh);
+    put_rows<MN, SC, PBb>(sCh, sCl, vcc);
+    put_rows<MN, MP, PBb>(sHh, sHl, vh);
+  }
   __syncthreads();
   const int ti = w & 3;
   f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
