@@ -340,10 +340,40 @@ __device__ __forceinline__ void put_rows(u16 *hi, u16 *lo,
   }
 }
 
+// The MN / 32 k-step fragments of row `row` of a [SC][MN] fp32 tile in global
+// memory (zero past row n): lane (kg, l16) holds k = 32 ks + 8 kg .. +7, split
+// in registers exactly as store4_split splits the LDS planes.
+struct RowFrags {
+  float4 v[MN / 32][2];
+};
+__device__ __forceinline__ void fetch_row_frags(const float *src, int64_t tok, int row, int n,
+                                                int kg, RowFrags &f) {
+#pragma unroll
+  for (int ks = 0; ks < MN / 32; ++ks) {
+    const float *p = src + (int64_t)row * tok + 32 * ks + 8 * kg;
+    f.v[ks][0] = row < n ? *reinterpret_cast<const float4 *>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
+    f.v[ks][1] =
+        row < n ? *reinterpret_cast<const float4 *>(p + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+__device__ __forceinline__ Frag split_frag(const float4 &a, const float4 &b) {
+  const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  Frag f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    u16 hh, ll;
+    split(x[e], hh, ll);
+    f.hi[e] = (short)hh;
+    f.lo[e] = (short)ll;
+  }
+  return f;
+}
+
 __global__ __launch_bounds__(MNT) void k_ssd_chunk_mma(SsdArgs a, float *__restrict__ ws) {
+  // C never enters LDS (each wave splits its row tile of C in registers) and
+  // w B overwrites B, so two workgroups fit in one CU's LDS
   __shared__ __attribute__((aligned(16))) u16 sXh[SC * PXb], sXl[SC * PXb];
-  __shared__ __attribute__((aligned(16))) u16 sBh[SC * PBb], sBl[SC * PBb];
-  __shared__ __attribute__((aligned(16))) u16 sCh[SC * PBb], sCl[SC * PBb];   // C, then w B
+  __shared__ __attribute__((aligned(16))) u16 sBh[SC * PBb], sBl[SC * PBb];   // B, then w B
   __shared__ __attribute__((aligned(16))) u16 sMh[SC * PMb], sMl[SC * PMb];
   __shared__ float sDt[SC], sCs[SC], sW[SC];
   const int c = blockIdx.x, h = blockIdx.y, s = blockIdx.z, tid = threadIdx.x;
@@ -356,15 +386,20 @@ __global__ __launch_bounds__(MNT) void k_ssd_chunk_mma(SsdArgs a, float *__restr
   const float *xc = a.x + s * a.x_seq + (int64_t)t0 * a.x_tok + (int64_t)h * MP;
   const float *bc = a.Bm + s * a.bc_seq + (int64_t)t0 * a.bc_tok + (int64_t)gi * MN;
   const float *cc = a.Cm + s * a.bc_seq + (int64_t)t0 * a.bc_tok + (int64_t)gi * MN;
+  // M's 10 lower 16x16 tiles (ti >= tj) go to waves 0..5 by token tile, so a
+  // wave needs one row tile of C: w0 (3; 0,1), w1 (3; 2,3), w2 (2; 0,1),
+  // w3 (2; 2), w4 (1; 0,1), w5 (0; 0); waves 6 and 7 have none
+  const int mti = w < 2 ? 3 : w < 4 ? 2 : w == 4 ? 1 : 0;
+  const int mtj = (w == 1 || w == 3) ? 2 : 0;
+  const int mnt = w < 6 ? ((w == 3 || w == 5) ? 1 : 2) : 0;
+  RowFrags fcr;
   {
-    float4 vx[rows_per_thread<MP, SC>()], vb[rows_per_thread<MN, SC>()],
-        vcc[rows_per_thread<MN, SC>()];
+    float4 vx[rows_per_thread<MP, SC>()], vb[rows_per_thread<MN, SC>()];
     fetch_rows<MP, SC>(xc, a.x_tok, n, vx);
     fetch_rows<MN, SC>(bc, a.bc_tok, n, vb);
-    fetch_rows<MN, SC>(cc, a.bc_tok, n, vcc);
+    if (mnt > 0) fetch_row_frags(cc, a.bc_tok, 16 * mti + l16, n, kg, fcr);
     put_rows<MP, SC, PXb>(sXh, sXl, vx);
     put_rows<MN, SC, PBb>(sBh, sBl, vb);
-    put_rows<MN, SC, PBb>(sCh, sCl, vcc);
   }
   {   // M starts at zero (its upper tiles stay so)
     uint4 *z0 = reinterpret_cast<uint4 *>(sMh), *z1 = reinterpret_cast<uint4 *>(sMl);
@@ -373,15 +408,16 @@ __global__ __launch_bounds__(MNT) void k_ssd_chunk_mma(SsdArgs a, float *__restr
   __syncthreads();
   if (tid < SC) sW[tid] = expf(sCs[SC - 1] - sCs[tid]) * sDt[tid];   // w_s = e^{c_n - c_s} dt_s
 
-  // M[t][s] = e^{c_t - c_s} (C_t . B_s) dt_s, lower 16x16 tiles (ti >= tj):
-  // 10 tiles, wave w takes tiles w and w + 8
-  for (int jt = w; jt < 10; jt += 8) {
-    const int ti = jt < 1 ? 0 : jt < 3 ? 1 : jt < 6 ? 2 : 3, tj = jt - ti * (ti + 1) / 2;
+  // M[t][s] = e^{c_t - c_s} (C_t . B_s) dt_s, lower 16x16 tiles (ti >= tj)
+  Frag fc[MN / 32];
+#pragma unroll
+  for (int ks = 0; ks < MN / 32; ++ks) fc[ks] = split_frag(fcr.v[ks][0], fcr.v[ks][1]);
+  for (int jj = 0; jj < mnt; ++jj) {
+    const int ti = mti, tj = mtj + jj;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < MN / 32; ++ks)
-      acc = mfma3(frag(sCh, sCl, PBb, 16 * ti + l16, 32 * ks + 8 * kg),
-                  frag(sBh, sBl, PBb, 16 * tj + l16, 32 * ks + 8 * kg), acc);
+      acc = mfma3(fc[ks], frag(sBh, sBl, PBb, 16 * tj + l16, 32 * ks + 8 * kg), acc);
     const int u = 16 * tj + l16;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -394,9 +430,9 @@ __global__ __launch_bounds__(MNT) void k_ssd_chunk_mma(SsdArgs a, float *__restr
       sMl[t * PMb + u] = ll;
     }
   }
-  __syncthreads();   // M complete; C no longer needed
-  // w_s B_s into C's planes, for the state contribution, from the B planes
-  // already in LDS (hi + lo is B to 2^-16 relative; rows past n are zero)
+  __syncthreads();   // M complete; B no longer read as B
+  // w_s B_s over B's planes (each thread rewrites the elements it reads), for
+  // the state contribution (hi + lo is B to 2^-16 relative; rows past n are zero)
   for (int e = tid; e < SC * MN / 4; e += MNT) {
     const int r = e / (MN / 4), c4 = (e - r * (MN / 4)) * 4;
     const uint2 hb = *reinterpret_cast<const uint2 *>(sBh + r * PBb + c4);
@@ -407,7 +443,7 @@ __global__ __launch_bounds__(MNT) void k_ssd_chunk_mma(SsdArgs a, float *__restr
     v[1] = bf16_value((u16)(hb.x >> 16)) + bf16_value((u16)(lb.x >> 16));
     v[2] = bf16_value((u16)(hb.y & 0xffffu)) + bf16_value((u16)(lb.y & 0xffffu));
     v[3] = bf16_value((u16)(hb.y >> 16)) + bf16_value((u16)(lb.y >> 16));
-    store4_split(sCh + r * PBb + c4, sCl + r * PBb + c4, f * v[0], f * v[1], f * v[2], f * v[3]);
+    store4_split(sBh + r * PBb + c4, sBl + r * PBb + c4, f * v[0], f * v[1], f * v[2], f * v[3]);
   }
 
   // y_t (intra-chunk part) = sum_s M[t][s] x_s + D x_t: 16 tiles (t, p), wave w
@@ -449,7 +485,7 @@ __global__ __launch_bounds__(MNT) void k_ssd_chunk_mma(SsdArgs a, float *__restr
       const Frag fx = frag_tr(sXh, sXl, PXb, 32 * ks, 16 * tp, kg, l16);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        acc[j] = mfma3(fx, frag_tr(sCh, sCl, PBb, 32 * ks, 16 * (4 * (w >> 2) + j), kg, l16),
+        acc[j] = mfma3(fx, frag_tr(sBh, sBl, PBb, 32 * ks, 16 * (4 * (w >> 2) + j), kg, l16),
                        acc[j]);
     }
     float *blk = ws_block<MP, MN>(ws, s, h, c, a.H, a.n_chunks);
@@ -467,9 +503,9 @@ __global__ __launch_bounds__(MNT) void k_ssd_chunk_mma(SsdArgs a, float *__restr
 }
 
 // y_t += e^{c_t} sum_k C_t[k] h0[p][k]: 16 tiles (t, p), wave w takes token
-// tile w & 3 and value tiles 2 (w >> 2), +1
+// tile w & 3 and value tiles 2 (w >> 2), +1.  Only h0 goes through LDS; each
+// wave splits its row tile of C in registers.
 __global__ __launch_bounds__(MNT) void k_ssd_out_mma(SsdArgs a, const float *__restrict__ ws) {
-  __shared__ __attribute__((aligned(16))) u16 sCh[SC * PBb], sCl[SC * PBb];
   __shared__ __attribute__((aligned(16))) u16 sHh[MP * PBb], sHl[MP * PBb];
   __shared__ float sDt[SC], sCs[SC];
   const int c = blockIdx.x, h = blockIdx.y, s = blockIdx.z, tid = threadIdx.x;
@@ -479,21 +515,21 @@ __global__ __launch_bounds__(MNT) void k_ssd_out_mma(SsdArgs a, const float *__r
   const float A = -expf(a.A_log[h]);
   chunk_dt(a.dt_raw, s * a.dt_seq + (int64_t)t0 * a.dt_tok, a.dt_tok, h, n, a.dt_bias[h], A,
            a.dt_min, a.dt_max, sDt, sCs);
+  const int ti = w & 3;
+  RowFrags fcr;
   {
-    float4 vcc[rows_per_thread<MN, SC>()], vh[rows_per_thread<MN, MP>()];
-    fetch_rows<MN, SC>(a.Cm + s * a.bc_seq + (int64_t)t0 * a.bc_tok + (int64_t)gi * MN,
-                       a.bc_tok, n, vcc);
+    float4 vh[rows_per_thread<MN, MP>()];
     fetch_rows<MN, MP>(ws_block<MP, MN>(const_cast<float *>(ws), s, h, c, a.H, a.n_chunks), MN,
                        MP, vh);
-    put_rows<MN, SC, PBb>(sCh, sCl, vcc);
+    fetch_row_frags(a.Cm + s * a.bc_seq + (int64_t)t0 * a.bc_tok + (int64_t)gi * MN, a.bc_tok,
+                    16 * ti + l16, n, kg, fcr);
     put_rows<MN, MP, PBb>(sHh, sHl, vh);
   }
   __syncthreads();
-  const int ti = w & 3;
   f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
   for (int ks = 0; ks < MN / 32; ++ks) {
-    const Frag fc = frag(sCh, sCl, PBb, 16 * ti + l16, 32 * ks + 8 * kg);
+    const Frag fc = split_frag(fcr.v[ks][0], fcr.v[ks][1]);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       acc[j] = mfma3(fc, frag(sHh, sHl, PBb, 16 * (2 * (w >> 2) + j) + l16, 32 * ks + 8 * kg),
