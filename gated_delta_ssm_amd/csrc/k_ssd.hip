@@ -238,13 +238,28 @@ __global__ __launch_bounds__(NT) void k_ssd_state(float *__restrict__ state, int
   float4 st = *sp;
   const size_t blocks = (size_t)n_seq * H * nc * (P * N);
   const float *dec = ws_decay(ws, blocks, s, h, 0, H, nc);
-  for (int c = 0; c < nc; ++c) {
-    float4 *bp = reinterpret_cast<float4 *>(ws_block<P, N>(ws, s, h, c, H, nc)) + e;
-    const float4 contrib = *bp;
-    const float gam = dec[c];
-    *bp = st;   // the state entering chunk c
-    st = make_float4(gam * st.x + contrib.x, gam * st.y + contrib.y, gam * st.z + contrib.z,
-                     gam * st.w + contrib.w);
+  // U chunks' contributions are loaded before the first is used: the grid has
+  // only P N / 4 threads per head, so each needs many bytes in flight
+  constexpr int U = 16;
+  float4 *bp = reinterpret_cast<float4 *>(ws_block<P, N>(ws, s, h, 0, H, nc)) + e;
+  for (int c0 = 0; c0 < nc; c0 += U) {
+    float4 contrib[U];
+    float gam[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c0 + u < nc) {
+        contrib[u] = bp[(size_t)(c0 + u) * (P * N / 4)];
+        gam[u] = dec[c0 + u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c0 + u < nc) {
+        bp[(size_t)(c0 + u) * (P * N / 4)] = st;   // the state entering chunk c0 + u
+        st = make_float4(gam[u] * st.x + contrib[u].x, gam[u] * st.y + contrib[u].y,
+                         gam[u] * st.z + contrib[u].z, gam[u] * st.w + contrib[u].w);
+      }
+    }
   }
   *sp = st;
 }
