@@ -385,11 +385,14 @@ __device__ __forceinline__ Frag split_frag(const float4 &a, const float4 &b) {
 }
 
 __global__ __launch_bounds__(MNT) void k_ssd_chunk_mma(SsdArgs a, float *__restrict__ ws) {
-  // C never enters LDS (each wave splits its row tile of C in registers) and
-  // w B overwrites B, so two workgroups fit in one CU's LDS
+  // Only x and B pass through LDS: each wave splits its row tile of C in
+  // registers, w B overwrites B once M is formed, and M (held in registers
+  // meanwhile) overwrites w B once the state contribution is formed, so three
+  // workgroups fit in one CU's LDS
   __shared__ __attribute__((aligned(16))) u16 sXh[SC * PXb], sXl[SC * PXb];
-  __shared__ __attribute__((aligned(16))) u16 sBh[SC * PBb], sBl[SC * PBb];   // B, then w B
-  __shared__ __attribute__((aligned(16))) u16 sMh[SC * PMb], sMl[SC * PMb];
+  __shared__ __attribute__((aligned(16))) u16 sBh[SC * PBb], sBl[SC * PBb];   // B, w B, M
+  static_assert(SC * PMb <= SC * PBb, "M fits in B's planes");
+  u16 *const sMh = sBh, *const sMl = sBl;
   __shared__ float sDt[SC], sCs[SC], sW[SC];
   const int c = blockIdx.x, h = blockIdx.y, s = blockIdx.z, tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
@@ -407,45 +410,43 @@ __global__ __launch_bounds__(MNT) void k_ssd_chunk_mma(SsdArgs a, float *__restr
   const int mti = w < 2 ? 3 : w < 4 ? 2 : w == 4 ? 1 : 0;
   const int mtj = (w == 1 || w == 3) ? 2 : 0;
   const int mnt = w < 6 ? ((w == 3 || w == 5) ? 1 : 2) : 0;
+  // the y tiles of this lane: token tile w & 3, value tiles 2 (w >> 2), +1
+  const int yti = w & 3;
   RowFrags fcr;
   {
     float4 vx[rows_per_thread<MP, SC>()], vb[rows_per_thread<MN, SC>()];
     fetch_rows<MP, SC>(xc, a.x_tok, n, vx);
     fetch_rows<MN, SC>(bc, a.bc_tok, n, vb);
-    if (mnt > 0) fetch_row_frags(cc, a.bc_tok, 16 * mti + l16, n, kg, fcr);
     put_rows<MP, SC, PXb>(sXh, sXl, vx);
     put_rows<MN, SC, PBb>(sBh, sBl, vb);
   }
-  {   // M starts at zero (its upper tiles stay so)
-    uint4 *z0 = reinterpret_cast<uint4 *>(sMh), *z1 = reinterpret_cast<uint4 *>(sMl);
-    for (int e = tid; e < SC * PMb * 2 / 16; e += MNT) z0[e] = z1[e] = make_uint4(0, 0, 0, 0);
-  }
+  if (mnt > 0) fetch_row_frags(cc, a.bc_tok, 16 * mti + l16, n, kg, fcr);
   __syncthreads();
   if (tid < SC) sW[tid] = expf(sCs[SC - 1] - sCs[tid]) * sDt[tid];   // w_s = e^{c_n - c_s} dt_s
 
   // M[t][s] = e^{c_t - c_s} (C_t . B_s) dt_s, lower 16x16 tiles (ti >= tj)
-  Frag fc[MN / 32];
+  float mv[2][4];   // this wave's M tiles, kept in registers until B's planes are free
+  if (mnt > 0) {
+    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-  for (int ks = 0; ks < MN / 32; ++ks) fc[ks] = split_frag(fcr.v[ks][0], fcr.v[ks][1]);
-  for (int jj = 0; jj < mnt; ++jj) {
-    const int ti = mti, tj = mtj + jj;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < MN / 32; ++ks) {
+      const Frag fc = split_frag(fcr.v[ks][0], fcr.v[ks][1]);
+      acc[0] = mfma3(fc, frag(sBh, sBl, PBb, 16 * mtj + l16, 32 * ks + 8 * kg), acc[0]);
+      if (mnt > 1)
+        acc[1] = mfma3(fc, frag(sBh, sBl, PBb, 16 * (mtj + 1) + l16, 32 * ks + 8 * kg), acc[1]);
+    }
 #pragma unroll
-    for (int ks = 0; ks < MN / 32; ++ks)
-      acc = mfma3(fc[ks], frag(sBh, sBl, PBb, 16 * tj + l16, 32 * ks + 8 * kg), acc);
-    const int u = 16 * tj + l16;
+    for (int jj = 0; jj < 2; ++jj) {
+      const int u = 16 * (mtj + jj) + l16;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 16 * ti + 4 * kg + r;
-      const float arg = u <= t ? sCs[t] - sCs[u] : 0.0f;
-      const float m = u <= t ? expf(arg) * acc[r] * sDt[u] : 0.0f;
-      u16 hh, ll;
-      split(m, hh, ll);
-      sMh[t * PMb + u] = hh;
-      sMl[t * PMb + u] = ll;
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * mti + 4 * kg + r;
+        const float arg = u <= t ? sCs[t] - sCs[u] : 0.0f;
+        mv[jj][r] = u <= t ? expf(arg) * acc[jj][r] * sDt[u] : 0.0f;
+      }
     }
   }
-  __syncthreads();   // M complete; B no longer read as B
+  __syncthreads();   // M formed; B no longer read as B
   // w_s B_s over B's planes (each thread rewrites the elements it reads), for
   // the state contribution (hi + lo is B to 2^-16 relative; rows past n are zero)
   for (int e = tid; e < SC * MN / 4; e += MNT) {
@@ -461,32 +462,7 @@ __global__ __launch_bounds__(MNT) void k_ssd_chunk_mma(SsdArgs a, float *__restr
     store4_split(sBh + r * PBb + c4, sBl + r * PBb + c4, f * v[0], f * v[1], f * v[2], f * v[3]);
   }
 
-  // y_t (intra-chunk part) = sum_s M[t][s] x_s + D x_t: 16 tiles (t, p), wave w
-  // takes token tile w & 3 and value tiles 2 (w >> 2), +1
-  {
-    const int ti = w & 3;
-    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-    for (int ks = 0; ks < SC / 32; ++ks) {
-      const Frag fm = frag_pi(sMh, sMl, PMb, 16 * ti + l16, 32 * ks, kg);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        acc[j] = mfma3(fm, frag_tr(sXh, sXl, PXb, 32 * ks, 16 * (2 * (w >> 2) + j), kg, l16),
-                       acc[j]);
-    }
-    const float Dh = a.D[h];
-    float *yc = a.y + s * a.y_seq + (int64_t)t0 * a.y_tok + (int64_t)h * MP;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int p = 16 * (2 * (w >> 2) + j) + l16;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * ti + 4 * kg + r;
-        if (t < n) yc[(int64_t)t * a.y_tok + p] = acc[j][r] + Dh * xc[(int64_t)t * a.x_tok + p];
-      }
-    }
-  }
-  __syncthreads();   // w B in LDS
+  __syncthreads();   // w B complete
 
   // state contribution Hc[p][k] = sum_s x_s[p] w_s B_s[k]: 4 x 8 tiles (p, k),
   // wave w takes value tile w & 3 and state tiles 4 (w >> 2) .. +3
@@ -515,6 +491,68 @@ __global__ __launch_bounds__(MNT) void k_ssd_chunk_mma(SsdArgs a, float *__restr
       *ws_decay(ws, blocks, s, h, c, a.H, a.n_chunks) = expf(sCs[SC - 1]);
     }
   }
+  float xv[2][4];   // x at this lane's y slots, for D x
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * yti + 4 * kg + r, p = 16 * (2 * (w >> 2) + j) + l16;
+      xv[j][r] = t < n ? xc[(int64_t)t * a.x_tok + p] : 0.0f;
+    }
+  __syncthreads();   // w B no longer read
+
+  // M over B's planes: waves 0..5 their lower tiles; waves 6 and 7 zero the
+  // upper tiles (0, 1) and (2, 3), the only ones the products below read
+  if (w < 6) {
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      if (jj >= mnt) break;
+      const int u = 16 * (mtj + jj) + l16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * mti + 4 * kg + r;
+        u16 hh, ll;
+        split(mv[jj][r], hh, ll);
+        sMh[t * PMb + u] = hh;
+        sMl[t * PMb + u] = ll;
+      }
+    }
+  } else {
+    const int zt = w == 6 ? 0 : 2;   // tile (zt, zt + 1)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * zt + 4 * kg + r, u = 16 * (zt + 1) + l16;
+      sMh[t * PMb + u] = 0;
+      sMl[t * PMb + u] = 0;
+    }
+  }
+  __syncthreads();
+
+  // y_t (intra-chunk part) = sum_s M[t][s] x_s + D x_t: 16 tiles (t, p), wave w
+  // takes token tile w & 3 and value tiles 2 (w >> 2), +1; token tiles 0 and 1
+  // need only positions s < 32
+  {
+    const int ti = yti;
+    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    for (int ks = 0; ks < (ti < 2 ? 1 : 2); ++ks) {
+      const Frag fm = frag_pi(sMh, sMl, PMb, 16 * ti + l16, 32 * ks, kg);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[j] = mfma3(fm, frag_tr(sXh, sXl, PXb, 32 * ks, 16 * (2 * (w >> 2) + j), kg, l16),
+                       acc[j]);
+    }
+    const float Dh = a.D[h];
+    float *yc = a.y + s * a.y_seq + (int64_t)t0 * a.y_tok + (int64_t)h * MP;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int p = 16 * (2 * (w >> 2) + j) + l16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * ti + 4 * kg + r;
+        if (t < n) yc[(int64_t)t * a.y_tok + p] = acc[j][r] + Dh * xv[j][r];
+      }
+    }
+  }
 }
 
 // y_t += e^{c_t} sum_k C_t[k] h0[p][k]: 16 tiles (t, p), wave w takes token
@@ -531,6 +569,17 @@ __global__ __launch_bounds__(MNT) void k_ssd_out_mma(SsdArgs a, const float *__r
   chunk_dt(a.dt_raw, s * a.dt_seq + (int64_t)t0 * a.dt_tok, a.dt_tok, h, n, a.dt_bias[h], A,
            a.dt_min, a.dt_max, sDt, sCs);
   const int ti = w & 3;
+  float *yc = a.y + s * a.y_seq + (int64_t)t0 * a.y_tok + (int64_t)h * MP;
+  float yv[2][4];   // the intra-chunk y this lane completes, read with the other loads
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int p = 16 * (2 * (w >> 2) + j) + l16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * ti + 4 * kg + r;
+      yv[j][r] = t < n ? yc[(int64_t)t * a.y_tok + p] : 0.0f;
+    }
+  }
   RowFrags fcr;
   {
     float4 vh[rows_per_thread<MN, MP>()];
@@ -550,14 +599,13 @@ __global__ __launch_bounds__(MNT) void k_ssd_out_mma(SsdArgs a, const float *__r
       acc[j] = mfma3(fc, frag(sHh, sHl, PBb, 16 * (2 * (w >> 2) + j) + l16, 32 * ks + 8 * kg),
                      acc[j]);
   }
-  float *yc = a.y + s * a.y_seq + (int64_t)t0 * a.y_tok + (int64_t)h * MP;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int p = 16 * (2 * (w >> 2) + j) + l16;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = 16 * ti + 4 * kg + r;
-      if (t < n) yc[(int64_t)t * a.y_tok + p] += expf(sCs[t]) * acc[j][r];
+      if (t < n) yc[(int64_t)t * a.y_tok + p] = yv[j][r] + expf(sCs[t]) * acc[j][r];
     }
   }
 }
