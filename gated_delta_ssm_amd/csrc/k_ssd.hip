@@ -38,11 +38,13 @@ constexpr int NT = 256;    // threads per workgroup
 __device__ __forceinline__ float softplus20(float v) { return v > 20.0f ? v : log1pf(expf(v)); }
 
 // Per-position dt and inclusive cumsum of dt A for the chunk, in LDS (wave 0;
-// positions past n get dt = 0, so the cumsum stays flat there).  Both
-// kernels that need c_t call this, so they agree bit for bit.
+// positions past n get dt = 0, so the cumsum stays flat there), and if asked
+// the state weights w_t = e^{c_n - c_t} dt_t.  Both kernels that need c_t call
+// this, so they agree bit for bit.
 __device__ __forceinline__ void chunk_dt(const float *dt_raw, int64_t dt_row0, int64_t dt_tok,
                                          int h, int n, float bias, float A, float dt_min,
-                                         float dt_max, float *sDt, float *sCs) {
+                                         float dt_max, float *sDt, float *sCs,
+                                         float *sW = nullptr) {
   const int t = threadIdx.x;
   if (t < SC) {
     float d = 0.0f;
@@ -58,6 +60,8 @@ __device__ __forceinline__ void chunk_dt(const float *dt_raw, int64_t dt_row0, i
     }
     sDt[t] = d;
     sCs[t] = c;
+    const float cn = __shfl(c, SC - 1, 64);
+    if (sW != nullptr) sW[t] = expf(cn - c) * d;
   }
 }
 
@@ -400,7 +404,7 @@ __global__ __launch_bounds__(MNT) void k_ssd_chunk_mma(SsdArgs a, float *__restr
   const int t0 = c * SC, n = min(SC, a.n_tok - t0);
   const float A = -expf(a.A_log[h]);
   chunk_dt(a.dt_raw, s * a.dt_seq + (int64_t)t0 * a.dt_tok, a.dt_tok, h, n, a.dt_bias[h], A,
-           a.dt_min, a.dt_max, sDt, sCs);
+           a.dt_min, a.dt_max, sDt, sCs, sW);
   const float *xc = a.x + s * a.x_seq + (int64_t)t0 * a.x_tok + (int64_t)h * MP;
   const float *bc = a.Bm + s * a.bc_seq + (int64_t)t0 * a.bc_tok + (int64_t)gi * MN;
   const float *cc = a.Cm + s * a.bc_seq + (int64_t)t0 * a.bc_tok + (int64_t)gi * MN;
@@ -413,16 +417,24 @@ __global__ __launch_bounds__(MNT) void k_ssd_chunk_mma(SsdArgs a, float *__restr
   // the y tiles of this lane: token tile w & 3, value tiles 2 (w >> 2), +1
   const int yti = w & 3;
   RowFrags fcr;
+  float xv[2][4];   // x at this lane's y slots, for D x
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * yti + 4 * kg + r, p = 16 * (2 * (w >> 2) + j) + l16;
+      xv[j][r] = t < n ? xc[(int64_t)t * a.x_tok + p] : 0.0f;
+    }
+  float4 vb[rows_per_thread<MN, SC>()];   // B, kept for w B
   {
-    float4 vx[rows_per_thread<MP, SC>()], vb[rows_per_thread<MN, SC>()];
+    float4 vx[rows_per_thread<MP, SC>()];
     fetch_rows<MP, SC>(xc, a.x_tok, n, vx);
     fetch_rows<MN, SC>(bc, a.bc_tok, n, vb);
+    if (mnt > 0) fetch_row_frags(cc, a.bc_tok, 16 * mti + l16, n, kg, fcr);
     put_rows<MP, SC, PXb>(sXh, sXl, vx);
     put_rows<MN, SC, PBb>(sBh, sBl, vb);
   }
-  if (mnt > 0) fetch_row_frags(cc, a.bc_tok, 16 * mti + l16, n, kg, fcr);
   __syncthreads();
-  if (tid < SC) sW[tid] = expf(sCs[SC - 1] - sCs[tid]) * sDt[tid];   // w_s = e^{c_n - c_s} dt_s
 
   // M[t][s] = e^{c_t - c_s} (C_t . B_s) dt_s, lower 16x16 tiles (ti >= tj)
   float mv[2][4];   // this wave's M tiles, kept in registers until B's planes are free
@@ -447,19 +459,14 @@ __global__ __launch_bounds__(MNT) void k_ssd_chunk_mma(SsdArgs a, float *__restr
     }
   }
   __syncthreads();   // M formed; B no longer read as B
-  // w_s B_s over B's planes (each thread rewrites the elements it reads), for
-  // the state contribution (hi + lo is B to 2^-16 relative; rows past n are zero)
-  for (int e = tid; e < SC * MN / 4; e += MNT) {
-    const int r = e / (MN / 4), c4 = (e - r * (MN / 4)) * 4;
-    const uint2 hb = *reinterpret_cast<const uint2 *>(sBh + r * PBb + c4);
-    const uint2 lb = *reinterpret_cast<const uint2 *>(sBl + r * PBb + c4);
+  // w_s B_s over B's planes, for the state contribution: each thread scales
+  // the fp32 B elements it stored there (rows past n are zero)
+#pragma unroll
+  for (int i = 0; i < rows_per_thread<MN, SC>(); ++i) {
+    const int e = tid + i * MNT, r = e / (MN / 4), c4 = (e - r * (MN / 4)) * 4;
     const float f = sW[r];
-    float v[4];
-    v[0] = bf16_value((u16)(hb.x & 0xffffu)) + bf16_value((u16)(lb.x & 0xffffu));
-    v[1] = bf16_value((u16)(hb.x >> 16)) + bf16_value((u16)(lb.x >> 16));
-    v[2] = bf16_value((u16)(hb.y & 0xffffu)) + bf16_value((u16)(lb.y & 0xffffu));
-    v[3] = bf16_value((u16)(hb.y >> 16)) + bf16_value((u16)(lb.y >> 16));
-    store4_split(sBh + r * PBb + c4, sBl + r * PBb + c4, f * v[0], f * v[1], f * v[2], f * v[3]);
+    store4_split(sBh + r * PBb + c4, sBl + r * PBb + c4, f * vb[i].x, f * vb[i].y, f * vb[i].z,
+                 f * vb[i].w);
   }
 
   __syncthreads();   // w B complete
@@ -491,14 +498,6 @@ __global__ __launch_bounds__(MNT) void k_ssd_chunk_mma(SsdArgs a, float *__restr
       *ws_decay(ws, blocks, s, h, c, a.H, a.n_chunks) = expf(sCs[SC - 1]);
     }
   }
-  float xv[2][4];   // x at this lane's y slots, for D x
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 16 * yti + 4 * kg + r, p = 16 * (2 * (w >> 2) + j) + l16;
-      xv[j][r] = t < n ? xc[(int64_t)t * a.x_tok + p] : 0.0f;
-    }
   __syncthreads();   // w B no longer read
 
   // M over B's planes: waves 0..5 their lower tiles; waves 6 and 7 zero the
