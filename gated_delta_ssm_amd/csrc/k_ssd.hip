@@ -20,8 +20,10 @@
 //                state entering it is written over its contribution, then
 //                h <- e^{c_n} h + contribution; the last h is the new state
 //   k_ssd_out    every chunk again: y_t += e^{c_t} h0 C_t
-// All arithmetic is fp32 on the vector ALUs, 4 x 4 (or 4 x 8) register tiles
-// over LDS rows read as float4.
+// At head_dim 64 / state 128 the chunk and output kernels run their products
+// as 16x16x32 bf16 MFMA tiles with each fp32 operand split into hi + lo
+// (k_ssd_chunk_mma, k_ssd_out_mma); other shapes use fp32 on the vector ALUs,
+// 4 x 4 (or 4 x 8) register tiles over LDS rows read as float4.
 #include <hip/hip_runtime.h>
 
 #include "bf16_frag.hpp"
