@@ -33,6 +33,19 @@ __device__ __forceinline__ void split(float x, u16 &hi, u16 &lo) {
   lo = bf16_bits(x - bf16_value(hi));
 }
 
+// split() of two values at once, packed as stored: element 0 in the low half.
+// One v_cvt_pk_bf16_f32 per plane; the same roundings as split(), so the
+// same bits.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split2(float a, float b, unsigned &hi, unsigned &lo) {
+  const unsigned h = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, bf16x2v));
+  const float ha = __builtin_bit_cast(float, h << 16);
+  const float hb = __builtin_bit_cast(float, h & 0xffff0000u);
+  lo = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a - ha, b - hb}, bf16x2v));
+  hi = h;
+}
+
 __device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -98,28 +111,18 @@ __device__ __forceinline__ Frag frag_tr(const u16 *hi, const u16 *lo, int pitch,
 
 // Split 4 floats and store them as 4 consecutive bf16 in each plane.
 __device__ __forceinline__ void store4_split(u16 *hi, u16 *lo, float a, float b, float c, float d) {
-  u16 h[4], l[4];
-  split(a, h[0], l[0]);
-  split(b, h[1], l[1]);
-  split(c, h[2], l[2]);
-  split(d, h[3], l[3]);
-  *reinterpret_cast<uint2 *>(hi) =
-      make_uint2(h[0] | ((unsigned)h[1] << 16), h[2] | ((unsigned)h[3] << 16));
-  *reinterpret_cast<uint2 *>(lo) =
-      make_uint2(l[0] | ((unsigned)l[1] << 16), l[2] | ((unsigned)l[3] << 16));
+  unsigned h0, l0, h1, l1;
+  split2(a, b, h0, l0);
+  split2(c, d, h1, l1);
+  *reinterpret_cast<uint2 *>(hi) = make_uint2(h0, h1);
+  *reinterpret_cast<uint2 *>(lo) = make_uint2(l0, l1);
 }
 
 // Split 8 floats into one 16-byte store per plane.
 __device__ __forceinline__ void store8_split(u16 *hi, u16 *lo, const float (&x)[8]) {
   unsigned h[4], l[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    u16 h0, l0, h1, l1;
-    split(x[2 * e], h0, l0);
-    split(x[2 * e + 1], h1, l1);
-    h[e] = h0 | ((unsigned)h1 << 16);
-    l[e] = l0 | ((unsigned)l1 << 16);
-  }
+  for (int e = 0; e < 4; ++e) split2(x[2 * e], x[2 * e + 1], h[e], l[e]);
   *reinterpret_cast<uint4 *>(hi) = make_uint4(h[0], h[1], h[2], h[3]);
   *reinterpret_cast<uint4 *>(lo) = make_uint4(l[0], l[1], l[2], l[3]);
 }
