@@ -46,6 +46,17 @@ __device__ __forceinline__ void split2(float a, float b, unsigned &hi, unsigned 
   hi = h;
 }
 
+// Eight values split into one fragment (slot e holds x[e]).
+__device__ __forceinline__ Frag split8(const float (&x)[8]) {
+  unsigned h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) split2(x[2 * e], x[2 * e + 1], h[e], l[e]);
+  Frag f;
+  f.hi = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
+  f.lo = __builtin_bit_cast(bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
+  return f;
+}
+
 __device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

@@ -93,15 +93,10 @@ __device__ __forceinline__ h16x8 frag_ws(const u16 *base, int m, int ks, int n_k
 }
 // fp16 -> bf16 hi + lo, exactly (an fp16 value has 11 significant bits)
 __device__ __forceinline__ Frag split_h(const h16x8 &x) {
-  Frag f;
+  float v[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    u16 hi, lo;
-    split((float)x[e], hi, lo);
-    f.hi[e] = (short)hi;
-    f.lo[e] = (short)lo;
-  }
-  return f;
+  for (int e = 0; e < 8; ++e) v[e] = (float)x[e];
+  return split8(v);
 }
 // 8 floats -> one 16-byte store of fp16 (round to nearest even)
 __device__ __forceinline__ void store8_h(u16 *p, const float (&x)[8]) {
@@ -225,16 +220,14 @@ __device__ __forceinline__ void t_frags(const float *sA, const float *sBeta, con
   const float tv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
   const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
   const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+  float v1[8], v2[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    u16 h, l;
-    split(tv[e] * (bv[e] * ev[e]), h, l);
-    f1.hi[e] = (short)h;
-    f1.lo[e] = (short)l;
-    split(tv[e] * bv[e], h, l);
-    f2.hi[e] = (short)h;
-    f2.lo[e] = (short)l;
+    v1[e] = tv[e] * (bv[e] * ev[e]);
+    v2[e] = tv[e] * bv[e];
   }
+  f1 = split8(v1);
+  f2 = split8(v2);
 }
 
 // ---- fp32 16x16 block products for the triangular inverse

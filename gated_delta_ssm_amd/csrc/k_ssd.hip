@@ -378,15 +378,8 @@ __device__ __forceinline__ void fetch_row_frags(const float *src, int64_t tok, i
   }
 }
 __device__ __forceinline__ Frag split_frag(const float4 &a, const float4 &b) {
-  unsigned h[4], l[4];
-  split2(a.x, a.y, h[0], l[0]);
-  split2(a.z, a.w, h[1], l[1]);
-  split2(b.x, b.y, h[2], l[2]);
-  split2(b.z, b.w, h[3], l[3]);
-  Frag f;
-  f.hi = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
-  f.lo = __builtin_bit_cast(bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
-  return f;
+  const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  return split8(x);
 }
 
 __global__ __launch_bounds__(MNT) void k_ssd_chunk_mma(SsdArgs a, float *__restrict__ ws) {
