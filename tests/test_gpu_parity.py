@@ -954,6 +954,73 @@ def test_mamba2_ssd_deterministic():
     assert bits_equal(ya, yb) and bits_equal(sa, sb)
 
 
+def test_workspace_contents_do_not_matter():
+    # every workspace value a chunked or Mamba-2 call reads is written earlier
+    # in the same call (padding chunks and partial last chunks included): a
+    # workspace filled with 0xFF bytes (NaN as fp32) gives, bit for bit, the
+    # results of a zero-filled one
+    log_case("workspace_contents")
+
+    def both(call, nbytes):
+        outs = []
+        for fill in (0x00, 0xFF):
+            ws = torch.full((max(nbytes, 1),), fill, dtype=torch.uint8, device=DEV)
+            outs.append(call(ws))
+        return outs
+
+    # fixed-length chunked: 3 chunks per head, so the scan runs a padding chunk
+    inp = make_inputs("prefill", seed=71, n_tok=130, H=4, Hk=2, n_seq=2, state_std=0.05)
+    wl = inp["wl"]
+    g3 = oracle_g(inp)
+
+    def chunked(ws):
+        st = on_dev(inp["state"]).clone()
+        y = torch.full_like(on_dev(inp["v"]), float("nan"))
+        gdn().gdn_recurrence_chunked(st, on_dev(inp["q"]), on_dev(inp["k"]), on_dev(inp["v"]),
+                                     on_dev(g3), on_dev(inp["beta"]), y, scale=wl.scale,
+                                     chunk=64, workspace=ws)
+        return y, st
+    (ya, sa), (yb, sb) = both(chunked, gdn().gdn_recurrence_chunked_workspace_bytes(
+        2, 130, 4, 2, wl.S, 64))
+    assert not torch.isnan(ya).any()
+    assert bits_equal(ya, yb) and bits_equal(sa, sb)
+
+    # packed prompts with an empty and a one-position sequence
+    lens = [70, 0, 1, 129]
+    inp = make_inputs("prefill", seed=73, n_tok=max(lens), H=4, Hk=2, n_seq=len(lens),
+                      state_std=0.05)
+    wl = inp["wl"]
+    pk = pack_varlen(inp, lens, oracle_g(inp))
+
+    def varlen(ws):
+        st = on_dev(inp["state"]).clone()
+        y = torch.full_like(on_dev(pk["v"]), float("nan"))
+        gdn().gdn_recurrence_chunked_varlen(st, on_dev(pk["q"]), on_dev(pk["k"]), on_dev(pk["v"]),
+                                            on_dev(pk["g"]), on_dev(pk["beta"]), y, pk["cu"],
+                                            scale=wl.scale, chunk=64, workspace=ws)
+        return y, st
+    (ya, sa), (yb, sb) = both(varlen, gdn().gdn_recurrence_chunked_varlen_workspace_bytes(
+        len(lens), pk["cu"][-1], 4, 2, wl.S, 64))
+    assert not torch.isnan(ya).any()
+    assert bits_equal(ya, yb) and bits_equal(sa, sb)
+
+    # Mamba-2: a one-position last chunk, MFMA and VALU shapes
+    for (H, G, P, N) in [(4, 2, 64, 128), (2, 1, 32, 64)]:
+        mi = make_mamba2_inputs(2, 129, H, G, P, N, seed=79, state_std=0.1)
+
+        def ssd(ws):
+            st = on_dev(mi["state"]).clone()
+            y = torch.full_like(on_dev(mi["x"]), float("nan"))
+            gdn().gdn_mamba2_ssd_chunked(st, on_dev(mi["x"]), on_dev(mi["B"]), on_dev(mi["C"]),
+                                         on_dev(mi["dt_raw"]), on_dev(mi["A_log"]),
+                                         on_dev(mi["D"]), on_dev(mi["dt_bias"]), y,
+                                         dt_min=mi["dt_min"], dt_max=mi["dt_max"], workspace=ws)
+            return y, st
+        (ya, sa), (yb, sb) = both(ssd, gdn().gdn_mamba2_ssd_workspace_bytes(2, 129, H, P, N, 64))
+        assert not torch.isnan(ya).any()
+        assert bits_equal(ya, yb) and bits_equal(sa, sb), (H, G, P, N)
+
+
 # ------------------------------------------------------------------------------------- measurement aid
 
 def test_stream_copy_exact():
