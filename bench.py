@@ -125,7 +125,7 @@ def main():
     import torch
 
     import gated_delta_ssm_amd as gdn
-    from gdn_inputs import WORKLOADS, make_inputs
+    from gdn_inputs import WORKLOADS, Workload, make_inputs
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -364,36 +364,41 @@ def main():
              "step_one_launch_ms": step_one}
     del graph, s_st, s_g, s_y, s_o, sc, s_hist, s_conv
 
-    # ---------------------------------------------------------------- K = 2 verify
-    # 16 sequences x 2 draft positions in one gdn_decode_step launch, with the
-    # position-0 state and conv-history snapshots written inline
-    vw_ = WORKLOADS["verify2"]
-    vi_ = make_inputs(vw_)
-    vc = {k: v.to(dev) for k, v in vi_.items() if isinstance(v, torch.Tensor)}
-    vn, vT, vH, vS, vC = vw_.n_seq, vw_.n_tok, vw_.H, vw_.S, vw_.conv_dim
-    v_st, v_hist = vc["state"].clone(), vc["conv_hist"].clone()
-    v_out = torch.empty(vn, vT, vH, vS, device=dev)
-    v_snap = torch.empty(vn, vT - 1, vH, vS, vS, device=dev)
-    v_csnap = torch.empty(vn, vT - 1, vC, vw_.d_conv - 1, device=dev)
-    v_ws = torch.zeros(gdn.gdn_decode_step_workspace_bytes(vn, vw_.Hk) // 4, dtype=torch.int32,
-                       device=dev)
+    # ---------------------------------------------------------------- K-position verify
+    # 16 sequences x K draft positions in one gdn_decode_step launch, with the
+    # state and conv-history snapshots after every position but the last
+    # written inline (K = 2 is the headline verify; 4 and 8 show the generic K)
+    def verify_case(K):
+        vw_ = WORKLOADS["verify2"]
+        if K != vw_.n_tok:
+            vw_ = Workload(**{**vw_.__dict__, "name": f"verify{K}", "n_tok": K})
+        vi_ = make_inputs(vw_)
+        vc = {k: v.to(dev) for k, v in vi_.items() if isinstance(v, torch.Tensor)}
+        vn, vT, vH, vS, vC = vw_.n_seq, vw_.n_tok, vw_.H, vw_.S, vw_.conv_dim
+        v_st, v_hist = vc["state"].clone(), vc["conv_hist"].clone()
+        v_out = torch.empty(vn, vT, vH, vS, device=dev)
+        v_snap = torch.empty(vn, vT - 1, vH, vS, vS, device=dev)
+        v_csnap = torch.empty(vn, vT - 1, vC, vw_.d_conv - 1, device=dev)
+        v_ws = torch.zeros(gdn.gdn_decode_step_workspace_bytes(vn, vw_.Hk) // 4,
+                           dtype=torch.int32, device=dev)
 
-    def verify_step(i=0):
-        gdn.gdn_decode_step(v_st, vc["x"][..., :vC], vc["conv_w"], v_hist,
-                            vc["alpha"].view(vn, vT, vH), vc["dt"], vc["a"], vc["beta"],
-                            vc["norm_w"], vc["z"].view(vn, vT, vH, vS), v_out, scale=vw_.scale,
-                            l2_eps=vw_.l2_eps, norm_eps=vw_.norm_eps, workspace=v_ws,
-                            snap=v_snap, conv_snap=v_csnap)
-    v_ms = burst(verify_step)
-    v_state_bytes = vn * vH * vS * vS * 4
-    verify = {"workload": "verify2: 16 seq x 2 positions, 32 value / 16 q-k heads, 128x128 "
-                          "state, conv 8192 ch, state and conv-history snapshots after "
-                          "position 0, one gdn_decode_step launch (same buffers each launch: "
-                          "the 32 MiB state stays in the MALL)",
-              "ms": v_ms,
-              "state_GBs": 3 * v_state_bytes / (v_ms * 1e-3) / 1e9,
-              "state_bytes_note": "state read + final write + snapshot write"}
-    del v_st, v_hist, v_out, v_snap, v_csnap, vc
+        def verify_step(i=0):
+            gdn.gdn_decode_step(v_st, vc["x"][..., :vC], vc["conv_w"], v_hist,
+                                vc["alpha"].view(vn, vT, vH), vc["dt"], vc["a"], vc["beta"],
+                                vc["norm_w"], vc["z"].view(vn, vT, vH, vS), v_out,
+                                scale=vw_.scale, l2_eps=vw_.l2_eps, norm_eps=vw_.norm_eps,
+                                workspace=v_ws, snap=v_snap, conv_snap=v_csnap)
+        v_ms = burst(verify_step)
+        v_state_bytes = vn * vH * vS * vS * 4
+        return {"workload": f"verify{K}: 16 seq x {K} positions, 32 value / 16 q-k heads, "
+                            "128x128 state, conv 8192 ch, state and conv-history snapshots "
+                            "after every position but the last, one gdn_decode_step launch "
+                            "(same buffers each launch: the 32 MiB state stays in the MALL)",
+                "ms": v_ms,
+                "state_GBs": (K + 1) * v_state_bytes / (v_ms * 1e-3) / 1e9,
+                "state_bytes_note": f"state read + final write + {K - 1} snapshot write(s)"}
+    verify = verify_case(2)
+    verify_more = {str(K): verify_case(K) for K in (4, 8)}
 
     # ---------------------------------------------------------------- prefill pass
     pw = WORKLOADS["prefill"]
@@ -636,6 +641,7 @@ def main():
             "conv_alone_GBs": by["conv"] / (bursts["conv_step_rotated_hist"] * 1e-3) / 1e9,
             "small_batch_gate_recurrence_norm": small,
             "verify2_step": verify,
+            "verify_k_steps": verify_more,
             "burst_ms_per_launch": bursts,
             "recurrence_burst_GBs": rec_burst_gbs,
             "copy_peak": {"what": "gdn_stream_copy (16-byte non-temporal loads and stores), "
