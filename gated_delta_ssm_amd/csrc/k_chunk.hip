@@ -3,7 +3,8 @@
 // k_chunk_small.hip).
 //
 // The pages state the chunked idea (ssm_mamba.rs, spark_model, "Mamba-2 SSD
-// chunked prefill scan" comment: ceil(T/64) sequential links instead of T) and
+// chunked prefill scan" comment: one dependent step per 64-position chunk
+// rather than one per position) and
 // that the sequential scan is its correctness reference (fm_kernel_ssm.h,
 // Foundry, fm_ssm_recurrence_seq_at).  The algebra is derived from the
 // sequential definition.  For a chunk of n <= 64 positions starting from

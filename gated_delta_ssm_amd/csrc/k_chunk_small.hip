@@ -2,7 +2,7 @@
 // recurrence for state sizes 32 and 64, in fp32 on the vector ALUs.
 //
 // ssm_mamba.rs (spark_model), "Mamba-2 SSD chunked prefill scan" comment: the
-// idea of running a long prompt as ceil(T / 64) sequential chunk links.  The
+// idea of running a long prompt with one dependent step per 64-position chunk.  The
 // algebra per chunk of n <= 64 positions from state S0, with G the inclusive
 // cumulative sum of g over the chunk (fm_kernel_ssm.h, "Delta-rule
 // recurrence" section, is the sequential definition it reproduces):

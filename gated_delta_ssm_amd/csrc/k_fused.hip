@@ -1,7 +1,7 @@
 // k_fused.hip -- the decode / K-position verify layer core in one launch:
 // decay gate -> gated delta-rule recurrence -> gated RMSNorm.
 //
-// fm_kernel_ssm.h (Foundry) states that the decay gate is pure dispatch cost
+// fm_kernel_ssm.h (Foundry) notes that the decay gate costs only its dispatch
 // and should ride with its neighbours rather than run alone; ssm_mamba.rs
 // (spark_model), conv1d_update_l2norm, fuses neighbouring ops to save a
 // launch per layer.  Here the gate and the norm ride with the recurrence.

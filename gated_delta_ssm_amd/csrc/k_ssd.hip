@@ -2,8 +2,8 @@
 // form.  ssm_mamba.rs (spark_model layers/ops), mamba2_ssm_prefill: its
 // arguments (state h, x, B and C projections, raw dt with a per-head bias and
 // dt_min / dt_max limits, A_log, the D skip, n_groups) and the "Mamba-2 SSD
-// chunked prefill scan" comment (the scan as dense products with ceil(T/64)
-// sequential links).  Per head (group gi = h / (H / G)), token t:
+// chunked prefill scan" comment (dense matrix products inside each chunk, one
+// dependent step per chunk).  Per head (group gi = h / (H / G)), token t:
 //   dt = clamp(softplus(dt_raw + dt_bias), dt_min, dt_max),  A = -exp(A_log)
 //   h  <- exp(dt A) h + dt x B^T        (h [P][N])
 //   y  =  h C + D x

@@ -82,7 +82,8 @@ int gdn_decay_gate(const float *alpha, const float *dt, const float *a, float *g
  * Per sequence s, position t, channel c:
  *   window = [hist[c][0] .. hist[c][d_conv-2], x[t][c]]  (oldest first)
  *   o      = silu(sum_j w[c][j] * window[j])
- *   hist[c] drops its oldest tap and appends the RAW x[t][c]
+ *   then hist[c] shifts by one place: its oldest value leaves and the input
+ *   x[t][c] itself (not the activated o) becomes its newest value
  *   for c < qk_channels: o /= sqrt(sum over c's head_dim block of o^2 + l2_eps)
  *
  *   x     element x[s][t][c] at x + s*x_seq_stride + t*x_tok_stride + c  (in)
@@ -151,9 +152,9 @@ size_t gdn_recurrence_chunked_workspace_bytes(int n_seq, int n_tok, int n_v_head
                                               int n_qk_heads, int S, int chunk);
 
 /*
- * The same recurrence over a long prompt in chunked (WY / UT-transform) form:
- * the T sequential links become ceil(T/chunk) ([AT] "Mamba-2 SSD chunked
- * prefill scan" comment); [FM] fm_ssm_recurrence_seq_at is the sequential scan
+ * The same recurrence over a long prompt in chunked (WY / UT-transform) form,
+ * one dependent step per chunk of positions instead of one per position ([AT]
+ * "Mamba-2 SSD chunked prefill scan" comment); [FM] fm_ssm_recurrence_seq_at is the sequential scan
  * it is validated against.  Per chunk of n <= chunk tokens from state S0, with
  * G_t the inclusive within-chunk cumulative sum of g:
  *   A  = strictly_lower(beta_t e^{G_t-G_s} k_t.k_s),  T = (I + A)^{-1}
@@ -202,8 +203,8 @@ size_t gdn_recurrence_chunked_varlen_workspace_bytes(int n_seq, int total_tok, i
  * The chunked recurrence of gdn_recurrence_chunked over a packed batch of
  * sequences of different lengths, in one call: every sequence runs the
  * chunked form from its own state, its chunks starting at its own first
- * position.  [AT] "Mamba-2 SSD chunked prefill scan" comment (ceil(T/64)
- * sequential links per sequence); [FM] fm_ssm_recurrence_seq_at is the
+ * position.  [AT] "Mamba-2 SSD chunked prefill scan" comment (one dependent
+ * step per chunk of each sequence); [FM] fm_ssm_recurrence_seq_at is the
  * per-sequence definition.
  *
  *   cu_seqlens  HOST array of n_seq + 1 int32: sequence s holds packed token
@@ -249,7 +250,8 @@ size_t gdn_mamba2_ssd_workspace_bytes(int n_seq, int n_tok, int n_heads, int hea
  * [AT] mamba2_ssm_prefill (its arguments: state, x, B and C projections, raw
  * dt with a per-head bias and dt_min / dt_max limits, A_log, the D skip,
  * n_groups, per-tensor token strides) and its "Mamba-2 SSD chunked prefill
- * scan" comment (ceil(T/64) sequential links, the rest dense products).  Per
+ * scan" comment (one dependent step per 64-position chunk, everything else as
+ * dense matrix products).  Per
  * sequence, head h (group h / (n_heads / n_groups)) and token t:
  *   dt = min(max(softplus(dt_raw + dt_bias), dt_min), dt_max)   (softplus
  *        guarded at 20),  A = -exp(A_log)

@@ -73,8 +73,9 @@ static double silu(double x) { return x / (1.0 + exp(-x)); }
  * Depthwise causal conv1d + SiLU with per-head L2 norm on the Q/K channels.
  *   [FM] "Causal depthwise conv1d + SiLU" section, fm_ssm_conv1d_silu_at and
  *        fm_ssm_conv1d_silu_seq_at: window = [history oldest..newest, x];
- *        out = silu(sum_t w[c][t] * window[t]); history drops its oldest tap and
- *        appends the RAW input.
+ *        out = silu(sum_t w[c][t] * window[t]); then the history shifts by one
+ *        place: its oldest value leaves and the input x itself (not the
+ *        activated output) becomes its newest value.
  *   [AT] conv1d_update_l2norm: channels [0, qk_channels) are L2-normalised per
  *        head_dim block after SiLU, the rest get SiLU only;
  *        gdn_verify_fused_conv_k2: the window after position 0 is the rollback
@@ -181,8 +182,9 @@ void oracle_recurrence_seq(double *S, const double *q, const double *k, const do
 /*
  * Chunked (WY / UT-transform) form of the same scan.
  *
- * The pages only state that a chunked path replaces the T sequential links by
- * ceil(T/64) ([AT] "Mamba-2 SSD chunked prefill scan" comment) and that the
+ * The pages only state that a chunked path needs one dependent step per
+ * 64-position chunk instead of one per position ([AT] "Mamba-2 SSD chunked
+ * prefill scan" comment) and that the
  * sequential scan is its permanent correctness reference ([FM]
  * fm_ssm_recurrence_seq_at doc).  The algebra below is derived from the
  * sequential definition by unrolling it over a chunk of n tokens that starts
@@ -392,8 +394,8 @@ void oracle_mamba2_ssd_seq(double *state, const double *x, const double *Bm, con
 
 /*
  * The same scan in chunked (state-space-duality) form: [AT] "Mamba-2 SSD
- * chunked prefill scan" comment (ceil(T/chunk) sequential links, the rest
- * dense products).  Derived from the sequential definition: with
+ * chunked prefill scan" comment (one dependent step per chunk, everything
+ * else as dense matrix products).  Derived from the sequential definition: with
  * c_t = sum_{s<=t} dt_s A (inclusive, within the chunk) and h0 the state
  * entering the chunk,
  *   y_t  = sum_{s<=t} e^{c_t - c_s} (C_t . B_s) dt_s x_s + e^{c_t} C_t h0^T + D x_t
