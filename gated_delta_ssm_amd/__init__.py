@@ -56,6 +56,9 @@ _SIGS = {
     "gdn_decode_step": (_I, [_P, _L, _P, _L, _L, _P, _P, _L, _P, _L, _L, _P, _P, _P, _P, _P,
                              _P, _L, _L, _P, _L, _L, _P, _P, _L, _L, _P, _L, _I, _I, _I, _I,
                              _I, _I, _F, _F, _F, _P, _SZ, _P]),
+    "gdn_decode_step_noalloc": (_I, [_P, _L, _P, _L, _L, _P, _P, _L, _P, _L, _L, _P, _P, _P, _P,
+                                     _P, _P, _L, _L, _P, _L, _L, _P, _P, _L, _L, _P, _L, _I, _I,
+                                     _I, _I, _I, _I, _F, _F, _F, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -403,20 +406,10 @@ def gdn_decode_step_workspace_bytes(n_seq: int, n_qk_heads: int) -> int:
     return int(_lib.gdn_decode_step_workspace_bytes(n_seq, n_qk_heads))
 
 
-def gdn_decode_step(state: torch.Tensor, x: torch.Tensor, conv_w: torch.Tensor,
-                    conv_state: torch.Tensor, alpha: torch.Tensor, dt: torch.Tensor,
-                    a: torch.Tensor, beta: torch.Tensor, norm_w: torch.Tensor, z: torch.Tensor,
-                    out: torch.Tensor, *, scale: float, l2_eps: float, norm_eps: float,
-                    workspace: torch.Tensor | None = None, g: torch.Tensor | None = None,
-                    y: torch.Tensor | None = None, snap: torch.Tensor | None = None,
-                    conv_snap: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """Conv1d + SiLU + L2 -> decay gate -> recurrence -> gated RMSNorm in one
-    launch.  x [n_seq][n_tok][>= conv_dim] (any row strides) with conv_dim =
-    (2*Hk + H)*S channels q | k | v; conv_w [conv_dim][d_conv]; conv_state
-    [n_seq][conv_dim][d_conv-1] rolled in place; the other tensors as
-    gdn_decode_fused; conv_snap [n_seq][n_tok-1][conv_dim][d_conv-1].
-    workspace: int32 counters, zero before first use and left zero by every
-    call (allocated zeroed here when None)."""
+def _step_args(state, x, conv_w, conv_state, alpha, dt, a, beta, norm_w, z, out, scale,
+               l2_eps, norm_eps, g, y, snap, conv_snap):
+    """Checks and the C arguments of the one-launch decode step up to (not
+    including) its workspace arguments; also returns (n_seq, Hk)."""
     n_seq, H, S, _ = state.shape
     C, D = conv_w.shape
     if C % S or (C // S - H) < 2 or (C // S - H) % 2:
@@ -465,16 +458,55 @@ def gdn_decode_step(state: torch.Tensor, x: torch.Tensor, conv_w: torch.Tensor,
         if tuple(conv_snap.shape) != (n_seq, n_tok - 1, C, D - 1):
             raise ValueError("conv_snap shape mismatch")
         cs_seq, cs_tok = conv_snap.stride(0), conv_snap.stride(1)
+    args = (_ptr(state), state.stride(0), _ptr(x), x.stride(1), x.stride(0), _ptr(conv_w),
+            _ptr(conv_state), conv_state.stride(0), _ptr(conv_snap), cs_tok, cs_seq, _ptr(alpha),
+            _ptr(dt), _ptr(a), _ptr(beta), _ptr(norm_w), _ptr(z), z.stride(1), z.stride(0),
+            _ptr(out), out.stride(1), out.stride(0), _ptr(g), _ptr(y), y_tok, y_seq, _ptr(snap),
+            sn_seq, n_seq, n_tok, H, Hk, S, D, scale, l2_eps, norm_eps)
+    return args, n_seq, Hk
+
+
+def gdn_decode_step(state: torch.Tensor, x: torch.Tensor, conv_w: torch.Tensor,
+                    conv_state: torch.Tensor, alpha: torch.Tensor, dt: torch.Tensor,
+                    a: torch.Tensor, beta: torch.Tensor, norm_w: torch.Tensor, z: torch.Tensor,
+                    out: torch.Tensor, *, scale: float, l2_eps: float, norm_eps: float,
+                    workspace: torch.Tensor | None = None, g: torch.Tensor | None = None,
+                    y: torch.Tensor | None = None, snap: torch.Tensor | None = None,
+                    conv_snap: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Conv1d + SiLU + L2 -> decay gate -> recurrence -> gated RMSNorm in one
+    launch.  x [n_seq][n_tok][>= conv_dim] (any row strides) with conv_dim =
+    (2*Hk + H)*S channels q | k | v; conv_w [conv_dim][d_conv]; conv_state
+    [n_seq][conv_dim][d_conv-1] rolled in place; the other tensors as
+    gdn_decode_fused; conv_snap [n_seq][n_tok-1][conv_dim][d_conv-1].
+    workspace: int32 counters, zero before first use and left zero by every
+    call (allocated zeroed here when None)."""
+    args, n_seq, Hk = _step_args(state, x, conv_w, conv_state, alpha, dt, a, beta, norm_w, z,
+                                 out, scale, l2_eps, norm_eps, g, y, snap, conv_snap)
     need = gdn_decode_step_workspace_bytes(n_seq, Hk)
     if workspace is None:
         workspace = torch.zeros(max(need, 4) // 4, dtype=torch.int32, device=state.device)
     _check("gdn_decode_step", _lib.gdn_decode_step(
-        _ptr(state), state.stride(0), _ptr(x), x.stride(1), x.stride(0), _ptr(conv_w),
-        _ptr(conv_state), conv_state.stride(0), _ptr(conv_snap), cs_tok, cs_seq, _ptr(alpha),
-        _ptr(dt), _ptr(a), _ptr(beta), _ptr(norm_w), _ptr(z), z.stride(1), z.stride(0),
-        _ptr(out), out.stride(1), out.stride(0), _ptr(g), _ptr(y), y_tok, y_seq, _ptr(snap),
-        sn_seq, n_seq, n_tok, H, Hk, S, D, scale, l2_eps, norm_eps, _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream, out)))
+        *args, _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream, out)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 65536   # GDN_NOALLOC_SCRATCH_BYTES
+
+
+def gdn_decode_step_noalloc(state: torch.Tensor, x: torch.Tensor, conv_w: torch.Tensor,
+                            conv_state: torch.Tensor, alpha: torch.Tensor, dt: torch.Tensor,
+                            a: torch.Tensor, beta: torch.Tensor, norm_w: torch.Tensor,
+                            z: torch.Tensor, out: torch.Tensor, *, scale: float, l2_eps: float,
+                            norm_eps: float, g: torch.Tensor | None = None,
+                            y: torch.Tensor | None = None, snap: torch.Tensor | None = None,
+                            conv_snap: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """gdn_decode_step with its ticket counters in the library's own device
+    array (no workspace, nothing allocated here or in the library); calls on
+    one GPU share that array, so they must not overlap in time."""
+    args, _, _ = _step_args(state, x, conv_w, conv_state, alpha, dt, a, beta, norm_w, z, out,
+                            scale, l2_eps, norm_eps, g, y, snap, conv_snap)
+    _check("gdn_decode_step_noalloc", _lib.gdn_decode_step_noalloc(*args, _stream(stream, out)))
     return out
 
 

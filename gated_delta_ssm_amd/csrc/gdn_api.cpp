@@ -1,9 +1,101 @@
 // gdn_api.cpp -- the extern "C" entry points declared in include/gdn.h:
 // validate on the host, then hand over to the kernel family's launcher.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+
 #include "gdn.h"
 
 #include "launch.hpp"
 #include "validate.hpp"
+
+namespace {
+
+// The argument block of the one-launch decode step (conv -> gate ->
+// recurrence -> norm), shared by gdn_decode_step and gdn_decode_step_noalloc;
+// cnt is the ticket counter array.
+int launch_step(float *state, int64_t state_seq_stride, const float *x, int64_t x_tok_stride,
+                int64_t x_seq_stride, const float *conv_w, float *conv_state,
+                int64_t conv_state_seq_stride, float *conv_snap, int64_t conv_snap_tok_stride,
+                int64_t conv_snap_seq_stride, const float *alpha, const float *dt,
+                const float *a, const float *beta, const float *norm_w, const float *z,
+                int64_t z_tok_stride, int64_t z_seq_stride, float *out, int64_t out_tok_stride,
+                int64_t out_seq_stride, float *g, float *y, int64_t y_tok_stride,
+                int64_t y_seq_stride, float *snap, int64_t snap_seq_stride, int n_seq, int n_tok,
+                int n_v_heads, int n_qk_heads, int S, int d_conv, float scale, float l2_eps,
+                float norm_eps, int *cnt, hipStream_t stream) {
+  gdn::StepArgs sa{};
+  sa.f.r = gdn::RecurArgs{state,          state_seq_stride, nullptr,     nullptr,
+                          0,              0,                nullptr,     0,
+                          0,              nullptr,          beta,        out,
+                          out_tok_stride, out_seq_stride,   snap,        snap_seq_stride,
+                          n_seq,          n_tok,            n_v_heads,   n_qk_heads,
+                          S,              scale};
+  sa.f.alpha = alpha;
+  sa.f.dt = dt;
+  sa.f.a = a;
+  sa.f.w = norm_w;
+  sa.f.z = z;
+  sa.f.z_tok = z_tok_stride;
+  sa.f.z_seq = z_seq_stride;
+  sa.f.g = g;
+  sa.f.y = y;
+  sa.f.y_tok = y_tok_stride;
+  sa.f.y_seq = y_seq_stride;
+  sa.f.eps = norm_eps;
+  sa.x = x;
+  sa.x_tok = x_tok_stride;
+  sa.x_seq = x_seq_stride;
+  sa.cw = conv_w;
+  sa.hist = conv_state;
+  sa.h_seq = conv_state_seq_stride;
+  sa.csnap = conv_snap;
+  sa.cs_tok = conv_snap_tok_stride;
+  sa.cs_seq = conv_snap_seq_stride;
+  sa.D = d_conv;
+  sa.l2_eps = l2_eps;
+  sa.cnt = cnt;
+  return gdn::launch_decode_step(sa, stream);
+}
+
+// ---- the no-allocation decode step's ticket counters
+// One array per GPU (each device holds its own copy at its own address).  In
+// host code `step_scratch` names a host-side stand-in, never the device
+// memory: kernels and memory operations get the address that
+// hipGetSymbolAddress returns for the current device, kept per device.
+__device__ __align__(256) int step_scratch[GDN_NOALLOC_SCRATCH_BYTES / sizeof(int)];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+int *scratch_dev_ptr[MAX_DEVICES] = {};
+
+__global__ void k_clear_ints(int *p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+// The current device's scratch address; on the first call on a device, look
+// it up and clear the array with a kernel on `stream` (a kernel, not a memset
+// node, so the clear is also valid inside a captured graph).
+int step_scratch_ptr(hipStream_t stream, int **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return GDN_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(step_scratch)) != hipSuccess || !p)
+      return GDN_ERR_LAUNCH;
+    constexpr int n = GDN_NOALLOC_SCRATCH_BYTES / sizeof(int);
+    const int rc = gdn::launch_kernel(k_clear_ints, dim3((n + 255) / 256), dim3(256), 0, stream,
+                                      static_cast<int *>(p), n);
+    if (rc != GDN_OK) return rc;
+    scratch_dev_ptr[dev] = static_cast<int *>(p);
+  }
+  *out = scratch_dev_ptr[dev];
+  return GDN_OK;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -16,6 +108,7 @@ const char *gdn_strerror(int status) {
     case GDN_ERR_ALIAS: return "an output overlaps an input where that is not allowed";
     case GDN_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
     case GDN_ERR_LAUNCH: return "the HIP runtime refused the kernel launch";
+    case GDN_ERR_SCRATCH: return "sizes exceed the fixed scratch array of a no-allocation call";
     default: return "unknown gdn status";
   }
 }
@@ -244,38 +337,46 @@ int gdn_decode_step(float *state, int64_t state_seq_stride, const float *x, int6
       y_tok_stride, y_seq_stride, snap, snap_seq_stride, n_seq, n_tok, n_v_heads, n_qk_heads, S,
       d_conv, workspace, workspace_bytes);
   if (rc != GDN_OK) return rc;
-  gdn::StepArgs sa{};
-  sa.f.r = gdn::RecurArgs{state,          state_seq_stride, nullptr,     nullptr,
-                          0,              0,                nullptr,     0,
-                          0,              nullptr,          beta,        out,
-                          out_tok_stride, out_seq_stride,   snap,        snap_seq_stride,
-                          n_seq,          n_tok,            n_v_heads,   n_qk_heads,
-                          S,              scale};
-  sa.f.alpha = alpha;
-  sa.f.dt = dt;
-  sa.f.a = a;
-  sa.f.w = norm_w;
-  sa.f.z = z;
-  sa.f.z_tok = z_tok_stride;
-  sa.f.z_seq = z_seq_stride;
-  sa.f.g = g;
-  sa.f.y = y;
-  sa.f.y_tok = y_tok_stride;
-  sa.f.y_seq = y_seq_stride;
-  sa.f.eps = norm_eps;
-  sa.x = x;
-  sa.x_tok = x_tok_stride;
-  sa.x_seq = x_seq_stride;
-  sa.cw = conv_w;
-  sa.hist = conv_state;
-  sa.h_seq = conv_state_seq_stride;
-  sa.csnap = conv_snap;
-  sa.cs_tok = conv_snap_tok_stride;
-  sa.cs_seq = conv_snap_seq_stride;
-  sa.D = d_conv;
-  sa.l2_eps = l2_eps;
-  sa.cnt = static_cast<int *>(workspace);
-  return gdn::launch_decode_step(sa, stream);
+  return launch_step(state, state_seq_stride, x, x_tok_stride, x_seq_stride, conv_w, conv_state,
+                     conv_state_seq_stride, conv_snap, conv_snap_tok_stride,
+                     conv_snap_seq_stride, alpha, dt, a, beta, norm_w, z, z_tok_stride,
+                     z_seq_stride, out, out_tok_stride, out_seq_stride, g, y, y_tok_stride,
+                     y_seq_stride, snap, snap_seq_stride, n_seq, n_tok, n_v_heads, n_qk_heads,
+                     S, d_conv, scale, l2_eps, norm_eps, static_cast<int *>(workspace), stream);
+}
+
+int gdn_decode_step_noalloc(float *state, int64_t state_seq_stride, const float *x,
+                            int64_t x_tok_stride, int64_t x_seq_stride, const float *conv_w,
+                            float *conv_state, int64_t conv_state_seq_stride, float *conv_snap,
+                            int64_t conv_snap_tok_stride, int64_t conv_snap_seq_stride,
+                            const float *alpha, const float *dt, const float *a,
+                            const float *beta, const float *norm_w, const float *z,
+                            int64_t z_tok_stride, int64_t z_seq_stride, float *out,
+                            int64_t out_tok_stride, int64_t out_seq_stride, float *g, float *y,
+                            int64_t y_tok_stride, int64_t y_seq_stride, float *snap,
+                            int64_t snap_seq_stride, int n_seq, int n_tok, int n_v_heads,
+                            int n_qk_heads, int S, int d_conv, float scale, float l2_eps,
+                            float norm_eps, hipStream_t stream) {
+  // the fixed array's limit first: a clear error for sizes beyond it
+  if (n_seq >= 1 && n_qk_heads >= 1 &&
+      gdn::step_workspace_bytes(n_seq, n_qk_heads) > GDN_NOALLOC_SCRATCH_BYTES)
+    return GDN_ERR_SCRATCH;
+  const int rc = gdn::check_step(
+      state, state_seq_stride, x, x_tok_stride, x_seq_stride, conv_w, conv_state,
+      conv_state_seq_stride, conv_snap, conv_snap_tok_stride, conv_snap_seq_stride, alpha, dt, a,
+      beta, norm_w, z, z_tok_stride, z_seq_stride, out, out_tok_stride, out_seq_stride, g, y,
+      y_tok_stride, y_seq_stride, snap, snap_seq_stride, n_seq, n_tok, n_v_heads, n_qk_heads, S,
+      d_conv, nullptr, 0, /*lib_scratch=*/true);
+  if (rc != GDN_OK) return rc;
+  int *cnt = nullptr;
+  const int src = step_scratch_ptr(stream, &cnt);
+  if (src != GDN_OK) return src;
+  return launch_step(state, state_seq_stride, x, x_tok_stride, x_seq_stride, conv_w, conv_state,
+                     conv_state_seq_stride, conv_snap, conv_snap_tok_stride,
+                     conv_snap_seq_stride, alpha, dt, a, beta, norm_w, z, z_tok_stride,
+                     z_seq_stride, out, out_tok_stride, out_seq_stride, g, y, y_tok_stride,
+                     y_seq_stride, snap, snap_seq_stride, n_seq, n_tok, n_v_heads, n_qk_heads,
+                     S, d_conv, scale, l2_eps, norm_eps, cnt, stream);
 }
 
 }  // extern "C"

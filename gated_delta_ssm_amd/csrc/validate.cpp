@@ -321,7 +321,7 @@ int check_step(const float *state, int64_t st_seq, const float *x, int64_t x_tok
                int64_t z_seq, const float *out, int64_t o_tok, int64_t o_seq, const float *g,
                const float *y, int64_t y_tok, int64_t y_seq, const float *snap, int64_t sn_seq,
                int n_seq, int n_tok, int H, int Hk, int S, int D, const void *ws,
-               size_t ws_bytes) {
+               size_t ws_bytes, bool lib_scratch) {
   if (n_seq < 1 || n_tok < 1 || H < 1 || Hk < 1 || H % Hk != 0) return GDN_ERR_SHAPE;
   if (n_tok > (S <= 128 ? 32 : 16)) return GDN_ERR_SHAPE;   // positions staged in LDS
   if (D < 2 || D > 8) return GDN_ERR_SHAPE;
@@ -347,7 +347,9 @@ int check_step(const float *state, int64_t st_seq, const float *x, int64_t x_tok
   if (!aligned(x, 16) || !aligned(cw, 16) || !aligned(hist, 16) || (csnap && !aligned(csnap, 16)) ||
       x_tok % 4 || x_seq % 4 || h_seq % 4 || cs_tok % 4 || cs_seq % 4)
     return GDN_ERR_SHAPE;
-  if (!ws || ws_bytes < step_workspace_bytes(n_seq, Hk) || !aligned(ws, 4))
+  // the library's own scratch array is checked by its caller and cannot
+  // overlap caller memory
+  if (!lib_scratch && (!ws || ws_bytes < step_workspace_bytes(n_seq, Hk) || !aligned(ws, 4)))
     return GDN_ERR_WORKSPACE;
   const int64_t row = (int64_t)H * S, st_len = (int64_t)S * S * H;
   const Span in[] = {span_of(x, n_seq, x_seq, n_tok, x_tok, C),
@@ -367,7 +369,7 @@ int check_step(const float *state, int64_t st_seq, const float *x, int64_t x_tok
                        span_of(hist, n_seq, h_seq, 1, 0, hlen),
                        csnap && n_snap > 0 ? span_of(csnap, n_seq, cs_seq, n_snap, cs_tok, hlen)
                                            : Span{},
-                       Span{(uintptr_t)ws, (uintptr_t)ws + ws_bytes}};
+                       lib_scratch ? Span{} : Span{(uintptr_t)ws, (uintptr_t)ws + ws_bytes}};
   constexpr int NO = sizeof(outs) / sizeof(outs[0]);
   for (const Span &o : outs)
     for (const Span &i : in)

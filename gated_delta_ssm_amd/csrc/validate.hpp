@@ -60,6 +60,6 @@ int check_step(const float *state, int64_t st_seq, const float *x, int64_t x_tok
                int64_t z_seq, const float *out, int64_t o_tok, int64_t o_seq, const float *g,
                const float *y, int64_t y_tok, int64_t y_seq, const float *snap, int64_t sn_seq,
                int n_seq, int n_tok, int H, int Hk, int S, int D, const void *ws,
-               size_t ws_bytes);
+               size_t ws_bytes, bool lib_scratch = false);
 
 }  // namespace gdn

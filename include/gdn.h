@@ -45,7 +45,8 @@ typedef enum {
   GDN_ERR_UNSUPPORTED = -3, /* a valid shape this library has no kernel for */
   GDN_ERR_ALIAS = -4,       /* outputs overlap inputs where that is not allowed */
   GDN_ERR_WORKSPACE = -5,   /* the workspace is missing, too small or misaligned */
-  GDN_ERR_LAUNCH = -6       /* the HIP runtime refused the launch */
+  GDN_ERR_LAUNCH = -6,      /* the HIP runtime refused the launch */
+  GDN_ERR_SCRATCH = -7      /* the sizes exceed a fixed on-device scratch array */
 } gdn_status;
 
 /* Static, NUL-terminated description of a status code. */
@@ -388,6 +389,41 @@ int gdn_decode_step(float *state, int64_t state_seq_stride, const float *x, int6
                     int n_tok, int n_v_heads, int n_qk_heads, int S, int d_conv, float scale,
                     float l2_eps, float norm_eps, void *workspace, size_t workspace_bytes,
                     hipStream_t stream);
+
+/* Bytes of the on-device scratch array of gdn_decode_step_noalloc (per GPU). */
+#define GDN_NOALLOC_SCRATCH_BYTES 65536
+
+/*
+ * gdn_decode_step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, kernels and results (bit for bit) as gdn_decode_step, with
+ * no workspace argument: the ticket counters live in a file-scope device array
+ * of GDN_NOALLOC_SCRATCH_BYTES bytes inside the library, one copy per GPU,
+ * held until the process ends.  The call allocates nothing (no hipMalloc, no
+ * hipFree, no allocating library routine).
+ *
+ *   Limit: gdn_decode_step_workspace_bytes(n_seq, n_qk_heads) must not exceed
+ *   GDN_NOALLOC_SCRATCH_BYTES (n_seq * n_qk_heads <= 8192), else
+ *   GDN_ERR_SCRATCH before anything is launched.
+ *   Set-up: the first call on a device (with that device current) looks up
+ *   the array's device address and clears it with a small kernel on `stream`;
+ *   every call whose work completes leaves the counters it used at zero.
+ *   Sharing: every call on one GPU uses that GPU's one array, so calls whose
+ *   work may overlap in time on one GPU (different streams, or concurrent
+ *   host threads) race on the counters; serialise them on one stream.
+ */
+int gdn_decode_step_noalloc(float *state, int64_t state_seq_stride, const float *x,
+                            int64_t x_tok_stride, int64_t x_seq_stride, const float *conv_w,
+                            float *conv_state, int64_t conv_state_seq_stride, float *conv_snap,
+                            int64_t conv_snap_tok_stride, int64_t conv_snap_seq_stride,
+                            const float *alpha, const float *dt, const float *a,
+                            const float *beta, const float *norm_w, const float *z,
+                            int64_t z_tok_stride, int64_t z_seq_stride, float *out,
+                            int64_t out_tok_stride, int64_t out_seq_stride, float *g, float *y,
+                            int64_t y_tok_stride, int64_t y_seq_stride, float *snap,
+                            int64_t snap_seq_stride, int n_seq, int n_tok, int n_v_heads,
+                            int n_qk_heads, int S, int d_conv, float scale, float l2_eps,
+                            float norm_eps, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -12,7 +12,7 @@ import gated_delta_ssm_amd as gdn
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADERS = [os.path.join(ROOT, "include", h) for h in ("gdn.h", "gdn_measure.h")]
 
-OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_ALIAS, ERR_WS = 0, -1, -2, -3, -4, -5
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_ALIAS, ERR_WS, ERR_SCRATCH = 0, -1, -2, -3, -4, -5, -7
 FAKE = 0x10000            # never dereferenced: validation rejects first
 L = gdn._lib
 
@@ -32,7 +32,7 @@ def test_header_declarations_all_exported():
 
 
 def test_strerror_and_version():
-    for s in (0, -1, -2, -3, -4, -5, -6):
+    for s in (0, -1, -2, -3, -4, -5, -6, -7):
         assert len(L.gdn_strerror(s)) >= 2
     assert L.gdn_version() >= 100
 
@@ -288,6 +288,34 @@ def test_step_validation_and_workspace_query():
     assert step(ws=FAKE) == ERR_ALIAS                                   # counters over the state
     assert step(csnap=FAKE + 6 * MB + 256, cst=768, css=768) == ERR_ALIAS  # snapshot over history
     assert step(out=FAKE + 4 * MB + 512) == ERR_ALIAS                   # out over x
+
+
+def step_noalloc(n=2, **kw):
+    S, H, Hk = 32, 4, kw.pop("Hk", 2)
+    MB = 1 << 20
+    C = (2 * Hk + H) * S
+    a = dict(state=FAKE, x=FAKE + 4 * MB, cw=FAKE + 5 * MB, hist=FAKE + 6 * MB,
+             alpha=FAKE + 16 * MB, dt=FAKE + 17 * MB, a=FAKE + 18 * MB, beta=FAKE + 20 * MB,
+             w=FAKE + 22 * MB, z=FAKE + 24 * MB, out=FAKE + 28 * MB, D=4, T=2)
+    a.update(kw)
+    return L.gdn_decode_step_noalloc(
+        a["state"], H * S * S, a["x"], C, 2 * C, a["cw"], a["hist"], (a["D"] - 1) * C, None, 0, 0,
+        a["alpha"], a["dt"], a["a"], a["beta"], a["w"], a["z"], H * S, 2 * H * S, a["out"],
+        H * S, 2 * H * S, None, None, 0, 0, None, 0, n, a["T"], H, Hk, S, a["D"], 0.125, 1e-6,
+        1e-6, None)
+
+
+def test_step_noalloc_validation():
+    # the fixed scratch array holds n_seq * n_qk_heads * 2 counters of 4 bytes
+    m = re.search(r"#define GDN_NOALLOC_SCRATCH_BYTES (\d+)", open(HEADERS[0]).read())
+    assert m and int(m.group(1)) == gdn.NOALLOC_SCRATCH_BYTES == 65536
+    assert step_noalloc(n=4097, Hk=2) == ERR_SCRATCH                   # 8194 > 8192 pairs
+    assert step_noalloc(n=4097, Hk=2, x=None) == ERR_SCRATCH            # the limit comes first
+    # the workspace-free call keeps every other rule of gdn_decode_step
+    assert step_noalloc(D=5) == ERR_UNSUP
+    assert step_noalloc(T=33) == ERR_SHAPE and step_noalloc(Hk=3) == ERR_SHAPE
+    assert step_noalloc(x=None) == ERR_NULL and step_noalloc(hist=None) == ERR_NULL
+    assert step_noalloc(hist=FAKE + 4 * (1 << 20) + 64) == ERR_ALIAS
 
 
 def test_stream_copy_validation():
