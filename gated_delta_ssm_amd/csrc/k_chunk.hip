@@ -28,12 +28,18 @@
 //     XCD so they share its L2.  A chunk's operands are requested while the
 //     chunk before it runs.
 //
-// Precision: every contraction runs on MFMA v_mfma_f32_16x16x32_bf16 with each
-// fp32 operand split into bf16 hi + lo, accumulating hi*hi + hi*lo + lo*hi in
-// fp32 (relative error ~2^-16 per product instead of bf16's 2^-8).  The
-// triangular inverse, the gate cumsum, every exponential and the state carry
-// are fp32.  Exponentials are only taken of non-positive arguments (masked
-// before the exp), so g must be <= 0, which the decay gate guarantees.
+// Precision: phase A's contractions run on MFMA v_mfma_f32_16x16x32_bf16 with
+// each fp32 operand split into bf16 hi + lo, accumulating hi*hi + hi*lo +
+// lo*hi in fp32 (relative error ~2^-16 per product instead of bf16's 2^-8).
+// Phase B's operands W, Q', K' are stored as fp16 (their entries are bounded
+// by 1, see the workspace notes); its products take them as they are on
+// v_mfma_f32_16x16x32_f16 against the fp32 state or U tile split into fp16
+// hi + lo (hi*W + lo*W: the split keeps 22 significant bits), each tile first
+// scaled by a power of two chosen from a running bound on its norm so that
+// the split cannot overflow fp16.  The triangular inverse, the gate cumsum,
+// every exponential and the state carry are fp32.  Exponentials are only
+// taken of non-positive arguments (masked before the exp), so g must be <= 0,
+// which the decay gate guarantees.
 //
 // MFMA operand layout (16x16x32 bf16, wave64): lane l holds row (l % 16) of
 // A / column (l % 16) of B, and 8 k values chosen by l / 16; the accumulator
@@ -42,6 +48,7 @@
 #include <hip/hip_runtime.h>
 
 #include "bf16_frag.hpp"
+#include "wave.hpp"
 #include "gdn.h"
 #include "launch.hpp"
 
@@ -52,8 +59,8 @@ namespace {
 constexpr int CH = 64;           // positions per chunk
 constexpr int DK = 128;          // key dimension (state rows)
 constexpr int DV = 128;          // value dimension (state columns)
-constexpr int NBLK = 16;         // value columns per scan workgroup
-constexpr int NVB = DV / NBLK;   // scan workgroups per head
+constexpr int NBLK = 16;         // value columns per value tile of the scan
+constexpr int NVB = DV / NBLK;   // value tiles per head
 
 // ----------------------------------------------------------------------------- workspace
 // Per (sequence, head, chunk), all offsets in bytes, each region 256-aligned.
@@ -68,19 +75,32 @@ constexpr int NVB = DV / NBLK;   // scan workgroups per head
 //
 // W, Q' and K' are stored as fp16 (relative rounding 2^-11), half the bytes
 // of a bf16 hi + lo pair: the scan is bound by the operand bytes each CU
-// pulls from L2 per chunk, so this halves its operand traffic.  The scan
-// splits each fp16 value into bf16 hi + lo in registers, which is exact (11
-// significant bits), so its products stay split-bf16 and its own operands --
-// the state and U tiles -- keep fp32 range.  W, Q' and K' themselves are
-// bounded by the unit-length keys and queries (K' entries by |k|, W and Q'
-// through T = (I + A)^{-1} with beta <= 1), far inside fp16's range.
+// pulls from L2 per chunk.  They are small: with beta_t |k_t|^2 <= 2 every
+// factor I - beta_t k_t k_t^T has spectral norm <= 1, and with g <= 0
+// row t of W is beta_t e^{G_t} M^T k_t and row t of Q' is e^{G_t} M'^T q_t
+// for products M, M' of such factors, so |W[t][i]| <= beta_t |k_t| and
+// |Q'[t][i]| <= |q_t|; |K'[t][i]| <= |k_t[i]|.  For unit-length keys and
+// queries every entry is at most 2 in magnitude.
+// K' is kept as two fp16 planes, hi and lo = fp16(K' - hi) (22 significant
+// bits): the state update K'^T U sums 64 rank-one terms that can cancel
+// (repeated or low-rank keys with beta near 1 and no decay make the terms of
+// size |v| while their sum stays of size |v|), so single fp16 rounding of K'
+// would show in the state at ~2^-11 * sqrt(64) relative; W and Q' meet no
+// such cancellation and stay single fp16.
+// The header (WS_G) holds e^{G_n}, b = sum_t beta_t |k_t| |v_t| and
+// a = max_t beta_t |k_t| over the chunk's positions: a chunk raises the
+// state's spectral norm by at most b (each position adds at most
+// beta_t |k_t| |v_t|), and every entry of U (row t is the sequential delta
+// beta_t (v_t - (decayed S_{t-1})^T k_t)) is at most b + a * (the state's
+// bound), which is how the scan picks its fp16 scaling without a reduction.
 constexpr size_t WS_PLANE = (size_t)CH * DK * 2;        // one fp16 64x128 matrix
 constexpr size_t WS_W = 0;                              // W   (4 token tiles x 4 k-steps)
 constexpr size_t WS_Q = WS_PLANE;                       // Q'  (4 x 4)
-constexpr size_t WS_K = 2 * WS_PLANE;                   // K'^T (8 key tiles x 2 k-steps)
-constexpr size_t WS_U = 3 * WS_PLANE;                   // Ut  fp32 accumulator tiles
+constexpr size_t WS_K = 2 * WS_PLANE;                   // K'^T (8 key tiles x 2 k-steps), hi
+constexpr size_t WS_KL = 3 * WS_PLANE;                  // K'^T lo: K' - hi, in fp16
+constexpr size_t WS_U = 4 * WS_PLANE;                   // Ut  fp32 accumulator tiles
 constexpr size_t WS_O = WS_U + (size_t)DV * CH * 4;     // Oi  fp32 accumulator tiles
-constexpr size_t WS_G = WS_O + (size_t)DV * CH * 4;     // e^{G_n}
+constexpr size_t WS_G = WS_O + (size_t)DV * CH * 4;     // e^{G_n}, b, a (float4)
 constexpr size_t WS_CHUNK = WS_G + 256;
 
 typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
@@ -92,13 +112,6 @@ __device__ __forceinline__ int frag_off(int m, int ks, int n_ks, int lane) {
 __device__ __forceinline__ h16x8 frag_ws(const u16 *base, int m, int ks, int n_ks, int lane) {
   return *reinterpret_cast<const h16x8 *>(base + frag_off(m, ks, n_ks, lane));
 }
-// fp16 -> bf16 hi + lo, exactly (an fp16 value has 11 significant bits)
-__device__ __forceinline__ Frag split_h(const h16x8 &x) {
-  float v[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = (float)x[e];
-  return split8(v);
-}
 // 8 floats -> one 16-byte store of fp16 (round to nearest even)
 __device__ __forceinline__ void store8_h(u16 *p, const float (&x)[8]) {
   h16x8 h;
@@ -106,6 +119,29 @@ __device__ __forceinline__ void store8_h(u16 *p, const float (&x)[8]) {
   for (int e = 0; e < 8; ++e) h[e] = (_Float16)x[e];
   *reinterpret_cast<h16x8 *>(p) = h;
 }
+__device__ __forceinline__ float sumsq8(const float4 &a, const float4 &b) {
+  return a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w + b.x * b.x + b.y * b.y + b.z * b.z +
+         b.w * b.w;
+}
+// maximum over the wave (exact in any order)
+__device__ __forceinline__ float group_max64(float x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
+  return x;
+}
+
+// 8 floats -> 16-byte stores of fp16 hi and lo = fp16(x - hi)
+__device__ __forceinline__ void store8_h2(u16 *ph, u16 *pl, const float (&x)[8]) {
+  h16x8 h, l;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    h[e] = (_Float16)x[e];
+    l[e] = (_Float16)(x[e] - (float)h[e]);
+  }
+  *reinterpret_cast<h16x8 *>(ph) = h;
+  *reinterpret_cast<h16x8 *>(pl) = l;
+}
+
 // float offset of the accumulator tile (value tile d, token tile m) for lane
 __device__ __forceinline__ int acc_off(int d, int m, int lane) {
   return ((d * 4 + m) * 64 + lane) * 4;
@@ -120,7 +156,7 @@ __device__ __forceinline__ int acc_off(int d, int m, int lane) {
 //   L_A : A, then T in place (fp32 [64][68]);  L_S: four 16x16 blocks (pitch XP) of the inverse
 //         (T1 = T diag(beta e^G) and T2 = T diag(beta) are formed from it as
 //         fragments, in registers)
-//   L_G : G, beta, e^G, e^{G_n - G}
+//   L_G : G, beta, e^G, e^{G_n - G};  L_N: |k_t|^2, |v_t|^2
 // The products are computed transposed (feature index as the MFMA row):
 //   W^T = K^T T1^T,  Ut^T = V^T T2^T,  Q'^T = e^G Q^T - W^T (LQK)^T,
 //   Oi^T = Ut^T (LQK)^T
@@ -138,7 +174,8 @@ constexpr int L_A = L_L + TILE64;
 constexpr int L_S = L_A + CH * PA * 4;
 constexpr int XP = 17;   // pitch (fp32) of the inverse's scratch blocks
 constexpr int L_G = L_S + 4 * 16 * XP * 4;
-constexpr int L_TOTAL = L_G + 4 * CH * 4;
+constexpr int L_N = L_G + 4 * CH * 4;   // |k_t|^2, |v_t|^2
+constexpr int L_TOTAL = L_N + 2 * CH * 4;
 static_assert(L_TOTAL <= 160 * 1024, "phase A LDS fits one CU");
 
 // Lower 16x16 tiles of K K^T (A = beta_t e^{G_t - G_s} k_t.k_s, strictly lower)
@@ -419,6 +456,7 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
   float *scratch = reinterpret_cast<float *>(smem + L_S);
   float *sG = reinterpret_cast<float *>(smem + L_G);
   float *sBeta = sG + CH, *sEG = sG + 2 * CH, *sEGn = sG + 3 * CH;
+  float *sNK = reinterpret_cast<float *>(smem + L_N), *sNV = sNK + CH;
 
   // (L o QK^T) and A, which lie back to back, are cleared once: every item
   // writes every entry of their lower 16x16 tiles (zeros above the diagonal
@@ -473,13 +511,15 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
     sEGn[lane] = expf(gn - x);
   }
   load_gb(in, nx, lane, gv, bv);
-  // S1. K, Q rows -> LDS (bf16 hi/lo)
+  // S1. K, Q rows -> LDS (bf16 hi/lo); |k_t|^2 of each row (16 lanes per row)
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     int row, col;
     row8_of(i, tid, row, col);
     store_row8(kh + row * PR + col, klo + row * PR + col, kr[2 * i], kr[2 * i + 1], row < n);
     store_row8(qh + row * PR + col, qlo + row * PR + col, qr[2 * i], qr[2 * i + 1], row < n);
+    const float nk = group_sum<16>(sumsq8(kr[2 * i], kr[2 * i + 1]));
+    if ((tid & 15) == 0) sNK[row] = row < n ? nk : 0.0f;
   }
   load_kq(in, nx, tid, kr, qr);
   __syncthreads();
@@ -493,10 +533,11 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
   } else {
     lower_tiles<2>(w, kh, klo, qh, qlo, sA, lqh, lql, sG, sBeta, l16, kg);
   }
-  // S2b. K'^T fragments (K' = diag(e^{G_n - G}) K) straight from the K tile:
-  // wave w writes key tile w, both token k-steps
+  // S2b. K'^T fragments (K' = diag(e^{G_n - G}) K) straight from the K tile,
+  // as fp16 hi and lo planes: wave w writes key tile w, both token k-steps
   {
     u16 *ktg = reinterpret_cast<u16 *>(wc + WS_K);
+    u16 *ktl = reinterpret_cast<u16 *>(wc + WS_KL);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const Frag f = frag_tr(kh, klo, PR, 32 * ks, 16 * w, kg, l16);
@@ -504,7 +545,7 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         x[e] = (bf16_value((u16)f.hi[e]) + bf16_value((u16)f.lo[e])) * sEGn[pi_k(32 * ks, kg, e)];
-      store8_h(ktg + frag_off(w, ks, 2, lane), x);
+      store8_h2(ktg + frag_off(w, ks, 2, lane), ktl + frag_off(w, ks, 2, lane), x);
     }
   }
   __syncthreads();
@@ -528,6 +569,8 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
     int row, col;
     row8_of(i, tid, row, col);
     store_row8(qh + row * PR + col, qlo + row * PR + col, vr[2 * i], vr[2 * i + 1], row < n);
+    const float nv = group_sum<16>(sumsq8(vr[2 * i], vr[2 * i + 1]));
+    if ((tid & 15) == 0) sNV[row] = row < n ? nv : 0.0f;
   }
   load_v(in, nx, tid, vr);
   __syncthreads();  // every diagonal block read before any is overwritten
@@ -682,8 +725,15 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
       store8_h(qg + frag_off(2 * tp + m, kp, 4, lane), xq);
     }
   }
-  // every thread stores the same value: no store behind a branch
-  *reinterpret_cast<float *>(wc + WS_G) = sEG[CH - 1];
+  // the chunk's header: every wave forms b and a from the row norms with the
+  // same butterflies, so every thread stores the same bits (no store behind
+  // a branch)
+  {
+    const float bk = sBeta[lane] * sqrtf(sNK[lane]);
+    const float b = group_sum<64>(bk * sqrtf(sNV[lane]));
+    const float am = group_max64(bk);
+    *reinterpret_cast<float4 *>(wc + WS_G) = make_float4(sEG[CH - 1], b, am, 0.0f);
+  }
   __syncthreads();   // the next item rewrites every LDS tile
   it = nx;
   };
@@ -700,25 +750,141 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
 // Wave w owns key tile w of the state (one accumulator) and token tile w & 3
 // of P^T (w < 4) or of y^T (w >= 4).  S and U travel through LDS as row-major
 // [key][j] / [token][j] tiles and are read back by transpose reads.
+template <int VT>
 struct ChunkOps {
   h16x8 b[4];    // W (P waves) or Q' (y waves) fragments of token tile w & 3, 4 key k-steps
-  h16x8 k[2];    // K'^T fragments of key tile w, 2 token k-steps
-  float4 add;    // Ut (P waves) or Oi (y waves) accumulator tile (b, w & 3)
-  float gam;     // e^{G_n}
+  h16x8 k[2];    // K'^T fragments of key tile w, 2 token k-steps (hi)
+  h16x8 kl[2];   // and their lo parts
+  float4 add[VT];  // Ut (P waves) or Oi (y waves) accumulator tiles (value tile, w & 3)
+  float hdr;     // header word lane & 3: e^{G_n}, b, a, 0
 };
 
-__device__ __forceinline__ void load_chunk(ChunkOps &o, const unsigned char *wc, int w, int lane,
-                                           int blk) {
+// The header is read as one word per lane (lane l: word l & 3), a vector
+// load: a scalar load of it would share the LDS wait counter, so every LDS
+// wait behind it would also wait for the scalar cache.  hdr_word() hands every
+// lane word i.
+__device__ __forceinline__ float load_hdr(const unsigned char *wc, int lane) {
+  return reinterpret_cast<const float *>(wc + WS_G)[lane & 3];
+}
+__device__ __forceinline__ float hdr_word(float hdr, int i) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, hdr), i));
+}
+
+// blk: the workgroup's first value tile
+template <int VT>
+__device__ __forceinline__ void load_chunk(ChunkOps<VT> &o, const unsigned char *wc, int w,
+                                           int lane, int blk) {
   const bool pw = w < 4;
   const u16 *bg = reinterpret_cast<const u16 *>(wc + (pw ? WS_W : WS_Q));
   const u16 *kgp = reinterpret_cast<const u16 *>(wc + WS_K);
+  const u16 *klp = reinterpret_cast<const u16 *>(wc + WS_KL);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) o.b[ks] = frag_ws(bg, w & 3, ks, 4, lane);
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) o.k[ks] = frag_ws(kgp, w, ks, 2, lane);
+  for (int ks = 0; ks < 2; ++ks) {
+    o.k[ks] = frag_ws(kgp, w, ks, 2, lane);
+    o.kl[ks] = frag_ws(klp, w, ks, 2, lane);
+  }
   const float *addp = reinterpret_cast<const float *>(wc + (pw ? WS_U : WS_O));
-  o.add = *reinterpret_cast<const float4 *>(addp + acc_off(blk, w & 3, lane));
-  o.gam = *reinterpret_cast<const float *>(wc + WS_G);
+#pragma unroll
+  for (int d = 0; d < VT; ++d)
+    o.add[d] = *reinterpret_cast<const float4 *>(addp + acc_off(blk + d, w & 3, lane));
+  o.hdr = load_hdr(wc, lane);
+}
+
+// ---- fp16 operands of the scan
+typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
+struct FragH {
+  h16x8 hi, lo;
+};
+// two floats -> fp16 hi and lo halves (x = hi + lo + O(2^-22 |x|) for x in
+// fp16's normal range; x - hi is exact in fp32)
+__device__ __forceinline__ void split2_h(float a, float b, unsigned &hi, unsigned &lo) {
+  const h16x2 h = __builtin_convertvector(f32x2{a, b}, h16x2);
+  const h16x2 l = __builtin_convertvector(f32x2{a - (float)h[0], b - (float)h[1]}, h16x2);
+  hi = __builtin_bit_cast(unsigned, h);
+  lo = __builtin_bit_cast(unsigned, l);
+}
+// 4 floats times `sc` (a power of two) split into 4 consecutive fp16 per plane
+__device__ __forceinline__ void store4_split_h(u16 *hi, u16 *lo, const f32x4 &x, float sc) {
+  unsigned h0, l0, h1, l1;
+  split2_h(x[0] * sc, x[1] * sc, h0, l0);
+  split2_h(x[2] * sc, x[3] * sc, h1, l1);
+  *reinterpret_cast<uint2 *>(hi) = make_uint2(h0, h1);
+  *reinterpret_cast<uint2 *>(lo) = make_uint2(l0, l1);
+}
+__device__ __forceinline__ h16x8 cat_h(v4s a, v4s b) {
+  return __builtin_bit_cast(h16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+// frag_tr for fp16 planes (the transpose read moves 16-bit values of any type)
+__device__ __forceinline__ FragH frag_tr_h(const u16 *hi, const u16 *lo, int pitch, int k0,
+                                           int nb, int kg, int l16) {
+  const int o = (k0 + 4 * kg + (l16 >> 2)) * pitch + nb + 4 * (l16 & 3);
+  FragH f;
+  f.hi = cat_h(tr4(hi + o), tr4(hi + o + 16 * pitch));
+  f.lo = cat_h(tr4(lo + o), tr4(lo + o + 16 * pitch));
+  return f;
+}
+// c += (a.hi + a.lo) b on fp16 MFMA (b exact in fp16)
+__device__ __forceinline__ f32x4 mfma2_h(const FragH &a, const h16x8 &b, f32x4 c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.lo, b, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.hi, b, c, 0, 0, 0);
+  return c;
+}
+// c += (a.hi + a.lo)(bh + bl), dropping a.lo * bl (2^-22 relative)
+__device__ __forceinline__ f32x4 mfma3_h(const FragH &a, const h16x8 &bh, const h16x8 &bl,
+                                         f32x4 c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.lo, bh, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.hi, bl, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.hi, bh, c, 0, 0, 0);
+  return c;
+}
+
+// Power-of-two scales of one chunk, identical in every wave (they follow from
+// the running bound and the chunk header only): the state tile is multiplied
+// by sS = 2^-eS and U by sU = 2^-eU before the fp16 split, with e chosen so
+// that the bound times the scale is below 2^14 (fp16 reaches 65504).
+struct Scales {
+  float sS, iS, sU, iU;   // 2^-eS, 2^eS, 2^-eU, 2^eU
+};
+__device__ __forceinline__ float pow2i(int e) { return __builtin_bit_cast(float, (e + 127) << 23); }
+__device__ __forceinline__ Scales chunk_scales(float &bound, float hdr) {
+  const float hb = hdr_word(hdr, 1), ha = hdr_word(hdr, 2);
+  const float bs = bound;                   // the state entering the chunk
+  const float nb = bound + hb;              // every state inside it
+  const float bu = hb + ha * nb;            // every entry of U
+  bound = nb;
+  int es, eu;
+  (void)frexpf(bs, &es);                    // bs = m 2^es, m in [0.5, 1)
+  (void)frexpf(bu, &eu);
+  es = min(max(es - 14, -100), 100);
+  eu = min(max(eu - 14, -100), 100);
+  return Scales{pow2i(-es), pow2i(es), pow2i(-eu), pow2i(eu)};
+}
+
+// The Frobenius norm (a bound on the spectral norm) of the state's columns in
+// each value tile, over the 8 waves that hold its key tiles: each wave's
+// butterfly sum, then the 8 partial sums in a fixed order, so every wave gets
+// the same bits.  `red` is VT x 8 floats of LDS owned by the 8 waves.  Each
+// value tile carries its own bound (and so its own scales), which makes a
+// tile's arithmetic independent of how many tiles a workgroup holds.
+template <int VT>
+__device__ __forceinline__ void tile_norms(const f32x4 (&st)[VT], float *red, int w, int lane,
+                                           float (&bound)[VT]) {
+#pragma unroll
+  for (int d = 0; d < VT; ++d) {
+    const float ss = group_sum<64>(st[d][0] * st[d][0] + st[d][1] * st[d][1] +
+                                   st[d][2] * st[d][2] + st[d][3] * st[d][3]);
+    if (lane == 0) red[8 * d + w] = ss;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int d = 0; d < VT; ++d) {
+    float t = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t += red[8 * d + i];
+    bound[d] = sqrtf(t);
+  }
 }
 
 // The chunks one (sequence, head) walks in phase B: its first workspace slot,
@@ -767,65 +933,111 @@ __device__ __forceinline__ void xcd_order(int b, int nwg, int per, int &sh, int 
 
 constexpr int SPB = 24;   // pitch (bf16) of the [128][16] S tile and the [64][16] U tile
 
-__device__ __forceinline__ void scan_chunk(const ChunkOps &o, f32x4 &st, u16 *ssh, u16 *ssl,
-                                           u16 *suh, u16 *sul, float *yc, int64_t y_tok, int n,
+// One chunk of the scan on a workgroup's VT value tiles.  The state tile of
+// value tile d (values 16d + 4kg + r of key 16w + l16) goes to LDS as rows
+// [i][j] of the S tile (pitch SP); P waves (w < 4) form U^T = Ut^T - S^T W^T
+// for token tile w and write it as rows [t][j] of the U tile; y waves form
+// y^T = scale (S^T Q'^T + Oi^T); then every wave updates its state tiles with
+// U^T K'.  The B operands (W or Q', K') are loaded once and serve all VT tiles.
+template <int VT>
+__device__ __forceinline__ void scan_chunk(const ChunkOps<VT> &o, float (&bound)[VT],
+                                           f32x4 (&st)[VT], u16 *ssh, u16 *ssl, u16 *suh,
+                                           u16 *sul, float *yc, int64_t y_tok, int n,
                                            float scale, int w, int l16, int kg) {
-  // state tile (values 4kg+r of key 16w + l16) -> S rows [i][j]
-  store4_split(ssh + (16 * w + l16) * SPB + 4 * kg, ssl + (16 * w + l16) * SPB + 4 * kg, st[0],
-               st[1], st[2], st[3]);
-  __syncthreads();
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  constexpr int SP = NBLK * VT + 8;
+  // nothing of this chunk's work is scheduled above this point: its header
+  // words were loaded a chunk ago, and reading them earlier would wait for
+  // the operand loads still in flight
+  __builtin_amdgcn_sched_barrier(0);
+  Scales sc[VT];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-    acc = mfma3(frag_tr(ssh, ssl, SPB, 32 * ks, 0, kg, l16), split_h(o.b[ks]), acc);
-  const int t = 16 * (w & 3) + l16;   // this lane's token; values 4kg + r
-  if (w < 4) {
-    store4_split(suh + t * SPB + 4 * kg, sul + t * SPB + 4 * kg, o.add.x - acc[0],
-                 o.add.y - acc[1], o.add.z - acc[2], o.add.w - acc[3]);
-  } else if (t < n) {
-    *reinterpret_cast<float4 *>(yc + (int64_t)t * y_tok + 4 * kg) =
-        make_float4(scale * (acc[0] + o.add.x), scale * (acc[1] + o.add.y),
-                    scale * (acc[2] + o.add.z), scale * (acc[3] + o.add.w));
+  for (int d = 0; d < VT; ++d) {
+    sc[d] = chunk_scales(bound[d], o.hdr);
+    store4_split_h(ssh + (16 * w + l16) * SP + 16 * d + 4 * kg,
+                   ssl + (16 * w + l16) * SP + 16 * d + 4 * kg, st[d], sc[d].sS);
   }
   __syncthreads();
-  st = st * o.gam;
+  f32x4 acc[VT];
+#pragma unroll
+  for (int d = 0; d < VT; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int d = 0; d < VT; ++d)
+      acc[d] = mfma2_h(frag_tr_h(ssh, ssl, SP, 32 * ks, 16 * d, kg, l16), o.b[ks], acc[d]);
+  const int t = 16 * (w & 3) + l16;   // this lane's token; values 4kg + r
+#pragma unroll
+  for (int d = 0; d < VT; ++d) {
+    const f32x4 p = acc[d] * sc[d].iS;
+    const float4 ad = o.add[d];
+    if (w < 4) {
+      const f32x4 u = {ad.x - p[0], ad.y - p[1], ad.z - p[2], ad.w - p[3]};
+      store4_split_h(suh + t * SP + 16 * d + 4 * kg, sul + t * SP + 16 * d + 4 * kg, u,
+                     sc[d].sU);
+    } else if (t < n) {
+      *reinterpret_cast<float4 *>(yc + (int64_t)t * y_tok + 16 * d + 4 * kg) =
+          make_float4(scale * (p[0] + ad.x), scale * (p[1] + ad.y), scale * (p[2] + ad.z),
+                      scale * (p[3] + ad.w));
+    }
+  }
+  __syncthreads();
+  f32x4 du[VT];
+#pragma unroll
+  for (int d = 0; d < VT; ++d) du[d] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
-    st = mfma3(frag_tr(suh, sul, SPB, 32 * ks, 0, kg, l16), split_h(o.k[ks]), st);
+#pragma unroll
+    for (int d = 0; d < VT; ++d)
+      du[d] = mfma3_h(frag_tr_h(suh, sul, SP, 32 * ks, 16 * d, kg, l16), o.k[ks], o.kl[ks],
+                      du[d]);
+  const float gam = hdr_word(o.hdr, 0);
+#pragma unroll
+  for (int d = 0; d < VT; ++d) st[d] = st[d] * gam + du[d] * sc[d].iU;
 }
 
-template <class TAB>
+template <class TAB, int VT>
 __global__ __launch_bounds__(512) void k_chunk_scan(
     float *__restrict__ state, int64_t st_seq, const unsigned char *__restrict__ ws,
     float *__restrict__ y, int64_t y_tok, int64_t y_seq, int n_tok, int n_chunks, int H,
     float scale, const TAB tab) {
-  __shared__ __attribute__((aligned(16))) u16 ssh[DK * SPB], ssl[DK * SPB];
-  __shared__ __attribute__((aligned(16))) u16 suh[CH * SPB], sul[CH * SPB];
+  constexpr int SP = NBLK * VT + 8;
+  __shared__ __attribute__((aligned(16))) u16 ssh[DK * SP], ssl[DK * SP];
+  __shared__ __attribute__((aligned(16))) u16 suh[CH * SP], sul[CH * SP];
+  __shared__ float red[8 * VT];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
-  // the 8 value blocks of one head on one XCD (xcd_order)
+  // the NVB / VT workgroups of one head on one XCD (xcd_order)
   int sh, blk;
-  xcd_order(blockIdx.x, gridDim.x, NVB, sh, blk);
+  xcd_order(blockIdx.x, gridDim.x, NVB / VT, sh, blk);
+  blk *= VT;   // first value tile
   const int h = sh % H, s = sh / H;
   const HeadChunks hc = head_chunks(tab, s, h, H, n_tok, n_chunks);
 
-  // state element (value j = 16 blk + 4kg + r, key i = 16w + l16), value-major
+  // state element (value j = 16 (blk + d) + 4kg + r, key i = 16w + l16), value-major
   float *sp = state + s * st_seq + (int64_t)h * DK * DV +
               (int64_t)(blk * NBLK + 4 * kg) * DK + 16 * w + l16;
-  f32x4 st = {sp[0], sp[DK], sp[2 * DK], sp[3 * DK]};
+  f32x4 st[VT];
+#pragma unroll
+  for (int d = 0; d < VT; ++d) {
+    const float *p = sp + (int64_t)16 * d * DK;
+    st[d] = f32x4{p[0], p[DK], p[2 * DK], p[3 * DK]};
+  }
+  float bound[VT];
+  tile_norms(st, red, w, lane, bound);
   const unsigned char *wh = ws + hc.first * WS_CHUNK;
   float *yh = y + s * y_seq + hc.row0 * y_tok + (int64_t)h * DV + blk * NBLK;
   auto chunk_ptr = [&](int c) { return wh + (size_t)max(min(c, hc.nch - 1), 0) * WS_CHUNK; };
-  auto run = [&](const ChunkOps &o, int c) {
-    scan_chunk(o, st, ssh, ssl, suh, sul, yh + (int64_t)c * CH * y_tok, y_tok,
-               min(CH, hc.len - c * CH), scale, w, l16, kg);
+  auto run = [&](const ChunkOps<VT> &o, int c) {
+    scan_chunk<VT>(o, bound, st, ssh, ssl, suh, sul, yh + (int64_t)c * CH * y_tok, y_tok,
+                   min(CH, hc.len - c * CH), scale, w, l16, kg);
   };
 
   // Two operand sets: chunk c + 2's are requested as soon as chunk c has run
   // (into the registers chunk c used), so each request has the whole of
-  // chunk c + 1 to arrive.  n_chunks is even (the workspace is padded with an identity chunk), so the
-  // loop has no tail; a tail would make the compiler copy the operand
-  // registers at the loop head, which waits for every load in flight.
-  ChunkOps a, b;
+  // chunk c + 1 to arrive.  n_chunks is even (the workspace is padded with an
+  // identity chunk), so the loop has no tail; a tail would make the compiler
+  // copy the operand registers at the loop head, which waits for every load
+  // in flight.
+  ChunkOps<VT> a, b;
   load_chunk(a, chunk_ptr(0), w, lane, blk);
   load_chunk(b, chunk_ptr(1), w, lane, blk);
   for (int c = 0; c < hc.nch; c += 2) {
@@ -834,29 +1046,34 @@ __global__ __launch_bounds__(512) void k_chunk_scan(
     run(b, c + 1);
     load_chunk(b, chunk_ptr(c + 3), w, lane, blk);
   }
-  sp[0] = st[0];
-  sp[DK] = st[1];
-  sp[2 * DK] = st[2];
-  sp[3 * DK] = st[3];
+#pragma unroll
+  for (int d = 0; d < VT; ++d) {
+    float *p = sp + (int64_t)16 * d * DK;
+    p[0] = st[d][0];
+    p[DK] = st[d][1];
+    p[2 * DK] = st[d][2];
+    p[3 * DK] = st[d][3];
+  }
 }
 
 // ---- phase B for grids that exceed one pass of the chip
 // One 16-wave workgroup per (sequence, head, pair of value blocks): waves
 // 8g .. 8g+7 run exactly the per-wave arithmetic of k_chunk_scan on value
 // block 2p + g, so the results are bit-identical to it.  The two groups share
-// one copy of each chunk's W, Q' and K' (the first 48 KB of its workspace,
-// copied byte for byte), which halves the head's operand reads from L2; the
-// price is that every wave now reads its fragments from LDS, so this form
-// only pays once the 8-wave grid would need a second pass.
+// one copy of each chunk's W, Q' and K' hi and lo (the first 64 KB of its
+// workspace, copied byte for byte), which halves the head's operand reads
+// from L2; the price is that every wave now reads its fragments from LDS, so
+// this form only pays once the 8-wave grid would need a second pass.
 // The copy is staged through registers one chunk ahead: each thread holds 32
-// bytes of W and Q' and 16 bytes of K'.  W and Q' are rewritten in LDS right
+// bytes of W and Q' and 32 bytes of K'.  W and Q' are rewritten in LDS right
 // after the barrier that ends their last reads (the U barrier), K' right
 // after the barrier that ends the state update's reads (the S barrier).
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int OPS_WQ = (int)(2 * WS_PLANE);   // W and Q', workspace bytes [0, 32 KiB)
-constexpr int OPS_K = (int)WS_PLANE;          // K'^T, workspace bytes [32, 48 KiB)
+constexpr int OPS_K = (int)(2 * WS_PLANE);    // K'^T hi and lo, workspace bytes [32, 64 KiB)
 constexpr int PAIR_THREADS = 1024;
-static_assert(WS_W == 0 && WS_Q == WS_PLANE && WS_K == (size_t)OPS_WQ, "operand layout");
+static_assert(WS_W == 0 && WS_Q == WS_PLANE && WS_K == (size_t)OPS_WQ &&
+              WS_KL == WS_K + WS_PLANE, "operand layout");
 static_assert(OPS_WQ % (16 * PAIR_THREADS) == 0 && OPS_K % (16 * PAIR_THREADS) == 0, "copy split");
 
 template <class TAB>
@@ -868,6 +1085,7 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_chunk_scan_pair(
   __shared__ __attribute__((aligned(16))) u16 ssh[2][DK * SPB], ssl[2][DK * SPB];
   __shared__ __attribute__((aligned(16))) u16 suh[2][CH * SPB], sul[2][CH * SPB];
   __shared__ __attribute__((aligned(16))) unsigned char ops[OPS_WQ + OPS_K];
+  __shared__ float red[2][8];
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
   const int grp = tid >> 9, w = (tid >> 6) & 7;
   // the 4 workgroups of one head on one XCD (xcd_order; the grid, 4 per head,
@@ -881,6 +1099,13 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_chunk_scan_pair(
   float *sp = state + s * st_seq + (int64_t)h * DK * DV +
               (int64_t)(blk * NBLK + 4 * kg) * DK + 16 * w + l16;
   f32x4 st = {sp[0], sp[DK], sp[2 * DK], sp[3 * DK]};
+  float bound;
+  {
+    const f32x4 st1[1] = {st};
+    float b1[1];
+    tile_norms<1>(st1, red[grp], w, lane, b1);
+    bound = b1[0];
+  }
   const unsigned char *wh = ws + hc.first * WS_CHUNK;
   float *yh = y + s * y_seq + hc.row0 * y_tok + (int64_t)h * DV + blk * NBLK;
   auto chunk_ptr = [&](int c) { return wh + (size_t)max(min(c, hc.nch - 1), 0) * WS_CHUNK; };
@@ -911,27 +1136,30 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_chunk_scan_pair(
     for (int i = 0; i < NK; ++i)
       *reinterpret_cast<u32x4 *>(ops + OPS_WQ + 16 * (tid + PAIR_THREADS * i)) = rk[i];
   };
-  auto load_add = [&](const unsigned char *wc, float4 &add, float &gam)
+  auto load_add = [&](const unsigned char *wc, float4 &add, float &hdr)
       __attribute__((always_inline)) {
     const float *addp = reinterpret_cast<const float *>(wc + (w < 4 ? WS_U : WS_O));
     add = *reinterpret_cast<const float4 *>(addp + add_off);
-    gam = *reinterpret_cast<const float *>(wc + WS_G);
+    hdr = load_hdr(wc, lane);
   };
-  auto run = [&](int c, const float4 &add, float gam) __attribute__((always_inline)) {
-    store4_split(s_hi + (16 * w + l16) * SPB + 4 * kg, s_lo + (16 * w + l16) * SPB + 4 * kg,
-                 st[0], st[1], st[2], st[3]);
+  auto run = [&](int c, const float4 &add, float hdr) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);   // as in scan_chunk
+    const Scales sc = chunk_scales(bound, hdr);
+    store4_split_h(s_hi + (16 * w + l16) * SPB + 4 * kg, s_lo + (16 * w + l16) * SPB + 4 * kg,
+                   st, sc.sS);
     __syncthreads();   // S barrier: W, Q' of chunk c and the S tiles are in LDS
     put_k();           // K' of chunk c, first read after the U barrier
     load_k(chunk_ptr(c + 1));
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const Frag b = split_h(*reinterpret_cast<const h16x8 *>(b_lds + frag_off(w & 3, ks, 4, lane)));
-      acc = mfma3(frag_tr(s_hi, s_lo, SPB, 32 * ks, 0, kg, l16), b, acc);
+      const h16x8 b = *reinterpret_cast<const h16x8 *>(b_lds + frag_off(w & 3, ks, 4, lane));
+      acc = mfma2_h(frag_tr_h(s_hi, s_lo, SPB, 32 * ks, 0, kg, l16), b, acc);
     }
+    acc = acc * sc.iS;
     if (w < 4) {
-      store4_split(u_hi + t * SPB + 4 * kg, u_lo + t * SPB + 4 * kg, add.x - acc[0],
-                   add.y - acc[1], add.z - acc[2], add.w - acc[3]);
+      const f32x4 u = {add.x - acc[0], add.y - acc[1], add.z - acc[2], add.w - acc[3]};
+      store4_split_h(u_hi + t * SPB + 4 * kg, u_lo + t * SPB + 4 * kg, u, sc.sU);
     } else if (t < min(CH, hc.len - c * CH)) {
       *reinterpret_cast<float4 *>(yh + (int64_t)(c * CH + t) * y_tok + 4 * kg) =
           make_float4(scale * (acc[0] + add.x), scale * (acc[1] + add.y),
@@ -940,12 +1168,15 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_chunk_scan_pair(
     __syncthreads();   // U barrier: K' and the U tiles are in LDS, W and Q' are read
     put_wq();          // W, Q' of chunk c + 1
     load_wq(chunk_ptr(c + 2));
-    st = st * gam;
+    f32x4 du = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const Frag kf = split_h(*reinterpret_cast<const h16x8 *>(k_lds + frag_off(w, ks, 2, lane)));
-      st = mfma3(frag_tr(u_hi, u_lo, SPB, 32 * ks, 0, kg, l16), kf, st);
+      const h16x8 kh = *reinterpret_cast<const h16x8 *>(k_lds + frag_off(w, ks, 2, lane));
+      const h16x8 kl =
+          *reinterpret_cast<const h16x8 *>(k_lds + CH * DK + frag_off(w, ks, 2, lane));
+      du = mfma3_h(frag_tr_h(u_hi, u_lo, SPB, 32 * ks, 0, kg, l16), kh, kl, du);
     }
+    st = st * hdr_word(hdr, 0) + du * sc.iU;
   };
 
   load_wq(chunk_ptr(0));
@@ -953,15 +1184,15 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_chunk_scan_pair(
   load_wq(chunk_ptr(1));
   load_k(chunk_ptr(0));
   float4 add0, add1;
-  float gam0, gam1;
-  load_add(chunk_ptr(0), add0, gam0);
-  load_add(chunk_ptr(1), add1, gam1);
+  float hdr0, hdr1;
+  load_add(chunk_ptr(0), add0, hdr0);
+  load_add(chunk_ptr(1), add1, hdr1);
   // the chunk count is even, as for k_chunk_scan
   for (int c = 0; c < hc.nch; c += 2) {
-    run(c, add0, gam0);
-    load_add(chunk_ptr(c + 2), add0, gam0);
-    run(c + 1, add1, gam1);
-    load_add(chunk_ptr(c + 3), add1, gam1);
+    run(c, add0, hdr0);
+    load_add(chunk_ptr(c + 2), add0, hdr0);
+    run(c + 1, add1, hdr1);
+    load_add(chunk_ptr(c + 3), add1, hdr1);
   }
   sp[0] = st[0];
   sp[DK] = st[1];
@@ -1016,17 +1247,19 @@ static int launch_two_phase(const RecurArgs &a, const TAB &tab, const TIN *q, co
                          a.qk_tok, a.qk_seq, v, a.v_tok, a.v_seq, a.g, a.beta, wsb, a.n_tok,
                          n_chunks, a.H, a.Hk, n_items, tab);
   if (rc != GDN_OK) return rc;
-  // phase B: 8-wave workgroups while they fit in one pass of the chip (one per
-  // CU: their registers allow no second); past that, the 16-wave form whose
-  // pairs of value blocks share operand copies
-  const int nwg = a.n_seq * a.H * NVB;  // a multiple of 8 (NVB == 8)
-  if (nwg > cus)
-    return launch_kernel(k_chunk_scan_pair<TAB>, dim3(nwg / 2), dim3(PAIR_THREADS), 0, stream,
-                         a.state, a.st_seq, (const unsigned char *)wsb, a.y, a.y_tok, a.y_seq,
-                         a.n_tok, n_chunks, a.H, a.scale, tab);
-  return launch_kernel(k_chunk_scan<TAB>, dim3(nwg), dim3(512), 0, stream, a.state, a.st_seq,
-                       (const unsigned char *)wsb, a.y, a.y_tok, a.y_seq, a.n_tok, n_chunks, a.H,
-                       a.scale, tab);
+  // phase B: 8-wave workgroups of one value tile each while they fit in one
+  // pass of the chip (measured: two or four tiles per workgroup lengthen the
+  // chain more than they save in operand traffic, 168 and 241 against 133 us
+  // at 32 heads); past that, the 16-wave form whose pairs of value tiles share
+  // operand copies in LDS.  All forms give the same bits.
+  const int units = a.n_seq * a.H;
+  if (units * NVB > cus)
+    return launch_kernel(k_chunk_scan_pair<TAB>, dim3(units * (NVB / 2)), dim3(PAIR_THREADS), 0,
+                         stream, a.state, a.st_seq, (const unsigned char *)wsb, a.y, a.y_tok,
+                         a.y_seq, a.n_tok, n_chunks, a.H, a.scale, tab);
+  return launch_kernel(k_chunk_scan<TAB, 1>, dim3(units * NVB), dim3(512), 0, stream, a.state,
+                       a.st_seq, (const unsigned char *)wsb, a.y, a.y_tok, a.y_seq, a.n_tok,
+                       n_chunks, a.H, a.scale, tab);
 }
 
 int launch_recur_chunked(const RecurArgs &a, int chunk, void *ws, size_t ws_bytes,

@@ -163,9 +163,25 @@ size_t gdn_recurrence_chunked_workspace_bytes(int n_seq, int n_tok, int n_v_head
  *   y  = scale [diag(e^G) Q S0 + (L o Q K^T) U],  L[t][s] = e^{G_t-G_s} (s <= t)
  *   S  = e^{G_n} S0 + (diag(e^{G_n-G}) K)^T U
  * Same tensor arguments and layouts as gdn_recurrence_decode (no snapshots).
- * The intra-chunk contractions use bf16 MFMA with fp32 accumulation; the
- * state is carried in fp32.  Agreement with the sequential scan is a
- * tolerance, not bit identity.
+ *
+ * Preconditions (the chunked form's algebra and storage rely on them; the
+ * token-by-token entry point needs neither):
+ *   - g <= 0 at every position (true for gdn_decay_gate's output): every
+ *     exponential the chunked form takes is of a non-positive argument;
+ *   - beta_t |k_t|^2 <= 2 at every position (true for unit-length keys and
+ *     beta in [0, 1]), so every factor I - beta_t k_t k_t^T has spectral
+ *     norm <= 1.  Under these two, |T[t][s]| <= beta_t for s < t, every entry
+ *     of W and K' is at most beta_t |k_t| resp. |k_t|, and every entry of Q'
+ *     is at most |q_t| (the factors are products of such contractions).
+ * Numerics at S = 128: the intra-chunk products (K K^T, Q K^T, W, U~, Q',
+ * O_i) run on bf16 MFMA with each fp32 operand split into hi + lo and fp32
+ * accumulation; the triangular inverse, cumulative gate, exponentials and the
+ * state carry are fp32.  W and Q' are stored in the workspace as fp16 and K'
+ * as fp16 hi + lo; the inter-chunk products use them on fp16 MFMA against the
+ * state and U split into fp16 hi + lo after a power-of-two scaling chosen from
+ * a running bound on their norms (so no input size can overflow fp16).
+ * Agreement with the sequential scan is a tolerance (normwise 2e-3), not bit
+ * identity; outside the preconditions the results are not specified.
  *
  * chunk must be 64; S in {32, 64, 128} (256 returns GDN_ERR_UNSUPPORTED).
  * S = 128 runs the two-phase MFMA form above and needs a workspace: device

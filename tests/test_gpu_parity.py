@@ -676,6 +676,67 @@ def test_chunked_ragged_and_weak_decay(T, H, Hk, n_seq, g_scale):
     assert ey < 2e-3 and es < 2e-3
 
 
+def degenerate_keys(T, Hk, S, gen):
+    """Unit keys that stress the triangular solve: q/k head 0 repeats one key,
+    head 1 alternates +k and -k, head 2 draws keys from a 3-dimensional
+    subspace, any further head takes fresh random keys."""
+    def unit(x):
+        return x / x.norm(dim=-1, keepdim=True)
+    k = unit(torch.randn(1, T, Hk, S, generator=gen, dtype=torch.float64))
+    k0 = unit(torch.randn(S, generator=gen, dtype=torch.float64))
+    k[0, :, 0] = k0
+    if Hk > 1:
+        sign = torch.tensor([1.0 if t % 2 == 0 else -1.0 for t in range(T)], dtype=torch.float64)
+        k[0, :, 1] = sign[:, None] * k0[None, :]
+    if Hk > 2:
+        basis, _ = torch.linalg.qr(torch.randn(S, 3, generator=gen, dtype=torch.float64))
+        k[0, :, 2] = unit(torch.randn(T, 3, generator=gen, dtype=torch.float64) @ basis.T)
+    return k.float()
+
+
+@pytest.mark.parametrize("S", [128, 64])
+def test_chunked_degenerate_keys_no_decay(S):
+    # the chunked form's contract (unit keys, beta |k|^2 <= 2, g <= 0) at its
+    # edge: repeated, alternating and low-rank keys with beta = sigmoid(6) and
+    # no decay at all, 4096 positions, against the sequential fp64 scan
+    T, H, Hk = 4096, 6, 3
+    inp = make_inputs("prefill", seed=79, n_tok=T, H=H, Hk=Hk, S=S, head_dim=S)
+    wl = inp["wl"]
+    log_case("chunked_degenerate", T=T, H=H, Hk=Hk, S=S)
+    gen = torch.Generator("cpu").manual_seed(80)
+    inp = dict(inp)
+    inp["k"] = degenerate_keys(T, Hk, S, gen)
+    inp["beta"] = torch.full_like(inp["beta"], float(1.0 / (1.0 + math.exp(-6.0))))
+    g3 = torch.zeros(1, T, H)
+    y, st = run_chunked(inp, g3)
+    y_ref, s_ref, _ = oracle.recurrence_seq(inp["state"], inp["q"], inp["k"], inp["v"], g3,
+                                            inp["beta"], wl.scale)
+    ey, es = rel(y, y_ref), rel(st, s_ref)
+    print(f"[chunked degenerate keys S={S}] rel err y {ey:.3e} state {es:.3e}", flush=True)
+    assert ey < 2e-3 and es < 2e-3
+
+
+@pytest.mark.parametrize("v_scale,state_std", [(3000.0, 100.0), (1e-3, 1e-4)])
+def test_chunked_large_and_small_magnitudes(v_scale, state_std):
+    # values far from 1: the scan's fp16 operand splits are scaled by powers of
+    # two from a running norm bound, so neither large nor tiny states and
+    # values lose range or precision; 1000 positions, paired and 8-wave scans
+    for H, Hk in ((4, 2), (40, 8)):
+        inp = make_inputs("prefill", seed=83, n_tok=1000, H=H, Hk=Hk, state_std=state_std)
+        wl = inp["wl"]
+        log_case("chunked_magnitudes", v_scale=v_scale, state_std=state_std, H=H)
+        inp = dict(inp)
+        inp["v"] = inp["v"] * v_scale
+        g3 = oracle_g(inp) * 0.05
+        y, st = run_chunked(inp, g3)
+        y_ref, s_ref, _ = oracle.recurrence_seq(inp["state"], inp["q"], inp["k"], inp["v"], g3,
+                                                inp["beta"], wl.scale)
+        ey, es = rel(y, y_ref), rel(st, s_ref)
+        print(f"[chunked magnitudes v x{v_scale} state {state_std}] H={H} rel err y {ey:.3e} "
+              f"state {es:.3e}", flush=True)
+        assert ey < 2e-3 and es < 2e-3
+
+
 @pytest.mark.parametrize("T,H,Hk,n_seq", [(130, 33, 11, 1), (64, 20, 5, 2)])
 def test_chunked_paired_scan_grid(T, H, Hk, n_seq):
     # more than 256 sequence x head x 16-column units, so the scan runs as
