@@ -95,6 +95,25 @@ def chunked_flops(T: int, H: int, S: int, C: int = 64) -> float:
     return float(T) * H * (10 * C * S + 6 * S * S)
 
 
+# MFMA instructions the S = 128 chunked kernels issue per (sequence, head,
+# 64-position chunk), counted from the kernels' code:
+#   phase A, 16x16x32 bf16 (16384 flops each): K K^T and Q K^T on 20 lower
+#     tiles x 4 k-steps x 3 (hi/lo split) = 240; W and U~: 8 waves x 2 k-steps
+#     x 2 key tiles x 2 token tiles x 2 products x 3 = 384; Q' and O_i: 384;
+#   phase A, 16x16x4 fp32 (2048 flops each): the block inverse, 64;
+#   phase B, 16x16x32 fp16 (16384 flops each) per 16-column value tile: 8 waves
+#     x 4 k-steps x 2 (state hi/lo) = 64 for W S / Q' S, and 8 waves x 2
+#     k-steps x 3 (U hi/lo, K' hi/lo) = 48 for K'^T U; 8 value tiles per head.
+MFMA_FLOPS_PER_HEAD_CHUNK = (240 + 384 + 384) * 16384 + 64 * 2048 + 8 * (64 + 48) * 16384
+
+
+def chunked_executed_flops(n_tok: int, H: int, n_seq: int = 1) -> float:
+    """Flops of the MFMA instructions one chunked call issues (chunk count
+    padded to even, as the kernels do)."""
+    chunks = ((n_tok + 63) // 64 + 1) & ~1
+    return float(n_seq) * H * chunks * MFMA_FLOPS_PER_HEAD_CHUNK
+
+
 def chunked_attainable(T: int, H: int, Hk: int, S: int, ws_bytes: int, tflops: float) -> dict:
     """Roofline-attainable bf16 MFMA fraction of the chunked recurrence: its
     algorithmic flops over its HBM bytes give the arithmetic intensity, and
@@ -368,34 +387,49 @@ def main():
     # 16 sequences x K draft positions in one gdn_decode_step launch, with the
     # state and conv-history snapshots after every position but the last
     # written inline (K = 2 is the headline verify; 4 and 8 show the generic K)
-    def verify_case(K):
+    def verify_case(K, pools=6):
+        # cold: `pools` disjoint sets of state, snapshots, conv history and
+        # output rotated launch by launch (at K = 2 each set holds 64 MiB of
+        # state and snapshots, six of them 384 MiB, beyond the 256 MB MALL);
+        # MALL-hot: the same launch repeated on one set
         vw_ = WORKLOADS["verify2"]
         if K != vw_.n_tok:
             vw_ = Workload(**{**vw_.__dict__, "name": f"verify{K}", "n_tok": K})
         vi_ = make_inputs(vw_)
         vc = {k: v.to(dev) for k, v in vi_.items() if isinstance(v, torch.Tensor)}
         vn, vT, vH, vS, vC = vw_.n_seq, vw_.n_tok, vw_.H, vw_.S, vw_.conv_dim
-        v_st, v_hist = vc["state"].clone(), vc["conv_hist"].clone()
-        v_out = torch.empty(vn, vT, vH, vS, device=dev)
-        v_snap = torch.empty(vn, vT - 1, vH, vS, vS, device=dev)
-        v_csnap = torch.empty(vn, vT - 1, vC, vw_.d_conv - 1, device=dev)
+        sets = []
+        for _ in range(pools):
+            sets.append(dict(st=vc["state"].clone(), hist=vc["conv_hist"].clone(),
+                             out=torch.empty(vn, vT, vH, vS, device=dev),
+                             snap=torch.empty(vn, vT - 1, vH, vS, vS, device=dev),
+                             csnap=torch.empty(vn, vT - 1, vC, vw_.d_conv - 1, device=dev)))
         v_ws = torch.zeros(gdn.gdn_decode_step_workspace_bytes(vn, vw_.Hk) // 4,
                            dtype=torch.int32, device=dev)
 
-        def verify_step(i=0):
-            gdn.gdn_decode_step(v_st, vc["x"][..., :vC], vc["conv_w"], v_hist,
+        def verify_step(i=0, rotate=True):
+            b = sets[i % pools] if rotate else sets[0]
+            gdn.gdn_decode_step(b["st"], vc["x"][..., :vC], vc["conv_w"], b["hist"],
                                 vc["alpha"].view(vn, vT, vH), vc["dt"], vc["a"], vc["beta"],
-                                vc["norm_w"], vc["z"].view(vn, vT, vH, vS), v_out,
+                                vc["norm_w"], vc["z"].view(vn, vT, vH, vS), b["out"],
                                 scale=vw_.scale, l2_eps=vw_.l2_eps, norm_eps=vw_.norm_eps,
-                                workspace=v_ws, snap=v_snap, conv_snap=v_csnap)
-        v_ms = burst(verify_step)
+                                workspace=v_ws, snap=b["snap"], conv_snap=b["csnap"])
+        cold_ms = burst(verify_step)
+        hot_ms = burst(lambda i: verify_step(i, rotate=False))
         v_state_bytes = vn * vH * vS * vS * 4
+        per_set = (K + 1) * v_state_bytes // 2 ** 20
+        del sets
         return {"workload": f"verify{K}: 16 seq x {K} positions, 32 value / 16 q-k heads, "
                             "128x128 state, conv 8192 ch, state and conv-history snapshots "
-                            "after every position but the last, one gdn_decode_step launch "
-                            "(same buffers each launch: the 32 MiB state stays in the MALL)",
-                "ms": v_ms,
-                "state_GBs": (K + 1) * v_state_bytes / (v_ms * 1e-3) / 1e9,
+                            "after every position but the last, one gdn_decode_step launch",
+                "ms": cold_ms,
+                "state_GBs": (K + 1) * v_state_bytes / (cold_ms * 1e-3) / 1e9,
+                "cold_note": f"{pools} buffer sets rotated launch by launch (state + snapshots "
+                             f"{per_set} MiB per set, {pools * per_set} MiB in all, beyond the "
+                             "256 MB MALL)",
+                "ms_mall_hot": hot_ms,
+                "state_GBs_mall_hot": (K + 1) * v_state_bytes / (hot_ms * 1e-3) / 1e9,
+                "hot_note": "the same buffers every launch: the state can stay in the MALL",
                 "state_bytes_note": f"state read + final write + {K - 1} snapshot write(s)"}
     verify = verify_case(2)
     verify_more = {str(K): verify_case(K) for K in (4, 8)}
@@ -462,6 +496,16 @@ def main():
         e1.record(stream)
         e1.synchronize()
         pass_ms = e0.elapsed_time(e1) / args.prefill_iters
+        # the chunked call alone, back to back between one event pair
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for _ in range(args.prefill_iters):
+            gdn.gdn_recurrence_chunked(pst, pq, pk, pv, pg.view(1, T, PH), pc["beta"], py,
+                                       scale=pw.scale, workspace=ws)
+        c1.record(stream)
+        c1.synchronize()
+        chunk_call_ms = c0.elapsed_time(c1) / args.prefill_iters
         # per-op split: a second, instrumented run with events between launches
         for _ in range(args.prefill_iters):
             prefill_pass(timed=True)
@@ -469,23 +513,34 @@ def main():
         seg = np.array([[m[j].elapsed_time(m[j + 1]) for j in range(4)] for m in ev["marks"]])
         seg = seg.mean(axis=0)                           # ms: gate, conv, chunked, norm
         fl = chunked_flops(T, PH, PS)
+        xfl = chunked_executed_flops(T, PH)
         prefill = {
             "workload": "prefill: 1 seq x 4096 tokens, 32 value / 16 q-k heads, 128x128 state, "
                         "conv 8192 ch, chunk 64",
             "tokens_per_s": T / (pass_ms * 1e-3),
             "pass_ms": pass_ms,
             "recurrence_tokens_per_s": T / (seg[2] * 1e-3),
+            "chunked_call_ms": chunk_call_ms,
+            "chunked_call_tokens_per_s": T / (chunk_call_ms * 1e-3),
+            "chunked_call_note": f"{args.prefill_iters} gdn_recurrence_chunked calls back to "
+                                 "back between one event pair (phase A and the scan)",
             "ms": {"gate": seg[0], "conv": seg[1], "chunked_recurrence": seg[2], "norm": seg[3]},
             "ms_note": "per-op split from a separate pass with events between launches; each "
                        "segment then carries the event pair's dispatch gaps, so the segments "
                        "sum to more than pass_ms",
             "chunked_algorithmic_tflops": fl / (seg[2] * 1e-3) / 1e12,
             "chunked_frac_of_bf16_peak": fl / (seg[2] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-            "chunked_frac_of_fp32_matrix_peak": fl / (seg[2] * 1e-3) / 1e12 / FP32_MATRIX_PEAK_TFLOPS,
-            "chunked_peak_note": "algorithmic flops (one product each); the kernels take every "
-                                 "product as three bf16 MFMAs (hi*hi + hi*lo + lo*hi), which keeps "
-                                 "fp32-level precision, so bf16 peak bounds the executed MFMAs and "
-                                 "the fp32 matrix peak is what single fp32 MFMAs would reach",
+            "chunked_executed_mfma_tflops": xfl / (seg[2] * 1e-3) / 1e12,
+            "chunked_executed_frac_of_bf16_peak": xfl / (seg[2] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "chunked_fp32_equivalent_frac": fl / (seg[2] * 1e-3) / 1e12 / FP32_MATRIX_PEAK_TFLOPS,
+            "chunked_peak_note": "frac_of_bf16_peak: algorithmic flops (one product each) over "
+                                 "the dense bf16 MFMA peak (the fp16 MFMA peak is the same); "
+                                 "executed: the flops of the MFMA instructions the kernels issue "
+                                 "(bf16 hi/lo splits in phase A, fp16 with hi/lo state and K' in "
+                                 "phase B, fp32 16x16x4 in the block inverse), counted from the "
+                                 "code; fp32_equivalent_frac divides the algorithmic rate by the "
+                                 "fp32 matrix peak of an instruction the kernels do not issue, "
+                                 "for comparison with an fp32 formulation only",
             "chunked_attainable": chunked_attainable(T, PH, PHk, PS, ws.numel(),
                                                      fl / (seg[2] * 1e-3) / 1e12),
         }
@@ -531,6 +586,9 @@ def main():
                         "heads, 128x128 state each, one gdn_recurrence_chunked_varlen call",
             "ms": vms, "recurrence_tokens_per_s": total / (vms * 1e-3),
             "chunked_algorithmic_tflops": vfl / (vms * 1e-3) / 1e12,
+            "chunked_executed_frac_of_bf16_peak":
+                sum(chunked_executed_flops(n, PH) for n in lens) / (vms * 1e-3) / 1e12
+                / BF16_PEAK_TFLOPS,
             "note": "the chunked recurrence only (gate, conv, norm are per-token kernels); "
                     f"{args.prefill_iters} calls back to back between one event pair"}
         del vq, vk, vv, vg, vbeta, vst, vy, vws
