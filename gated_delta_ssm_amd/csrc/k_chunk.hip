@@ -119,6 +119,14 @@ __device__ __forceinline__ void store8_h(u16 *p, const float (&x)[8]) {
   for (int e = 0; e < 8; ++e) h[e] = (_Float16)x[e];
   *reinterpret_cast<h16x8 *>(p) = h;
 }
+// DPP move with CTRL on the rows in ROW_MASK; lanes whose source is out of
+// range, and lanes of masked rows, read 0
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_zero(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xF, true));
+}
+
 __device__ __forceinline__ float sumsq8(const float4 &a, const float4 &b) {
   return a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w + b.x * b.x + b.y * b.y + b.z * b.z +
          b.w * b.w;
@@ -495,20 +503,25 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
   const TIN *qc = q + it.s * qk_seq + (int64_t)it.tb * qk_tok + it.hk * DK;
   unsigned char *wc = ws + it.slot * WS_CHUNK;
 
-  // S0. gate cumsum (wave 0)
+  // S0. gate cumsum (wave 0): an inclusive scan over the 64 lanes on DPP
+  // (row shifts within each 16-lane row, then the row totals broadcast across
+  // rows), and the exponentials as the hardware base-2 exponential of
+  // x log2(e) (all arguments are <= 0)
   if (w == 0) {
     float x = lane < n ? gv : 0.0f;
     const float b = lane < n ? bv : 0.0f;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float y = __shfl_up(x, off, 64);
-      if (lane >= off) x += y;
-    }
-    const float gn = __shfl(x, 63, 64);
+    x += dpp_zero<0x111, 0xF>(x);   // row_shr:1
+    x += dpp_zero<0x112, 0xF>(x);   // row_shr:2
+    x += dpp_zero<0x114, 0xF>(x);   // row_shr:4
+    x += dpp_zero<0x118, 0xF>(x);   // row_shr:8
+    x += dpp_zero<0x142, 0xA>(x);   // row_bcast:15 into rows 1 and 3
+    x += dpp_zero<0x143, 0xC>(x);   // row_bcast:31 into rows 2 and 3
+    const float gn = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+    constexpr float LOG2E = 1.4426950408889634f;
     sG[lane] = x;
     sBeta[lane] = b;
-    sEG[lane] = expf(x);
-    sEGn[lane] = expf(gn - x);
+    sEG[lane] = __builtin_amdgcn_exp2f(x * LOG2E);
+    sEGn[lane] = __builtin_amdgcn_exp2f((gn - x) * LOG2E);
   }
   load_gb(in, nx, lane, gv, bv);
   // S1. K, Q rows -> LDS (bf16 hi/lo); |k_t|^2 of each row (16 lanes per row)
