@@ -40,6 +40,9 @@ _SIGS = {
     "gdn_recurrence_chunked_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "gdn_recurrence_chunked": (_I, [_P, _L, _P, _P, _L, _L, _P, _L, _L, _P, _P, _P, _L, _L,
                                     _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
+    "gdn_prefill_chunked_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "gdn_prefill_chunked": (_I, [_P, _L, _P, _L, _L, _P, _P, _L, _P, _P, _P, _P, _P, _L, _L,
+                                 _I, _I, _I, _I, _I, _I, _F, _F, _I, _P, _SZ, _P]),
     "gdn_recurrence_chunked_varlen_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "gdn_recurrence_chunked_varlen": (_I, [_P, _L, _P, _P, _L, _P, _L, _I, _P, _P, _P, _L,
                                            _P, _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
@@ -227,6 +230,59 @@ def gdn_recurrence_chunked(state: torch.Tensor, q: torch.Tensor, k: torch.Tensor
         _ptr(v), v.stride(1), v.stride(0), _ptr(g), _ptr(beta), _ptr(y), y.stride(1),
         y.stride(0), n_seq, n_tok, H, Hk, S, scale, chunk, _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream, y)))
+    return y
+
+
+def gdn_prefill_chunked_workspace_bytes(n_seq: int, n_tok: int, n_v_heads: int,
+                                        n_qk_heads: int, S: int, chunk: int = 64) -> int:
+    return int(_lib.gdn_prefill_chunked_workspace_bytes(n_seq, n_tok, n_v_heads, n_qk_heads, S,
+                                                        chunk))
+
+
+def gdn_prefill_chunked(state: torch.Tensor, x: torch.Tensor, conv_w: torch.Tensor,
+                        conv_state: torch.Tensor, alpha: torch.Tensor, dt: torch.Tensor,
+                        a: torch.Tensor, beta: torch.Tensor, y: torch.Tensor, *, scale: float,
+                        l2_eps: float, chunk: int = 64, workspace: torch.Tensor | None = None,
+                        stream=None) -> torch.Tensor:
+    """Decay gate + conv1d/SiLU/L2 + chunked recurrence in two launches.
+    state [n_seq][H][S][S] (in place); x [n_seq][n_tok][>= conv_dim] with
+    conv_dim = (2*Hk + H)*S channels q | k | v; conv_w [conv_dim][d_conv];
+    conv_state [n_seq][conv_dim][d_conv-1] rolled in place; alpha, beta
+    [n_seq][n_tok][H]; dt, a [H]; y [n_seq][n_tok][H][S].  If no workspace
+    is given one is allocated here through torch."""
+    n_seq, H, S, _ = state.shape
+    C, D = conv_w.shape
+    if C % S or (C // S - H) < 2 or (C // S - H) % 2:
+        raise ValueError(f"conv_dim {C} is not (2*Hk + H)*S for H={H}, S={S}")
+    Hk = (C // S - H) // 2
+    if x.dim() != 3 or x.shape[0] != n_seq or x.shape[2] < C:
+        raise ValueError("x shape mismatch")
+    n_tok = x.shape[1]
+    if tuple(conv_state.shape) != (n_seq, C, D - 1):
+        raise ValueError("conv_state shape mismatch")
+    if tuple(alpha.shape) != (n_seq, n_tok, H) or beta.shape != alpha.shape:
+        raise ValueError("alpha / beta shape mismatch")
+    if tuple(dt.shape) != (H,) or tuple(a.shape) != (H,):
+        raise ValueError("dt / a shape mismatch")
+    if tuple(y.shape) != (n_seq, n_tok, H, S):
+        raise ValueError("y shape mismatch")
+    _dev_f32("state", state, 3)
+    _dev_f32("x", x, 1)
+    _dev_f32("conv_w", conv_w, 2)
+    _dev_f32("conv_state", conv_state, 2)
+    _dev_f32("y", y, 2)
+    for n, t in (("alpha", alpha), ("beta", beta)):
+        _dev_f32(n, t, 3)
+    for n, t in (("dt", dt), ("a", a)):
+        _dev_f32(n, t, 1)
+    need = gdn_prefill_chunked_workspace_bytes(n_seq, n_tok, H, Hk, S, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=state.device)
+    _check("gdn_prefill_chunked", _lib.gdn_prefill_chunked(
+        _ptr(state), state.stride(0), _ptr(x), x.stride(1), x.stride(0), _ptr(conv_w),
+        _ptr(conv_state), conv_state.stride(0), _ptr(alpha), _ptr(dt), _ptr(a), _ptr(beta),
+        _ptr(y), y.stride(1), y.stride(0), n_seq, n_tok, H, Hk, S, D, scale, l2_eps, chunk,
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, y)))
     return y
 
 

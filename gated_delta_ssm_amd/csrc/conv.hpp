@@ -18,14 +18,29 @@ namespace gdn {
 
 constexpr int CPL = 4;   // channels per lane
 
+// SiLU of a conv output, a / (1 + e^-a), on the hardware base-2 exponential
+// (of -a log2(e)) and reciprocal, each about 1 ulp: a few instructions where
+// the libm exponential and a correctly rounded division take dozens, which
+// matters where the conv runs inside a compute-bound kernel.  For a below
+// about -88 the exponential overflows and the result is -0 (the exact value
+// is below 1e-36 in magnitude).
+__device__ __forceinline__ float conv_silu(float a) {
+  return a * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-a * 1.4426950408889634f));
+}
+
 // acc = sum_j w[j] * win[j] in tap order, oldest tap first, explicit FMAs.
 template <int D>
 __device__ __forceinline__ float conv_position(const float (&w)[D], const float (&win)[D]) {
   float acc = w[0] * win[0];
 #pragma unroll
   for (int j = 1; j < D; ++j) acc = __builtin_fmaf(w[j], win[j], acc);
-  return silu(acc);
+  return conv_silu(acc);
 }
+
+// 1 / sqrt(x) for the L2 step, the hardware reciprocal square root (about
+// 1 ulp; x >= eps > 0 here): one instruction where a correctly rounded square
+// root and division take about thirty.
+__device__ __forceinline__ float l2_rsqrt(float x) { return __builtin_amdgcn_rsqf(x); }
 
 // 1 / sqrt(sum over the lane's L2 head of o^2 + eps); LPH4 lanes per head.
 template <int LPH4>
@@ -34,7 +49,7 @@ __device__ __forceinline__ float l2_scale(const float (&o)[CPL], float eps) {
 #pragma unroll
   for (int c = 1; c < CPL; ++c) ss = __builtin_fmaf(o[c], o[c], ss);
   ss = group_sum<LPH4>(ss);
-  return 1.0f / sqrtf(ss + eps);
+  return l2_rsqrt(ss + eps);
 }
 
 // The lane's channels: chc[c] is channel c0 + c clamped to the last channel

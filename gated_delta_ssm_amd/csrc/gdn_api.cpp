@@ -189,6 +189,38 @@ int gdn_recurrence_chunked(float *state, int64_t state_seq_stride, const float *
   return gdn::launch_recur_chunked(a, chunk, workspace, workspace_bytes, stream);
 }
 
+size_t gdn_prefill_chunked_workspace_bytes(int n_seq, int n_tok, int n_v_heads, int n_qk_heads,
+                                           int S, int chunk) {
+  if (S != 128 || chunk != 64) return 0;
+  return gdn_recurrence_chunked_workspace_bytes(n_seq, n_tok, n_v_heads, n_qk_heads, S, chunk);
+}
+
+int gdn_prefill_chunked(float *state, int64_t state_seq_stride, const float *x,
+                        int64_t x_tok_stride, int64_t x_seq_stride, const float *conv_w,
+                        float *conv_state, int64_t conv_state_seq_stride, const float *alpha,
+                        const float *dt, const float *a, const float *beta, float *y,
+                        int64_t y_tok_stride, int64_t y_seq_stride, int n_seq, int n_tok,
+                        int n_v_heads, int n_qk_heads, int S, int d_conv, float scale,
+                        float l2_eps, int chunk, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  const size_t need =
+      gdn_prefill_chunked_workspace_bytes(n_seq, n_tok, n_v_heads, n_qk_heads, S, chunk);
+  const int rc = gdn::check_prefill(state, state_seq_stride, x, x_tok_stride, x_seq_stride,
+                                    conv_w, conv_state, conv_state_seq_stride, alpha, dt, a, beta,
+                                    y, y_tok_stride, y_seq_stride, n_seq, n_tok, n_v_heads,
+                                    n_qk_heads, S, d_conv, chunk, workspace, workspace_bytes,
+                                    need);
+  if (rc != GDN_OK) return rc;
+  gdn::RecurArgs ra{state,   state_seq_stride, nullptr,      nullptr,      0,
+                    0,       nullptr,          0,            0,            nullptr,
+                    beta,    y,                y_tok_stride, y_seq_stride, nullptr,
+                    0,       n_seq,            n_tok,        n_v_heads,    n_qk_heads,
+                    S,       scale};
+  const gdn::PrefillConv pc{x, x_tok_stride, x_seq_stride, conv_w, conv_state,
+                            conv_state_seq_stride, alpha, dt, a, d_conv, l2_eps};
+  return gdn::launch_prefill_chunked(ra, pc, chunk, workspace, workspace_bytes, stream);
+}
+
 size_t gdn_recurrence_chunked_varlen_workspace_bytes(int n_seq, int total_tok, int n_v_heads,
                                                      int n_qk_heads, int S, int chunk) {
   if (n_seq < 1 || n_seq > GDN_VARLEN_MAX_SEQ || total_tok < 0 || n_v_heads < 1 ||

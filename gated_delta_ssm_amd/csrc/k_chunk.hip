@@ -21,7 +21,12 @@
 //   k_chunk_prep (phase A) -- every (sequence, head, chunk) independently:
 //     everything that does not depend on S0, written to a workspace in the
 //     exact register layout the scan loads.  Persistent: one workgroup per CU
-//     walks its chunks, loading the next chunk while computing this one.
+//     walks its chunks, loading the next chunk while computing this one.  Its
+//     K, Q, V and g come either as given (gdn_recurrence_chunked) or from the
+//     layer's conv input and gate inputs (gdn_prefill_chunked: the decay gate
+//     and the conv1d + SiLU + L2 of ssm_mamba.rs conv1d_update_prefill are
+//     computed here, bit for bit as the gate and conv kernels compute them,
+//     and never stored); the scan then also writes the conv history.
 //   k_chunk_scan (phase B) -- one workgroup per (sequence, head, block of 16
 //     value columns), walking the chunks in order: the value columns of S are
 //     independent, so 8 workgroups share a head, and they are mapped to one
@@ -48,6 +53,8 @@
 #include <hip/hip_runtime.h>
 
 #include "bf16_frag.hpp"
+#include "conv.hpp"
+#include "gate.hpp"
 #include "wave.hpp"
 #include "gdn.h"
 #include "launch.hpp"
@@ -127,9 +134,13 @@ __device__ __forceinline__ float dpp_zero(float x) {
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xF, true));
 }
 
-__device__ __forceinline__ float sumsq8(const float4 &a, const float4 &b) {
-  return a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w + b.x * b.x + b.y * b.y + b.z * b.z +
-         b.w * b.w;
+// |x|^2 of a 128-wide row held as channel quads l and 16 + l by the 16 lanes
+// l of a DPP row: each quad's sum left to right, the lane's two quads added,
+// then the 16-lane butterfly (every lane gets the same bits)
+__device__ __forceinline__ float row_sumsq(const float4 &a, const float4 &b) {
+  const float sa = a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+  const float sb = b.x * b.x + b.y * b.y + b.z * b.z + b.w * b.w;
+  return group_sum<16>(sa + sb);
 }
 // maximum over the wave (exact in any order)
 __device__ __forceinline__ float group_max64(float x) {
@@ -159,12 +170,14 @@ __device__ __forceinline__ int acc_off(int d, int m, int lane) {
 // One workgroup (8 waves) per CU, one (sequence, head, chunk) at a time.  All
 // row-major LDS tiles are bf16 hi/lo planes.  Plan (bytes):
 //   L_K : K rows [t][i]            -> later W rows [s][i]
-//   L_Q : Q rows [t][i] -> V rows  -> later Ut rows [s][j]
+//   L_Q : Q rows [t][i]               (also the source of Q in Q')
+//   L_V : V rows [t][j]            -> later Ut rows [s][j]
 //   L_L : L o Q K^T                 [t][s]
 //   L_A : A, then T in place (fp32 [64][68]);  L_S: four 16x16 blocks (pitch XP) of the inverse
 //         (T1 = T diag(beta e^G) and T2 = T diag(beta) are formed from it as
 //         fragments, in registers)
 //   L_G : G, beta, e^G, e^{G_n - G};  L_N: |k_t|^2, |v_t|^2
+//   L_T : the 4 conv taps of each of the item's 3 x 128 K, Q, V channels
 // The products are computed transposed (feature index as the MFMA row):
 //   W^T = K^T T1^T,  Ut^T = V^T T2^T,  Q'^T = e^G Q^T - W^T (LQK)^T,
 //   Oi^T = Ut^T (LQK)^T
@@ -177,13 +190,15 @@ constexpr int TILE128 = 2 * CH * PR * 2;
 constexpr int TILE64 = 2 * CH * PS * 2;
 constexpr int L_K = 0;
 constexpr int L_Q = L_K + TILE128;
-constexpr int L_L = L_Q + TILE128;
+constexpr int L_V = L_Q + TILE128;
+constexpr int L_L = L_V + TILE128;
 constexpr int L_A = L_L + TILE64;
 constexpr int L_S = L_A + CH * PA * 4;
 constexpr int XP = 17;   // pitch (fp32) of the inverse's scratch blocks
 constexpr int L_G = L_S + 4 * 16 * XP * 4;
 constexpr int L_N = L_G + 4 * CH * 4;   // |k_t|^2, |v_t|^2
-constexpr int L_TOTAL = L_N + 2 * CH * 4;
+constexpr int L_T = L_N + 2 * CH * 4;   // conv taps of the item's K, Q, V channels (ConvSrc)
+constexpr int L_TOTAL = L_T + 3 * DK * 16;
 static_assert(L_TOTAL <= 160 * 1024, "phase A LDS fits one CU");
 
 // Lower 16x16 tiles of K K^T (A = beta_t e^{G_t - G_s} k_t.k_s, strictly lower)
@@ -315,6 +330,7 @@ struct PrepItem {
               // pipeline has no tail): it yields e^{G_n} = 1 and all-zero
               // operands, which leaves the state unchanged
   int nl;     // last valid row, for clamped loads
+  int t0;     // the chunk's first position within its sequence
   int tb;     // row of the chunk's first load (clamped to the sequence's last
               // row for padding chunks); within the sequence for a fixed-length
               // batch, within the packed token rows for a variable-length one
@@ -332,6 +348,7 @@ __device__ __forceinline__ PrepItem prep_item(int u, int n_chunks, int H, int Hk
   const int t0 = c * CH;
   it.n = max(0, min(CH, n_tok - t0));
   it.nl = max(it.n - 1, 0);
+  it.t0 = t0;
   it.tb = min(t0, n_tok - 1);
   it.grow = (int64_t)it.s * n_tok + it.tb;
   it.slot = ((size_t)it.s * H + it.h) * n_chunks + c;
@@ -355,38 +372,40 @@ __device__ __forceinline__ PrepItem prep_item(int u, int n_chunks, int H, int Hk
   const int t0 = (gc - tab.ch0[lo]) * CH;
   it.n = max(0, min(CH, len - t0));
   it.nl = max(it.n - 1, 0);
+  it.t0 = t0;
   it.tb = tab.tok0[lo] + min(t0, len - 1);
   it.grow = it.tb;
   it.slot = (size_t)it.h * n_chunks + gc;
   return it;
 }
 
-// The loads of one item, in the order they are first needed.  Rows past n
-// read a valid row and are zeroed where they are used: a load behind a branch
-// would make the compiler wait for every load in flight at the join.
-// q, k, v elements are fp32 or bf16 (TIN = u16, the bit pattern); either way
-// they are widened to fp32 on load, exactly, so a bf16 call equals an fp32
-// call on the same values bit for bit.
-template <class TIN>
-struct PrepIn {
-  const TIN *q, *k, *v;
-  const float *g, *beta;
-  int64_t qk_tok, qk_seq, v_tok, v_seq;
-  int n_tok, H;
+// ---- phase A inputs
+// An item's gate values and K, Q, V rows come from one of two sources with one
+// interface:
+//   Regs         the next item's loads, in flight while the current item runs
+//   load_gate    g (or what g is computed from) and beta of the chunk's 64
+//                positions, one position per lane
+//   gate         the lane's g
+//   load_rows    the K, Q, V rows (or what they are computed from)
+//   rows_to_lds  K, Q, V rows into their LDS tiles as bf16 hi/lo (rows past n
+//                as zeros) and the row norms |k_t|^2, |v_t|^2 (0 past n)
+//   taps_to_lds  what rows_to_lds reads from LDS besides the rows (after the
+//                last read of the current item's, before the next item)
+// Only wave 7, which forms the gate cumsum, loads the gate values.
+// Rows past n read a valid row and are zeroed where they are used: a load
+// behind a branch would make the compiler wait for every load in flight at
+// the join.
+struct Tiles {
+  u16 *kh, *kl, *qh, *ql, *vh, *vl;
+  float *sNK, *sNV;
+  float4 *taps;   // [3][128]
 };
 __device__ __forceinline__ float bf16_to_f32(unsigned b) { return __builtin_bit_cast(float, b << 16); }
-// 8 consecutive elements as two float4 (16- or 32-byte aligned loads)
-__device__ __forceinline__ void load8f(const float *p, float4 &a, float4 &b) {
-  a = *reinterpret_cast<const float4 *>(p);
-  b = *reinterpret_cast<const float4 *>(p + 4);
-}
-__device__ __forceinline__ void load8f(const u16 *p, float4 &a, float4 &b) {
-  const uint4 u = *reinterpret_cast<const uint4 *>(p);
-  a = make_float4(bf16_to_f32(u.x & 0xffffu), bf16_to_f32(u.x >> 16), bf16_to_f32(u.y & 0xffffu),
-                  bf16_to_f32(u.y >> 16));
-  b = make_float4(bf16_to_f32(u.z & 0xffffu), bf16_to_f32(u.z >> 16), bf16_to_f32(u.w & 0xffffu),
-                  bf16_to_f32(u.w >> 16));
-}
+// Rows of 128 features are moved by the 16 lanes l of a DPP row, lane l
+// holding the feature quads l and 16 + l (features 4l .. 4l+3 and
+// 64 + 4l .. 64 + 4l+3): each load instruction then reads 256 contiguous
+// bytes per row, and the quads are the 4-channel groups of the conv
+// kernels' lanes.
 // 4 consecutive elements as a float4
 __device__ __forceinline__ float4 load4f(const float *p) {
   return *reinterpret_cast<const float4 *>(p);
@@ -396,75 +415,283 @@ __device__ __forceinline__ float4 load4f(const u16 *p) {
   return make_float4(bf16_to_f32(u.x & 0xffffu), bf16_to_f32(u.x >> 16),
                      bf16_to_f32(u.y & 0xffffu), bf16_to_f32(u.y >> 16));
 }
-template <class TIN>
-__device__ __forceinline__ void load_gb(const PrepIn<TIN> &in, const PrepItem &it, int lane, float &gv,
-                                        float &bv) {
-  const int64_t gi = (it.grow + min(lane, it.nl)) * in.H + it.h;
-  gv = in.g[gi];
-  bv = in.beta[gi];
+// the lane's two quads of the row at p
+template <class T>
+__device__ __forceinline__ void load_quads(const T *p, int l, float4 &a, float4 &b) {
+  a = load4f(p + 4 * l);
+  b = load4f(p + 64 + 4 * l);
 }
-// Thread tid holds 8 consecutive floats of a row in each of two passes:
-// pass i covers row (i * 512 + tid) / 16, columns 8 * (tid % 16) .. + 7, as
-// registers r[2i] and r[2i + 1].
-__device__ __forceinline__ void row8_of(int i, int tid, int &row, int &col) {
-  const int idx = i * 512 + tid;
-  row = idx >> 4;
-  col = (idx & 15) * 8;
-}
-template <class TIN>
-__device__ __forceinline__ void load_kq(const PrepIn<TIN> &in, const PrepItem &it, int tid,
-                                        float4 (&kr)[4], float4 (&qr)[4]) {
-  const int64_t base = it.s * in.qk_seq + (int64_t)it.tb * in.qk_tok + it.hk * DK;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    int row, col;
-    row8_of(i, tid, row, col);
-    const int64_t o = base + (int64_t)min(row, it.nl) * in.qk_tok + col;
-    load8f(in.k + o, kr[2 * i], kr[2 * i + 1]);
-    load8f(in.q + o, qr[2 * i], qr[2 * i + 1]);
-  }
-}
-template <class TIN>
-__device__ __forceinline__ void load_v(const PrepIn<TIN> &in, const PrepItem &it, int tid,
-                                       float4 (&vr)[4]) {
-  const int64_t base = it.s * in.v_seq + (int64_t)it.tb * in.v_tok + it.h * DV;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    int row, col;
-    row8_of(i, tid, row, col);
-    load8f(in.v + base + (int64_t)min(row, it.nl) * in.v_tok + col, vr[2 * i], vr[2 * i + 1]);
-  }
-}
+// Thread tid moves row (i * 512 + tid) / 16 in pass i (i = 0, 1) as lane
+// l = tid % 16 of its row.
+__device__ __forceinline__ int row_of(int i, int tid) { return (i * 512 + tid) >> 4; }
+// the lane's two quads into the bf16 hi/lo planes of row `row` of a tile;
 // rows past n are written as zeros
-__device__ __forceinline__ void store_row8(u16 *hi, u16 *lo, const float4 &a, const float4 &b,
-                                           bool valid) {
-  const float x[8] = {valid ? a.x : 0.f, valid ? a.y : 0.f, valid ? a.z : 0.f, valid ? a.w : 0.f,
-                      valid ? b.x : 0.f, valid ? b.y : 0.f, valid ? b.z : 0.f, valid ? b.w : 0.f};
-  store8_split(hi, lo, x);
+__device__ __forceinline__ void store_quads(u16 *hi, u16 *lo, int row, int l, const float4 &a,
+                                            const float4 &b, bool valid) {
+  const int o = row * PR + 4 * l;
+  if (valid) {
+    store4_split(hi + o, lo + o, a.x, a.y, a.z, a.w);
+    store4_split(hi + o + 64, lo + o + 64, b.x, b.y, b.z, b.w);
+  } else {
+    store4_split(hi + o, lo + o, 0.f, 0.f, 0.f, 0.f);
+    store4_split(hi + o + 64, lo + o + 64, 0.f, 0.f, 0.f, 0.f);
+  }
 }
 
+// q, k, v, g as given; q, k, v elements fp32 or bf16 (TIN = u16, the bit
+// pattern), widened to fp32 on load, exactly, so a bf16 call equals an fp32
+// call on the same values bit for bit.
+template <class TIN>
+struct DirectSrc {
+  const TIN *q, *k, *v;
+  const float *g, *beta;
+  int64_t qk_tok, qk_seq, v_tok, v_seq;
+  int n_tok, H;
+  struct Regs {
+    float4 kr[4], qr[4], vr[4];
+    float gv, bv;
+  };
+  __device__ __forceinline__ void load_gate(const PrepItem &it, int lane, Regs &r) const {
+    const int64_t gi = (it.grow + min(lane, it.nl)) * H + it.h;
+    r.gv = g[gi];
+    r.bv = beta[gi];
+  }
+  __device__ __forceinline__ float gate(const Regs &r) const { return r.gv; }
+  // part 0: K rows, 1: Q rows, 2: V rows
+  template <int PART>
+  __device__ __forceinline__ void load_rows(const PrepItem &it, int tid, Regs &r) const {
+    const int64_t kb = it.s * qk_seq + (int64_t)it.tb * qk_tok + it.hk * DK;
+    const int64_t vb = it.s * v_seq + (int64_t)it.tb * v_tok + it.h * DV;
+    const int l = tid & 15;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int rr = min(row_of(i, tid), it.nl);
+      if constexpr (PART == 0)
+        load_quads(k + kb + (int64_t)rr * qk_tok, l, r.kr[2 * i], r.kr[2 * i + 1]);
+      if constexpr (PART == 1)
+        load_quads(q + kb + (int64_t)rr * qk_tok, l, r.qr[2 * i], r.qr[2 * i + 1]);
+      if constexpr (PART == 2)
+        load_quads(v + vb + (int64_t)rr * v_tok, l, r.vr[2 * i], r.vr[2 * i + 1]);
+    }
+  }
+  __device__ __forceinline__ void rows_to_lds(const PrepItem &it, int tid, const Regs &r,
+                                              const Tiles &t) const {
+    const int l = tid & 15;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = row_of(i, tid);
+      const bool valid = row < it.n;
+      store_quads(t.kh, t.kl, row, l, r.kr[2 * i], r.kr[2 * i + 1], valid);
+      store_quads(t.qh, t.ql, row, l, r.qr[2 * i], r.qr[2 * i + 1], valid);
+      store_quads(t.vh, t.vl, row, l, r.vr[2 * i], r.vr[2 * i + 1], valid);
+      const float nk = row_sumsq(r.kr[2 * i], r.kr[2 * i + 1]);
+      const float nv = row_sumsq(r.vr[2 * i], r.vr[2 * i + 1]);
+      if (l == 0) {
+        t.sNK[row] = valid ? nk : 0.0f;
+        t.sNV[row] = valid ? nv : 0.0f;
+      }
+    }
+  }
+  __device__ __forceinline__ void taps_to_lds(int, const Regs &, const Tiles &) const {}
+};
+
+__device__ __forceinline__ float f4_at(const float4 &v, int e) {
+  return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+}
+
+// The layer's own inputs: the conv input rows x (channels: q heads, k heads,
+// v heads, S = 128 wide), the 4-tap conv weights and history, alpha (g is
+// decay_gate_value(alpha, dt[h], a[h]), as the gate kernel computes it) and
+// beta.  K, Q, V are the conv1d + SiLU outputs (K and Q then L2-normalised
+// per head) with the conv kernels' arithmetic: conv_position() per channel,
+// and the L2 sum of squares in the same tree as their 32-lane butterfly over
+// 4-channel lanes (that butterfly sums channel quads 0..15 and 16..31 of the
+// head in two 16-lane trees, then adds the two: here a lane holds quads l
+// and 16 + l, and runs the two 16-lane trees itself), so K, Q, V are bit for
+// bit the rows gdn_conv1d_silu_l2norm writes.
+// Lanes: waves 0, 1 hold K, waves 2, 3 Q (8 rows each: rows 8rg .. 8rg+7,
+// rg = tid / 16 % 8), waves 4..7 V (4 rows each: rows 4rg .. 4rg+3,
+// rg = tid / 16 % 16), so every SIMD (waves w and w + 4) computes 12 rows:
+// the conv is VALU work, about 20 instructions per output.  A lane holds
+// quads l, 16 + l (l = tid % 16) of its rows, the 16 lanes of a DPP row
+// sharing their rows, and keeps the input rows of its rows' windows (11
+// rows for K and Q, 7 for V).  The taps go through LDS (L_T), one 16-byte
+// record per channel, read by every lane that needs them.
+struct ConvSrc {
+  const float *x;
+  int64_t x_tok, x_seq;
+  const float *w;       // [conv channel][4 taps], oldest tap first
+  const float *hist;    // [sequence][conv channel][3], oldest first
+  int64_t h_seq;
+  const float *alpha, *dt, *a, *beta;
+  float eps;
+  int n_tok, H, Hk;
+  struct Regs {
+    float4 raw[11][2];   // [input row][quad l, quad 16 + l]
+    float4 tw;           // lane tid < 384: the taps of channel tid % 128 of matrix tid / 128
+    float gv, bv, dtv, av;
+  };
+  __device__ __forceinline__ int64_t chan0(const PrepItem &it, int m) const {
+    return m == 0 ? (int64_t)(Hk + it.hk) * DK
+                  : m == 1 ? (int64_t)it.hk * DK : (int64_t)2 * Hk * DK + (int64_t)it.h * DV;
+  }
+  __device__ __forceinline__ void load_gate(const PrepItem &it, int lane, Regs &r) const {
+    const int64_t gi = (it.grow + min(lane, it.nl)) * H + it.h;
+    r.gv = alpha[gi];
+    r.bv = beta[gi];
+    r.dtv = dt[it.h];
+    r.av = a[it.h];
+  }
+  __device__ __forceinline__ float gate(const Regs &r) const {
+    return decay_gate_value(r.gv, r.dtv, r.av);
+  }
+  // the lane's matrix (0 K, 1 Q, 2 V), first row and row count
+  __device__ __forceinline__ static void lane_rows(int tid, int &m, int &row0, int &nrow) {
+    const int w = tid >> 6;
+    m = w < 4 ? w >> 1 : 2;
+    nrow = w < 4 ? 8 : 4;
+    row0 = w < 4 ? 8 * ((tid >> 4) & 7) : 4 * ((tid >> 4) & 15);
+  }
+  // part 0: input rows 0..3, 1: rows 4..7, 2: rows 8..10 and the taps.
+  // In a sequence's first chunk, rows 0..2 of the lanes whose first row is 0
+  // are positions before 0, read from the history ([channel][tap]) instead
+  // of x: that item (a uniform branch) reads rows 0..2 element by element,
+  // each lane from its own source.  Either way only loads into the same
+  // registers are issued, so the later wait for them counts these loads
+  // alone (a wait after a branch whose loads are newer than the item's
+  // stores would also wait for the stores).
+  template <int PART>
+  __device__ __forceinline__ void load_rows(const PrepItem &it, int tid, Regs &r) const {
+    const int l = tid & 15;
+    int m, row0, nrow;
+    lane_rows(tid, m, row0, nrow);
+    const int64_t ch = chan0(it, m) + 4 * l;
+    const float *xs = x + it.s * x_seq + ch;
+    // input row j is position t0 + row0 - 3 + j (a V lane needs rows 0..6)
+    auto pos = [&](int j) { return min(max(it.t0 + row0 - 3 + j, 0), n_tok - 1); };
+    auto row = [&](int j) __attribute__((always_inline)) {
+      const float *xr = xs + (int64_t)pos(j) * x_tok;
+      r.raw[j][0] = load4f(xr);
+      r.raw[j][1] = load4f(xr + 64);
+    };
+    if constexpr (PART == 0) {
+      if (it.t0 == 0) {
+        const float *hp = hist + it.s * h_seq + ch * 3;
+        const bool from_hist = row0 == 0;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+          const float *xr = xs + (int64_t)pos(j) * x_tok;
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int c = (e & 3) + (e >> 2) * 64;   // channel offset from ch
+            v[e] = from_hist ? hp[c * 3 + j] : xr[c];
+          }
+          r.raw[j][0] = make_float4(v[0], v[1], v[2], v[3]);
+          r.raw[j][1] = make_float4(v[4], v[5], v[6], v[7]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 3; ++j) row(j);
+      }
+      row(3);
+    }
+    if constexpr (PART == 1) {
+#pragma unroll
+      for (int j = 4; j < 7; ++j) row(j);
+      if (nrow == 8) row(7);   // uniform per wave
+    }
+    if constexpr (PART == 2) {
+      if (nrow == 8) {         // uniform per wave
+#pragma unroll
+        for (int j = 8; j < 11; ++j) row(j);
+      }
+      // the item's taps, 16 contiguous bytes per lane (lanes 384..511 read
+      // the first record again and store nothing)
+      const int tm = min(tid >> 7, 2), tc = tid < 384 ? tid & 127 : 0;
+      r.tw = *reinterpret_cast<const float4 *>(w + (chan0(it, tm) + tc) * 4);
+    }
+  }
+  __device__ __forceinline__ void taps_to_lds(int tid, const Regs &r, const Tiles &t) const {
+    if (tid < 384) t.taps[tid] = r.tw;
+  }
+  __device__ __forceinline__ void rows_to_lds(const PrepItem &it, int tid, const Regs &r,
+                                              const Tiles &t) const {
+    const int l = tid & 15;
+    int m, row0, nrow;
+    lane_rows(tid, m, row0, nrow);
+    // the K, Q, V tiles are evenly spaced, |v|^2 follows |k|^2 (an offset,
+    // not a choice among pointers, which the compiler would keep in memory)
+    static_assert(L_Q - L_K == TILE128 && L_V - L_Q == TILE128, "tile spacing");
+    u16 *hi = t.kh + m * (TILE128 / 2);
+    u16 *lo = hi + CH * PR;
+    float *sn = t.sNK + (m == 0 ? 0 : CH);
+    float wv[8][4];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float4 tv = t.taps[m * DK + 4 * l + (e & 3) + (e >> 2) * 64];
+      wv[e][0] = tv.x;
+      wv[e][1] = tv.y;
+      wv[e][2] = tv.z;
+      wv[e][3] = tv.w;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i < nrow) {   // uniform per wave
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float win[4] = {f4_at(r.raw[i][e >> 2], e & 3), f4_at(r.raw[i + 1][e >> 2], e & 3),
+                                f4_at(r.raw[i + 2][e >> 2], e & 3),
+                                f4_at(r.raw[i + 3][e >> 2], e & 3)};
+          o[e] = conv_position<4>(wv[e], win);
+        }
+        if (m < 2) {
+          float sa = o[0] * o[0], sb = o[4] * o[4];
+#pragma unroll
+          for (int e = 1; e < 4; ++e) {
+            sa = __builtin_fmaf(o[e], o[e], sa);
+            sb = __builtin_fmaf(o[4 + e], o[4 + e], sb);
+          }
+          const float inv = l2_rsqrt(group_sum<16>(sa) + group_sum<16>(sb) + eps);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] *= inv;
+        }
+        const int row = row0 + i;
+        const bool valid = row < it.n;
+        const float4 a0 = make_float4(o[0], o[1], o[2], o[3]);
+        const float4 a1 = make_float4(o[4], o[5], o[6], o[7]);
+        store_quads(hi, lo, row, l, a0, a1, valid);
+        if (m != 1) {
+          const float nr = row_sumsq(a0, a1);
+          if (l == 0) sn[row] = valid ? nr : 0.0f;
+        }
+      }
+    }
+  }
+};
+
 // Persistent: workgroup b handles items b, b + G, b + 2G, ... (G = grid size,
-// at most one workgroup per CU given the LDS it takes).  The next item's g,
-// beta, K, Q and V are loaded into registers as soon as the current item has
-// consumed them, so a workgroup's loads and stores overlap its own compute
+// at most one workgroup per CU given the LDS it takes).  The next item's
+// gate values and rows are loaded into registers as soon as the current item
+// has consumed them, so a workgroup's loads and stores overlap its own compute
 // instead of every CU loading, then computing, then storing in lockstep.
-template <class TAB, class TIN>
-__global__ __launch_bounds__(512) void k_chunk_prep(
-    const TIN *__restrict__ q, const TIN *__restrict__ k, int64_t qk_tok, int64_t qk_seq,
-    const TIN *__restrict__ v, int64_t v_tok, int64_t v_seq, const float *__restrict__ g,
-    const float *__restrict__ beta, unsigned char *__restrict__ ws, int n_tok, int n_chunks,
-    int H, int Hk, int n_items, const TAB tab) {
+template <class TAB, class SRC>
+__global__ __launch_bounds__(512) void k_chunk_prep(const SRC src, unsigned char *__restrict__ ws,
+                                                    int n_tok, int n_chunks, int H, int Hk,
+                                                    int n_items, const TAB tab) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[L_TOTAL];
-  const PrepIn<TIN> in{q, k, v, g, beta, qk_tok, qk_seq, v_tok, v_seq, n_tok, H};
 
   u16 *kh = reinterpret_cast<u16 *>(smem + L_K), *klo = kh + CH * PR;
   u16 *qh = reinterpret_cast<u16 *>(smem + L_Q), *qlo = qh + CH * PR;
+  u16 *vh = reinterpret_cast<u16 *>(smem + L_V), *vlo = vh + CH * PR;
   u16 *lqh = reinterpret_cast<u16 *>(smem + L_L), *lql = lqh + CH * PS;
   float *sA = reinterpret_cast<float *>(smem + L_A);
   float *scratch = reinterpret_cast<float *>(smem + L_S);
   float *sG = reinterpret_cast<float *>(smem + L_G);
   float *sBeta = sG + CH, *sEG = sG + 2 * CH, *sEGn = sG + 3 * CH;
   float *sNK = reinterpret_cast<float *>(smem + L_N), *sNV = sNK + CH;
+  const Tiles tiles{kh, klo, qh, qlo, vh, vlo, sNK, sNV, reinterpret_cast<float4 *>(smem + L_T)};
 
   // (L o QK^T) and A, which lie back to back, are cleared once: every item
   // writes every entry of their lower 16x16 tiles (zeros above the diagonal
@@ -479,11 +706,13 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
   }
   // the grid never exceeds n_items, so every workgroup has a first item
   PrepItem it = prep_item(blockIdx.x, n_chunks, H, Hk, n_tok, tab);
-  float gv, bv;
-  float4 kr[4], qr[4], vr[4];
-  load_gb(in, it, threadIdx.x & 63, gv, bv);
-  load_kq(in, it, threadIdx.x, kr, qr);
-  load_v(in, it, threadIdx.x, vr);
+  typename SRC::Regs pre;
+  if ((threadIdx.x >> 6) == 7) src.load_gate(it, threadIdx.x & 63, pre);
+  src.template load_rows<0>(it, threadIdx.x, pre);
+  src.template load_rows<1>(it, threadIdx.x, pre);
+  src.template load_rows<2>(it, threadIdx.x, pre);
+  src.taps_to_lds(threadIdx.x, pre, tiles);
+  __syncthreads();
 
   // One item; the first is peeled off the loop below so that the loop head is
   // reached from one place only and the compiler's load/store counts there
@@ -499,17 +728,16 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
   // then redundant but in bounds, and no load sits behind a branch)
   const PrepItem nx = prep_item(u + gridDim.x < n_items ? u + gridDim.x : u, n_chunks, H, Hk,
                                 n_tok, tab);
-  const int n = it.n, nl = it.nl;
-  const TIN *qc = q + it.s * qk_seq + (int64_t)it.tb * qk_tok + it.hk * DK;
+  const int n = it.n;
   unsigned char *wc = ws + it.slot * WS_CHUNK;
 
-  // S0. gate cumsum (wave 0): an inclusive scan over the 64 lanes on DPP
+  // S0. gate cumsum (wave 7): an inclusive scan over the 64 lanes on DPP
   // (row shifts within each 16-lane row, then the row totals broadcast across
   // rows), and the exponentials as the hardware base-2 exponential of
   // x log2(e) (all arguments are <= 0)
-  if (w == 0) {
-    float x = lane < n ? gv : 0.0f;
-    const float b = lane < n ? bv : 0.0f;
+  if (w == 7) {
+    float x = lane < n ? src.gate(pre) : 0.0f;
+    const float b = lane < n ? pre.bv : 0.0f;
     x += dpp_zero<0x111, 0xF>(x);   // row_shr:1
     x += dpp_zero<0x112, 0xF>(x);   // row_shr:2
     x += dpp_zero<0x114, 0xF>(x);   // row_shr:4
@@ -523,18 +751,12 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
     sEG[lane] = __builtin_amdgcn_exp2f(x * LOG2E);
     sEGn[lane] = __builtin_amdgcn_exp2f((gn - x) * LOG2E);
   }
-  load_gb(in, nx, lane, gv, bv);
-  // S1. K, Q rows -> LDS (bf16 hi/lo); |k_t|^2 of each row (16 lanes per row)
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    int row, col;
-    row8_of(i, tid, row, col);
-    store_row8(kh + row * PR + col, klo + row * PR + col, kr[2 * i], kr[2 * i + 1], row < n);
-    store_row8(qh + row * PR + col, qlo + row * PR + col, qr[2 * i], qr[2 * i + 1], row < n);
-    const float nk = group_sum<16>(sumsq8(kr[2 * i], kr[2 * i + 1]));
-    if ((tid & 15) == 0) sNK[row] = row < n ? nk : 0.0f;
-  }
-  load_kq(in, nx, tid, kr, qr);
+  if (w == 7) src.load_gate(nx, lane, pre);
+  // S1. K, Q, V rows -> LDS (bf16 hi/lo); |k_t|^2, |v_t|^2 of each row
+  src.rows_to_lds(it, tid, pre, tiles);
+  // the next item's rows in three parts, spread over the item so that no
+  // section issues them all at once
+  src.template load_rows<0>(nx, tid, pre);
   __syncthreads();
 
   // S2a. K K^T and Q K^T on the 10 lower tile positions each: 20 tiles; waves
@@ -546,6 +768,7 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
   } else {
     lower_tiles<2>(w, kh, klo, qh, qlo, sA, lqh, lql, sG, sBeta, l16, kg);
   }
+  src.template load_rows<1>(nx, tid, pre);
   // S2b. K'^T fragments (K' = diag(e^{G_n - G}) K) straight from the K tile,
   // as fp16 hi and lo planes: wave w writes key tile w, both token k-steps
   {
@@ -563,9 +786,9 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
   }
   __syncthreads();
 
+  src.template load_rows<2>(nx, tid, pre);
   // S3a. T = (I + A)^{-1} in place: threads 0..63 invert the four 16x16
-  // diagonal blocks (one column each, forward substitution in fp32); the
-  // other threads move V into the Q tile (Q is no longer needed).
+  // diagonal blocks (one column each, forward substitution in fp32).
   float x[16];
   if (tid < 64) {
     const int b = tid >> 4, cc = tid & 15;
@@ -577,15 +800,6 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
       x[r] = acc;
     }
   }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    int row, col;
-    row8_of(i, tid, row, col);
-    store_row8(qh + row * PR + col, qlo + row * PR + col, vr[2 * i], vr[2 * i + 1], row < n);
-    const float nv = group_sum<16>(sumsq8(vr[2 * i], vr[2 * i + 1]));
-    if ((tid & 15) == 0) sNV[row] = row < n ? nv : 0.0f;
-  }
-  load_v(in, nx, tid, vr);
   __syncthreads();  // every diagonal block read before any is overwritten
   if (tid < 64) {
     const int b = tid >> 4, cc = tid & 15;
@@ -634,16 +848,6 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
   // S5. W^T = K^T T1^T and Ut^T = V^T T2^T.  Wave w owns key/value tiles
   // 2kp, 2kp+1 (kp = w & 3) and token tiles 2tp, 2tp+1 (tp = w >> 2).
   const int kp = w & 3, tp = w >> 2;
-  // Q at the accumulator positions of Q'^T, needed in S6; loaded now so the
-  // loads are in flight during the products
-  float4 qa[2][2];
-#pragma unroll
-  for (int d = 0; d < 2; ++d)
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int t = 16 * (2 * tp + m) + l16;
-      qa[d][m] = load4f(qc + (int64_t)min(t, nl) * qk_tok + 16 * (2 * kp + d) + 4 * kg);
-    }
   f32x4 accW[2][2], accU[2][2];
 #pragma unroll
   for (int d = 0; d < 2; ++d)
@@ -659,7 +863,7 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
 #pragma unroll
     for (int d = 0; d < 2; ++d) {
       const Frag ak = frag_tr(kh, klo, PR, 32 * ks, 16 * (2 * kp + d), kg, l16);
-      const Frag av = frag_tr(qh, qlo, PR, 32 * ks, 16 * (2 * kp + d), kg, l16);
+      const Frag av = frag_tr(vh, vlo, PR, 32 * ks, 16 * (2 * kp + d), kg, l16);
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         accW[d][m] = mfma3(ak, bt1[m], accW[d][m]);
@@ -682,7 +886,7 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
     }
   }
   __syncthreads();  // K and V tiles are rewritten below
-  // W rows [s][i] into the K tile, Ut rows [s][j] into the Q/V tile
+  // W rows [s][i] into the K tile, Ut rows [s][j] into the V tile
 #pragma unroll
   for (int d = 0; d < 2; ++d)
 #pragma unroll
@@ -690,7 +894,7 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
       const int row = 16 * (2 * tp + m) + l16, col = 16 * (2 * kp + d) + 4 * kg;
       store4_split(kh + row * PR + col, klo + row * PR + col, accW[d][m][0], accW[d][m][1],
                    accW[d][m][2], accW[d][m][3]);
-      store4_split(qh + row * PR + col, qlo + row * PR + col, accU[d][m][0], accU[d][m][1],
+      store4_split(vh + row * PR + col, vlo + row * PR + col, accU[d][m][0], accU[d][m][1],
                    accU[d][m][2], accU[d][m][3]);
     }
   __syncthreads();
@@ -709,7 +913,7 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
 #pragma unroll
     for (int d = 0; d < 2; ++d) {
       const Frag aw = frag_tr(kh, klo, PR, 32 * ks, 16 * (2 * kp + d), kg, l16);
-      const Frag au = frag_tr(qh, qlo, PR, 32 * ks, 16 * (2 * kp + d), kg, l16);
+      const Frag au = frag_tr(vh, vlo, PR, 32 * ks, 16 * (2 * kp + d), kg, l16);
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         accQ[d][m] = mfma3(aw, bl[m], accQ[d][m]);
@@ -727,7 +931,16 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
       float xq[8];
 #pragma unroll
       for (int d = 0; d < 2; ++d) {
-        const float4 qv = qa[d][m];
+        // Q at this accumulator position: hi + lo of the Q tile (exact in
+        // fp32, within 2^-17 of the row as given; zero past n)
+        const int qo = t * PR + 16 * (2 * kp + d) + 4 * kg;
+        const uint2 qhv = *reinterpret_cast<const uint2 *>(qh + qo);
+        const uint2 qlv = *reinterpret_cast<const uint2 *>(qlo + qo);
+        const float4 qv = make_float4(
+            bf16_to_f32(qhv.x & 0xffffu) + bf16_to_f32(qlv.x & 0xffffu),
+            bf16_to_f32(qhv.x >> 16) + bf16_to_f32(qlv.x >> 16),
+            bf16_to_f32(qhv.y & 0xffffu) + bf16_to_f32(qlv.y & 0xffffu),
+            bf16_to_f32(qhv.y >> 16) + bf16_to_f32(qlv.y >> 16));
         xq[4 * d + 0] = eg * qv.x - accQ[d][m][0];
         xq[4 * d + 1] = eg * qv.y - accQ[d][m][1];
         xq[4 * d + 2] = eg * qv.z - accQ[d][m][2];
@@ -738,15 +951,15 @@ __global__ __launch_bounds__(512) void k_chunk_prep(
       store8_h(qg + frag_off(2 * tp + m, kp, 4, lane), xq);
     }
   }
-  // the chunk's header: every wave forms b and a from the row norms with the
-  // same butterflies, so every thread stores the same bits (no store behind
-  // a branch)
-  {
+  // the chunk's header, formed and stored by wave 0 (every lane stores the
+  // same bits)
+  if (w == 0) {
     const float bk = sBeta[lane] * sqrtf(sNK[lane]);
     const float b = group_sum<64>(bk * sqrtf(sNV[lane]));
     const float am = group_max64(bk);
     *reinterpret_cast<float4 *>(wc + WS_G) = make_float4(sEG[CH - 1], b, am, 0.0f);
   }
+  src.taps_to_lds(tid, pre, tiles);
   __syncthreads();   // the next item rewrites every LDS tile
   it = nx;
   };
@@ -944,6 +1157,55 @@ __device__ __forceinline__ void xcd_order(int b, int nwg, int per, int &sh, int 
   }
 }
 
+// The conv history after a sequence's last position, when phase A took its
+// K, Q, V from the conv (ConvSrc): phase B writes it, since phase A's first
+// chunks read the old history and no phase A workgroup can know when the
+// others are done with it.  Each scan workgroup takes the channels of its
+// value columns [c0, c0 + nc): the v channels of head h and, in the first
+// value head of each query/key group, the q and k channels of the group's
+// head.  Thread t < 3 nc takes one channel (part t / nc: v, q, k) and
+// its 3 taps, new tap j = input position n_tok - 3 + j, or old tap
+// n_tok + j when that position is before 0; the taps are read in the
+// prologue and written after the scan, by the same thread, so no tap is
+// overwritten before it is read.  hist == nullptr: no history (x is then any
+// valid address and the reads are discarded).
+struct HistOut {
+  const float *x;
+  int64_t x_tok, x_seq;
+  float *hist;
+  int64_t h_seq;
+  int n_tok, Hk, G;   // G value heads per query/key head
+};
+struct HistTaps {
+  float v[3];
+  float *dst;        // the channel's 3 taps, or nullptr
+};
+__device__ __forceinline__ HistTaps hist_read(const HistOut &ho, int s, int h, int c0, int nc,
+                                              int tid) {
+  const int part = tid / nc, i = tid % nc, hk = h / ho.G;
+  const bool on = ho.hist != nullptr && part < (h % ho.G == 0 ? 3 : 1);
+  const int64_t ch = part == 0 ? (int64_t)2 * ho.Hk * DK + (int64_t)h * DV + c0 + i
+                   : part == 1 ? (int64_t)hk * DK + c0 + i
+                               : (int64_t)(ho.Hk + hk) * DK + c0 + i;
+  HistTaps r;
+  float *hp = on ? ho.hist + s * ho.h_seq + ch * 3 : nullptr;
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const int p = ho.n_tok - 3 + j;
+    const float *src = !on ? ho.x : p >= 0 ? ho.x + s * ho.x_seq + (int64_t)p * ho.x_tok + ch
+                                           : hp + (p + 3);
+    r.v[j] = *src;
+  }
+  r.dst = hp;
+  return r;
+}
+__device__ __forceinline__ void hist_write(const HistTaps &r) {
+  if (r.dst != nullptr) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) r.dst[j] = r.v[j];
+  }
+}
+
 constexpr int SPB = 24;   // pitch (bf16) of the [128][16] S tile and the [64][16] U tile
 
 // One chunk of the scan on a workgroup's VT value tiles.  The state tile of
@@ -1012,7 +1274,7 @@ template <class TAB, int VT>
 __global__ __launch_bounds__(512) void k_chunk_scan(
     float *__restrict__ state, int64_t st_seq, const unsigned char *__restrict__ ws,
     float *__restrict__ y, int64_t y_tok, int64_t y_seq, int n_tok, int n_chunks, int H,
-    float scale, const TAB tab) {
+    float scale, const TAB tab, const HistOut ho) {
   constexpr int SP = NBLK * VT + 8;
   __shared__ __attribute__((aligned(16))) u16 ssh[DK * SP], ssl[DK * SP];
   __shared__ __attribute__((aligned(16))) u16 suh[CH * SP], sul[CH * SP];
@@ -1024,6 +1286,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan(
   blk *= VT;   // first value tile
   const int h = sh % H, s = sh / H;
   const HeadChunks hc = head_chunks(tab, s, h, H, n_tok, n_chunks);
+  const HistTaps taps = hist_read(ho, s, h, blk * NBLK, VT * NBLK, tid);
 
   // state element (value j = 16 (blk + d) + 4kg + r, key i = 16w + l16), value-major
   float *sp = state + s * st_seq + (int64_t)h * DK * DV +
@@ -1067,6 +1330,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan(
     p[2 * DK] = st[d][2];
     p[3 * DK] = st[d][3];
   }
+  hist_write(taps);
 }
 
 // ---- phase B for grids that exceed one pass of the chip
@@ -1093,7 +1357,7 @@ template <class TAB>
 __global__ __launch_bounds__(PAIR_THREADS) void k_chunk_scan_pair(
     float *__restrict__ state, int64_t st_seq, const unsigned char *__restrict__ ws,
     float *__restrict__ y, int64_t y_tok, int64_t y_seq, int n_tok, int n_chunks, int H,
-    float scale, const TAB tab) {
+    float scale, const TAB tab, const HistOut ho) {
   constexpr int NWQ = OPS_WQ / (16 * PAIR_THREADS), NK = OPS_K / (16 * PAIR_THREADS);
   __shared__ __attribute__((aligned(16))) u16 ssh[2][DK * SPB], ssl[2][DK * SPB];
   __shared__ __attribute__((aligned(16))) u16 suh[2][CH * SPB], sul[2][CH * SPB];
@@ -1108,6 +1372,7 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_chunk_scan_pair(
   const int h = sh % H, s = sh / H;
   const int blk = 2 * pair + grp;
   const HeadChunks hc = head_chunks(tab, s, h, H, n_tok, n_chunks);
+  const HistTaps taps = hist_read(ho, s, h, 2 * pair * NBLK, 2 * NBLK, tid);
 
   float *sp = state + s * st_seq + (int64_t)h * DK * DV +
               (int64_t)(blk * NBLK + 4 * kg) * DK + 16 * w + l16;
@@ -1211,6 +1476,7 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_chunk_scan_pair(
   sp[DK] = st[1];
   sp[2 * DK] = st[2];
   sp[3 * DK] = st[3];
+  hist_write(taps);
 }
 
 }  // namespace
@@ -1247,18 +1513,16 @@ static int device_cu_count() {
 
 // Phase A then phase B of one call; n_chunks is the per-sequence chunk count
 // (fixed-length batch) or the packed total (variable-length batch).
-template <class TAB, class TIN>
-static int launch_two_phase(const RecurArgs &a, const TAB &tab, const TIN *q, const TIN *k,
-                            const TIN *v, int n_chunks, int n_items, unsigned char *wsb,
-                            hipStream_t stream) {
+template <class TAB, class SRC>
+static int launch_two_phase(const RecurArgs &a, const TAB &tab, const SRC &src, const HistOut &ho,
+                            int n_chunks, int n_items, unsigned char *wsb, hipStream_t stream) {
   // phase A: one persistent workgroup per CU (its LDS allows no more), or one
   // per item when there are fewer items than CUs
   const int cus = device_cu_count();
   if (cus <= 0) return GDN_ERR_LAUNCH;
   const int grid_a = n_items < cus ? n_items : cus;
-  int rc = launch_kernel(k_chunk_prep<TAB, TIN>, dim3(grid_a), dim3(512), 0, stream, q, k,
-                         a.qk_tok, a.qk_seq, v, a.v_tok, a.v_seq, a.g, a.beta, wsb, a.n_tok,
-                         n_chunks, a.H, a.Hk, n_items, tab);
+  int rc = launch_kernel(k_chunk_prep<TAB, SRC>, dim3(grid_a), dim3(512), 0, stream, src, wsb,
+                         a.n_tok, n_chunks, a.H, a.Hk, n_items, tab);
   if (rc != GDN_OK) return rc;
   // phase B: 8-wave workgroups of one value tile each while they fit in one
   // pass of the chip (measured: two or four tiles per workgroup lengthen the
@@ -1269,10 +1533,20 @@ static int launch_two_phase(const RecurArgs &a, const TAB &tab, const TIN *q, co
   if (units * NVB > cus)
     return launch_kernel(k_chunk_scan_pair<TAB>, dim3(units * (NVB / 2)), dim3(PAIR_THREADS), 0,
                          stream, a.state, a.st_seq, (const unsigned char *)wsb, a.y, a.y_tok,
-                         a.y_seq, a.n_tok, n_chunks, a.H, a.scale, tab);
+                         a.y_seq, a.n_tok, n_chunks, a.H, a.scale, tab, ho);
   return launch_kernel(k_chunk_scan<TAB, 1>, dim3(units * NVB), dim3(512), 0, stream, a.state,
                        a.st_seq, (const unsigned char *)wsb, a.y, a.y_tok, a.y_seq, a.n_tok,
-                       n_chunks, a.H, a.scale, tab);
+                       n_chunks, a.H, a.scale, tab, ho);
+}
+
+// No conv history to write: any valid address for the discarded reads.
+static HistOut no_hist(const RecurArgs &a) {
+  return HistOut{a.state, 0, 0, nullptr, 0, 3, a.Hk, a.H / a.Hk};
+}
+
+template <class TIN>
+static DirectSrc<TIN> direct_src(const RecurArgs &a, const TIN *q, const TIN *k, const TIN *v) {
+  return DirectSrc<TIN>{q, k, v, a.g, a.beta, a.qk_tok, a.qk_seq, a.v_tok, a.v_seq, a.n_tok, a.H};
 }
 
 int launch_recur_chunked(const RecurArgs &a, int chunk, void *ws, size_t ws_bytes,
@@ -1282,8 +1556,8 @@ int launch_recur_chunked(const RecurArgs &a, int chunk, void *ws, size_t ws_byte
   const int n_chunks = padded_chunks(a.n_tok);
   if (ws_bytes < chunked_workspace_bytes(a.n_seq, a.n_tok, a.H, a.Hk, a.S, chunk))
     return GDN_ERR_WORKSPACE;
-  return launch_two_phase(a, NoTab{}, a.q, a.k, a.v, n_chunks, n_chunks * a.H * a.n_seq,
-                          static_cast<unsigned char *>(ws), stream);
+  return launch_two_phase(a, NoTab{}, direct_src(a, a.q, a.k, a.v), no_hist(a), n_chunks,
+                          n_chunks * a.H * a.n_seq, static_cast<unsigned char *>(ws), stream);
 }
 
 int launch_recur_chunked_varlen(const RecurArgs &a, const VarTab &tab, bool bf16_in, int chunk,
@@ -1295,10 +1569,26 @@ int launch_recur_chunked_varlen(const RecurArgs &a, const VarTab &tab, bool bf16
   if (ws_bytes < (size_t)n_chunks * a.H * WS_CHUNK) return GDN_ERR_WORKSPACE;
   unsigned char *wsb = static_cast<unsigned char *>(ws);
   if (bf16_in)
-    return launch_two_phase(a, tab, reinterpret_cast<const u16 *>(a.q),
-                            reinterpret_cast<const u16 *>(a.k), reinterpret_cast<const u16 *>(a.v),
-                            n_chunks, n_chunks * a.H, wsb, stream);
-  return launch_two_phase(a, tab, a.q, a.k, a.v, n_chunks, n_chunks * a.H, wsb, stream);
+    return launch_two_phase(a, tab,
+                            direct_src(a, reinterpret_cast<const u16 *>(a.q),
+                                       reinterpret_cast<const u16 *>(a.k),
+                                       reinterpret_cast<const u16 *>(a.v)),
+                            no_hist(a), n_chunks, n_chunks * a.H, wsb, stream);
+  return launch_two_phase(a, tab, direct_src(a, a.q, a.k, a.v), no_hist(a), n_chunks,
+                          n_chunks * a.H, wsb, stream);
+}
+
+int launch_prefill_chunked(const RecurArgs &a, const PrefillConv &pc, int chunk, void *ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  if (chunk != CH || a.S != DK || pc.D != 4) return GDN_ERR_UNSUPPORTED;
+  const int n_chunks = padded_chunks(a.n_tok);
+  if (ws_bytes < chunked_workspace_bytes(a.n_seq, a.n_tok, a.H, a.Hk, a.S, chunk))
+    return GDN_ERR_WORKSPACE;
+  const ConvSrc src{pc.x,     pc.x_tok, pc.x_seq, pc.w,    pc.hist, pc.h_seq, pc.alpha,
+                    pc.dt,    pc.a,     a.beta,   pc.eps,  a.n_tok, a.H,      a.Hk};
+  const HistOut ho{pc.x, pc.x_tok, pc.x_seq, pc.hist, pc.h_seq, a.n_tok, a.Hk, a.H / a.Hk};
+  return launch_two_phase(a, NoTab{}, src, ho, n_chunks, n_chunks * a.H * a.n_seq,
+                          static_cast<unsigned char *>(ws), stream);
 }
 
 }  // namespace gdn

@@ -69,6 +69,21 @@ size_t chunked_workspace_bytes(int n_seq, int n_tok, int H, int Hk, int S, int c
 int launch_recur_chunked(const RecurArgs &a, int chunk, void *ws, size_t ws_bytes,
                          hipStream_t stream);
 
+// The conv and gate inputs of the fused prefill (gdn_prefill_chunked): the
+// RecurArgs' q, k, v and g are unused, its beta, state, y and sizes are used.
+struct PrefillConv {
+  const float *x;
+  int64_t x_tok, x_seq;
+  const float *w;
+  float *hist;
+  int64_t h_seq;
+  const float *alpha, *dt, *a;
+  int D;
+  float eps;
+};
+int launch_prefill_chunked(const RecurArgs &a, const PrefillConv &pc, int chunk, void *ws,
+                           size_t ws_bytes, hipStream_t stream);
+
 // Sequence map of a chunked call, passed to the kernels by value.  NoTab: a
 // fixed-length batch (sequence s at s * seq_stride, n_tok positions each).
 // VarTab: a packed variable-length batch; sequence s holds token rows

@@ -314,6 +314,52 @@ size_t step_workspace_bytes(int n_seq, int Hk) {
   return (size_t)n_seq * (size_t)Hk * 2 * sizeof(int32_t);
 }
 
+int check_prefill(const float *state, int64_t st_seq, const float *x, int64_t x_tok,
+                  int64_t x_seq, const float *cw, const float *hist, int64_t h_seq,
+                  const float *alpha, const float *dt, const float *a, const float *beta,
+                  const float *y, int64_t y_tok, int64_t y_seq, int n_seq, int n_tok, int H,
+                  int Hk, int S, int D, int chunk, const void *ws, size_t ws_bytes,
+                  size_t ws_needed) {
+  if (n_seq < 1 || n_tok < 1 || H < 1 || Hk < 1 || H % Hk != 0) return GDN_ERR_SHAPE;
+  if (S < 32 || S % 32 != 0 || S > 256) return GDN_ERR_SHAPE;
+  if (D < 2 || D > 8) return GDN_ERR_SHAPE;
+  if (S != 128 || D != 4 || chunk != 64) return GDN_ERR_UNSUPPORTED;
+  if (st_seq < 0 || x_tok < 0 || x_seq < 0 || h_seq < 0 || y_tok < 0 || y_seq < 0)
+    return GDN_ERR_SHAPE;
+  if (!state || !x || !cw || !hist || !alpha || !dt || !a || !beta || !y) return GDN_ERR_NULL;
+  const int64_t C = (2 * (int64_t)Hk + H) * S;
+  if (C > INT32_MAX / 8) return GDN_ERR_SHAPE;
+  if (n_tok > 1 && x_tok < C) return GDN_ERR_SHAPE;
+  const int64_t hlen = C * (D - 1), row = (int64_t)H * S, st_len = (int64_t)S * S * H;
+  if (!rows_disjoint(n_seq, st_seq, 1, 0, st_len)) return GDN_ERR_SHAPE;
+  if (!rows_disjoint(n_seq, h_seq, 1, 0, hlen)) return GDN_ERR_SHAPE;
+  if (!rows_disjoint(n_seq, y_seq, n_tok, y_tok, row)) return GDN_ERR_SHAPE;
+  // 16-byte accesses of the state, x, the taps, the history and y
+  if (!aligned(state, 16) || !aligned(x, 16) || !aligned(cw, 16) || !aligned(hist, 16) ||
+      !aligned(y, 16) || st_seq % 4 || x_tok % 4 || x_seq % 4 || h_seq % 4 || y_tok % 4 ||
+      y_seq % 4)
+    return GDN_ERR_SHAPE;
+  if (!ws || ws_bytes < ws_needed || !aligned(ws, 256)) return GDN_ERR_WORKSPACE;
+  const int64_t rows = (int64_t)n_seq * n_tok * H;
+  const Span in[] = {span_of(x, n_seq, x_seq, n_tok, x_tok, C),
+                     span_of(cw, 1, 0, 1, 0, C * D),
+                     span_of(alpha, 1, 0, 1, 0, rows),
+                     span_of(beta, 1, 0, 1, 0, rows),
+                     span_of(dt, 1, 0, 1, 0, H),
+                     span_of(a, 1, 0, 1, 0, H)};
+  const Span outs[] = {span_of(state, n_seq, st_seq, 1, 0, st_len),
+                       span_of(hist, n_seq, h_seq, 1, 0, hlen),
+                       span_of(y, n_seq, y_seq, n_tok, y_tok, row),
+                       Span{(uintptr_t)ws, (uintptr_t)ws + ws_bytes}};
+  for (const Span &o : outs) {
+    for (const Span &i : in)
+      if (overlap(o, i)) return GDN_ERR_ALIAS;
+    for (const Span &o2 : outs)
+      if (&o2 != &o && overlap(o, o2)) return GDN_ERR_ALIAS;
+  }
+  return GDN_OK;
+}
+
 int check_step(const float *state, int64_t st_seq, const float *x, int64_t x_tok, int64_t x_seq,
                const float *cw, const float *hist, int64_t h_seq, const float *csnap,
                int64_t cs_tok, int64_t cs_seq, const float *alpha, const float *dt,

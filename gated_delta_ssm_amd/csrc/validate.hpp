@@ -51,6 +51,15 @@ int check_fused(const float *state, int64_t st_seq, const float *q, const float 
                 int64_t y_seq, const float *snap, int64_t sn_seq, int n_seq, int n_tok, int H,
                 int Hk, int S);
 
+// The fused prefill: conv input x with (2 Hk + H) S channels, conv taps and
+// history, alpha / dt / a of the gate, beta, the state and y.
+int check_prefill(const float *state, int64_t st_seq, const float *x, int64_t x_tok,
+                  int64_t x_seq, const float *cw, const float *hist, int64_t h_seq,
+                  const float *alpha, const float *dt, const float *a, const float *beta,
+                  const float *y, int64_t y_tok, int64_t y_seq, int n_seq, int n_tok, int H,
+                  int Hk, int S, int D, int chunk, const void *ws, size_t ws_bytes,
+                  size_t ws_needed);
+
 size_t step_workspace_bytes(int n_seq, int Hk);
 
 int check_step(const float *state, int64_t st_seq, const float *x, int64_t x_tok, int64_t x_seq,

@@ -199,6 +199,59 @@ int gdn_recurrence_chunked(float *state, int64_t state_seq_stride, const float *
                            int n_qk_heads, int S, float scale, int chunk, void *workspace,
                            size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Workspace bytes gdn_prefill_chunked needs (0 if the sizes are invalid or
+ * unsupported); the same amount as gdn_recurrence_chunked at S = 128.
+ */
+size_t gdn_prefill_chunked_workspace_bytes(int n_seq, int n_tok, int n_v_heads, int n_qk_heads,
+                                           int S, int chunk);
+
+/*
+ * The prefill layer core up to the norm in two launches: decay gate (as
+ * gdn_decay_gate) and depthwise conv1d + SiLU + per-head L2 (as
+ * gdn_conv1d_silu_l2norm) computed inside the chunked recurrence's first
+ * phase, then the chunked recurrence (as gdn_recurrence_chunked).  [AT]
+ * conv1d_update_prefill (the conv of every position depends on inputs only,
+ * so it runs token-parallel with the per-position arithmetic unchanged) and
+ * conv1d_update_l2norm (fusing neighbouring ops saves launches and memory
+ * passes); [AT] "Mamba-2 SSD chunked prefill scan" comment; [FM] "Causal
+ * depthwise conv1d + SiLU" and "Decay gate" sections.  The conv outputs and
+ * g never go to device memory.
+ *
+ * The conv row of a position carries conv_dim = (2*n_qk_heads + n_v_heads)*S
+ * channels: q heads at [0, Hk*S), k heads at [Hk*S, 2*Hk*S), v heads at
+ * [2*Hk*S, conv_dim), i.e. qk_channels = 2*Hk*S and head_dim = S for the
+ * conv.
+ *   x            element x[s][t][c] at x + s*x_seq_stride + t*x_tok_stride + c (in)
+ *   conv_w       [conv_dim][d_conv], tap d_conv-1 meets the newest input  (in)
+ *   conv_state   [s][conv_dim][d_conv-1] at conv_state + s*conv_state_seq_stride,
+ *                oldest tap first, updated in place to the window after the
+ *                last position                                          (in/out)
+ *   alpha        [n_seq][n_tok][n_v_heads] dense; dt, a [n_v_heads]: the
+ *                decay gate's inputs, g = a*softplus(alpha + dt)         (in)
+ *   beta         [n_seq][n_tok][n_v_heads] dense, already sigmoid'd    (in)
+ *   state, y     as gdn_recurrence_chunked                    (in/out, out)
+ *   workspace    at least gdn_prefill_chunked_workspace_bytes(...) bytes,
+ *                256-byte aligned, under gdn_recurrence_chunked's rules
+ * Supported: S = 128, d_conv = 4, chunk = 64 (other valid sizes return
+ * GDN_ERR_UNSUPPORTED); x, conv_w, conv_state, the state and y 16-byte aligned
+ * with strides that are multiples of 4; n_tok >= 1.  The preconditions of
+ * gdn_recurrence_chunked apply to the conv outputs and g (the L2 step gives
+ * unit-length q and k; a <= 0 gives g <= 0).
+ * Results (y, state and conv_state) are bit-identical to gdn_decay_gate into
+ * g, gdn_conv1d_silu_l2norm into a buffer, then gdn_recurrence_chunked on the
+ * buffer's q, k, v channels.  No output may overlap an input, another output
+ * or the workspace.
+ */
+int gdn_prefill_chunked(float *state, int64_t state_seq_stride, const float *x,
+                        int64_t x_tok_stride, int64_t x_seq_stride, const float *conv_w,
+                        float *conv_state, int64_t conv_state_seq_stride, const float *alpha,
+                        const float *dt, const float *a, const float *beta, float *y,
+                        int64_t y_tok_stride, int64_t y_seq_stride, int n_seq, int n_tok,
+                        int n_v_heads, int n_qk_heads, int S, int d_conv, float scale,
+                        float l2_eps, int chunk, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
 /* Most sequences one gdn_recurrence_chunked_varlen call takes. */
 #define GDN_VARLEN_MAX_SEQ 256
 

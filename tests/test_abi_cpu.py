@@ -318,6 +318,48 @@ def test_step_noalloc_validation():
     assert step_noalloc(hist=FAKE + 4 * (1 << 20) + 64) == ERR_ALIAS
 
 
+def prefill(**kw):
+    """gdn_prefill_chunked on fake addresses, valid except for what kw changes
+    (every case below fails a host check, so nothing is launched)."""
+    MB = 1 << 20
+    S, H, Hk, T = 128, 4, 2, 100
+    C = (2 * Hk + H) * S
+    a = dict(state=FAKE, sts=H * S * S, x=FAKE + 4 * MB, xt=C, xs=T * C, cw=FAKE + 8 * MB,
+             hist=FAKE + 9 * MB, hs=3 * C, alpha=FAKE + 10 * MB, dt=FAKE + 11 * MB,
+             a=FAKE + 12 * MB, beta=FAKE + 13 * MB, y=FAKE + 16 * MB, yt=H * S, ys=T * H * S,
+             n=1, T=T, H=H, Hk=Hk, S=S, D=4, chunk=64, ws=FAKE + 64 * MB, wsb=None)
+    a.update(kw)
+    need = L.gdn_prefill_chunked_workspace_bytes(a["n"], a["T"], a["H"], a["Hk"], 128, 64)
+    return L.gdn_prefill_chunked(
+        a["state"], a["sts"], a["x"], a["xt"], a["xs"], a["cw"], a["hist"], a["hs"], a["alpha"],
+        a["dt"], a["a"], a["beta"], a["y"], a["yt"], a["ys"], a["n"], a["T"], a["H"], a["Hk"],
+        a["S"], a["D"], 0.088, 1e-6, a["chunk"], a["ws"], need if a["wsb"] is None else a["wsb"],
+        None)
+
+
+def test_prefill_validation_and_workspace_query():
+    MB = 1 << 20
+    assert (L.gdn_prefill_chunked_workspace_bytes(1, 4096, 32, 16, 128, 64) ==
+            L.gdn_recurrence_chunked_workspace_bytes(1, 4096, 32, 16, 128, 64) > 0)
+    assert L.gdn_prefill_chunked_workspace_bytes(1, 4096, 32, 16, 64, 64) == 0
+    assert L.gdn_prefill_chunked_workspace_bytes(1, 4096, 32, 16, 128, 32) == 0
+    assert prefill(D=3) == ERR_UNSUP and prefill(chunk=32) == ERR_UNSUP
+    assert prefill(S=64, sts=4 * 64 * 64) == ERR_UNSUP
+    assert prefill(D=9) == ERR_SHAPE and prefill(T=0) == ERR_SHAPE and prefill(Hk=3) == ERR_SHAPE
+    for k in ("state", "x", "cw", "hist", "alpha", "dt", "a", "beta", "y"):
+        assert prefill(**{k: None}) == ERR_NULL, k
+    assert prefill(ws=None) == ERR_WS and prefill(wsb=16) == ERR_WS
+    assert prefill(ws=FAKE + 64 * MB + 16) == ERR_WS                 # not 256-byte aligned
+    assert prefill(x=FAKE + 4 * MB + 8) == ERR_SHAPE                 # x not 16-byte aligned
+    assert prefill(xt=1026) == ERR_SHAPE                             # stride not a multiple of 4
+    assert prefill(xt=512, xs=512 * 100) == ERR_SHAPE                # rows shorter than conv_dim
+    assert prefill(n=2, hs=100) == ERR_SHAPE                         # histories overlap
+    assert prefill(hist=FAKE + 4 * MB + 64) == ERR_ALIAS             # history over x
+    assert prefill(y=FAKE + 12 * MB) == ERR_ALIAS                    # y over a
+    assert prefill(ws=FAKE + 4 * MB) == ERR_ALIAS                    # workspace over x
+    assert prefill(y=FAKE + 64 * MB) == ERR_ALIAS                    # y over the workspace
+
+
 def test_stream_copy_validation():
     assert L.gdn_stream_copy(FAKE, FAKE + (1 << 20), 0, None) == OK            # nothing launched
     assert L.gdn_stream_copy(None, FAKE, 64, None) == ERR_NULL

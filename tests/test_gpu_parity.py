@@ -951,6 +951,81 @@ def test_chunked_deterministic():
     assert bits_equal(ya, yb) and bits_equal(sa, sb)
 
 
+# ------------------------------------------------------------------------------- fused prefill
+
+def prefill_two_ways(inp):
+    """The prefill core as one gdn_prefill_chunked call and as gdn_decay_gate +
+    gdn_conv1d_silu_l2norm into a buffer + gdn_recurrence_chunked on its q, k,
+    v channels; returns both results (state, conv history, y)."""
+    wl = inp["wl"]
+    n, T, H, Hk, S, C = wl.n_seq, wl.n_tok, wl.H, wl.Hk, wl.S, wl.conv_dim
+    nan = float("nan")
+    d = {k: on_dev(inp[k]) for k in ("alpha", "dt", "a", "beta", "x", "conv_w")}
+    x = d["x"][:, :, :C]
+
+    def outs():
+        return dict(state=on_dev(inp["state"]).clone(), hist=on_dev(inp["conv_hist"]).clone(),
+                    y=torch.full((n, T, H, S), nan, device=DEV))
+
+    r = outs()
+    g = torch.full((n * T, H), nan, device=DEV)
+    gdn().gdn_decay_gate(d["alpha"], d["dt"], d["a"], g)
+    cout = torch.full((n, T, C), nan, device=DEV)
+    gdn().gdn_conv1d_silu_l2norm(x, d["conv_w"], r["hist"], cout, qk_channels=2 * Hk * S,
+                                 head_dim=S, l2_eps=wl.l2_eps)
+    q = cout[:, :, :Hk * S].unflatten(-1, (Hk, S))
+    k = cout[:, :, Hk * S:2 * Hk * S].unflatten(-1, (Hk, S))
+    v = cout[:, :, 2 * Hk * S:].unflatten(-1, (H, S))
+    gdn().gdn_recurrence_chunked(r["state"], q, k, v, g.view(n, T, H), d["beta"], r["y"],
+                                 scale=wl.scale)
+    f = outs()
+    gdn().gdn_prefill_chunked(f["state"], x, d["conv_w"], f["hist"], d["alpha"].view(n, T, H),
+                              d["dt"], d["a"], d["beta"], f["y"], scale=wl.scale,
+                              l2_eps=wl.l2_eps)
+    return r, f
+
+
+PREFILL_CASES = [("prefill", None),                                     # 4096 x 32 / 16 heads
+                 ("tiny", step_shape(128, 8, 4, 130, 2)),               # ragged, two sequences
+                 ("tiny", step_shape(128, 4, 2, 1, 1)),                 # one position: history
+                 ("tiny", step_shape(128, 4, 4, 2, 2)),                 # two positions, G = 1
+                 ("tiny", step_shape(128, 6, 3, 67, 3, x_pad=8)),       # padded rows
+                 ("tiny", step_shape(128, 4, 1, 64, 1)),                # one chunk, G = 4
+                 ("tiny", step_shape(128, 24, 8, 200, 2))]              # the paired scan's grid
+
+
+@pytest.mark.parametrize("name,shape", PREFILL_CASES)
+def test_prefill_fused_bit_identical_to_three_calls(name, shape):
+    inp = inputs(name) if shape is None else make_inputs(name, seed=47, **shape)
+    wl = inp["wl"]
+    log_case("prefill_fused", n_seq=wl.n_seq, n_tok=wl.n_tok, H=wl.H, Hk=wl.Hk)
+    r, f = prefill_two_ways(inp)
+    for key in r:
+        assert bits_equal(f[key], r[key]), key
+
+
+def test_prefill_fused_against_oracle_chain():
+    # conv -> gate -> sequential recurrence in the fp64 oracle, ragged, two
+    # sequences with their own histories and states
+    inp = make_inputs("tiny", seed=53, **step_shape(128, 4, 2, 100, 2))
+    wl = inp["wl"]
+    n, T, H, Hk, S, C = wl.n_seq, wl.n_tok, wl.H, wl.Hk, wl.S, wl.conv_dim
+    log_case("prefill_fused_oracle", n_seq=n, n_tok=T)
+    _, f = prefill_two_ways(inp)
+    o_r, hist_r, _ = oracle.conv1d_silu_l2norm(inp["x"][:, :, :C], inp["conv_w"],
+                                               inp["conv_hist"], wl.qk_channels, wl.head_dim,
+                                               wl.l2_eps)
+    q_r = o_r[:, :, :Hk * S].reshape(n, T, Hk, S)
+    k_r = o_r[:, :, Hk * S:2 * Hk * S].reshape(n, T, Hk, S)
+    v_r = o_r[:, :, 2 * Hk * S:].reshape(n, T, H, S)
+    g_r = oracle.decay_gate(inp["alpha"], inp["dt"], inp["a"]).reshape(n, T, H)
+    y_r, s_r, _ = oracle.recurrence_seq(inp["state"], q_r, k_r, v_r, g_r, inp["beta"], wl.scale)
+    assert rel(f["hist"], hist_r) == 0.0     # the history only holds raw inputs
+    ey, es = rel(f["y"], y_r), rel(f["state"], s_r)
+    print(f"[prefill fused] rel err y {ey:.3e} state {es:.3e}", flush=True)
+    assert ey < 2e-3 and es < 2e-3
+
+
 # ------------------------------------------------------------------------------------- Mamba-2 SSD
 
 def ssd_oracle(inp):
