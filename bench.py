@@ -14,8 +14,9 @@ state cannot stay in the 256 MB MALL between steps ("cold"); a same-pool
 
 value = decode state GB/s of the whole step: (state bytes read + written) /
 step time.  The prefill half of the metric (tokens/s of the 4096-token prompt
-through gate, token-parallel conv, chunked recurrence and norm) is timed in the
-same run and reported under "prefill".
+through gate, conv, chunked recurrence and norm) is timed in the same run and
+reported under "prefill": as gdn_prefill_chunked (gate and conv inside the
+chunked recurrence's first phase) + gdn_gated_rmsnorm, and as four launches.
 
 Prints ONE JSON line.  --gpus N > 1 is refused: this build runs on one GPU.
 """
@@ -472,6 +473,12 @@ def main():
             marks[4].record(stream)
             ev.setdefault("marks", []).append(marks)
 
+    def prefill_fused_launches():
+        gdn.gdn_prefill_chunked(pst, pc["x"], pc["conv_w"], phist, pc["alpha"].view(1, T, PH),
+                                pc["dt"], pc["a"], pc["beta"], py, scale=pw.scale,
+                                l2_eps=pw.l2_eps, workspace=ws)
+        gdn.gdn_gated_rmsnorm(py.view(T, PH, PS), pc["norm_w"], pc["z"], pn, eps=pw.norm_eps)
+
     def prefill_launches():
         gdn.gdn_decay_gate(pc["alpha"], pc["dt"], pc["a"], pg)
         gdn.gdn_conv1d_silu_l2norm(pc["x"], pc["conv_w"], phist, pout,
@@ -496,6 +503,24 @@ def main():
         e1.record(stream)
         e1.synchronize()
         pass_ms = e0.elapsed_time(e1) / args.prefill_iters
+        # the same pass as gdn_prefill_chunked + norm (two launches)
+        for _ in range(2):
+            prefill_fused_launches()
+        e0.record(stream)
+        for _ in range(args.prefill_iters):
+            prefill_fused_launches()
+        e1.record(stream)
+        e1.synchronize()
+        fused_pass_ms = e0.elapsed_time(e1) / args.prefill_iters
+        # the fused call alone (gate + conv + chunked recurrence)
+        e0.record(stream)
+        for _ in range(args.prefill_iters):
+            gdn.gdn_prefill_chunked(pst, pc["x"], pc["conv_w"], phist, pc["alpha"].view(1, T, PH),
+                                    pc["dt"], pc["a"], pc["beta"], py, scale=pw.scale,
+                                    l2_eps=pw.l2_eps, workspace=ws)
+        e1.record(stream)
+        e1.synchronize()
+        fused_call_ms = e0.elapsed_time(e1) / args.prefill_iters
         # the chunked call alone, back to back between one event pair
         c0 = torch.cuda.Event(enable_timing=True)
         c1 = torch.cuda.Event(enable_timing=True)
@@ -517,8 +542,18 @@ def main():
         prefill = {
             "workload": "prefill: 1 seq x 4096 tokens, 32 value / 16 q-k heads, 128x128 state, "
                         "conv 8192 ch, chunk 64",
-            "tokens_per_s": T / (pass_ms * 1e-3),
-            "pass_ms": pass_ms,
+            "tokens_per_s": T / (min(pass_ms, fused_pass_ms) * 1e-3),
+            "pass_ms": min(pass_ms, fused_pass_ms),
+            "pass_note": "the faster of the two forms of the layer pass below",
+            "fused_pass_ms": fused_pass_ms,
+            "fused_pass_tokens_per_s": T / (fused_pass_ms * 1e-3),
+            "fused_pass_note": f"{args.prefill_iters} passes of gdn_prefill_chunked + "
+                               "gdn_gated_rmsnorm back to back between one event pair",
+            "fused_call_ms": fused_call_ms,
+            "fused_call_note": "gdn_prefill_chunked alone: decay gate, conv1d + SiLU + L2 and "
+                               "the chunked recurrence in two launches",
+            "four_launch_pass_ms": pass_ms,
+            "four_launch_pass_tokens_per_s": T / (pass_ms * 1e-3),
             "recurrence_tokens_per_s": T / (seg[2] * 1e-3),
             "chunked_call_ms": chunk_call_ms,
             "chunked_call_tokens_per_s": T / (chunk_call_ms * 1e-3),
