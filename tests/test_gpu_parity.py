@@ -1004,6 +1004,50 @@ def test_prefill_fused_bit_identical_to_three_calls(name, shape):
         assert bits_equal(f[key], r[key]), key
 
 
+def test_prefill_fused_workspace_contents_and_graph_replay():
+    # a NaN-filled workspace gives the zeroed workspace's bits; the two launches
+    # captured in a HIP graph and replayed three times (eager work between the
+    # replays) give the eager call's bits every time
+    inp = make_inputs("tiny", seed=59, **step_shape(128, 4, 2, 150, 1))
+    wl = inp["wl"]
+    n, T, H, Hk, S, C = wl.n_seq, wl.n_tok, wl.H, wl.Hk, wl.S, wl.conv_dim
+    log_case("prefill_fused_ws_graph", n_tok=T)
+    d = {k: on_dev(inp[k]) for k in ("alpha", "dt", "a", "beta", "x", "conv_w")}
+    x, a3 = d["x"][:, :, :C], d["alpha"].view(n, T, H)
+    nb = gdn().gdn_prefill_chunked_workspace_bytes(n, T, H, Hk, S)
+
+    def run(ws, st, hist, y):
+        gdn().gdn_prefill_chunked(st, x, d["conv_w"], hist, a3, d["dt"], d["a"], d["beta"], y,
+                                  scale=wl.scale, l2_eps=wl.l2_eps, workspace=ws)
+
+    def fresh():
+        return (on_dev(inp["state"]).clone(), on_dev(inp["conv_hist"]).clone(),
+                torch.full((n, T, H, S), float("nan"), device=DEV))
+
+    ref = fresh()
+    run(torch.zeros(nb, dtype=torch.uint8, device=DEV), *ref)
+    ws = torch.full((nb,), 255, dtype=torch.uint8, device=DEV)   # fp32 NaN patterns
+    got = fresh()
+    run(ws, *got)
+    for a, b in zip(got, ref):
+        assert bits_equal(a, b)
+    st, hist, y = fresh()
+    st0, hist0 = st.clone(), hist.clone()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(ws, st, hist, y)
+    for _ in range(3):
+        st.copy_(st0)
+        hist.copy_(hist0)
+        y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((st, hist, y), ref):
+            assert bits_equal(a, b)
+
+
 def test_prefill_fused_against_oracle_chain():
     # conv -> gate -> sequential recurrence in the fp64 oracle, ragged, two
     # sequences with their own histories and states
