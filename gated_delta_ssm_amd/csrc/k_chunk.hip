@@ -337,13 +337,18 @@ struct PrepItem {
   int64_t grow;   // g / beta row of tb
   size_t slot;    // workspace chunk slot
 };
-// Fixed-length batch: item u = (sequence, head, chunk), chunks fastest.
+// Fixed-length batch: item u = (chunk, sequence, head), heads fastest, the
+// chunks from the last to the first.  Phase B reads chunk 0 of every head
+// first and the last chunk last; the workspace outgrows the last-level cache
+// (MALL) at long prompts, and written in the reverse of its read order, what
+// the cache still holds when phase B starts is what phase B reads first.
 __device__ __forceinline__ PrepItem prep_item(int u, int n_chunks, int H, int Hk, int n_tok,
-                                              const NoTab &) {
+                                              const NoTab &, int n_items) {
   PrepItem it;
-  const int c = u % n_chunks;
-  it.h = (u / n_chunks) % H;
-  it.s = u / (n_chunks * H);
+  const int nsh = n_items / n_chunks;   // sequences x heads
+  const int c = n_chunks - 1 - u / nsh;
+  it.h = (u % nsh) % H;
+  it.s = (u % nsh) / H;
   it.hk = it.h / (H / Hk);
   const int t0 = c * CH;
   it.n = max(0, min(CH, n_tok - t0));
@@ -357,7 +362,7 @@ __device__ __forceinline__ PrepItem prep_item(int u, int n_chunks, int H, int Hk
 // Variable-length batch: item u = (head, packed chunk gc), gc fastest; the
 // sequence holding gc is found by binary search over the chunk offsets.
 __device__ __forceinline__ PrepItem prep_item(int u, int n_chunks, int H, int Hk, int,
-                                              const VarTab &tab) {
+                                              const VarTab &tab, int) {
   PrepItem it;
   const int gc = u % n_chunks;
   it.h = u / n_chunks;
@@ -406,9 +411,12 @@ __device__ __forceinline__ float bf16_to_f32(unsigned b) { return __builtin_bit_
 // 64 + 4l .. 64 + 4l+3): each load instruction then reads 256 contiguous
 // bytes per row, and the quads are the 4-channel groups of the conv
 // kernels' lanes.
-// 4 consecutive elements as a float4
+// 4 consecutive elements as a float4.  fp32 inputs are read once per item
+// (q and k once per value head of their group) and loaded non-temporally,
+// so that they do not displace the workspace from the last-level cache.
 __device__ __forceinline__ float4 load4f(const float *p) {
-  return *reinterpret_cast<const float4 *>(p);
+  const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+  return make_float4(v[0], v[1], v[2], v[3]);
 }
 __device__ __forceinline__ float4 load4f(const u16 *p) {
   const uint2 u = *reinterpret_cast<const uint2 *>(p);
@@ -705,7 +713,7 @@ __global__ __launch_bounds__(512) void k_chunk_prep(const SRC src, unsigned char
       zp[e] = make_uint4(0, 0, 0, 0);
   }
   // the grid never exceeds n_items, so every workgroup has a first item
-  PrepItem it = prep_item(blockIdx.x, n_chunks, H, Hk, n_tok, tab);
+  PrepItem it = prep_item(blockIdx.x, n_chunks, H, Hk, n_tok, tab, n_items);
   typename SRC::Regs pre;
   if ((threadIdx.x >> 6) == 7) src.load_gate(it, threadIdx.x & 63, pre);
   src.template load_rows<0>(it, threadIdx.x, pre);
@@ -727,7 +735,7 @@ __global__ __launch_bounds__(512) void k_chunk_prep(const SRC src, unsigned char
   // the item after this one (this one again on the last pass: its loads are
   // then redundant but in bounds, and no load sits behind a branch)
   const PrepItem nx = prep_item(u + gridDim.x < n_items ? u + gridDim.x : u, n_chunks, H, Hk,
-                                n_tok, tab);
+                                n_tok, tab, n_items);
   const int n = it.n;
   unsigned char *wc = ws + it.slot * WS_CHUNK;
 
@@ -1249,10 +1257,11 @@ __device__ __forceinline__ void scan_chunk(const ChunkOps<VT> &o, float (&bound)
       const f32x4 u = {ad.x - p[0], ad.y - p[1], ad.z - p[2], ad.w - p[3]};
       store4_split_h(suh + t * SP + 16 * d + 4 * kg, sul + t * SP + 16 * d + 4 * kg, u,
                      sc[d].sU);
-    } else if (t < n) {
-      *reinterpret_cast<float4 *>(yc + (int64_t)t * y_tok + 16 * d + 4 * kg) =
-          make_float4(scale * (p[0] + ad.x), scale * (p[1] + ad.y), scale * (p[2] + ad.z),
-                      scale * (p[3] + ad.w));
+    } else if (t < n) {   // y is not read again here: a non-temporal store
+      __builtin_nontemporal_store(
+          f32x4{scale * (p[0] + ad.x), scale * (p[1] + ad.y), scale * (p[2] + ad.z),
+                scale * (p[3] + ad.w)},
+          reinterpret_cast<f32x4 *>(yc + (int64_t)t * y_tok + 16 * d + 4 * kg));
     }
   }
   __syncthreads();
@@ -1439,9 +1448,10 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_chunk_scan_pair(
       const f32x4 u = {add.x - acc[0], add.y - acc[1], add.z - acc[2], add.w - acc[3]};
       store4_split_h(u_hi + t * SPB + 4 * kg, u_lo + t * SPB + 4 * kg, u, sc.sU);
     } else if (t < min(CH, hc.len - c * CH)) {
-      *reinterpret_cast<float4 *>(yh + (int64_t)(c * CH + t) * y_tok + 4 * kg) =
-          make_float4(scale * (acc[0] + add.x), scale * (acc[1] + add.y),
-                      scale * (acc[2] + add.z), scale * (acc[3] + add.w));
+      __builtin_nontemporal_store(
+          f32x4{scale * (acc[0] + add.x), scale * (acc[1] + add.y), scale * (acc[2] + add.z),
+                scale * (acc[3] + add.w)},
+          reinterpret_cast<f32x4 *>(yh + (int64_t)(c * CH + t) * y_tok + 4 * kg));
     }
     __syncthreads();   // U barrier: K' and the U tiles are in LDS, W and Q' are read
     put_wq();          // W, Q' of chunk c + 1
