@@ -227,7 +227,7 @@ size_t gdn_recurrence_chunked_varlen_workspace_bytes(int n_seq, int total_tok, i
       n_qk_heads < 1 || n_v_heads % n_qk_heads)
     return 0;
   if ((S != 32 && S != 64 && S != 128) || chunk != 64) return 0;
-  return gdn::chunked_varlen_workspace_bytes(n_seq, total_tok, n_v_heads, S);
+  return gdn::chunked_varlen_workspace_bytes(n_seq, total_tok, n_v_heads, n_qk_heads, S);
 }
 
 int gdn_recurrence_chunked_varlen(float *state, int64_t state_seq_stride, const void *q,

@@ -12,15 +12,20 @@
 // g inside the chunk:
 //   A  = strictly_lower(beta_t e^{G_t-G_s} k_t.k_s),  T = (I + A)^{-1}
 //   W  = T diag(beta e^G) K           Ut = T diag(beta) V
-//   L  = lower(e^{G_t-G_s})  (diagonal included)
-//   Q' = diag(e^G) Q - (L o Q K^T) W  Oi = (L o Q K^T) Ut
-//   U  = Ut - W S0,   y = scale (Q' S0 + Oi),   S = e^{G_n} S0 + K'^T U,
-//   K' = diag(e^{G_n-G}) K.
-// Only the last three lines depend on S0, so the work splits in two kernels:
+//   M  = lower(e^{G_t-G_s}) o Q K^T  (diagonal included)
+//   U  = Ut - W S0
+//   y  = scale (diag(e^G) Q S0 + M U)
+//   S  = e^{G_n} S0 + K^T diag(e^{G_n-G}) U.
+// (U is the chunk's block of sequential deltas beta_t (v_t - S_{t-1}^T k_t);
+// y_t reads the state after position t, whose part from inside the chunk is
+// the sum over s <= t of e^{G_t-G_s} k_s U_s^T.)  Only the last three lines
+// depend on S0, so the work splits in two kernels:
 //
 //   k_chunk_prep (phase A) -- every (sequence, head, chunk) independently:
 //     everything that does not depend on S0, written to a workspace in the
-//     exact register layout the scan loads.  Persistent: one workgroup per CU
+//     exact register layout the scan loads: W, M, Ut per value head; Q and K
+//     per query/key head, written once and read by every value head of the
+//     group.  Persistent: one workgroup per CU
 //     walks its chunks, loading the next chunk while computing this one.  Its
 //     K, Q, V and g come either as given (gdn_recurrence_chunked) or from the
 //     layer's conv input and gate inputs (gdn_prefill_chunked: the decay gate
@@ -36,10 +41,10 @@
 // Precision: phase A's contractions run on MFMA v_mfma_f32_16x16x32_bf16 with
 // each fp32 operand split into bf16 hi + lo, accumulating hi*hi + hi*lo +
 // lo*hi in fp32 (relative error ~2^-16 per product instead of bf16's 2^-8).
-// Phase B's operands W, Q', K' are stored as fp16 (their entries are bounded
-// by 1, see the workspace notes); its products take them as they are on
-// v_mfma_f32_16x16x32_f16 against the fp32 state or U tile split into fp16
-// hi + lo (hi*W + lo*W: the split keeps 22 significant bits), each tile first
+// Phase B's operands W, Q, M and K are stored as fp16 (their entries are
+// bounded by 1, see the workspace notes; K as hi + lo); its products take them
+// as they are on v_mfma_f32_16x16x32_f16 against the fp32 state or U tile
+// split into fp16 hi + lo (hi*W + lo*W: the split keeps 22 significant bits), each tile first
 // scaled by a power of two chosen from a running bound on its norm so that
 // the split cannot overflow fp16.  The triangular inverse, the gate cumsum,
 // every exponential and the state carry are fp32.  Exponentials are only
@@ -70,45 +75,59 @@ constexpr int NBLK = 16;         // value columns per value tile of the scan
 constexpr int NVB = DV / NBLK;   // value tiles per head
 
 // ----------------------------------------------------------------------------- workspace
-// Per (sequence, head, chunk), all offsets in bytes, each region 256-aligned.
-//   W, Q'  : fragment (token tile m, key k-step ks) = 64 lanes x 16 B (8 fp16),
+// Two regions.  Value slots, one per (sequence, value head, chunk), all
+// offsets in bytes, each region 256-aligned:
+//   W      : fragment (token tile m, key k-step ks) = 64 lanes x 16 B (8 fp16),
 //            lane (kg, l16) holding row 16m + l16, keys pi(32ks, kg)
-//   K'^T   : fragment (key tile m, token k-step ks), lane holding key row
-//            16m + l16, tokens pi(32ks, kg)
-//   Ut, Oi : fp32 accumulator tiles [value tile][token tile][lane][4], lane
+//   M^T    : fragment (token tile m, token k-step ks), lane holding row
+//            16m + l16 of M, positions pi(32ks, kg); hi and lo planes
+//   Ut     : fp32 accumulator tiles [value tile][token tile][lane][4], lane
 //            (kg, l16) holding values 16d + 4kg + r of token 16m + l16
+//   header : e^{G_n}, b, a, 0; e^{G_t} (64 floats); e^{G_n - G_t} (64 floats)
+// Key slots, one per (sequence, query/key head, chunk), after all value slots:
+//   Q      : fragment (token tile m, key k-step ks) as W
+//   K^T    : fragment (key tile m, token k-step ks), lane holding key row
+//            16m + l16, tokens pi(32ks, kg); hi and lo planes
 // These are the exact register images the scan loads, so each of its wave
-// loads is 1 KiB (or 1 KiB of float4) of consecutive bytes.
+// loads is 1 KiB (or 1 KiB of float4) of consecutive bytes.  Q and K depend on
+// the query/key head only: the first value head of each group writes them and
+// every value head of the group reads them.
 //
-// W, Q' and K' are stored as fp16 (relative rounding 2^-11), half the bytes
-// of a bf16 hi + lo pair: the scan is bound by the operand bytes each CU
-// pulls from L2 per chunk.  They are small: with beta_t |k_t|^2 <= 2 every
-// factor I - beta_t k_t k_t^T has spectral norm <= 1, and with g <= 0
-// row t of W is beta_t e^{G_t} M^T k_t and row t of Q' is e^{G_t} M'^T q_t
-// for products M, M' of such factors, so |W[t][i]| <= beta_t |k_t| and
-// |Q'[t][i]| <= |q_t|; |K'[t][i]| <= |k_t[i]|.  For unit-length keys and
+// W, Q, M and K are stored as fp16 (relative rounding 2^-11): the scan is
+// bound by the operand bytes each CU pulls from L2 per chunk.  They are small:
+// with beta_t |k_t|^2 <= 2 every factor I - beta_t k_t k_t^T has spectral
+// norm <= 1, and with g <= 0 row t of W is beta_t e^{G_t} P^T k_t for a
+// product P of such factors, so |W[t][i]| <= beta_t |k_t|; |Q[t][i]| <= |q_t|,
+// |K[t][i]| <= |k_t| and |M[t][s]| <= |q_t| |k_s|.  For unit-length keys and
 // queries every entry is at most 2 in magnitude.
-// K' is kept as two fp16 planes, hi and lo = fp16(K' - hi) (22 significant
-// bits): the state update K'^T U sums 64 rank-one terms that can cancel
-// (repeated or low-rank keys with beta near 1 and no decay make the terms of
-// size |v| while their sum stays of size |v|), so single fp16 rounding of K'
-// would show in the state at ~2^-11 * sqrt(64) relative; W and Q' meet no
-// such cancellation and stay single fp16.
-// The header (WS_G) holds e^{G_n}, b = sum_t beta_t |k_t| |v_t| and
-// a = max_t beta_t |k_t| over the chunk's positions: a chunk raises the
-// state's spectral norm by at most b (each position adds at most
-// beta_t |k_t| |v_t|), and every entry of U (row t is the sequential delta
-// beta_t (v_t - (decayed S_{t-1})^T k_t)) is at most b + a * (the state's
-// bound), which is how the scan picks its fp16 scaling without a reduction.
+// K and M are kept as two fp16 planes, hi and lo = fp16(x - hi) (22
+// significant bits): the state update K^T diag(e^{G_n-G}) U and y's M U sum
+// 64 terms that can cancel (repeated or low-rank keys with beta near 1 and no
+// decay make the terms of size |v| while their sum stays of size |v|), so
+// single fp16 rounding of K or M would show in the state or in y at
+// ~2^-11 * sqrt(64) relative; W and Q meet no such cancellation (they multiply
+// the state, whose rows do not cancel this way) and stay single fp16.
+// The header's b = sum_t beta_t |k_t| |v_t| and a = max_t beta_t |k_t| over
+// the chunk's positions: a chunk raises the state's spectral norm by at most
+// b (each position adds at most beta_t |k_t| |v_t|), and every entry of U
+// (row t is the sequential delta beta_t (v_t - (decayed S_{t-1})^T k_t)) is
+// at most b + a * (the state's bound), which is how the scan picks its fp16
+// scaling without a reduction.
 constexpr size_t WS_PLANE = (size_t)CH * DK * 2;        // one fp16 64x128 matrix
-constexpr size_t WS_W = 0;                              // W   (4 token tiles x 4 k-steps)
-constexpr size_t WS_Q = WS_PLANE;                       // Q'  (4 x 4)
-constexpr size_t WS_K = 2 * WS_PLANE;                   // K'^T (8 key tiles x 2 k-steps), hi
-constexpr size_t WS_KL = 3 * WS_PLANE;                  // K'^T lo: K' - hi, in fp16
-constexpr size_t WS_U = 4 * WS_PLANE;                   // Ut  fp32 accumulator tiles
-constexpr size_t WS_O = WS_U + (size_t)DV * CH * 4;     // Oi  fp32 accumulator tiles
-constexpr size_t WS_G = WS_O + (size_t)DV * CH * 4;     // e^{G_n}, b, a (float4)
-constexpr size_t WS_CHUNK = WS_G + 256;
+constexpr size_t WV_W = 0;                              // W   (4 token tiles x 4 k-steps)
+constexpr size_t WV_M = WS_PLANE;                       // M^T (4 token tiles x 2 k-steps), hi
+constexpr size_t WV_ML = WV_M + (size_t)CH * CH * 2;    // M^T lo: M - hi, in fp16
+constexpr size_t WV_U = WV_ML + (size_t)CH * CH * 2;    // Ut  fp32 accumulator tiles
+constexpr size_t WV_G = WV_U + (size_t)DV * CH * 4;     // e^{G_n}, b, a (float4)
+constexpr size_t WV_EG = WV_G + 16;                     // e^{G_t}
+constexpr size_t WV_D = WV_EG + (size_t)CH * 4;         // e^{G_n - G_t}
+constexpr size_t WV_CHUNK = WV_G + 768;
+constexpr size_t WK_Q = 0;                              // Q   (4 token tiles x 4 k-steps)
+constexpr size_t WK_K = WS_PLANE;                       // K^T (8 key tiles x 2 k-steps), hi
+constexpr size_t WK_KL = 2 * WS_PLANE;                  // K^T lo: K - hi, in fp16
+constexpr size_t WK_CHUNK = 3 * WS_PLANE;
+static_assert(WV_D + CH * 4 <= WV_CHUNK && WV_CHUNK % 256 == 0 && WK_CHUNK % 256 == 0,
+              "workspace slots");
 
 typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
 
@@ -169,20 +188,19 @@ __device__ __forceinline__ int acc_off(int d, int m, int lane) {
 // ----------------------------------------------------------------------------- phase A
 // One workgroup (8 waves) per CU, one (sequence, head, chunk) at a time.  All
 // row-major LDS tiles are bf16 hi/lo planes.  Plan (bytes):
-//   L_K : K rows [t][i]            -> later W rows [s][i]
-//   L_Q : Q rows [t][i]               (also the source of Q in Q')
-//   L_V : V rows [t][j]            -> later Ut rows [s][j]
-//   L_L : L o Q K^T                 [t][s]
+//   L_K : K rows [t][i]
+//   L_Q : Q rows [t][i]
+//   L_V : V rows [t][j]
+//   L_L : M = L o Q K^T             [t][s]
 //   L_A : A, then T in place (fp32 [64][68]);  L_S: four 16x16 blocks (pitch XP) of the inverse
 //         (T1 = T diag(beta e^G) and T2 = T diag(beta) are formed from it as
 //         fragments, in registers)
 //   L_G : G, beta, e^G, e^{G_n - G};  L_N: |k_t|^2, |v_t|^2
 //   L_T : the 4 conv taps of each of the item's 3 x 128 K, Q, V channels
 // The products are computed transposed (feature index as the MFMA row):
-//   W^T = K^T T1^T,  Ut^T = V^T T2^T,  Q'^T = e^G Q^T - W^T (LQK)^T,
-//   Oi^T = Ut^T (LQK)^T
-// with K^T, V^T, W^T, Ut^T read from row-major tiles by transpose reads, so a
-// wave's accumulators are already the scan's fragments.
+//   W^T = K^T T1^T,  Ut^T = V^T T2^T
+// with K^T, V^T read from row-major tiles by transpose reads, so a wave's
+// accumulators are already the scan's fragments.
 constexpr int PR = 136;   // pitch (bf16) of a [64][128] row-major tile
 constexpr int PS = 72;    // pitch (bf16) of a [64][64] tile
 constexpr int PA = 68;    // pitch (fp32) of the [64][64] inverse
@@ -335,7 +353,9 @@ struct PrepItem {
               // row for padding chunks); within the sequence for a fixed-length
               // batch, within the packed token rows for a variable-length one
   int64_t grow;   // g / beta row of tb
-  size_t slot;    // workspace chunk slot
+  size_t slot;    // value slot
+  size_t kslot;   // key slot of the chunk's query/key head
+  bool kown;      // the first value head of its group: writes the key slot
 };
 // Fixed-length batch: item u = (chunk, sequence, head), heads fastest, the
 // chunks from the last to the first.  Phase B reads chunk 0 of every head
@@ -357,6 +377,8 @@ __device__ __forceinline__ PrepItem prep_item(int u, int n_chunks, int H, int Hk
   it.tb = min(t0, n_tok - 1);
   it.grow = (int64_t)it.s * n_tok + it.tb;
   it.slot = ((size_t)it.s * H + it.h) * n_chunks + c;
+  it.kslot = ((size_t)it.s * Hk + it.hk) * n_chunks + c;
+  it.kown = it.h % (H / Hk) == 0;
   return it;
 }
 // Variable-length batch: item u = (head, packed chunk gc), gc fastest; the
@@ -381,6 +403,8 @@ __device__ __forceinline__ PrepItem prep_item(int u, int n_chunks, int H, int Hk
   it.tb = tab.tok0[lo] + min(t0, len - 1);
   it.grow = it.tb;
   it.slot = (size_t)it.h * n_chunks + gc;
+  it.kslot = (size_t)it.hk * n_chunks + gc;
+  it.kown = it.h % (H / Hk) == 0;
   return it;
 }
 
@@ -686,8 +710,9 @@ struct ConvSrc {
 // instead of every CU loading, then computing, then storing in lockstep.
 template <class TAB, class SRC>
 __global__ __launch_bounds__(512) void k_chunk_prep(const SRC src, unsigned char *__restrict__ ws,
-                                                    int n_tok, int n_chunks, int H, int Hk,
-                                                    int n_items, const TAB tab) {
+                                                    unsigned char *__restrict__ wsk, int n_tok,
+                                                    int n_chunks, int H, int Hk, int n_items,
+                                                    const TAB tab) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[L_TOTAL];
 
   u16 *kh = reinterpret_cast<u16 *>(smem + L_K), *klo = kh + CH * PR;
@@ -737,7 +762,8 @@ __global__ __launch_bounds__(512) void k_chunk_prep(const SRC src, unsigned char
   const PrepItem nx = prep_item(u + gridDim.x < n_items ? u + gridDim.x : u, n_chunks, H, Hk,
                                 n_tok, tab, n_items);
   const int n = it.n;
-  unsigned char *wc = ws + it.slot * WS_CHUNK;
+  unsigned char *wc = ws + it.slot * WV_CHUNK;
+  unsigned char *wk = wsk + it.kslot * WK_CHUNK;
 
   // S0. gate cumsum (wave 7): an inclusive scan over the 64 lanes on DPP
   // (row shifts within each 16-lane row, then the row totals broadcast across
@@ -777,18 +803,18 @@ __global__ __launch_bounds__(512) void k_chunk_prep(const SRC src, unsigned char
     lower_tiles<2>(w, kh, klo, qh, qlo, sA, lqh, lql, sG, sBeta, l16, kg);
   }
   src.template load_rows<1>(nx, tid, pre);
-  // S2b. K'^T fragments (K' = diag(e^{G_n - G}) K) straight from the K tile,
-  // as fp16 hi and lo planes: wave w writes key tile w, both token k-steps
-  {
-    u16 *ktg = reinterpret_cast<u16 *>(wc + WS_K);
-    u16 *ktl = reinterpret_cast<u16 *>(wc + WS_KL);
+  // S2b. K^T fragments straight from the K tile, as fp16 hi and lo planes
+  // (the first value head of a group only): wave w writes key tile w, both
+  // token k-steps
+  if (it.kown) {
+    u16 *ktg = reinterpret_cast<u16 *>(wk + WK_K);
+    u16 *ktl = reinterpret_cast<u16 *>(wk + WK_KL);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const Frag f = frag_tr(kh, klo, PR, 32 * ks, 16 * w, kg, l16);
       float x[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        x[e] = (bf16_value((u16)f.hi[e]) + bf16_value((u16)f.lo[e])) * sEGn[pi_k(32 * ks, kg, e)];
+      for (int e = 0; e < 8; ++e) x[e] = bf16_value((u16)f.hi[e]) + bf16_value((u16)f.lo[e]);
       store8_h2(ktg + frag_off(w, ks, 2, lane), ktl + frag_off(w, ks, 2, lane), x);
     }
   }
@@ -880,8 +906,8 @@ __global__ __launch_bounds__(512) void k_chunk_prep(const SRC src, unsigned char
     }
   }
   {  // W fragments and Ut tiles -> workspace
-    u16 *wg = reinterpret_cast<u16 *>(wc + WS_W);
-    float *ug = reinterpret_cast<float *>(wc + WS_U);
+    u16 *wg = reinterpret_cast<u16 *>(wc + WV_W);
+    float *ug = reinterpret_cast<float *>(wc + WV_U);
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const float xw[8] = {accW[0][m][0], accW[0][m][1], accW[0][m][2], accW[0][m][3],
@@ -893,70 +919,30 @@ __global__ __launch_bounds__(512) void k_chunk_prep(const SRC src, unsigned char
             make_float4(accU[d][m][0], accU[d][m][1], accU[d][m][2], accU[d][m][3]);
     }
   }
-  __syncthreads();  // K and V tiles are rewritten below
-  // W rows [s][i] into the K tile, Ut rows [s][j] into the V tile
-#pragma unroll
-  for (int d = 0; d < 2; ++d)
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int row = 16 * (2 * tp + m) + l16, col = 16 * (2 * kp + d) + 4 * kg;
-      store4_split(kh + row * PR + col, klo + row * PR + col, accW[d][m][0], accW[d][m][1],
-                   accW[d][m][2], accW[d][m][3]);
-      store4_split(vh + row * PR + col, vlo + row * PR + col, accU[d][m][0], accU[d][m][1],
-                   accU[d][m][2], accU[d][m][3]);
-    }
-  __syncthreads();
-
-  // S6. Q'^T = e^G Q^T - W^T (LQK)^T and Oi^T = Ut^T (LQK)^T
-  f32x4 accQ[2][2], accO[2][2];
-#pragma unroll
-  for (int d = 0; d < 2; ++d)
-#pragma unroll
-    for (int m = 0; m < 2; ++m) accQ[d][m] = accO[d][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    Frag bl[2];
-#pragma unroll
-    for (int m = 0; m < 2; ++m) bl[m] = frag_pi(lqh, lql, PS, 16 * (2 * tp + m) + l16, 32 * ks, kg);
-#pragma unroll
-    for (int d = 0; d < 2; ++d) {
-      const Frag aw = frag_tr(kh, klo, PR, 32 * ks, 16 * (2 * kp + d), kg, l16);
-      const Frag au = frag_tr(vh, vlo, PR, 32 * ks, 16 * (2 * kp + d), kg, l16);
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        accQ[d][m] = mfma3(aw, bl[m], accQ[d][m]);
-        accO[d][m] = mfma3(au, bl[m], accO[d][m]);
-      }
-    }
-  }
+  // S6. M^T fragments from the M tile (wave w: token tile w >> 1, position
+  // k-step w & 1) as fp16 hi and lo planes and, in the first value head of a
+  // group, Q fragments from the Q tile (wave w: token tile w & 3, key k-steps
+  // 2 (w >> 2) and 2 (w >> 2) + 1) as fp16, both of the tiles' bf16 hi + lo
   {
-    u16 *qg = reinterpret_cast<u16 *>(wc + WS_Q);
-    float *og = reinterpret_cast<float *>(wc + WS_O);
+    const int mt = w >> 1, ks = w & 1;
+    const Frag f = frag_pi(lqh, lql, PS, 16 * mt + l16, 32 * ks, kg);
+    float x[8];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int t = 16 * (2 * tp + m) + l16;
-      const float eg = t < n ? sEG[t] : 0.0f;
-      float xq[8];
+    for (int e = 0; e < 8; ++e) x[e] = bf16_value((u16)f.hi[e]) + bf16_value((u16)f.lo[e]);
+    store8_h2(reinterpret_cast<u16 *>(wc + WV_M) + frag_off(mt, ks, 2, lane),
+              reinterpret_cast<u16 *>(wc + WV_ML) + frag_off(mt, ks, 2, lane), x);
+  }
+  if (it.kown) {
+    const int mt = w & 3;
+    u16 *qg = reinterpret_cast<u16 *>(wk + WK_Q);
 #pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        // Q at this accumulator position: hi + lo of the Q tile (exact in
-        // fp32, within 2^-17 of the row as given; zero past n)
-        const int qo = t * PR + 16 * (2 * kp + d) + 4 * kg;
-        const uint2 qhv = *reinterpret_cast<const uint2 *>(qh + qo);
-        const uint2 qlv = *reinterpret_cast<const uint2 *>(qlo + qo);
-        const float4 qv = make_float4(
-            bf16_to_f32(qhv.x & 0xffffu) + bf16_to_f32(qlv.x & 0xffffu),
-            bf16_to_f32(qhv.x >> 16) + bf16_to_f32(qlv.x >> 16),
-            bf16_to_f32(qhv.y & 0xffffu) + bf16_to_f32(qlv.y & 0xffffu),
-            bf16_to_f32(qhv.y >> 16) + bf16_to_f32(qlv.y >> 16));
-        xq[4 * d + 0] = eg * qv.x - accQ[d][m][0];
-        xq[4 * d + 1] = eg * qv.y - accQ[d][m][1];
-        xq[4 * d + 2] = eg * qv.z - accQ[d][m][2];
-        xq[4 * d + 3] = eg * qv.w - accQ[d][m][3];
-        *reinterpret_cast<float4 *>(og + acc_off(2 * kp + d, 2 * tp + m, lane)) =
-            make_float4(accO[d][m][0], accO[d][m][1], accO[d][m][2], accO[d][m][3]);
-      }
-      store8_h(qg + frag_off(2 * tp + m, kp, 4, lane), xq);
+    for (int j = 0; j < 2; ++j) {
+      const int ks = 2 * (w >> 2) + j;
+      const Frag f = frag_pi(qh, qlo, PR, 16 * mt + l16, 32 * ks, kg);
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = bf16_value((u16)f.hi[e]) + bf16_value((u16)f.lo[e]);
+      store8_h(qg + frag_off(mt, ks, 4, lane), x);
     }
   }
   // the chunk's header, formed and stored by wave 0 (every lane stores the
@@ -965,7 +951,9 @@ __global__ __launch_bounds__(512) void k_chunk_prep(const SRC src, unsigned char
     const float bk = sBeta[lane] * sqrtf(sNK[lane]);
     const float b = group_sum<64>(bk * sqrtf(sNV[lane]));
     const float am = group_max64(bk);
-    *reinterpret_cast<float4 *>(wc + WS_G) = make_float4(sEG[CH - 1], b, am, 0.0f);
+    *reinterpret_cast<float4 *>(wc + WV_G) = make_float4(sEG[CH - 1], b, am, 0.0f);
+    reinterpret_cast<float *>(wc + WV_EG)[lane] = sEG[lane];
+    reinterpret_cast<float *>(wc + WV_D)[lane] = sEGn[lane];
   }
   src.taps_to_lds(tid, pre, tiles);
   __syncthreads();   // the next item rewrites every LDS tile
@@ -979,18 +967,27 @@ __global__ __launch_bounds__(512) void k_chunk_prep(const SRC src, unsigned char
 // One workgroup (8 waves) per (sequence, head, block b of 16 value columns),
 // computing the transposed recurrence on the state block S^T[j][i] (j in the
 // block, i over all 128 keys):
-//   P^T = S^T W^T,  U^T = Ut^T - P^T,  y^T = scale (S^T Q'^T + Oi^T),
-//   S^T <- e^{G_n} S^T + U^T K'
+//   P^T = S^T W^T,  U^T = Ut^T - P^T,  Y^T = S^T Q^T,
+//   S^T <- e^{G_n} S^T + (diag(e^{G_n-G}) U)^T K,
+//   y^T = scale (Y^T diag(e^G) + U^T M^T)
 // Wave w owns key tile w of the state (one accumulator) and token tile w & 3
-// of P^T (w < 4) or of y^T (w >= 4).  S and U travel through LDS as row-major
-// [key][j] / [token][j] tiles and are read back by transpose reads.
+// of P^T (w < 4) or of Y^T and y^T (w >= 4).  S, U and diag(e^{G_n-G}) U
+// travel through LDS as row-major [key][j] / [token][j] tiles and are read
+// back by transpose reads.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 template <int VT>
 struct ChunkOps {
-  h16x8 b[4];    // W (P waves) or Q' (y waves) fragments of token tile w & 3, 4 key k-steps
-  h16x8 k[2];    // K'^T fragments of key tile w, 2 token k-steps (hi)
+  h16x8 b[4];    // W (P waves) or Q (y waves) fragments of token tile w & 3, 4 key k-steps
+  h16x8 k[2];    // K^T fragments of key tile w, 2 token k-steps (hi)
   h16x8 kl[2];   // and their lo parts
-  float4 add[VT];  // Ut (P waves) or Oi (y waves) accumulator tiles (value tile, w & 3)
+  // P waves: the Ut accumulator tiles (value tile, w & 3); y waves: the M^T
+  // fragments of token tile w & 3, hi and lo of position k-step 0, then of
+  // k-step 1 (M is lower triangular, so token tiles 0 and 1 have no k-step
+  // 1).  Slots a wave does not use read the header instead (one line for the
+  // whole wave).
+  u32x4 x[VT < 4 ? 4 : VT];
   float hdr;     // header word lane & 3: e^{G_n}, b, a, 0
+  float tk;      // the lane's token t: e^{G_n - G_t} (P waves) or e^{G_t} (y waves)
 };
 
 // The header is read as one word per lane (lane l: word l & 3), a vector
@@ -998,20 +995,21 @@ struct ChunkOps {
 // wait behind it would also wait for the scalar cache.  hdr_word() hands every
 // lane word i.
 __device__ __forceinline__ float load_hdr(const unsigned char *wc, int lane) {
-  return reinterpret_cast<const float *>(wc + WS_G)[lane & 3];
+  return reinterpret_cast<const float *>(wc + WV_G)[lane & 3];
 }
 __device__ __forceinline__ float hdr_word(float hdr, int i) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, hdr), i));
 }
 
-// blk: the workgroup's first value tile
+// wv, wk: the chunk's value and key slots; blk: the workgroup's first value tile
 template <int VT>
-__device__ __forceinline__ void load_chunk(ChunkOps<VT> &o, const unsigned char *wc, int w,
-                                           int lane, int blk) {
+__device__ __forceinline__ void load_chunk(ChunkOps<VT> &o, const unsigned char *wv,
+                                           const unsigned char *wk, int w, int lane, int blk) {
+  constexpr int NX = VT < 4 ? 4 : VT;
   const bool pw = w < 4;
-  const u16 *bg = reinterpret_cast<const u16 *>(wc + (pw ? WS_W : WS_Q));
-  const u16 *kgp = reinterpret_cast<const u16 *>(wc + WS_K);
-  const u16 *klp = reinterpret_cast<const u16 *>(wc + WS_KL);
+  const u16 *bg = reinterpret_cast<const u16 *>(pw ? wv + WV_W : wk + WK_Q);
+  const u16 *kgp = reinterpret_cast<const u16 *>(wk + WK_K);
+  const u16 *klp = reinterpret_cast<const u16 *>(wk + WK_KL);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) o.b[ks] = frag_ws(bg, w & 3, ks, 4, lane);
 #pragma unroll
@@ -1019,11 +1017,18 @@ __device__ __forceinline__ void load_chunk(ChunkOps<VT> &o, const unsigned char 
     o.k[ks] = frag_ws(kgp, w, ks, 2, lane);
     o.kl[ks] = frag_ws(klp, w, ks, 2, lane);
   }
-  const float *addp = reinterpret_cast<const float *>(wc + (pw ? WS_U : WS_O));
+  const int t = 16 * (w & 3) + lane % 16;
 #pragma unroll
-  for (int d = 0; d < VT; ++d)
-    o.add[d] = *reinterpret_cast<const float4 *>(addp + acc_off(blk + d, w & 3, lane));
-  o.hdr = load_hdr(wc, lane);
+  for (int i = 0; i < NX; ++i) {
+    const bool p_use = i < VT, y_use = i < 2 || (i < 4 && (w & 3) >= 2);
+    const unsigned char *src =
+        pw ? (p_use ? wv + WV_U + 4 * acc_off(blk + i, w & 3, lane) : wv + WV_G)
+           : (y_use ? wv + ((i & 1) ? WV_ML : WV_M) + 2 * frag_off(w & 3, i >> 1, 2, lane)
+                    : wv + WV_G);
+    o.x[i] = *reinterpret_cast<const u32x4 *>(src);
+  }
+  o.hdr = load_hdr(wv, lane);
+  o.tk = reinterpret_cast<const float *>(wv + (pw ? WV_D : WV_EG))[t];
 }
 
 // ---- fp16 operands of the scan
@@ -1128,18 +1133,21 @@ __device__ __forceinline__ void tile_norms(const f32x4 (&st)[VT], float *red, in
 // back as it was read.  (The scan kernels have no early exit: on the 16-wave
 // form one changed its results even where it was never taken.)
 struct HeadChunks {
-  size_t first;
+  size_t first, kfirst;   // value and key slots of the first chunk
   int nch, len;
   int64_t row0;
 };
-__device__ __forceinline__ HeadChunks head_chunks(const NoTab &, int s, int h, int H, int n_tok,
-                                                  int n_chunks) {
-  return HeadChunks{((size_t)s * H + h) * n_chunks, n_chunks, n_tok, 0};
+__device__ __forceinline__ HeadChunks head_chunks(const NoTab &, int s, int h, int H, int Hk,
+                                                  int n_tok, int n_chunks) {
+  const int hk = h / (H / Hk);
+  return HeadChunks{((size_t)s * H + h) * n_chunks, ((size_t)s * Hk + hk) * n_chunks, n_chunks,
+                    n_tok, 0};
 }
-__device__ __forceinline__ HeadChunks head_chunks(const VarTab &tab, int s, int h, int, int,
-                                                  int n_chunks) {
-  const int nch = tab.ch0[s + 1] - tab.ch0[s];
-  return HeadChunks{nch > 0 ? (size_t)h * n_chunks + tab.ch0[s] : 0, nch,
+__device__ __forceinline__ HeadChunks head_chunks(const VarTab &tab, int s, int h, int H, int Hk,
+                                                  int, int n_chunks) {
+  const int nch = tab.ch0[s + 1] - tab.ch0[s], hk = h / (H / Hk);
+  return HeadChunks{nch > 0 ? (size_t)h * n_chunks + tab.ch0[s] : 0,
+                    nch > 0 ? (size_t)hk * n_chunks + tab.ch0[s] : 0, nch,
                     tab.tok0[s + 1] - tab.tok0[s], tab.tok0[s]};
 }
 
@@ -1219,14 +1227,17 @@ constexpr int SPB = 24;   // pitch (bf16) of the [128][16] S tile and the [64][1
 // One chunk of the scan on a workgroup's VT value tiles.  The state tile of
 // value tile d (values 16d + 4kg + r of key 16w + l16) goes to LDS as rows
 // [i][j] of the S tile (pitch SP); P waves (w < 4) form U^T = Ut^T - S^T W^T
-// for token tile w and write it as rows [t][j] of the U tile; y waves form
-// y^T = scale (S^T Q'^T + Oi^T); then every wave updates its state tiles with
-// U^T K'.  The B operands (W or Q', K') are loaded once and serve all VT tiles.
+// for token tile w and write U and diag(e^{G_n-G}) U as rows [t][j] of the U
+// and D tiles; y waves form Y^T = S^T Q^T; then every wave updates its state
+// tiles with the D tile times K, and the y waves add U^T M^T to
+// Y^T diag(e^G) for y.  The B operands (W or Q, K, M) are loaded once and
+// serve all VT tiles.
 template <int VT>
 __device__ __forceinline__ void scan_chunk(const ChunkOps<VT> &o, float (&bound)[VT],
                                            f32x4 (&st)[VT], u16 *ssh, u16 *ssl, u16 *suh,
-                                           u16 *sul, float *yc, int64_t y_tok, int n,
-                                           float scale, int w, int l16, int kg) {
+                                           u16 *sul, u16 *sdh, u16 *sdl, float *yc,
+                                           int64_t y_tok, int n, float scale, int w, int l16,
+                                           int kg) {
   constexpr int SP = NBLK * VT + 8;
   // nothing of this chunk's work is scheduled above this point: its header
   // words were loaded a chunk ago, and reading them earlier would wait for
@@ -1251,17 +1262,13 @@ __device__ __forceinline__ void scan_chunk(const ChunkOps<VT> &o, float (&bound)
   const int t = 16 * (w & 3) + l16;   // this lane's token; values 4kg + r
 #pragma unroll
   for (int d = 0; d < VT; ++d) {
-    const f32x4 p = acc[d] * sc[d].iS;
-    const float4 ad = o.add[d];
+    acc[d] = acc[d] * sc[d].iS;
     if (w < 4) {
-      const f32x4 u = {ad.x - p[0], ad.y - p[1], ad.z - p[2], ad.w - p[3]};
-      store4_split_h(suh + t * SP + 16 * d + 4 * kg, sul + t * SP + 16 * d + 4 * kg, u,
-                     sc[d].sU);
-    } else if (t < n) {   // y is not read again here: a non-temporal store
-      __builtin_nontemporal_store(
-          f32x4{scale * (p[0] + ad.x), scale * (p[1] + ad.y), scale * (p[2] + ad.z),
-                scale * (p[3] + ad.w)},
-          reinterpret_cast<f32x4 *>(yc + (int64_t)t * y_tok + 16 * d + 4 * kg));
+      const f32x4 ad = __builtin_bit_cast(f32x4, o.x[d]);
+      const f32x4 u = ad - acc[d];
+      const int off = t * SP + 16 * d + 4 * kg;
+      store4_split_h(suh + off, sul + off, u, sc[d].sU);
+      store4_split_h(sdh + off, sdl + off, u * o.tk, sc[d].sU);
     }
   }
   __syncthreads();
@@ -1272,8 +1279,24 @@ __device__ __forceinline__ void scan_chunk(const ChunkOps<VT> &o, float (&bound)
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
     for (int d = 0; d < VT; ++d)
-      du[d] = mfma3_h(frag_tr_h(suh, sul, SP, 32 * ks, 16 * d, kg, l16), o.k[ks], o.kl[ks],
+      du[d] = mfma3_h(frag_tr_h(sdh, sdl, SP, 32 * ks, 16 * d, kg, l16), o.k[ks], o.kl[ks],
                       du[d]);
+  if (w >= 4) {
+#pragma unroll
+    for (int d = 0; d < VT; ++d) {
+      f32x4 ym = mfma3_h(frag_tr_h(suh, sul, SP, 0, 16 * d, kg, l16),
+                         __builtin_bit_cast(h16x8, o.x[0]), __builtin_bit_cast(h16x8, o.x[1]),
+                         f32x4{0.f, 0.f, 0.f, 0.f});
+      if ((w & 3) >= 2)
+        ym = mfma3_h(frag_tr_h(suh, sul, SP, 32, 16 * d, kg, l16),
+                     __builtin_bit_cast(h16x8, o.x[2]), __builtin_bit_cast(h16x8, o.x[3]), ym);
+      if (t < n) {   // y is not read again here: a non-temporal store
+        const f32x4 yv = (acc[d] * o.tk + ym * sc[d].iU) * scale;
+        __builtin_nontemporal_store(
+            yv, reinterpret_cast<f32x4 *>(yc + (int64_t)t * y_tok + 16 * d + 4 * kg));
+      }
+    }
+  }
   const float gam = hdr_word(o.hdr, 0);
 #pragma unroll
   for (int d = 0; d < VT; ++d) st[d] = st[d] * gam + du[d] * sc[d].iU;
@@ -1282,11 +1305,12 @@ __device__ __forceinline__ void scan_chunk(const ChunkOps<VT> &o, float (&bound)
 template <class TAB, int VT>
 __global__ __launch_bounds__(512) void k_chunk_scan(
     float *__restrict__ state, int64_t st_seq, const unsigned char *__restrict__ ws,
-    float *__restrict__ y, int64_t y_tok, int64_t y_seq, int n_tok, int n_chunks, int H,
-    float scale, const TAB tab, const HistOut ho) {
+    const unsigned char *__restrict__ wsk, float *__restrict__ y, int64_t y_tok, int64_t y_seq,
+    int n_tok, int n_chunks, int H, int Hk, float scale, const TAB tab, const HistOut ho) {
   constexpr int SP = NBLK * VT + 8;
   __shared__ __attribute__((aligned(16))) u16 ssh[DK * SP], ssl[DK * SP];
   __shared__ __attribute__((aligned(16))) u16 suh[CH * SP], sul[CH * SP];
+  __shared__ __attribute__((aligned(16))) u16 sdh[CH * SP], sdl[CH * SP];
   __shared__ float red[8 * VT];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
   // the NVB / VT workgroups of one head on one XCD (xcd_order)
@@ -1294,7 +1318,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan(
   xcd_order(blockIdx.x, gridDim.x, NVB / VT, sh, blk);
   blk *= VT;   // first value tile
   const int h = sh % H, s = sh / H;
-  const HeadChunks hc = head_chunks(tab, s, h, H, n_tok, n_chunks);
+  const HeadChunks hc = head_chunks(tab, s, h, H, Hk, n_tok, n_chunks);
   const HistTaps taps = hist_read(ho, s, h, blk * NBLK, VT * NBLK, tid);
 
   // state element (value j = 16 (blk + d) + 4kg + r, key i = 16w + l16), value-major
@@ -1308,12 +1332,15 @@ __global__ __launch_bounds__(512) void k_chunk_scan(
   }
   float bound[VT];
   tile_norms(st, red, w, lane, bound);
-  const unsigned char *wh = ws + hc.first * WS_CHUNK;
+  const unsigned char *wh = ws + hc.first * WV_CHUNK, *wkh = wsk + hc.kfirst * WK_CHUNK;
   float *yh = y + s * y_seq + hc.row0 * y_tok + (int64_t)h * DV + blk * NBLK;
-  auto chunk_ptr = [&](int c) { return wh + (size_t)max(min(c, hc.nch - 1), 0) * WS_CHUNK; };
+  auto cidx = [&](int c) { return (size_t)max(min(c, hc.nch - 1), 0); };
+  auto load = [&](ChunkOps<VT> &o, int c) {
+    load_chunk(o, wh + cidx(c) * WV_CHUNK, wkh + cidx(c) * WK_CHUNK, w, lane, blk);
+  };
   auto run = [&](const ChunkOps<VT> &o, int c) {
-    scan_chunk<VT>(o, bound, st, ssh, ssl, suh, sul, yh + (int64_t)c * CH * y_tok, y_tok,
-                   min(CH, hc.len - c * CH), scale, w, l16, kg);
+    scan_chunk<VT>(o, bound, st, ssh, ssl, suh, sul, sdh, sdl, yh + (int64_t)c * CH * y_tok,
+                   y_tok, min(CH, hc.len - c * CH), scale, w, l16, kg);
   };
 
   // Two operand sets: chunk c + 2's are requested as soon as chunk c has run
@@ -1323,13 +1350,13 @@ __global__ __launch_bounds__(512) void k_chunk_scan(
   // copy the operand registers at the loop head, which waits for every load
   // in flight.
   ChunkOps<VT> a, b;
-  load_chunk(a, chunk_ptr(0), w, lane, blk);
-  load_chunk(b, chunk_ptr(1), w, lane, blk);
+  load(a, 0);
+  load(b, 1);
   for (int c = 0; c < hc.nch; c += 2) {
     run(a, c);
-    load_chunk(a, chunk_ptr(c + 2), w, lane, blk);
+    load(a, c + 2);
     run(b, c + 1);
-    load_chunk(b, chunk_ptr(c + 3), w, lane, blk);
+    load(b, c + 3);
   }
 #pragma unroll
   for (int d = 0; d < VT; ++d) {
@@ -1346,31 +1373,31 @@ __global__ __launch_bounds__(512) void k_chunk_scan(
 // One 16-wave workgroup per (sequence, head, pair of value blocks): waves
 // 8g .. 8g+7 run exactly the per-wave arithmetic of k_chunk_scan on value
 // block 2p + g, so the results are bit-identical to it.  The two groups share
-// one copy of each chunk's W, Q' and K' hi and lo (the first 64 KB of its
-// workspace, copied byte for byte), which halves the head's operand reads
-// from L2; the price is that every wave now reads its fragments from LDS, so
-// this form only pays once the 8-wave grid would need a second pass.
+// one LDS copy of each chunk's W, Q, K hi and lo, and M hi and lo (80 KiB,
+// copied byte for byte), which halves the head's operand reads from L2; the price is that
+// every wave now reads its fragments from LDS, so this form only pays once
+// the 8-wave grid would need a second pass.
 // The copy is staged through registers one chunk ahead: each thread holds 32
-// bytes of W and Q' and 32 bytes of K'.  W and Q' are rewritten in LDS right
-// after the barrier that ends their last reads (the U barrier), K' right
-// after the barrier that ends the state update's reads (the S barrier).
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-constexpr int OPS_WQ = (int)(2 * WS_PLANE);   // W and Q', workspace bytes [0, 32 KiB)
-constexpr int OPS_K = (int)(2 * WS_PLANE);    // K'^T hi and lo, workspace bytes [32, 64 KiB)
+// bytes of W and Q, 32 bytes of K and 16 bytes of M.  W and Q are rewritten in
+// LDS right after the barrier that ends their last reads (the U barrier), K
+// and M right after the barrier that ends the state update's and y's reads of
+// them (the S barrier).
+constexpr int OPS_WQ = (int)(2 * WS_PLANE);   // W (value slot), Q (key slot)
+constexpr int OPS_K = (int)(2 * WS_PLANE);    // K^T hi and lo (key slot)
+constexpr int OPS_M = 2 * CH * CH * 2;        // M^T hi and lo (value slot)
 constexpr int PAIR_THREADS = 1024;
-static_assert(WS_W == 0 && WS_Q == WS_PLANE && WS_K == (size_t)OPS_WQ &&
-              WS_KL == WS_K + WS_PLANE, "operand layout");
-static_assert(OPS_WQ % (16 * PAIR_THREADS) == 0 && OPS_K % (16 * PAIR_THREADS) == 0, "copy split");
+static_assert(WS_PLANE == 16 * PAIR_THREADS && WK_KL == WK_K + WS_PLANE &&
+              OPS_M == 16 * PAIR_THREADS && WV_ML == WV_M + OPS_M / 2, "copy split");
 
 template <class TAB>
 __global__ __launch_bounds__(PAIR_THREADS) void k_chunk_scan_pair(
     float *__restrict__ state, int64_t st_seq, const unsigned char *__restrict__ ws,
-    float *__restrict__ y, int64_t y_tok, int64_t y_seq, int n_tok, int n_chunks, int H,
-    float scale, const TAB tab, const HistOut ho) {
-  constexpr int NWQ = OPS_WQ / (16 * PAIR_THREADS), NK = OPS_K / (16 * PAIR_THREADS);
+    const unsigned char *__restrict__ wsk, float *__restrict__ y, int64_t y_tok, int64_t y_seq,
+    int n_tok, int n_chunks, int H, int Hk, float scale, const TAB tab, const HistOut ho) {
   __shared__ __attribute__((aligned(16))) u16 ssh[2][DK * SPB], ssl[2][DK * SPB];
   __shared__ __attribute__((aligned(16))) u16 suh[2][CH * SPB], sul[2][CH * SPB];
-  __shared__ __attribute__((aligned(16))) unsigned char ops[OPS_WQ + OPS_K];
+  __shared__ __attribute__((aligned(16))) u16 sdh[2][CH * SPB], sdl[2][CH * SPB];
+  __shared__ __attribute__((aligned(16))) unsigned char ops[OPS_WQ + OPS_K + OPS_M];
   __shared__ float red[2][8];
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
   const int grp = tid >> 9, w = (tid >> 6) & 7;
@@ -1380,7 +1407,7 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_chunk_scan_pair(
   xcd_order(blockIdx.x, gridDim.x, NVB / 2, sh, pair);
   const int h = sh % H, s = sh / H;
   const int blk = 2 * pair + grp;
-  const HeadChunks hc = head_chunks(tab, s, h, H, n_tok, n_chunks);
+  const HeadChunks hc = head_chunks(tab, s, h, H, Hk, n_tok, n_chunks);
   const HistTaps taps = hist_read(ho, s, h, 2 * pair * NBLK, 2 * NBLK, tid);
 
   float *sp = state + s * st_seq + (int64_t)h * DK * DV +
@@ -1393,50 +1420,58 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_chunk_scan_pair(
     tile_norms<1>(st1, red[grp], w, lane, b1);
     bound = b1[0];
   }
-  const unsigned char *wh = ws + hc.first * WS_CHUNK;
+  const unsigned char *wh = ws + hc.first * WV_CHUNK, *wkh = wsk + hc.kfirst * WK_CHUNK;
   float *yh = y + s * y_seq + hc.row0 * y_tok + (int64_t)h * DV + blk * NBLK;
-  auto chunk_ptr = [&](int c) { return wh + (size_t)max(min(c, hc.nch - 1), 0) * WS_CHUNK; };
+  auto cidx = [&](int c) { return (size_t)max(min(c, hc.nch - 1), 0); };
+  auto vptr = [&](int c) { return wh + cidx(c) * WV_CHUNK; };
+  auto kptr = [&](int c) { return wkh + cidx(c) * WK_CHUNK; };
   u16 *s_hi = ssh[grp], *s_lo = ssl[grp], *u_hi = suh[grp], *u_lo = sul[grp];
-  const u16 *b_lds = reinterpret_cast<const u16 *>(ops + (w < 4 ? WS_W : WS_Q));
+  u16 *d_hi = sdh[grp], *d_lo = sdl[grp];
+  const u16 *b_lds = reinterpret_cast<const u16 *>(ops + (w < 4 ? 0 : OPS_WQ / 2));
   const u16 *k_lds = reinterpret_cast<const u16 *>(ops + OPS_WQ);
-  const int add_off = acc_off(blk, w & 3, lane);
+  const u16 *m_lds = reinterpret_cast<const u16 *>(ops + OPS_WQ + OPS_K);
+  const int add_off = 4 * acc_off(blk, w & 3, lane);
   const int t = 16 * (w & 3) + l16;   // this lane's token; values 4kg + r
 
-  u32x4 rwq[NWQ], rk[NK];
-  auto load_wq = [&](const unsigned char *wc) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < NWQ; ++i)
-      rwq[i] = *reinterpret_cast<const u32x4 *>(wc + 16 * (tid + PAIR_THREADS * i));
+  u32x4 rwq[2], rk[2], rm;
+  auto load_wq = [&](int c) __attribute__((always_inline)) {
+    rwq[0] = *reinterpret_cast<const u32x4 *>(vptr(c) + WV_W + 16 * tid);
+    rwq[1] = *reinterpret_cast<const u32x4 *>(kptr(c) + WK_Q + 16 * tid);
   };
-  auto load_k = [&](const unsigned char *wc) __attribute__((always_inline)) {
+  auto load_k = [&](int c) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NK; ++i)
-      rk[i] = *reinterpret_cast<const u32x4 *>(wc + OPS_WQ + 16 * (tid + PAIR_THREADS * i));
+    for (int i = 0; i < 2; ++i)
+      rk[i] = *reinterpret_cast<const u32x4 *>(kptr(c) + WK_K + 16 * (tid + PAIR_THREADS * i));
+    rm = *reinterpret_cast<const u32x4 *>(vptr(c) + WV_M + 16 * tid);
   };
   auto put_wq = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NWQ; ++i)
+    for (int i = 0; i < 2; ++i)
       *reinterpret_cast<u32x4 *>(ops + 16 * (tid + PAIR_THREADS * i)) = rwq[i];
   };
   auto put_k = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NK; ++i)
+    for (int i = 0; i < 2; ++i)
       *reinterpret_cast<u32x4 *>(ops + OPS_WQ + 16 * (tid + PAIR_THREADS * i)) = rk[i];
+    *reinterpret_cast<u32x4 *>(ops + OPS_WQ + OPS_K + 16 * tid) = rm;
   };
-  auto load_add = [&](const unsigned char *wc, float4 &add, float &hdr)
+  // P waves: the Ut tile and e^{G_n - G_t}; y waves: e^{G_t} (their add slot
+  // reads the header, one line for the whole wave)
+  auto load_add = [&](int c, float4 &add, float &hdr, float &tk)
       __attribute__((always_inline)) {
-    const float *addp = reinterpret_cast<const float *>(wc + (w < 4 ? WS_U : WS_O));
-    add = *reinterpret_cast<const float4 *>(addp + add_off);
-    hdr = load_hdr(wc, lane);
+    const unsigned char *wv = vptr(c);
+    add = *reinterpret_cast<const float4 *>(w < 4 ? wv + WV_U + add_off : wv + WV_G);
+    hdr = load_hdr(wv, lane);
+    tk = reinterpret_cast<const float *>(wv + (w < 4 ? WV_D : WV_EG))[t];
   };
-  auto run = [&](int c, const float4 &add, float hdr) __attribute__((always_inline)) {
+  auto run = [&](int c, const float4 &add, float hdr, float tk) __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);   // as in scan_chunk
     const Scales sc = chunk_scales(bound, hdr);
     store4_split_h(s_hi + (16 * w + l16) * SPB + 4 * kg, s_lo + (16 * w + l16) * SPB + 4 * kg,
                    st, sc.sS);
-    __syncthreads();   // S barrier: W, Q' of chunk c and the S tiles are in LDS
-    put_k();           // K' of chunk c, first read after the U barrier
-    load_k(chunk_ptr(c + 1));
+    __syncthreads();   // S barrier: W, Q of chunk c and the S tiles are in LDS
+    put_k();           // K, M of chunk c, first read after the U barrier
+    load_k(c + 1);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -1445,42 +1480,52 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_chunk_scan_pair(
     }
     acc = acc * sc.iS;
     if (w < 4) {
-      const f32x4 u = {add.x - acc[0], add.y - acc[1], add.z - acc[2], add.w - acc[3]};
+      const f32x4 u = __builtin_bit_cast(f32x4, add) - acc;
       store4_split_h(u_hi + t * SPB + 4 * kg, u_lo + t * SPB + 4 * kg, u, sc.sU);
-    } else if (t < min(CH, hc.len - c * CH)) {
-      __builtin_nontemporal_store(
-          f32x4{scale * (acc[0] + add.x), scale * (acc[1] + add.y), scale * (acc[2] + add.z),
-                scale * (acc[3] + add.w)},
-          reinterpret_cast<f32x4 *>(yh + (int64_t)(c * CH + t) * y_tok + 4 * kg));
+      store4_split_h(d_hi + t * SPB + 4 * kg, d_lo + t * SPB + 4 * kg, u * tk, sc.sU);
     }
-    __syncthreads();   // U barrier: K' and the U tiles are in LDS, W and Q' are read
-    put_wq();          // W, Q' of chunk c + 1
-    load_wq(chunk_ptr(c + 2));
+    __syncthreads();   // U barrier: K, M and the U, D tiles are in LDS, W and Q are read
+    put_wq();          // W, Q of chunk c + 1
+    load_wq(c + 2);
     f32x4 du = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const h16x8 kh = *reinterpret_cast<const h16x8 *>(k_lds + frag_off(w, ks, 2, lane));
       const h16x8 kl =
           *reinterpret_cast<const h16x8 *>(k_lds + CH * DK + frag_off(w, ks, 2, lane));
-      du = mfma3_h(frag_tr_h(u_hi, u_lo, SPB, 32 * ks, 0, kg, l16), kh, kl, du);
+      du = mfma3_h(frag_tr_h(d_hi, d_lo, SPB, 32 * ks, 0, kg, l16), kh, kl, du);
+    }
+    if (w >= 4) {
+      auto mfr = [&](int ks, int plane) {
+        return *reinterpret_cast<const h16x8 *>(m_lds + plane * CH * CH +
+                                                frag_off(w & 3, ks, 2, lane));
+      };
+      f32x4 ym = mfma3_h(frag_tr_h(u_hi, u_lo, SPB, 0, 0, kg, l16), mfr(0, 0), mfr(0, 1),
+                         f32x4{0.f, 0.f, 0.f, 0.f});
+      if ((w & 3) >= 2)
+        ym = mfma3_h(frag_tr_h(u_hi, u_lo, SPB, 32, 0, kg, l16), mfr(1, 0), mfr(1, 1), ym);
+      if (t < min(CH, hc.len - c * CH))
+        __builtin_nontemporal_store((acc * tk + ym * sc.iU) * scale,
+                                    reinterpret_cast<f32x4 *>(yh + (int64_t)(c * CH + t) * y_tok +
+                                                              4 * kg));
     }
     st = st * hdr_word(hdr, 0) + du * sc.iU;
   };
 
-  load_wq(chunk_ptr(0));
+  load_wq(0);
   put_wq();   // visible after the first S barrier
-  load_wq(chunk_ptr(1));
-  load_k(chunk_ptr(0));
+  load_wq(1);
+  load_k(0);
   float4 add0, add1;
-  float hdr0, hdr1;
-  load_add(chunk_ptr(0), add0, hdr0);
-  load_add(chunk_ptr(1), add1, hdr1);
+  float hdr0, hdr1, tk0, tk1;
+  load_add(0, add0, hdr0, tk0);
+  load_add(1, add1, hdr1, tk1);
   // the chunk count is even, as for k_chunk_scan
   for (int c = 0; c < hc.nch; c += 2) {
-    run(c, add0, hdr0);
-    load_add(chunk_ptr(c + 2), add0, hdr0);
-    run(c + 1, add1, hdr1);
-    load_add(chunk_ptr(c + 3), add1, hdr1);
+    run(c, add0, hdr0, tk0);
+    load_add(c + 2, add0, hdr0, tk0);
+    run(c + 1, add1, hdr1, tk1);
+    load_add(c + 3, add1, hdr1, tk1);
   }
   sp[0] = st[0];
   sp[DK] = st[1];
@@ -1493,17 +1538,20 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_chunk_scan_pair(
 
 static_assert(CH == 64, "padded_chunks counts 64-position chunks");
 
-size_t chunked_workspace_bytes(int n_seq, int n_tok, int H, int, int S, int) {
+// bytes of the value and key slots of one chunk position over all heads
+static size_t slots_bytes(int H, int Hk) { return (size_t)H * WV_CHUNK + (size_t)Hk * WK_CHUNK; }
+
+size_t chunked_workspace_bytes(int n_seq, int n_tok, int H, int Hk, int S, int) {
   if (S != DK) return 0;   // the S = 32 / 64 form keeps everything on chip
-  return (size_t)n_seq * H * padded_chunks(n_tok) * WS_CHUNK;
+  return (size_t)n_seq * padded_chunks(n_tok) * slots_bytes(H, Hk);
 }
 
 // Sum over sequences of padded_chunks(len) <= sum(ceil(len / 64)) + n_seq
 // <= (total_tok + 63 n_seq) / 64 + n_seq, for any split of total_tok.
-size_t chunked_varlen_workspace_bytes(int n_seq, int total_tok, int H, int S) {
+size_t chunked_varlen_workspace_bytes(int n_seq, int total_tok, int H, int Hk, int S) {
   if (S != DK) return 0;
   const int64_t slots = ((int64_t)total_tok + 63 * (int64_t)n_seq) / CH + n_seq;
-  return (size_t)slots * H * WS_CHUNK;
+  return (size_t)slots * slots_bytes(H, Hk);
 }
 
 // Compute units of the current device, queried once per device.
@@ -1522,7 +1570,8 @@ static int device_cu_count() {
 }
 
 // Phase A then phase B of one call; n_chunks is the per-sequence chunk count
-// (fixed-length batch) or the packed total (variable-length batch).
+// (fixed-length batch) or the packed total (variable-length batch).  The
+// n_items value slots come first in the workspace, then the key slots.
 template <class TAB, class SRC>
 static int launch_two_phase(const RecurArgs &a, const TAB &tab, const SRC &src, const HistOut &ho,
                             int n_chunks, int n_items, unsigned char *wsb, hipStream_t stream) {
@@ -1531,8 +1580,9 @@ static int launch_two_phase(const RecurArgs &a, const TAB &tab, const SRC &src, 
   const int cus = device_cu_count();
   if (cus <= 0) return GDN_ERR_LAUNCH;
   const int grid_a = n_items < cus ? n_items : cus;
+  unsigned char *wsk = wsb + (size_t)n_items * WV_CHUNK;
   int rc = launch_kernel(k_chunk_prep<TAB, SRC>, dim3(grid_a), dim3(512), 0, stream, src, wsb,
-                         a.n_tok, n_chunks, a.H, a.Hk, n_items, tab);
+                         wsk, a.n_tok, n_chunks, a.H, a.Hk, n_items, tab);
   if (rc != GDN_OK) return rc;
   // phase B: 8-wave workgroups of one value tile each while they fit in one
   // pass of the chip (measured: two or four tiles per workgroup lengthen the
@@ -1542,11 +1592,12 @@ static int launch_two_phase(const RecurArgs &a, const TAB &tab, const SRC &src, 
   const int units = a.n_seq * a.H;
   if (units * NVB > cus)
     return launch_kernel(k_chunk_scan_pair<TAB>, dim3(units * (NVB / 2)), dim3(PAIR_THREADS), 0,
-                         stream, a.state, a.st_seq, (const unsigned char *)wsb, a.y, a.y_tok,
-                         a.y_seq, a.n_tok, n_chunks, a.H, a.scale, tab, ho);
+                         stream, a.state, a.st_seq, (const unsigned char *)wsb,
+                         (const unsigned char *)wsk, a.y, a.y_tok, a.y_seq, a.n_tok, n_chunks,
+                         a.H, a.Hk, a.scale, tab, ho);
   return launch_kernel(k_chunk_scan<TAB, 1>, dim3(units * NVB), dim3(512), 0, stream, a.state,
-                       a.st_seq, (const unsigned char *)wsb, a.y, a.y_tok, a.y_seq, a.n_tok,
-                       n_chunks, a.H, a.scale, tab, ho);
+                       a.st_seq, (const unsigned char *)wsb, (const unsigned char *)wsk, a.y,
+                       a.y_tok, a.y_seq, a.n_tok, n_chunks, a.H, a.Hk, a.scale, tab, ho);
 }
 
 // No conv history to write: any valid address for the discarded reads.
@@ -1576,7 +1627,7 @@ int launch_recur_chunked_varlen(const RecurArgs &a, const VarTab &tab, bool bf16
   if (a.S != DK) return launch_chunk_small_varlen(a, tab, bf16_in, stream);
   const int n_chunks = tab.ch0[tab.n_seq];   // packed total, even per sequence
   if (n_chunks == 0) return GDN_OK;           // every sequence is empty
-  if (ws_bytes < (size_t)n_chunks * a.H * WS_CHUNK) return GDN_ERR_WORKSPACE;
+  if (ws_bytes < (size_t)n_chunks * slots_bytes(a.H, a.Hk)) return GDN_ERR_WORKSPACE;
   unsigned char *wsb = static_cast<unsigned char *>(ws);
   if (bf16_in)
     return launch_two_phase(a, tab,

@@ -99,7 +99,7 @@ struct VarTab {
 // to even (0 for an empty sequence).
 inline int padded_chunks(int n_tok) { return ((n_tok + 63) / 64 + 1) & ~1; }
 // Workspace bound of a packed batch of n_seq sequences and total_tok positions.
-size_t chunked_varlen_workspace_bytes(int n_seq, int total_tok, int H, int S);
+size_t chunked_varlen_workspace_bytes(int n_seq, int total_tok, int H, int Hk, int S);
 // a.n_tok is the packed total; a.qk_seq, a.v_seq, a.y_seq are unused.  With
 // bf16_in, a.q, a.k, a.v point at bf16 elements (strides still in elements).
 int launch_recur_chunked_varlen(const RecurArgs &a, const VarTab &tab, bool bf16_in, int chunk,

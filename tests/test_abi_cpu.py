@@ -138,10 +138,11 @@ def test_chunked_varlen_validation_and_workspace_query():
     T = cu[-1]
     ws_need = L.gdn_recurrence_chunked_varlen_workspace_bytes(len(lens), T, H, Hk, S, 64)
     # the bound covers the padded chunk count of this split: 2 + 0 + 2 + 2 chunks
-    per_chunk = L.gdn_recurrence_chunked_workspace_bytes(1, 64, 1, 1, S, 64) // 2
-    assert ws_need >= 6 * H * per_chunk
+    # (per_chunk: the bytes of one chunk position over all heads)
+    per_chunk = L.gdn_recurrence_chunked_workspace_bytes(1, 64, H, Hk, S, 64) // 2
+    assert ws_need >= 6 * per_chunk
     # and of the worst split of T positions into 4 sequences
-    assert ws_need >= ((T + 63 * 4) // 64 + 4) * H * per_chunk
+    assert ws_need >= ((T + 63 * 4) // 64 + 4) * per_chunk
     assert L.gdn_recurrence_chunked_varlen_workspace_bytes(0, T, H, Hk, S, 64) == 0
     assert L.gdn_recurrence_chunked_varlen_workspace_bytes(257, T, H, Hk, S, 64) == 0
     assert L.gdn_recurrence_chunked_varlen_workspace_bytes(4, T, H, Hk, 64, 64) == 0
