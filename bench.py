@@ -92,7 +92,12 @@ def recorded_traffic(profile: str):
 
 
 def chunked_flops(T: int, H: int, S: int, C: int = 64) -> float:
-    """Algorithmic flops of the chunked recurrence: per token-head 10*C*S + 6*S^2."""
+    """Algorithmic flops of the chunked recurrence, per token-head 10*C*S + 6*S^2
+    (2 flops a multiply-add; per chunk of C positions: K K^T and Q K^T on their
+    lower halves, W, Ut, the intra-chunk output and its correction 2 C^2 S each;
+    the three products with the state 2 C S^2 each).  The kernels form y as
+    e^G Q S + M U, one C^2 S product fewer (8*C*S + 6*S^2); the figure is kept
+    as the method's count so that rates stay comparable."""
     return float(T) * H * (10 * C * S + 6 * S * S)
 
 
@@ -100,12 +105,14 @@ def chunked_flops(T: int, H: int, S: int, C: int = 64) -> float:
 # 64-position chunk), counted from the kernels' code:
 #   phase A, 16x16x32 bf16 (16384 flops each): K K^T and Q K^T on 20 lower
 #     tiles x 4 k-steps x 3 (hi/lo split) = 240; W and U~: 8 waves x 2 k-steps
-#     x 2 key tiles x 2 token tiles x 2 products x 3 = 384; Q' and O_i: 384;
+#     x 2 key tiles x 2 token tiles x 2 products x 3 = 384;
 #   phase A, 16x16x4 fp32 (2048 flops each): the block inverse, 64;
 #   phase B, 16x16x32 fp16 (16384 flops each) per 16-column value tile: 8 waves
-#     x 4 k-steps x 2 (state hi/lo) = 64 for W S / Q' S, and 8 waves x 2
-#     k-steps x 3 (U hi/lo, K' hi/lo) = 48 for K'^T U; 8 value tiles per head.
-MFMA_FLOPS_PER_HEAD_CHUNK = (240 + 384 + 384) * 16384 + 64 * 2048 + 8 * (64 + 48) * 16384
+#     x 4 k-steps x 2 (state hi/lo) = 64 for W S / Q S, 8 waves x 2 k-steps x 3
+#     (U hi/lo, K hi/lo) = 48 for the state update, and 3 + 3 + 6 + 6 = 18 for
+#     M U (U hi/lo, M hi/lo; token tiles 0 and 1 have one position k-step);
+#     8 value tiles per head.
+MFMA_FLOPS_PER_HEAD_CHUNK = (240 + 384) * 16384 + 64 * 2048 + 8 * (64 + 48 + 18) * 16384
 
 
 def chunked_executed_flops(n_tok: int, H: int, n_seq: int = 1) -> float:
@@ -571,8 +578,8 @@ def main():
             "chunked_peak_note": "frac_of_bf16_peak: algorithmic flops (one product each) over "
                                  "the dense bf16 MFMA peak (the fp16 MFMA peak is the same); "
                                  "executed: the flops of the MFMA instructions the kernels issue "
-                                 "(bf16 hi/lo splits in phase A, fp16 with hi/lo state and K' in "
-                                 "phase B, fp32 16x16x4 in the block inverse), counted from the "
+                                 "(bf16 hi/lo splits in phase A, fp16 with hi/lo state, U, K and M "
+                                 "in phase B, fp32 16x16x4 in the block inverse), counted from the "
                                  "code; fp32_equivalent_frac divides the algorithmic rate by the "
                                  "fp32 matrix peak of an instruction the kernels do not issue, "
                                  "for comparison with an fp32 formulation only",

@@ -362,13 +362,25 @@ struct PrepItem {
 // first and the last chunk last; the workspace outgrows the last-level cache
 // (MALL) at long prompts, and written in the reverse of its read order, what
 // the cache still holds when phase B starts is what phase B reads first.
+// Within a chunk, when the (sequence, query/key head) groups come in
+// multiples of 8, the G value heads of a group are items 8 apart: the
+// persistent grid (a multiple of 8 workgroups, workgroup b on XCD b % 8) then
+// runs them at the same time on one XCD, which reads the group's q and k rows
+// from HBM once.
 __device__ __forceinline__ PrepItem prep_item(int u, int n_chunks, int H, int Hk, int n_tok,
                                               const NoTab &, int n_items) {
   PrepItem it;
   const int nsh = n_items / n_chunks;   // sequences x heads
   const int c = n_chunks - 1 - u / nsh;
-  it.h = (u % nsh) % H;
-  it.s = (u % nsh) / H;
+  const int G = H / Hk, idx = u % nsh;
+  if (nsh % (8 * G) == 0) {
+    const int gi = (idx / (8 * G)) * 8 + idx % 8, mem = (idx / 8) % G;
+    it.s = gi / Hk;
+    it.h = (gi % Hk) * G + mem;
+  } else {
+    it.h = idx % H;
+    it.s = idx / H;
+  }
   it.hk = it.h / (H / Hk);
   const int t0 = c * CH;
   it.n = max(0, min(CH, n_tok - t0));
@@ -1152,14 +1164,14 @@ __device__ __forceinline__ HeadChunks head_chunks(const VarTab &tab, int s, int 
 }
 
 // XCD-aware order of the scan's workgroups.  Consecutive workgroup ids go to
-// different XCDs (id % 8).  The `per` workgroups of one (sequence, head) unit
-// get ids on one XCD, so they share its L2.  When the unit count is a multiple
-// of 8, consecutive units are interleaved over the 8 XCDs, so every XCD holds
-// an even share of every sequence: dealing each XCD a contiguous run of units
-// would give it whole sequences, and with sequences of different lengths the
-// XCD holding the longest would run long after the others are idle.
-// Otherwise units are dealt in contiguous runs (XCD x < r of nwg = 8q + r
-// taking q + 1 workgroups, the others q).
+// different XCDs (id % 8).  The `per` workgroups of one unit (a sequence and
+// query/key group) get ids on one XCD, so they share its L2.  When the unit
+// count is a multiple of 8, consecutive units are interleaved over the 8
+// XCDs, so every XCD holds an even share of every sequence: dealing each XCD
+// a contiguous run of units would give it whole sequences, and with sequences
+// of different lengths the XCD holding the longest would run long after the
+// others are idle.  Otherwise units are dealt in contiguous runs (XCD x < r
+// of nwg = 8q + r taking q + 1 workgroups, the others q).
 __device__ __forceinline__ void xcd_order(int b, int nwg, int per, int &sh, int &sub) {
   const int xcd = b % 8, idx = b / 8;
   if ((nwg / per) % 8 == 0) {
@@ -1313,11 +1325,14 @@ __global__ __launch_bounds__(512) void k_chunk_scan(
   __shared__ __attribute__((aligned(16))) u16 sdh[CH * SP], sdl[CH * SP];
   __shared__ float red[8 * VT];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
-  // the NVB / VT workgroups of one head on one XCD (xcd_order)
-  int sh, blk;
-  xcd_order(blockIdx.x, gridDim.x, NVB / VT, sh, blk);
-  blk *= VT;   // first value tile
-  const int h = sh % H, s = sh / H;
+  // the G NVB / VT workgroups of one (sequence, query/key head) group on one
+  // XCD (xcd_order), so the group's Q and K cross from the MALL into its L2
+  // once
+  int gu, sub;
+  const int G = H / Hk;
+  xcd_order(blockIdx.x, gridDim.x, G * (NVB / VT), gu, sub);
+  const int s = gu / Hk, h = (gu % Hk) * G + sub / (NVB / VT);
+  const int blk = (sub % (NVB / VT)) * VT;   // first value tile
   const HeadChunks hc = head_chunks(tab, s, h, H, Hk, n_tok, n_chunks);
   const HistTaps taps = hist_read(ho, s, h, blk * NBLK, VT * NBLK, tid);
 
@@ -1401,11 +1416,12 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_chunk_scan_pair(
   __shared__ float red[2][8];
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
   const int grp = tid >> 9, w = (tid >> 6) & 7;
-  // the 4 workgroups of one head on one XCD (xcd_order; the grid, 4 per head,
-  // need not be a multiple of 8)
-  int sh, pair;
-  xcd_order(blockIdx.x, gridDim.x, NVB / 2, sh, pair);
-  const int h = sh % H, s = sh / H;
+  // the 4 G workgroups of one (sequence, query/key head) group on one XCD
+  // (xcd_order; the grid need not be a multiple of 8)
+  int gu, sub;
+  const int G = H / Hk;
+  xcd_order(blockIdx.x, gridDim.x, G * (NVB / 2), gu, sub);
+  const int s = gu / Hk, h = (gu % Hk) * G + sub / (NVB / 2), pair = sub % (NVB / 2);
   const int blk = 2 * pair + grp;
   const HeadChunks hc = head_chunks(tab, s, h, H, Hk, n_tok, n_chunks);
   const HistTaps taps = hist_read(ho, s, h, 2 * pair * NBLK, 2 * NBLK, tid);
