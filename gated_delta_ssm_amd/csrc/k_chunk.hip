@@ -57,6 +57,8 @@
 // a row-major LDS tile are read with ds_read_b64_tr_b16 (gfx950).
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "bf16_frag.hpp"
 #include "conv.hpp"
 #include "gate.hpp"
@@ -987,19 +989,23 @@ __global__ __launch_bounds__(512) void k_chunk_prep(const SRC src, unsigned char
 // travel through LDS as row-major [key][j] / [token][j] tiles and are read
 // back by transpose reads.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-template <int VT>
+// A wave's role in the chunk step: P waves (w < 4) form P and U; y waves of
+// token tiles 0 and 1 need one position k-step of M (M is lower triangular),
+// those of token tiles 2 and 3 two.  Each role runs its own copy of the chunk
+// loop, so a wave loads exactly its operands, with no branch in the loop.
+enum : int { ROLE_P = 0, ROLE_Y1 = 1, ROLE_Y2 = 2 };
+template <int VT, int ROLE>
 struct ChunkOps {
+  static constexpr int NX = ROLE == ROLE_P ? VT : ROLE == ROLE_Y1 ? 2 : 4;
+  float hdr;     // header word lane & 3: e^{G_n}, b, a, 0
+  float tk;      // the lane's token t: e^{G_n - G_t} (P waves) or e^{G_t} (y waves)
   h16x8 b[4];    // W (P waves) or Q (y waves) fragments of token tile w & 3, 4 key k-steps
   h16x8 k[2];    // K^T fragments of key tile w, 2 token k-steps (hi)
   h16x8 kl[2];   // and their lo parts
   // P waves: the Ut accumulator tiles (value tile, w & 3); y waves: the M^T
-  // fragments of token tile w & 3, hi and lo of position k-step 0, then of
-  // k-step 1 (M is lower triangular, so token tiles 0 and 1 have no k-step
-  // 1).  Slots a wave does not use read the header instead (one line for the
-  // whole wave).
-  u32x4 x[VT < 4 ? 4 : VT];
-  float hdr;     // header word lane & 3: e^{G_n}, b, a, 0
-  float tk;      // the lane's token t: e^{G_n - G_t} (P waves) or e^{G_t} (y waves)
+  // fragments of token tile w & 3, hi and lo of position k-step 0 (and of
+  // k-step 1)
+  u32x4 x[NX];
 };
 
 // The header is read as one word per lane (lane l: word l & 3), a vector
@@ -1013,34 +1019,35 @@ __device__ __forceinline__ float hdr_word(float hdr, int i) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, hdr), i));
 }
 
-// wv, wk: the chunk's value and key slots; blk: the workgroup's first value tile
-template <int VT>
-__device__ __forceinline__ void load_chunk(ChunkOps<VT> &o, const unsigned char *wv,
+// wv, wk: the chunk's value and key slots; blk: the workgroup's first value
+// tile.  Loads are issued in the order the chunk step first uses them.
+template <int VT, int ROLE>
+__device__ __forceinline__ void load_chunk(ChunkOps<VT, ROLE> &o, const unsigned char *wv,
                                            const unsigned char *wk, int w, int lane, int blk) {
-  constexpr int NX = VT < 4 ? 4 : VT;
-  const bool pw = w < 4;
-  const u16 *bg = reinterpret_cast<const u16 *>(pw ? wv + WV_W : wk + WK_Q);
-  const u16 *kgp = reinterpret_cast<const u16 *>(wk + WK_K);
-  const u16 *klp = reinterpret_cast<const u16 *>(wk + WK_KL);
+  const int t = 16 * (w & 3) + lane % 16;
+  o.hdr = load_hdr(wv, lane);
+  o.tk = reinterpret_cast<const float *>(wv + (ROLE == ROLE_P ? WV_D : WV_EG))[t];
+  const u16 *bg = reinterpret_cast<const u16 *>(ROLE == ROLE_P ? wv + WV_W : wk + WK_Q);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) o.b[ks] = frag_ws(bg, w & 3, ks, 4, lane);
+  if constexpr (ROLE == ROLE_P) {
+#pragma unroll
+    for (int i = 0; i < VT; ++i)
+      o.x[i] = *reinterpret_cast<const u32x4 *>(wv + WV_U + 4 * acc_off(blk + i, w & 3, lane));
+  }
+  const u16 *kgp = reinterpret_cast<const u16 *>(wk + WK_K);
+  const u16 *klp = reinterpret_cast<const u16 *>(wk + WK_KL);
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     o.k[ks] = frag_ws(kgp, w, ks, 2, lane);
     o.kl[ks] = frag_ws(klp, w, ks, 2, lane);
   }
-  const int t = 16 * (w & 3) + lane % 16;
+  if constexpr (ROLE != ROLE_P) {
 #pragma unroll
-  for (int i = 0; i < NX; ++i) {
-    const bool p_use = i < VT, y_use = i < 2 || (i < 4 && (w & 3) >= 2);
-    const unsigned char *src =
-        pw ? (p_use ? wv + WV_U + 4 * acc_off(blk + i, w & 3, lane) : wv + WV_G)
-           : (y_use ? wv + ((i & 1) ? WV_ML : WV_M) + 2 * frag_off(w & 3, i >> 1, 2, lane)
-                    : wv + WV_G);
-    o.x[i] = *reinterpret_cast<const u32x4 *>(src);
+    for (int i = 0; i < ChunkOps<VT, ROLE>::NX; ++i)
+      o.x[i] = *reinterpret_cast<const u32x4 *>(wv + ((i & 1) ? WV_ML : WV_M) +
+                                                 2 * frag_off(w & 3, i >> 1, 2, lane));
   }
-  o.hdr = load_hdr(wv, lane);
-  o.tk = reinterpret_cast<const float *>(wv + (pw ? WV_D : WV_EG))[t];
 }
 
 // ---- fp16 operands of the scan
@@ -1244,8 +1251,8 @@ constexpr int SPB = 24;   // pitch (bf16) of the [128][16] S tile and the [64][1
 // tiles with the D tile times K, and the y waves add U^T M^T to
 // Y^T diag(e^G) for y.  The B operands (W or Q, K, M) are loaded once and
 // serve all VT tiles.
-template <int VT>
-__device__ __forceinline__ void scan_chunk(const ChunkOps<VT> &o, float (&bound)[VT],
+template <int VT, int ROLE>
+__device__ __forceinline__ void scan_chunk(const ChunkOps<VT, ROLE> &o, float (&bound)[VT],
                                            f32x4 (&st)[VT], u16 *ssh, u16 *ssl, u16 *suh,
                                            u16 *sul, u16 *sdh, u16 *sdl, float *yc,
                                            int64_t y_tok, int n, float scale, int w, int l16,
@@ -1275,7 +1282,7 @@ __device__ __forceinline__ void scan_chunk(const ChunkOps<VT> &o, float (&bound)
 #pragma unroll
   for (int d = 0; d < VT; ++d) {
     acc[d] = acc[d] * sc[d].iS;
-    if (w < 4) {
+    if constexpr (ROLE == ROLE_P) {
       const f32x4 ad = __builtin_bit_cast(f32x4, o.x[d]);
       const f32x4 u = ad - acc[d];
       const int off = t * SP + 16 * d + 4 * kg;
@@ -1293,13 +1300,13 @@ __device__ __forceinline__ void scan_chunk(const ChunkOps<VT> &o, float (&bound)
     for (int d = 0; d < VT; ++d)
       du[d] = mfma3_h(frag_tr_h(sdh, sdl, SP, 32 * ks, 16 * d, kg, l16), o.k[ks], o.kl[ks],
                       du[d]);
-  if (w >= 4) {
+  if constexpr (ROLE != ROLE_P) {
 #pragma unroll
     for (int d = 0; d < VT; ++d) {
       f32x4 ym = mfma3_h(frag_tr_h(suh, sul, SP, 0, 16 * d, kg, l16),
                          __builtin_bit_cast(h16x8, o.x[0]), __builtin_bit_cast(h16x8, o.x[1]),
                          f32x4{0.f, 0.f, 0.f, 0.f});
-      if ((w & 3) >= 2)
+      if constexpr (ROLE == ROLE_Y2)
         ym = mfma3_h(frag_tr_h(suh, sul, SP, 32, 16 * d, kg, l16),
                      __builtin_bit_cast(h16x8, o.x[2]), __builtin_bit_cast(h16x8, o.x[3]), ym);
       if (t < n) {   // y is not read again here: a non-temporal store
@@ -1324,7 +1331,8 @@ __global__ __launch_bounds__(512) void k_chunk_scan(
   __shared__ __attribute__((aligned(16))) u16 suh[CH * SP], sul[CH * SP];
   __shared__ __attribute__((aligned(16))) u16 sdh[CH * SP], sdl[CH * SP];
   __shared__ float red[8 * VT];
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   // the G NVB / VT workgroups of one (sequence, query/key head) group on one
   // XCD (xcd_order), so the group's Q and K cross from the MALL into its L2
   // once
@@ -1350,29 +1358,38 @@ __global__ __launch_bounds__(512) void k_chunk_scan(
   const unsigned char *wh = ws + hc.first * WV_CHUNK, *wkh = wsk + hc.kfirst * WK_CHUNK;
   float *yh = y + s * y_seq + hc.row0 * y_tok + (int64_t)h * DV + blk * NBLK;
   auto cidx = [&](int c) { return (size_t)max(min(c, hc.nch - 1), 0); };
-  auto load = [&](ChunkOps<VT> &o, int c) {
-    load_chunk(o, wh + cidx(c) * WV_CHUNK, wkh + cidx(c) * WK_CHUNK, w, lane, blk);
-  };
-  auto run = [&](const ChunkOps<VT> &o, int c) {
-    scan_chunk<VT>(o, bound, st, ssh, ssl, suh, sul, sdh, sdl, yh + (int64_t)c * CH * y_tok,
-                   y_tok, min(CH, hc.len - c * CH), scale, w, l16, kg);
-  };
-
   // Two operand sets: chunk c + 2's are requested as soon as chunk c has run
   // (into the registers chunk c used), so each request has the whole of
   // chunk c + 1 to arrive.  n_chunks is even (the workspace is padded with an
   // identity chunk), so the loop has no tail; a tail would make the compiler
   // copy the operand registers at the loop head, which waits for every load
-  // in flight.
-  ChunkOps<VT> a, b;
-  load(a, 0);
-  load(b, 1);
-  for (int c = 0; c < hc.nch; c += 2) {
-    run(a, c);
-    load(a, c + 2);
-    run(b, c + 1);
-    load(b, c + 3);
-  }
+  // in flight.  One copy of the loop per wave role (a uniform branch).
+  auto walk = [&](auto role) {
+    constexpr int ROLE = decltype(role)::value;
+    auto load = [&](ChunkOps<VT, ROLE> &o, int c) {
+      load_chunk(o, wh + cidx(c) * WV_CHUNK, wkh + cidx(c) * WK_CHUNK, w, lane, blk);
+    };
+    auto run = [&](const ChunkOps<VT, ROLE> &o, int c) {
+      scan_chunk<VT, ROLE>(o, bound, st, ssh, ssl, suh, sul, sdh, sdl,
+                           yh + (int64_t)c * CH * y_tok, y_tok, min(CH, hc.len - c * CH), scale,
+                           w, l16, kg);
+    };
+    ChunkOps<VT, ROLE> a, b;
+    load(a, 0);
+    load(b, 1);
+    for (int c = 0; c < hc.nch; c += 2) {
+      run(a, c);
+      load(a, c + 2);
+      run(b, c + 1);
+      load(b, c + 3);
+    }
+  };
+  if (w < 4)
+    walk(std::integral_constant<int, ROLE_P>{});
+  else if ((w & 3) < 2)
+    walk(std::integral_constant<int, ROLE_Y1>{});
+  else
+    walk(std::integral_constant<int, ROLE_Y2>{});
 #pragma unroll
   for (int d = 0; d < VT; ++d) {
     float *p = sp + (int64_t)16 * d * DK;
