@@ -1003,8 +1003,8 @@ struct ChunkOps {
   h16x8 k[2];    // K^T fragments of key tile w, 2 token k-steps (hi)
   h16x8 kl[2];   // and their lo parts
   // P waves: the Ut accumulator tiles (value tile, w & 3); y waves: the M^T
-  // fragments of token tile w & 3, hi and lo of position k-step 0 (and of
-  // k-step 1)
+  // fragments of the chunk before, token tile w & 3, hi and lo of position
+  // k-step 0 (and of k-step 1)
   u32x4 x[NX];
 };
 
@@ -1019,35 +1019,60 @@ __device__ __forceinline__ float hdr_word(float hdr, int i) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, hdr), i));
 }
 
-// wv, wk: the chunk's value and key slots; blk: the workgroup's first value
-// tile.  Loads are issued in the order the chunk step first uses them.
+// The operands of one chunk, by the part of the chunk step that consumes
+// them: wv, wk are the chunk's value and key slots, wvm the value slot of the
+// chunk before (y waves read its M), blk the workgroup's first value tile.
+// The scan requests each part of chunk c + 2 right after chunk c's step has
+// read that part, so the requests of the 8 waves spread over the step rather
+// than queueing at the texture addresser all at once.
+struct ChunkSrc {
+  const unsigned char *wv, *wk, *wvm;
+};
+// W or Q (and the P waves' Ut tiles: read where W is)
 template <int VT, int ROLE>
-__device__ __forceinline__ void load_chunk(ChunkOps<VT, ROLE> &o, const unsigned char *wv,
-                                           const unsigned char *wk, int w, int lane, int blk) {
-  const int t = 16 * (w & 3) + lane % 16;
-  o.hdr = load_hdr(wv, lane);
-  o.tk = reinterpret_cast<const float *>(wv + (ROLE == ROLE_P ? WV_D : WV_EG))[t];
-  const u16 *bg = reinterpret_cast<const u16 *>(ROLE == ROLE_P ? wv + WV_W : wk + WK_Q);
+__device__ __forceinline__ void load_b(ChunkOps<VT, ROLE> &o, const ChunkSrc &p, int w, int lane,
+                                       int blk) {
+  const u16 *bg = reinterpret_cast<const u16 *>(ROLE == ROLE_P ? p.wv + WV_W : p.wk + WK_Q);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) o.b[ks] = frag_ws(bg, w & 3, ks, 4, lane);
   if constexpr (ROLE == ROLE_P) {
 #pragma unroll
     for (int i = 0; i < VT; ++i)
-      o.x[i] = *reinterpret_cast<const u32x4 *>(wv + WV_U + 4 * acc_off(blk + i, w & 3, lane));
+      o.x[i] = *reinterpret_cast<const u32x4 *>(p.wv + WV_U + 4 * acc_off(blk + i, w & 3, lane));
   }
-  const u16 *kgp = reinterpret_cast<const u16 *>(wk + WK_K);
-  const u16 *klp = reinterpret_cast<const u16 *>(wk + WK_KL);
+}
+// y waves: the M^T fragments of the chunk before
+template <int VT, int ROLE>
+__device__ __forceinline__ void load_m(ChunkOps<VT, ROLE> &o, const ChunkSrc &p, int w,
+                                       int lane) {
+  if constexpr (ROLE != ROLE_P) {
+#pragma unroll
+    for (int i = 0; i < ChunkOps<VT, ROLE>::NX; ++i)
+      o.x[i] = *reinterpret_cast<const u32x4 *>(p.wvm + ((i & 1) ? WV_ML : WV_M) +
+                                                 2 * frag_off(w & 3, i >> 1, 2, lane));
+  }
+}
+// K^T hi and lo, and the header words
+template <int VT, int ROLE>
+__device__ __forceinline__ void load_k(ChunkOps<VT, ROLE> &o, const ChunkSrc &p, int w,
+                                       int lane) {
+  const u16 *kgp = reinterpret_cast<const u16 *>(p.wk + WK_K);
+  const u16 *klp = reinterpret_cast<const u16 *>(p.wk + WK_KL);
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     o.k[ks] = frag_ws(kgp, w, ks, 2, lane);
     o.kl[ks] = frag_ws(klp, w, ks, 2, lane);
   }
-  if constexpr (ROLE != ROLE_P) {
-#pragma unroll
-    for (int i = 0; i < ChunkOps<VT, ROLE>::NX; ++i)
-      o.x[i] = *reinterpret_cast<const u32x4 *>(wv + ((i & 1) ? WV_ML : WV_M) +
-                                                 2 * frag_off(w & 3, i >> 1, 2, lane));
-  }
+  o.hdr = load_hdr(p.wv, lane);
+  o.tk = reinterpret_cast<const float *>(p.wv + (ROLE == ROLE_P ? WV_D : WV_EG))[16 * (w & 3) +
+                                                                                 lane % 16];
+}
+template <int VT, int ROLE>
+__device__ __forceinline__ void load_chunk(ChunkOps<VT, ROLE> &o, const ChunkSrc &p, int w,
+                                           int lane, int blk) {
+  load_k(o, p, w, lane);
+  load_b(o, p, w, lane, blk);
+  load_m(o, p, w, lane);
 }
 
 // ---- fp16 operands of the scan
@@ -1243,21 +1268,56 @@ __device__ __forceinline__ void hist_write(const HistTaps &r) {
 
 constexpr int SPB = 24;   // pitch (bf16) of the [128][16] S tile and the [64][16] U tile
 
-// One chunk of the scan on a workgroup's VT value tiles.  The state tile of
+// y waves: what the y of a chunk still needs when the chunk step has run
+// (its U tile is formed only then; M U is added in the next chunk's step)
+template <int VT>
+struct YCarry {
+  f32x4 q[VT];    // (S^T Q^T) iS of the chunk, per value tile
+  float iU[VT];   // the chunk's U scales
+  float tk;       // e^{G_t} of the lane's token
+};
+
+// y^T of chunk c (its U tile in LDS at uh/ul): (Y^T diag(e^G) + U^T M^T) scale,
+// with M^T fragments m (hi, lo of position k-step 0, then of k-step 1)
+template <int VT, int ROLE>
+__device__ __forceinline__ void y_out(const YCarry<VT> &yc, const u32x4 (&m)[ROLE == ROLE_Y1 ? 2 : 4],
+                                      const u16 *uh, const u16 *ul, float *yp, int64_t y_tok,
+                                      int n, float scale, int t, int l16, int kg) {
+  constexpr int SP = NBLK * VT + 8;
+#pragma unroll
+  for (int d = 0; d < VT; ++d) {
+    f32x4 ym = mfma3_h(frag_tr_h(uh, ul, SP, 0, 16 * d, kg, l16),
+                       __builtin_bit_cast(h16x8, m[0]), __builtin_bit_cast(h16x8, m[1]),
+                       f32x4{0.f, 0.f, 0.f, 0.f});
+    if constexpr (ROLE == ROLE_Y2)
+      ym = mfma3_h(frag_tr_h(uh, ul, SP, 32, 16 * d, kg, l16),
+                   __builtin_bit_cast(h16x8, m[2]), __builtin_bit_cast(h16x8, m[3]), ym);
+    if (t < n) {   // y is not read again here: a non-temporal store
+      const f32x4 yv = (yc.q[d] * yc.tk + ym * yc.iU[d]) * scale;
+      __builtin_nontemporal_store(
+          yv, reinterpret_cast<f32x4 *>(yp + (int64_t)t * y_tok + 16 * d + 4 * kg));
+    }
+  }
+}
+
+// Chunk c of the scan on a workgroup's VT value tiles.  The state tile of
 // value tile d (values 16d + 4kg + r of key 16w + l16) goes to LDS as rows
 // [i][j] of the S tile (pitch SP); P waves (w < 4) form U^T = Ut^T - S^T W^T
 // for token tile w and write U and diag(e^{G_n-G}) U as rows [t][j] of the U
-// and D tiles; y waves form Y^T = S^T Q^T; then every wave updates its state
-// tiles with the D tile times K, and the y waves add U^T M^T to
-// Y^T diag(e^G) for y.  The B operands (W or Q, K, M) are loaded once and
-// serve all VT tiles.
+// tile (buffer c % 2) and of the D tile; y waves form Y^T = S^T Q^T and, in the
+// same stretch, finish y of chunk c - 1 with U^T M^T from the other U buffer
+// (y feeds nothing, so it stays off the chain from state to state); then
+// every wave updates its state tiles with the D tile times K.  The B operands
+// (W or Q, K, M) are loaded once and serve all VT tiles.  yp: y rows of the
+// sequence's first position; len: its positions.
 template <int VT, int ROLE>
-__device__ __forceinline__ void scan_chunk(const ChunkOps<VT, ROLE> &o, float (&bound)[VT],
-                                           f32x4 (&st)[VT], u16 *ssh, u16 *ssl, u16 *suh,
-                                           u16 *sul, u16 *sdh, u16 *sdl, float *yc,
-                                           int64_t y_tok, int n, float scale, int w, int l16,
-                                           int kg) {
+__device__ __forceinline__ void scan_chunk(ChunkOps<VT, ROLE> &o, const ChunkSrc &nx,
+                                           YCarry<VT> &yc, float (&bound)[VT], f32x4 (&st)[VT],
+                                           u16 *ssh, u16 *ssl, u16 *suh, u16 *sul, u16 *sdh,
+                                           u16 *sdl, float *yp, int64_t y_tok, int c, int len,
+                                           float scale, int w, int l16, int kg, int blk) {
   constexpr int SP = NBLK * VT + 8;
+  constexpr int UB = CH * SP;   // one U buffer
   // nothing of this chunk's work is scheduled above this point: its header
   // words were loaded a chunk ago, and reading them earlier would wait for
   // the operand loads still in flight
@@ -1280,15 +1340,32 @@ __device__ __forceinline__ void scan_chunk(const ChunkOps<VT, ROLE> &o, float (&
       acc[d] = mfma2_h(frag_tr_h(ssh, ssl, SP, 32 * ks, 16 * d, kg, l16), o.b[ks], acc[d]);
   const int t = 16 * (w & 3) + l16;   // this lane's token; values 4kg + r
 #pragma unroll
-  for (int d = 0; d < VT; ++d) {
-    acc[d] = acc[d] * sc[d].iS;
-    if constexpr (ROLE == ROLE_P) {
-      const f32x4 ad = __builtin_bit_cast(f32x4, o.x[d]);
-      const f32x4 u = ad - acc[d];
+  for (int d = 0; d < VT; ++d) acc[d] = acc[d] * sc[d].iS;
+  if constexpr (ROLE == ROLE_P) {
+#pragma unroll
+    for (int d = 0; d < VT; ++d) {
+      const f32x4 u = __builtin_bit_cast(f32x4, o.x[d]) - acc[d];
       const int off = t * SP + 16 * d + 4 * kg;
-      store4_split_h(suh + off, sul + off, u, sc[d].sU);
+      store4_split_h(suh + (c & 1) * UB + off, sul + (c & 1) * UB + off, u, sc[d].sU);
       store4_split_h(sdh + off, sdl + off, u * o.tk, sc[d].sU);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    load_b(o, nx, w, l16 + 16 * kg, blk);   // W and Ut of chunk c + 2
+  } else {
+    __builtin_amdgcn_sched_barrier(0);
+    load_b(o, nx, w, l16 + 16 * kg, blk);   // Q of chunk c + 2
+    if (c > 0)
+      y_out<VT, ROLE>(yc, o.x, suh + ((c - 1) & 1) * UB, sul + ((c - 1) & 1) * UB,
+                      yp + (int64_t)(c - 1) * CH * y_tok, y_tok, len - (c - 1) * CH, scale, t,
+                      l16, kg);
+#pragma unroll
+    for (int d = 0; d < VT; ++d) {
+      yc.q[d] = acc[d];
+      yc.iU[d] = sc[d].iU;
+    }
+    yc.tk = o.tk;
+    __builtin_amdgcn_sched_barrier(0);
+    load_m(o, nx, w, l16 + 16 * kg);        // M of chunk c + 1
   }
   __syncthreads();
   f32x4 du[VT];
@@ -1300,25 +1377,11 @@ __device__ __forceinline__ void scan_chunk(const ChunkOps<VT, ROLE> &o, float (&
     for (int d = 0; d < VT; ++d)
       du[d] = mfma3_h(frag_tr_h(sdh, sdl, SP, 32 * ks, 16 * d, kg, l16), o.k[ks], o.kl[ks],
                       du[d]);
-  if constexpr (ROLE != ROLE_P) {
-#pragma unroll
-    for (int d = 0; d < VT; ++d) {
-      f32x4 ym = mfma3_h(frag_tr_h(suh, sul, SP, 0, 16 * d, kg, l16),
-                         __builtin_bit_cast(h16x8, o.x[0]), __builtin_bit_cast(h16x8, o.x[1]),
-                         f32x4{0.f, 0.f, 0.f, 0.f});
-      if constexpr (ROLE == ROLE_Y2)
-        ym = mfma3_h(frag_tr_h(suh, sul, SP, 32, 16 * d, kg, l16),
-                     __builtin_bit_cast(h16x8, o.x[2]), __builtin_bit_cast(h16x8, o.x[3]), ym);
-      if (t < n) {   // y is not read again here: a non-temporal store
-        const f32x4 yv = (acc[d] * o.tk + ym * sc[d].iU) * scale;
-        __builtin_nontemporal_store(
-            yv, reinterpret_cast<f32x4 *>(yc + (int64_t)t * y_tok + 16 * d + 4 * kg));
-      }
-    }
-  }
   const float gam = hdr_word(o.hdr, 0);
 #pragma unroll
   for (int d = 0; d < VT; ++d) st[d] = st[d] * gam + du[d] * sc[d].iU;
+  __builtin_amdgcn_sched_barrier(0);
+  load_k(o, nx, w, l16 + 16 * kg);          // K and header of chunk c + 2
 }
 
 template <class TAB, int VT>
@@ -1328,7 +1391,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan(
     int n_tok, int n_chunks, int H, int Hk, float scale, const TAB tab, const HistOut ho) {
   constexpr int SP = NBLK * VT + 8;
   __shared__ __attribute__((aligned(16))) u16 ssh[DK * SP], ssl[DK * SP];
-  __shared__ __attribute__((aligned(16))) u16 suh[CH * SP], sul[CH * SP];
+  __shared__ __attribute__((aligned(16))) u16 suh[2 * CH * SP], sul[2 * CH * SP];
   __shared__ __attribute__((aligned(16))) u16 sdh[CH * SP], sdl[CH * SP];
   __shared__ float red[8 * VT];
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
@@ -1366,22 +1429,31 @@ __global__ __launch_bounds__(512) void k_chunk_scan(
   // in flight.  One copy of the loop per wave role (a uniform branch).
   auto walk = [&](auto role) {
     constexpr int ROLE = decltype(role)::value;
-    auto load = [&](ChunkOps<VT, ROLE> &o, int c) {
-      load_chunk(o, wh + cidx(c) * WV_CHUNK, wkh + cidx(c) * WK_CHUNK, w, lane, blk);
+    // the sources of chunk c (y waves: with the M of chunk c - 1)
+    auto src = [&](int c) {
+      return ChunkSrc{wh + cidx(c) * WV_CHUNK, wkh + cidx(c) * WK_CHUNK,
+                      wh + cidx(c - 1) * WV_CHUNK};
     };
-    auto run = [&](const ChunkOps<VT, ROLE> &o, int c) {
-      scan_chunk<VT, ROLE>(o, bound, st, ssh, ssl, suh, sul, sdh, sdl,
-                           yh + (int64_t)c * CH * y_tok, y_tok, min(CH, hc.len - c * CH), scale,
-                           w, l16, kg);
+    YCarry<VT> yc;
+    auto run = [&](ChunkOps<VT, ROLE> &o, int c) {
+      scan_chunk<VT, ROLE>(o, src(c + 2), yc, bound, st, ssh, ssl, suh, sul, sdh, sdl, yh, y_tok,
+                           c, hc.len, scale, w, l16, kg, blk);
     };
     ChunkOps<VT, ROLE> a, b;
-    load(a, 0);
-    load(b, 1);
+    load_chunk(a, src(0), w, lane, blk);
+    load_chunk(b, src(1), w, lane, blk);
     for (int c = 0; c < hc.nch; c += 2) {
       run(a, c);
-      load(a, c + 2);
       run(b, c + 1);
-      load(b, c + 3);
+    }
+    // y of the last chunk: set a was loaded for chunk nch, so it holds the M
+    // of chunk nch - 1, whose U tile is the last one written
+    if constexpr (ROLE != ROLE_P) {
+      const int c = hc.nch;
+      if (c > 0)
+        y_out<VT, ROLE>(yc, a.x, suh + ((c - 1) & 1) * CH * SP, sul + ((c - 1) & 1) * CH * SP,
+                        yh + (int64_t)(c - 1) * CH * y_tok, y_tok, hc.len - (c - 1) * CH, scale,
+                        16 * (w & 3) + l16, l16, kg);
     }
   };
   if (w < 4)
