@@ -171,13 +171,16 @@ size_t gdn_recurrence_chunked_workspace_bytes(int n_seq, int n_tok, int n_v_head
  *   - beta_t |k_t|^2 <= 2 at every position (true for unit-length keys and
  *     beta in [0, 1]), so every factor I - beta_t k_t k_t^T has spectral
  *     norm <= 1.  Under these two, |T[t][s]| <= beta_t for s < t, every entry
- *     of W and K' is at most beta_t |k_t| resp. |k_t|, and every entry of Q'
- *     is at most |q_t| (the factors are products of such contractions).
- * Numerics at S = 128: the intra-chunk products (K K^T, Q K^T, W, U~, Q',
- * O_i) run on bf16 MFMA with each fp32 operand split into hi + lo and fp32
- * accumulation; the triangular inverse, cumulative gate, exponentials and the
- * state carry are fp32.  W and Q' are stored in the workspace as fp16 and K'
- * as fp16 hi + lo; the inter-chunk products use them on fp16 MFMA against the
+ *     of W is at most beta_t |k_t| (its rows are products of such
+ *     contractions applied to beta_t e^{G_t} k_t), every entry of (L o Q K^T)
+ *     at most |q_t| |k_s|, and every entry of Q and K at most 1 for unit-length
+ *     queries and keys.
+ * Numerics at S = 128: the intra-chunk products (K K^T, Q K^T, W,
+ * T diag(beta) V) run on bf16 MFMA with each fp32 operand split into hi + lo
+ * and fp32 accumulation; the triangular inverse, cumulative gate,
+ * exponentials and the state carry are fp32.  W and Q are stored in the
+ * workspace as fp16, K and L o Q K^T as fp16 hi + lo (Q and K once per
+ * query/key head); the inter-chunk products use them on fp16 MFMA against the
  * state and U split into fp16 hi + lo after a power-of-two scaling chosen from
  * a running bound on their norms (so no input size can overflow fp16).
  * Agreement with the sequential scan is a tolerance (normwise 2e-3), not bit
