@@ -817,20 +817,16 @@ __global__ __launch_bounds__(512) void k_chunk_prep(const SRC src, unsigned char
     lower_tiles<2>(w, kh, klo, qh, qlo, sA, lqh, lql, sG, sBeta, l16, kg);
   }
   src.template load_rows<1>(nx, tid, pre);
-  // S2b. K^T fragments straight from the K tile, as fp16 hi and lo planes
-  // (the first value head of a group only): wave w writes key tile w, both
-  // token k-steps
-  if (it.kown) {
-    u16 *ktg = reinterpret_cast<u16 *>(wk + WK_K);
-    u16 *ktl = reinterpret_cast<u16 *>(wk + WK_KL);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const Frag f = frag_tr(kh, klo, PR, 32 * ks, 16 * w, kg, l16);
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = bf16_value((u16)f.hi[e]) + bf16_value((u16)f.lo[e]);
-      store8_h2(ktg + frag_off(w, ks, 2, lane), ktl + frag_off(w, ks, 2, lane), x);
-    }
+  // the chunk's header, formed and stored by wave 7 (its Gram share is one of
+  // the lighter ones; every lane stores the same bits): e^{G_n}, b, a, then
+  // e^{G_t} and e^{G_n - G_t}
+  if (w == 7) {
+    const float bk = sBeta[lane] * sqrtf(sNK[lane]);
+    const float b = group_sum<64>(bk * sqrtf(sNV[lane]));
+    const float am = group_max64(bk);
+    *reinterpret_cast<float4 *>(wc + WV_G) = make_float4(sEG[CH - 1], b, am, 0.0f);
+    reinterpret_cast<float *>(wc + WV_EG)[lane] = sEG[lane];
+    reinterpret_cast<float *>(wc + WV_D)[lane] = sEGn[lane];
   }
   __syncthreads();
 
@@ -846,6 +842,49 @@ __global__ __launch_bounds__(512) void k_chunk_prep(const SRC src, unsigned char
 #pragma unroll
       for (int j = 0; j < r; ++j) acc -= sA[(16 * b + r) * PA + 16 * b + j] * x[j];
       x[r] = acc;
+    }
+  }
+  // While wave 0 inverts, the waves store the fragments that need only the
+  // K, Q and M tiles (wave 0 its share after the inverse).
+  // S2b. K^T fragments straight from the K tile, as fp16 hi and lo planes
+  // (the first value head of a group only): wave w writes key tile w, both
+  // token k-steps
+  if (it.kown) {
+    u16 *ktg = reinterpret_cast<u16 *>(wk + WK_K);
+    u16 *ktl = reinterpret_cast<u16 *>(wk + WK_KL);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const Frag f = frag_tr(kh, klo, PR, 32 * ks, 16 * w, kg, l16);
+      float xf[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xf[e] = bf16_value((u16)f.hi[e]) + bf16_value((u16)f.lo[e]);
+      store8_h2(ktg + frag_off(w, ks, 2, lane), ktl + frag_off(w, ks, 2, lane), xf);
+    }
+  }
+  // S6. M^T fragments from the M tile (wave w: token tile w >> 1, position
+  // k-step w & 1) as fp16 hi and lo planes and, in the first value head of a
+  // group, Q fragments from the Q tile (wave w: token tile w & 3, key k-steps
+  // 2 (w >> 2) and 2 (w >> 2) + 1) as fp16, both of the tiles' bf16 hi + lo
+  {
+    const int mt = w >> 1, ks = w & 1;
+    const Frag f = frag_pi(lqh, lql, PS, 16 * mt + l16, 32 * ks, kg);
+    float xf[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xf[e] = bf16_value((u16)f.hi[e]) + bf16_value((u16)f.lo[e]);
+    store8_h2(reinterpret_cast<u16 *>(wc + WV_M) + frag_off(mt, ks, 2, lane),
+              reinterpret_cast<u16 *>(wc + WV_ML) + frag_off(mt, ks, 2, lane), xf);
+  }
+  if (it.kown) {
+    const int mt = w & 3;
+    u16 *qg = reinterpret_cast<u16 *>(wk + WK_Q);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int ks = 2 * (w >> 2) + j;
+      const Frag f = frag_pi(qh, qlo, PR, 16 * mt + l16, 32 * ks, kg);
+      float xf[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xf[e] = bf16_value((u16)f.hi[e]) + bf16_value((u16)f.lo[e]);
+      store8_h(qg + frag_off(mt, ks, 4, lane), xf);
     }
   }
   __syncthreads();  // every diagonal block read before any is overwritten
@@ -932,42 +971,6 @@ __global__ __launch_bounds__(512) void k_chunk_prep(const SRC src, unsigned char
         *reinterpret_cast<float4 *>(ug + acc_off(2 * kp + d, 2 * tp + m, lane)) =
             make_float4(accU[d][m][0], accU[d][m][1], accU[d][m][2], accU[d][m][3]);
     }
-  }
-  // S6. M^T fragments from the M tile (wave w: token tile w >> 1, position
-  // k-step w & 1) as fp16 hi and lo planes and, in the first value head of a
-  // group, Q fragments from the Q tile (wave w: token tile w & 3, key k-steps
-  // 2 (w >> 2) and 2 (w >> 2) + 1) as fp16, both of the tiles' bf16 hi + lo
-  {
-    const int mt = w >> 1, ks = w & 1;
-    const Frag f = frag_pi(lqh, lql, PS, 16 * mt + l16, 32 * ks, kg);
-    float x[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = bf16_value((u16)f.hi[e]) + bf16_value((u16)f.lo[e]);
-    store8_h2(reinterpret_cast<u16 *>(wc + WV_M) + frag_off(mt, ks, 2, lane),
-              reinterpret_cast<u16 *>(wc + WV_ML) + frag_off(mt, ks, 2, lane), x);
-  }
-  if (it.kown) {
-    const int mt = w & 3;
-    u16 *qg = reinterpret_cast<u16 *>(wk + WK_Q);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int ks = 2 * (w >> 2) + j;
-      const Frag f = frag_pi(qh, qlo, PR, 16 * mt + l16, 32 * ks, kg);
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = bf16_value((u16)f.hi[e]) + bf16_value((u16)f.lo[e]);
-      store8_h(qg + frag_off(mt, ks, 4, lane), x);
-    }
-  }
-  // the chunk's header, formed and stored by wave 0 (every lane stores the
-  // same bits)
-  if (w == 0) {
-    const float bk = sBeta[lane] * sqrtf(sNK[lane]);
-    const float b = group_sum<64>(bk * sqrtf(sNV[lane]));
-    const float am = group_max64(bk);
-    *reinterpret_cast<float4 *>(wc + WV_G) = make_float4(sEG[CH - 1], b, am, 0.0f);
-    reinterpret_cast<float *>(wc + WV_EG)[lane] = sEG[lane];
-    reinterpret_cast<float *>(wc + WV_D)[lane] = sEGn[lane];
   }
   src.taps_to_lds(tid, pre, tiles);
   __syncthreads();   // the next item rewrites every LDS tile
