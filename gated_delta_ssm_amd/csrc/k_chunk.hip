@@ -932,45 +932,38 @@ __global__ __launch_bounds__(512) void k_chunk_prep(const SRC src, unsigned char
     }
     __syncthreads();
   }
-  // S5. W^T = K^T T1^T and Ut^T = V^T T2^T.  Wave w owns key/value tiles
-  // 2kp, 2kp+1 (kp = w & 3) and token tiles 2tp, 2tp+1 (tp = w >> 2).
-  const int kp = w & 3, tp = w >> 2;
-  f32x4 accW[2][2], accU[2][2];
+  // S5. W^T = K^T T1^T and Ut^T = V^T T2^T.  Wave w owns token tile
+  // mt = w >> 1 and key/value tiles 4hf .. 4hf + 3 (hf = w & 1), so the T
+  // fragments it forms (one token tile, two k-steps) serve four tiles each.
+  const int mt = w >> 1, hf = w & 1;
+  f32x4 accW[4], accU[4];   // key / value tile 4hf + d
 #pragma unroll
-  for (int d = 0; d < 2; ++d)
-#pragma unroll
-    for (int m = 0; m < 2; ++m) accW[d][m] = accU[d][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int d = 0; d < 4; ++d) accW[d] = accU[d] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
-    Frag bt1[2], bt2[2];
+    Frag bt1, bt2;
+    t_frags(sA, sBeta, sEG, 16 * mt + l16, 32 * ks, kg, bt1, bt2);
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      t_frags(sA, sBeta, sEG, 16 * (2 * tp + m) + l16, 32 * ks, kg, bt1[m], bt2[m]);
-    }
-#pragma unroll
-    for (int d = 0; d < 2; ++d) {
-      const Frag ak = frag_tr(kh, klo, PR, 32 * ks, 16 * (2 * kp + d), kg, l16);
-      const Frag av = frag_tr(vh, vlo, PR, 32 * ks, 16 * (2 * kp + d), kg, l16);
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        accW[d][m] = mfma3(ak, bt1[m], accW[d][m]);
-        accU[d][m] = mfma3(av, bt2[m], accU[d][m]);
-      }
+    for (int d = 0; d < 4; ++d) {
+      const Frag ak = frag_tr(kh, klo, PR, 32 * ks, 16 * (4 * hf + d), kg, l16);
+      const Frag av = frag_tr(vh, vlo, PR, 32 * ks, 16 * (4 * hf + d), kg, l16);
+      accW[d] = mfma3(ak, bt1, accW[d]);
+      accU[d] = mfma3(av, bt2, accU[d]);
     }
   }
-  {  // W fragments and Ut tiles -> workspace
+  {  // W fragments (token tile mt, key k-steps 2hf, 2hf + 1) and Ut tiles -> workspace
     u16 *wg = reinterpret_cast<u16 *>(wc + WV_W);
     float *ug = reinterpret_cast<float *>(wc + WV_U);
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const float xw[8] = {accW[0][m][0], accW[0][m][1], accW[0][m][2], accW[0][m][3],
-                           accW[1][m][0], accW[1][m][1], accW[1][m][2], accW[1][m][3]};
-      store8_h(wg + frag_off(2 * tp + m, kp, 4, lane), xw);
-#pragma unroll
-      for (int d = 0; d < 2; ++d)
-        *reinterpret_cast<float4 *>(ug + acc_off(2 * kp + d, 2 * tp + m, lane)) =
-            make_float4(accU[d][m][0], accU[d][m][1], accU[d][m][2], accU[d][m][3]);
+    for (int p = 0; p < 2; ++p) {
+      const f32x4 a0 = accW[2 * p], a1 = accW[2 * p + 1];
+      const float xw[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      store8_h(wg + frag_off(mt, 2 * hf + p, 4, lane), xw);
     }
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      *reinterpret_cast<float4 *>(ug + acc_off(4 * hf + d, mt, lane)) =
+          make_float4(accU[d][0], accU[d][1], accU[d][2], accU[d][3]);
   }
   src.taps_to_lds(tid, pre, tiles);
   __syncthreads();   // the next item rewrites every LDS tile
