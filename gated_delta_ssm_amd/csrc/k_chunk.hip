@@ -449,9 +449,9 @@ __device__ __forceinline__ float bf16_to_f32(unsigned b) { return __builtin_bit_
 // 64 + 4l .. 64 + 4l+3): each load instruction then reads 256 contiguous
 // bytes per row, and the quads are the 4-channel groups of the conv
 // kernels' lanes.
-// 4 consecutive elements as a float4.  fp32 inputs are read once per item
-// (q and k once per value head of their group) and loaded non-temporally,
-// so that they do not displace the workspace from the last-level cache.
+// 4 consecutive elements as a float4.  fp32 inputs read once are loaded
+// non-temporally, so that they do not displace the workspace from the
+// last-level cache.
 __device__ __forceinline__ float4 load4f(const float *p) {
   const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
   return make_float4(v[0], v[1], v[2], v[3]);
@@ -460,6 +460,17 @@ __device__ __forceinline__ float4 load4f(const u16 *p) {
   const uint2 u = *reinterpret_cast<const uint2 *>(p);
   return make_float4(bf16_to_f32(u.x & 0xffffu), bf16_to_f32(u.x >> 16),
                      bf16_to_f32(u.y & 0xffffu), bf16_to_f32(u.y >> 16));
+}
+// q and k rows, read by every value head of their group (whose items run side
+// by side on one XCD): ordinary loads, so the group's later heads find them
+// in the XCD's L2 (measured: 1 to 2 % off the call against non-temporal ones)
+__device__ __forceinline__ void load_quads_shared(const float *p, int l, float4 &a, float4 &b) {
+  a = *reinterpret_cast<const float4 *>(p + 4 * l);
+  b = *reinterpret_cast<const float4 *>(p + 64 + 4 * l);
+}
+__device__ __forceinline__ void load_quads_shared(const u16 *p, int l, float4 &a, float4 &b) {
+  a = load4f(p + 4 * l);
+  b = load4f(p + 64 + 4 * l);
 }
 // the lane's two quads of the row at p
 template <class T>
@@ -513,9 +524,9 @@ struct DirectSrc {
     for (int i = 0; i < 2; ++i) {
       const int rr = min(row_of(i, tid), it.nl);
       if constexpr (PART == 0)
-        load_quads(k + kb + (int64_t)rr * qk_tok, l, r.kr[2 * i], r.kr[2 * i + 1]);
+        load_quads_shared(k + kb + (int64_t)rr * qk_tok, l, r.kr[2 * i], r.kr[2 * i + 1]);
       if constexpr (PART == 1)
-        load_quads(q + kb + (int64_t)rr * qk_tok, l, r.qr[2 * i], r.qr[2 * i + 1]);
+        load_quads_shared(q + kb + (int64_t)rr * qk_tok, l, r.qr[2 * i], r.qr[2 * i + 1]);
       if constexpr (PART == 2)
         load_quads(v + vb + (int64_t)rr * v_tok, l, r.vr[2 * i], r.vr[2 * i + 1]);
     }
