@@ -395,14 +395,21 @@ __device__ __forceinline__ PrepItem prep_item(int u, int n_chunks, int H, int Hk
   it.kown = it.h % (H / Hk) == 0;
   return it;
 }
-// Variable-length batch: item u = (head, packed chunk gc), gc fastest; the
-// sequence holding gc is found by binary search over the chunk offsets.
+// Variable-length batch: item u = (packed chunk gc, head), heads fastest, the
+// packed chunks from the last to the first, and the G value heads of a group
+// 8 items apart when H is a multiple of 8 G, as for a fixed-length batch: the
+// group's q and k rows then come from HBM once, and the chunks at the front
+// of the packing, which phase B's first workgroups read, are the last written.
+// The sequence holding gc is found by binary search over the chunk offsets.
 __device__ __forceinline__ PrepItem prep_item(int u, int n_chunks, int H, int Hk, int,
                                               const VarTab &tab, int) {
   PrepItem it;
-  const int gc = u % n_chunks;
-  it.h = u / n_chunks;
-  it.hk = it.h / (H / Hk);
+  const int G = H / Hk, gc = n_chunks - 1 - u / H, idx = u % H;
+  if (H % (8 * G) == 0)
+    it.h = ((idx / (8 * G)) * 8 + idx % 8) * G + (idx / 8) % G;
+  else
+    it.h = idx;
+  it.hk = it.h / G;
   int lo = 0, hi = tab.n_seq - 1;   // last s with ch0[s] <= gc: a nonempty sequence
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
